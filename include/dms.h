@@ -1,0 +1,236 @@
+/*
+ * dms.h — C ABI of the DMS (Dynamic Memory Sparsification) inference hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (pages cited by title and section):
+ *   - the per-KV-head keep/evict decision: logit = Linear(RMSNorm(h)) * scale
+ *     - offset, or the repurposed last element of the first query head of each
+ *     KV group times scale minus offset; a token is evicted when logit > 0
+ *     ("基于 DMS 的 KV Cache 压缩实战" walkthrough, sections 决策来源一,
+ *     决策来源二, 决策粒度, and the inference hard threshold in the Gumbel
+ *     section);
+ *   - delayed eviction into a per-head paged KV store: a marked token stays
+ *     visible until it leaves the sliding window w, then the token w positions
+ *     later overwrites its slot in place (same walkthrough, 延迟驱逐 and
+ *     推理模式);
+ *   - GQA decode attention and chunked-prefill attention over the resulting
+ *     ragged per-head cache (推理模式; 高级选项 Chunked Prefill; the exact
+ *     prefill with the eviction mask in the repository tree).
+ *
+ * Key j is visible to query i iff j <= i and (j is kept or i - j < w).
+ *
+ * Conventions for every call:
+ *   - Returns 0 (DMS_OK) or a negative dms_status.  Argument and configuration
+ *     errors are detected on the host before anything is launched; the
+ *     message is available from dms_last_error() (thread-local).
+ *   - Conditions only the device can see (page pool exhausted, a sequence
+ *     past its preallocated capacity, a sequence id out of range) set bits of
+ *     a sticky device status word and skip the affected writes; read it with
+ *     dms_cache_status().  After a nonzero device status the cache contents
+ *     are unspecified until the affected sequences are reset.
+ *   - All tensor pointers are device pointers owned by the caller, contiguous
+ *     row-major, unless stated otherwise.  The library allocates no device
+ *     memory: the cache lives in one caller-allocated buffer.
+ *   - Calls are asynchronous on the given stream (a hipStream_t passed as
+ *     void*; NULL is the null stream).  One cache handle must be used from one
+ *     stream at a time.
+ *   - "act" dtype is the dtype of hidden states, Q/K/V inputs and outputs:
+ *     float32 when kv_dtype is DMS_F32, bfloat16 otherwise.
+ */
+#ifndef DMS_H
+#define DMS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dms_status {
+  DMS_OK = 0,
+  DMS_ERR_ARG = -1,          /* null pointer, bad size, bad sequence id list */
+  DMS_ERR_CONFIG = -2,       /* configuration rejected by dms_config_validate */
+  DMS_ERR_CAPACITY = -3,     /* buffer too small, B or T above the configured maximum */
+  DMS_ERR_POOL = -4,         /* reserved: pool exhaustion is reported by the device status */
+  DMS_ERR_HIP = -5,          /* a HIP runtime call failed */
+  DMS_ERR_UNSUPPORTED = -6   /* shape/dtype combination without a kernel */
+} dms_status;
+
+/* Bits of the sticky device status word (dms_cache_status). */
+#define DMS_DEV_POOL_EXHAUSTED 0x1  /* an append needed a page and the pool was empty */
+#define DMS_DEV_CAPACITY 0x2        /* an append would pass max_tokens_per_seq */
+#define DMS_DEV_BAD_SEQ 0x4         /* a sequence id outside [0, max_batch) */
+
+typedef enum dms_dtype { DMS_F32 = 0, DMS_BF16 = 1, DMS_FP8_E4M3 = 2 } dms_dtype;
+typedef enum dms_decide_mode { DMS_DECIDE_LINEAR = 0, DMS_DECIDE_QNEURON = 1 } dms_decide_mode;
+typedef enum dms_alpha_per { DMS_ALPHA_PER_HEAD = 0, DMS_ALPHA_PER_LAYER = 1 } dms_alpha_per;
+
+/*
+ * Configuration of one layer's cache (walkthrough, Qwen3ConfigDMS parameter
+ * table and hard constraints: block_size > 0 and window > block_size).
+ */
+typedef struct dms_config {
+  int32_t max_batch;           /* sequence slots (ids 0..max_batch-1) */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv; Hq / Hkv must be 1, 2, 4 or 8 */
+  int32_t head_dim;            /* D: 32, 64 or 128 */
+  int32_t hidden;              /* H of the hidden states fed to the linear adapter (multiple of 4) */
+  int32_t window;              /* w: sliding window of delayed eviction (dms_window_size) */
+  int32_t block_size;          /* P: slots per page (dms_paged_attention_block_size) */
+  int32_t max_tokens_per_seq;  /* preallocated positions per sequence (dms_preallocate_for_tokens) */
+  int32_t pool_pages;          /* pages in the shared pool, over all sequences and heads */
+  int32_t max_chunk;           /* largest T of one append or prefill call (dms_chunked_prefill) */
+  int32_t kv_dtype;            /* dms_dtype of the pages */
+  int32_t decide_mode;         /* dms_decide_mode (dms_separate_alpha True -> LINEAR) */
+  int32_t alpha_per;           /* dms_alpha_per (dms_alpha_per) */
+  int32_t disable_eviction;    /* nonzero: every decision is "keep" (dms_disable_eviction) */
+  float alpha_scale;           /* dms_alpha_scale (100) */
+  float rms_eps;               /* RMSNorm epsilon of the adapter norm */
+  float softmax_scale;         /* 0 means 1/sqrt(head_dim) */
+} dms_config;
+
+typedef struct dms_cache dms_cache;
+
+/* Host-side copies of the cache tables (dms_cache_dump).  Any pointer may be NULL. */
+typedef struct dms_dump {
+  int32_t* lengths;      /* [max_batch][Hkv] live slots per head */
+  int32_t* page_table;   /* [max_batch][Hkv][max_pages_per_seq] page ids, -1 unused */
+  int32_t* slot_meta;    /* [pool_pages][block_size] position | (evict << 31) of each slot's token */
+  int32_t* ring;         /* [max_batch][Hkv][window] slot | (evict << 31) of position p at p % window */
+  int32_t* positions;    /* [max_batch] tokens appended per sequence */
+  int32_t* free_stack;   /* [pool_pages] free page ids, next pop at free_count-1 */
+  int32_t* free_count;   /* [1] */
+  void* k_pages;         /* [pool_pages][block_size][D] raw page bytes (kv dtype) */
+  void* v_pages;         /* same for V */
+  float* page_scales;    /* [pool_pages][2] fp8 K/V scales */
+} dms_dump;
+
+typedef struct dms_stats {
+  int64_t tokens;            /* sum over sequences and KV heads of appended tokens */
+  int64_t live_slots;        /* sum of per-head lengths */
+  int64_t pages_in_use;      /* pool pages held by sequences */
+  int64_t bytes_live;        /* K+V bytes of live slots */
+  int64_t bytes_allocated;   /* K+V bytes of held pages */
+  double cache_cr;           /* tokens / live_slots */
+} dms_stats;
+
+/* Validates a configuration.  DMS_ERR_CONFIG (with a message) when block_size
+ * <= 0, window <= block_size, Hq % Hkv != 0, an unsupported head_dim, group
+ * size or dtype, a bad enum, or a nonpositive size. */
+int dms_config_validate(const dms_config* cfg);
+
+/* Bytes of the single device buffer a cache with this configuration needs. */
+int dms_cache_bytes(const dms_config* cfg, size_t* bytes);
+
+/* Pages a sequence may hold per KV head: ceil(max_tokens_per_seq / block_size). */
+int dms_max_pages_per_seq(const dms_config* cfg, int32_t* pages);
+
+/*
+ * Creates a cache inside dev_buf (device memory of at least
+ * dms_cache_bytes(cfg), 256-byte aligned, owned by the caller and kept alive
+ * until dms_cache_destroy) and initialises it on `stream`: every sequence
+ * empty, the free stack ordered so pops return pages 0, 1, 2, ..., status 0.
+ * The host handle (*out) owns no device memory.
+ */
+int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* stream, dms_cache** out);
+
+/* Frees the host handle.  The device buffer stays the caller's. */
+int dms_cache_destroy(dms_cache* cache);
+
+/* Copy of the configuration the cache was created with. */
+int dms_cache_config(const dms_cache* cache, dms_config* cfg);
+
+/*
+ * Decision for B x T tokens (walkthrough, 决策来源一 / 决策来源二 / 决策粒度).
+ * LINEAR: hidden [B][T][H] (act dtype), rms_gamma [H] f32, W [Hkv][H] f32,
+ *   bias [Hkv] f32 or NULL, offsets [Hkv] f32.  Computes
+ *   z = W . (h / sqrt(mean(h^2) + eps) * gamma) (+ bias) in fp32,
+ *   logit = alpha_scale * z - offset.  q_inout is ignored (may be NULL).
+ * QNEURON: q_inout [B][T][Hq][D] (act dtype), offsets [Hkv] f32;
+ *   logit[b][k][t] = alpha_scale * q[b][t][k*g][D-1] - offset[k], after which
+ *   that element is set to 0 in place.  hidden/gamma/W/bias are ignored.
+ * alpha_per LAYER: every head takes head 0's logit (all k*g neurons are still
+ * zeroed).  evict = disable_eviction ? 0 : logit > 0.
+ * Outputs: logits_out [B][Hkv][T] f32 (may be NULL), evict_out [B][Hkv][T] u8.
+ * Pure function of its inputs; does not touch the cache state.
+ */
+int dms_decide(dms_cache* cache, const void* hidden, const float* rms_gamma, const float* W,
+               const float* bias, const float* offsets, void* q_inout, int B, int T,
+               float* logits_out, uint8_t* evict_out, void* stream);
+
+/*
+ * Appends T tokens to each of B sequences (walkthrough, 推理模式: if the token
+ * w positions back was marked, the new token overwrites its slot in place;
+ * otherwise it takes the next free slot, opening a page from the shared pool
+ * when the head's length is a multiple of block_size).
+ * seq_ids [B] int32 device array (NULL: row b is sequence b); ids in one call
+ * must be distinct.  k, v [B][T][Hkv][D] act dtype; evict [B][Hkv][T] u8.
+ * Token positions continue from each sequence's count of appended tokens.
+ * T == 1 is the decode append; T > 1 (<= max_chunk) gives exactly the slot
+ * table of T single-token appends and writes only each slot's final occupant.
+ * Pages are handed out in (row, head) row-major order, then token order.
+ * fp8 pages: a page's K and V scales are set when it is opened, from the
+ * largest magnitude the opening call writes into it (power of two with two
+ * binades of headroom); values are stored as e4m3 (nearest even, saturating).
+ * Device-side: DMS_DEV_CAPACITY, DMS_DEV_POOL_EXHAUSTED, DMS_DEV_BAD_SEQ.
+ * Order: after dms_prefill_attn for a prefill chunk, before dms_decode_attn
+ * for a decode token.
+ */
+int dms_append_evict(dms_cache* cache, const int32_t* seq_ids, const void* k, const void* v,
+                     const uint8_t* evict, int B, int T, void* stream);
+
+/*
+ * Decode attention (walkthrough, 推理模式: attention over the per-head paged
+ * cache).  For each row b and query head h (KV head h / g):
+ *   out[b][h] = softmax_s(scale * <q[b][h], K_s>) V_s over all live slots s of
+ *   that head — after the append of the current token the live slots are
+ *   exactly the visible keys, so no mask is applied.
+ * q [B][Hq][D], out [B][Hq][D] act dtype; seq_ids as in dms_append_evict.
+ * A head with no live slot gets zeros.  fp32 accumulation.
+ */
+int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, void* out, int B,
+                    void* stream);
+
+/*
+ * Prefill attention for one chunk of C new tokens per sequence (walkthrough,
+ * 高级选项 Chunked Prefill, and the exact prefill with the eviction mask),
+ * computed against the cache state *before* the chunk is appended.  Query i
+ * (position pos+i) sees cached slot s iff its token is kept or i - pos_s < w,
+ * and chunk key j iff j <= i and (evict[j] == 0 or i - j < w).
+ * q [B][C][Hq][D], k/v [B][C][Hkv][D], out [B][C][Hq][D] act dtype;
+ * evict [B][Hkv][C] u8.  C <= max_chunk.
+ */
+int dms_prefill_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, const void* k,
+                     const void* v, const uint8_t* evict, void* out, int B, int C, void* stream);
+
+/*
+ * Empties the listed sequences (walkthrough, 当前限制: the cache is reset
+ * between independent sequences).  Pages return to the pool in reverse
+ * page-table order, sequences and heads in reverse order, so the next pops
+ * return them in their original order.  seq_ids [n] device array, or NULL to
+ * reset sequences 0..n-1.
+ */
+int dms_seq_reset(dms_cache* cache, const int32_t* seq_ids, int n, void* stream);
+
+/* Synchronises `stream` and returns the sticky device status bits in *device_status. */
+int dms_cache_status(dms_cache* cache, void* stream, int32_t* device_status);
+
+/* Clears the sticky device status word (asynchronous). */
+int dms_cache_clear_status(dms_cache* cache, void* stream);
+
+/* Synchronises `stream` and copies the tables into host buffers. */
+int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out);
+
+/* Synchronises `stream` and summarises occupancy (walkthrough, 损失函数与压缩比调度:
+ * realised compression; here tokens / live slots). */
+int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out);
+
+/* Last error message of this thread ("" if none). */
+const char* dms_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMS_H */

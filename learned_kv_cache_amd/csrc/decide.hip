@@ -1,0 +1,168 @@
+// dms_decide: the per-KV-head keep/evict decision.
+//
+// Linear adapter ("基于 DMS 的 KV Cache 压缩实战" walkthrough, 决策来源二):
+//   logit[b][k][t] = alpha * (W_k . RMSNorm(h[b][t])) - offset_k.
+// Repurposed query neuron (same page, 决策来源一):
+//   logit[b][k][t] = alpha * q[b][t][k*g][D-1] - offset_k, then that element is
+//   set to zero.
+// Granularity (决策粒度): "layer" gives every head head 0's logit.
+// Threshold (Gumbel section, inference): evict = logit > 0; with
+// disable_eviction nothing is evicted.
+//
+// The projection reads h once (2 bytes per element for bf16) and does
+// Hkv + 1 fused multiply-adds per element, so it is bound by HBM, not by
+// arithmetic; it runs in fp32 on the vector ALUs.  Rounding the normalised
+// activations to bf16 for a matrix-core product would move logits by ~0.1,
+// far more than the 1e-2 margin the decisions are compared at.
+#include "dms_internal.h"
+
+namespace dms {
+
+struct DecideArgs {
+  const void* hidden;
+  const float* gamma;
+  const float* W;
+  const float* bias;
+  const float* offsets;
+  int ntok;            // B * T
+  int T;
+  int H;
+  float alpha;
+  float eps;
+  int per_layer;
+  int disable;
+  float* logits;       // [B][Hkv][T] or null
+  uint8_t* evict;      // [B][Hkv][T]
+};
+
+template <int N> __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], o);
+  }
+}
+
+// One wave per token: every lane accumulates sum(h^2) and, for each head,
+// sum(W_k * gamma * h) over its share of H; then z_k = r * dot_k with
+// r = 1 / sqrt(mean(h^2) + eps).
+template <typename ACT, int HKV>
+__global__ __launch_bounds__(256) void decide_linear_kernel(DecideArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= a.ntok) return;
+  const ACT* h = static_cast<const ACT*>(a.hidden) + static_cast<size_t>(tok) * a.H;
+  float acc[HKV + 1];
+#pragma unroll
+  for (int i = 0; i <= HKV; ++i) acc[i] = 0.0f;
+  for (int m = lane * 4; m < a.H; m += 256) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = load_act<ACT>(h, m + e);
+    const float4 gm = *reinterpret_cast<const float4*>(a.gamma + m);
+    const float gx[4] = {gm.x * x[0], gm.y * x[1], gm.z * x[2], gm.w * x[3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[HKV] = fmaf(x[e], x[e], acc[HKV]);
+#pragma unroll
+    for (int k = 0; k < HKV; ++k) {
+      const float4 w = *reinterpret_cast<const float4*>(a.W + static_cast<size_t>(k) * a.H + m);
+      acc[k] = fmaf(w.x, gx[0], acc[k]);
+      acc[k] = fmaf(w.y, gx[1], acc[k]);
+      acc[k] = fmaf(w.z, gx[2], acc[k]);
+      acc[k] = fmaf(w.w, gx[3], acc[k]);
+    }
+  }
+  wave_sum_n<HKV + 1>(acc);
+  if (lane != 0) return;
+  const float r = 1.0f / sqrtf(acc[HKV] / static_cast<float>(a.H) + a.eps);
+  const int b = tok / a.T, t = tok % a.T;
+  float lg0 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < HKV; ++k) {
+    float z = r * acc[k];
+    if (a.bias) z += a.bias[k];
+    float lg = a.alpha * z - a.offsets[k];
+    if (k == 0) lg0 = lg;
+    if (a.per_layer) lg = lg0;
+    const size_t o = (static_cast<size_t>(b) * HKV + k) * a.T + t;
+    if (a.logits) a.logits[o] = lg;
+    a.evict[o] = (!a.disable && lg > 0.0f) ? 1 : 0;
+  }
+}
+
+struct QneuronArgs {
+  void* q;             // [B][T][Hq][D]
+  const float* offsets;
+  int ntok, T, Hkv, g, D;
+  float alpha;
+  int per_layer, disable;
+  float* logits;
+  uint8_t* evict;
+};
+
+// One thread per token: read every group's neuron first, then zero them.
+template <typename ACT>
+__global__ void decide_qneuron_kernel(QneuronArgs a) {
+  const int tok = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tok >= a.ntok) return;
+  ACT* q = static_cast<ACT*>(a.q) + static_cast<size_t>(tok) * a.Hkv * a.g * a.D;
+  const int b = tok / a.T, t = tok % a.T;
+  const float lg0 = a.alpha * load_act<ACT>(q, static_cast<size_t>(a.D) - 1) - a.offsets[0];
+  for (int k = 0; k < a.Hkv; ++k) {
+    const size_t qi = static_cast<size_t>(k) * a.g * a.D + a.D - 1;
+    const float lg = a.per_layer ? lg0 : a.alpha * load_act<ACT>(q, qi) - a.offsets[k];
+    const size_t o = (static_cast<size_t>(b) * a.Hkv + k) * a.T + t;
+    if (a.logits) a.logits[o] = lg;
+    a.evict[o] = (!a.disable && lg > 0.0f) ? 1 : 0;
+  }
+  for (int k = 0; k < a.Hkv; ++k) store_act<ACT>(q, static_cast<size_t>(k) * a.g * a.D + a.D - 1, 0.0f);
+}
+
+template <typename ACT>
+static void launch_linear(const DecideArgs& a, int hkv, hipStream_t st) {
+  const dim3 grid((a.ntok + 3) / 4), block(256);
+  switch (hkv) {
+    case 1: hipLaunchKernelGGL((decide_linear_kernel<ACT, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decide_linear_kernel<ACT, 2>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decide_linear_kernel<ACT, 4>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decide_linear_kernel<ACT, 8>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decide_linear_kernel<ACT, 16>), grid, block, 0, st, a); break;
+    default: break;
+  }
+}
+
+}  // namespace dms
+
+using namespace dms;
+
+extern "C" int dms_decide(dms_cache* cache, const void* hidden, const float* rms_gamma, const float* W,
+                          const float* bias, const float* offsets, void* q_inout, int B, int T,
+                          float* logits_out, uint8_t* evict_out, void* stream) {
+  if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
+  const dms_config& c = cache->cfg;
+  if (B <= 0 || T <= 0) return fail(DMS_ERR_ARG, "B and T must be positive");
+  if (!offsets || !evict_out) return fail(DMS_ERR_ARG, "offsets and evict_out are required");
+  const bool act_f32 = c.kv_dtype == DMS_F32;
+  hipStream_t st = as_stream(stream);
+  if (c.decide_mode == DMS_DECIDE_LINEAR) {
+    if (!hidden || !rms_gamma || !W) return fail(DMS_ERR_ARG, "hidden, rms_gamma and W are required");
+    const int hkv = c.num_kv_heads;
+    if (hkv != 1 && hkv != 2 && hkv != 4 && hkv != 8 && hkv != 16)
+      return fail(DMS_ERR_UNSUPPORTED, "linear decision needs num_kv_heads in {1,2,4,8,16}");
+    if ((reinterpret_cast<uintptr_t>(rms_gamma) | reinterpret_cast<uintptr_t>(W)) % 16 != 0)
+      return fail(DMS_ERR_ARG, "rms_gamma and W must be 16-byte aligned");
+    DecideArgs a{hidden, rms_gamma, W, bias, offsets, B * T, T, c.hidden, c.alpha_scale, c.rms_eps,
+                 c.alpha_per == DMS_ALPHA_PER_LAYER, c.disable_eviction != 0, logits_out, evict_out};
+    if (act_f32) launch_linear<float>(a, hkv, st);
+    else launch_linear<uint16_t>(a, hkv, st);
+  } else {
+    if (!q_inout) return fail(DMS_ERR_ARG, "q_inout is required for the query-neuron decision");
+    QneuronArgs a{q_inout, offsets, B * T, T, c.num_kv_heads, c.num_q_heads / c.num_kv_heads, c.head_dim,
+                  c.alpha_scale, c.alpha_per == DMS_ALPHA_PER_LAYER, c.disable_eviction != 0, logits_out,
+                  evict_out};
+    const dim3 grid((B * T + 255) / 256), block(256);
+    if (act_f32) hipLaunchKernelGGL(decide_qneuron_kernel<float>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(decide_qneuron_kernel<uint16_t>, grid, block, 0, st, a);
+  }
+  return check_hip(hipGetLastError(), "dms_decide launch");
+}

@@ -1,0 +1,374 @@
+// Host side of the DMS C ABI: configuration checks, the layout of the single
+// cache buffer, creation/initialisation, reset, status, dump and stats.
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dms_internal.h"
+
+namespace dms {
+
+static thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DMS_OK;
+  return fail(DMS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int kv_elem_bytes(int kv_dtype) {
+  switch (kv_dtype) {
+    case DMS_F32: return 4;
+    case DMS_BF16: return 2;
+    case DMS_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int compute_layout(const dms_config& c, Layout* L) {
+  const size_t elem = static_cast<size_t>(kv_elem_bytes(c.kv_dtype));
+  const size_t pool = static_cast<size_t>(c.pool_pages);
+  const size_t P = static_cast<size_t>(c.block_size);
+  const size_t D = static_cast<size_t>(c.head_dim);
+  const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
+  const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + P - 1) / P;
+  const size_t g = static_cast<size_t>(c.num_q_heads / c.num_kv_heads);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->k_pages = take(pool * P * D * elem);
+  L->v_pages = take(pool * P * D * elem);
+  L->scales = take(pool * 2 * sizeof(float));
+  L->page_amax = take(pool * 2 * sizeof(uint32_t));
+  L->slot_meta = take(pool * P * sizeof(int32_t));
+  L->page_table = take(units * maxp * sizeof(int32_t));
+  L->lengths = take(units * sizeof(int32_t));
+  L->ring = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
+  L->pos = take(static_cast<size_t>(c.max_batch) * sizeof(int32_t));
+  L->free_stack = take(pool * sizeof(int32_t));
+  L->ctl = take(kCtlWords * sizeof(int32_t));
+  L->chunk_slot = take(units * static_cast<size_t>(c.max_chunk) * sizeof(int32_t));
+  L->chunk_info = take(units * 8 * sizeof(int32_t));
+  L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
+  L->partial_records = kMaxDecodeGrid + kMaxUnits;
+  L->partials = take(static_cast<size_t>(L->partial_records) * g * (D + 2) * sizeof(float));
+  L->total = off;
+  return DMS_OK;
+}
+
+static int validate(const dms_config* c) {
+  if (!c) return fail(DMS_ERR_ARG, "config is NULL");
+  if (c->max_batch <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->hidden <= 0 || c->max_tokens_per_seq <= 0 || c->pool_pages <= 0 || c->max_chunk <= 0)
+    return fail(DMS_ERR_CONFIG, "sizes must be positive");
+  if (c->block_size <= 0) return fail(DMS_ERR_CONFIG, "block_size must be > 0");
+  if (c->window <= c->block_size) return fail(DMS_ERR_CONFIG, "window must be greater than block_size");
+  if (c->num_q_heads % c->num_kv_heads != 0)
+    return fail(DMS_ERR_CONFIG, "num_q_heads must be a multiple of num_kv_heads");
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return fail(DMS_ERR_CONFIG, "group size must be 1, 2, 4 or 8");
+  if (c->num_kv_heads > 16) return fail(DMS_ERR_CONFIG, "num_kv_heads must be <= 16");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(DMS_ERR_CONFIG, "head_dim must be 32, 64 or 128");
+  if (c->hidden % 4 != 0) return fail(DMS_ERR_CONFIG, "hidden must be a multiple of 4");
+  if (kv_elem_bytes(c->kv_dtype) == 0) return fail(DMS_ERR_CONFIG, "bad kv_dtype");
+  if (c->decide_mode != DMS_DECIDE_LINEAR && c->decide_mode != DMS_DECIDE_QNEURON)
+    return fail(DMS_ERR_CONFIG, "bad decide_mode");
+  if (c->alpha_per != DMS_ALPHA_PER_HEAD && c->alpha_per != DMS_ALPHA_PER_LAYER)
+    return fail(DMS_ERR_CONFIG, "alpha_per must be head or layer");
+  if (c->max_chunk > kMaxChunk) return fail(DMS_ERR_CONFIG, "max_chunk above 8192");
+  if (static_cast<int64_t>(c->max_batch) * c->num_kv_heads > kMaxUnits)
+    return fail(DMS_ERR_CONFIG, "max_batch * num_kv_heads above 2048");
+  if (!(c->alpha_scale == c->alpha_scale) || !(c->rms_eps >= 0.0f) || !(c->softmax_scale >= 0.0f))
+    return fail(DMS_ERR_CONFIG, "alpha_scale, rms_eps and softmax_scale must be finite, eps and scale >= 0");
+  if (static_cast<int64_t>(c->pool_pages) * c->block_size >= (1ll << 31))
+    return fail(DMS_ERR_CONFIG, "pool_pages * block_size must stay below 2^31");
+  if (c->max_tokens_per_seq >= (1 << 30)) return fail(DMS_ERR_CONFIG, "max_tokens_per_seq too large");
+  return DMS_OK;
+}
+
+int decode_grid_for(const dms_cache* c) { return c->decode_grid; }
+
+// Fills the control words, the free stack (pops return 0, 1, 2, ...), empty
+// lengths/positions, unused page-table entries and zero decode counters.
+__global__ void init_kernel(DevCache d, Geo g, int units) {
+  const int64_t n = static_cast<int64_t>(blockDim.x) * gridDim.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < g.pool; i += n) d.free_stack[i] = g.pool - 1 - static_cast<int32_t>(i);
+  for (int64_t i = i0; i < static_cast<int64_t>(units) * g.maxp; i += n) d.page_table[i] = -1;
+  for (int64_t i = i0; i < units; i += n) d.lengths[i] = 0;
+  for (int64_t i = i0; i < g.Bmax; i += n) d.pos[i] = 0;
+  for (int64_t i = i0; i < kCtlWords; i += n) d.ctl[i] = (i == kCtlFreeCount) ? g.pool : 0;
+  for (int64_t i = i0; i < static_cast<int64_t>(kMaxUnits) * 4; i += n) d.unit_info[i] = 0;
+  for (int64_t i = i0; i < static_cast<int64_t>(g.pool) * 2; i += n) {
+    d.scales[i] = 1.0f;
+    d.page_amax[i] = 0u;
+  }
+}
+
+// Returns the listed sequences' pages to the pool.  Pairs (sequence, head) are
+// visited in reverse list order; each pair pushes its pages in reverse page
+// order, so later pops return them in their original order.
+__global__ __launch_bounds__(1024) void reset_kernel(DevCache d, Geo g, const int32_t* seq_ids, int n) {
+  __shared__ int s_wave[16];
+  __shared__ int s_base;
+  __shared__ int s_free;
+  const int tid = threadIdx.x;
+  const int npairs = n * g.Hkv;
+  if (tid == 0) {
+    s_free = d.ctl[kCtlFreeCount];
+    s_base = 0;
+  }
+  __syncthreads();
+  for (int r0 = 0; r0 < npairs; r0 += 1024) {
+    // r indexes pairs in push order: r = 0 is the last pair of the list.
+    const int r = r0 + tid;
+    int seq = -1, kh = 0, npg = 0;
+    if (r < npairs) {
+      const int p = npairs - 1 - r;
+      const int row = p / g.Hkv;
+      kh = p % g.Hkv;
+      seq = seq_ids ? seq_ids[row] : row;
+      if (seq < 0 || seq >= g.Bmax) {
+        set_status(d.ctl, DMS_DEV_BAD_SEQ);
+        seq = -1;
+      } else {
+        const int L = d.lengths[seq * g.Hkv + kh];
+        npg = (L + g.P - 1) / g.P;
+      }
+    }
+    // exclusive scan of npg over the block
+    int x = npg;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int wave_off = 0, round_total = 0;
+    for (int i = 0; i < 16; ++i) {
+      if (i < wave) wave_off += s_wave[i];
+      round_total += s_wave[i];
+    }
+    const int excl = s_base + wave_off + x - npg;
+    if (seq >= 0) {
+      const int32_t* pt = d.page_table + (static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp;
+      for (int j = 0; j < npg; ++j) {
+        const int dst = s_free + excl + j;
+        if (dst < g.pool) d.free_stack[dst] = pt[npg - 1 - j];
+      }
+    }
+    __syncthreads();
+    if (tid == 0) s_base += round_total;
+    __syncthreads();
+  }
+  // clear the pairs after every push has read its page table
+  for (int r = tid; r < npairs; r += 1024) {
+    const int row = r / g.Hkv, kh = r % g.Hkv;
+    const int seq = seq_ids ? seq_ids[row] : row;
+    if (seq < 0 || seq >= g.Bmax) continue;
+    int32_t* pt = d.page_table + (static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp;
+    for (int j = 0; j < g.maxp; ++j) pt[j] = -1;
+    d.lengths[seq * g.Hkv + kh] = 0;
+    if (kh == 0) d.pos[seq] = 0;
+  }
+  if (tid == 0) d.ctl[kCtlFreeCount] = min(g.pool, s_free + s_base);
+}
+
+__global__ void clear_status_kernel(int32_t* ctl) { ctl[kCtlStatus] = 0; }
+
+}  // namespace dms
+
+using namespace dms;
+
+extern "C" {
+
+const char* dms_last_error(void) { return g_last_error.c_str(); }
+
+int dms_config_validate(const dms_config* cfg) {
+  int s = validate(cfg);
+  if (s == DMS_OK) g_last_error.clear();
+  return s;
+}
+
+int dms_cache_bytes(const dms_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(DMS_ERR_ARG, "bytes is NULL");
+  int s = validate(cfg);
+  if (s) return s;
+  Layout L;
+  compute_layout(*cfg, &L);
+  *bytes = L.total;
+  return DMS_OK;
+}
+
+int dms_max_pages_per_seq(const dms_config* cfg, int32_t* pages) {
+  if (!pages) return fail(DMS_ERR_ARG, "pages is NULL");
+  int s = validate(cfg);
+  if (s) return s;
+  *pages = (cfg->max_tokens_per_seq + cfg->block_size - 1) / cfg->block_size;
+  return DMS_OK;
+}
+
+int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* stream, dms_cache** out) {
+  if (!out) return fail(DMS_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  int s = validate(cfg);
+  if (s) return s;
+  if (!dev_buf) return fail(DMS_ERR_ARG, "device buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 256 != 0) return fail(DMS_ERR_ARG, "device buffer must be 256-byte aligned");
+  Layout L;
+  compute_layout(*cfg, &L);
+  if (bytes < L.total)
+    return fail(DMS_ERR_CAPACITY, "device buffer smaller than dms_cache_bytes (" + std::to_string(L.total) + ")");
+  auto* c = new dms_cache();
+  c->cfg = *cfg;
+  c->layout = L;
+  uint8_t* base = static_cast<uint8_t*>(dev_buf);
+  c->dev.k_pages = base + L.k_pages;
+  c->dev.v_pages = base + L.v_pages;
+  c->dev.scales = reinterpret_cast<float*>(base + L.scales);
+  c->dev.page_amax = reinterpret_cast<uint32_t*>(base + L.page_amax);
+  c->dev.slot_meta = reinterpret_cast<int32_t*>(base + L.slot_meta);
+  c->dev.page_table = reinterpret_cast<int32_t*>(base + L.page_table);
+  c->dev.lengths = reinterpret_cast<int32_t*>(base + L.lengths);
+  c->dev.ring = reinterpret_cast<int32_t*>(base + L.ring);
+  c->dev.pos = reinterpret_cast<int32_t*>(base + L.pos);
+  c->dev.free_stack = reinterpret_cast<int32_t*>(base + L.free_stack);
+  c->dev.ctl = reinterpret_cast<int32_t*>(base + L.ctl);
+  c->dev.chunk_slot = reinterpret_cast<int32_t*>(base + L.chunk_slot);
+  c->dev.chunk_info = reinterpret_cast<int32_t*>(base + L.chunk_info);
+  c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
+  c->dev.partials = reinterpret_cast<float*>(base + L.partials);
+  Geo& g = c->geo;
+  g.Bmax = cfg->max_batch;
+  g.Hq = cfg->num_q_heads;
+  g.Hkv = cfg->num_kv_heads;
+  g.D = cfg->head_dim;
+  g.g = cfg->num_q_heads / cfg->num_kv_heads;
+  g.H = cfg->hidden;
+  g.w = cfg->window;
+  g.P = cfg->block_size;
+  g.maxp = (cfg->max_tokens_per_seq + cfg->block_size - 1) / cfg->block_size;
+  g.pool = cfg->pool_pages;
+  g.max_tokens = cfg->max_tokens_per_seq;
+  g.max_chunk = cfg->max_chunk;
+  g.kv_dtype = cfg->kv_dtype;
+  const float sc = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg->head_dim));
+  g.scale_log2 = sc * 1.4426950408889634f;
+  int dev = 0;
+  if ((s = check_hip(hipGetDevice(&dev), "hipGetDevice"))) { delete c; return s; }
+  c->device = dev;
+  int cus = 256;
+  if ((s = check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                     "hipDeviceGetAttribute"))) { delete c; return s; }
+  c->num_cus = cus;
+  int grid = 2 * cus;
+  if (const char* e = std::getenv("DMS_DECODE_WGS")) grid = std::atoi(e);
+  c->decode_grid = std::max(1, std::min(grid, kMaxDecodeGrid));
+  const int units = cfg->max_batch * cfg->num_kv_heads;
+  hipLaunchKernelGGL(init_kernel, dim3(256), dim3(256), 0, as_stream(stream), c->dev, g, units);
+  if ((s = check_hip(hipGetLastError(), "init_kernel launch"))) { delete c; return s; }
+  *out = c;
+  return DMS_OK;
+}
+
+int dms_cache_destroy(dms_cache* cache) {
+  delete cache;
+  return DMS_OK;
+}
+
+int dms_cache_config(const dms_cache* cache, dms_config* cfg) {
+  if (!cache || !cfg) return fail(DMS_ERR_ARG, "NULL argument");
+  *cfg = cache->cfg;
+  return DMS_OK;
+}
+
+int dms_seq_reset(dms_cache* cache, const int32_t* seq_ids, int n, void* stream) {
+  if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
+  if (n < 0 || n > cache->geo.Bmax) return fail(DMS_ERR_ARG, "n must be in [0, max_batch]");
+  if (n == 0) return DMS_OK;
+  hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(1024), 0, as_stream(stream), cache->dev, cache->geo, seq_ids, n);
+  return check_hip(hipGetLastError(), "reset_kernel launch");
+}
+
+int dms_cache_status(dms_cache* cache, void* stream, int32_t* device_status) {
+  if (!cache || !device_status) return fail(DMS_ERR_ARG, "NULL argument");
+  int s = check_hip(hipMemcpyAsync(device_status, cache->dev.ctl + kCtlStatus, sizeof(int32_t),
+                                   hipMemcpyDeviceToHost, as_stream(stream)), "hipMemcpyAsync");
+  if (s) return s;
+  return check_hip(hipStreamSynchronize(as_stream(stream)), "hipStreamSynchronize");
+}
+
+int dms_cache_clear_status(dms_cache* cache, void* stream) {
+  if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
+  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(1), 0, as_stream(stream), cache->dev.ctl);
+  return check_hip(hipGetLastError(), "clear_status_kernel launch");
+}
+
+int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out) {
+  if (!cache || !out) return fail(DMS_ERR_ARG, "NULL argument");
+  const Geo& g = cache->geo;
+  const int64_t units = static_cast<int64_t>(g.Bmax) * g.Hkv;
+  const size_t elem = static_cast<size_t>(kv_elem_bytes(g.kv_dtype));
+  hipStream_t st = as_stream(stream);
+  struct Item { void* dst; const void* src; size_t bytes; };
+  const Item items[] = {
+      {out->lengths, cache->dev.lengths, units * sizeof(int32_t)},
+      {out->page_table, cache->dev.page_table, units * g.maxp * sizeof(int32_t)},
+      {out->slot_meta, cache->dev.slot_meta, static_cast<size_t>(g.pool) * g.P * sizeof(int32_t)},
+      {out->ring, cache->dev.ring, units * g.w * sizeof(int32_t)},
+      {out->positions, cache->dev.pos, static_cast<size_t>(g.Bmax) * sizeof(int32_t)},
+      {out->free_stack, cache->dev.free_stack, static_cast<size_t>(g.pool) * sizeof(int32_t)},
+      {out->free_count, cache->dev.ctl + kCtlFreeCount, sizeof(int32_t)},
+      {out->k_pages, cache->dev.k_pages, static_cast<size_t>(g.pool) * g.P * g.D * elem},
+      {out->v_pages, cache->dev.v_pages, static_cast<size_t>(g.pool) * g.P * g.D * elem},
+      {out->page_scales, cache->dev.scales, static_cast<size_t>(g.pool) * 2 * sizeof(float)},
+  };
+  for (const Item& it : items) {
+    if (!it.dst) continue;
+    int s = check_hip(hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+    if (s) return s;
+  }
+  return check_hip(hipStreamSynchronize(st), "hipStreamSynchronize");
+}
+
+int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out) {
+  if (!cache || !out) return fail(DMS_ERR_ARG, "NULL argument");
+  const Geo& g = cache->geo;
+  std::vector<int32_t> len(static_cast<size_t>(g.Bmax) * g.Hkv), pos(g.Bmax);
+  dms_dump d;
+  std::memset(&d, 0, sizeof(d));
+  d.lengths = len.data();
+  d.positions = pos.data();
+  int s = dms_cache_dump(cache, stream, &d);
+  if (s) return s;
+  int64_t tokens = 0, live = 0, pages = 0;
+  for (int b = 0; b < g.Bmax; ++b) tokens += static_cast<int64_t>(pos[b]) * g.Hkv;
+  for (int32_t L : len) {
+    live += L;
+    pages += (L + g.P - 1) / g.P;
+  }
+  const int64_t row_bytes = static_cast<int64_t>(g.D) * kv_elem_bytes(g.kv_dtype);
+  out->tokens = tokens;
+  out->live_slots = live;
+  out->pages_in_use = pages;
+  out->bytes_live = live * row_bytes * 2;
+  out->bytes_allocated = pages * g.P * row_bytes * 2;
+  out->cache_cr = live ? static_cast<double>(tokens) / static_cast<double>(live) : 0.0;
+  return DMS_OK;
+}
+
+}  // extern "C"

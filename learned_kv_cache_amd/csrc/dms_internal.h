@@ -1,0 +1,160 @@
+// Internal declarations of the DMS HIP library: the device layout of one
+// cache, launch helpers and small device utilities shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "dms.h"
+
+namespace dms {
+
+constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
+constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
+constexpr int kMaxDecodeGrid = 4096;   // workgroups of the decode attention kernel
+constexpr int kCtlWords = 64;
+constexpr int kCtlFreeCount = 0;
+constexpr int kCtlStatus = 1;
+
+// Device pointers carved out of the caller's buffer (see compute_layout).
+struct DevCache {
+  uint8_t* k_pages;      // [pool][P][D] kv dtype
+  uint8_t* v_pages;      // [pool][P][D]
+  float* scales;         // [pool][2] fp8 K/V scales
+  uint32_t* page_amax;   // [pool][2] fp8 amax of the opening call (float bits)
+  int32_t* slot_meta;    // [pool][P] position | evict << 31
+  int32_t* page_table;   // [Bmax][Hkv][maxp]
+  int32_t* lengths;      // [Bmax][Hkv]
+  int32_t* ring;         // [Bmax][Hkv][w] slot | evict << 31 of position p at p % w
+  int32_t* pos;          // [Bmax]
+  int32_t* free_stack;   // [pool]
+  int32_t* ctl;          // [kCtlWords]
+  int32_t* chunk_slot;   // [Bmax*Hkv][max_chunk] slot of each chunk token
+  int32_t* chunk_info;   // [Bmax*Hkv][8]
+  int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count
+  float* partials;       // decode split partials
+};
+
+// Geometry shared by every kernel of one cache.
+struct Geo {
+  int Bmax, Hq, Hkv, D, g, H, w, P, maxp, pool, max_tokens, max_chunk;
+  int kv_dtype;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct Layout {
+  size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, pos,
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, partials, total;
+  int64_t partial_records;
+};
+
+}  // namespace dms
+
+struct dms_cache {
+  dms_config cfg;
+  dms::Geo geo;
+  dms::DevCache dev;
+  dms::Layout layout;
+  int device;
+  int num_cus;
+  int decode_grid;
+};
+
+namespace dms {
+
+// Error reporting (thread-local message).
+int fail(int status, const std::string& msg);
+int check_hip(hipError_t e, const char* what);
+int kv_elem_bytes(int kv_dtype);
+int compute_layout(const dms_config& c, Layout* L);
+int decode_grid_for(const dms_cache* c);
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------------------
+// device utilities
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_act(const T* p, size_t i);
+template <> __device__ __forceinline__ float load_act<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_act<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+template <typename T> __device__ __forceinline__ void store_act(T* p, size_t i, float v);
+template <> __device__ __forceinline__ void store_act<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_act<uint16_t>(uint16_t* p, size_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+// e4m3fn ("OCP" fp8: bias 7, largest finite 448, no infinities).
+// Encode: |x| already clamped to <= 448; nearest value, ties to even code;
+// a result of magnitude zero is stored as +0.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    float qf = rintf(a * 512.0f);            // exact scaling, nearest-even integer 0..8
+    code = static_cast<uint32_t>(qf);        // 8 becomes the smallest normal (exp 1, man 0)
+  } else {
+    uint32_t au = __float_as_uint(a);
+    int e = static_cast<int>((au >> 23) & 0xFF) - 127;
+    uint32_t m = au & 0x7FFFFFu;
+    uint32_t keep = m >> 20;
+    uint32_t rem = m & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep++;
+    if (keep == 8u) { keep = 0; e++; }
+    code = (static_cast<uint32_t>(e + 7) << 3) | keep;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return static_cast<uint8_t>(code == 0 ? 0u : (code | sign));
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t sign = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t m = c & 0x7u;
+  float mag = (e == 0) ? static_cast<float>(m) * 0.001953125f
+                       : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float(__float_as_uint(mag) | sign);
+}
+
+// Power-of-two page scale: the smallest 2^e with amax <= 448 * 2^e, times 4.
+__device__ __forceinline__ float page_scale_from_amax(float amax) {
+  if (!(amax > 0.0f)) return ldexpf(1.0f, -98);
+  int k;
+  float m = frexpf(amax, &k);               // amax = m * 2^k, m in [0.5, 1)
+  int e = k - 9 + (m > 0.875f ? 1 : 0);
+  return ldexpf(1.0f, e + 2);
+}
+
+__device__ __forceinline__ void set_status(int32_t* ctl, int bits) {
+  atomicOr(reinterpret_cast<int*>(ctl + kCtlStatus), bits);
+}
+
+// Wave-wide (64 lanes) prefix count of a predicate: returns the number of set
+// lanes below this one; *total receives the wave's count.
+__device__ __forceinline__ int wave_rank(bool pred, int* total) {
+  uint64_t m = __ballot(pred);
+  int lane = threadIdx.x & 63;
+  uint64_t below = (lane == 0) ? 0ull : (m & ((~0ull) >> (64 - lane)));
+  *total = __popcll(m);
+  return __popcll(below);
+}
+
+}  // namespace dms

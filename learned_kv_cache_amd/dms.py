@@ -1,0 +1,285 @@
+"""ctypes binding of libdms (include/dms.h): argument marshalling only.
+
+Every function here checks shapes/dtypes/devices of torch tensors, turns them
+into raw pointers and calls the C ABI function of the same name.  All the
+work runs in the HIP kernels of libdms.so; there is no fallback.  PyTorch
+supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdms.so")
+_lib = None
+
+DMS_OK = 0
+DMS_ERR_ARG = -1
+DMS_ERR_CONFIG = -2
+DMS_ERR_CAPACITY = -3
+DMS_ERR_POOL = -4
+DMS_ERR_HIP = -5
+DMS_ERR_UNSUPPORTED = -6
+
+DMS_DEV_POOL_EXHAUSTED = 0x1
+DMS_DEV_CAPACITY = 0x2
+DMS_DEV_BAD_SEQ = 0x4
+
+DMS_F32, DMS_BF16, DMS_FP8_E4M3 = 0, 1, 2
+DMS_DECIDE_LINEAR, DMS_DECIDE_QNEURON = 0, 1
+DMS_ALPHA_PER_HEAD, DMS_ALPHA_PER_LAYER = 0, 1
+
+KV_DTYPES = {"f32": DMS_F32, "bf16": DMS_BF16, "fp8": DMS_FP8_E4M3}
+
+EXPORTS = (
+    "dms_config_validate", "dms_cache_bytes", "dms_max_pages_per_seq", "dms_cache_create",
+    "dms_cache_destroy", "dms_cache_config", "dms_decide", "dms_append_evict", "dms_decode_attn",
+    "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
+    "dms_cache_dump", "dms_cache_stats", "dms_last_error",
+)
+
+
+class DmsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class dms_config(ctypes.Structure):
+    _fields_ = [
+        ("max_batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("hidden", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("max_tokens_per_seq", ctypes.c_int32), ("pool_pages", ctypes.c_int32),
+        ("max_chunk", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("decide_mode", ctypes.c_int32),
+        ("alpha_per", ctypes.c_int32), ("disable_eviction", ctypes.c_int32), ("alpha_scale", ctypes.c_float),
+        ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class dms_dump(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "lengths", "page_table", "slot_meta", "ring", "positions", "free_stack", "free_count",
+        "k_pages", "v_pages", "page_scales")]
+
+
+class dms_stats(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("live_slots", ctypes.c_int64), ("pages_in_use", ctypes.c_int64),
+                ("bytes_live", ctypes.c_int64), ("bytes_allocated", ctypes.c_int64), ("cache_cr", ctypes.c_double)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Loads libdms.so (built by ``python -m learned_kv_cache_amd.build``); raises if missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m learned_kv_cache_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        cfgp = ctypes.POINTER(dms_config)
+        sig = {
+            "dms_config_validate": [cfgp],
+            "dms_cache_bytes": [cfgp, ctypes.POINTER(sz)],
+            "dms_max_pages_per_seq": [cfgp, ctypes.POINTER(ctypes.c_int32)],
+            "dms_cache_create": [cfgp, vp, sz, vp, ctypes.POINTER(vp)],
+            "dms_cache_destroy": [vp],
+            "dms_cache_config": [vp, cfgp],
+            "dms_decide": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp],
+            "dms_append_evict": [vp, vp, vp, vp, vp, i32, i32, vp],
+            "dms_decode_attn": [vp, vp, vp, vp, i32, vp],
+            "dms_prefill_attn": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
+            "dms_seq_reset": [vp, vp, i32, vp],
+            "dms_cache_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
+            "dms_cache_clear_status": [vp, vp],
+            "dms_cache_dump": [vp, vp, ctypes.POINTER(dms_dump)],
+            "dms_cache_stats": [vp, vp, ctypes.POINTER(dms_stats)],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.dms_last_error.argtypes = []
+        L.dms_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> int:
+    if status != DMS_OK:
+        raise DmsError(status, lib().dms_last_error().decode())
+    return status
+
+
+def make_config(*, max_batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, hidden: int,
+                window: int, block_size: int, max_tokens_per_seq: int, pool_pages: int, max_chunk: int,
+                kv_dtype: str = "bf16", decide_mode: str = "linear", alpha_per: str = "head",
+                disable_eviction: bool = False, alpha_scale: float = 100.0, rms_eps: float = 1e-6,
+                softmax_scale: float = 0.0) -> dms_config:
+    return dms_config(
+        max_batch, num_q_heads, num_kv_heads, head_dim, hidden, window, block_size, max_tokens_per_seq,
+        pool_pages, max_chunk, KV_DTYPES[kv_dtype], DMS_DECIDE_LINEAR if decide_mode == "linear" else DMS_DECIDE_QNEURON,
+        DMS_ALPHA_PER_HEAD if alpha_per == "head" else DMS_ALPHA_PER_LAYER, int(disable_eviction),
+        alpha_scale, rms_eps, softmax_scale)
+
+
+def dms_config_validate(cfg: dms_config) -> int:
+    return _check(lib().dms_config_validate(ctypes.byref(cfg)))
+
+
+def dms_cache_bytes(cfg: dms_config) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().dms_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def dms_max_pages_per_seq(cfg: dms_config) -> int:
+    n = ctypes.c_int32()
+    _check(lib().dms_max_pages_per_seq(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None, device=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+class DmsCache:
+    """One layer's cache: owns the device buffer (a torch uint8 tensor) and the handle."""
+
+    def __init__(self, cfg: dms_config, device: str = "cuda", stream=None):
+        self.cfg = cfg
+        nbytes = dms_cache_bytes(cfg)
+        self.buffer = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.buffer.data_ptr()
+        self._base = (base + 255) // 256 * 256
+        self.max_pages = dms_max_pages_per_seq(cfg)
+        h = ctypes.c_void_p()
+        _check(lib().dms_cache_create(ctypes.byref(cfg), self._base, nbytes, _stream(stream), ctypes.byref(h)))
+        self.handle = h
+        self.act_dtype = torch.float32 if cfg.kv_dtype == DMS_F32 else torch.bfloat16
+
+    def close(self):
+        if self.handle:
+            lib().dms_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dms_decide(cache: DmsCache, hidden, rms_gamma, W, bias, offsets, q_inout, B: int, T: int,
+               logits_out, evict_out, stream=None) -> int:
+    c = cache.cfg
+    ad = cache.act_dtype
+    if c.decide_mode == DMS_DECIDE_LINEAR:
+        hp = _ptr(hidden, "hidden", ad, B * T * c.hidden)
+        gp = _ptr(rms_gamma, "rms_gamma", torch.float32, c.hidden)
+        wp = _ptr(W, "W", torch.float32, c.num_kv_heads * c.hidden)
+        qp = None
+    else:
+        hp = gp = wp = None
+        qp = _ptr(q_inout, "q_inout", ad, B * T * c.num_q_heads * c.head_dim)
+    bp = _ptr(bias, "bias", torch.float32, c.num_kv_heads)
+    op = _ptr(offsets, "offsets", torch.float32, c.num_kv_heads)
+    lp = _ptr(logits_out, "logits_out", torch.float32, B * c.num_kv_heads * T)
+    ep = _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads * T)
+    return _check(lib().dms_decide(cache.handle, hp, gp, wp, bp, op, qp, B, T, lp, ep, _stream(stream)))
+
+
+def dms_append_evict(cache: DmsCache, seq_ids, k, v, evict, B: int, T: int, stream=None) -> int:
+    c = cache.cfg
+    n = B * T * c.num_kv_heads * c.head_dim
+    sp = _ptr(seq_ids, "seq_ids", torch.int32, B)
+    return _check(lib().dms_append_evict(
+        cache.handle, sp, _ptr(k, "k", cache.act_dtype, n), _ptr(v, "v", cache.act_dtype, n),
+        _ptr(evict, "evict", torch.uint8, B * c.num_kv_heads * T), B, T, _stream(stream)))
+
+
+def dms_decode_attn(cache: DmsCache, seq_ids, q, out, B: int, stream=None) -> int:
+    c = cache.cfg
+    n = B * c.num_q_heads * c.head_dim
+    return _check(lib().dms_decode_attn(
+        cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), _ptr(q, "q", cache.act_dtype, n),
+        _ptr(out, "out", cache.act_dtype, n), B, _stream(stream)))
+
+
+def dms_prefill_attn(cache: DmsCache, seq_ids, q, k, v, evict, out, B: int, C: int, stream=None) -> int:
+    c = cache.cfg
+    nq = B * C * c.num_q_heads * c.head_dim
+    nk = B * C * c.num_kv_heads * c.head_dim
+    return _check(lib().dms_prefill_attn(
+        cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), _ptr(q, "q", cache.act_dtype, nq),
+        _ptr(k, "k", cache.act_dtype, nk), _ptr(v, "v", cache.act_dtype, nk),
+        _ptr(evict, "evict", torch.uint8, B * c.num_kv_heads * C), _ptr(out, "out", cache.act_dtype, nq),
+        B, C, _stream(stream)))
+
+
+def dms_seq_reset(cache: DmsCache, seq_ids, n: int, stream=None) -> int:
+    return _check(lib().dms_seq_reset(cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, n), n, _stream(stream)))
+
+
+def dms_cache_status(cache: DmsCache, stream=None) -> int:
+    s = ctypes.c_int32()
+    _check(lib().dms_cache_status(cache.handle, _stream(stream), ctypes.byref(s)))
+    return s.value
+
+
+def dms_cache_clear_status(cache: DmsCache, stream=None) -> int:
+    return _check(lib().dms_cache_clear_status(cache.handle, _stream(stream)))
+
+
+def dms_cache_stats(cache: DmsCache, stream=None) -> dict:
+    st = dms_stats()
+    _check(lib().dms_cache_stats(cache.handle, _stream(stream), ctypes.byref(st)))
+    return {f: getattr(st, f) for f, _ in dms_stats._fields_}
+
+
+_KV_NP = {DMS_F32: np.float32, DMS_BF16: np.uint16, DMS_FP8_E4M3: np.uint8}
+
+
+def dms_cache_dump(cache: DmsCache, pages: bool = False, stream=None) -> dict:
+    """Host copies of the tables (numpy).  pages=True also copies K/V page bytes and scales."""
+    c = cache.cfg
+    units = c.max_batch * c.num_kv_heads
+    out = {
+        "lengths": np.zeros((c.max_batch, c.num_kv_heads), np.int32),
+        "page_table": np.zeros((c.max_batch, c.num_kv_heads, cache.max_pages), np.int32),
+        "slot_meta": np.zeros((c.pool_pages, c.block_size), np.int32),
+        "ring": np.zeros((c.max_batch, c.num_kv_heads, c.window), np.int32),
+        "positions": np.zeros(c.max_batch, np.int32),
+        "free_stack": np.zeros(c.pool_pages, np.int32),
+        "free_count": np.zeros(1, np.int32),
+    }
+    if pages:
+        et = _KV_NP[c.kv_dtype]
+        out["k_pages"] = np.zeros((c.pool_pages, c.block_size, c.head_dim), et)
+        out["v_pages"] = np.zeros((c.pool_pages, c.block_size, c.head_dim), et)
+        out["page_scales"] = np.zeros((c.pool_pages, 2), np.float32)
+    d = dms_dump(**{k: v.ctypes.data for k, v in out.items()})
+    _check(lib().dms_cache_dump(cache.handle, _stream(stream), ctypes.byref(d)))
+    assert units == out["lengths"].size
+    return out

@@ -157,62 +157,74 @@ def eviction_fractions(wl: Workload, gen: np.random.Generator) -> np.ndarray:
     return gen.uniform(lo, hi, size=wl.Hkv)
 
 
-@dataclasses.dataclass
 class Draw:
-    """All random inputs of one run (numpy float32 arrays holding the storage dtype's values).
+    """All random inputs of one run.
 
-    Per-token tensors are lists with one array per sequence, of length
-    ``ctx[b] + decode_steps`` (ragged when the contexts are).
+    Scalars and small tensors (p_h, ctx, W, gamma) are held; per-token tensors
+    (h, q, k, v) are regenerated on demand, one sequence at a time, from that
+    sequence's child seed, so a run with hundreds of thousands of tokens never
+    sits in memory whole.  Values are float32 holding the storage dtype's
+    values; per-token tensors of sequence b have ``ctx[b] + decode_steps`` rows.
+    Redraws (``set_rows``) are kept as overlays and applied on every access.
     """
 
-    wl: Workload
-    ctx: np.ndarray                  # [B] prompt lengths
-    p_h: np.ndarray                  # [Hkv] target eviction fractions
-    W: np.ndarray                    # [Hkv, hidden] float32 (linear adapter)
-    gamma: np.ndarray                # [hidden] float32 (RMSNorm weight)
-    h: Optional[List[np.ndarray]]    # B x [T_b, hidden]
-    q: List[np.ndarray]              # B x [T_b, Hq, D]
-    k: List[np.ndarray]              # B x [T_b, Hkv, D]
-    v: List[np.ndarray]              # B x [T_b, Hkv, D]
-    gens: Dict[str, np.random.Generator]
+    TAILS = ("h", "q", "k", "v")
+
+    def __init__(self, wl: Workload, run_id: int = 0):
+        self.wl = wl
+        ss = np.random.SeedSequence([1000 + wl.cfg_id, run_id])
+        kids = dict(zip(STREAMS, ss.spawn(len(STREAMS))))
+        self.gens = {name: np.random.Generator(np.random.PCG64(kids[name])) for name in STREAMS}
+        self.p_h = eviction_fractions(wl, self.gens["p_h"])
+        self.ctx = context_lengths(wl, self.gens["ctx"])
+        self.W = self.gens["W"].normal(0.0, wl.weight_std(), size=(wl.Hkv, wl.hidden)).astype(np.float32)
+        self.gamma = np.ones(wl.hidden, dtype=np.float32)
+        self._seeds = {name: kids[name].spawn(wl.B) for name in self.TAILS}
+        self._overlay: Dict[Tuple[str, int], Dict[int, np.ndarray]] = {}
+        self._cache: Dict[Tuple[str, int], np.ndarray] = {}
+        self._last: Dict[str, Tuple[int, np.ndarray]] = {}    # most recent sequence per tensor
 
     def T(self, b: int) -> int:
         return int(self.ctx[b]) + self.wl.decode_steps
 
+    def _tail(self, name: str):
+        wl = self.wl
+        return {"h": (wl.hidden,), "q": (wl.Hq, wl.D), "k": (wl.Hkv, wl.D), "v": (wl.Hkv, wl.D)}[name]
+
+    def tensor(self, name: str, b: int, keep: bool = False) -> np.ndarray:
+        """Per-token tensor ``name`` of sequence b: [T_b, ...] float32."""
+        key = (name, b)
+        if key in self._cache:
+            return self._cache[key]
+        last = self._last.get(name)
+        if last is not None and last[0] == b:
+            return last[1]
+        gen = np.random.Generator(np.random.PCG64(self._seeds[name][b]))
+        x = normal(gen, (self.T(b),) + self._tail(name), self.wl.act_dtype)
+        for t, row in self._overlay.get(key, {}).items():
+            x[t] = row
+        if keep:
+            self._cache[key] = x
+        else:
+            self._last[name] = (b, x)
+        return x
+
+    def set_rows(self, name: str, b: int, rows: Dict[int, np.ndarray]) -> None:
+        """Record redrawn rows (position -> values) of ``name`` for sequence b."""
+        self._overlay.setdefault((name, b), {}).update(rows)
+        self._cache.pop((name, b), None)
+        if self._last.get(name, (None,))[0] == b:
+            del self._last[name]
+
     def stacked(self, name: str) -> np.ndarray:
-        """[B, T, ...] view of a per-token tensor (all sequences equally long)."""
-        xs = getattr(self, name)
-        return np.stack(xs, axis=0)
+        """[B, T, ...] of a per-token tensor (all sequences equally long)."""
+        return np.stack([self.tensor(name, b) for b in range(self.wl.B)], axis=0)
 
 
-def draw(wl: Workload, run_id: int = 0, with_hidden: Optional[bool] = None) -> Draw:
-    """Draw every random input of a run, stream by stream, in a fixed order.
-
-    p_h, W and contexts come from their own streams.  Each per-token tensor
-    stream (h, q, k, v) is spawned into one child per sequence.
-    """
-    ss = np.random.SeedSequence([1000 + wl.cfg_id, run_id])
-    kids = dict(zip(STREAMS, ss.spawn(len(STREAMS))))
-    gens = {name: np.random.Generator(np.random.PCG64(kids[name])) for name in STREAMS}
-    p_h = eviction_fractions(wl, gens["p_h"])
-    ctx = context_lengths(wl, gens["ctx"])
-    if with_hidden is None:
-        with_hidden = wl.decide == "linear"
-    W = gens["W"].normal(0.0, wl.weight_std(), size=(wl.Hkv, wl.hidden)).astype(np.float32)
-    gamma = np.ones(wl.hidden, dtype=np.float32)
-
-    def per_seq(name, tail):
-        out = []
-        for b, child in enumerate(kids[name].spawn(wl.B)):
-            gen = np.random.Generator(np.random.PCG64(child))
-            out.append(normal(gen, (int(ctx[b]) + wl.decode_steps,) + tail, wl.act_dtype))
-        return out
-
-    h = per_seq("h", (wl.hidden,)) if with_hidden else None
-    q = per_seq("q", (wl.Hq, wl.D))
-    k = per_seq("k", (wl.Hkv, wl.D))
-    v = per_seq("v", (wl.Hkv, wl.D))
-    return Draw(wl=wl, ctx=ctx, p_h=p_h, W=W, gamma=gamma, h=h, q=q, k=k, v=v, gens=gens)
+def draw(wl: Workload, run_id: int = 0) -> Draw:
+    """Inputs of one run: p_h, W and contexts from their own streams; each
+    per-token stream (h, q, k, v) spawned into one child per sequence."""
+    return Draw(wl, run_id)
 
 
 # ---------------------------------------------------------------------------
@@ -235,18 +247,7 @@ def offset_for_fraction(pre_offset_logits: np.ndarray, p: float) -> float:
     return float(0.5 * (u[kept - 1] + u[kept]))
 
 
-def redraw_rows(x: np.ndarray, rows: np.ndarray, gen: np.random.Generator, dtype: str) -> int:
-    """Redraw x[rows] (boolean mask over the leading axes) from N(0,1) in place."""
-    idx = np.argwhere(rows)
-    for ix in idx:
-        sl = tuple(int(i) for i in ix)
-        x[sl] = normal(gen, x[sl].shape, dtype)
-    return len(idx)
-
-
-def redraw_elements(x: np.ndarray, mask: np.ndarray, gen: np.random.Generator, dtype: str) -> int:
-    """Redraw the elements of x selected by a boolean mask of x's shape, in place."""
-    n = int(mask.sum())
-    if n:
-        x[mask] = normal(gen, (n,), dtype)
-    return n
+def redraw(gen: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """Fresh N(0,1) values from the resample stream (for rows that sit too close
+    to the decision threshold)."""
+    return normal(gen, shape, dtype)

@@ -458,8 +458,12 @@ def effective_kv(sim: CacheSim, b: int, kh: int, x: np.ndarray, which: int) -> n
     x = np.asarray(x, dtype=np.float64)
     if not sim.fp8:
         return x
+    sc = np.array([s[which] if s is not None else np.nan for s in sim.tok_scale[b][kh][: x.shape[0]]])
+    if len(sc) < x.shape[0]:
+        sc = np.concatenate([sc, np.full(x.shape[0] - len(sc), np.nan)])
+    written = ~np.isnan(sc)
     out = x.copy()
-    for t, sc in enumerate(sim.tok_scale[b][kh][: x.shape[0]]):
-        if sc is not None:
-            out[t] = fp8_roundtrip(x[t], sc[which])
+    if written.any():
+        s = sc[written][:, None]
+        out[written] = e4m3_decode(e4m3_encode(x[written] / s)) * s
     return out

@@ -1,0 +1,354 @@
+"""Test harness: prepares seeded workloads with the oracle and drives the HIP
+path and the oracle side by side.
+
+Offsets per head come from the oracle's pre-offset logits pooled over the
+whole run (midpoint of the order statistics around the (1-p) quantile), and
+every token whose logit lies within 1e-2 of the threshold is redrawn from the
+resample stream, so no decision depends on rounding.  No input or expected
+value comes from the HIP path.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+import time
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+import oracle
+from learned_kv_cache_amd import synth
+
+MARGIN = 1e-2
+EPS = 1e-6
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class Prepared:
+    wl: synth.Workload
+    draw: synth.Draw
+    offsets: np.ndarray            # [Hkv] float32 values
+    logits: List[np.ndarray]       # per sequence [Hkv, T_b] float64 (after granularity)
+    evict: List[np.ndarray]        # per sequence [Hkv, T_b] uint8
+
+
+def _pre_offset_linear(d: synth.Draw, b: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    wl = d.wl
+    h = d.tensor("h", b)
+    if rows is not None:
+        h = h[rows]
+    lg, _ = oracle.decide_linear(h[None], d.gamma, d.W, np.zeros(wl.Hkv), alpha_scale=wl.alpha_scale, eps=EPS)
+    return lg[0]                                      # [Hkv, T]
+
+
+def _pre_offset_qneuron(d: synth.Draw, b: int) -> np.ndarray:
+    wl = d.wl
+    q = d.tensor("q", b)
+    return wl.alpha_scale * q[:, :: wl.g, -1].astype(np.float64).T   # [Hkv, T]
+
+
+def prepare(wl: synth.Workload, run_id: int = 0, max_rounds: int = 50) -> Prepared:
+    d = synth.draw(wl, run_id)
+    B, Hkv = wl.B, wl.Hkv
+    pre = _pre_offset_linear if wl.decide == "linear" else _pre_offset_qneuron
+    u = [pre(d, b) for b in range(B)]
+    if wl.fixed_offset is not None:
+        off = np.full(Hkv, wl.fixed_offset)
+    else:
+        off = np.array([synth.offset_for_fraction(np.concatenate([u[b][k] for b in range(B)]), d.p_h[k])
+                        for k in range(Hkv)])
+    off = off.astype(np.float32).astype(np.float64)   # the HIP path receives float32 offsets
+    for b in range(B):
+        for _ in range(max_rounds):
+            bad_t = np.flatnonzero(np.any(np.abs(u[b] - off[:, None]) < MARGIN, axis=0))
+            if bad_t.size == 0:
+                break
+            gen = d.gens["resample"]
+            if wl.decide == "linear":
+                rows = {int(t): synth.redraw(gen, (wl.hidden,), wl.act_dtype) for t in bad_t}
+                d.set_rows("h", b, rows)
+                u[b][:, bad_t] = _pre_offset_linear(d, b, bad_t)
+            else:
+                q = d.tensor("q", b)
+                rows = {}
+                for t in bad_t:
+                    r = q[t].copy()
+                    for k in range(Hkv):
+                        if abs(wl.alpha_scale * float(r[k * wl.g, -1]) - off[k]) < MARGIN:
+                            r[k * wl.g, -1] = synth.redraw(gen, (), wl.act_dtype)
+                    rows[int(t)] = r
+                d.set_rows("q", b, rows)
+                u[b] = _pre_offset_qneuron(d, b)
+        else:
+            raise RuntimeError("margin redraw did not converge")
+    logits, evict = [], []
+    for b in range(B):
+        lg = u[b] - off[:, None]
+        if wl.alpha_per == "layer":
+            lg = np.repeat(lg[:1], Hkv, axis=0)
+        e = (lg > 0).astype(np.uint8)
+        if wl.disable_eviction:
+            e[...] = 0
+        logits.append(lg)
+        evict.append(e)
+    return Prepared(wl=wl, draw=d, offsets=off.astype(np.float32), logits=logits, evict=evict)
+
+
+# ---------------------------------------------------------------------------
+# device side (imported lazily so CPU-only collection never loads torch.cuda)
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    torch = _torch()
+    if dtype == "bf16":
+        bits = synth.bf16_bits(np.ascontiguousarray(x, np.float32))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    if dtype == "u8":
+        return torch.from_numpy(np.ascontiguousarray(x, np.uint8)).cuda()
+    if dtype == "i32":
+        return torch.from_numpy(np.ascontiguousarray(x, np.int32)).cuda()
+    raise ValueError(dtype)
+
+
+def from_dev(t) -> np.ndarray:
+    torch = _torch()
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def tolerance(wl: synth.Workload):
+    """(max abs, mean abs) error bounds of attention outputs against the float64 oracle."""
+    if wl.act_dtype == "f32":
+        return 1e-4, 1e-5
+    return 2e-2, 2e-3
+
+
+class Runner:
+    """One layer's cache on the GPU plus the oracle's model of it."""
+
+    def __init__(self, prep: Prepared, pool_pages: Optional[int] = None, max_chunk: Optional[int] = None):
+        torch = _torch()
+        from learned_kv_cache_amd import dms
+        self.dms = dms
+        self.prep = prep
+        wl = self.wl = prep.wl
+        self.max_tokens = int(max(prep.draw.T(b) for b in range(wl.B)))
+        if pool_pages is None:
+            pool_pages = sum(wl.Hkv * (-(-prep.draw.T(b) // wl.block)) for b in range(wl.B))
+        self.cfg = dms.make_config(
+            max_batch=wl.B, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
+            window=wl.window, block_size=wl.block, max_tokens_per_seq=self.max_tokens, pool_pages=pool_pages,
+            max_chunk=max_chunk or wl.chunk, kv_dtype=wl.kv_dtype, decide_mode=wl.decide,
+            alpha_per=wl.alpha_per, disable_eviction=wl.disable_eviction, alpha_scale=wl.alpha_scale,
+            rms_eps=EPS)
+        self.cache = dms.DmsCache(self.cfg)
+        self.sim = oracle.CacheSim(wl.B, wl.Hkv, wl.window, wl.block, self.max_tokens, pool_pages,
+                                   fp8=wl.kv_dtype == "fp8")
+        self.W = to_dev(prep.draw.W, "f32")
+        self.gamma = to_dev(prep.draw.gamma, "f32")
+        self.off = to_dev(prep.offsets, "f32")
+        self.scale = 1.0 / np.sqrt(wl.D)
+        self._dec: Dict = {}                                  # cached decode rows per (tensor, sequence)
+        self.torch = torch
+
+    # -- decisions ----------------------------------------------------------
+    def row(self, name: str, b: int, t: int) -> np.ndarray:
+        """Row t of a per-token tensor; decode rows of every sequence are cached."""
+        d = self.prep.draw
+        c0 = int(d.ctx[b])
+        if t < c0:
+            return d.tensor(name, b)[t]
+        key = (name, b)
+        if key not in self._dec:
+            self._dec[key] = d.tensor(name, b)[c0:].copy()
+        return self._dec[key][t - c0]
+
+    def decide(self, seqs: Sequence[int], s: int, C: int, q_dev=None):
+        """GPU decision for positions [s, s+C) of the listed sequences; checks
+        flags (bit-exact) and logits against the oracle.  Returns evict (device)."""
+        torch, dms, wl, d = self.torch, self.dms, self.wl, self.prep.draw
+        B = len(seqs)
+        logits = torch.empty(B * wl.Hkv * C, dtype=torch.float32, device="cuda")
+        evict = torch.empty(B * wl.Hkv * C, dtype=torch.uint8, device="cuda")
+        if wl.decide == "linear":
+            if C == 1:
+                h = to_dev(np.stack([self.row("h", b, s) for b in seqs])[:, None], wl.act_dtype)
+            else:
+                h = to_dev(np.stack([d.tensor("h", b)[s:s + C] for b in seqs]), wl.act_dtype)
+            dms.dms_decide(self.cache, h, self.gamma, self.W, None, self.off, None, B, C, logits, evict)
+        else:
+            dms.dms_decide(self.cache, None, None, None, None, self.off, q_dev, B, C, logits, evict)
+        ref_e = np.stack([self.prep.evict[b][:, s:s + C] for b in seqs])
+        ref_l = np.stack([self.prep.logits[b][:, s:s + C] for b in seqs])
+        got_e = evict.cpu().numpy().reshape(B, wl.Hkv, C)
+        got_l = logits.cpu().numpy().reshape(B, wl.Hkv, C)
+        assert np.array_equal(got_e, ref_e), f"decisions differ at {np.argwhere(got_e != ref_e)[:5]}"
+        np.testing.assert_allclose(got_l, ref_l, atol=5e-3, rtol=0)
+        return evict
+
+    def q_rows(self, seqs, s, C):
+        """Queries of positions [s, s+C) as the attention sees them (neuron zeroed for
+        query-neuron decisions), [B, C, Hq, D] float32."""
+        wl, d = self.wl, self.prep.draw
+        q = np.stack([d.tensor("q", b)[s:s + C] for b in seqs]).copy()
+        if wl.decide == "qneuron":
+            q[:, :, :: wl.g, -1] = 0.0
+        return q
+
+    # -- oracle attention ------------------------------------------------------
+    def kv_view(self, b: int, upto: int, raw_from: Optional[int] = None):
+        """K, V [upto, Hkv, D] as attention reads them: fp8-rounded where stored
+        (positions < raw_from), raw from raw_from on."""
+        d = self.prep.draw
+        K = d.tensor("k", b, keep=True)[:upto].astype(np.float64)
+        V = d.tensor("v", b, keep=True)[:upto].astype(np.float64)
+        if self.sim.fp8:
+            lim = upto if raw_from is None else raw_from
+            for kh in range(self.wl.Hkv):
+                K[:lim, kh] = oracle.effective_kv(self.sim, b, kh, K[:lim, kh], 0)
+                V[:lim, kh] = oracle.effective_kv(self.sim, b, kh, V[:lim, kh], 1)
+        return K, V
+
+    def oracle_rows(self, b: int, q_rows: np.ndarray, rows: np.ndarray, raw_from: Optional[int] = None):
+        upto = int(rows.max()) + 1
+        K, V = self.kv_view(b, upto, raw_from)
+        e = self.prep.evict[b][:, :upto]
+        return oracle.attention_rows(q_rows, K, V, e, self.wl.window, rows, self.scale)
+
+    # -- steps -------------------------------------------------------------------
+    def prefill_chunk(self, seqs: Sequence[int], s: int, C: int, check_rows: Optional[int] = None,
+                      attend: bool = True, rng: Optional[np.random.Generator] = None):
+        """decide -> prefill attention -> append for positions [s, s+C)."""
+        torch, dms, wl, d = self.torch, self.dms, self.wl, self.prep.draw
+        B = len(seqs)
+        seq_dev = to_dev(np.asarray(seqs, np.int32), "i32")
+        q_raw = np.stack([d.tensor("q", b)[s:s + C] for b in seqs])
+        q_dev = to_dev(q_raw, wl.act_dtype)
+        evict = self.decide(seqs, s, C, q_dev=q_dev)
+        k_np = np.stack([d.tensor("k", b)[s:s + C] for b in seqs])
+        v_np = np.stack([d.tensor("v", b)[s:s + C] for b in seqs])
+        k_dev, v_dev = to_dev(k_np, wl.act_dtype), to_dev(v_np, wl.act_dtype)
+        stats = None
+        if attend:
+            out = torch.empty_like(q_dev)
+            dms.dms_prefill_attn(self.cache, seq_dev, q_dev, k_dev, v_dev, evict, out, B, C)
+            if check_rows is not None:
+                got = from_dev(out).reshape(B, C, wl.Hq, wl.D)
+                qz = self.q_rows(seqs, s, C)
+                errs = []
+                for i, b in enumerate(seqs):
+                    if check_rows >= C:
+                        loc = np.arange(C)
+                    else:
+                        rng = rng or np.random.default_rng(s)
+                        loc = np.unique(np.concatenate([rng.choice(C, check_rows - 8, replace=False),
+                                                        np.arange(C - 8, C)]))
+                    ref = self.oracle_rows(b, qz[i, loc], s + loc, raw_from=s)
+                    errs.append(np.abs(got[i, loc] - ref))
+                err = np.concatenate([e.ravel() for e in errs])
+                stats = (float(err.max()), float(err.mean()))
+                mx, mn = tolerance(wl)
+                assert stats[0] <= mx and stats[1] <= mn, f"prefill attention error {stats}"
+        dms.dms_append_evict(self.cache, seq_dev, k_dev, v_dev, evict, B, C)
+        e_np = np.stack([self.prep.evict[b][:, s:s + C] for b in seqs])
+        self.sim.append(list(seqs), e_np, k_np, v_np)
+        return stats
+
+    def decode_step(self, seqs: Sequence[int], positions: Sequence[int], check: bool = True):
+        """decide -> append -> decode attention for one token per listed sequence."""
+        torch, dms, wl, d = self.torch, self.dms, self.wl, self.prep.draw
+        B = len(seqs)
+        seq_dev = to_dev(np.asarray(seqs, np.int32), "i32")
+        q_np = np.stack([self.row("q", b, t) for b, t in zip(seqs, positions)])
+        q_dev = to_dev(q_np[:, None], wl.act_dtype)
+        # decide works per (row, T=1); rows may sit at different positions
+        if len(set(positions)) == 1:
+            evict = self.decide(seqs, positions[0], 1, q_dev=q_dev)
+        else:
+            evs = []
+            for i, (b, t) in enumerate(zip(seqs, positions)):
+                evs.append(self.decide([b], t, 1, q_dev=q_dev[i:i + 1]))
+            evict = torch.cat(evs)
+        k_np = np.stack([self.row("k", b, t) for b, t in zip(seqs, positions)])[:, None]
+        v_np = np.stack([self.row("v", b, t) for b, t in zip(seqs, positions)])[:, None]
+        k_dev, v_dev = to_dev(k_np, wl.act_dtype), to_dev(v_np, wl.act_dtype)
+        dms.dms_append_evict(self.cache, seq_dev, k_dev, v_dev, evict, B, 1)
+        e_np = np.stack([self.prep.evict[b][:, t:t + 1] for b, t in zip(seqs, positions)])
+        self.sim.append(list(seqs), e_np, k_np, v_np)
+        out = torch.empty(B * wl.Hq * wl.D, dtype=q_dev.dtype, device="cuda")
+        dms.dms_decode_attn(self.cache, seq_dev, q_dev.view(-1), out, B)
+        if not check:
+            return None
+        got = from_dev(out).reshape(B, wl.Hq, wl.D)
+        errs = []
+        for i, (b, t) in enumerate(zip(seqs, positions)):
+            qz = q_np[i].astype(np.float64).copy()
+            if wl.decide == "qneuron":
+                qz[:: wl.g, -1] = 0.0
+            ref = self.oracle_rows(b, qz[None], np.array([t]))[0]
+            errs.append(np.abs(got[i] - ref))
+        err = np.stack(errs)
+        stats = (float(err.max()), float(err.mean()))
+        mx, mn = tolerance(wl)
+        assert stats[0] <= mx and stats[1] <= mn, f"decode attention error {stats} at positions {positions[:4]}"
+        return stats
+
+    # -- tables ------------------------------------------------------------------
+    def check_tables(self, pages: bool = False):
+        """Lengths, page tables, slot metadata, ring, positions and the free stack
+        must equal the oracle's sequential model bit for bit."""
+        wl, sim = self.wl, self.sim
+        dump = self.dms.dms_cache_dump(self.cache, pages=pages)
+        assert np.array_equal(dump["positions"], np.asarray(sim.pos, np.int32))
+        assert np.array_equal(dump["lengths"], np.asarray(sim.L, np.int32))
+        assert int(dump["free_count"][0]) == len(sim.free)
+        n = len(sim.free)
+        assert np.array_equal(dump["free_stack"][:n], np.asarray(sim.free, np.int32))
+        P = wl.block
+        for b in range(wl.B):
+            for kh in range(wl.Hkv):
+                pages_ref = sim.pages[b][kh]
+                pt = dump["page_table"][b, kh]
+                assert list(pt[: len(pages_ref)]) == pages_ref, (b, kh)
+                assert (pt[len(pages_ref):] == -1).all()
+                L = sim.L[b][kh]
+                meta_ref = sim.slot_meta(b, kh)
+                slots = np.arange(L)
+                got_meta = dump["slot_meta"][np.asarray(pages_ref)[slots // P], slots % P] if L else np.zeros(0)
+                assert np.array_equal(got_meta.astype(np.int64) & 0xFFFFFFFF, meta_ref & 0xFFFFFFFF), (b, kh)
+                ring = sim.ring(b, kh)
+                for t, (slot, e) in ring.items():
+                    val = int(dump["ring"][b, kh, t % wl.window]) & 0xFFFFFFFF
+                    assert val == (slot | (e << 31)), (b, kh, t)
+                if pages and L:
+                    self._check_page_values(dump, b, kh, pages_ref, L)
+        return dump
+
+    def _check_page_values(self, dump, b, kh, pages_ref, L):
+        wl, sim, d = self.wl, self.sim, self.prep.draw
+        P = wl.block
+        occ = sim.slot_table(b, kh)
+        slots = np.arange(L)
+        pg = np.asarray(pages_ref)[slots // P]
+        for name, which in (("k", 0), ("v", 1)):
+            x = d.tensor(name, b)[occ, kh]                 # [L, D] raw values of the occupants
+            stored = dump[f"{name}_pages"][pg, slots % P]
+            if wl.kv_dtype == "f32":
+                assert np.array_equal(stored, x.astype(np.float32))
+            elif wl.kv_dtype == "bf16":
+                assert np.array_equal(stored, synth.bf16_bits(x))
+            else:
+                sc = np.array([sim.tok_scale[b][kh][t][which] for t in occ])
+                assert np.array_equal(dump["page_scales"][pg, which].astype(np.float64), sc)
+                codes = oracle.e4m3_encode(x.astype(np.float64) / sc[:, None])
+                assert np.array_equal(stored, codes)

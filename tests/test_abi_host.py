@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI (no GPU work): exports, configuration checks,
+buffer sizing, and that the binding refuses to run without the library."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from learned_kv_cache_amd import dms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dms.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(dms_\w+)\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 15
+    L = ctypes.CDLL(dms.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(dms.EXPORTS)
+
+
+def base(**kw):
+    c = dict(max_batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, hidden=256, window=16, block_size=8,
+             max_tokens_per_seq=100, pool_pages=32, max_chunk=64)
+    c.update(kw)
+    return dms.make_config(**c)
+
+
+def test_valid_config_and_sizes():
+    cfg = base()
+    assert dms.dms_config_validate(cfg) == 0
+    assert dms.dms_max_pages_per_seq(cfg) == 13
+    n1 = dms.dms_cache_bytes(cfg)
+    n2 = dms.dms_cache_bytes(base(pool_pages=64))
+    # doubling the pool adds K+V pages (bf16) plus metadata
+    assert n2 - n1 >= 32 * 8 * 64 * 2 * 2
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(block_size=0), "block_size"),
+    (dict(window=8), "window must be greater"),
+    (dict(window=7), "window must be greater"),
+    (dict(num_q_heads=6, num_kv_heads=4), "multiple"),
+    (dict(num_q_heads=24, num_kv_heads=2), "group size"),
+    (dict(head_dim=96), "head_dim"),
+    (dict(hidden=130), "hidden"),
+    (dict(max_chunk=10000), "max_chunk"),
+    (dict(max_batch=0), "positive"),
+    (dict(max_batch=300, num_kv_heads=8, num_q_heads=32), "2048"),
+])
+def test_invalid_configs_are_rejected(kw, msg):
+    with pytest.raises(dms.DmsError) as ei:
+        dms.dms_config_validate(base(**kw))
+    assert ei.value.status == dms.DMS_ERR_CONFIG
+    assert msg in str(ei.value)
+
+
+def test_bad_enums_are_rejected():
+    cfg = base()
+    cfg.kv_dtype = 7
+    with pytest.raises(dms.DmsError):
+        dms.dms_config_validate(cfg)
+    cfg = base()
+    cfg.alpha_per = 2
+    with pytest.raises(dms.DmsError):
+        dms.dms_config_validate(cfg)
+
+
+def test_null_arguments_fail_before_any_launch():
+    L = dms.lib()
+    assert L.dms_cache_bytes(None, None) == dms.DMS_ERR_ARG
+    assert L.dms_decide(None, None, None, None, None, None, None, 1, 1, None, None, None) == dms.DMS_ERR_ARG
+    assert L.dms_append_evict(None, None, None, None, None, 1, 1, None) == dms.DMS_ERR_ARG
+    assert L.dms_decode_attn(None, None, None, None, 1, None) == dms.DMS_ERR_ARG
+    assert L.dms_prefill_attn(None, None, None, None, None, None, None, 1, 1, None) == dms.DMS_ERR_ARG
+    assert L.dms_seq_reset(None, None, 1, None) == dms.DMS_ERR_ARG
+    cfg = base()
+    out = ctypes.c_void_p()
+    assert L.dms_cache_create(ctypes.byref(cfg), None, 0, None, ctypes.byref(out)) == dms.DMS_ERR_ARG
+    assert L.dms_cache_create(ctypes.byref(cfg), ctypes.c_void_p(256), 16, None, ctypes.byref(out)) == \
+        dms.DMS_ERR_CAPACITY
+    assert b"smaller" in L.dms_last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(dms, "_lib", None)
+    monkeypatch.setattr(dms, "_LIB_PATH", os.path.join(ROOT, "no_such_lib.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        dms.lib()
