@@ -1,0 +1,430 @@
+#!/usr/bin/env python3
+"""Decode throughput of the DMS hot path on one MI355X.
+
+Workload: Qwen3-8B-shaped attention layer (hidden 4096, 32 query / 8 KV heads,
+head_dim 128, bf16), B = 8 sequences with an 8192-token prompt, window 512,
+block 256, per-head eviction fractions drawn from U[0.85, 0.92].  The cache of
+every one of 36 layers (Qwen3-8B depth) is built separately, so one decode
+step streams ~1.7 GB of live K/V, far more than the 256 MB Infinity Cache.
+
+A step is one decode token for every sequence through all 36 layers: per layer
+dms_decide (RMSNorm + linear adapter + threshold) -> dms_append_evict
+(delayed eviction, in-place slot reuse) -> dms_decode_attn.  Steps are
+captured as HIP graphs and replayed; inputs (hidden states, Q, K, V of every
+step) are resident in HBM before the timed region.
+
+Output: one JSON line (metric, value = decode tokens/s per layer, roofline of
+the decode-attention kernel, CPU-oracle baseline, prefill figures).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DMS decode tok/s/layer + HBM GB/s vs peak, Qwen3-8B layer shape, ctx 8K, B=8"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode_attn.hip", "dms_internal.h"):
+        with open(os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kind: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/*.json), if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+
+class Layer:
+    def __init__(self, idx, cfg, wl, dms, torch, gen, steps_total):
+        self.idx = idx
+        B, H, Hq, Hkv, D = wl.B, wl.hidden, wl.Hq, wl.Hkv, wl.D
+        self.cache = dms.DmsCache(cfg)
+        self.W = (torch.randn(Hkv, H, generator=gen, device="cuda") / math.sqrt(H)).contiguous()
+        self.gamma = torch.ones(H, device="cuda")
+        self.p_h = 0.85 + 0.07 * torch.rand(Hkv, generator=gen, device="cuda")
+        self.seed = 1_000_003 * (idx + 1)
+        S = steps_total
+        self.h_dec = torch.randn(S, B, H, generator=gen, device="cuda").to(torch.bfloat16)
+        self.q_dec = torch.randn(S, B, Hq, D, generator=gen, device="cuda").to(torch.bfloat16)
+        self.k_dec = torch.randn(S, B, Hkv, D, generator=gen, device="cuda").to(torch.bfloat16)
+        self.v_dec = torch.randn(S, B, Hkv, D, generator=gen, device="cuda").to(torch.bfloat16)
+        self.evict = torch.empty(B * Hkv, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
+        self.off = torch.zeros(Hkv, device="cuda")
+
+
+def prompt_chunk(layer, c, wl, torch):
+    """Hidden states, K and V of prompt chunk c (regenerated from its own seed)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(layer.seed + 17 * c)
+    h = torch.randn(wl.B, wl.chunk, wl.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(wl.B, wl.chunk, wl.Hkv, wl.D, generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn(wl.B, wl.chunk, wl.Hkv, wl.D, generator=g, device="cuda").to(torch.bfloat16)
+    return h, k, v
+
+
+def calibrate_and_fill(layer, wl, dms, torch):
+    """Per-head offsets so that a fraction p_h of the run's tokens is evicted
+    (midpoint of the order statistics around the (1-p) quantile of the
+    pre-offset logits), then the 8192-token prompt goes in through
+    dms_decide + dms_append_evict in chunks of 4096."""
+    B, Hkv, C = wl.B, wl.Hkv, wl.chunk
+    n_chunks = wl.prefill // C
+    zero = torch.zeros(Hkv, device="cuda")
+    logits = []
+    ev = torch.empty(B * Hkv * C, dtype=torch.uint8, device="cuda")
+    for c in range(n_chunks):
+        h, _, _ = prompt_chunk(layer, c, wl, torch)
+        lg = torch.empty(B, Hkv, C, device="cuda")
+        dms.dms_decide(layer.cache, h, layer.gamma, layer.W, None, zero, None, B, C, lg, ev)
+        logits.append(lg.permute(1, 0, 2).reshape(Hkv, -1))
+    S = layer.h_dec.shape[0]
+    lg = torch.empty(S * B, Hkv, 1, device="cuda")
+    evd = torch.empty(S * B * Hkv, dtype=torch.uint8, device="cuda")
+    dms.dms_decide(layer.cache, layer.h_dec, layer.gamma, layer.W, None, zero, None, S * B, 1, lg, evd)
+    logits.append(lg.permute(1, 0, 2).reshape(Hkv, -1))
+    allv = torch.cat(logits, dim=1)
+    srt, _ = torch.sort(allv, dim=1)
+    n = srt.shape[1]
+    kept = torch.round((1.0 - layer.p_h) * n).long().clamp(1, n - 1)
+    lo = srt.gather(1, (kept - 1)[:, None])[:, 0]
+    hi = srt.gather(1, kept[:, None])[:, 0]
+    layer.off.copy_(0.5 * (lo + hi))
+    for c in range(n_chunks):
+        h, k, v = prompt_chunk(layer, c, wl, torch)
+        dms.dms_decide(layer.cache, h, layer.gamma, layer.W, None, layer.off, None, B, C, None, ev)
+        dms.dms_append_evict(layer.cache, None, k, v, ev, B, C)
+
+
+def decode_step(layers, s, wl, dms):
+    B = wl.B
+    for L in layers:
+        dms.dms_decide(L.cache, L.h_dec[s], L.gamma, L.W, None, L.off, None, B, 1, None, L.evict)
+        dms.dms_append_evict(L.cache, None, L.k_dec[s], L.v_dec[s], L.evict, B, 1)
+        dms.dms_decode_attn(L.cache, None, L.q_dec[s], L.out, B)
+
+
+# ---------------------------------------------------------------------------
+
+
+def run_decode(args, dms, synth, torch):
+    wl = synth.QWEN8B_DECODE
+    S = args.warmup + args.steps
+    max_tokens = wl.prefill + S
+    pool_pages = wl.B * wl.Hkv * math.ceil(max_tokens / wl.block)
+    cfg = dms.make_config(
+        max_batch=wl.B, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
+        window=wl.window, block_size=wl.block, max_tokens_per_seq=max_tokens, pool_pages=pool_pages,
+        max_chunk=wl.chunk, kv_dtype="bf16", decide_mode="linear", alpha_per="head")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + wl.cfg_id)
+    layers = []
+    t0 = time.time()
+    for i in range(args.layers):
+        L = Layer(i, cfg, wl, dms, torch, gen, S)
+        calibrate_and_fill(L, wl, dms, torch)
+        layers.append(L)
+    torch.cuda.synchronize()
+    for L in layers:
+        assert dms.dms_cache_status(L.cache) == 0
+    log(f"{args.layers} layers filled with {wl.prefill} tokens x {wl.B} sequences in {time.time() - t0:.1f}s")
+
+    graphs = []
+    if not args.eager:
+        for s in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                decode_step(layers, s, wl, dms)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        log(f"captured {S} step graphs")
+
+    def step(s):
+        if graphs:
+            graphs[s].replay()
+        else:
+            decode_step(layers, s, wl, dms)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    live0 = [dms.dms_cache_stats(L.cache) for L in layers]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for s in range(args.warmup, S):
+        step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed_ms = ev0.elapsed_time(ev1)
+    live1 = [dms.dms_cache_stats(L.cache) for L in layers]
+    for L in layers:
+        assert dms.dms_cache_status(L.cache) == 0
+    ms_per_step = elapsed_ms / args.steps
+    tok_s_layer = wl.B * args.steps * args.layers / (elapsed_ms / 1e3)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {tok_s_layer / 1e6:.3f} M tok/s/layer")
+
+    # Decode-attention kernel alone: back-to-back calls over the 36 layer caches
+    # (the state is not changed by attention), HIP events on the launch stream.
+    reps = args.attn_reps
+    for L in layers:
+        dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(reps):
+        for L in layers:
+            dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B)
+    a1.record()
+    torch.cuda.synchronize()
+    attn_us = a0.elapsed_time(a1) * 1e3 / (reps * len(layers))
+
+    row_bytes = wl.D * 2
+    kv_live = float(np.mean([s["bytes_live"] for s in live1]))          # K+V bytes the attention reads
+    kv_live_mid = float(np.mean([(a["bytes_live"] + b["bytes_live"]) / 2 for a, b in zip(live0, live1)]))
+    qo_bytes = 2 * wl.B * wl.Hq * wl.D * 2
+    pages = float(np.mean([s["pages_in_use"] for s in live1]))
+    attn_bytes = kv_live + qo_bytes + pages * 4
+    attn_gbs = attn_bytes / (attn_us * 1e-6) / 1e9
+    mean_L = kv_live / (wl.B * wl.Hkv * 2 * row_bytes)
+    step_bytes = kv_live_mid + qo_bytes
+    stats = live1[0]
+    return {
+        "value": tok_s_layer,
+        "ms_per_step": ms_per_step,
+        "attn_us": attn_us,
+        "attn_bytes": attn_bytes,
+        "attn_gbs": attn_gbs,
+        "mean_live_slots_per_head": mean_L,
+        "layer_step_us": ms_per_step * 1e3 / args.layers,
+        "step_kv_gbs": step_bytes * args.layers / (ms_per_step * 1e-3) / 1e9,
+        "kv_bytes_resident_per_layer": float(np.mean([s["bytes_allocated"] for s in live1])),
+        "kv_bytes_live_per_layer": kv_live,
+        "dense_bf16_kv_bytes_per_layer": float(wl.B * wl.Hkv * (wl.prefill + S) * 2 * row_bytes),
+        "cache_cr": stats["cache_cr"],
+        "graphs": bool(graphs),
+    }
+
+
+def run_prefill(args, dms, synth, torch):
+    """32K-token prompt in 4096-token chunks (query-neuron decisions, offset 5):
+    per chunk dms_decide -> dms_prefill_attn -> dms_append_evict."""
+    wl = synth.QWEN8B_PREFILL32K
+    T, C = wl.prefill, wl.chunk
+    cfg = dms.make_config(
+        max_batch=1, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
+        window=wl.window, block_size=wl.block, max_tokens_per_seq=T, pool_pages=wl.Hkv * (T // wl.block),
+        max_chunk=C, kv_dtype="bf16", decide_mode="qneuron", alpha_per="head")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + wl.cfg_id)
+    q = torch.randn(T // C, 1, C, wl.Hq, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn(T // C, 1, C, wl.Hkv, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(T // C, 1, C, wl.Hkv, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    off = torch.full((wl.Hkv,), float(wl.fixed_offset), device="cuda")
+    ev = torch.empty(T // C, wl.Hkv * C, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, C, wl.Hq, wl.D, dtype=torch.bfloat16, device="cuda")
+
+    def once(qq, times=None):
+        cache = dms.DmsCache(cfg)
+        for c in range(T // C):
+            dms.dms_decide(cache, None, None, None, None, off, qq[c], 1, C, None, ev[c])
+            if times is not None:
+                times[c][0].record()
+            dms.dms_prefill_attn(cache, None, qq[c], k[c], v[c], ev[c], out, 1, C)
+            if times is not None:
+                times[c][1].record()
+            dms.dms_append_evict(cache, None, k[c], v[c], ev[c], 1, C)
+        return cache
+
+    once(q.clone())
+    torch.cuda.synchronize()
+    qq = q.clone()
+    times = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T // C)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    once(qq, times)
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    attn_ms = sum(a.elapsed_time(b) for a, b in times)
+    # useful flops: 4 * D per (query head, visible key) pair; |V(i)| = (i+1) - #{j <= i-w: e_j}
+    e = ev.view(T // C, wl.Hkv, C).permute(1, 0, 2).reshape(wl.Hkv, T).to(torch.int64)
+    ce = torch.cumsum(e, dim=1)
+    i = torch.arange(T, device="cuda")
+    evicted_out = torch.where(i >= wl.window, ce[:, (i - wl.window).clamp(min=0)], torch.zeros_like(ce))
+    vis = (i + 1)[None, :] - evicted_out
+    useful = 4.0 * wl.D * wl.g * float(vis.sum())
+    return {
+        "workload": wl.name,
+        "tokens": T,
+        "ms_per_prompt": total_ms,
+        "tok_s": T / (total_ms / 1e3),
+        "attn_ms": attn_ms,
+        "useful_tflop": useful / 1e12,
+        "attn_tflops": useful / (attn_ms * 1e-3) / 1e12,
+        "frac_bf16_peak": useful / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "evict_fraction": float(e.float().mean()),
+    }
+
+
+def cpu_baseline(steps: int):
+    """The CPU oracle (float64 NumPy) on a bounded sample of the same decode
+    workload: one layer, B = 8, 8192-token prompt, `steps` decode steps of
+    decide + cache simulation + masked attention.  Prompt state is built
+    untimed."""
+    import oracle
+    from learned_kv_cache_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    wl = synth.QWEN8B_DECODE
+    d = synth.draw(wl, run_id=7)
+    B, Hkv = wl.B, wl.Hkv
+    pre = []
+    for b in range(B):
+        lg, _ = oracle.decide_linear(d.tensor("h", b)[None, : wl.prefill], d.gamma, d.W, np.zeros(Hkv),
+                                     alpha_scale=wl.alpha_scale, eps=1e-6)
+        pre.append(lg[0])
+    off = np.array([synth.offset_for_fraction(np.concatenate([p[k] for p in pre]), d.p_h[k]) for k in range(Hkv)])
+    e_hist = [(p - off[:, None] > 0).astype(np.uint8) for p in pre]
+    sim = oracle.CacheSim(B, Hkv, wl.window, wl.block, wl.prefill + steps, B * Hkv * 64)
+    for s in range(0, wl.prefill, wl.chunk):
+        sim.append(list(range(B)), np.stack([e[:, s:s + wl.chunk] for e in e_hist]))
+    K = [d.tensor("k", b, keep=True) for b in range(B)]
+    V = [d.tensor("v", b, keep=True) for b in range(B)]
+    hd = [d.decode_rows("h", b) for b in range(B)]
+    qd = [d.decode_rows("q", b) for b in range(B)]
+    scale = 1.0 / math.sqrt(wl.D)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        t = wl.prefill + i
+        h = np.stack([hd[b][i] for b in range(B)])[:, None]
+        _, e = oracle.decide_linear(h, d.gamma, d.W, off, alpha_scale=wl.alpha_scale, eps=1e-6)
+        sim.append(list(range(B)), e)
+        for b in range(B):
+            e_hist[b] = np.concatenate([e_hist[b], e[b]], axis=1)
+            oracle.attention_rows(qd[b][i][None], K[b][: t + 1], V[b][: t + 1], e_hist[b], wl.window, [t], scale)
+    dt = time.perf_counter() - t0
+    return {
+        "value": B * steps / dt,
+        "unit": "tok/s/layer",
+        "cores": blas_threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"{steps} decode steps of one Qwen3-8B-shaped layer, B=8, ctx 8192 (float64 NumPy: "
+                  f"decide + cache simulation + masked attention); prompt state built untimed",
+        "seconds": dt,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--attn-reps", type=int, default=20)
+    ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying graphs")
+    ap.add_argument("--cpu-steps", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the DMS decode path has no multi-GPU mode in this build", file=sys.stderr)
+        return 2
+    import torch
+    from learned_kv_cache_amd import dms, synth
+    dms.lib()
+    torch.cuda.set_device(0)
+    dec = run_decode(args, dms, synth, torch)
+    pre = None if args.no_prefill else run_prefill(args, dms, synth, torch)
+    if pre:
+        log(f"prefill: {pre['ms_per_prompt']:.1f} ms per 32K prompt, attention {pre['attn_tflops']:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(args.cpu_steps)
+        log(f"cpu baseline {cpu['value']:.1f} tok/s/layer in {cpu['seconds']:.1f}s")
+    traffic = traffic_from_profiles("decode_attn")
+    line = {
+        "metric": METRIC,
+        "value": dec["value"],
+        "unit": "tok/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3-8b_layer_ctx8k_b8_decode",
+            "layers": args.layers, "batch": 8, "ctx": 8192, "hidden": 4096, "q_heads": 32, "kv_heads": 8,
+            "head_dim": 128, "window": 512, "block": 256, "evict_fraction": [0.85, 0.92],
+            "step": "per layer: dms_decide -> dms_append_evict -> dms_decode_attn",
+            "graphs": dec["graphs"], "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "decode_attn (dms_decode_attn)",
+            "bound": "hbm",
+            "achieved": dec["attn_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec["attn_gbs"] / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec["attn_bytes"],
+            "avg_launch_us": dec["attn_us"],
+        },
+        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "layer_step_us": dec["layer_step_us"],
+        "step_kv_gbs": dec["step_kv_gbs"],
+        "mean_live_slots_per_head": dec["mean_live_slots_per_head"],
+        "kv_bytes_resident_per_layer": dec["kv_bytes_resident_per_layer"],
+        "kv_bytes_live_per_layer": dec["kv_bytes_live_per_layer"],
+        "dense_bf16_kv_bytes_per_layer": dec["dense_bf16_kv_bytes_per_layer"],
+        "cache_cr": dec["cache_cr"],
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -179,7 +179,8 @@ class Draw:
         self.ctx = context_lengths(wl, self.gens["ctx"])
         self.W = self.gens["W"].normal(0.0, wl.weight_std(), size=(wl.Hkv, wl.hidden)).astype(np.float32)
         self.gamma = np.ones(wl.hidden, dtype=np.float32)
-        self._seeds = {name: kids[name].spawn(wl.B) for name in self.TAILS}
+        # per sequence, one child for the prompt rows and one for the decode rows
+        self._seeds = {name: kids[name].spawn(2 * wl.B) for name in self.TAILS}
         self._overlay: Dict[Tuple[str, int], Dict[int, np.ndarray]] = {}
         self._cache: Dict[Tuple[str, int], np.ndarray] = {}
         self._last: Dict[str, Tuple[int, np.ndarray]] = {}    # most recent sequence per tensor
@@ -199,14 +200,30 @@ class Draw:
         last = self._last.get(name)
         if last is not None and last[0] == b:
             return last[1]
-        gen = np.random.Generator(np.random.PCG64(self._seeds[name][b]))
-        x = normal(gen, (self.T(b),) + self._tail(name), self.wl.act_dtype)
+        x = np.concatenate([self._rows(name, b, 0), self._rows(name, b, 1)], axis=0)
         for t, row in self._overlay.get(key, {}).items():
             x[t] = row
         if keep:
             self._cache[key] = x
         else:
             self._last[name] = (b, x)
+        return x
+
+    def _rows(self, name: str, b: int, part: int) -> np.ndarray:
+        n = int(self.ctx[b]) if part == 0 else self.wl.decode_steps
+        gen = np.random.Generator(np.random.PCG64(self._seeds[name][2 * b + part]))
+        return normal(gen, (n,) + self._tail(name), self.wl.act_dtype)
+
+    def decode_rows(self, name: str, b: int) -> np.ndarray:
+        """Rows ctx[b] .. ctx[b] + decode_steps - 1 of ``name`` (cheap: drawn alone)."""
+        key = (name, b)
+        if key in self._cache:
+            return self._cache[key][int(self.ctx[b]):]
+        x = self._rows(name, b, 1)
+        c0 = int(self.ctx[b])
+        for t, row in self._overlay.get(key, {}).items():
+            if t >= c0:
+                x[t - c0] = row
         return x
 
     def set_rows(self, name: str, b: int, rows: Dict[int, np.ndarray]) -> None:

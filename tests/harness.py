@@ -80,7 +80,7 @@ def prepare(wl: synth.Workload, run_id: int = 0, max_rounds: int = 50) -> Prepar
                     r = q[t].copy()
                     for k in range(Hkv):
                         if abs(wl.alpha_scale * float(r[k * wl.g, -1]) - off[k]) < MARGIN:
-                            r[k * wl.g, -1] = synth.redraw(gen, (), wl.act_dtype)
+                            r[k * wl.g, -1] = synth.redraw(gen, (1,), wl.act_dtype)[0]
                     rows[int(t)] = r
                 d.set_rows("q", b, rows)
                 u[b] = _pre_offset_qneuron(d, b)
@@ -170,7 +170,7 @@ class Runner:
             return d.tensor(name, b)[t]
         key = (name, b)
         if key not in self._dec:
-            self._dec[key] = d.tensor(name, b)[c0:].copy()
+            self._dec[key] = d.decode_rows(name, b).copy()
         return self._dec[key][t - c0]
 
     def decide(self, seqs: Sequence[int], s: int, C: int, q_dev=None):
