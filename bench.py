@@ -195,17 +195,20 @@ def run_decode(args, dms, synth, torch):
     tok_s_layer = wl.B * args.steps * args.layers / (elapsed_ms / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {tok_s_layer / 1e6:.3f} M tok/s/layer")
 
-    # Decode-attention kernel alone: back-to-back calls over the 36 layer caches
-    # (the state is not changed by attention), HIP events on the launch stream.
+    # Decode attention alone: one graph holding the dms_decode_attn calls of
+    # all layers (the cache state does not change), replayed; HIP events on the
+    # launch stream around the replays; average per call.
     reps = args.attn_reps
-    for L in layers:
-        dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B)
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        for L in layers:
+            dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B)
+    ga.replay()
     torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
     for _ in range(reps):
-        for L in layers:
-            dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B)
+        ga.replay()
     a1.record()
     torch.cuda.synchronize()
     attn_us = a0.elapsed_time(a1) * 1e3 / (reps * len(layers))

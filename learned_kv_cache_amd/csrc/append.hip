@@ -54,12 +54,28 @@ __device__ __forceinline__ float row_amax(const ACT* src, int D, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode append (T = 1): one workgroup; 1024 pairs per round.
+// Decode append (T = 1): one workgroup of 1024 threads; pairs (row, KV head)
+// in rounds of up to 1024.  One thread per pair decides the slot; CPP threads
+// per pair copy its K and V rows, whose input values are loaded at the start
+// of the round so the copy does not wait on the slot decision's loads.  The
+// dependent loads are: position -> ring entry -> page (free stack or table).
+template <typename ACT, int KV>
+__device__ __forceinline__ void copy_part(uint8_t* pages, int64_t dst_row, int D, int e0, int ne, const float* x,
+                                          float inv_scale) {
+  for (int i = 0; i < ne; ++i) {
+    const int e = e0 + i;
+    if (KV == DMS_F32) reinterpret_cast<float*>(pages)[dst_row * D + e] = x[i];
+    else if (KV == DMS_BF16) reinterpret_cast<uint16_t*>(pages)[dst_row * D + e] = f32_to_bf16(x[i]);
+    else pages[dst_row * D + e] = f32_to_e4m3(x[i] * inv_scale);
+  }
+}
+
 template <typename ACT, int KV>
 __global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
+  constexpr int MAXE = 16;                  // elements per thread in the copy (D <= 128, CPP >= 8)
   __shared__ int s_wave[16];
-  __shared__ int s_dst[1024];    // destination row (page * P + offset), -1: nothing to write
-  __shared__ int s_page[1024];   // page of the destination
+  __shared__ int s_dst[1024];               // destination row (page * P + offset), -1: nothing to write
+  __shared__ int s_page[1024];
   __shared__ uint8_t s_new[1024];
   __shared__ int s_free, s_used;
   const DevCache& d = a.d;
@@ -70,30 +86,49 @@ __global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
     s_free = d.ctl[kCtlFreeCount];
     s_used = 0;
   }
-  __syncthreads();
   for (int p0 = 0; p0 < npairs; p0 += 1024) {
+    const int nround = min(1024, npairs - p0);
+    // copy geometry of this round: CPP threads per pair, ne elements each
+    int cpp = 1024 / nround;
+    cpp = cpp >= 64 ? 64 : (cpp >= 32 ? 32 : (cpp >= 16 ? 16 : (cpp >= 8 ? 8 : (cpp >= 4 ? 4 : (cpp >= 2 ? 2 : 1)))));
+    while (cpp > 1 && (g.D % cpp != 0 || g.D / cpp < 2)) cpp >>= 1;
+    const int ne_max = g.D / cpp;
+    const int cpair = tid / cpp, cpart = tid % cpp;
+    const bool copier = cpair < nround && ne_max <= MAXE;
+    float kx[MAXE], vx[MAXE];
+    if (copier) {
+      const size_t src = static_cast<size_t>(p0 + cpair) * g.D + cpart * ne_max;   // [B][1][Hkv][D]
+      const ACT* ks = static_cast<const ACT*>(a.k) + src;
+      const ACT* vs = static_cast<const ACT*>(a.v) + src;
+#pragma unroll
+      for (int i = 0; i < MAXE; ++i) {
+        kx[i] = i < ne_max ? load_act<ACT>(ks, i) : 0.0f;
+        vx[i] = i < ne_max ? load_act<ACT>(vs, i) : 0.0f;
+      }
+    }
     const int p = p0 + tid;
     bool valid = false, need = false, overwrite = false;
-    int seq = 0, kh = 0, t = 0, slot = 0, e = 0, unit = 0;
+    int kh = 0, t = 0, slot = 0, e = 0, unit = 0;
     if (p < npairs) {
       const int row = p / g.Hkv;
       kh = p % g.Hkv;
-      seq = a.seq_ids ? a.seq_ids[row] : row;
+      const int seq = a.seq_ids ? a.seq_ids[row] : row;
       if (seq < 0 || seq >= g.Bmax) {
         set_status(d.ctl, DMS_DEV_BAD_SEQ);
       } else {
+        unit = seq * g.Hkv + kh;
         t = d.pos[seq];
+        const int len = d.lengths[unit];
+        e = a.evict[p] ? 1 : 0;
         if (t + 1 > g.max_tokens) {
           set_status(d.ctl, DMS_DEV_CAPACITY);
         } else {
-          unit = seq * g.Hkv + kh;
-          e = a.evict[p] ? 1 : 0;
           const int rv = (t >= g.w) ? d.ring[static_cast<int64_t>(unit) * g.w + t % g.w] : 0;
           if (t >= g.w && rv < 0) {
             overwrite = true;
             slot = rv & 0x7FFFFFFF;
           } else {
-            slot = d.lengths[unit];
+            slot = len;
             need = (slot % g.P) == 0;
           }
           valid = true;
@@ -130,39 +165,65 @@ __global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
       d.ring[static_cast<int64_t>(unit) * g.w + t % g.w] = slot | (e << 31);
       d.slot_meta[static_cast<int64_t>(page) * g.P + slot % g.P] = t | (e << 31);
     }
-    s_dst[tid] = valid ? page * g.P + slot % g.P : -1;
-    s_page[tid] = page;
-    s_new[tid] = (valid && need) ? 1 : 0;
+    if (tid < nround) {
+      s_dst[tid] = valid ? page * g.P + slot % g.P : -1;
+      s_page[tid] = page;
+      s_new[tid] = (valid && need) ? 1 : 0;
+    }
     __syncthreads();
-    const int rows = min(1024, npairs - p0);
-    for (int r = wave; r < rows; r += 16) {
-      const int dst = s_dst[r];
-      if (dst < 0) continue;
-      const int pr = p0 + r;
-      const int row = pr / g.Hkv, khr = pr % g.Hkv;
-      const size_t src = (static_cast<size_t>(row) * g.Hkv + khr) * g.D;   // [B][1][Hkv][D]
+    if (cpair < nround) {
+      const int dst = s_dst[cpair];
+      const size_t src = static_cast<size_t>(p0 + cpair) * g.D + cpart * ne_max;
       const ACT* ks = static_cast<const ACT*>(a.k) + src;
       const ACT* vs = static_cast<const ACT*>(a.v) + src;
       float inv_k = 1.0f, inv_v = 1.0f;
       if (KV == DMS_FP8_E4M3) {
-        const int pg = s_page[r];
-        float sk, sv;
-        if (s_new[r]) {
-          sk = page_scale_from_amax(row_amax<ACT>(ks, g.D, lane));
-          sv = page_scale_from_amax(row_amax<ACT>(vs, g.D, lane));
-          if (lane == 0) {
-            d.scales[2 * pg] = sk;
-            d.scales[2 * pg + 1] = sv;
-          }
-        } else {
-          sk = d.scales[2 * pg];
-          sv = d.scales[2 * pg + 1];
+        // amax over the row's cpp threads (contiguous lanes of one wave)
+        float mk = 0.0f, mv = 0.0f;
+        for (int i = 0; i < ne_max; ++i) {
+          mk = fmaxf(mk, fabsf(copier ? kx[i < MAXE ? i : 0] : load_act<ACT>(ks, i)));
+          mv = fmaxf(mv, fabsf(copier ? vx[i < MAXE ? i : 0] : load_act<ACT>(vs, i)));
         }
-        inv_k = 1.0f / sk;
-        inv_v = 1.0f / sv;
+        for (int o = 1; o < cpp; o <<= 1) {
+          mk = fmaxf(mk, __shfl_xor(mk, o));
+          mv = fmaxf(mv, __shfl_xor(mv, o));
+        }
+        if (dst >= 0) {
+          const int pg = s_page[cpair];
+          float sk, sv;
+          if (s_new[cpair]) {
+            sk = page_scale_from_amax(mk);
+            sv = page_scale_from_amax(mv);
+            if (cpart == 0) {
+              d.scales[2 * pg] = sk;
+              d.scales[2 * pg + 1] = sv;
+            }
+          } else {
+            sk = d.scales[2 * pg];
+            sv = d.scales[2 * pg + 1];
+          }
+          inv_k = 1.0f / sk;
+          inv_v = 1.0f / sv;
+        }
       }
-      store_row<ACT, KV>(d.k_pages, dst, ks, g.D, lane, inv_k);
-      store_row<ACT, KV>(d.v_pages, dst, vs, g.D, lane, inv_v);
+      if (dst >= 0) {
+        if (copier) {
+          copy_part<ACT, KV>(d.k_pages, dst, g.D, cpart * ne_max, ne_max, kx, inv_k);
+          copy_part<ACT, KV>(d.v_pages, dst, g.D, cpart * ne_max, ne_max, vx, inv_v);
+        } else {
+          // rows split over few threads: copy in pieces of MAXE elements
+          for (int i0 = 0; i0 < ne_max; i0 += MAXE) {
+            const int n = min(MAXE, ne_max - i0);
+            float tk[MAXE], tv[MAXE];
+            for (int i = 0; i < n; ++i) {
+              tk[i] = load_act<ACT>(ks, i0 + i);
+              tv[i] = load_act<ACT>(vs, i0 + i);
+            }
+            copy_part<ACT, KV>(d.k_pages, dst, g.D, cpart * ne_max + i0, n, tk, inv_k);
+            copy_part<ACT, KV>(d.v_pages, dst, g.D, cpart * ne_max + i0, n, tv, inv_v);
+          }
+        }
+      }
     }
     __syncthreads();
     if (tid == 0) s_used += round_total;

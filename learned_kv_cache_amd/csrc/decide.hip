@@ -10,10 +10,10 @@
 // disable_eviction nothing is evicted.
 //
 // The projection reads h once (2 bytes per element for bf16) and does
-// Hkv + 1 fused multiply-adds per element, so it is bound by HBM, not by
-// arithmetic; it runs in fp32 on the vector ALUs.  Rounding the normalised
-// activations to bf16 for a matrix-core product would move logits by ~0.1,
-// far more than the 1e-2 margin the decisions are compared at.
+// Hkv + 1 fused multiply-adds per element, so it is bound by HBM (prefill) or
+// by latency (decode), not by arithmetic; it runs in fp32 on the vector ALUs.
+// Rounding the normalised activations to bf16 for a matrix-core product would
+// move logits by ~0.1, far more than the 1e-2 margin decisions are compared at.
 #include "dms_internal.h"
 
 namespace dms {
@@ -43,43 +43,82 @@ template <int N> __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
   }
 }
 
-// One wave per token: every lane accumulates sum(h^2) and, for each head,
-// sum(W_k * gamma * h) over its share of H; then z_k = r * dot_k with
+// TT tokens per 256-thread workgroup.  Thread t owns the elements
+// [4t + 1024i, 4t + 1024i + 4) of the hidden vector for i = 0..H/1024-1 and
+// keeps its W and gamma values in registers for all TT tokens; every lane
+// accumulates sum(h^2) and, per head, sum(W_k * gamma * h); waves reduce with
+// shuffles, the four waves through LDS; then z_k = r * dot_k with
 // r = 1 / sqrt(mean(h^2) + eps).
-template <typename ACT, int HKV>
+template <typename ACT, int HKV, int TT, int NCH>
 __global__ __launch_bounds__(256) void decide_linear_kernel(DecideArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= a.ntok) return;
-  const ACT* h = static_cast<const ACT*>(a.hidden) + static_cast<size_t>(tok) * a.H;
-  float acc[HKV + 1];
+  __shared__ float s_red[4][TT][HKV + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok0 = blockIdx.x * TT;
+  float acc[TT][HKV + 1];
 #pragma unroll
-  for (int i = 0; i <= HKV; ++i) acc[i] = 0.0f;
-  for (int m = lane * 4; m < a.H; m += 256) {
-    float x[4];
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = load_act<ACT>(h, m + e);
-    const float4 gm = *reinterpret_cast<const float4*>(a.gamma + m);
-    const float gx[4] = {gm.x * x[0], gm.y * x[1], gm.z * x[2], gm.w * x[3]};
+    for (int k = 0; k <= HKV; ++k) acc[t][k] = 0.0f;
+  for (int m0 = 4 * tid; m0 < a.H; m0 += 1024 * NCH) {
+    float4 w[NCH][HKV];
+    float4 gm[NCH];
+    bool okc[NCH];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[HKV] = fmaf(x[e], x[e], acc[HKV]);
+    for (int c = 0; c < NCH; ++c) {
+      const int m = m0 + 1024 * c;
+      okc[c] = m < a.H;
+      gm[c] = okc[c] ? *reinterpret_cast<const float4*>(a.gamma + m) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < HKV; ++k) {
-      const float4 w = *reinterpret_cast<const float4*>(a.W + static_cast<size_t>(k) * a.H + m);
-      acc[k] = fmaf(w.x, gx[0], acc[k]);
-      acc[k] = fmaf(w.y, gx[1], acc[k]);
-      acc[k] = fmaf(w.z, gx[2], acc[k]);
-      acc[k] = fmaf(w.w, gx[3], acc[k]);
+      for (int k = 0; k < HKV; ++k)
+        w[c][k] = okc[c] ? *reinterpret_cast<const float4*>(a.W + static_cast<size_t>(k) * a.H + m)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const int tok = tok0 + t;
+      if (tok >= a.ntok) break;
+      const ACT* h = static_cast<const ACT*>(a.hidden) + static_cast<size_t>(tok) * a.H;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (!okc[c]) continue;
+        const int m = m0 + 1024 * c;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = load_act<ACT>(h, m + e);
+        const float gx[4] = {gm[c].x * x[0], gm[c].y * x[1], gm[c].z * x[2], gm[c].w * x[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][HKV] = fmaf(x[e], x[e], acc[t][HKV]);
+#pragma unroll
+        for (int k = 0; k < HKV; ++k) {
+          acc[t][k] = fmaf(w[c][k].x, gx[0], acc[t][k]);
+          acc[t][k] = fmaf(w[c][k].y, gx[1], acc[t][k]);
+          acc[t][k] = fmaf(w[c][k].z, gx[2], acc[t][k]);
+          acc[t][k] = fmaf(w[c][k].w, gx[3], acc[t][k]);
+        }
+      }
     }
   }
-  wave_sum_n<HKV + 1>(acc);
-  if (lane != 0) return;
-  const float r = 1.0f / sqrtf(acc[HKV] / static_cast<float>(a.H) + a.eps);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) wave_sum_n<HKV + 1>(acc[t]);
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int k = 0; k <= HKV; ++k) s_red[wave][t][k] = acc[t][k];
+  }
+  __syncthreads();
+  if (tid >= TT) return;
+  const int tok = tok0 + tid;
+  if (tok >= a.ntok) return;
+  float tot[HKV + 1];
+#pragma unroll
+  for (int k = 0; k <= HKV; ++k) tot[k] = s_red[0][tid][k] + s_red[1][tid][k] + s_red[2][tid][k] + s_red[3][tid][k];
+  const float r = 1.0f / sqrtf(tot[HKV] / static_cast<float>(a.H) + a.eps);
   const int b = tok / a.T, t = tok % a.T;
   float lg0 = 0.0f;
 #pragma unroll
   for (int k = 0; k < HKV; ++k) {
-    float z = r * acc[k];
+    float z = r * tot[k];
     if (a.bias) z += a.bias[k];
     float lg = a.alpha * z - a.offsets[k];
     if (k == 0) lg0 = lg;
@@ -118,15 +157,26 @@ __global__ void decide_qneuron_kernel(QneuronArgs a) {
   for (int k = 0; k < a.Hkv; ++k) store_act<ACT>(q, static_cast<size_t>(k) * a.g * a.D + a.D - 1, 0.0f);
 }
 
+template <typename ACT, int HKV>
+static void launch_linear_h(const DecideArgs& a, hipStream_t st) {
+  // few tokens (decode): one token per workgroup, all loads of a thread in
+  // flight at once; many tokens (prefill chunks): 4 tokens share W registers
+  if (a.ntok <= 512) {
+    hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 1, (HKV <= 8 ? 4 : 2)>), dim3(a.ntok), dim3(256), 0, st, a);
+  } else {
+    constexpr int NCH = HKV <= 8 ? 2 : 1;
+    hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 4, NCH>), dim3((a.ntok + 3) / 4), dim3(256), 0, st, a);
+  }
+}
+
 template <typename ACT>
 static void launch_linear(const DecideArgs& a, int hkv, hipStream_t st) {
-  const dim3 grid((a.ntok + 3) / 4), block(256);
   switch (hkv) {
-    case 1: hipLaunchKernelGGL((decide_linear_kernel<ACT, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decide_linear_kernel<ACT, 2>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decide_linear_kernel<ACT, 4>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((decide_linear_kernel<ACT, 8>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((decide_linear_kernel<ACT, 16>), grid, block, 0, st, a); break;
+    case 1: launch_linear_h<ACT, 1>(a, st); break;
+    case 2: launch_linear_h<ACT, 2>(a, st); break;
+    case 4: launch_linear_h<ACT, 4>(a, st); break;
+    case 8: launch_linear_h<ACT, 8>(a, st); break;
+    case 16: launch_linear_h<ACT, 16>(a, st); break;
     default: break;
   }
 }

@@ -16,7 +16,7 @@
 // * Each lane loads 16 contiguous bytes of a K row and of a V row; LPR lanes
 //   cover one row, a wave covers 64/LPR rows per pass, NP passes are in flight.
 // * Online softmax per wave in base 2; waves merge through LDS; units split
-//   over several workgroups are merged by a small combine kernel.
+//   over several workgroups are merged by a second, small kernel.
 #include "dms_internal.h"
 
 namespace dms {
@@ -28,6 +28,7 @@ struct DecodeArgs {
   const void* q;
   void* out;
   int B;
+  int lanes_per_row;   // fast kernel row layout (8 or 16 lanes per bf16 row of 128)
 };
 
 template <int KV> struct KvTraits;
@@ -362,6 +363,544 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for bf16 and fp8 pages (D = 64 or 128).
+//
+// Each lane owns 16 bytes of a row (8 bf16 or 16 fp8 elements), LPR lanes a
+// row, RG = 64 / LPR rows per wave and pass, 4 waves per workgroup.  Every
+// load of a round (NP passes) is issued before any arithmetic, so one
+// workgroup keeps NP * 4 * RG rows of K and V in flight.  Scores use the
+// packed bf16 dot product (fp8 codes are widened to bf16 exactly); the row sum
+// runs over LPR lanes with DPP; probabilities are rounded to bf16 for the
+// P.V dot products, accumulation is fp32.  A unit split over workgroups
+// leaves one partial per workgroup (records 2w and 2w+1: a workgroup's first
+// and last segment) that decode_merge_kernel combines.  (Merging inside the
+// kernel through a last-arrival counter needs a device-scope release per
+// workgroup, which writes back the whole L2 of its XCD; a second small launch
+// is far cheaper.)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPR lanes of a row (LPR in {4, 8, 16}); every lane gets the sum.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_mov<0xB1>(x);                      // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);                      // quad_perm [2,3,0,1]
+  if (LPR >= 8) x += dpp_mov<0x141>(x);       // row_half_mirror
+  if (LPR >= 16) x += dpp_mov<0x140>(x);      // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// four fp8 codes -> two bf16 pairs (exact)
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+template <int LPR>
+__device__ __forceinline__ float cross_rows_max(float x) {
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// K/V rows of NP passes held in registers (one 16-byte piece or more per lane per row).
+template <int NP, int NV>
+struct KvChunk {
+  uint4 k[NP][NV];
+  uint4 v[NP][NV];
+  int pg[NP];
+};
+
+// Issues the loads of passes [pass0, pass0 + NP) of a segment; rows at or past
+// `hi` are not loaded.
+template <int D, int NP, bool FP8, int LPR>
+__device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c, const uint8_t* __restrict__ kp,
+                                           const uint8_t* __restrict__ vp, int pt_reg, int first_page, int lo, int pass0,
+                                           int hi, int wave, int lane_row, int lane_col, int psh, int pmask) {
+  constexpr int RB = D * (FP8 ? 1 : 2);
+  constexpr int BPL = RB / LPR;
+  constexpr int NV = BPL / 16;
+  constexpr int RG = 64 / LPR;
+  constexpr int RPP = 4 * RG;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int r = lo + (pass0 + p) * RPP + wave * RG + lane_row;
+    const bool ok = r < hi;
+    c.pg[p] = __shfl(pt_reg, ok ? (r >> psh) - first_page : 0);
+    const uint32_t off = (static_cast<uint32_t>(c.pg[p]) * static_cast<uint32_t>(pmask + 1) +
+                          static_cast<uint32_t>(r & pmask)) * static_cast<uint32_t>(RB) +
+                         static_cast<uint32_t>(lane_col * BPL);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (ok) {
+        c.k[p][j] = *reinterpret_cast<const uint4*>(kp + off + 16 * j);
+        c.v[p][j] = *reinterpret_cast<const uint4*>(vp + off + 16 * j);
+      } else {
+        c.k[p][j] = make_uint4(0, 0, 0, 0);
+        c.v[p][j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Online-softmax update with the rows of one chunk.
+template <int D, int G, int NP, bool FP8, int LPR>
+__device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c,
+                                              const float* __restrict__ scales, int lo, int pass0, int hi, int wave,
+                                              int lane_row, float scale_log2,
+                                              const uint32_t (&qv)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2)) / 2],
+                                              float (&m)[G], float (&l)[G],
+                                              float (&o)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2))]) {
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int RB = D * EB;
+  constexpr int BPL = RB / LPR;
+  constexpr int NV = BPL / 16;
+  constexpr int EPL = BPL / EB;
+  constexpr int QW = EPL / 2;
+  constexpr int RG = 64 / LPR;
+  constexpr int RPP = 4 * RG;
+  bool ok[NP];
+  float sk[NP], sv[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    ok[p] = lo + (pass0 + p) * RPP + wave * RG + lane_row < hi;
+    sk[p] = scale_log2;
+    sv[p] = 1.0f;
+    if (FP8) {
+      sk[p] *= scales[2 * c.pg[p]];
+      sv[p] = scales[2 * c.pg[p] + 1];
+    }
+  }
+  float s[NP][G];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t kw[QW];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const uint32_t raw[4] = {c.k[p][j].x, c.k[p][j].y, c.k[p][j].z, c.k[p][j].w};
+      if (FP8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) fp8x4_to_bf16(raw[t], kw[8 * j + 2 * t], kw[8 * j + 2 * t + 1]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kw[4 * j + t] = raw[t];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < QW; ++j) acc = dot2(qv[h][j], kw[j], acc);
+      acc = row_sum<LPR>(acc) * sk[p];
+      s[p][h] = ok[p] ? acc : -INFINITY;
+    }
+  }
+  float pe[NP][G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = s[0][h];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) mx = fmaxf(mx, s[p][h]);
+    mx = cross_rows_max<LPR>(mx);
+    const float m_new = fmaxf(m[h], mx);
+    // a chunk whose wave has no row leaves the state as it is (wave-uniform)
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[h] - m_new);
+    const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
+    m[h] = m_new;
+    l[h] *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      pe[p][h] = __builtin_amdgcn_exp2f(s[p][h] - msub);   // -inf gives 0
+      l[h] += pe[p][h];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NP; p += 2) {
+    uint32_t va[QW], vb[QW];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const uint32_t ra[4] = {c.v[p][j].x, c.v[p][j].y, c.v[p][j].z, c.v[p][j].w};
+      const uint32_t rc[4] = {c.v[p + 1][j].x, c.v[p + 1][j].y, c.v[p + 1][j].z, c.v[p + 1][j].w};
+      if (FP8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          fp8x4_to_bf16(ra[t], va[8 * j + 2 * t], va[8 * j + 2 * t + 1]);
+          fp8x4_to_bf16(rc[t], vb[8 * j + 2 * t], vb[8 * j + 2 * t + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          va[4 * j + t] = ra[t];
+          vb[4 * j + t] = rc[t];
+        }
+      }
+    }
+    uint32_t pk[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pk[h] = pack_bf16(pe[p][h] * sv[p], pe[p + 1][h] * sv[p + 1]);
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+      const uint32_t lo2 = __builtin_amdgcn_perm(vb[j], va[j], 0x05040100u);   // (row p, row p+1) of element 2j
+      const uint32_t hi2 = __builtin_amdgcn_perm(vb[j], va[j], 0x07060302u);   // element 2j+1
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        o[h][2 * j] = dot2(pk[h], lo2, o[h][2 * j]);
+        o[h][2 * j + 1] = dot2(pk[h], hi2, o[h][2 * j + 1]);
+      }
+    }
+  }
+}
+
+template <int D, int G, int NP, bool FP8, int LPR>
+__global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int RB = D * EB;
+  constexpr int BPL = RB / LPR;
+  constexpr int EPL = BPL / EB;
+  constexpr int QW = EPL / 2;
+  constexpr int RG = 64 / LPR;
+  constexpr int RPP = 4 * RG;
+  constexpr int NV = BPL / 16;
+  static_assert(NP % 2 == 0, "passes are paired for the P.V dot products");
+  static_assert(BPL % 16 == 0, "a lane loads whole 16-byte pieces");
+
+  __shared__ int s_start[kMaxUnits + 1];
+  __shared__ int s_tmp[4];
+  __shared__ float s_o[4][G][D];
+  __shared__ float s_ml[4][G][2];
+
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane_row = lane / LPR, lane_col = lane % LPR;
+  const int units = a.B * g.Hkv;
+  const int grid = gridDim.x;
+
+  // -- unit prefix (live slots of every (row, KV head), concatenated) --------
+  if (units <= 64) {
+    if (wave == 0) {
+      int L = 0;
+      if (lane < units) {
+        const int row = lane / g.Hkv, kh = lane % g.Hkv;
+        const int seq = a.seq_ids ? a.seq_ids[row] : row;
+        if (seq >= 0 && seq < g.Bmax) L = d.lengths[seq * g.Hkv + kh];
+        else if (blockIdx.x == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+      }
+      int incl = L;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (lane < units) s_start[lane] = incl - L;
+      if (lane == 63) s_start[units] = incl;
+    }
+    __syncthreads();
+  } else {
+    const int per = (units + 255) / 256;
+    const int u0 = tid * per;
+    int len[8];
+    int sum = 0;
+    for (int i = 0; i < per; ++i) {
+      const int u = u0 + i;
+      int L = 0;
+      if (u < units) {
+        const int row = u / g.Hkv, kh = u % g.Hkv;
+        const int seq = a.seq_ids ? a.seq_ids[row] : row;
+        if (seq >= 0 && seq < g.Bmax) L = d.lengths[seq * g.Hkv + kh];
+        else if (blockIdx.x == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+      }
+      len[i] = L;
+      sum += L;
+    }
+    int W;
+    int run = block_scan_256(sum, s_tmp, &W);
+    for (int i = 0; i < per; ++i) {
+      const int u = u0 + i;
+      if (u < units) s_start[u] = run;
+      run += len[i];
+    }
+    if (tid == 0) s_start[units] = W;
+    __syncthreads();
+  }
+  const int W = s_start[units];
+  const int c = max((W + grid - 1) / grid, RPP);
+
+  // per-unit merge plan for decode_merge_kernel: first/last workgroup and
+  // whether the first workgroup's record is its last segment
+  if (blockIdx.x == 0) {
+    for (int uu = tid; uu < units; uu += 256) {
+      const int us = s_start[uu], ue = s_start[uu + 1];
+      int32_t* ui = d.unit_info + 4 * uu;
+      if (ue == us) {
+        ui[0] = -1;
+        ui[1] = -1;
+        ui[2] = 0;
+      } else {
+        ui[0] = us / c;
+        ui[1] = (ue - 1) / c;
+        ui[2] = (us != (us / c) * c) ? 1 : 0;
+      }
+    }
+  }
+
+  int a0 = blockIdx.x * c;
+  const int a1 = min(a0 + c, W);
+  if (a0 >= a1) return;
+  int lo_u = 0, hi_u = units - 1;
+  while (lo_u < hi_u) {
+    const int mid = (lo_u + hi_u + 1) >> 1;
+    if (s_start[mid] <= a0) lo_u = mid; else hi_u = mid - 1;
+  }
+  int u = lo_u;
+  bool first_seg = true;
+  uint16_t* obase = static_cast<uint16_t*>(a.out);
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
+  const int psh = g.Pshift, pmask = g.P - 1;
+
+  while (a0 < a1) {
+    const int ustart = s_start[u], uend = s_start[u + 1];
+    const int seg_end = min(a1, uend);
+    const int lo = a0 - ustart, hi = seg_end - ustart;
+    const int row = u / g.Hkv, kh = u % g.Hkv;
+    const int seq = a.seq_ids ? a.seq_ids[row] : row;
+    const int32_t* pt = d.page_table + (static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp;
+
+    uint32_t qv[G][QW];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint16_t* qp = qbase + (static_cast<size_t>(row) * g.Hq + kh * G + h) * D + lane_col * EPL;
+#pragma unroll
+      for (int j = 0; j < QW; j += 4) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(qp + 2 * j);
+        qv[h][j] = t4.x;
+        qv[h][j + 1] = t4.y;
+        qv[h][j + 2] = t4.z;
+        qv[h][j + 3] = t4.w;
+      }
+    }
+    float m[G], l[G], o[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
+    }
+    // pages of the segment, up to 64 at a time (lane i holds page first + i);
+    // chunks of NP passes are double-buffered: the loads of chunk i+1 are in
+    // flight while chunk i is computed
+    for (int pb = lo >> psh; pb <= (hi - 1) >> psh; pb += 64) {
+      const int plast = min((hi - 1) >> psh, pb + 63);
+      const int pt_reg = (pb + lane <= plast) ? pt[pb + lane] : 0;
+      const int blo = max(lo, pb << psh), bhi = min(hi, (plast + 1) << psh);
+      const int npass = (bhi - blo + RPP - 1) / RPP;
+      KvChunk<NP, NV> ca, cb;
+      load_chunk<D, NP, FP8, LPR>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, 0, bhi, wave, lane_row, lane_col, psh, pmask);
+      for (int p0 = 0; p0 < npass; p0 += 2 * NP) {
+        if (p0 + NP < npass)
+          load_chunk<D, NP, FP8, LPR>(cb, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + NP, bhi, wave, lane_row, lane_col,
+                                      psh, pmask);
+        compute_chunk<D, G, NP, FP8, LPR>(ca, d.scales, blo, p0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o);
+        if (p0 + NP >= npass) break;
+        if (p0 + 2 * NP < npass)
+          load_chunk<D, NP, FP8, LPR>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + 2 * NP, bhi, wave, lane_row,
+                                      lane_col, psh, pmask);
+        compute_chunk<D, G, NP, FP8, LPR>(cb, d.scales, blo, p0 + NP, bhi, wave, lane_row, g.scale_log2, qv, m, l, o);
+      }
+    }
+
+    // rows of a wave -> one partial per wave
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) {
+        l[h] += __shfl_xor(l[h], off);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+      }
+    }
+    if (lane_row == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_o[wave][h][lane_col * EPL + e] = o[h][e];
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_ml[wave][h][0] = m[h];
+        s_ml[wave][h][1] = l[h];
+      }
+    }
+    __syncthreads();
+    const int w0 = ustart / c, w1 = (uend - 1) / c;
+    const bool split = w1 > w0;
+    const int rec = 2 * blockIdx.x + (first_seg ? 0 : 1);
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int h = idx / D, dd = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][h][0]);
+      float ov = 0.0f, lv = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float f = exp2f(s_ml[w][h][0] - M);     // -inf gives 0
+          ov += f * s_o[w][h][dd];
+          lv += f * s_ml[w][h][1];
+        }
+      }
+      if (!split) {
+        obase[(static_cast<size_t>(row) * g.Hq + kh * G + h) * D + dd] = f32_to_bf16(lv > 0.0f ? ov / lv : 0.0f);
+      } else {
+        float* pr = d.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
+        pr[dd] = ov;
+        if (dd == 0) {
+          pr[D] = M;
+          pr[D + 1] = lv;
+        }
+      }
+    }
+    __syncthreads();
+    first_seg = false;
+    a0 = seg_end;
+    ++u;
+    while (u < units && s_start[u + 1] <= a0) ++u;
+  }
+}
+
+// Merges the partial records of units split over several workgroups and
+// zero-fills heads without live slots.  unit_info[4u] = first workgroup,
+// [4u+1] = last workgroup (-1: empty), [4u+2] = 1 when the first workgroup's
+// record for the unit is its second segment.  All loads of a batch of 8
+// records are issued before any of them is used.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const Geo& g = a.g;
+  const int u = blockIdx.x;
+  const int w0 = a.d.unit_info[4 * u], w1 = a.d.unit_info[4 * u + 1], odd = a.d.unit_info[4 * u + 2];
+  if (w1 >= 0 && w1 == w0) return;                 // written by the attention kernel
+  const int row = u / g.Hkv, kh = u % g.Hkv;
+  uint16_t* obase = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(row) * g.Hq + kh * G) * D;
+  constexpr int PER = (G * D + 255) / 256;
+  if (w1 < 0) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) obase[idx] = 0;
+    return;
+  }
+  const int n = w1 - w0 + 1;
+  float M[PER], O[PER], L[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    M[i] = -INFINITY;
+    O[i] = 0.0f;
+    L[i] = 0.0f;
+  }
+  for (int b0 = 0; b0 < n; b0 += 8) {
+    float mv[8][PER], lv[8][PER], ov[8][PER];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = w0 + b0 + j;
+      const int rec = (b0 + j == 0 && odd) ? 2 * w + 1 : 2 * w;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        const int h = idx / D, dd = idx % D;
+        if (b0 + j < n && idx < G * D) {
+          const float* pr = a.d.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
+          mv[j][i] = pr[D];
+          lv[j][i] = pr[D + 1];
+          ov[j][i] = pr[dd];
+        } else {
+          mv[j][i] = -INFINITY;
+          lv[j][i] = 0.0f;
+          ov[j][i] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float mb = M[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mb = fmaxf(mb, mv[j][i]);
+      if (mb == -INFINITY) continue;
+      const float f0 = exp2f(M[i] - mb);
+      O[i] *= f0;
+      L[i] *= f0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = exp2f(mv[j][i] - mb);
+        O[i] = fmaf(f, ov[j][i], O[i]);
+        L[i] = fmaf(f, lv[j][i], L[i]);
+      }
+      M[i] = mb;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    if (idx < G * D) obase[idx] = f32_to_bf16(L[i] > 0.0f ? O[i] / L[i] : 0.0f);
+  }
+}
+
+template <int D, int G, bool FP8, int NP>
+static void launch_fast_np(const DecodeArgs& a, int grid, hipStream_t st) {
+  // default: one 16-byte piece per lane (LPR = row bytes / 16, at most 16);
+  // DMS_DECODE_LPR=8 selects 32 bytes per lane for 256-byte rows
+  constexpr int RB = D * (FP8 ? 1 : 2);
+  constexpr int LPR1 = RB / 16 >= 16 ? 16 : RB / 16;
+  if constexpr (RB / 16 >= 16) {
+    if (a.lanes_per_row == 8) {
+      hipLaunchKernelGGL((decode_attn_fast_kernel<D, G, NP, FP8, 8>), dim3(grid), dim3(256), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_attn_fast_kernel<D, G, NP, FP8, LPR1>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int D, int G, bool FP8>
+static int launch_fast_dg(const DecodeArgs& a, int grid, int np, hipStream_t st) {
+  switch (np) {
+    case 2: launch_fast_np<D, G, FP8, 2>(a, grid, st); break;
+    case 4: launch_fast_np<D, G, FP8, 4>(a, grid, st); break;
+    case 6: launch_fast_np<D, G, FP8, 6>(a, grid, st); break;
+    default: launch_fast_np<D, G, FP8, 8>(a, grid, st); break;
+  }
+  hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.B * a.g.Hkv), dim3(256), 0, st, a);
+  return DMS_OK;
+}
+
+template <int D, bool FP8>
+static int launch_fast_d(const DecodeArgs& a, int grid, int np, hipStream_t st) {
+  switch (a.g.g) {
+    case 1: return launch_fast_dg<D, 1, FP8>(a, grid, np, st);
+    case 2: return launch_fast_dg<D, 2, FP8>(a, grid, np, st);
+    case 4: return launch_fast_dg<D, 4, FP8>(a, grid, np, st);
+    case 8: return launch_fast_dg<D, 8, FP8>(a, grid, np, st);
+    default: return fail(DMS_ERR_UNSUPPORTED, "group size");
+  }
+}
+
 template <typename ACT, int KV, int D, int G>
 static int launch_decode_dg(const DecodeArgs& a, int grid, hipStream_t st) {
   constexpr int NP = 4;
@@ -402,15 +941,26 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   const Geo& g = cache->geo;
   if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
-  DecodeArgs a{cache->dev, g, seq_ids, q, out, B};
+  DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr};
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
   int s;
-  switch (g.kv_dtype) {
-    case DMS_F32: s = launch_decode<float, DMS_F32>(a, grid, st); break;
-    case DMS_BF16: s = launch_decode<uint16_t, DMS_BF16>(a, grid, st); break;
-    case DMS_FP8_E4M3: s = launch_decode<uint16_t, DMS_FP8_E4M3>(a, grid, st); break;
-    default: return fail(DMS_ERR_UNSUPPORTED, "kv dtype");
+  // fast path: bf16/fp8 pages, D 64/128, power-of-two pages, page bytes addressable in 32 bits
+  const bool fast = (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) &&
+                    g.Pshift >= 0 && cache->layout.v_pages - cache->layout.k_pages < (1ull << 32) &&
+                    !cache->force_generic;
+  if (fast) {
+    const bool fp8 = g.kv_dtype == DMS_FP8_E4M3;
+    const int np = cache->decode_np > 0 ? cache->decode_np : 2;
+    if (g.D == 128) s = fp8 ? launch_fast_d<128, true>(a, grid, np, st) : launch_fast_d<128, false>(a, grid, np, st);
+    else s = fp8 ? launch_fast_d<64, true>(a, grid, np, st) : launch_fast_d<64, false>(a, grid, np, st);
+  } else {
+    switch (g.kv_dtype) {
+      case DMS_F32: s = launch_decode<float, DMS_F32>(a, grid, st); break;
+      case DMS_BF16: s = launch_decode<uint16_t, DMS_BF16>(a, grid, st); break;
+      case DMS_FP8_E4M3: s = launch_decode<uint16_t, DMS_FP8_E4M3>(a, grid, st); break;
+      default: return fail(DMS_ERR_UNSUPPORTED, "kv dtype");
+    }
   }
   if (s) return s;
   return check_hip(hipGetLastError(), "dms_decode_attn launch");

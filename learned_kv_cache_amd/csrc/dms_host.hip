@@ -62,7 +62,7 @@ int compute_layout(const dms_config& c, Layout* L) {
   L->chunk_slot = take(units * static_cast<size_t>(c.max_chunk) * sizeof(int32_t));
   L->chunk_info = take(units * 8 * sizeof(int32_t));
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
-  L->partial_records = kMaxDecodeGrid + kMaxUnits;
+  L->partial_records = 2 * kMaxDecodeGrid + kMaxUnits;
   L->partials = take(static_cast<size_t>(L->partial_records) * g * (D + 2) * sizeof(float));
   L->total = off;
   return DMS_OK;
@@ -266,6 +266,9 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   g.max_tokens = cfg->max_tokens_per_seq;
   g.max_chunk = cfg->max_chunk;
   g.kv_dtype = cfg->kv_dtype;
+  g.Pshift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == cfg->block_size) g.Pshift = sh;
   const float sc = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg->head_dim));
   g.scale_log2 = sc * 1.4426950408889634f;
   int dev = 0;
@@ -278,6 +281,12 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   int grid = 2 * cus;
   if (const char* e = std::getenv("DMS_DECODE_WGS")) grid = std::atoi(e);
   c->decode_grid = std::max(1, std::min(grid, kMaxDecodeGrid));
+  c->decode_np = 0;
+  if (const char* e = std::getenv("DMS_DECODE_NP")) c->decode_np = std::atoi(e);
+  c->decode_lpr = 0;
+  if (const char* e = std::getenv("DMS_DECODE_LPR")) c->decode_lpr = std::atoi(e);
+  const char* fg = std::getenv("DMS_DECODE_GENERIC");
+  c->force_generic = fg && fg[0] == '1';
   const int units = cfg->max_batch * cfg->num_kv_heads;
   hipLaunchKernelGGL(init_kernel, dim3(256), dim3(256), 0, as_stream(stream), c->dev, g, units);
   if ((s = check_hip(hipGetLastError(), "init_kernel launch"))) { delete c; return s; }

@@ -35,7 +35,7 @@ struct DevCache {
   int32_t* ctl;          // [kCtlWords]
   int32_t* chunk_slot;   // [Bmax*Hkv][max_chunk] slot of each chunk token
   int32_t* chunk_info;   // [Bmax*Hkv][8]
-  int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count
+  int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
   float* partials;       // decode split partials
 };
 
@@ -43,6 +43,7 @@ struct DevCache {
 struct Geo {
   int Bmax, Hq, Hkv, D, g, H, w, P, maxp, pool, max_tokens, max_chunk;
   int kv_dtype;
+  int Pshift;            // log2(P) when P is a power of two, else -1
   float scale_log2;      // softmax scale * log2(e)
 };
 
@@ -62,6 +63,9 @@ struct dms_cache {
   int device;
   int num_cus;
   int decode_grid;
+  int decode_np;
+  int decode_lpr;        // lanes per row of the decode kernel (DMS_DECODE_LPR; 0: default)         // passes in flight per round of the decode kernel (DMS_DECODE_NP; 0: default)
+  bool force_generic;    // DMS_DECODE_GENERIC=1: use the reference-layout decode kernels
 };
 
 namespace dms {

@@ -115,9 +115,12 @@ WORKLOADS = {w.name: w for w in (TINY, LLAMA1B_DECODE, QWEN8B_DECODE, QWEN8B_PRE
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                                  # finite inputs: no wrap-around
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:

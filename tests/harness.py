@@ -9,7 +9,9 @@ value comes from the HIP path.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 import sys
 import time
 from typing import Dict, List, Optional, Sequence
@@ -56,7 +58,9 @@ def prepare(wl: synth.Workload, run_id: int = 0, max_rounds: int = 50) -> Prepar
     d = synth.draw(wl, run_id)
     B, Hkv = wl.B, wl.Hkv
     pre = _pre_offset_linear if wl.decide == "linear" else _pre_offset_qneuron
-    u = [pre(d, b) for b in range(B)]
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:       # numpy releases the GIL
+        u = list(ex.map(lambda b: pre(d, b), range(B)))
     if wl.fixed_offset is not None:
         off = np.full(Hkv, wl.fixed_offset)
     else:
