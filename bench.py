@@ -8,8 +8,9 @@ every one of 36 layers (Qwen3-8B depth) is built separately, so one decode
 step streams ~1.7 GB of live K/V, far more than the 256 MB Infinity Cache.
 
 A step is one decode token for every sequence through all 36 layers: per layer
-dms_decide (RMSNorm + linear adapter + threshold) -> dms_append_evict
-(delayed eviction, in-place slot reuse) -> dms_decode_attn.  Steps are
+dms_decode_prepare (RMSNorm + linear adapter + threshold, then delayed
+eviction with in-place slot reuse, one launch) -> dms_decode_attn.
+(--unfused: dms_decide -> dms_append_evict -> dms_decode_attn.)  Steps are
 captured as HIP graphs and replayed; inputs (hidden states, Q, K, V of every
 step) are resident in HBM before the timed region.
 
@@ -127,11 +128,15 @@ def calibrate_and_fill(layer, wl, dms, torch):
         dms.dms_append_evict(layer.cache, None, k, v, ev, B, C)
 
 
-def decode_step(layers, s, wl, dms):
+def decode_step(layers, s, wl, dms, fused=True):
     B = wl.B
     for L in layers:
-        dms.dms_decide(L.cache, L.h_dec[s], L.gamma, L.W, None, L.off, None, B, 1, None, L.evict)
-        dms.dms_append_evict(L.cache, None, L.k_dec[s], L.v_dec[s], L.evict, B, 1)
+        if fused:
+            dms.dms_decode_prepare(L.cache, None, L.h_dec[s], L.gamma, L.W, None, L.off, None, L.k_dec[s],
+                                   L.v_dec[s], B, None, L.evict)
+        else:
+            dms.dms_decide(L.cache, L.h_dec[s], L.gamma, L.W, None, L.off, None, B, 1, None, L.evict)
+            dms.dms_append_evict(L.cache, None, L.k_dec[s], L.v_dec[s], L.evict, B, 1)
         dms.dms_decode_attn(L.cache, None, L.q_dec[s], L.out, B)
 
 
@@ -165,7 +170,7 @@ def run_decode(args, dms, synth, torch):
         for s in range(S):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                decode_step(layers, s, wl, dms)
+                decode_step(layers, s, wl, dms, fused=not args.unfused)
             graphs.append(g)
         torch.cuda.synchronize()
         log(f"captured {S} step graphs")
@@ -174,7 +179,7 @@ def run_decode(args, dms, synth, torch):
         if graphs:
             graphs[s].replay()
         else:
-            decode_step(layers, s, wl, dms)
+            decode_step(layers, s, wl, dms, fused=not args.unfused)
 
     for s in range(args.warmup):
         step(s)
@@ -361,6 +366,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying graphs")
+    ap.add_argument("--unfused", action="store_true", help="separate decide and append launches")
     ap.add_argument("--cpu-steps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -401,7 +407,8 @@ def main() -> int:
             "workload": "qwen3-8b_layer_ctx8k_b8_decode",
             "layers": args.layers, "batch": 8, "ctx": 8192, "hidden": 4096, "q_heads": 32, "kv_heads": 8,
             "head_dim": 128, "window": 512, "block": 256, "evict_fraction": [0.85, 0.92],
-            "step": "per layer: dms_decide -> dms_append_evict -> dms_decode_attn",
+            "step": ("per layer: dms_decide -> dms_append_evict -> dms_decode_attn" if args.unfused else
+                     "per layer: dms_decode_prepare (decide + append) -> dms_decode_attn"),
             "graphs": dec["graphs"], "parallelism": "none (1 GPU)",
         },
         "roofline": {

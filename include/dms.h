@@ -181,6 +181,20 @@ int dms_append_evict(dms_cache* cache, const int32_t* seq_ids, const void* k, co
                      const uint8_t* evict, int B, int T, void* stream);
 
 /*
+ * One decode token per row: the decision (dms_decide with T = 1) followed by
+ * the append (dms_append_evict with T = 1) of the same tokens, in one call, so
+ * a layer's decode step is dms_decode_prepare -> dms_decode_attn.  Results are
+ * identical to calling the two functions in turn.
+ * hidden [B][H] (LINEAR) or q_inout [B][Hq][D] (QNEURON, neuron zeroed in
+ * place); k, v [B][Hkv][D]; logits_out [B][Hkv] (may be NULL), evict_out
+ * [B][Hkv] u8 (written, then read by the append).  B <= max_batch.
+ * Device-side errors as in dms_append_evict.
+ */
+int dms_decode_prepare(dms_cache* cache, const int32_t* seq_ids, const void* hidden, const float* rms_gamma,
+                       const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,
+                       const void* v, int B, float* logits_out, uint8_t* evict_out, void* stream);
+
+/*
  * Decode attention (walkthrough, 推理模式: attention over the per-head paged
  * cache).  For each row b and query head h (KV head h / g):
  *   out[b][h] = softmax_s(scale * <q[b][h], K_s>) V_s over all live slots s of

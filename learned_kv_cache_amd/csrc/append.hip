@@ -26,7 +26,18 @@ struct AppendArgs {
   const uint8_t* evict;
   int B;
   int T;
+  // decode append finishing a split decision (dec_partials) instead of reading flags
+  int from_partials;
+  const float* bias;
+  const float* offsets;
+  float alpha, eps;
+  int per_layer, disable;
+  float* logits_out;
+  uint8_t* evict_out;
 };
+
+bool launch_decide_split(const dms_cache* c, const void* hidden, const float* gamma, const float* W, int B,
+                         hipStream_t st);
 
 // Stores one row of D activations as kv-dtype page bytes (fp8: with scale s).
 template <typename ACT, int KV>
@@ -54,85 +65,177 @@ __device__ __forceinline__ float row_amax(const ACT* src, int D, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode append (T = 1): one workgroup of 1024 threads; pairs (row, KV head)
-// in rounds of up to 1024.  One thread per pair decides the slot; CPP threads
-// per pair copy its K and V rows, whose input values are loaded at the start
-// of the round so the copy does not wait on the slot decision's loads.  The
-// dependent loads are: position -> ring entry -> page (free stack or table).
-template <typename ACT, int KV>
-__device__ __forceinline__ void copy_part(uint8_t* pages, int64_t dst_row, int D, int e0, int ne, const float* x,
-                                          float inv_scale) {
-  for (int i = 0; i < ne; ++i) {
-    const int e = e0 + i;
-    if (KV == DMS_F32) reinterpret_cast<float*>(pages)[dst_row * D + e] = x[i];
-    else if (KV == DMS_BF16) reinterpret_cast<uint16_t*>(pages)[dst_row * D + e] = f32_to_bf16(x[i]);
-    else pages[dst_row * D + e] = f32_to_e4m3(x[i] * inv_scale);
+// Decode append (T = 1): one workgroup of 512 threads; pairs (row, KV head)
+// in rounds of up to 512.
+//
+// Latency, not bandwidth, sets the cost of this step, so the loads the slot
+// decision waits on are issued first (position, length, the page of the
+// head's last slot, the flag), then the ring entry of position t - w (it
+// carries the slot and its flat page row, so an in-place overwrite needs no
+// page-table lookup), then the K/V rows as 16-byte pieces.  Only a head that
+// opens a page reads the free stack.  Cross-lane reductions use DPP.
+
+constexpr int kAppThreads = 512;
+constexpr int kAppPieces = 4;       // prefetched 16-byte pieces of K (and V) per thread
+
+template <int LPR>
+__device__ __forceinline__ float row_max_dyn_helper(float x) { return row_max_dpp<LPR>(x); }
+
+__device__ __forceinline__ float piece_row_max(float x, int ppr) {
+  switch (ppr) {
+    case 2: return row_max_dpp<2>(x);
+    case 4: return row_max_dpp<4>(x);
+    case 8: return row_max_dpp<8>(x);
+    case 16: return row_max_dpp<16>(x);
+    default: return x;
   }
 }
 
+// 16 input bytes (8 bf16 or 4 f32) -> page bytes at dst (fp8: 8 or 4 bytes)
 template <typename ACT, int KV>
-__global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
-  constexpr int MAXE = 16;                  // elements per thread in the copy (D <= 128, CPP >= 8)
-  __shared__ int s_wave[16];
-  __shared__ int s_dst[1024];               // destination row (page * P + offset), -1: nothing to write
-  __shared__ int s_page[1024];
-  __shared__ uint8_t s_new[1024];
+__device__ __forceinline__ void store_piece(uint8_t* pages, int64_t row, int row_bytes, int piece, const uint4& x,
+                                            float inv_scale) {
+  if (KV == DMS_FP8_E4M3) {
+    constexpr int N = 16 / sizeof(ACT);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    float f[N];
+    if (sizeof(ACT) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) f[i] = __uint_as_float(w[i]);
+    }
+    uint8_t* dst = pages + row * row_bytes + piece * N;
+    if (N == 8) {
+      uint2 o;
+      o.x = f32_to_e4m3(f[0] * inv_scale) | (f32_to_e4m3(f[1] * inv_scale) << 8) |
+            (f32_to_e4m3(f[2] * inv_scale) << 16) | (static_cast<uint32_t>(f32_to_e4m3(f[3] * inv_scale)) << 24);
+      o.y = f32_to_e4m3(f[4] * inv_scale) | (f32_to_e4m3(f[5] * inv_scale) << 8) |
+            (f32_to_e4m3(f[6] * inv_scale) << 16) | (static_cast<uint32_t>(f32_to_e4m3(f[7] * inv_scale)) << 24);
+      *reinterpret_cast<uint2*>(dst) = o;
+    } else {
+      for (int i = 0; i < N; ++i) dst[i] = f32_to_e4m3(f[i] * inv_scale);
+    }
+  } else {
+    // same element type in and out: a raw copy
+    *reinterpret_cast<uint4*>(pages + row * row_bytes + piece * 16) = x;
+  }
+}
+
+__device__ __forceinline__ float piece_amax(const uint4& x, bool bf16) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (bf16) {
+      m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    } else {
+      m = fmaxf(m, fabsf(__uint_as_float(w[i])));
+    }
+  }
+  return m;
+}
+
+template <typename ACT, int KV>
+__global__ __launch_bounds__(kAppThreads) void append_decode_kernel(AppendArgs a) {
+  constexpr int NW = kAppThreads / 64;
+  __shared__ int s_wave[NW];
+  __shared__ int s_dst[kAppThreads];
+  __shared__ int s_page[kAppThreads];
+  __shared__ uint8_t s_new[kAppThreads];
   __shared__ int s_free, s_used;
   const DevCache& d = a.d;
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int npairs = a.B * g.Hkv;
+  const int in_row_bytes = g.D * static_cast<int>(sizeof(ACT));
+  const int ppr = in_row_bytes / 16;                       // 16-byte pieces per row
+  const int page_row_bytes = g.D * (KV == DMS_F32 ? 4 : (KV == DMS_BF16 ? 2 : 1));
   if (tid == 0) {
     s_free = d.ctl[kCtlFreeCount];
     s_used = 0;
   }
-  for (int p0 = 0; p0 < npairs; p0 += 1024) {
-    const int nround = min(1024, npairs - p0);
-    // copy geometry of this round: CPP threads per pair, ne elements each
-    int cpp = 1024 / nround;
-    cpp = cpp >= 64 ? 64 : (cpp >= 32 ? 32 : (cpp >= 16 ? 16 : (cpp >= 8 ? 8 : (cpp >= 4 ? 4 : (cpp >= 2 ? 2 : 1)))));
-    while (cpp > 1 && (g.D % cpp != 0 || g.D / cpp < 2)) cpp >>= 1;
-    const int ne_max = g.D / cpp;
-    const int cpair = tid / cpp, cpart = tid % cpp;
-    const bool copier = cpair < nround && ne_max <= MAXE;
-    float kx[MAXE], vx[MAXE];
-    if (copier) {
-      const size_t src = static_cast<size_t>(p0 + cpair) * g.D + cpart * ne_max;   // [B][1][Hkv][D]
-      const ACT* ks = static_cast<const ACT*>(a.k) + src;
-      const ACT* vs = static_cast<const ACT*>(a.v) + src;
-#pragma unroll
-      for (int i = 0; i < MAXE; ++i) {
-        kx[i] = i < ne_max ? load_act<ACT>(ks, i) : 0.0f;
-        vx[i] = i < ne_max ? load_act<ACT>(vs, i) : 0.0f;
-      }
-    }
+  for (int p0 = 0; p0 < npairs; p0 += kAppThreads) {
+    const int nround = min(kAppThreads, npairs - p0);
+    // 1. what the slot decision waits on
     const int p = p0 + tid;
-    bool valid = false, need = false, overwrite = false;
-    int kh = 0, t = 0, slot = 0, e = 0, unit = 0;
+    int seq = -1, t = 0, len = 0, cur = -1, e = 0, unit = 0;
     if (p < npairs) {
       const int row = p / g.Hkv;
-      kh = p % g.Hkv;
-      const int seq = a.seq_ids ? a.seq_ids[row] : row;
+      seq = a.seq_ids ? a.seq_ids[row] : row;
+      if (seq >= 0 && seq < g.Bmax) {
+        unit = seq * g.Hkv + p % g.Hkv;
+        t = d.pos[seq];
+        len = d.lengths[unit];
+        cur = d.cur_page[unit];
+      }
+      if (a.from_partials) {
+        // finish the decision of (row, head): add the hidden-dimension splits
+        const int kh = p % g.Hkv, kk = a.per_layer ? 0 : kh;
+        const int ns = g.H / kDecSplit;
+        const float* pp = d.dec_partials + static_cast<size_t>(row) * kDecSplitsMax * 17;
+        float ss = 0.0f, dk = 0.0f;
+        for (int sp = 0; sp < ns; ++sp) {
+          ss += pp[sp * 17 + g.Hkv];
+          dk += pp[sp * 17 + kk];
+        }
+        const float r = 1.0f / sqrtf(ss / static_cast<float>(g.H) + a.eps);
+        float z = r * dk;
+        if (a.bias) z += a.bias[kk];
+        const float lg = a.alpha * z - a.offsets[kk];
+        if (a.logits_out) a.logits_out[p] = lg;
+        e = (!a.disable && lg > 0.0f) ? 1 : 0;
+        a.evict_out[p] = static_cast<uint8_t>(e);
+      } else if (seq >= 0 && seq < g.Bmax) {
+        e = a.evict[p] ? 1 : 0;
+      }
+    }
+    // 2. K/V pieces of this round (used after the decision)
+    const int npieces = nround * ppr;
+    uint4 kpc[kAppPieces], vpc[kAppPieces];
+#pragma unroll
+    for (int i = 0; i < kAppPieces; ++i) {
+      const int pc = tid + i * kAppThreads;
+      if (pc < npieces) {
+        const uint8_t* src = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(p0) * in_row_bytes;
+        kpc[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(pc) * 16);
+        vpc[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v) +
+                                                 static_cast<size_t>(p0) * in_row_bytes + static_cast<size_t>(pc) * 16);
+      } else {
+        kpc[i] = make_uint4(0, 0, 0, 0);
+        vpc[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    // 3. the slot
+    bool valid = false, need = false, overwrite = false;
+    int slot = 0, page = -1, dst = -1;
+    if (p < npairs) {
       if (seq < 0 || seq >= g.Bmax) {
         set_status(d.ctl, DMS_DEV_BAD_SEQ);
+      } else if (t + 1 > g.max_tokens) {
+        set_status(d.ctl, DMS_DEV_CAPACITY);
       } else {
-        unit = seq * g.Hkv + kh;
-        t = d.pos[seq];
-        const int len = d.lengths[unit];
-        e = a.evict[p] ? 1 : 0;
-        if (t + 1 > g.max_tokens) {
-          set_status(d.ctl, DMS_DEV_CAPACITY);
-        } else {
-          const int rv = (t >= g.w) ? d.ring[static_cast<int64_t>(unit) * g.w + t % g.w] : 0;
-          if (t >= g.w && rv < 0) {
+        if (t >= g.w) {
+          const int64_t ri = static_cast<int64_t>(unit) * g.w + t % g.w;
+          const int rv = d.ring[ri];
+          if (rv < 0) {
             overwrite = true;
             slot = rv & 0x7FFFFFFF;
-          } else {
-            slot = len;
-            need = (slot % g.P) == 0;
+            dst = d.ring_row[ri];
+            page = dst / g.P;
           }
-          valid = true;
         }
+        if (!overwrite) {
+          slot = len;
+          need = (slot % g.P) == 0;
+          page = need ? -1 : cur;
+        }
+        valid = true;
       }
     }
     int wtot;
@@ -140,61 +243,65 @@ __global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
     if (lane == 0) s_wave[wave] = wtot;
     __syncthreads();
     int off = 0, round_total = 0;
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NW; ++i) {
       if (i < wave) off += s_wave[i];
       round_total += s_wave[i];
     }
-    int page = -1;
-    if (valid) {
-      int32_t* pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
-      if (need) {
-        const int R = s_used + off + wr;
-        if (R < s_free) {
-          page = d.free_stack[s_free - 1 - R];
-          pt[slot / g.P] = page;
-        } else {
-          set_status(d.ctl, DMS_DEV_POOL_EXHAUSTED);
-          valid = false;
-        }
+    if (valid && need) {
+      const int R = s_used + off + wr;
+      if (R < s_free) {
+        page = d.free_stack[s_free - 1 - R];
+        d.page_table[static_cast<int64_t>(unit) * g.maxp + slot / g.P] = page;
+        d.cur_page[unit] = page;
       } else {
-        page = pt[slot / g.P];
+        set_status(d.ctl, DMS_DEV_POOL_EXHAUSTED);
+        valid = false;
       }
     }
     if (valid) {
+      if (!overwrite) dst = page * g.P + slot % g.P;
       if (!overwrite) d.lengths[unit] = slot + 1;
       d.ring[static_cast<int64_t>(unit) * g.w + t % g.w] = slot | (e << 31);
-      d.slot_meta[static_cast<int64_t>(page) * g.P + slot % g.P] = t | (e << 31);
+      d.ring_row[static_cast<int64_t>(unit) * g.w + t % g.w] = dst;
+      d.slot_meta[dst] = t | (e << 31);
     }
     if (tid < nround) {
-      s_dst[tid] = valid ? page * g.P + slot % g.P : -1;
+      s_dst[tid] = valid ? dst : -1;
       s_page[tid] = page;
       s_new[tid] = (valid && need) ? 1 : 0;
     }
     __syncthreads();
-    if (cpair < nround) {
-      const int dst = s_dst[cpair];
-      const size_t src = static_cast<size_t>(p0 + cpair) * g.D + cpart * ne_max;
-      const ACT* ks = static_cast<const ACT*>(a.k) + src;
-      const ACT* vs = static_cast<const ACT*>(a.v) + src;
+    // 4. copy: piece pc belongs to pair pc / ppr (pieces of a row are adjacent lanes)
+    for (int i = 0; i * kAppThreads < npieces; ++i) {
+      const int pc = tid + i * kAppThreads;
+      const bool have = pc < npieces;
+      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+      if (have) {
+        if (i < kAppPieces) {
+          kx = kpc[i < kAppPieces ? i : 0];
+          vx = vpc[i < kAppPieces ? i : 0];
+        } else {
+          kx = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + static_cast<size_t>(p0) * in_row_bytes +
+                                               static_cast<size_t>(pc) * 16);
+          vx = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v) + static_cast<size_t>(p0) * in_row_bytes +
+                                               static_cast<size_t>(pc) * 16);
+        }
+      }
+      const int pr = have ? pc / ppr : 0;
+      const int piece = have ? pc % ppr : 0;
+      const int dsti = have ? s_dst[pr] : -1;
       float inv_k = 1.0f, inv_v = 1.0f;
       if (KV == DMS_FP8_E4M3) {
-        // amax over the row's cpp threads (contiguous lanes of one wave)
-        float mk = 0.0f, mv = 0.0f;
-        for (int i = 0; i < ne_max; ++i) {
-          mk = fmaxf(mk, fabsf(copier ? kx[i < MAXE ? i : 0] : load_act<ACT>(ks, i)));
-          mv = fmaxf(mv, fabsf(copier ? vx[i < MAXE ? i : 0] : load_act<ACT>(vs, i)));
-        }
-        for (int o = 1; o < cpp; o <<= 1) {
-          mk = fmaxf(mk, __shfl_xor(mk, o));
-          mv = fmaxf(mv, __shfl_xor(mv, o));
-        }
-        if (dst >= 0) {
-          const int pg = s_page[cpair];
+        // row amax over the row's ppr lanes (one DPP row or part of it)
+        const float mk = piece_row_max(piece_amax(kx, sizeof(ACT) == 2), ppr);
+        const float mv = piece_row_max(piece_amax(vx, sizeof(ACT) == 2), ppr);
+        if (dsti >= 0) {
+          const int pg = s_page[pr];
           float sk, sv;
-          if (s_new[cpair]) {
+          if (s_new[pr]) {
             sk = page_scale_from_amax(mk);
             sv = page_scale_from_amax(mv);
-            if (cpart == 0) {
+            if (piece == 0) {
               d.scales[2 * pg] = sk;
               d.scales[2 * pg + 1] = sv;
             }
@@ -206,23 +313,9 @@ __global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
           inv_v = 1.0f / sv;
         }
       }
-      if (dst >= 0) {
-        if (copier) {
-          copy_part<ACT, KV>(d.k_pages, dst, g.D, cpart * ne_max, ne_max, kx, inv_k);
-          copy_part<ACT, KV>(d.v_pages, dst, g.D, cpart * ne_max, ne_max, vx, inv_v);
-        } else {
-          // rows split over few threads: copy in pieces of MAXE elements
-          for (int i0 = 0; i0 < ne_max; i0 += MAXE) {
-            const int n = min(MAXE, ne_max - i0);
-            float tk[MAXE], tv[MAXE];
-            for (int i = 0; i < n; ++i) {
-              tk[i] = load_act<ACT>(ks, i0 + i);
-              tv[i] = load_act<ACT>(vs, i0 + i);
-            }
-            copy_part<ACT, KV>(d.k_pages, dst, g.D, cpart * ne_max + i0, n, tk, inv_k);
-            copy_part<ACT, KV>(d.v_pages, dst, g.D, cpart * ne_max + i0, n, tv, inv_v);
-          }
-        }
+      if (dsti >= 0) {
+        store_piece<ACT, KV>(d.k_pages, dsti, page_row_bytes, piece, kx, inv_k);
+        store_piece<ACT, KV>(d.v_pages, dsti, page_row_bytes, piece, vx, inv_v);
       }
     }
     __syncthreads();
@@ -230,7 +323,7 @@ __global__ __launch_bounds__(1024) void append_decode_kernel(AppendArgs a) {
     __syncthreads();
   }
   // positions advance after every pair has read them
-  for (int row = tid; row < a.B; row += 1024) {
+  for (int row = tid; row < a.B; row += kAppThreads) {
     const int seq = a.seq_ids ? a.seq_ids[row] : row;
     if (seq >= 0 && seq < g.Bmax && d.pos[seq] + 1 <= g.max_tokens) d.pos[seq] += 1;
   }
@@ -373,6 +466,8 @@ __global__ __launch_bounds__(1024) void chunk_alloc_kernel(AppendArgs a) {
           d.page_amax[2 * page + 1] = 0u;
         }
         d.lengths[unit] = info[2] + info[3];
+        const int Lnew = info[2] + info[3];
+        if (Lnew > 0) d.cur_page[unit] = need > 0 ? d.free_stack[s_free - 1 - (R0 + need - 1)] : pt[(Lnew - 1) / g.P];
         if (kh == 0) d.pos[seq] = info[1] + a.T;
       } else {
         set_status(d.ctl, DMS_DEV_POOL_EXHAUSTED);
@@ -433,10 +528,13 @@ __global__ __launch_bounds__(kTokPerWG * 64) void chunk_write_kernel(AppendArgs 
   const int e = ev[tt] ? 1 : 0;
   const int slot = d.chunk_slot[static_cast<int64_t>(pair) * g.max_chunk + tt];
   const int t = info[1] + tt;
-  if (lane == 0 && tt >= a.T - g.w) d.ring[static_cast<int64_t>(unit) * g.w + t % g.w] = slot | (e << 31);
-  if (e && tt + g.w < a.T) return;                  // not the final occupant of its slot
   const int page = d.page_table[static_cast<int64_t>(unit) * g.maxp + slot / g.P];
   const int64_t dst = static_cast<int64_t>(page) * g.P + slot % g.P;
+  if (lane == 0 && tt >= a.T - g.w) {
+    d.ring[static_cast<int64_t>(unit) * g.w + t % g.w] = slot | (e << 31);
+    d.ring_row[static_cast<int64_t>(unit) * g.w + t % g.w] = static_cast<int32_t>(dst);
+  }
+  if (e && tt + g.w < a.T) return;                  // not the final occupant of its slot
   if (lane == 0) d.slot_meta[dst] = t | (e << 31);
   const size_t src = ((static_cast<size_t>(row) * a.T + tt) * g.Hkv + kh) * g.D;
   float inv_k = 1.0f, inv_v = 1.0f;
@@ -463,7 +561,7 @@ __global__ __launch_bounds__(kTokPerWG * 64) void chunk_write_kernel(AppendArgs 
 template <typename ACT, int KV>
 static void launch_append(const AppendArgs& a, hipStream_t st) {
   if (a.T == 1) {
-    hipLaunchKernelGGL((append_decode_kernel<ACT, KV>), dim3(1), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL((append_decode_kernel<ACT, KV>), dim3(1), dim3(kAppThreads), 0, st, a);
     return;
   }
   const int npairs = a.B * a.g.Hkv;
@@ -486,7 +584,15 @@ extern "C" int dms_append_evict(dms_cache* cache, const int32_t* seq_ids, const 
   if (B <= 0 || T <= 0) return fail(DMS_ERR_ARG, "B and T must be positive");
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
   if (T > g.max_chunk) return fail(DMS_ERR_CAPACITY, "T above max_chunk");
-  AppendArgs a{cache->dev, g, seq_ids, k, v, evict, B, T};
+  AppendArgs a{};
+  a.d = cache->dev;
+  a.g = g;
+  a.seq_ids = seq_ids;
+  a.k = k;
+  a.v = v;
+  a.evict = evict;
+  a.B = B;
+  a.T = T;
   hipStream_t st = as_stream(stream);
   switch (g.kv_dtype) {
     case DMS_F32: launch_append<float, DMS_F32>(a, st); break;
@@ -495,4 +601,52 @@ extern "C" int dms_append_evict(dms_cache* cache, const int32_t* seq_ids, const 
     default: return fail(DMS_ERR_UNSUPPORTED, "kv dtype");
   }
   return check_hip(hipGetLastError(), "dms_append_evict launch");
+}
+
+extern "C" int dms_decode_prepare(dms_cache* cache, const int32_t* seq_ids, const void* hidden,
+                                  const float* rms_gamma, const float* W, const float* bias, const float* offsets,
+                                  void* q_inout, const void* k, const void* v, int B, float* logits_out,
+                                  uint8_t* evict_out, void* stream) {
+  if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
+  const dms_config& c = cache->cfg;
+  const Geo& g = cache->geo;
+  if (!k || !v || !offsets || !evict_out) return fail(DMS_ERR_ARG, "k, v, offsets and evict_out are required");
+  if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
+  if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
+  hipStream_t st = as_stream(stream);
+  if (c.decide_mode == DMS_DECIDE_LINEAR) {
+    if (!hidden || !rms_gamma || !W) return fail(DMS_ERR_ARG, "hidden, rms_gamma and W are required");
+    // the hidden dimension split over H / 512 workgroups per token; the
+    // append kernel adds the splits and finishes the logits
+    if (launch_decide_split(cache, hidden, rms_gamma, W, B, st)) {
+      AppendArgs a{};
+      a.d = cache->dev;
+      a.g = g;
+      a.seq_ids = seq_ids;
+      a.k = k;
+      a.v = v;
+      a.evict = nullptr;
+      a.B = B;
+      a.T = 1;
+      a.from_partials = 1;
+      a.bias = bias;
+      a.offsets = offsets;
+      a.alpha = c.alpha_scale;
+      a.eps = c.rms_eps;
+      a.per_layer = c.alpha_per == DMS_ALPHA_PER_LAYER;
+      a.disable = c.disable_eviction != 0;
+      a.logits_out = logits_out;
+      a.evict_out = evict_out;
+      switch (g.kv_dtype) {
+        case DMS_BF16: hipLaunchKernelGGL((append_decode_kernel<uint16_t, DMS_BF16>), dim3(1), dim3(kAppThreads), 0, st, a); break;
+        case DMS_FP8_E4M3: hipLaunchKernelGGL((append_decode_kernel<uint16_t, DMS_FP8_E4M3>), dim3(1), dim3(kAppThreads), 0, st, a); break;
+        default: return fail(DMS_ERR_UNSUPPORTED, "kv dtype");
+      }
+      return check_hip(hipGetLastError(), "dms_decode_prepare launch");
+    }
+  }
+  // other shapes and the query-neuron decision: decide, then append
+  int s = dms_decide(cache, hidden, rms_gamma, W, bias, offsets, q_inout, B, 1, logits_out, evict_out, stream);
+  if (s) return s;
+  return dms_append_evict(cache, seq_ids, k, v, evict_out, B, 1, stream);
 }

@@ -129,6 +129,132 @@ __global__ __launch_bounds__(256) void decide_linear_kernel(DecideArgs a) {
   }
 }
 
+// One token per 256-thread workgroup, bf16 hidden states with H a multiple
+// of 16: thread t owns elements [16t + 4096i, 16t + 4096i + 16); its loads
+// (two 16-byte pieces of h, gamma and the W rows) are all in flight at once;
+// the Hkv + 1 sums reduce with DPP, then across the four waves through LDS.
+template <int HKV>
+__global__ __launch_bounds__(256) void decide_linear_tok_kernel(DecideArgs a) {
+  __shared__ float s_red[4][HKV + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok = blockIdx.x;
+  const uint16_t* h = static_cast<const uint16_t*>(a.hidden) + static_cast<size_t>(tok) * a.H;
+  float acc[HKV + 1];
+#pragma unroll
+  for (int k = 0; k <= HKV; ++k) acc[k] = 0.0f;
+  for (int m = 16 * tid; m < a.H; m += 4096) {
+    const uint4 h0 = *reinterpret_cast<const uint4*>(h + m);
+    const uint4 h1 = *reinterpret_cast<const uint4*>(h + m + 8);
+    float4 gm[4];
+    float4 w[HKV][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      gm[c] = *reinterpret_cast<const float4*>(a.gamma + m + 4 * c);
+#pragma unroll
+      for (int k = 0; k < HKV; ++k) w[k][c] = *reinterpret_cast<const float4*>(a.W + static_cast<size_t>(k) * a.H + m + 4 * c);
+    }
+    const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(hw[i] << 16);
+      x[2 * i + 1] = __uint_as_float(hw[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float gx[4] = {gm[c].x * x[4 * c], gm[c].y * x[4 * c + 1], gm[c].z * x[4 * c + 2], gm[c].w * x[4 * c + 3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[HKV] = fmaf(x[4 * c + e], x[4 * c + e], acc[HKV]);
+#pragma unroll
+      for (int k = 0; k < HKV; ++k) {
+        acc[k] = fmaf(w[k][c].x, gx[0], acc[k]);
+        acc[k] = fmaf(w[k][c].y, gx[1], acc[k]);
+        acc[k] = fmaf(w[k][c].z, gx[2], acc[k]);
+        acc[k] = fmaf(w[k][c].w, gx[3], acc[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k <= HKV; ++k) acc[k] = wave_sum_dpp(acc[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k <= HKV; ++k) s_red[wave][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid >= HKV) return;
+  const float ss = s_red[0][HKV] + s_red[1][HKV] + s_red[2][HKV] + s_red[3][HKV];
+  const float r = 1.0f / sqrtf(ss / static_cast<float>(a.H) + a.eps);
+  auto logit = [&](int k) {
+    float z = r * (s_red[0][k] + s_red[1][k] + s_red[2][k] + s_red[3][k]);
+    if (a.bias) z += a.bias[k];
+    return a.alpha * z - a.offsets[k];
+  };
+  const int k = tid;
+  const float lg = a.per_layer ? logit(0) : logit(k);
+  const int b = tok / a.T, t = tok % a.T;
+  const size_t o = (static_cast<size_t>(b) * HKV + k) * a.T + t;
+  if (a.logits) a.logits[o] = lg;
+  a.evict[o] = (!a.disable && lg > 0.0f) ? 1 : 0;
+}
+
+// Split decode decision: workgroup (s, token) sums over hidden elements
+// [512 s, 512 s + 512): sum(h^2) and, per head, sum(W_k * gamma * h), written
+// to dec_partials[token][s][0..HKV]; the append kernel adds the splits and
+// finishes r, z and the logit.  Thread t owns two elements.
+template <int HKV>
+__global__ __launch_bounds__(256) void decide_split_kernel(const uint16_t* __restrict__ hidden,
+                                                           const float* __restrict__ gamma,
+                                                           const float* __restrict__ W, int H,
+                                                           float* __restrict__ part) {
+  __shared__ float s_red[4][HKV + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sp = blockIdx.x, tok = blockIdx.y;
+  const int m = sp * kDecSplit + 2 * tid;
+  const uint32_t hw = *reinterpret_cast<const uint32_t*>(hidden + static_cast<size_t>(tok) * H + m);
+  const float2 gm = *reinterpret_cast<const float2*>(gamma + m);
+  float2 w[HKV];
+#pragma unroll
+  for (int k = 0; k < HKV; ++k) w[k] = *reinterpret_cast<const float2*>(W + static_cast<size_t>(k) * H + m);
+  const float x0 = __uint_as_float(hw << 16), x1 = __uint_as_float(hw & 0xFFFF0000u);
+  const float g0 = gm.x * x0, g1 = gm.y * x1;
+  float acc[HKV + 1];
+  acc[HKV] = fmaf(x0, x0, x1 * x1);
+#pragma unroll
+  for (int k = 0; k < HKV; ++k) acc[k] = fmaf(w[k].x, g0, w[k].y * g1);
+#pragma unroll
+  for (int k = 0; k <= HKV; ++k) acc[k] = wave_sum_dpp(acc[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k <= HKV; ++k) s_red[wave][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid <= HKV)
+    part[(static_cast<size_t>(tok) * kDecSplitsMax + sp) * 17 + tid] =
+        s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+}
+
+// Launches the split decision of B tokens (bf16 hidden, H a multiple of 512,
+// Hkv <= 16); returns false when the shape does not qualify.
+bool launch_decide_split(const dms_cache* c, const void* hidden, const float* gamma, const float* W, int B,
+                         hipStream_t st) {
+  const Geo& g = c->geo;
+  if (g.kv_dtype == DMS_F32 || g.H % kDecSplit != 0 || g.H / kDecSplit > kDecSplitsMax) return false;
+  if ((reinterpret_cast<uintptr_t>(hidden) % 4) || (reinterpret_cast<uintptr_t>(gamma) % 8) ||
+      (reinterpret_cast<uintptr_t>(W) % 8))
+    return false;
+  const dim3 grid(g.H / kDecSplit, B);
+  const uint16_t* h = static_cast<const uint16_t*>(hidden);
+  switch (g.Hkv) {
+    case 1: hipLaunchKernelGGL(decide_split_kernel<1>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
+    case 2: hipLaunchKernelGGL(decide_split_kernel<2>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
+    case 4: hipLaunchKernelGGL(decide_split_kernel<4>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
+    case 8: hipLaunchKernelGGL(decide_split_kernel<8>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
+    case 16: hipLaunchKernelGGL(decide_split_kernel<16>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
+    default: return false;
+  }
+  return true;
+}
+
 struct QneuronArgs {
   void* q;             // [B][T][Hq][D]
   const float* offsets;
@@ -162,7 +288,10 @@ static void launch_linear_h(const DecideArgs& a, hipStream_t st) {
   // few tokens (decode): one token per workgroup, all loads of a thread in
   // flight at once; many tokens (prefill chunks): 4 tokens share W registers
   if (a.ntok <= 512) {
-    hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 1, (HKV <= 8 ? 4 : 2)>), dim3(a.ntok), dim3(256), 0, st, a);
+    if (sizeof(ACT) == 2 && HKV <= 8 && a.H % 16 == 0)
+      hipLaunchKernelGGL((decide_linear_tok_kernel<HKV <= 8 ? HKV : 8>), dim3(a.ntok), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 1, (HKV <= 8 ? 4 : 2)>), dim3(a.ntok), dim3(256), 0, st, a);
   } else {
     constexpr int NCH = HKV <= 8 ? 2 : 1;
     hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 4, NCH>), dim3((a.ntok + 3) / 4), dim3(256), 0, st, a);

@@ -413,11 +413,10 @@ __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
+// Max over all row groups of the wave (x uniform within each group), returned to every lane.
 template <int LPR>
 __device__ __forceinline__ float cross_rows_max(float x) {
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  return lane63(rows_max_to_last(fold_groups_max<LPR>(x)));
 }
 
 // K/V rows of NP passes held in registers (one 16-byte piece or more per lane per row).
@@ -443,7 +442,12 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
   for (int p = 0; p < NP; ++p) {
     const int r = lo + (pass0 + p) * RPP + wave * RG + lane_row;
     const bool ok = r < hi;
-    c.pg[p] = __shfl(pt_reg, ok ? (r >> psh) - first_page : 0);
+    // a wave's RG rows of a pass span at most two pages: read both entries
+    // from the lanes holding them (uniform lane indices, no LDS crossbar)
+    const int rf = lo + (pass0 + p) * RPP + wave * RG;
+    const int pf = __builtin_amdgcn_readlane(pt_reg, min((rf >> psh) - first_page, 63));
+    const int pl = __builtin_amdgcn_readlane(pt_reg, min(((rf + RG - 1) >> psh) - first_page, 63));
+    c.pg[p] = ok ? (((r >> psh) == (rf >> psh)) ? pf : pl) : 0;
     const uint32_t off = (static_cast<uint32_t>(c.pg[p]) * static_cast<uint32_t>(pmask + 1) +
                           static_cast<uint32_t>(r & pmask)) * static_cast<uint32_t>(RB) +
                          static_cast<uint32_t>(lane_col * BPL);
@@ -585,8 +589,8 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
 
   __shared__ int s_start[kMaxUnits + 1];
   __shared__ int s_tmp[4];
-  __shared__ float s_o[4][G][D];
-  __shared__ float s_ml[4][G][2];
+  __shared__ float s_o[4][4][G][D];             // [wave][DPP row][head][dim]
+  __shared__ float s_ml[4][4][G][2];            // m (row 0 only) and l per row
 
   const DevCache& d = a.d;
   const Geo& g = a.g;
@@ -729,29 +733,29 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
       }
     }
 
-    // rows of a wave -> one partial per wave
+    // per-column sums over the wave's rows go through LDS: lanes of the first
+    // 16-lane row group fold the other groups of their DPP row first
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      l[h] = fold_groups_sum<LPR>(l[h]);
 #pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) {
-        l[h] += __shfl_xor(l[h], off);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off);
-      }
+      for (int e = 0; e < EPL; ++e) o[h][e] = fold_groups_sum<LPR>(o[h][e]);
     }
-    if (lane_row == 0) {
+    const int drow = lane >> 4;                   // DPP row 0..3
+    if ((lane & 15) < LPR) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_o[wave][h][lane_col * EPL + e] = o[h][e];
+        for (int e = 0; e < EPL; ++e) s_o[wave][drow][h][lane_col * EPL + e] = o[h][e];
+      }
+      if (lane_col == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_ml[wave][drow][h][1] = l[h];
       }
     }
     if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s_ml[wave][h][0] = m[h];
-        s_ml[wave][h][1] = l[h];
-      }
+      for (int h = 0; h < G; ++h) s_ml[wave][0][h][0] = m[h];
     }
     __syncthreads();
     const int w0 = ustart / c, w1 = (uend - 1) / c;
@@ -761,14 +765,14 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
       const int h = idx / D, dd = idx % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][h][0]);
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h][0]);
       float ov = 0.0f, lv = 0.0f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float f = exp2f(s_ml[w][h][0] - M);     // -inf gives 0
-          ov += f * s_o[w][h][dd];
-          lv += f * s_ml[w][h][1];
+          const float f = exp2f(s_ml[w][0][h][0] - M);     // -inf gives 0
+          ov += f * (s_o[w][0][h][dd] + s_o[w][1][h][dd] + s_o[w][2][h][dd] + s_o[w][3][h][dd]);
+          lv += f * (s_ml[w][0][h][1] + s_ml[w][1][h][1] + s_ml[w][2][h][1] + s_ml[w][3][h][1]);
         }
       }
       if (!split) {

@@ -56,6 +56,8 @@ int compute_layout(const dms_config& c, Layout* L) {
   L->page_table = take(units * maxp * sizeof(int32_t));
   L->lengths = take(units * sizeof(int32_t));
   L->ring = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
+  L->ring_row = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
+  L->cur_page = take(units * sizeof(int32_t));
   L->pos = take(static_cast<size_t>(c.max_batch) * sizeof(int32_t));
   L->free_stack = take(pool * sizeof(int32_t));
   L->ctl = take(kCtlWords * sizeof(int32_t));
@@ -64,6 +66,7 @@ int compute_layout(const dms_config& c, Layout* L) {
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
   L->partial_records = 2 * kMaxDecodeGrid + kMaxUnits;
   L->partials = take(static_cast<size_t>(L->partial_records) * g * (D + 2) * sizeof(float));
+  L->dec_partials = take(static_cast<size_t>(c.max_batch) * kDecSplitsMax * 17 * sizeof(float));
   L->total = off;
   return DMS_OK;
 }
@@ -108,7 +111,10 @@ __global__ void init_kernel(DevCache d, Geo g, int units) {
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   for (int64_t i = i0; i < g.pool; i += n) d.free_stack[i] = g.pool - 1 - static_cast<int32_t>(i);
   for (int64_t i = i0; i < static_cast<int64_t>(units) * g.maxp; i += n) d.page_table[i] = -1;
-  for (int64_t i = i0; i < units; i += n) d.lengths[i] = 0;
+  for (int64_t i = i0; i < units; i += n) {
+    d.lengths[i] = 0;
+    d.cur_page[i] = -1;
+  }
   for (int64_t i = i0; i < g.Bmax; i += n) d.pos[i] = 0;
   for (int64_t i = i0; i < kCtlWords; i += n) d.ctl[i] = (i == kCtlFreeCount) ? g.pool : 0;
   for (int64_t i = i0; i < static_cast<int64_t>(kMaxUnits) * 4; i += n) d.unit_info[i] = 0;
@@ -183,6 +189,7 @@ __global__ __launch_bounds__(1024) void reset_kernel(DevCache d, Geo g, const in
     int32_t* pt = d.page_table + (static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp;
     for (int j = 0; j < g.maxp; ++j) pt[j] = -1;
     d.lengths[seq * g.Hkv + kh] = 0;
+    d.cur_page[seq * g.Hkv + kh] = -1;
     if (kh == 0) d.pos[seq] = 0;
   }
   if (tid == 0) d.ctl[kCtlFreeCount] = min(g.pool, s_free + s_base);
@@ -245,6 +252,8 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.page_table = reinterpret_cast<int32_t*>(base + L.page_table);
   c->dev.lengths = reinterpret_cast<int32_t*>(base + L.lengths);
   c->dev.ring = reinterpret_cast<int32_t*>(base + L.ring);
+  c->dev.ring_row = reinterpret_cast<int32_t*>(base + L.ring_row);
+  c->dev.cur_page = reinterpret_cast<int32_t*>(base + L.cur_page);
   c->dev.pos = reinterpret_cast<int32_t*>(base + L.pos);
   c->dev.free_stack = reinterpret_cast<int32_t*>(base + L.free_stack);
   c->dev.ctl = reinterpret_cast<int32_t*>(base + L.ctl);
@@ -252,6 +261,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.chunk_info = reinterpret_cast<int32_t*>(base + L.chunk_info);
   c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
   c->dev.partials = reinterpret_cast<float*>(base + L.partials);
+  c->dev.dec_partials = reinterpret_cast<float*>(base + L.dec_partials);
   Geo& g = c->geo;
   g.Bmax = cfg->max_batch;
   g.Hq = cfg->num_q_heads;

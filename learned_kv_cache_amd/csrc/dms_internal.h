@@ -17,6 +17,8 @@ constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
 constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
 constexpr int kMaxDecodeGrid = 4096;   // workgroups of the decode attention kernel
 constexpr int kCtlWords = 64;
+constexpr int kDecSplit = 512;         // hidden elements per workgroup of the split decode decision
+constexpr int kDecSplitsMax = 16;      // H <= 8192 for the split path
 constexpr int kCtlFreeCount = 0;
 constexpr int kCtlStatus = 1;
 
@@ -30,6 +32,8 @@ struct DevCache {
   int32_t* page_table;   // [Bmax][Hkv][maxp]
   int32_t* lengths;      // [Bmax][Hkv]
   int32_t* ring;         // [Bmax][Hkv][w] slot | evict << 31 of position p at p % w
+  int32_t* ring_row;     // [Bmax][Hkv][w] flat page row (page * P + slot % P) of that slot
+  int32_t* cur_page;     // [Bmax][Hkv] page holding slot L-1 (-1: none)
   int32_t* pos;          // [Bmax]
   int32_t* free_stack;   // [pool]
   int32_t* ctl;          // [kCtlWords]
@@ -37,6 +41,7 @@ struct DevCache {
   int32_t* chunk_info;   // [Bmax*Hkv][8]
   int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
   float* partials;       // decode split partials
+  float* dec_partials;   // [Bmax][kDecSplitsMax][17] decode decision partial sums
 };
 
 // Geometry shared by every kernel of one cache.
@@ -48,8 +53,8 @@ struct Geo {
 };
 
 struct Layout {
-  size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, partials, total;
+  size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, partials, dec_partials, total;
   int64_t partial_records;
 };
 
@@ -150,6 +155,68 @@ __device__ __forceinline__ float page_scale_from_amax(float amax) {
 __device__ __forceinline__ void set_status(int32_t* ctl, int bits) {
   atomicOr(reinterpret_cast<int*>(ctl + kCtlStatus), bits);
 }
+
+// ---- cross-lane reductions on DPP (full-rate VALU; no LDS crossbar) ----
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float x, float old) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, x),
+                                                               CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the LPR (2, 4, 8 or 16) lanes of a row; every lane of the row gets it.
+template <int LPR>
+__device__ __forceinline__ float row_sum_dpp(float x) {
+  if (LPR >= 2) x += dpp_f<0xB1, 0xF>(x, 0.0f);      // quad_perm [1,0,3,2]
+  if (LPR >= 4) x += dpp_f<0x4E, 0xF>(x, 0.0f);      // quad_perm [2,3,0,1]
+  if (LPR >= 8) x += dpp_f<0x141, 0xF>(x, 0.0f);     // row_half_mirror
+  if (LPR >= 16) x += dpp_f<0x140, 0xF>(x, 0.0f);    // row_mirror
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ float row_max_dpp(float x) {
+  if (LPR >= 2) x = fmaxf(x, dpp_f<0xB1, 0xF>(x, -INFINITY));
+  if (LPR >= 4) x = fmaxf(x, dpp_f<0x4E, 0xF>(x, -INFINITY));
+  if (LPR >= 8) x = fmaxf(x, dpp_f<0x141, 0xF>(x, -INFINITY));
+  if (LPR >= 16) x = fmaxf(x, dpp_f<0x140, 0xF>(x, -INFINITY));
+  return x;
+}
+
+// After a row-level reduction (every lane of each 16-lane row holds its row's
+// value), fold the four rows: row_bcast15 feeds rows 1 and 3 from the rows
+// before them, row_bcast31 feeds rows 2 and 3 from lane 31; lane 63 then
+// holds the result of all four rows.
+__device__ __forceinline__ float rows_sum_to_last(float x) {
+  x += dpp_f<0x142, 0xA>(x, 0.0f);
+  x += dpp_f<0x143, 0xC>(x, 0.0f);
+  return x;
+}
+__device__ __forceinline__ float rows_max_to_last(float x) {
+  x = fmaxf(x, dpp_f<0x142, 0xA>(x, -INFINITY));
+  x = fmaxf(x, dpp_f<0x143, 0xC>(x, -INFINITY));
+  return x;
+}
+// Fold row groups of LPR lanes inside each 16-lane row (row_ror moves lane
+// i + k to lane i), so every lane of a row ends with the row's value; for
+// per-column data this sums the same column of the row's groups.
+template <int LPR>
+__device__ __forceinline__ float fold_groups_sum(float x) {
+  if (LPR <= 8) x += dpp_f<0x128, 0xF>(x, 0.0f);     // row_ror:8
+  if (LPR <= 4) x += dpp_f<0x124, 0xF>(x, 0.0f);     // row_ror:4
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ float fold_groups_max(float x) {
+  if (LPR <= 8) x = fmaxf(x, dpp_f<0x128, 0xF>(x, -INFINITY));
+  if (LPR <= 4) x = fmaxf(x, dpp_f<0x124, 0xF>(x, -INFINITY));
+  return x;
+}
+
+__device__ __forceinline__ float lane63(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+// Whole-wave sum / max, returned to every lane.
+__device__ __forceinline__ float wave_sum_dpp(float x) { return lane63(rows_sum_to_last(row_sum_dpp<16>(x))); }
+__device__ __forceinline__ float wave_max_dpp(float x) { return lane63(rows_max_to_last(row_max_dpp<16>(x))); }
 
 // Wave-wide (64 lanes) prefix count of a predicate: returns the number of set
 // lanes below this one; *total receives the wave's count.

@@ -22,8 +22,9 @@ def _cuda():
     return torch
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("mode", ["head", "layer", "disabled"])
-def test_tiny_prefill_then_decode_every_step(mode):
+def test_tiny_prefill_then_decode_every_step(mode, fused):
     _cuda()
     wl = synth.TINY
     if mode == "layer":
@@ -38,7 +39,7 @@ def test_tiny_prefill_then_decode_every_step(mode):
     log(f"tiny {mode}: prefill err {st}")
     r.check_tables(pages=True)
     for t in range(64, 128):
-        r.decode_step([0], [t])
+        r.decode_step([0], [t], fused=fused)
         r.check_tables(pages=True)
     log(f"tiny {mode}: decode ok, stats {r.sim.stats()}")
     if mode == "disabled":
@@ -75,8 +76,8 @@ def test_tiny_reset_and_reuse():
     r.prefill_chunk([2, 0], 0, 40, check_rows=8)
     r.check_tables(pages=True)
     for t in range(40, 50):
-        r.decode_step([2, 0], [t, t])
-    r.decode_step([1], [80])
+        r.decode_step([2, 0], [t, t], fused=t % 2 == 0)
+    r.decode_step([1], [80], fused=True)
     r.check_tables(pages=True)
     assert r.dms.dms_cache_status(r.cache) == 0
 
@@ -134,7 +135,7 @@ def test_llama1b_prefill_8k_then_decode():
     r.check_tables(pages=True)
     worst = (0.0, 0.0)
     for i in range(wl.decode_steps):
-        st = r.decode_step([0], [8192 + i])
+        st = r.decode_step([0], [8192 + i], fused=i % 2 == 1)
         worst = (max(worst[0], st[0]), max(worst[1], st[1]))
     r.check_tables()
     stats = r.dms.dms_cache_stats(r.cache)
@@ -156,7 +157,7 @@ def test_qwen8b_ctx8k_b8_decode():
     r.check_tables()
     worst = (0.0, 0.0)
     for i in range(wl.decode_steps):
-        st = r.decode_step(seqs, [8192 + i] * wl.B)
+        st = r.decode_step(seqs, [8192 + i] * wl.B, fused=True)
         worst = (max(worst[0], st[0]), max(worst[1], st[1]))
         if i % 32 == 31:
             r.check_tables()
@@ -177,7 +178,7 @@ def test_qwen8b_prefill_32k_chunked(variant):
         log(f"prefill32k {variant}: chunk {s} err {st}")
     r.check_tables()
     for i in range(wl.decode_steps):
-        r.decode_step([0], [32768 + i], check=(i % 16 == 0))
+        r.decode_step([0], [32768 + i], check=(i % 16 == 0), fused=i % 2 == 0)
     r.check_tables()
 
 
@@ -197,7 +198,7 @@ def test_qwen8b_fp8_serving_b64():
     r.check_tables()
     seqs = list(range(wl.B))
     for i in range(wl.decode_steps):
-        st = r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], check=(i % 32 == 0))
+        st = r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], check=(i % 32 == 0), fused=True)
         if st:
             log(f"fp8 serving: step {i} err {st}")
     r.check_tables()
