@@ -20,7 +20,6 @@ the decode-attention kernel, CPU-oracle baseline, prefill figures).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -42,14 +41,6 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("decode_attn.hip", "dms_internal.h"):
-        with open(os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profiles(kind: str):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/*.json), if
     they were taken on the current kernel source; else None."""
@@ -58,7 +49,8 @@ def traffic_from_profiles(kind: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_hash") != kernel_source_hash():
+    from learned_kv_cache_amd.counters import source_hash
+    if rec.get("source_hash") != source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -358,6 +350,20 @@ def cpu_baseline(steps: int):
     }
 
 
+def copy_calibration(mib: int, torch) -> None:
+    """A plain read-once/write-once elementwise kernel over `mib` MiB of bf16
+    (torch.neg), run 4 times: its FETCH_SIZE and WRITE_SIZE readings scale the
+    counters of the other kernels (learned_kv_cache_amd.counters)."""
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 4 x {mib} MiB read + write")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +376,8 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="end with a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -433,6 +441,8 @@ def main() -> int:
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, torch)
     return 0
 
 

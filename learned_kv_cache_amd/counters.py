@@ -1,0 +1,100 @@
+"""HBM traffic per kernel launch from rocprofv3 counter runs.
+
+Two `rocprofv3 --pmc` passes over the same program give FETCH_SIZE (first
+pass) and WRITE_SIZE (second pass), in KiB per dispatch.  On MI355X these
+counters do not read the full device traffic at face value, so each is scaled
+by what it reads for a plain elementwise copy of known size that the same
+program runs at its end (`bench.py --copy-calib MiB`: torch.neg over a bf16
+tensor, which reads and writes that many bytes once).
+
+    python -m learned_kv_cache_amd.counters FETCH.csv WRITE.csv \
+        --kernel decode_attn_fast_kernel --copy-mib 1024 --out profiles/decode_attn_counters.json
+
+The record carries a hash of the kernel's sources; bench.py reports the
+traffic only while the hash matches the current sources.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "learned_kv_cache_amd", "csrc")
+
+# The sources that decide what the decode attention kernel does.
+DECODE_ATTN_SOURCES = ("decode_attn.hip", "dms_internal.h")
+COPY_KERNEL = "neg_kernel"
+
+
+def source_hash(files=DECODE_ATTN_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def per_dispatch(path: str, counter: str, kernel: str):
+    """Counter values (KiB) of every dispatch whose kernel name holds `kernel`."""
+    vals = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def calibrated(path: str, counter: str, kernel: str, copy_kib: float):
+    k = per_dispatch(path, counter, kernel)
+    c = per_dispatch(path, counter, COPY_KERNEL)
+    # the calibration copies are the large ones; small neg launches elsewhere are ignored
+    c = [x for x in c if x > 0.05 * copy_kib]
+    if not k:
+        raise SystemExit(f"{path}: no {counter} rows for a kernel named like {kernel!r}")
+    if not c:
+        raise SystemExit(f"{path}: no {counter} rows for the calibration copy ({COPY_KERNEL})")
+    factor = copy_kib / statistics.mean(c)
+    return {
+        "dispatches": len(k),
+        "kib_per_dispatch_raw": statistics.mean(k),
+        "copy_kib_raw": statistics.mean(c),
+        "copy_kib_expected": copy_kib,
+        "factor": factor,
+        "bytes_per_dispatch": statistics.mean(k) * factor * 1024.0,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("fetch_csv")
+    ap.add_argument("write_csv")
+    ap.add_argument("--kernel", default="decode_attn_fast_kernel")
+    ap.add_argument("--copy-mib", type=float, default=1024.0)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", action="append", default=[], help="command lines that made the CSVs")
+    a = ap.parse_args(argv)
+    kib = a.copy_mib * 1024.0
+    f = calibrated(a.fetch_csv, "FETCH_SIZE", a.kernel, kib)
+    w = calibrated(a.write_csv, "WRITE_SIZE", a.kernel, kib)
+    rec = {
+        "kernel": a.kernel,
+        "source_hash": source_hash(),
+        "fetch": f,
+        "write": w,
+        "hbm_bytes_per_launch": f["bytes_per_dispatch"] + w["bytes_per_dispatch"],
+        "commands": a.command,
+    }
+    with open(a.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
