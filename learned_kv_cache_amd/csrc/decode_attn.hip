@@ -949,10 +949,14 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
   int s;
-  // fast path: bf16/fp8 pages, D 64/128, power-of-two pages, page bytes addressable in 32 bits
+  // fast path: bf16/fp8 pages, D 64/128, power-of-two pages holding at least
+  // the 64 / lanes-per-row rows a wave reads per pass (so they span at most two
+  // pages), page bytes addressable in 32 bits
+  const int row_bytes = g.D * (g.kv_dtype == DMS_FP8_E4M3 ? 1 : 2);
+  const int lpr = row_bytes / 16 >= 16 ? (cache->decode_lpr == 8 ? 8 : 16) : row_bytes / 16;
   const bool fast = (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) &&
-                    g.Pshift >= 0 && cache->layout.v_pages - cache->layout.k_pages < (1ull << 32) &&
-                    !cache->force_generic;
+                    g.Pshift >= 0 && (1 << g.Pshift) >= 64 / lpr &&
+                    cache->layout.v_pages - cache->layout.k_pages < (1ull << 32) && !cache->force_generic;
   if (fast) {
     const bool fp8 = g.kv_dtype == DMS_FP8_E4M3;
     const int np = cache->decode_np > 0 ? cache->decode_np : 2;

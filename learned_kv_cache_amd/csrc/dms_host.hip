@@ -295,7 +295,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   if (const char* e = std::getenv("DMS_DECODE_NP")) c->decode_np = std::atoi(e);
   c->decode_lpr = 0;
   if (const char* e = std::getenv("DMS_DECODE_LPR")) c->decode_lpr = std::atoi(e);
-  const char* fg = std::getenv("DMS_DECODE_GENERIC");
+  const char* fg = std::getenv("DMS_GENERIC_KERNELS");
   c->force_generic = fg && fg[0] == '1';
   const int units = cfg->max_batch * cfg->num_kv_heads;
   hipLaunchKernelGGL(init_kernel, dim3(256), dim3(256), 0, as_stream(stream), c->dev, g, units);

@@ -68,9 +68,9 @@ struct dms_cache {
   int device;
   int num_cus;
   int decode_grid;
-  int decode_np;
-  int decode_lpr;        // lanes per row of the decode kernel (DMS_DECODE_LPR; 0: default)         // passes in flight per round of the decode kernel (DMS_DECODE_NP; 0: default)
-  bool force_generic;    // DMS_DECODE_GENERIC=1: use the reference-layout decode kernels
+  int decode_np;         // passes in flight per round of the decode kernel (DMS_DECODE_NP; 0: default)
+  int decode_lpr;        // lanes per row of the decode kernel (DMS_DECODE_LPR; 0: default)
+  bool force_generic;    // DMS_GENERIC_KERNELS=1: vector-ALU decode and prefill attention kernels only
 };
 
 namespace dms {

@@ -8,8 +8,14 @@
 // (their position and flag from the slot metadata); chunk keys from the
 // caller's K/V with the chunk's own flags.
 //
-// This file holds the vector-ALU kernel: one wave per (query token, KV head)
-// serving all g query heads.  It covers every dtype and head size.
+// Two kernels:
+//  * prefill_attn_mfma_kernel (bf16 activations, bf16 or fp8 pages, head_dim
+//    64/128, GQA group 1/2/4, block a multiple of 32): flash-attention on the
+//    16x16x32 bf16 matrix cores.  Both products keep the query on the MFMA
+//    column:  S^T = K Q^T  and  O^T = V^T P^T,  so the probabilities leave the
+//    first product already in the operand layout of the second and the
+//    softmax statistics of a column never leave its lane.
+//  * prefill_attn_generic_kernel: vector ALU, every dtype and head size.
 #include "dms_internal.h"
 
 namespace dms {
@@ -164,6 +170,451 @@ static int launch_generic(const PrefillArgs& a, hipStream_t st) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel.
+//
+// Workgroup: 4 waves, one (sequence, KV head) and a block of query tokens.
+// Each wave owns 4 column tiles of 16 queries: for group size G, 4/G groups
+// of 16 consecutive tokens times the G query heads of the KV head (the mask
+// depends on the token only).  Keys stream through LDS in blocks of 32: the
+// cache slots 0..L-1 first (visibility from the slot metadata), then the
+// chunk's own keys up to the workgroup's last token.  Each key carries a
+// visibility interval [lo, hi) of query positions: lo = its position, hi =
+// position + w when its flag is set (delayed eviction), else unbounded.
+//
+// MFMA 16x16x32 bf16 operand layout (lane l, G4 = l / 16, i = 0..7):
+//   A[row l%16][k 8*G4+i], B[k 8*G4+i][col l%16], D[row 4*G4+r][col l%16].
+// S^T = K Q^T: A = K rows from LDS, B = Q^T fragments held in registers;
+// lane l gets the scores of keys 4*G4+r (and 16+4*G4+r) for query l%16.
+// O^T = V^T P^T: B = P^T is exactly those 8 probabilities per lane when the
+// key index k of the second product is permuted as
+//   k = 8*G4 + i  <->  key (i < 4 ? 4*G4 + i : 16 + 4*G4 + i - 4),
+// so V^T is stored in LDS with its key columns in that order.
+
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
+typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPfKB = 32;         // keys per LDS block
+constexpr int kPfThreads = 256;   // 4 waves
+constexpr int kPfNoLimit = 0x7FFFFFFF;
+constexpr float kPfRescaleLog2 = 8.0f;   // running max is raised only when exceeded by this (log2 units)
+
+template <int D, int G>
+struct PfShape {
+  static constexpr int TG = 4 / G;            // token groups of 16 per wave
+  static constexpr int NT = 4;                // column tiles per wave
+  static constexpr int TOKW = 16 * TG;        // tokens per wave
+  static constexpr int TOKB = 4 * TOKW;       // tokens per workgroup
+  static constexpr int KS = D / 32;           // k-steps of S^T over head_dim
+  static constexpr int DT = D / 16;           // 16-row tiles of O^T
+  static constexpr int KROW = 2 * D + 16;     // bytes per K row in LDS (padded: conflict-free reads)
+  static constexpr int VROW = 2 * kPfKB + 16; // bytes per V^T row
+  static constexpr int V_OFF = kPfKB * KROW;
+  static constexpr int LO_OFF = V_OFF + D * VROW;
+  static constexpr int HI_OFF = LO_OFF + 4 * kPfKB;
+  static constexpr int BUF = HI_OFF + 4 * kPfKB;
+  static constexpr int KPIECES = kPfKB * D / 8 / kPfThreads;    // 16-byte K pieces per thread per block
+  static constexpr int VTHREADS = (kPfKB / 2) * (D / 8);        // threads holding a V key pair piece
+  static_assert(KPIECES >= 1 && VTHREADS <= kPfThreads, "shape");
+  static_assert(BUF % 16 == 0, "LDS alignment");
+};
+
+// LDS column of key k (0..31) in the permuted V^T storage.
+__device__ __forceinline__ int pf_vcol(int k) {
+  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
+
+// Lane l and lane l ^ 32, and l ^ 16 (v_permlane32_swap / v_permlane16_swap
+// return the pair (own, partner) in a lane-independent order).
+__device__ __forceinline__ float pf_max_x32(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pf_max_x16(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pf_sum_x32(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pf_sum_x16(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ uint32_t pf_pack(float lo, float hi) {
+  pf_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, pf_bf16x2));
+}
+
+// Eight e4m3 codes times a power-of-two page scale -> eight bf16 (exact).
+__device__ __forceinline__ uint4 pf_fp8x8_to_bf16(uint32_t w0, uint32_t w1, float sc) {
+  const pf_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const pf_f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  return make_uint4(pf_pack(a[0] * sc, a[1] * sc), pf_pack(b[0] * sc, b[1] * sc), pf_pack(c[0] * sc, c[1] * sc),
+                    pf_pack(e[0] * sc, e[1] * sc));
+}
+
+// One key row's source for staging.
+struct PfKey {
+  const uint8_t* k;   // row start (bytes)
+  const uint8_t* v;
+  float sk, sv;       // fp8 page scales (1 for bf16 rows)
+  int kind;           // 0: past the end (zeros), 1: cache page row, 2: chunk row
+  int lo, hi;         // visibility interval of query positions
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ PfKey pf_key(const PrefillArgs& a, const int32_t* pt, int row, int kh, int L, int s0,
+                                        int nk, const uint8_t* ev, int kk) {
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  PfKey r;
+  r.sk = r.sv = 1.0f;
+  if (kk < L) {
+    const int page = pt[kk >> g.Pshift];
+    const int64_t prow = (static_cast<int64_t>(page) << g.Pshift) + (kk & (g.P - 1));
+    constexpr int EB = FP8 ? 1 : 2;
+    r.k = d.k_pages + prow * D * EB;
+    r.v = d.v_pages + prow * D * EB;
+    if (FP8) {
+      r.sk = d.scales[2 * page];
+      r.sv = d.scales[2 * page + 1];
+    }
+    const int meta = d.slot_meta[prow];
+    r.lo = meta & 0x7FFFFFFF;
+    r.hi = meta < 0 ? r.lo + g.w : kPfNoLimit;
+    r.kind = 1;
+  } else if (kk < nk) {
+    const int j = kk - L;
+    const size_t off = ((static_cast<size_t>(row) * a.C + j) * g.Hkv + kh) * D * 2;
+    r.k = static_cast<const uint8_t*>(a.k) + off;
+    r.v = static_cast<const uint8_t*>(a.v) + off;
+    r.lo = s0 + j;
+    r.hi = ev[j] ? s0 + j + g.w : kPfNoLimit;
+    r.kind = 2;
+  } else {
+    r.k = r.v = nullptr;
+    r.lo = kPfNoLimit;
+    r.hi = 0;
+    r.kind = 0;
+  }
+  return r;
+}
+
+// 16-byte piece (8 elements starting at element 8*dc) of a key row, as loaded.
+struct PfRaw {
+  uint4 w;
+  float sc;
+  int kind;
+};
+
+template <bool FP8>
+__device__ __forceinline__ PfRaw pf_load(const uint8_t* base, float sc, int kind, int dc) {
+  PfRaw r;
+  r.sc = sc;
+  r.kind = kind;
+  if (kind == 0) {
+    r.w = make_uint4(0, 0, 0, 0);
+  } else if (FP8 && kind == 1) {
+    const uint2 t = *reinterpret_cast<const uint2*>(base + 8 * dc);
+    r.w = make_uint4(t.x, t.y, 0, 0);
+  } else {
+    r.w = *reinterpret_cast<const uint4*>(base + 16 * dc);
+  }
+  return r;
+}
+
+template <bool FP8>
+__device__ __forceinline__ uint4 pf_bf16(const PfRaw& r) {
+  if (FP8 && r.kind == 1) return pf_fp8x8_to_bf16(r.w.x, r.w.y, r.sc);
+  return r.w;
+}
+
+template <int D, int G, bool FP8>
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(PrefillArgs a) {
+  using S = PfShape<D, G>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BUF];
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, G4 = lane >> 4;
+
+  // Linear workgroup id -> (pair, token block), the heaviest (last) token
+  // blocks first; consecutive ids cycle through the pairs.
+  const int npairs = a.B * g.Hkv;
+  const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
+  const int pair = blockIdx.x % npairs;
+  const int tb = ntb - 1 - static_cast<int>(blockIdx.x) / npairs;
+  const int row = pair / g.Hkv, kh = pair % g.Hkv;
+  const int seq = a.seq_ids ? a.seq_ids[row] : row;
+  if (seq < 0 || seq >= g.Bmax) {
+    if (tid == 0 && tb == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+    return;
+  }
+  const int unit = seq * g.Hkv + kh;
+  const int s0 = d.pos[seq];
+  const int L = d.lengths[unit];
+  const int tok0 = tb * S::TOKB;
+  const int tok_end = min(tok0 + S::TOKB, a.C);
+  const int nk = L + tok_end;
+  const int nblk = (nk + kPfKB - 1) / kPfKB;
+  const int32_t* pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
+  const uint8_t* ev = a.evict + static_cast<int64_t>(pair) * a.C;
+
+  // ---- this lane's query columns: tile c = tg * G + h
+  const int wtok = tok0 + wave * S::TOKW;
+  int qpos[S::TG];
+  bool qok[S::TG];
+#pragma unroll
+  for (int tg = 0; tg < S::TG; ++tg) {
+    const int t = wtok + tg * 16 + l16;
+    qok[tg] = t < a.C;
+    qpos[tg] = qok[tg] ? s0 + t : -1;
+  }
+  // tokens grow with tg, so the first group is live whenever any is; groups
+  // past the chunk end hold position -1 and must not lower the upper bound
+  const int qmin = qpos[0];
+  int qmax = qpos[0];
+#pragma unroll
+  for (int tg = 1; tg < S::TG; ++tg) qmax = max(qmax, qpos[tg]);
+  const bool lane_live = qok[0];
+
+  pf_bf16x8 qf[S::NT][S::KS];
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int tg = 0; tg < S::TG; ++tg) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int c = tg * G + h;
+      const int t = wtok + tg * 16 + l16;
+      const size_t qrow = ((static_cast<size_t>(row) * a.C + t) * g.Hq + kh * G + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (qok[tg]) w = *reinterpret_cast<const uint4*>(qbase + qrow + 32 * ks + 8 * G4);
+        qf[c][ks] = __builtin_bit_cast(pf_bf16x8, w);
+      }
+    }
+  }
+
+  pf_f32x4 o[S::NT][S::DT];
+  float m[S::NT], lsum[S::NT], mb[S::NT];
+#pragma unroll
+  for (int c = 0; c < S::NT; ++c) {
+    m[c] = -INFINITY;
+    mb[c] = 0.0f;
+    lsum[c] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) o[c][dt] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const float cs = g.scale_log2;
+
+  // ---- staging roles
+  // K: piece p -> key (idx / (D/8)), element chunk (idx % (D/8)), idx = tid + 256 p
+  // V: thread -> key pair (tid / (D/8)), element chunk (tid % (D/8)); writes V^T
+  // lo/hi: threads 0..31 -> key tid
+  PfRaw kraw[S::KPIECES], vraw0, vraw1;
+  int klo = 0, khi = 0;
+  auto stage_load = [&](int blk) {
+    const int kb = blk * kPfKB;
+#pragma unroll
+    for (int p = 0; p < S::KPIECES; ++p) {
+      const int idx = tid + kPfThreads * p;
+      const PfKey key = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + idx / (D / 8));
+      kraw[p] = pf_load<FP8>(key.k, key.sk, key.kind, idx % (D / 8));
+    }
+    if (tid < S::VTHREADS) {
+      const int kp = tid / (D / 8), dc = tid % (D / 8);
+      const PfKey k0 = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + 2 * kp);
+      const PfKey k1 = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + 2 * kp + 1);
+      vraw0 = pf_load<FP8>(k0.v, k0.sv, k0.kind, dc);
+      vraw1 = pf_load<FP8>(k1.v, k1.sv, k1.kind, dc);
+    }
+    if (tid < kPfKB) {
+      const PfKey key = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + tid);
+      klo = key.lo;
+      khi = key.hi;
+    }
+  };
+  auto stage_write = [&](int buf) {
+    uint8_t* b = smem + buf * S::BUF;
+#pragma unroll
+    for (int p = 0; p < S::KPIECES; ++p) {
+      const int idx = tid + kPfThreads * p;
+      *reinterpret_cast<uint4*>(b + (idx / (D / 8)) * S::KROW + 16 * (idx % (D / 8))) = pf_bf16<FP8>(kraw[p]);
+    }
+    if (tid < S::VTHREADS) {
+      const int kp = tid / (D / 8), dc = tid % (D / 8);
+      const uint4 x = pf_bf16<FP8>(vraw0), y = pf_bf16<FP8>(vraw1);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+      uint8_t* vt = b + S::V_OFF + 2 * pf_vcol(2 * kp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // elements 2e and 2e+1 of keys 2kp (low half) and 2kp+1 (high half)
+        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * e) * S::VROW) = __builtin_amdgcn_perm(ys[e], xs[e], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * e + 1) * S::VROW) = __builtin_amdgcn_perm(ys[e], xs[e], 0x07060302u);
+      }
+    }
+    if (tid < kPfKB) {
+      reinterpret_cast<int*>(b + S::LO_OFF)[tid] = klo;
+      reinterpret_cast<int*>(b + S::HI_OFF)[tid] = khi;
+    }
+  };
+
+  stage_load(0);
+  stage_write(0);
+  __syncthreads();
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    if (blk + 1 < nblk) stage_load(blk + 1);
+    const uint8_t* b = smem + (blk & 1) * S::BUF;
+
+    // visibility of this block for the wave
+    const int4 lo0 = *reinterpret_cast<const int4*>(b + S::LO_OFF + 16 * G4);
+    const int4 lo1 = *reinterpret_cast<const int4*>(b + S::LO_OFF + 64 + 16 * G4);
+    const int4 hi0 = *reinterpret_cast<const int4*>(b + S::HI_OFF + 16 * G4);
+    const int4 hi1 = *reinterpret_cast<const int4*>(b + S::HI_OFF + 64 + 16 * G4);
+    const int lmin = min(min(min(lo0.x, lo0.y), min(lo0.z, lo0.w)), min(min(lo1.x, lo1.y), min(lo1.z, lo1.w)));
+    const int lmax = max(max(max(lo0.x, lo0.y), max(lo0.z, lo0.w)), max(max(lo1.x, lo1.y), max(lo1.z, lo1.w)));
+    const int hmin = min(min(min(hi0.x, hi0.y), min(hi0.z, hi0.w)), min(min(hi1.x, hi1.y), min(hi1.z, hi1.w)));
+    const int hmax = max(max(max(hi0.x, hi0.y), max(hi0.z, hi0.w)), max(max(hi1.x, hi1.y), max(hi1.z, hi1.w)));
+    const bool lane_none = !lane_live || lmin > qmax || hmax <= qmin;
+    const bool lane_all = !lane_live || (lmax <= qmin && hmin > qmax);
+    if (!__all(lane_none)) {
+      // S^T = K Q^T
+      pf_f32x4 s[2][S::NT];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < S::NT; ++c) s[kt][c] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const pf_bf16x8 kf = *reinterpret_cast<const pf_bf16x8*>(b + (16 * kt + l16) * S::KROW + 64 * ks + 16 * G4);
+#pragma unroll
+          for (int c = 0; c < S::NT; ++c)
+            s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks], s[kt][c], 0, 0, 0);
+        }
+      }
+      if (!__all(lane_all)) {
+        const int los[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
+        const int his[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
+#pragma unroll
+        for (int c = 0; c < S::NT; ++c) {
+          const int qp = qpos[c / G];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool vis = los[e] <= qp && qp < his[e];
+            s[e >> 2][c][e & 3] = vis ? s[e >> 2][c][e & 3] : -INFINITY;
+          }
+        }
+      }
+      // running max per column, raised lazily
+      float mx[S::NT];
+      bool need = false;
+#pragma unroll
+      for (int c = 0; c < S::NT; ++c) {
+        float x = fmaxf(fmaxf(fmaxf(s[0][c][0], s[0][c][1]), fmaxf(s[0][c][2], s[0][c][3])),
+                        fmaxf(fmaxf(s[1][c][0], s[1][c][1]), fmaxf(s[1][c][2], s[1][c][3])));
+        x = pf_max_x32(x);
+        x = pf_max_x16(x);
+        mx[c] = x;
+        need |= x * cs > m[c] * cs + kPfRescaleLog2;
+      }
+      if (__any(need)) {
+#pragma unroll
+        for (int c = 0; c < S::NT; ++c) {
+          if (mx[c] * cs > m[c] * cs + kPfRescaleLog2) {
+            const float alpha = __builtin_amdgcn_exp2f((m[c] - mx[c]) * cs);   // 0 from -inf
+            m[c] = mx[c];
+            mb[c] = mx[c] * cs;
+            lsum[c] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < S::DT; ++dt) o[c][dt] *= alpha;
+          }
+        }
+      }
+      // P^T (bf16) and O^T += V^T P^T
+      pf_bf16x8 pk[S::NT];
+#pragma unroll
+      for (int c = 0; c < S::NT; ++c) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][c][e & 3], cs, -mb[c]));
+        lsum[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        const uint4 w = make_uint4(pf_pack(p[0], p[1]), pf_pack(p[2], p[3]), pf_pack(p[4], p[5]), pf_pack(p[6], p[7]));
+        pk[c] = __builtin_bit_cast(pf_bf16x8, w);
+      }
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+        const pf_bf16x8 vf = *reinterpret_cast<const pf_bf16x8*>(b + S::V_OFF + (16 * dt + l16) * S::VROW + 16 * G4);
+#pragma unroll
+        for (int c = 0; c < S::NT; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[c], o[c][dt], 0, 0, 0);
+      }
+    }
+    if (blk + 1 < nblk) stage_write((blk + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds d = 16 dt + 4 G4 + r of its column
+  uint16_t* obase = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int tg = 0; tg < S::TG; ++tg) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int c = tg * G + h;
+      float lt = pf_sum_x32(lsum[c]);
+      lt = pf_sum_x16(lt);
+      if (!qok[tg]) continue;
+      const float inv = 1.0f / lt;
+      const int t = wtok + tg * 16 + l16;
+      uint16_t* orow = obase + ((static_cast<size_t>(row) * a.C + t) * g.Hq + kh * G + h) * D + 4 * G4;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+        const pf_f32x4 v = o[c][dt];
+        *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pf_pack(v[0] * inv, v[1] * inv), pf_pack(v[2] * inv, v[3] * inv));
+      }
+    }
+  }
+}
+
+template <int D, int G, bool FP8>
+static int launch_mfma_dgf(const PrefillArgs& a, hipStream_t st) {
+  using S = PfShape<D, G>;
+  const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
+  const dim3 grid(ntb * a.B * a.g.Hkv), block(kPfThreads);
+  hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, FP8>), grid, block, 0, st, a);
+  return DMS_OK;
+}
+
+template <int D, bool FP8>
+static int launch_mfma_d(const PrefillArgs& a, hipStream_t st) {
+  switch (a.g.g) {
+    case 1: return launch_mfma_dgf<D, 1, FP8>(a, st);
+    case 2: return launch_mfma_dgf<D, 2, FP8>(a, st);
+    case 4: return launch_mfma_dgf<D, 4, FP8>(a, st);
+    default: return fail(DMS_ERR_UNSUPPORTED, "group size");
+  }
+}
+
+static bool mfma_ok(const Geo& g) {
+  return (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) &&
+         (g.g == 1 || g.g == 2 || g.g == 4) && g.Pshift >= 5;
+}
+
+static int launch_mfma(const PrefillArgs& a, hipStream_t st) {
+  const bool fp8 = a.g.kv_dtype == DMS_FP8_E4M3;
+  if (a.g.D == 128) return fp8 ? launch_mfma_d<128, true>(a, st) : launch_mfma_d<128, false>(a, st);
+  return fp8 ? launch_mfma_d<64, true>(a, st) : launch_mfma_d<64, false>(a, st);
+}
+
 }  // namespace dms
 
 using namespace dms;
@@ -179,11 +630,15 @@ extern "C" int dms_prefill_attn(dms_cache* cache, const int32_t* seq_ids, const 
   PrefillArgs a{cache->dev, g, seq_ids, q, k, v, evict, out, B, C};
   hipStream_t st = as_stream(stream);
   int s;
-  switch (g.kv_dtype) {
-    case DMS_F32: s = launch_generic<float, DMS_F32>(a, st); break;
-    case DMS_BF16: s = launch_generic<uint16_t, DMS_BF16>(a, st); break;
-    case DMS_FP8_E4M3: s = launch_generic<uint16_t, DMS_FP8_E4M3>(a, st); break;
-    default: return fail(DMS_ERR_UNSUPPORTED, "kv dtype");
+  if (mfma_ok(g) && !cache->force_generic) {
+    s = launch_mfma(a, st);
+  } else {
+    switch (g.kv_dtype) {
+      case DMS_F32: s = launch_generic<float, DMS_F32>(a, st); break;
+      case DMS_BF16: s = launch_generic<uint16_t, DMS_BF16>(a, st); break;
+      case DMS_FP8_E4M3: s = launch_generic<uint16_t, DMS_FP8_E4M3>(a, st); break;
+      default: return fail(DMS_ERR_UNSUPPORTED, "kv dtype");
+    }
   }
   if (s) return s;
   return check_hip(hipGetLastError(), "dms_prefill_attn launch");
