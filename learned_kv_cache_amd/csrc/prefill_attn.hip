@@ -174,14 +174,14 @@ static int launch_generic(const PrefillArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Matrix-core kernel.
 //
-// Workgroup: 4 waves, one (sequence, KV head) and a block of query tokens.
-// Each wave owns 4 column tiles of 16 queries: for group size G, 4/G groups
-// of 16 consecutive tokens times the G query heads of the KV head (the mask
-// depends on the token only).  Keys stream through LDS in blocks of 32: the
-// cache slots 0..L-1 first (visibility from the slot metadata), then the
-// chunk's own keys up to the workgroup's last token.  Each key carries a
-// visibility interval [lo, hi) of query positions: lo = its position, hi =
-// position + w when its flag is set (delayed eviction), else unbounded.
+// Workgroup: 8 waves (two per SIMD, so one wave's softmax overlaps the other's
+// matrix products), one (sequence, KV head) and a block of query tokens.  Each
+// wave owns 2 column tiles of 16 queries (token x query head; the mask depends
+// on the token only).  Keys stream through LDS in blocks of 32: the cache
+// slots 0..L-1 first (visibility from the slot metadata), then the chunk's own
+// keys up to the workgroup's last token.  Each key carries a visibility
+// interval [lo, hi) of query positions: lo = its position, hi = position + w
+// when its flag is set (delayed eviction), else unbounded.
 //
 // MFMA 16x16x32 bf16 operand layout (lane l, G4 = l / 16, i = 0..7):
 //   A[row l%16][k 8*G4+i], B[k 8*G4+i][col l%16], D[row 4*G4+r][col l%16].
@@ -190,7 +190,9 @@ static int launch_generic(const PrefillArgs& a, hipStream_t st) {
 // O^T = V^T P^T: B = P^T is exactly those 8 probabilities per lane when the
 // key index k of the second product is permuted as
 //   k = 8*G4 + i  <->  key (i < 4 ? 4*G4 + i : 16 + 4*G4 + i - 4),
-// so V^T is stored in LDS with its key columns in that order.
+// so V^T is stored in LDS with its key columns in that order.  One more
+// product with an all-ones A gives the softmax denominator of the same
+// bf16-rounded probabilities in every row of an extra accumulator tile.
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
@@ -198,16 +200,19 @@ typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
 typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfKB = 32;         // keys per LDS block
-constexpr int kPfThreads = 256;   // 4 waves
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfNoLimit = 0x7FFFFFFF;
 constexpr float kPfRescaleLog2 = 8.0f;   // running max is raised only when exceeded by this (log2 units)
 
 template <int D, int G>
 struct PfShape {
-  static constexpr int TG = 4 / G;            // token groups of 16 per wave
-  static constexpr int NT = 4;                // column tiles per wave
+  static constexpr int HW = G < 2 ? G : 2;    // query heads per wave
+  static constexpr int HS = G / HW;           // waves sharing one token group (head split)
+  static constexpr int TG = 2 / HW;           // 16-token groups per wave
+  static constexpr int NT = TG * HW;          // column tiles per wave (2)
   static constexpr int TOKW = 16 * TG;        // tokens per wave
-  static constexpr int TOKB = 4 * TOKW;       // tokens per workgroup
+  static constexpr int TOKB = TOKW * kPfWaves / HS;   // tokens per workgroup
   static constexpr int KS = D / 32;           // k-steps of S^T over head_dim
   static constexpr int DT = D / 16;           // 16-row tiles of O^T
   static constexpr int KROW = 2 * D + 16;     // bytes per K row in LDS (padded: conflict-free reads)
@@ -216,9 +221,11 @@ struct PfShape {
   static constexpr int LO_OFF = V_OFF + D * VROW;
   static constexpr int HI_OFF = LO_OFF + 4 * kPfKB;
   static constexpr int BUF = HI_OFF + 4 * kPfKB;
-  static constexpr int KPIECES = kPfKB * D / 8 / kPfThreads;    // 16-byte K pieces per thread per block
-  static constexpr int VTHREADS = (kPfKB / 2) * (D / 8);        // threads holding a V key pair piece
-  static_assert(KPIECES >= 1 && VTHREADS <= kPfThreads, "shape");
+  static constexpr int DC = D / 8;            // 16-byte pieces per bf16 row
+  static constexpr int KTHREADS = kPfKB * DC;         // one K piece each
+  static constexpr int VTHREADS = (kPfKB / 2) * DC;   // one V key-pair piece each
+  static constexpr int VFIRST = kPfThreads - VTHREADS;
+  static_assert(NT == 2 && KTHREADS <= kPfThreads && VTHREADS <= kPfThreads, "shape");
   static_assert(BUF % 16 == 0, "LDS alignment");
 };
 
@@ -227,8 +234,8 @@ __device__ __forceinline__ int pf_vcol(int k) {
   return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
 }
 
-// Lane l and lane l ^ 32, and l ^ 16 (v_permlane32_swap / v_permlane16_swap
-// return the pair (own, partner) in a lane-independent order).
+// max / sum of lane l and lane l ^ 32 (resp. l ^ 16): v_permlane32_swap and
+// v_permlane16_swap return the pair (own, partner) in a lane-independent order.
 __device__ __forceinline__ float pf_max_x32(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
@@ -236,14 +243,6 @@ __device__ __forceinline__ float pf_max_x32(float x) {
 __device__ __forceinline__ float pf_max_x16(float x) {
   auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float pf_sum_x32(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float pf_sum_x16(float x) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 __device__ __forceinline__ uint32_t pf_pack(float lo, float hi) {
@@ -259,72 +258,46 @@ __device__ __forceinline__ uint4 pf_fp8x8_to_bf16(uint32_t w0, uint32_t w1, floa
                     pf_pack(e[0] * sc, e[1] * sc));
 }
 
-// One key row's source for staging.
-struct PfKey {
-  const uint8_t* k;   // row start (bytes)
-  const uint8_t* v;
-  float sk, sv;       // fp8 page scales (1 for bf16 rows)
-  int kind;           // 0: past the end (zeros), 1: cache page row, 2: chunk row
-  int lo, hi;         // visibility interval of query positions
+// Per-call constants of one (sequence, KV head) as staging needs them.
+struct PfSrc {
+  const int32_t* pt;
+  const uint8_t* kchunk;   // chunk key 0 of this KV head (bytes)
+  const uint8_t* vchunk;
+  const uint8_t* ev;
+  int L, s0, nk;
+  int64_t chunk_stride;    // bytes between consecutive chunk keys
 };
 
-template <int D, bool FP8>
-__device__ __forceinline__ PfKey pf_key(const PrefillArgs& a, const int32_t* pt, int row, int kh, int L, int s0,
-                                        int nk, const uint8_t* ev, int kk) {
-  const DevCache& d = a.d;
-  const Geo& g = a.g;
-  PfKey r;
-  r.sk = r.sv = 1.0f;
-  if (kk < L) {
-    const int page = pt[kk >> g.Pshift];
-    const int64_t prow = (static_cast<int64_t>(page) << g.Pshift) + (kk & (g.P - 1));
-    constexpr int EB = FP8 ? 1 : 2;
-    r.k = d.k_pages + prow * D * EB;
-    r.v = d.v_pages + prow * D * EB;
-    if (FP8) {
-      r.sk = d.scales[2 * page];
-      r.sv = d.scales[2 * page + 1];
-    }
-    const int meta = d.slot_meta[prow];
-    r.lo = meta & 0x7FFFFFFF;
-    r.hi = meta < 0 ? r.lo + g.w : kPfNoLimit;
-    r.kind = 1;
-  } else if (kk < nk) {
-    const int j = kk - L;
-    const size_t off = ((static_cast<size_t>(row) * a.C + j) * g.Hkv + kh) * D * 2;
-    r.k = static_cast<const uint8_t*>(a.k) + off;
-    r.v = static_cast<const uint8_t*>(a.v) + off;
-    r.lo = s0 + j;
-    r.hi = ev[j] ? s0 + j + g.w : kPfNoLimit;
-    r.kind = 2;
-  } else {
-    r.k = r.v = nullptr;
-    r.lo = kPfNoLimit;
-    r.hi = 0;
-    r.kind = 0;
-  }
-  return r;
-}
-
-// 16-byte piece (8 elements starting at element 8*dc) of a key row, as loaded.
+// A 16-byte piece (8 elements from element 8*dc) of key kk's K or V row, as
+// loaded; `page` is the block's cache page (uniform), valid when kk < L.
 struct PfRaw {
   uint4 w;
   float sc;
-  int kind;
+  int kind;     // 0: zeros (past the keys), 1: cache page row, 2: chunk row
 };
 
-template <bool FP8>
-__device__ __forceinline__ PfRaw pf_load(const uint8_t* base, float sc, int kind, int dc) {
+template <int D, bool FP8>
+__device__ __forceinline__ PfRaw pf_load(const PrefillArgs& a, const PfSrc& q, int page, int kk, int dc, bool v) {
   PfRaw r;
-  r.sc = sc;
-  r.kind = kind;
-  if (kind == 0) {
-    r.w = make_uint4(0, 0, 0, 0);
-  } else if (FP8 && kind == 1) {
-    const uint2 t = *reinterpret_cast<const uint2*>(base + 8 * dc);
-    r.w = make_uint4(t.x, t.y, 0, 0);
+  r.sc = 1.0f;
+  if (kk < q.L) {
+    const int64_t prow = (static_cast<int64_t>(page) << a.g.Pshift) + (kk & (a.g.P - 1));
+    r.kind = 1;
+    if (FP8) {
+      const uint8_t* base = (v ? a.d.v_pages : a.d.k_pages) + prow * D;
+      const uint2 t = *reinterpret_cast<const uint2*>(base + 8 * dc);
+      r.w = make_uint4(t.x, t.y, 0, 0);
+      r.sc = a.d.scales[2 * page + (v ? 1 : 0)];
+    } else {
+      const uint8_t* base = (v ? a.d.v_pages : a.d.k_pages) + prow * D * 2;
+      r.w = *reinterpret_cast<const uint4*>(base + 16 * dc);
+    }
+  } else if (kk < q.nk) {
+    r.kind = 2;
+    r.w = *reinterpret_cast<const uint4*>((v ? q.vchunk : q.kchunk) + (kk - q.L) * q.chunk_stride + 16 * dc);
   } else {
-    r.w = *reinterpret_cast<const uint4*>(base + 16 * dc);
+    r.kind = 0;
+    r.w = make_uint4(0, 0, 0, 0);
   }
   return r;
 }
@@ -336,7 +309,7 @@ __device__ __forceinline__ uint4 pf_bf16(const PfRaw& r) {
 }
 
 template <int D, int G, bool FP8>
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillArgs a) {
   using S = PfShape<D, G>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BUF];
   const DevCache& d = a.d;
@@ -358,27 +331,34 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
     return;
   }
   const int unit = seq * g.Hkv + kh;
-  const int s0 = d.pos[seq];
-  const int L = d.lengths[unit];
+  PfSrc src;
+  src.pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
+  src.L = d.lengths[unit];
+  src.s0 = d.pos[seq];
   const int tok0 = tb * S::TOKB;
   const int tok_end = min(tok0 + S::TOKB, a.C);
-  const int nk = L + tok_end;
-  const int nblk = (nk + kPfKB - 1) / kPfKB;
-  const int32_t* pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
-  const uint8_t* ev = a.evict + static_cast<int64_t>(pair) * a.C;
+  src.nk = src.L + tok_end;
+  src.chunk_stride = static_cast<int64_t>(g.Hkv) * D * 2;
+  const size_t chunk0 = (static_cast<size_t>(row) * a.C * g.Hkv + kh) * D * 2;
+  src.kchunk = static_cast<const uint8_t*>(a.k) + chunk0;
+  src.vchunk = static_cast<const uint8_t*>(a.v) + chunk0;
+  src.ev = a.evict + static_cast<int64_t>(pair) * a.C;
+  const int nblk = (src.nk + kPfKB - 1) / kPfKB;
 
-  // ---- this lane's query columns: tile c = tg * G + h
-  const int wtok = tok0 + wave * S::TOKW;
+  // ---- this wave's query columns: tile c = tg * HW + h
+  const int hp = wave % S::HS, tp = wave / S::HS;
+  const int wtok = tok0 + tp * S::TOKW;
+  const int head0 = kh * G + hp * S::HW;
   int qpos[S::TG];
   bool qok[S::TG];
 #pragma unroll
   for (int tg = 0; tg < S::TG; ++tg) {
     const int t = wtok + tg * 16 + l16;
     qok[tg] = t < a.C;
-    qpos[tg] = qok[tg] ? s0 + t : -1;
+    qpos[tg] = qok[tg] ? src.s0 + t : -1;
   }
-  // tokens grow with tg, so the first group is live whenever any is; groups
-  // past the chunk end hold position -1 and must not lower the upper bound
+  // tokens grow with tg: the first group is live whenever any is; groups past
+  // the chunk end hold position -1 and must not lower the upper bound
   const int qmin = qpos[0];
   int qmax = qpos[0];
 #pragma unroll
@@ -390,10 +370,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
 #pragma unroll
   for (int tg = 0; tg < S::TG; ++tg) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int c = tg * G + h;
+    for (int h = 0; h < S::HW; ++h) {
+      const int c = tg * S::HW + h;
       const int t = wtok + tg * 16 + l16;
-      const size_t qrow = ((static_cast<size_t>(row) * a.C + t) * g.Hq + kh * G + h) * D;
+      const size_t qrow = ((static_cast<size_t>(row) * a.C + t) * g.Hq + head0 + h) * D;
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         uint4 w = make_uint4(0, 0, 0, 0);
@@ -403,67 +383,73 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
     }
   }
 
-  pf_f32x4 o[S::NT][S::DT];
-  float m[S::NT], lsum[S::NT], mb[S::NT];
+  pf_f32x4 o[S::NT][S::DT], lacc[S::NT];
+  float m[S::NT], mb[S::NT];
 #pragma unroll
   for (int c = 0; c < S::NT; ++c) {
     m[c] = -INFINITY;
     mb[c] = 0.0f;
-    lsum[c] = 0.0f;
+    lacc[c] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) o[c][dt] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   const float cs = g.scale_log2;
+  const pf_bf16x8 ones = __builtin_bit_cast(pf_bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  // ---- staging roles
-  // K: piece p -> key (idx / (D/8)), element chunk (idx % (D/8)), idx = tid + 256 p
-  // V: thread -> key pair (tid / (D/8)), element chunk (tid % (D/8)); writes V^T
-  // lo/hi: threads 0..31 -> key tid
-  PfRaw kraw[S::KPIECES], vraw0, vraw1;
+  // ---- staging roles (fixed per thread)
+  // K: thread < KTHREADS -> key tid / DC, piece tid % DC; the piece-0 thread of
+  //    each key also produces the key's visibility interval.
+  // V: thread >= VFIRST -> key pair (tid - VFIRST) / DC, piece % DC; writes V^T.
+  const int kkey = tid / S::DC, kdc = tid % S::DC;
+  const int vidx = tid - S::VFIRST;
+  const int vpair = vidx / S::DC, vdc = vidx % S::DC;
+  PfRaw kraw, vraw0, vraw1;
   int klo = 0, khi = 0;
   auto stage_load = [&](int blk) {
     const int kb = blk * kPfKB;
-#pragma unroll
-    for (int p = 0; p < S::KPIECES; ++p) {
-      const int idx = tid + kPfThreads * p;
-      const PfKey key = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + idx / (D / 8));
-      kraw[p] = pf_load<FP8>(key.k, key.sk, key.kind, idx % (D / 8));
+    const int page = kb < src.L ? src.pt[kb >> g.Pshift] : 0;   // one page per key block
+    if (tid < S::KTHREADS) {
+      const int kk = kb + kkey;
+      kraw = pf_load<D, FP8>(a, src, page, kk, kdc, false);
+      if (kdc == 0) {
+        if (kk < src.L) {
+          const int meta = d.slot_meta[(static_cast<int64_t>(page) << g.Pshift) + (kk & (g.P - 1))];
+          klo = meta & 0x7FFFFFFF;
+          khi = meta < 0 ? klo + g.w : kPfNoLimit;
+        } else if (kk < src.nk) {
+          klo = src.s0 + (kk - src.L);
+          khi = src.ev[kk - src.L] ? klo + g.w : kPfNoLimit;
+        } else {
+          klo = kPfNoLimit;
+          khi = 0;
+        }
+      }
     }
-    if (tid < S::VTHREADS) {
-      const int kp = tid / (D / 8), dc = tid % (D / 8);
-      const PfKey k0 = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + 2 * kp);
-      const PfKey k1 = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + 2 * kp + 1);
-      vraw0 = pf_load<FP8>(k0.v, k0.sv, k0.kind, dc);
-      vraw1 = pf_load<FP8>(k1.v, k1.sv, k1.kind, dc);
-    }
-    if (tid < kPfKB) {
-      const PfKey key = pf_key<D, FP8>(a, pt, row, kh, L, s0, nk, ev, kb + tid);
-      klo = key.lo;
-      khi = key.hi;
+    if (vidx >= 0) {
+      vraw0 = pf_load<D, FP8>(a, src, page, kb + 2 * vpair, vdc, true);
+      vraw1 = pf_load<D, FP8>(a, src, page, kb + 2 * vpair + 1, vdc, true);
     }
   };
   auto stage_write = [&](int buf) {
     uint8_t* b = smem + buf * S::BUF;
-#pragma unroll
-    for (int p = 0; p < S::KPIECES; ++p) {
-      const int idx = tid + kPfThreads * p;
-      *reinterpret_cast<uint4*>(b + (idx / (D / 8)) * S::KROW + 16 * (idx % (D / 8))) = pf_bf16<FP8>(kraw[p]);
-    }
-    if (tid < S::VTHREADS) {
-      const int kp = tid / (D / 8), dc = tid % (D / 8);
-      const uint4 x = pf_bf16<FP8>(vraw0), y = pf_bf16<FP8>(vraw1);
-      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-      uint8_t* vt = b + S::V_OFF + 2 * pf_vcol(2 * kp);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // elements 2e and 2e+1 of keys 2kp (low half) and 2kp+1 (high half)
-        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * e) * S::VROW) = __builtin_amdgcn_perm(ys[e], xs[e], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * e + 1) * S::VROW) = __builtin_amdgcn_perm(ys[e], xs[e], 0x07060302u);
+    if (tid < S::KTHREADS) {
+      *reinterpret_cast<uint4*>(b + kkey * S::KROW + 16 * kdc) = pf_bf16<FP8>(kraw);
+      if (kdc == 0) {
+        reinterpret_cast<int*>(b + S::LO_OFF)[kkey] = klo;
+        reinterpret_cast<int*>(b + S::HI_OFF)[kkey] = khi;
       }
     }
-    if (tid < kPfKB) {
-      reinterpret_cast<int*>(b + S::LO_OFF)[tid] = klo;
-      reinterpret_cast<int*>(b + S::HI_OFF)[tid] = khi;
+    if (vidx >= 0) {
+      const uint4 x = pf_bf16<FP8>(vraw0), y = pf_bf16<FP8>(vraw1);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+      uint8_t* vt = b + S::V_OFF + 2 * pf_vcol(2 * vpair);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // elements 2e and 2e+1 of keys 2*vpair (low half) and 2*vpair+1 (high half)
+        *reinterpret_cast<uint32_t*>(vt + (8 * vdc + 2 * e) * S::VROW) = __builtin_amdgcn_perm(ys[e], xs[e], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vt + (8 * vdc + 2 * e + 1) * S::VROW) =
+            __builtin_amdgcn_perm(ys[e], xs[e], 0x07060302u);
+      }
     }
   };
 
@@ -490,17 +476,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
       // S^T = K Q^T
       pf_f32x4 s[2][S::NT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int c = 0; c < S::NT; ++c) s[kt][c] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           const pf_bf16x8 kf = *reinterpret_cast<const pf_bf16x8*>(b + (16 * kt + l16) * S::KROW + 64 * ks + 16 * G4);
 #pragma unroll
           for (int c = 0; c < S::NT; ++c)
-            s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks], s[kt][c], 0, 0, 0);
+            s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                kf, qf[c][ks], ks == 0 ? pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f} : s[kt][c], 0, 0, 0);
         }
       }
       if (!__all(lane_all)) {
@@ -508,7 +491,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
         const int his[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
 #pragma unroll
         for (int c = 0; c < S::NT; ++c) {
-          const int qp = qpos[c / G];
+          const int qp = qpos[c / S::HW];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const bool vis = los[e] <= qp && qp < his[e];
@@ -516,7 +499,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
           }
         }
       }
-      // running max per column, raised lazily
+      // running max per column, raised lazily (probabilities stay below 2^8)
       float mx[S::NT];
       bool need = false;
 #pragma unroll
@@ -535,22 +518,22 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
             const float alpha = __builtin_amdgcn_exp2f((m[c] - mx[c]) * cs);   // 0 from -inf
             m[c] = mx[c];
             mb[c] = mx[c] * cs;
-            lsum[c] *= alpha;
+            lacc[c] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < S::DT; ++dt) o[c][dt] *= alpha;
           }
         }
       }
-      // P^T (bf16) and O^T += V^T P^T
+      // P^T (bf16) and O^T += V^T P^T, denominator += 1^T P^T
       pf_bf16x8 pk[S::NT];
 #pragma unroll
       for (int c = 0; c < S::NT; ++c) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][c][e & 3], cs, -mb[c]));
-        lsum[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         const uint4 w = make_uint4(pf_pack(p[0], p[1]), pf_pack(p[2], p[3]), pf_pack(p[4], p[5]), pf_pack(p[6], p[7]));
         pk[c] = __builtin_bit_cast(pf_bf16x8, w);
+        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[c], lacc[c], 0, 0, 0);
       }
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) {
@@ -567,15 +550,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attn_mfma_kernel(Prefil
   uint16_t* obase = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int tg = 0; tg < S::TG; ++tg) {
+    if (!qok[tg]) continue;
+    const int t = wtok + tg * 16 + l16;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int c = tg * G + h;
-      float lt = pf_sum_x32(lsum[c]);
-      lt = pf_sum_x16(lt);
-      if (!qok[tg]) continue;
-      const float inv = 1.0f / lt;
-      const int t = wtok + tg * 16 + l16;
-      uint16_t* orow = obase + ((static_cast<size_t>(row) * a.C + t) * g.Hq + kh * G + h) * D + 4 * G4;
+    for (int h = 0; h < S::HW; ++h) {
+      const int c = tg * S::HW + h;
+      const float inv = 1.0f / lacc[c][0];
+      uint16_t* orow = obase + ((static_cast<size_t>(row) * a.C + t) * g.Hq + head0 + h) * D + 4 * G4;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) {
         const pf_f32x4 v = o[c][dt];
