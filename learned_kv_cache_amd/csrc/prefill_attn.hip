@@ -189,12 +189,21 @@ static int launch_generic(const PrefillArgs& a, hipStream_t st) {
 // lane l gets the scores of keys 4*G4+r (and 16+4*G4+r) for query l%16.
 // O^T = V^T P^T: B = P^T is exactly those 8 probabilities per lane when the
 // key index k of the second product is permuted as
-//   k = 8*G4 + i  <->  key (i < 4 ? 4*G4 + i : 16 + 4*G4 + i - 4),
-// so V^T is stored in LDS with its key columns in that order.  One more
-// product with an all-ones A gives the softmax denominator of the same
+//   k = 8*G4 + i  <->  key (i < 4 ? 4*G4 + i : 16 + 4*G4 + i - 4).
+// V stays row-major in LDS like K; its A fragments (4 keys at one head_dim
+// column per lane, twice) come from the transposing LDS read
+// ds_read_b64_tr_b16: within 16 lanes, lane i receives elements i, 16+i,
+// 32+i, 48+i of the 64 the group addresses, so lanes 4r..4r+3 pointing at 16
+// consecutive columns of key row r hand lane i the column i of 4 keys.  One
+// more product with an all-ones A gives the softmax denominator of the same
 // bf16-rounded probabilities in every row of an extra accumulator tile.
+//
+// LDS rows are 2*D + 32 bytes: with that stride both the K reads (16 bytes
+// per lane) and the transposing V reads are free of bank conflicts on gfx950.
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) pf_i16x4 pf_lds_i16x4;
 typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
 typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
@@ -215,24 +224,16 @@ struct PfShape {
   static constexpr int TOKB = TOKW * kPfWaves / HS;   // tokens per workgroup
   static constexpr int KS = D / 32;           // k-steps of S^T over head_dim
   static constexpr int DT = D / 16;           // 16-row tiles of O^T
-  static constexpr int KROW = 2 * D + 16;     // bytes per K row in LDS (padded: conflict-free reads)
-  static constexpr int VROW = 2 * kPfKB + 16; // bytes per V^T row
-  static constexpr int V_OFF = kPfKB * KROW;
-  static constexpr int LO_OFF = V_OFF + D * VROW;
+  static constexpr int ROW = 2 * D + 32;      // bytes per K or V row in LDS
+  static constexpr int V_OFF = kPfKB * ROW;
+  static constexpr int LO_OFF = 2 * kPfKB * ROW;
   static constexpr int HI_OFF = LO_OFF + 4 * kPfKB;
   static constexpr int BUF = HI_OFF + 4 * kPfKB;
   static constexpr int DC = D / 8;            // 16-byte pieces per bf16 row
-  static constexpr int KTHREADS = kPfKB * DC;         // one K piece each
-  static constexpr int VTHREADS = (kPfKB / 2) * DC;   // one V key-pair piece each
-  static constexpr int VFIRST = kPfThreads - VTHREADS;
-  static_assert(NT == 2 && KTHREADS <= kPfThreads && VTHREADS <= kPfThreads, "shape");
+  static constexpr int STHREADS = kPfKB * DC; // threads staging one K and one V piece each
+  static_assert(NT == 2 && STHREADS <= kPfThreads, "shape");
   static_assert(BUF % 16 == 0, "LDS alignment");
 };
-
-// LDS column of key k (0..31) in the permuted V^T storage.
-__device__ __forceinline__ int pf_vcol(int k) {
-  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
-}
 
 // max / sum of lane l and lane l ^ 32 (resp. l ^ 16): v_permlane32_swap and
 // v_permlane16_swap return the pair (own, partner) in a lane-independent order.
@@ -396,22 +397,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   const float cs = g.scale_log2;
   const pf_bf16x8 ones = __builtin_bit_cast(pf_bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  // ---- staging roles (fixed per thread)
-  // K: thread < KTHREADS -> key tid / DC, piece tid % DC; the piece-0 thread of
-  //    each key also produces the key's visibility interval.
-  // V: thread >= VFIRST -> key pair (tid - VFIRST) / DC, piece % DC; writes V^T.
-  const int kkey = tid / S::DC, kdc = tid % S::DC;
-  const int vidx = tid - S::VFIRST;
-  const int vpair = vidx / S::DC, vdc = vidx % S::DC;
-  PfRaw kraw, vraw0, vraw1;
+  // ---- staging roles (fixed per thread): thread < STHREADS stages piece
+  // tid % DC of key tid / DC for K and V; the piece-0 thread of each key also
+  // produces the key's visibility interval.
+  const int skey = tid / S::DC, sdc = tid % S::DC;
+  PfRaw kraw, vraw;
   int klo = 0, khi = 0;
   auto stage_load = [&](int blk) {
     const int kb = blk * kPfKB;
     const int page = kb < src.L ? src.pt[kb >> g.Pshift] : 0;   // one page per key block
-    if (tid < S::KTHREADS) {
-      const int kk = kb + kkey;
-      kraw = pf_load<D, FP8>(a, src, page, kk, kdc, false);
-      if (kdc == 0) {
+    if (tid < S::STHREADS) {
+      const int kk = kb + skey;
+      kraw = pf_load<D, FP8>(a, src, page, kk, sdc, false);
+      vraw = pf_load<D, FP8>(a, src, page, kk, sdc, true);
+      if (sdc == 0) {
         if (kk < src.L) {
           const int meta = d.slot_meta[(static_cast<int64_t>(page) << g.Pshift) + (kk & (g.P - 1))];
           klo = meta & 0x7FFFFFFF;
@@ -425,30 +424,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
         }
       }
     }
-    if (vidx >= 0) {
-      vraw0 = pf_load<D, FP8>(a, src, page, kb + 2 * vpair, vdc, true);
-      vraw1 = pf_load<D, FP8>(a, src, page, kb + 2 * vpair + 1, vdc, true);
-    }
   };
   auto stage_write = [&](int buf) {
     uint8_t* b = smem + buf * S::BUF;
-    if (tid < S::KTHREADS) {
-      *reinterpret_cast<uint4*>(b + kkey * S::KROW + 16 * kdc) = pf_bf16<FP8>(kraw);
-      if (kdc == 0) {
-        reinterpret_cast<int*>(b + S::LO_OFF)[kkey] = klo;
-        reinterpret_cast<int*>(b + S::HI_OFF)[kkey] = khi;
-      }
-    }
-    if (vidx >= 0) {
-      const uint4 x = pf_bf16<FP8>(vraw0), y = pf_bf16<FP8>(vraw1);
-      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-      uint8_t* vt = b + S::V_OFF + 2 * pf_vcol(2 * vpair);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // elements 2e and 2e+1 of keys 2*vpair (low half) and 2*vpair+1 (high half)
-        *reinterpret_cast<uint32_t*>(vt + (8 * vdc + 2 * e) * S::VROW) = __builtin_amdgcn_perm(ys[e], xs[e], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vt + (8 * vdc + 2 * e + 1) * S::VROW) =
-            __builtin_amdgcn_perm(ys[e], xs[e], 0x07060302u);
+    if (tid < S::STHREADS) {
+      *reinterpret_cast<uint4*>(b + skey * S::ROW + 16 * sdc) = pf_bf16<FP8>(kraw);
+      *reinterpret_cast<uint4*>(b + S::V_OFF + skey * S::ROW + 16 * sdc) = pf_bf16<FP8>(vraw);
+      if (sdc == 0) {
+        reinterpret_cast<int*>(b + S::LO_OFF)[skey] = klo;
+        reinterpret_cast<int*>(b + S::HI_OFF)[skey] = khi;
       }
     }
   };
@@ -479,7 +463,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
       for (int ks = 0; ks < S::KS; ++ks) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const pf_bf16x8 kf = *reinterpret_cast<const pf_bf16x8*>(b + (16 * kt + l16) * S::KROW + 64 * ks + 16 * G4);
+          const pf_bf16x8 kf = *reinterpret_cast<const pf_bf16x8*>(b + (16 * kt + l16) * S::ROW + 64 * ks + 16 * G4);
 #pragma unroll
           for (int c = 0; c < S::NT; ++c)
             s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -537,7 +521,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
       }
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) {
-        const pf_bf16x8 vf = *reinterpret_cast<const pf_bf16x8*>(b + S::V_OFF + (16 * dt + l16) * S::VROW + 16 * G4);
+        // keys 4*G4 + 0..3 and 16 + 4*G4 + 0..3 at column 16*dt + l16
+        const uint8_t* vb = b + S::V_OFF + (4 * G4 + (l16 >> 2)) * S::ROW + 32 * dt + 8 * (l16 & 3);
+        const pf_i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vb));
+        const pf_i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vb + 16 * S::ROW));
+        const pf_bf16x8 vf = __builtin_bit_cast(pf_bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int c = 0; c < S::NT; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[c], o[c][dt], 0, 0, 0);
       }
