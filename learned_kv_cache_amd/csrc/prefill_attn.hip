@@ -212,9 +212,10 @@ constexpr int kPfKB = 32;         // keys per LDS block
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfNoLimit = 0x7FFFFFFF;
+constexpr int kPfMaxPages = 4096;  // page-table entries of a unit held in LDS (larger tables: vector kernel)
 constexpr float kPfRescaleLog2 = 8.0f;   // running max is raised only when exceeded by this (log2 units)
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 struct PfShape {
   static constexpr int HW = G < 2 ? G : 2;    // query heads per wave
   static constexpr int HS = G / HW;           // waves sharing one token group (head split)
@@ -224,15 +225,26 @@ struct PfShape {
   static constexpr int TOKB = TOKW * kPfWaves / HS;   // tokens per workgroup
   static constexpr int KS = D / 32;           // k-steps of S^T over head_dim
   static constexpr int DT = D / 16;           // 16-row tiles of O^T
-  static constexpr int ROW = 2 * D + 32;      // bytes per K or V row in LDS
+  // LDS tiles of one key block.  bf16 pages arrive by direct global->LDS
+  // loads into unpadded rows whose 16-byte chunks are XOR-swizzled per row;
+  // fp8 pages are dequantised through registers into rows padded to 2D+32
+  // bytes.  Both layouts keep the K reads and the transposing V reads free of
+  // bank conflicts on gfx950.
+  static constexpr bool DMA = !FP8;
+  static constexpr int ROW = DMA ? 2 * D : 2 * D + 32;
+  static constexpr int CPR = 2 * D / 16;      // 16-byte chunks per row
   static constexpr int V_OFF = kPfKB * ROW;
-  static constexpr int LO_OFF = 2 * kPfKB * ROW;
+  static constexpr int META_OFF = 2 * kPfKB * ROW;   // slot metadata of the block's cache keys
+  static constexpr int LO_OFF = META_OFF + 4 * kPfKB;
   static constexpr int HI_OFF = LO_OFF + 4 * kPfKB;
   static constexpr int BUF = HI_OFF + 4 * kPfKB;
   static constexpr int DC = D / 8;            // 16-byte pieces per bf16 row
-  static constexpr int STHREADS = kPfKB * DC; // threads staging one K and one V piece each
+  static constexpr int STHREADS = kPfKB * DC; // register path: threads staging one K and one V piece each
   static_assert(NT == 2 && STHREADS <= kPfThreads, "shape");
-  static_assert(BUF % 16 == 0, "LDS alignment");
+  static_assert(BUF % 16 == 0 && (!DMA || 1024 % ROW == 0), "LDS layout");
+  __device__ static int swz(int r) { return D == 128 ? 2 * (r & 7) : (r & 6); }
+  // byte offset of 16-byte chunk c of row r in a tile
+  __device__ static int off(int r, int c) { return r * ROW + 16 * (DMA ? (c ^ swz(r)) : c); }
 };
 
 // max / sum of lane l and lane l ^ 32 (resp. l ^ 16): v_permlane32_swap and
@@ -281,24 +293,25 @@ template <int D, bool FP8>
 __device__ __forceinline__ PfRaw pf_load(const PrefillArgs& a, const PfSrc& q, int page, int kk, int dc, bool v) {
   PfRaw r;
   r.sc = 1.0f;
-  if (kk < q.L) {
-    const int64_t prow = (static_cast<int64_t>(page) << a.g.Pshift) + (kk & (a.g.P - 1));
-    r.kind = 1;
-    if (FP8) {
+  // keys past the end are masked out by their visibility interval; they read
+  // the last key's row so every loaded value is finite
+  const int kc = min(kk, q.nk - 1);
+  const bool cache = kc < q.L;
+  r.kind = cache ? 1 : 2;
+  const int64_t prow = (static_cast<int64_t>(page) << a.g.Pshift) + (kc & (a.g.P - 1));
+  if (FP8) {
+    if (cache) {
       const uint8_t* base = (v ? a.d.v_pages : a.d.k_pages) + prow * D;
       const uint2 t = *reinterpret_cast<const uint2*>(base + 8 * dc);
       r.w = make_uint4(t.x, t.y, 0, 0);
       r.sc = a.d.scales[2 * page + (v ? 1 : 0)];
     } else {
-      const uint8_t* base = (v ? a.d.v_pages : a.d.k_pages) + prow * D * 2;
-      r.w = *reinterpret_cast<const uint4*>(base + 16 * dc);
+      r.w = *reinterpret_cast<const uint4*>((v ? q.vchunk : q.kchunk) + (kc - q.L) * q.chunk_stride + 16 * dc);
     }
-  } else if (kk < q.nk) {
-    r.kind = 2;
-    r.w = *reinterpret_cast<const uint4*>((v ? q.vchunk : q.kchunk) + (kk - q.L) * q.chunk_stride + 16 * dc);
   } else {
-    r.kind = 0;
-    r.w = make_uint4(0, 0, 0, 0);
+    const uint8_t* pbase = (v ? a.d.v_pages : a.d.k_pages) + prow * D * 2;
+    const uint8_t* cbase = (v ? q.vchunk : q.kchunk) + (kc - q.L) * q.chunk_stride;
+    r.w = *reinterpret_cast<const uint4*>((cache ? pbase : cbase) + 16 * dc);
   }
   return r;
 }
@@ -309,14 +322,24 @@ __device__ __forceinline__ uint4 pf_bf16(const PfRaw& r) {
   return r.w;
 }
 
+typedef __attribute__((address_space(3))) void pf_lds_void;
+typedef __attribute__((address_space(1))) void pf_glb_void;
+
 template <int D, int G, bool FP8>
 __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillArgs a) {
-  using S = PfShape<D, G>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BUF];
+  using S = PfShape<D, G, FP8>;
+  // two key-block buffers as separate arrays: with the loop unrolled by two
+  // each step's buffers are static, so loads into one are known not to alias
+  // reads of the other
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf0[S::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf1[S::BUF];
+  __shared__ int s_pt[kPfMaxPages];      // the unit's page table
+  __shared__ uint8_t s_ev[kMaxChunk];    // the chunk's evict flags of this KV head
   const DevCache& d = a.d;
   const Geo& g = a.g;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int l16 = lane & 15, G4 = lane >> 4;
 
   // Linear workgroup id -> (pair, token block), the heaviest (last) token
@@ -327,7 +350,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   const int tb = ntb - 1 - static_cast<int>(blockIdx.x) / npairs;
   const int row = pair / g.Hkv, kh = pair % g.Hkv;
   const int seq = a.seq_ids ? a.seq_ids[row] : row;
-  if (seq < 0 || seq >= g.Bmax) {
+  if (seq < 0 || seq >= g.Bmax) {   // uniform over the workgroup: no wave reaches a barrier
     if (tid == 0 && tb == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
     return;
   }
@@ -397,55 +420,40 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   const float cs = g.scale_log2;
   const pf_bf16x8 ones = __builtin_bit_cast(pf_bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  // ---- staging roles (fixed per thread): thread < STHREADS stages piece
-  // tid % DC of key tid / DC for K and V; the piece-0 thread of each key also
-  // produces the key's visibility interval.
-  const int skey = tid / S::DC, sdc = tid % S::DC;
-  PfRaw kraw, vraw;
-  int klo = 0, khi = 0;
-  auto stage_load = [&](int blk) {
-    const int kb = blk * kPfKB;
-    const int page = kb < src.L ? src.pt[kb >> g.Pshift] : 0;   // one page per key block
-    if (tid < S::STHREADS) {
-      const int kk = kb + skey;
-      kraw = pf_load<D, FP8>(a, src, page, kk, sdc, false);
-      vraw = pf_load<D, FP8>(a, src, page, kk, sdc, true);
-      if (sdc == 0) {
-        if (kk < src.L) {
-          const int meta = d.slot_meta[(static_cast<int64_t>(page) << g.Pshift) + (kk & (g.P - 1))];
-          klo = meta & 0x7FFFFFFF;
-          khi = meta < 0 ? klo + g.w : kPfNoLimit;
-        } else if (kk < src.nk) {
-          klo = src.s0 + (kk - src.L);
-          khi = src.ev[kk - src.L] ? klo + g.w : kPfNoLimit;
-        } else {
-          klo = kPfNoLimit;
-          khi = 0;
-        }
-      }
-    }
-  };
-  auto stage_write = [&](int buf) {
-    uint8_t* b = smem + buf * S::BUF;
-    if (tid < S::STHREADS) {
-      *reinterpret_cast<uint4*>(b + skey * S::ROW + 16 * sdc) = pf_bf16<FP8>(kraw);
-      *reinterpret_cast<uint4*>(b + S::V_OFF + skey * S::ROW + 16 * sdc) = pf_bf16<FP8>(vraw);
-      if (sdc == 0) {
-        reinterpret_cast<int*>(b + S::LO_OFF)[skey] = klo;
-        reinterpret_cast<int*>(b + S::HI_OFF)[skey] = khi;
-      }
-    }
-  };
-
-  stage_load(0);
-  stage_write(0);
+  // ---- the unit's page table and the chunk's evict flags, once
+  {
+    const int npages = (src.L + g.P - 1) >> g.Pshift;   // <= kPfMaxPages (checked at launch)
+    for (int i = tid; i < npages; i += kPfThreads) s_pt[i] = src.pt[i];
+    for (int i = tid; i < tok_end; i += kPfThreads) s_ev[i] = src.ev[i];
+  }
   __syncthreads();
+  // page of a key block (P is a multiple of the block: one page per block)
+  auto block_page = [&](int kb) { return kb < src.L ? s_pt[kb >> g.Pshift] : 0; };
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    if (blk + 1 < nblk) stage_load(blk + 1);
-    const uint8_t* b = smem + (blk & 1) * S::BUF;
+  // ---- visibility intervals [lo, hi) of a block's keys, by lanes 0..31 of the
+  // last wave; cache keys decode the slot metadata staged at META_OFF
+  const bool vis_wave = wave == kPfWaves - 1;
+  auto vis_write = [&](int blk, uint8_t* b, int meta) {
+    if (vis_wave && lane < kPfKB) {
+      const int kk = blk * kPfKB + lane;
+      int lo, hi;
+      if (kk < src.L) {
+        lo = meta & 0x7FFFFFFF;
+        hi = meta < 0 ? lo + g.w : kPfNoLimit;
+      } else if (kk < src.nk) {
+        lo = src.s0 + (kk - src.L);
+        hi = s_ev[kk - src.L] ? lo + g.w : kPfNoLimit;
+      } else {
+        lo = kPfNoLimit;
+        hi = 0;
+      }
+      reinterpret_cast<int*>(b + S::LO_OFF)[lane] = lo;
+      reinterpret_cast<int*>(b + S::HI_OFF)[lane] = hi;
+    }
+  };
 
-    // visibility of this block for the wave
+  // ---- one key block's products and softmax (LDS buffer b)
+  auto compute = [&](const uint8_t* b) {
     const int4 lo0 = *reinterpret_cast<const int4*>(b + S::LO_OFF + 16 * G4);
     const int4 lo1 = *reinterpret_cast<const int4*>(b + S::LO_OFF + 64 + 16 * G4);
     const int4 hi0 = *reinterpret_cast<const int4*>(b + S::HI_OFF + 16 * G4);
@@ -456,82 +464,188 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
     const int hmax = max(max(max(hi0.x, hi0.y), max(hi0.z, hi0.w)), max(max(hi1.x, hi1.y), max(hi1.z, hi1.w)));
     const bool lane_none = !lane_live || lmin > qmax || hmax <= qmin;
     const bool lane_all = !lane_live || (lmax <= qmin && hmin > qmax);
-    if (!__all(lane_none)) {
-      // S^T = K Q^T
-      pf_f32x4 s[2][S::NT];
+    if (__all(lane_none)) return;
+    // S^T = K Q^T
+    pf_f32x4 s[2][S::NT];
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
+    for (int ks = 0; ks < S::KS; ++ks) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const pf_bf16x8 kf = *reinterpret_cast<const pf_bf16x8*>(b + (16 * kt + l16) * S::ROW + 64 * ks + 16 * G4);
+      for (int kt = 0; kt < 2; ++kt) {
+        const pf_bf16x8 kf = *reinterpret_cast<const pf_bf16x8*>(b + S::off(16 * kt + l16, 4 * ks + G4));
 #pragma unroll
-          for (int c = 0; c < S::NT; ++c)
-            s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                kf, qf[c][ks], ks == 0 ? pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f} : s[kt][c], 0, 0, 0);
-        }
-      }
-      if (!__all(lane_all)) {
-        const int los[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
-        const int his[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
-#pragma unroll
-        for (int c = 0; c < S::NT; ++c) {
-          const int qp = qpos[c / S::HW];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const bool vis = los[e] <= qp && qp < his[e];
-            s[e >> 2][c][e & 3] = vis ? s[e >> 2][c][e & 3] : -INFINITY;
-          }
-        }
-      }
-      // running max per column, raised lazily (probabilities stay below 2^8)
-      float mx[S::NT];
-      bool need = false;
-#pragma unroll
-      for (int c = 0; c < S::NT; ++c) {
-        float x = fmaxf(fmaxf(fmaxf(s[0][c][0], s[0][c][1]), fmaxf(s[0][c][2], s[0][c][3])),
-                        fmaxf(fmaxf(s[1][c][0], s[1][c][1]), fmaxf(s[1][c][2], s[1][c][3])));
-        x = pf_max_x32(x);
-        x = pf_max_x16(x);
-        mx[c] = x;
-        need |= x * cs > m[c] * cs + kPfRescaleLog2;
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int c = 0; c < S::NT; ++c) {
-          if (mx[c] * cs > m[c] * cs + kPfRescaleLog2) {
-            const float alpha = __builtin_amdgcn_exp2f((m[c] - mx[c]) * cs);   // 0 from -inf
-            m[c] = mx[c];
-            mb[c] = mx[c] * cs;
-            lacc[c] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < S::DT; ++dt) o[c][dt] *= alpha;
-          }
-        }
-      }
-      // P^T (bf16) and O^T += V^T P^T, denominator += 1^T P^T
-      pf_bf16x8 pk[S::NT];
-#pragma unroll
-      for (int c = 0; c < S::NT; ++c) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][c][e & 3], cs, -mb[c]));
-        const uint4 w = make_uint4(pf_pack(p[0], p[1]), pf_pack(p[2], p[3]), pf_pack(p[4], p[5]), pf_pack(p[6], p[7]));
-        pk[c] = __builtin_bit_cast(pf_bf16x8, w);
-        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[c], lacc[c], 0, 0, 0);
-      }
-#pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) {
-        // keys 4*G4 + 0..3 and 16 + 4*G4 + 0..3 at column 16*dt + l16
-        const uint8_t* vb = b + S::V_OFF + (4 * G4 + (l16 >> 2)) * S::ROW + 32 * dt + 8 * (l16 & 3);
-        const pf_i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vb));
-        const pf_i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vb + 16 * S::ROW));
-        const pf_bf16x8 vf = __builtin_bit_cast(pf_bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int c = 0; c < S::NT; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[c], o[c][dt], 0, 0, 0);
+        for (int c = 0; c < S::NT; ++c)
+          s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf, qf[c][ks], ks == 0 ? pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f} : s[kt][c], 0, 0, 0);
       }
     }
-    if (blk + 1 < nblk) stage_write((blk + 1) & 1);
+    if (!__all(lane_all)) {
+      const int los[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
+      const int his[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
+#pragma unroll
+      for (int c = 0; c < S::NT; ++c) {
+        const int qp = qpos[c / S::HW];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool vis = los[e] <= qp && qp < his[e];
+          s[e >> 2][c][e & 3] = vis ? s[e >> 2][c][e & 3] : -INFINITY;
+        }
+      }
+    }
+    // running max per column, raised lazily (probabilities stay below 2^8)
+    float mx[S::NT];
+    bool need = false;
+#pragma unroll
+    for (int c = 0; c < S::NT; ++c) {
+      float x = fmaxf(fmaxf(fmaxf(s[0][c][0], s[0][c][1]), fmaxf(s[0][c][2], s[0][c][3])),
+                      fmaxf(fmaxf(s[1][c][0], s[1][c][1]), fmaxf(s[1][c][2], s[1][c][3])));
+      x = pf_max_x32(x);
+      x = pf_max_x16(x);
+      mx[c] = x;
+      need |= x * cs > m[c] * cs + kPfRescaleLog2;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int c = 0; c < S::NT; ++c) {
+        if (mx[c] * cs > m[c] * cs + kPfRescaleLog2) {
+          const float alpha = __builtin_amdgcn_exp2f((m[c] - mx[c]) * cs);   // 0 from -inf
+          m[c] = mx[c];
+          mb[c] = mx[c] * cs;
+          lacc[c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < S::DT; ++dt) o[c][dt] *= alpha;
+        }
+      }
+    }
+    // P^T (bf16) and O^T += V^T P^T, denominator += 1^T P^T
+    pf_bf16x8 pk[S::NT];
+#pragma unroll
+    for (int c = 0; c < S::NT; ++c) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][c][e & 3], cs, -mb[c]));
+      const uint4 w = make_uint4(pf_pack(p[0], p[1]), pf_pack(p[2], p[3]), pf_pack(p[4], p[5]), pf_pack(p[6], p[7]));
+      pk[c] = __builtin_bit_cast(pf_bf16x8, w);
+      lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[c], lacc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+      // keys 4*G4 + 0..3 and 16 + 4*G4 + 0..3 at column 16*dt + l16
+      const int r0 = 4 * G4 + (l16 >> 2), ch = 2 * dt + ((l16 & 3) >> 1), half = 8 * (l16 & 1);
+      const uint8_t* vb = b + S::V_OFF;
+      const pf_i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vb + S::off(r0, ch) + half));
+      const pf_i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vb + S::off(r0 + 16, ch) + half));
+      const pf_bf16x8 vf = __builtin_bit_cast(pf_bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int c = 0; c < S::NT; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[c], o[c][dt], 0, 0, 0);
+    }
+  };
+
+  if constexpr (S::DMA) {
+    // ---- bf16 pages: direct global->LDS loads.  Lane i of a wave-wide load
+    // writes bytes [16 i, 16 i + 16) of a 1 KB stretch (whole rows); it reads
+    // the chunk that the row's swizzle places there.  Keys past the end read
+    // the last key's row (finite values; their interval hides them).
+    auto row_src = [&](int page, int kk, bool v) {
+      const int kc = min(kk, src.nk - 1);
+      const uint8_t* pr = (v ? d.v_pages : d.k_pages) +
+                          ((static_cast<int64_t>(page) << g.Pshift) + (kc & (g.P - 1))) * (D * 2);
+      const uint8_t* cr = (v ? src.vchunk : src.kchunk) + static_cast<int64_t>(kc - src.L) * src.chunk_stride;
+      return kc < src.L ? pr : cr;
+    };
+    auto dma_issue = [&](int blk, uint8_t* b) {
+      const int kb = blk * kPfKB;
+      const int page = block_page(kb);
+      constexpr int RPW = 1024 / S::ROW;   // rows per wave-wide load
+      if constexpr (D == 128) {
+        const int r = wave * RPW + lane / S::CPR, c = (lane % S::CPR) ^ S::swz(r);
+        __builtin_amdgcn_global_load_lds((const pf_glb_void*)(row_src(page, kb + r, false) + 16 * c),
+                                         (pf_lds_void*)(b + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const pf_glb_void*)(row_src(page, kb + r, true) + 16 * c),
+                                         (pf_lds_void*)(b + S::V_OFF + wave * 1024), 16, 0, 0);
+      } else {
+        const int w4 = wave & 3;
+        const bool isv = wave >= 4;
+        const int r = w4 * RPW + lane / S::CPR, c = (lane % S::CPR) ^ S::swz(r);
+        __builtin_amdgcn_global_load_lds((const pf_glb_void*)(row_src(page, kb + r, isv) + 16 * c),
+                                         (pf_lds_void*)(b + (isv ? S::V_OFF : 0) + w4 * 1024), 16, 0, 0);
+      }
+      if (vis_wave && kb < src.L && lane < kPfKB) {
+        const int kc = min(kb + lane, src.L - 1);   // same page as kb
+        __builtin_amdgcn_global_load_lds(
+            (const pf_glb_void*)(d.slot_meta + (static_cast<int64_t>(page) << g.Pshift) + (kc & (g.P - 1))),
+            (pf_lds_void*)(b + S::META_OFF), 4, 0, 0);
+      }
+    };
+    auto vis_from_lds = [&](int blk, uint8_t* b) {
+      const int meta = vis_wave && lane < kPfKB ? reinterpret_cast<const int*>(b + S::META_OFF)[lane] : 0;
+      vis_write(blk, b, meta);
+    };
+
+    dma_issue(0, sbuf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vis_from_lds(0, sbuf0);
     __syncthreads();
+    // block blk in sbuf0 while blk+1 loads into sbuf1, then the reverse; each
+    // step ends with this wave's loads complete and one barrier
+    for (int blk = 0; blk < nblk; blk += 2) {
+      if (blk + 1 < nblk) dma_issue(blk + 1, sbuf1);
+      compute(sbuf0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (blk + 1 < nblk) vis_from_lds(blk + 1, sbuf1);
+      __syncthreads();
+      if (blk + 1 >= nblk) break;
+      if (blk + 2 < nblk) dma_issue(blk + 2, sbuf0);
+      compute(sbuf1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (blk + 2 < nblk) vis_from_lds(blk + 2, sbuf0);
+      __syncthreads();
+    }
+  } else {
+    // ---- fp8 pages: loads into registers two blocks ahead of the LDS
+    // writes; staging runs unconditionally (blocks past the end load clamped
+    // rows and land in a buffer nobody reads again), so every path issues and
+    // consumes the same loads
+    const int skey = tid / S::DC, sdc = tid % S::DC;
+    struct Stage {
+      PfRaw k, v;
+      int meta;     // slot metadata of the key's cache row (visibility wave)
+    };
+    Stage st0, st1;
+    auto stage_load = [&](int blk, Stage& sg) {
+      const int kb = blk * kPfKB;
+      const int page = block_page(kb);
+      if (tid < S::STHREADS) {
+        const int kk = kb + skey;
+        sg.k = pf_load<D, FP8>(a, src, page, kk, sdc, false);
+        sg.v = pf_load<D, FP8>(a, src, page, kk, sdc, true);
+      }
+      if (vis_wave) {
+        const int kk = kb + (lane & 31);
+        sg.meta = d.slot_meta[kk < src.L ? (static_cast<int64_t>(page) << g.Pshift) + (kk & (g.P - 1)) : 0];
+      }
+    };
+    auto stage_write = [&](uint8_t* b, int blk, const Stage& sg) {
+      if (tid < S::STHREADS) {
+        *reinterpret_cast<uint4*>(b + S::off(skey, sdc)) = pf_bf16<FP8>(sg.k);
+        *reinterpret_cast<uint4*>(b + S::V_OFF + S::off(skey, sdc)) = pf_bf16<FP8>(sg.v);
+      }
+      vis_write(blk, b, sg.meta);
+    };
+    stage_load(0, st0);
+    stage_write(sbuf0, 0, st0);
+    stage_load(1, st1);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; blk += 2) {
+      stage_load(blk + 2, st0);
+      compute(sbuf0);
+      stage_write(sbuf1, blk + 1, st1);
+      __syncthreads();
+      if (blk + 1 >= nblk) break;
+      stage_load(blk + 3, st1);
+      compute(sbuf1);
+      stage_write(sbuf0, blk + 2, st0);
+      __syncthreads();
+    }
   }
 
   // ---- normalise and store: lane holds d = 16 dt + 4 G4 + r of its column
@@ -556,7 +670,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
 
 template <int D, int G, bool FP8>
 static int launch_mfma_dgf(const PrefillArgs& a, hipStream_t st) {
-  using S = PfShape<D, G>;
+  using S = PfShape<D, G, FP8>;
   const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
   const dim3 grid(ntb * a.B * a.g.Hkv), block(kPfThreads);
   hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, FP8>), grid, block, 0, st, a);
@@ -575,7 +689,7 @@ static int launch_mfma_d(const PrefillArgs& a, hipStream_t st) {
 
 static bool mfma_ok(const Geo& g) {
   return (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) &&
-         (g.g == 1 || g.g == 2 || g.g == 4) && g.Pshift >= 5;
+         (g.g == 1 || g.g == 2 || g.g == 4) && g.Pshift >= 5 && g.maxp <= kPfMaxPages;
 }
 
 static int launch_mfma(const PrefillArgs& a, hipStream_t st) {
