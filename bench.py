@@ -237,65 +237,87 @@ def run_decode(args, dms, synth, torch):
     }
 
 
-def run_prefill(args, dms, synth, torch):
-    """32K-token prompt in 4096-token chunks (query-neuron decisions, offset 5):
-    per chunk dms_decide -> dms_prefill_attn -> dms_append_evict."""
-    wl = synth.QWEN8B_PREFILL32K
+def run_prefill(args, dms, synth, torch, variant="qneuron"):
+    """32K-token prompt in 4096-token chunks: per chunk dms_decide ->
+    dms_prefill_attn -> dms_append_evict, each call timed with HIP events on
+    the launch stream.  variant "qneuron": decision from the last query
+    element (offset 5); "linear": RMSNorm + linear adapter over a
+    4096-wide bf16 hidden state (a = 100, offset 5)."""
+    wl = synth.QWEN8B_PREFILL32K if variant == "qneuron" else synth.QWEN8B_PREFILL32K_LINEAR
     T, C = wl.prefill, wl.chunk
+    nch = T // C
     cfg = dms.make_config(
         max_batch=1, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
         window=wl.window, block_size=wl.block, max_tokens_per_seq=T, pool_pages=wl.Hkv * (T // wl.block),
-        max_chunk=C, kv_dtype="bf16", decide_mode="qneuron", alpha_per="head")
+        max_chunk=C, kv_dtype="bf16", decide_mode=wl.decide, alpha_per="head")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1000 + wl.cfg_id)
-    q = torch.randn(T // C, 1, C, wl.Hq, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
-    k = torch.randn(T // C, 1, C, wl.Hkv, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
-    v = torch.randn(T // C, 1, C, wl.Hkv, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    q = torch.randn(nch, 1, C, wl.Hq, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn(nch, 1, C, wl.Hkv, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(nch, 1, C, wl.Hkv, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    h = W = gamma = None
+    if variant == "linear":
+        h = torch.randn(nch, 1, C, wl.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+        W = torch.randn(wl.Hkv, wl.hidden, generator=gen, device="cuda") / math.sqrt(wl.hidden)
+        gamma = torch.ones(wl.hidden, device="cuda")
     off = torch.full((wl.Hkv,), float(wl.fixed_offset), device="cuda")
-    ev = torch.empty(T // C, wl.Hkv * C, dtype=torch.uint8, device="cuda")
+    ev = torch.empty(nch, wl.Hkv * C, dtype=torch.uint8, device="cuda")
     out = torch.empty(1, C, wl.Hq, wl.D, dtype=torch.bfloat16, device="cuda")
 
-    def once(qq, times=None):
+    def once(qq, ev_times=None):
         cache = dms.DmsCache(cfg)
-        for c in range(T // C):
-            dms.dms_decide(cache, None, None, None, None, off, qq[c], 1, C, None, ev[c])
-            if times is not None:
-                times[c][0].record()
+        for c in range(nch):
+            e = ev_times[c] if ev_times else None
+            if e:
+                e[0].record()
+            if variant == "qneuron":
+                dms.dms_decide(cache, None, None, None, None, off, qq[c], 1, C, None, ev[c])
+            else:
+                dms.dms_decide(cache, h[c], gamma, W, None, off, None, 1, C, None, ev[c])
+            if e:
+                e[1].record()
             dms.dms_prefill_attn(cache, None, qq[c], k[c], v[c], ev[c], out, 1, C)
-            if times is not None:
-                times[c][1].record()
+            if e:
+                e[2].record()
             dms.dms_append_evict(cache, None, k[c], v[c], ev[c], 1, C)
+            if e:
+                e[3].record()
         return cache
 
     once(q.clone())
     torch.cuda.synchronize()
     qq = q.clone()
-    times = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T // C)]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    times = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nch)]
     once(qq, times)
-    e1.record()
     torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    attn_ms = sum(a.elapsed_time(b) for a, b in times)
+    decide_ms = sum(t[0].elapsed_time(t[1]) for t in times)
+    attn_ms = sum(t[1].elapsed_time(t[2]) for t in times)
+    append_ms = sum(t[2].elapsed_time(t[3]) for t in times)
+    total_ms = times[0][0].elapsed_time(times[-1][3])
     # useful flops: 4 * D per (query head, visible key) pair; |V(i)| = (i+1) - #{j <= i-w: e_j}
-    e = ev.view(T // C, wl.Hkv, C).permute(1, 0, 2).reshape(wl.Hkv, T).to(torch.int64)
+    e = ev.view(nch, wl.Hkv, C).permute(1, 0, 2).reshape(wl.Hkv, T).to(torch.int64)
     ce = torch.cumsum(e, dim=1)
     i = torch.arange(T, device="cuda")
     evicted_out = torch.where(i >= wl.window, ce[:, (i - wl.window).clamp(min=0)], torch.zeros_like(ce))
     vis = (i + 1)[None, :] - evicted_out
     useful = 4.0 * wl.D * wl.g * float(vis.sum())
-    return {
+    res = {
         "workload": wl.name,
         "tokens": T,
         "ms_per_prompt": total_ms,
         "tok_s": T / (total_ms / 1e3),
+        "decide_ms": decide_ms,
         "attn_ms": attn_ms,
+        "append_ms": append_ms,
         "useful_tflop": useful / 1e12,
         "attn_tflops": useful / (attn_ms * 1e-3) / 1e12,
         "frac_bf16_peak": useful / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "evict_fraction": float(e.float().mean()),
     }
+    if variant == "linear":
+        hbytes = T * wl.hidden * 2
+        res["decide_hbm_gbs"] = hbytes / (decide_ms * 1e-3) / 1e9
+    return res
 
 
 def cpu_baseline(steps: int):
@@ -389,9 +411,12 @@ def main() -> int:
     dms.lib()
     torch.cuda.set_device(0)
     dec = run_decode(args, dms, synth, torch)
-    pre = None if args.no_prefill else run_prefill(args, dms, synth, torch)
-    if pre:
-        log(f"prefill: {pre['ms_per_prompt']:.1f} ms per 32K prompt, attention {pre['attn_tflops']:.1f} TFLOP/s")
+    pre = None
+    if not args.no_prefill:
+        pre = {v: run_prefill(args, dms, synth, torch, v) for v in ("qneuron", "linear")}
+        for v, r in pre.items():
+            log(f"prefill {v}: {r['ms_per_prompt']:.1f} ms per 32K prompt (decide {r['decide_ms']:.2f}, "
+                f"attention {r['attn_ms']:.2f} = {r['attn_tflops']:.1f} TFLOP/s, append {r['append_ms']:.2f} ms)")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -283,15 +283,100 @@ __global__ void decide_qneuron_kernel(QneuronArgs a) {
   for (int k = 0; k < a.Hkv; ++k) store_act<ACT>(q, static_cast<size_t>(k) * a.g * a.D + a.D - 1, 0.0f);
 }
 
+
+// Prefill chunks, bf16 hidden states, H a multiple of 8: TT tokens per
+// 256-thread workgroup.  Thread t owns elements [8t + 2048i, 8t + 2048i + 8)
+// of each token row; per slab it keeps gamma * W_k of its 8 elements in
+// registers and issues the TT 16-byte loads of h together, so h streams from
+// HBM once, in full 4 KB rows per wave-instruction.  The TT x (Hkv + 1) sums
+// reduce with DPP inside each wave, then across the four waves through LDS.
+template <int HKV, int TT>
+__global__ __launch_bounds__(256) void decide_linear_chunk_kernel(DecideArgs a) {
+  __shared__ float s_red[4][TT][HKV + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok0 = blockIdx.x * TT;
+  const int ntt = min(TT, a.ntok - tok0);
+  const uint16_t* hb = static_cast<const uint16_t*>(a.hidden) + static_cast<size_t>(tok0) * a.H;
+  float acc[TT][HKV + 1];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int k = 0; k <= HKV; ++k) acc[t][k] = 0.0f;
+  for (int m = 8 * tid; m < a.H; m += 2048) {
+    uint4 hv[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      hv[t] = t < ntt ? *reinterpret_cast<const uint4*>(hb + static_cast<size_t>(t) * a.H + m) : make_uint4(0, 0, 0, 0);
+    const float4 g0 = *reinterpret_cast<const float4*>(a.gamma + m);
+    const float4 g1 = *reinterpret_cast<const float4*>(a.gamma + m + 4);
+    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float gw[HKV][8];
+#pragma unroll
+    for (int k = 0; k < HKV; ++k) {
+      const float4 w0 = *reinterpret_cast<const float4*>(a.W + static_cast<size_t>(k) * a.H + m);
+      const float4 w1 = *reinterpret_cast<const float4*>(a.W + static_cast<size_t>(k) * a.H + m + 4);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gw[k][e] = wv[e] * gm[e];
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const uint32_t u[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __uint_as_float((e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16));
+        acc[t][HKV] = fmaf(x, x, acc[t][HKV]);
+#pragma unroll
+        for (int k = 0; k < HKV; ++k) acc[t][k] = fmaf(gw[k][e], x, acc[t][k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int k = 0; k <= HKV; ++k) acc[t][k] = wave_sum_dpp(acc[t][k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int k = 0; k <= HKV; ++k) s_red[wave][t][k] = acc[t][k];
+  }
+  __syncthreads();
+  if (tid >= ntt) return;
+  const int tok = tok0 + tid;
+  float tot[HKV + 1];
+#pragma unroll
+  for (int k = 0; k <= HKV; ++k) tot[k] = (s_red[0][tid][k] + s_red[1][tid][k]) + (s_red[2][tid][k] + s_red[3][tid][k]);
+  const float r = 1.0f / sqrtf(tot[HKV] / static_cast<float>(a.H) + a.eps);
+  const int b = tok / a.T, t = tok % a.T;
+  float lg0 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < HKV; ++k) {
+    float z = r * tot[k];
+    if (a.bias) z += a.bias[k];
+    float lg = a.alpha * z - a.offsets[k];
+    if (k == 0) lg0 = lg;
+    if (a.per_layer) lg = lg0;
+    const size_t o = (static_cast<size_t>(b) * HKV + k) * a.T + t;
+    if (a.logits) a.logits[o] = lg;
+    a.evict[o] = (!a.disable && lg > 0.0f) ? 1 : 0;
+  }
+}
+
 template <typename ACT, int HKV>
 static void launch_linear_h(const DecideArgs& a, hipStream_t st) {
   // few tokens (decode): one token per workgroup, all loads of a thread in
-  // flight at once; many tokens (prefill chunks): 4 tokens share W registers
+  // flight at once; many tokens (prefill chunks): 8 tokens share gamma * W
+  // registers (bf16), or 4 tokens share W (fp32 activations)
   if (a.ntok <= 512) {
     if (sizeof(ACT) == 2 && HKV <= 8 && a.H % 16 == 0)
       hipLaunchKernelGGL((decide_linear_tok_kernel<HKV <= 8 ? HKV : 8>), dim3(a.ntok), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 1, (HKV <= 8 ? 4 : 2)>), dim3(a.ntok), dim3(256), 0, st, a);
+  } else if (sizeof(ACT) == 2 && HKV <= 8 && a.H % 8 == 0 && reinterpret_cast<uintptr_t>(a.hidden) % 16 == 0) {
+    constexpr int TT = 8;
+    hipLaunchKernelGGL((decide_linear_chunk_kernel<HKV <= 8 ? HKV : 8, TT>), dim3((a.ntok + TT - 1) / TT), dim3(256),
+                       0, st, a);
   } else {
     constexpr int NCH = HKV <= 8 ? 2 : 1;
     hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 4, NCH>), dim3((a.ntok + 3) / 4), dim3(256), 0, st, a);
