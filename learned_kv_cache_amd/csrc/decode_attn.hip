@@ -574,6 +574,70 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
   }
 }
 
+
+// Combines the partial records (m, l, o) of one unit's workgroups w0..w1 into
+// its bf16 output [G][D] (256 threads); the records are read with
+// device-scope atomic loads (written by workgroups on other XCDs).  The first workgroup's record is its
+// second segment when `odd`.  All loads of a batch of 8 records are issued
+// before any of them is used.
+template <int D, int G>
+__device__ __forceinline__ void merge_unit_records(float* partials, int w0, int w1, int odd, uint16_t* out) {
+  constexpr int PER = (G * D + 255) / 256;
+  const int n = w1 - w0 + 1;
+  float M[PER], O[PER], L[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    M[i] = -INFINITY;
+    O[i] = 0.0f;
+    L[i] = 0.0f;
+  }
+  for (int b0 = 0; b0 < n; b0 += 8) {
+    float mv[8][PER], lv[8][PER], ov[8][PER];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = w0 + b0 + j;
+      const int rec = (b0 + j == 0 && odd) ? 2 * w + 1 : 2 * w;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        const int h = idx / D, dd = idx % D;
+        if (b0 + j < n && idx < G * D) {
+          float* pr = partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
+          mv[j][i] = __hip_atomic_load(pr + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          lv[j][i] = __hip_atomic_load(pr + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ov[j][i] = __hip_atomic_load(pr + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          mv[j][i] = -INFINITY;
+          lv[j][i] = 0.0f;
+          ov[j][i] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float mb = M[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mb = fmaxf(mb, mv[j][i]);
+      if (mb == -INFINITY) continue;
+      const float f0 = exp2f(M[i] - mb);
+      O[i] *= f0;
+      L[i] *= f0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = exp2f(mv[j][i] - mb);
+        O[i] = fmaf(f, ov[j][i], O[i]);
+        L[i] = fmaf(f, lv[j][i], L[i]);
+      }
+      M[i] = mb;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    if (idx < G * D) out[idx] = f32_to_bf16(L[i] > 0.0f ? O[i] / L[i] : 0.0f);
+  }
+}
+
 template <int D, int G, int NP, bool FP8, int LPR>
 __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
   constexpr int EB = FP8 ? 1 : 2;
@@ -649,21 +713,13 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
   const int W = s_start[units];
   const int c = max((W + grid - 1) / grid, RPP);
 
-  // per-unit merge plan for decode_merge_kernel: first/last workgroup and
-  // whether the first workgroup's record is its last segment
+  // heads without live slots have no workgroup: workgroup 0 writes zeros
   if (blockIdx.x == 0) {
-    for (int uu = tid; uu < units; uu += 256) {
-      const int us = s_start[uu], ue = s_start[uu + 1];
-      int32_t* ui = d.unit_info + 4 * uu;
-      if (ue == us) {
-        ui[0] = -1;
-        ui[1] = -1;
-        ui[2] = 0;
-      } else {
-        ui[0] = us / c;
-        ui[1] = (ue - 1) / c;
-        ui[2] = (us != (us / c) * c) ? 1 : 0;
-      }
+    uint16_t* ob = static_cast<uint16_t*>(a.out);
+    for (int uu = 0; uu < units; ++uu) {
+      if (s_start[uu + 1] != s_start[uu]) continue;
+      const int row = uu / g.Hkv, kh = uu % g.Hkv;
+      for (int idx = tid; idx < G * D; idx += 256) ob[(static_cast<size_t>(row) * g.Hq + kh * G) * D + idx] = 0;
     }
   }
 
@@ -778,12 +834,32 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
       if (!split) {
         obase[(static_cast<size_t>(row) * g.Hq + kh * G + h) * D + dd] = f32_to_bf16(lv > 0.0f ? ov / lv : 0.0f);
       } else {
+        // device-coherent stores (no L2 write-back of the XCD needed)
         float* pr = d.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
-        pr[dd] = ov;
+        __hip_atomic_store(pr + dd, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (dd == 0) {
-          pr[D] = M;
-          pr[D + 1] = lv;
+          __hip_atomic_store(pr + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(pr + D + 1, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+      }
+    }
+    if (split) {
+      // The last workgroup of the unit to finish combines its records.  The
+      // records are written and read with device-scope (coherent across XCDs)
+      // atomic stores and loads, so no fence has to write back or invalidate
+      // an L2: each wave waits for its record stores to complete, then one
+      // thread counts the arrival; the workgroup that brings the count to the
+      // unit's number of workgroups merges and resets the counter for the
+      // next call.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      int32_t* cnt = d.unit_info + 4 * u + 3;
+      if (tid == 0) s_tmp[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
+      __syncthreads();
+      if (s_tmp[0]) {
+        merge_unit_records<D, G>(d.partials, w0, w1, (ustart != w0 * c) ? 1 : 0,
+                                 obase + (static_cast<size_t>(row) * g.Hq + kh * G) * D);
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
@@ -791,79 +867,6 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
     a0 = seg_end;
     ++u;
     while (u < units && s_start[u + 1] <= a0) ++u;
-  }
-}
-
-// Merges the partial records of units split over several workgroups and
-// zero-fills heads without live slots.  unit_info[4u] = first workgroup,
-// [4u+1] = last workgroup (-1: empty), [4u+2] = 1 when the first workgroup's
-// record for the unit is its second segment.  All loads of a batch of 8
-// records are issued before any of them is used.
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  const Geo& g = a.g;
-  const int u = blockIdx.x;
-  const int w0 = a.d.unit_info[4 * u], w1 = a.d.unit_info[4 * u + 1], odd = a.d.unit_info[4 * u + 2];
-  if (w1 >= 0 && w1 == w0) return;                 // written by the attention kernel
-  const int row = u / g.Hkv, kh = u % g.Hkv;
-  uint16_t* obase = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(row) * g.Hq + kh * G) * D;
-  constexpr int PER = (G * D + 255) / 256;
-  if (w1 < 0) {
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) obase[idx] = 0;
-    return;
-  }
-  const int n = w1 - w0 + 1;
-  float M[PER], O[PER], L[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    M[i] = -INFINITY;
-    O[i] = 0.0f;
-    L[i] = 0.0f;
-  }
-  for (int b0 = 0; b0 < n; b0 += 8) {
-    float mv[8][PER], lv[8][PER], ov[8][PER];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = w0 + b0 + j;
-      const int rec = (b0 + j == 0 && odd) ? 2 * w + 1 : 2 * w;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int idx = threadIdx.x + 256 * i;
-        const int h = idx / D, dd = idx % D;
-        if (b0 + j < n && idx < G * D) {
-          const float* pr = a.d.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
-          mv[j][i] = pr[D];
-          lv[j][i] = pr[D + 1];
-          ov[j][i] = pr[dd];
-        } else {
-          mv[j][i] = -INFINITY;
-          lv[j][i] = 0.0f;
-          ov[j][i] = 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      float mb = M[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mb = fmaxf(mb, mv[j][i]);
-      if (mb == -INFINITY) continue;
-      const float f0 = exp2f(M[i] - mb);
-      O[i] *= f0;
-      L[i] *= f0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float f = exp2f(mv[j][i] - mb);
-        O[i] = fmaf(f, ov[j][i], O[i]);
-        L[i] = fmaf(f, lv[j][i], L[i]);
-      }
-      M[i] = mb;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    if (idx < G * D) obase[idx] = f32_to_bf16(L[i] > 0.0f ? O[i] / L[i] : 0.0f);
   }
 }
 
@@ -890,7 +893,6 @@ static int launch_fast_dg(const DecodeArgs& a, int grid, int np, hipStream_t st)
     case 6: launch_fast_np<D, G, FP8, 6>(a, grid, st); break;
     default: launch_fast_np<D, G, FP8, 8>(a, grid, st); break;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.B * a.g.Hkv), dim3(256), 0, st, a);
   return DMS_OK;
 }
 
