@@ -197,63 +197,6 @@ __global__ __launch_bounds__(256) void decide_linear_tok_kernel(DecideArgs a) {
   a.evict[o] = (!a.disable && lg > 0.0f) ? 1 : 0;
 }
 
-// Split decode decision: workgroup (s, token) sums over hidden elements
-// [512 s, 512 s + 512): sum(h^2) and, per head, sum(W_k * gamma * h), written
-// to dec_partials[token][s][0..HKV]; the append kernel adds the splits and
-// finishes r, z and the logit.  Thread t owns two elements.
-template <int HKV>
-__global__ __launch_bounds__(256) void decide_split_kernel(const uint16_t* __restrict__ hidden,
-                                                           const float* __restrict__ gamma,
-                                                           const float* __restrict__ W, int H,
-                                                           float* __restrict__ part) {
-  __shared__ float s_red[4][HKV + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sp = blockIdx.x, tok = blockIdx.y;
-  const int m = sp * kDecSplit + 2 * tid;
-  const uint32_t hw = *reinterpret_cast<const uint32_t*>(hidden + static_cast<size_t>(tok) * H + m);
-  const float2 gm = *reinterpret_cast<const float2*>(gamma + m);
-  float2 w[HKV];
-#pragma unroll
-  for (int k = 0; k < HKV; ++k) w[k] = *reinterpret_cast<const float2*>(W + static_cast<size_t>(k) * H + m);
-  const float x0 = __uint_as_float(hw << 16), x1 = __uint_as_float(hw & 0xFFFF0000u);
-  const float g0 = gm.x * x0, g1 = gm.y * x1;
-  float acc[HKV + 1];
-  acc[HKV] = fmaf(x0, x0, x1 * x1);
-#pragma unroll
-  for (int k = 0; k < HKV; ++k) acc[k] = fmaf(w[k].x, g0, w[k].y * g1);
-#pragma unroll
-  for (int k = 0; k <= HKV; ++k) acc[k] = wave_sum_dpp(acc[k]);
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k <= HKV; ++k) s_red[wave][k] = acc[k];
-  }
-  __syncthreads();
-  if (tid <= HKV)
-    part[(static_cast<size_t>(tok) * kDecSplitsMax + sp) * 17 + tid] =
-        s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
-}
-
-// Launches the split decision of B tokens (bf16 hidden, H a multiple of 512,
-// Hkv <= 16); returns false when the shape does not qualify.
-bool launch_decide_split(const dms_cache* c, const void* hidden, const float* gamma, const float* W, int B,
-                         hipStream_t st) {
-  const Geo& g = c->geo;
-  if (g.kv_dtype == DMS_F32 || g.H % kDecSplit != 0 || g.H / kDecSplit > kDecSplitsMax) return false;
-  if ((reinterpret_cast<uintptr_t>(hidden) % 4) || (reinterpret_cast<uintptr_t>(gamma) % 8) ||
-      (reinterpret_cast<uintptr_t>(W) % 8))
-    return false;
-  const dim3 grid(g.H / kDecSplit, B);
-  const uint16_t* h = static_cast<const uint16_t*>(hidden);
-  switch (g.Hkv) {
-    case 1: hipLaunchKernelGGL(decide_split_kernel<1>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
-    case 2: hipLaunchKernelGGL(decide_split_kernel<2>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
-    case 4: hipLaunchKernelGGL(decide_split_kernel<4>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
-    case 8: hipLaunchKernelGGL(decide_split_kernel<8>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
-    case 16: hipLaunchKernelGGL(decide_split_kernel<16>, grid, dim3(256), 0, st, h, gamma, W, g.H, c->dev.dec_partials); break;
-    default: return false;
-  }
-  return true;
-}
 
 struct QneuronArgs {
   void* q;             // [B][T][Hq][D]

@@ -66,7 +66,6 @@ int compute_layout(const dms_config& c, Layout* L) {
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
   L->partial_records = 2 * kMaxDecodeGrid + kMaxUnits;
   L->partials = take(static_cast<size_t>(L->partial_records) * g * (D + 2) * sizeof(float));
-  L->dec_partials = take(static_cast<size_t>(c.max_batch) * kDecSplitsMax * 17 * sizeof(float));
   L->total = off;
   return DMS_OK;
 }
@@ -261,7 +260,6 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.chunk_info = reinterpret_cast<int32_t*>(base + L.chunk_info);
   c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
   c->dev.partials = reinterpret_cast<float*>(base + L.partials);
-  c->dev.dec_partials = reinterpret_cast<float*>(base + L.dec_partials);
   Geo& g = c->geo;
   g.Bmax = cfg->max_batch;
   g.Hq = cfg->num_q_heads;

@@ -17,10 +17,9 @@ constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
 constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
 constexpr int kMaxDecodeGrid = 4096;   // workgroups of the decode attention kernel
 constexpr int kCtlWords = 64;
-constexpr int kDecSplit = 512;         // hidden elements per workgroup of the split decode decision
-constexpr int kDecSplitsMax = 16;      // H <= 8192 for the split path
 constexpr int kCtlFreeCount = 0;
 constexpr int kCtlStatus = 1;
+constexpr int kCtlPrepArrive = 2;    // arrival counter of the fused decode decision + append
 
 // Device pointers carved out of the caller's buffer (see compute_layout).
 struct DevCache {
@@ -41,7 +40,6 @@ struct DevCache {
   int32_t* chunk_info;   // [Bmax*Hkv][8]
   int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
   float* partials;       // decode split partials
-  float* dec_partials;   // [Bmax][kDecSplitsMax][17] decode decision partial sums
 };
 
 // Geometry shared by every kernel of one cache.
@@ -54,7 +52,7 @@ struct Geo {
 
 struct Layout {
   size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, partials, dec_partials, total;
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, partials, total;
   int64_t partial_records;
 };
 
