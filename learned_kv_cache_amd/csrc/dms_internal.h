@@ -15,7 +15,7 @@ namespace dms {
 
 constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
 constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
-constexpr int kMaxDecodeGrid = 4096;   // workgroups of the decode attention kernel
+constexpr int kMaxDecodeGrid = 2048;   // workgroups of the decode attention kernel
 constexpr int kCtlWords = 64;
 constexpr int kCtlFreeCount = 0;
 constexpr int kCtlStatus = 1;
