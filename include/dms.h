@@ -207,6 +207,27 @@ int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, voi
                     void* stream);
 
 /*
+ * A layer's whole decode step in one call: the decision and append of
+ * dms_decode_prepare and the attention of dms_decode_attn for one token per
+ * row (walkthrough, 推理模式, and the FastDMS post's fused decode path).
+ * Results equal those of the two calls in turn, up to the order of the
+ * floating-point sums in the attention.
+ * Arguments as in dms_decode_prepare; q_inout [B][Hq][D] is also the query of
+ * the attention (QNEURON: its decision neuron is zeroed in place and plays no
+ * part); out [B][Hq][D] act dtype.
+ * bf16 pages (fast decode shapes, 16-byte aligned q_inout, k, v, out and,
+ * LINEAR, hidden, rms_gamma, W with hidden a multiple of 8) run as one
+ * launch: the workgroups that prepare a (row, KV head) pair run beside those
+ * of the attention, which takes the current token from k/v and masks the
+ * slot it overwrites; the last workgroup to finish its reads of the shared
+ * tables commits the append.  Other configurations call dms_decode_prepare,
+ * then dms_decode_attn.  Device-side errors as in dms_append_evict.
+ */
+int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden, const float* rms_gamma,
+                    const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,
+                    const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* stream);
+
+/*
  * Prefill attention for one chunk of C new tokens per sequence (walkthrough,
  * 高级选项 Chunked Prefill, and the exact prefill with the eviction mask),
  * computed against the cache state *before* the chunk is appended.  Query i

@@ -14,25 +14,10 @@
 // row-major order, tokens in order inside a pair, ranks from a wave ballot
 // scan, pages popped from one free stack.  No racing atomics decide an id.
 #include "dms_internal.h"
+#include "decode_prep.h"
 
 namespace dms {
 
-struct AppendArgs {
-  DevCache d;
-  Geo g;
-  const int32_t* seq_ids;
-  const void* k;
-  const void* v;
-  const uint8_t* evict;
-  int B;
-  int T;
-  const float* bias;
-  const float* offsets;
-  float alpha, eps;
-  int per_layer, disable;
-  float* logits_out;
-  uint8_t* evict_out;
-};
 
 
 // Stores one row of D activations as kv-dtype page bytes (fp8: with scale s).
@@ -73,69 +58,6 @@ __device__ __forceinline__ float row_amax(const ACT* src, int D, int lane) {
 
 constexpr int kAppThreads = 512;
 constexpr int kAppPieces = 4;       // prefetched 16-byte pieces of K (and V) per thread
-
-template <int LPR>
-__device__ __forceinline__ float row_max_dyn_helper(float x) { return row_max_dpp<LPR>(x); }
-
-__device__ __forceinline__ float piece_row_max(float x, int ppr) {
-  switch (ppr) {
-    case 2: return row_max_dpp<2>(x);
-    case 4: return row_max_dpp<4>(x);
-    case 8: return row_max_dpp<8>(x);
-    case 16: return row_max_dpp<16>(x);
-    default: return x;
-  }
-}
-
-// 16 input bytes (8 bf16 or 4 f32) -> page bytes at dst (fp8: 8 or 4 bytes)
-template <typename ACT, int KV>
-__device__ __forceinline__ void store_piece(uint8_t* pages, int64_t row, int row_bytes, int piece, const uint4& x,
-                                            float inv_scale) {
-  if (KV == DMS_FP8_E4M3) {
-    constexpr int N = 16 / sizeof(ACT);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    float f[N];
-    if (sizeof(ACT) == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) f[i] = __uint_as_float(w[i]);
-    }
-    uint8_t* dst = pages + row * row_bytes + piece * N;
-    if (N == 8) {
-      uint2 o;
-      o.x = f32_to_e4m3(f[0] * inv_scale) | (f32_to_e4m3(f[1] * inv_scale) << 8) |
-            (f32_to_e4m3(f[2] * inv_scale) << 16) | (static_cast<uint32_t>(f32_to_e4m3(f[3] * inv_scale)) << 24);
-      o.y = f32_to_e4m3(f[4] * inv_scale) | (f32_to_e4m3(f[5] * inv_scale) << 8) |
-            (f32_to_e4m3(f[6] * inv_scale) << 16) | (static_cast<uint32_t>(f32_to_e4m3(f[7] * inv_scale)) << 24);
-      *reinterpret_cast<uint2*>(dst) = o;
-    } else {
-      for (int i = 0; i < N; ++i) dst[i] = f32_to_e4m3(f[i] * inv_scale);
-    }
-  } else {
-    // same element type in and out: a raw copy
-    *reinterpret_cast<uint4*>(pages + row * row_bytes + piece * 16) = x;
-  }
-}
-
-__device__ __forceinline__ float piece_amax(const uint4& x, bool bf16) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (bf16) {
-      m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
-      m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
-    } else {
-      m = fmaxf(m, fabsf(__uint_as_float(w[i])));
-    }
-  }
-  return m;
-}
 
 template <typename ACT, int KV>
 __global__ __launch_bounds__(kAppThreads) void append_decode_kernel(AppendArgs a) {
@@ -311,243 +233,24 @@ __global__ __launch_bounds__(kAppThreads) void append_decode_kernel(AppendArgs a
 
 
 // ---------------------------------------------------------------------------
-// dms_decode_prepare for the linear decision with bf16 activations: the
-// decision and the append of one decode token per sequence in one launch,
-// one 256-thread workgroup per (batch row, KV head) pair.
-//
-// A workgroup computes its head's logit (RMSNorm of the row's hidden state
-// dotted with the adapter row; decision 决策来源二), then places the token:
-// in place over the slot of position t - w when that token was marked, else
-// at the head's next slot when it falls inside the current page.  Pairs that
-// open a page, the shared free stack and the sequence positions are handled
-// by the last workgroup to finish (an arrival counter): every read of shared
-// state by the other workgroups has then happened, and the pops follow the
-// same row-major rank order as dms_append_evict.  The plan records passed to
-// it are written and read with device-scope atomic stores and loads
-// (coherent across XCDs without L2 write-back).
-
-constexpr int kPrepThreads = 256;
+// dms_decode_prepare, linear decision with bf16 activations: decision and
+// append of one decode token per sequence in one launch, one workgroup per
+// (batch row, KV head) pair (prep_pair); the last workgroup to arrive opens
+// pages and advances positions (prep_commit).
 
 template <int KV>
-__device__ __forceinline__ void prep_store_row(const DevCache& d, int64_t dst, int page, bool new_page, int ppr,
-                                               int piece, const uint4& kx, const uint4& vx, bool active) {
-  const int page_row_bytes = (KV == DMS_BF16 ? 2 : 1) * ppr * 8;
-  float inv_k = 1.0f, inv_v = 1.0f;
-  if (KV == DMS_FP8_E4M3) {
-    const float mk = piece_row_max(piece_amax(kx, true), ppr);
-    const float mv = piece_row_max(piece_amax(vx, true), ppr);
-    float sk, sv;
-    if (new_page) {
-      sk = page_scale_from_amax(mk);
-      sv = page_scale_from_amax(mv);
-      if (active && piece == 0) {
-        d.scales[2 * page] = sk;
-        d.scales[2 * page + 1] = sv;
-      }
-    } else {
-      sk = d.scales[2 * page];
-      sv = d.scales[2 * page + 1];
-    }
-    inv_k = 1.0f / sk;
-    inv_v = 1.0f / sv;
-  }
-  if (active) {
-    store_piece<uint16_t, KV>(d.k_pages, dst, page_row_bytes, piece, kx, inv_k);
-    store_piece<uint16_t, KV>(d.v_pages, dst, page_row_bytes, piece, vx, inv_v);
-  }
-}
-
-template <int KV>
-__global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(AppendArgs a, const uint16_t* hidden,
-                                                                    const float* gamma, const float* W) {
-  __shared__ float s_red[4][2];
-  __shared__ int s_last, s_free, s_used, s_n;
-  __shared__ int s_wave[4];
-  __shared__ int s_q[kPrepThreads], s_dst[kPrepThreads], s_page[kPrepThreads];
-  const DevCache& d = a.d;
-  const Geo& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int npairs = a.B * g.Hkv;
-  const int p = blockIdx.x;
-  const int row = p / g.Hkv, kh = p % g.Hkv;
-  const int kk = a.per_layer ? 0 : kh;
-  const int seq = a.seq_ids ? a.seq_ids[row] : row;
-  const bool seq_ok = seq >= 0 && seq < g.Bmax;
-  const int unit = seq_ok ? seq * g.Hkv + kh : 0;
-  const int ppr = g.D / 8;                       // 16-byte pieces of a bf16 row
-
-  // 1. everything the slot waits on, and the K/V row
-  int t = 0, len = 0, cur = -1;
-  if (seq_ok) {
-    t = d.pos[seq];
-    len = d.lengths[unit];
-    cur = d.cur_page[unit];
-  }
-  uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-  const size_t rowoff = static_cast<size_t>(p) * g.D * 2;
-  if (tid < ppr) {
-    kx = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + rowoff + 16 * tid);
-    vx = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v) + rowoff + 16 * tid);
-  }
-  // 2. the decision: sum(h^2) and sum(gamma * W_k * h) over the row
-  float ss = 0.0f, dk = 0.0f;
-  const uint16_t* h = hidden + static_cast<size_t>(row) * g.H;
-  const float* w = W + static_cast<size_t>(kk) * g.H;
-  for (int m = 8 * tid; m < g.H; m += 8 * kPrepThreads) {
-    const uint4 hv = *reinterpret_cast<const uint4*>(h + m);
-    const float4 g0 = *reinterpret_cast<const float4*>(gamma + m), g1 = *reinterpret_cast<const float4*>(gamma + m + 4);
-    const float4 w0 = *reinterpret_cast<const float4*>(w + m), w1 = *reinterpret_cast<const float4*>(w + m + 4);
-    const uint32_t u[4] = {hv.x, hv.y, hv.z, hv.w};
-    const float gw[8] = {g0.x * w0.x, g0.y * w0.y, g0.z * w0.z, g0.w * w0.w,
-                         g1.x * w1.x, g1.y * w1.y, g1.z * w1.z, g1.w * w1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = __uint_as_float((e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16));
-      ss = fmaf(x, x, ss);
-      dk = fmaf(gw[e], x, dk);
-    }
-  }
-  const int64_t ri = static_cast<int64_t>(unit) * g.w + (t % g.w);
-  int rv = 0, rrow = -1;
-  if (seq_ok && t >= g.w) {
-    rv = d.ring[ri];
-    rrow = d.ring_row[ri];
-  }
-  ss = wave_sum_dpp(ss);
-  dk = wave_sum_dpp(dk);
-  if (lane == 0) {
-    s_red[wave][0] = ss;
-    s_red[wave][1] = dk;
-  }
-  __syncthreads();
-  ss = (s_red[0][0] + s_red[1][0]) + (s_red[2][0] + s_red[3][0]);
-  dk = (s_red[0][1] + s_red[1][1]) + (s_red[2][1] + s_red[3][1]);
-  const float r = 1.0f / sqrtf(ss / static_cast<float>(g.H) + a.eps);
-  float z = r * dk;
-  if (a.bias) z += a.bias[kk];
-  const float lg = a.alpha * z - a.offsets[kk];
-  const int e = (!a.disable && lg > 0.0f) ? 1 : 0;
-  if (tid == 0) {
-    a.evict_out[p] = static_cast<uint8_t>(e);
-    if (a.logits_out) a.logits_out[p] = lg;
-  }
-
-  // 3. the slot: in place, or the next slot of the current page, or deferred
-  bool valid = seq_ok, deferred = false;
-  int slot = 0, dst = -1, page = -1;
-  if (!seq_ok) {
-    if (tid == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
-  } else if (t + 1 > g.max_tokens) {
-    if (tid == 0) set_status(d.ctl, DMS_DEV_CAPACITY);
-    valid = false;
-  } else if (t >= g.w && rv < 0) {
-    slot = rv & 0x7FFFFFFF;
-    dst = rrow;
-    page = dst / g.P;
-  } else {
-    slot = len;
-    if (slot % g.P == 0) {
-      deferred = true;
-    } else {
-      page = cur;
-      dst = page * g.P + slot % g.P;
-    }
-  }
-  if (valid && !deferred) {
-    if (tid == 0) {
-      if (slot == len) d.lengths[unit] = slot + 1;
-      d.ring[ri] = slot | (e << 31);
-      d.ring_row[ri] = dst;
-      d.slot_meta[dst] = t | (e << 31);
-    }
-    if (wave == 0) prep_store_row<KV>(d, dst, page, false, ppr, lane % ppr, kx, vx, lane < ppr);
-  }
-
-  // 4. plan record, arrival
-  if (tid == 0) {
-    int32_t* pl = d.chunk_info + static_cast<int64_t>(p) * 8;
-    __hip_atomic_store(pl + 0, (valid && deferred) ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pl + 1, unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pl + 2, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pl + 3, slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pl + 4, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+__global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(AppendArgs a, PrepIn in) {
+  __shared__ PrepShared sh;
+  const int npairs = a.B * a.g.Hkv;
+  prep_pair<KV>(a, in, blockIdx.x, false, sh);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) {
-    s_last = __hip_atomic_fetch_add(d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             npairs - 1;
-    s_free = d.ctl[kCtlFreeCount];
-    s_used = 0;
-  }
+  if (threadIdx.x == 0)
+    sh.last = __hip_atomic_fetch_add(a.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              npairs - 1;
   __syncthreads();
-  if (!s_last) return;
-
-  // 5. last workgroup: pairs opening a page (row-major rank order), the pool
-  // top, the positions, the counter
-  for (int p0 = 0; p0 < npairs; p0 += kPrepThreads) {
-    const int q = p0 + tid;
-    int need = 0, qu = 0, qt = 0, qslot = 0, qe = 0;
-    if (q < npairs) {
-      int32_t* pl = d.chunk_info + static_cast<int64_t>(q) * 8;
-      need = __hip_atomic_load(pl + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      qu = __hip_atomic_load(pl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      qt = __hip_atomic_load(pl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      qslot = __hip_atomic_load(pl + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      qe = __hip_atomic_load(pl + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    int wtot;
-    const int wr = wave_rank(need != 0, &wtot);
-    if (lane == 0) s_wave[wave] = wtot;
-    if (tid == 0) s_n = 0;
-    __syncthreads();
-    int off = 0, tot = 0;
-    for (int i = 0; i < 4; ++i) {
-      if (i < wave) off += s_wave[i];
-      tot += s_wave[i];
-    }
-    if (need) {
-      const int R = s_used + off + wr;
-      if (R < s_free) {
-        const int pg = d.free_stack[s_free - 1 - R];
-        const int qdst = pg * g.P + qslot % g.P;
-        d.page_table[static_cast<int64_t>(qu) * g.maxp + qslot / g.P] = pg;
-        d.cur_page[qu] = pg;
-        d.lengths[qu] = qslot + 1;
-        const int64_t qri = static_cast<int64_t>(qu) * g.w + (qt % g.w);
-        d.ring[qri] = qslot | (qe << 31);
-        d.ring_row[qri] = qdst;
-        d.slot_meta[qdst] = qt | (qe << 31);
-        const int at = atomicAdd(&s_n, 1);
-        s_q[at] = q;
-        s_dst[at] = qdst;
-        s_page[at] = pg;
-      } else {
-        set_status(d.ctl, DMS_DEV_POOL_EXHAUSTED);
-      }
-    }
-    __syncthreads();
-    // rows of the pairs that opened a page: one wave per row
-    for (int i = wave; i < s_n; i += 4) {
-      const int q2 = s_q[i];
-      const size_t ro = static_cast<size_t>(q2) * g.D * 2;
-      const int piece = lane % ppr;
-      const uint4 k2 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + ro + 16 * piece);
-      const uint4 v2 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v) + ro + 16 * piece);
-      prep_store_row<KV>(d, s_dst[i], s_page[i], true, ppr, piece, k2, v2, lane < ppr);
-    }
-    __syncthreads();
-    if (tid == 0) s_used += tot;
-    __syncthreads();
-  }
-  for (int rr = tid; rr < a.B; rr += kPrepThreads) {
-    const int sq = a.seq_ids ? a.seq_ids[rr] : rr;
-    if (sq >= 0 && sq < g.Bmax && d.pos[sq] + 1 <= g.max_tokens) d.pos[sq] += 1;
-  }
-  if (tid == 0) {
-    d.ctl[kCtlFreeCount] = s_free - min(s_used, s_free);
-    __hip_atomic_store(d.ctl + kCtlPrepArrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (!sh.last) return;
+  prep_commit<KV>(a, in, npairs, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -835,12 +538,19 @@ extern "C" int dms_decode_prepare(dms_cache* cache, const int32_t* seq_ids, cons
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
   hipStream_t st = as_stream(stream);
   const bool bf16_act = g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3;
-  if (c.decide_mode == DMS_DECIDE_LINEAR && bf16_act) {
-    if (!hidden || !rms_gamma || !W) return fail(DMS_ERR_ARG, "hidden, rms_gamma and W are required");
-    if ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(rms_gamma) |
-         reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) % 16 != 0)
-      return fail(DMS_ERR_ARG, "hidden, rms_gamma, W, k and v must be 16-byte aligned");
-    if (c.hidden % 8 != 0) return fail(DMS_ERR_UNSUPPORTED, "hidden must be a multiple of 8");
+  const bool linear = c.decide_mode == DMS_DECIDE_LINEAR;
+  if (bf16_act) {
+    if (linear) {
+      if (!hidden || !rms_gamma || !W) return fail(DMS_ERR_ARG, "hidden, rms_gamma and W are required");
+      if ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(rms_gamma) |
+           reinterpret_cast<uintptr_t>(W)) % 16 != 0)
+        return fail(DMS_ERR_ARG, "hidden, rms_gamma and W must be 16-byte aligned");
+      if (c.hidden % 8 != 0) return fail(DMS_ERR_UNSUPPORTED, "hidden must be a multiple of 8");
+    } else if (!q_inout) {
+      return fail(DMS_ERR_ARG, "q_inout is required");
+    }
+    if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) % 16 != 0)
+      return fail(DMS_ERR_ARG, "k and v must be 16-byte aligned");
     AppendArgs a{};
     a.d = cache->dev;
     a.g = g;
@@ -858,14 +568,14 @@ extern "C" int dms_decode_prepare(dms_cache* cache, const int32_t* seq_ids, cons
     a.disable = c.disable_eviction != 0;
     a.logits_out = logits_out;
     a.evict_out = evict_out;
-    const auto* hb = static_cast<const uint16_t*>(hidden);
+    PrepIn in{static_cast<const uint16_t*>(hidden), rms_gamma, W, static_cast<uint16_t*>(q_inout), linear ? 0 : 1};
     if (g.kv_dtype == DMS_BF16)
-      hipLaunchKernelGGL((decode_prepare_kernel<DMS_BF16>), dim3(B * g.Hkv), dim3(kPrepThreads), 0, st, a, hb, rms_gamma, W);
+      hipLaunchKernelGGL((decode_prepare_kernel<DMS_BF16>), dim3(B * g.Hkv), dim3(kPrepThreads), 0, st, a, in);
     else
-      hipLaunchKernelGGL((decode_prepare_kernel<DMS_FP8_E4M3>), dim3(B * g.Hkv), dim3(kPrepThreads), 0, st, a, hb, rms_gamma, W);
+      hipLaunchKernelGGL((decode_prepare_kernel<DMS_FP8_E4M3>), dim3(B * g.Hkv), dim3(kPrepThreads), 0, st, a, in);
     return check_hip(hipGetLastError(), "dms_decode_prepare launch");
   }
-  // other shapes and the query-neuron decision: decide, then append
+  // f32 activations: decide, then append
   int s = dms_decide(cache, hidden, rms_gamma, W, bias, offsets, q_inout, B, 1, logits_out, evict_out, stream);
   if (s) return s;
   return dms_append_evict(cache, seq_ids, k, v, evict_out, B, 1, stream);

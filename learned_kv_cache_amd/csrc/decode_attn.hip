@@ -18,6 +18,7 @@
 // * Online softmax per wave in base 2; waves merge through LDS; units split
 //   over several workgroups are merged by a second, small kernel.
 #include "dms_internal.h"
+#include "decode_prep.h"
 
 namespace dms {
 
@@ -429,10 +430,13 @@ struct KvChunk {
 
 // Issues the loads of passes [pass0, pass0 + NP) of a segment; rows at or past
 // `hi` are not loaded.
-template <int D, int NP, bool FP8, int LPR>
+// STEP: row `vrow` of the unit is the current token, read from the input rows
+// kin/vin (this lane's bytes) instead of a page.
+template <int D, int NP, bool FP8, int LPR, bool STEP = false>
 __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c, const uint8_t* __restrict__ kp,
                                            const uint8_t* __restrict__ vp, int pt_reg, int first_page, int lo, int pass0,
-                                           int hi, int wave, int lane_row, int lane_col, int psh, int pmask) {
+                                           int hi, int wave, int lane_row, int lane_col, int psh, int pmask,
+                                           int vrow = -1, const uint8_t* kin = nullptr, const uint8_t* vin = nullptr) {
   constexpr int RB = D * (FP8 ? 1 : 2);
   constexpr int BPL = RB / LPR;
   constexpr int NV = BPL / 16;
@@ -451,11 +455,14 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
     const uint32_t off = (static_cast<uint32_t>(c.pg[p]) * static_cast<uint32_t>(pmask + 1) +
                           static_cast<uint32_t>(r & pmask)) * static_cast<uint32_t>(RB) +
                          static_cast<uint32_t>(lane_col * BPL);
+    const bool cur = STEP && r == vrow;
+    const uint8_t* kb = cur ? kin : kp + off;
+    const uint8_t* vb = cur ? vin : vp + off;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       if (ok) {
-        c.k[p][j] = *reinterpret_cast<const uint4*>(kp + off + 16 * j);
-        c.v[p][j] = *reinterpret_cast<const uint4*>(vp + off + 16 * j);
+        c.k[p][j] = *reinterpret_cast<const uint4*>(kb + 16 * j);
+        c.v[p][j] = *reinterpret_cast<const uint4*>(vb + 16 * j);
       } else {
         c.k[p][j] = make_uint4(0, 0, 0, 0);
         c.v[p][j] = make_uint4(0, 0, 0, 0);
@@ -465,13 +472,15 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
 }
 
 // Online-softmax update with the rows of one chunk.
-template <int D, int G, int NP, bool FP8, int LPR>
+// STEP: slot `skip` of the unit (the key the current token overwrites) is masked.
+template <int D, int G, int NP, bool FP8, int LPR, bool STEP = false>
 __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c,
                                               const float* __restrict__ scales, int lo, int pass0, int hi, int wave,
                                               int lane_row, float scale_log2,
                                               const uint32_t (&qv)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2)) / 2],
                                               float (&m)[G], float (&l)[G],
-                                              float (&o)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2))]) {
+                                              float (&o)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2))],
+                                              int skip = -1) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int RB = D * EB;
   constexpr int BPL = RB / LPR;
@@ -484,7 +493,8 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
   float sk[NP], sv[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    ok[p] = lo + (pass0 + p) * RPP + wave * RG + lane_row < hi;
+    const int r = lo + (pass0 + p) * RPP + wave * RG + lane_row;
+    ok[p] = r < hi && (!STEP || r != skip);
     sk[p] = scale_log2;
     sv[p] = 1.0f;
     if (FP8) {
@@ -638,8 +648,70 @@ __device__ __forceinline__ void merge_unit_records(float* partials, int w0, int 
   }
 }
 
-template <int D, int G, int NP, bool FP8, int LPR>
-__global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
+// Inputs of the fused decode step that the attention role reads.
+struct StepArgs {
+  const uint8_t* k;        // [B][Hkv][D] bf16 rows of the current token
+  const uint8_t* v;
+  int npairs;              // workgroups of the prepare role (B * Hkv), placed first in the grid
+  int arrivals;            // npairs + attention workgroups: the commit waits for all of them
+  int qneuron;             // the decision neuron (last element of each group's first query head) reads as zero
+};
+
+template <int G, int D, bool STEP>
+struct FastLds {
+  int start[kMaxUnits + 1];
+  int ext[STEP ? kMaxUnits : 1];    // STEP: -1 no current token, else 1 + the slot it overwrites (0: appended)
+  int tmp[4];
+  union {
+    float o[4][4][G][D];               // [wave][DPP row][head][dim]
+    PrepShared prep;                   // the commit (before any use of o)
+  };
+  float ml[4][4][G][2];                // m (row 0 only) and l per row
+};
+
+// Live slots (and, STEP, the current token's placement) of unit u.
+template <bool STEP>
+__device__ __forceinline__ int unit_slots(const DecodeArgs& a, int u, int wg, int* ext) {
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int row = u / g.Hkv, kh = u % g.Hkv;
+  const int seq = a.seq_ids ? a.seq_ids[row] : row;
+  *ext = -1;
+  if (seq < 0 || seq >= g.Bmax) {
+    if (wg == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+    return 0;
+  }
+  const int unit = seq * g.Hkv + kh;
+  int L = d.lengths[unit];
+  if (STEP) {
+    // the current token: in place over the slot of position t - w when that
+    // token was marked, else appended as slot L (the prepare role's choice)
+    const int t = d.pos[seq];
+    if (t + 1 <= g.max_tokens) {
+      int skip = -1;
+      if (t >= g.w) {
+        const int rv = d.ring[static_cast<int64_t>(unit) * g.w + t % g.w];
+        if (rv < 0) skip = rv & 0x7FFFFFFF;
+      }
+      *ext = skip + 1;
+      L += 1;
+    }
+  }
+  return L;
+}
+
+// The attention of dms_decode_attn (workgroup wg of `grid`).  STEP: the
+// attention of the fused decode step, run before the current token is in the
+// cache: each unit's rows are its live slots plus one more, the current
+// token, read from the input rows; the slot the token overwrites in place is
+// masked.  The same keys as after the append.  Once every workgroup has read
+// the lengths, positions and ring entries it works from, it arrives on the
+// step's counter; the last of the step's workgroups to arrive commits the
+// prepare role's tables (prep_commit).
+template <int D, int G, int NP, bool FP8, int LPR, bool STEP>
+__device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const AppendArgs* ap, const PrepIn* pin,
+                                                      const StepArgs* sa, int wg, int grid,
+                                                      FastLds<G, D, STEP>& lds) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int RB = D * EB;
   constexpr int BPL = RB / LPR;
@@ -650,36 +722,31 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
   constexpr int NV = BPL / 16;
   static_assert(NP % 2 == 0, "passes are paired for the P.V dot products");
   static_assert(BPL % 16 == 0, "a lane loads whole 16-byte pieces");
+  static_assert(!STEP || !FP8, "the fused step reads bf16 input rows as cache rows");
 
-  __shared__ int s_start[kMaxUnits + 1];
-  __shared__ int s_tmp[4];
-  __shared__ float s_o[4][4][G][D];             // [wave][DPP row][head][dim]
-  __shared__ float s_ml[4][4][G][2];            // m (row 0 only) and l per row
-
+  int* s_start = lds.start;
+  int* s_tmp = lds.tmp;
   const DevCache& d = a.d;
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lane_row = lane / LPR, lane_col = lane % LPR;
   const int units = a.B * g.Hkv;
-  const int grid = gridDim.x;
 
   // -- unit prefix (live slots of every (row, KV head), concatenated) --------
   if (units <= 64) {
     if (wave == 0) {
-      int L = 0;
-      if (lane < units) {
-        const int row = lane / g.Hkv, kh = lane % g.Hkv;
-        const int seq = a.seq_ids ? a.seq_ids[row] : row;
-        if (seq >= 0 && seq < g.Bmax) L = d.lengths[seq * g.Hkv + kh];
-        else if (blockIdx.x == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
-      }
+      int L = 0, ext = -1;
+      if (lane < units) L = unit_slots<STEP>(a, lane, wg, &ext);
       int incl = L;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(incl, o);
         if (lane >= o) incl += y;
       }
-      if (lane < units) s_start[lane] = incl - L;
+      if (lane < units) {
+        s_start[lane] = incl - L;
+        if (STEP) lds.ext[lane] = ext;
+      }
       if (lane == 63) s_start[units] = incl;
     }
     __syncthreads();
@@ -690,12 +757,10 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
     int sum = 0;
     for (int i = 0; i < per; ++i) {
       const int u = u0 + i;
-      int L = 0;
+      int L = 0, ext = -1;
       if (u < units) {
-        const int row = u / g.Hkv, kh = u % g.Hkv;
-        const int seq = a.seq_ids ? a.seq_ids[row] : row;
-        if (seq >= 0 && seq < g.Bmax) L = d.lengths[seq * g.Hkv + kh];
-        else if (blockIdx.x == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+        L = unit_slots<STEP>(a, u, wg, &ext);
+        if (STEP) lds.ext[u] = ext;
       }
       len[i] = L;
       sum += L;
@@ -710,11 +775,20 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
     if (tid == 0) s_start[units] = W;
     __syncthreads();
   }
+  if constexpr (STEP) {
+    // every read of state the commit changes is done: arrive
+    if (tid == 0)
+      lds.prep.last = __hip_atomic_fetch_add(d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      sa->arrivals - 1;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(lds.prep.last)) prep_commit<DMS_BF16>(*ap, *pin, sa->npairs, lds.prep);
+    __syncthreads();
+  }
   const int W = s_start[units];
   const int c = max((W + grid - 1) / grid, RPP);
 
   // heads without live slots have no workgroup: workgroup 0 writes zeros
-  if (blockIdx.x == 0) {
+  if (wg == 0) {
     uint16_t* ob = static_cast<uint16_t*>(a.out);
     for (int uu = 0; uu < units; ++uu) {
       if (s_start[uu + 1] != s_start[uu]) continue;
@@ -723,7 +797,7 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
     }
   }
 
-  int a0 = blockIdx.x * c;
+  int a0 = wg * c;
   const int a1 = min(a0 + c, W);
   if (a0 >= a1) return;
   int lo_u = 0, hi_u = units - 1;
@@ -744,6 +818,19 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
     const int row = u / g.Hkv, kh = u % g.Hkv;
     const int seq = a.seq_ids ? a.seq_ids[row] : row;
     const int32_t* pt = d.page_table + (static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp;
+    int vrow = -1, skip = -1;
+    const uint8_t* kin = nullptr;
+    const uint8_t* vin = nullptr;
+    if constexpr (STEP) {
+      const int ext = lds.ext[u];
+      if (ext >= 0) {
+        vrow = uend - ustart - 1;
+        skip = ext - 1;
+      }
+      const size_t ro = (static_cast<size_t>(row) * g.Hkv + kh) * RB + lane_col * BPL;
+      kin = sa->k + ro;
+      vin = sa->v + ro;
+    }
 
     uint32_t qv[G][QW];
 #pragma unroll
@@ -758,6 +845,8 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
         qv[h][j + 3] = t4.w;
       }
     }
+    // the decision neuron plays no part in attention (the commit zeroes it in memory)
+    if (STEP && sa->qneuron && lane_col == LPR - 1) qv[0][QW - 1] &= 0xFFFFu;
     float m[G], l[G], o[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -775,20 +864,22 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
       const int blo = max(lo, pb << psh), bhi = min(hi, (plast + 1) << psh);
       const int npass = (bhi - blo + RPP - 1) / RPP;
       KvChunk<NP, NV> ca, cb;
-      load_chunk<D, NP, FP8, LPR>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, 0, bhi, wave, lane_row, lane_col, psh, pmask);
+      load_chunk<D, NP, FP8, LPR, STEP>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, 0, bhi, wave, lane_row, lane_col, psh,
+                                        pmask, vrow, kin, vin);
       for (int p0 = 0; p0 < npass; p0 += 2 * NP) {
         if (p0 + NP < npass)
-          load_chunk<D, NP, FP8, LPR>(cb, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + NP, bhi, wave, lane_row, lane_col,
-                                      psh, pmask);
-        compute_chunk<D, G, NP, FP8, LPR>(ca, d.scales, blo, p0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o);
+          load_chunk<D, NP, FP8, LPR, STEP>(cb, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + NP, bhi, wave, lane_row,
+                                            lane_col, psh, pmask, vrow, kin, vin);
+        compute_chunk<D, G, NP, FP8, LPR, STEP>(ca, d.scales, blo, p0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o,
+                                                skip);
         if (p0 + NP >= npass) break;
         if (p0 + 2 * NP < npass)
-          load_chunk<D, NP, FP8, LPR>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + 2 * NP, bhi, wave, lane_row,
-                                      lane_col, psh, pmask);
-        compute_chunk<D, G, NP, FP8, LPR>(cb, d.scales, blo, p0 + NP, bhi, wave, lane_row, g.scale_log2, qv, m, l, o);
+          load_chunk<D, NP, FP8, LPR, STEP>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + 2 * NP, bhi, wave,
+                                            lane_row, lane_col, psh, pmask, vrow, kin, vin);
+        compute_chunk<D, G, NP, FP8, LPR, STEP>(cb, d.scales, blo, p0 + NP, bhi, wave, lane_row, g.scale_log2, qv, m,
+                                                l, o, skip);
       }
     }
-
     // per-column sums over the wave's rows go through LDS: lanes of the first
     // 16-lane row group fold the other groups of their DPP row first
 #pragma unroll
@@ -802,33 +893,33 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_o[wave][drow][h][lane_col * EPL + e] = o[h][e];
+        for (int e = 0; e < EPL; ++e) lds.o[wave][drow][h][lane_col * EPL + e] = o[h][e];
       }
       if (lane_col == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) s_ml[wave][drow][h][1] = l[h];
+        for (int h = 0; h < G; ++h) lds.ml[wave][drow][h][1] = l[h];
       }
     }
     if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) s_ml[wave][0][h][0] = m[h];
+      for (int h = 0; h < G; ++h) lds.ml[wave][0][h][0] = m[h];
     }
     __syncthreads();
     const int w0 = ustart / c, w1 = (uend - 1) / c;
     const bool split = w1 > w0;
-    const int rec = 2 * blockIdx.x + (first_seg ? 0 : 1);
+    const int rec = 2 * wg + (first_seg ? 0 : 1);
     for (int idx = tid; idx < G * D; idx += 256) {
       const int h = idx / D, dd = idx % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h][0]);
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, lds.ml[w][0][h][0]);
       float ov = 0.0f, lv = 0.0f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float f = exp2f(s_ml[w][0][h][0] - M);     // -inf gives 0
-          ov += f * (s_o[w][0][h][dd] + s_o[w][1][h][dd] + s_o[w][2][h][dd] + s_o[w][3][h][dd]);
-          lv += f * (s_ml[w][0][h][1] + s_ml[w][1][h][1] + s_ml[w][2][h][1] + s_ml[w][3][h][1]);
+          const float f = exp2f(lds.ml[w][0][h][0] - M);     // -inf gives 0
+          ov += f * (lds.o[w][0][h][dd] + lds.o[w][1][h][dd] + lds.o[w][2][h][dd] + lds.o[w][3][h][dd]);
+          lv += f * (lds.ml[w][0][h][1] + lds.ml[w][1][h][1] + lds.ml[w][2][h][1] + lds.ml[w][3][h][1]);
         }
       }
       if (!split) {
@@ -868,6 +959,35 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
     ++u;
     while (u < units && s_start[u + 1] <= a0) ++u;
   }
+}
+
+
+template <int D, int G, int NP, bool FP8, int LPR>
+__global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
+  __shared__ FastLds<G, D, false> lds;
+  decode_attn_fast_body<D, G, NP, FP8, LPR, false>(a, nullptr, nullptr, nullptr, blockIdx.x, gridDim.x, lds);
+}
+
+// dms_decode_step: workgroups [0, npairs) prepare the current token of one
+// (row, KV head) pair each (decision, placement, plan record) and arrive on
+// the step's counter; the others run the attention (STEP).  The last arrival
+// commits.
+template <int D, int G, int NP, int LPR>
+__global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
+  __shared__ FastLds<G, D, true> lds;
+  if (static_cast<int>(blockIdx.x) < sa.npairs) {
+    prep_pair<DMS_BF16>(ap, pin, blockIdx.x, true, lds.prep);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      lds.prep.last = __hip_atomic_fetch_add(ap.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == sa.arrivals - 1;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(lds.prep.last)) prep_commit<DMS_BF16>(ap, pin, sa.npairs, lds.prep);
+    return;
+  }
+  decode_attn_fast_body<D, G, NP, false, LPR, true>(a, &ap, &pin, &sa, blockIdx.x - sa.npairs,
+                                                    gridDim.x - sa.npairs, lds);
 }
 
 template <int D, int G, bool FP8, int NP>
@@ -936,6 +1056,45 @@ static int launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
   }
 }
 
+template <int D, int G>
+static void launch_step_dg(const DecodeArgs& a, const AppendArgs& ap, const PrepIn& pin, const StepArgs& sa, int grid,
+                           hipStream_t st) {
+  constexpr int RB = D * 2;
+  constexpr int LPR1 = RB / 16 >= 16 ? 16 : RB / 16;
+  if constexpr (RB / 16 >= 16) {
+    if (a.lanes_per_row == 8) {
+      hipLaunchKernelGGL((decode_step_kernel<D, G, 2, 8>), dim3(grid), dim3(256), 0, st, a, ap, pin, sa);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_step_kernel<D, G, 2, LPR1>), dim3(grid), dim3(256), 0, st, a, ap, pin, sa);
+}
+
+template <int D>
+static int launch_step_d(const DecodeArgs& a, const AppendArgs& ap, const PrepIn& pin, const StepArgs& sa, int grid,
+                         hipStream_t st) {
+  switch (a.g.g) {
+    case 1: launch_step_dg<D, 1>(a, ap, pin, sa, grid, st); return DMS_OK;
+    case 2: launch_step_dg<D, 2>(a, ap, pin, sa, grid, st); return DMS_OK;
+    case 4: launch_step_dg<D, 4>(a, ap, pin, sa, grid, st); return DMS_OK;
+    case 8: launch_step_dg<D, 8>(a, ap, pin, sa, grid, st); return DMS_OK;
+    default: return fail(DMS_ERR_UNSUPPORTED, "group size");
+  }
+}
+
+// The fast decode attention applies: bf16/fp8 pages, D 64/128, power-of-two
+// pages holding at least the 64 / lanes-per-row rows a wave reads per pass
+// (so they span at most two pages), page bytes addressable in 32 bits.
+static bool fast_decode_ok(const dms_cache* cache, int* lpr_out) {
+  const Geo& g = cache->geo;
+  const int row_bytes = g.D * (g.kv_dtype == DMS_FP8_E4M3 ? 1 : 2);
+  const int lpr = row_bytes / 16 >= 16 ? (cache->decode_lpr == 8 ? 8 : 16) : row_bytes / 16;
+  if (lpr_out) *lpr_out = lpr;
+  return (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) && g.Pshift >= 0 &&
+         (1 << g.Pshift) >= 64 / lpr && cache->layout.v_pages - cache->layout.k_pages < (1ull << 32) &&
+         !cache->force_generic;
+}
+
 }  // namespace dms
 
 using namespace dms;
@@ -951,15 +1110,7 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
   int s;
-  // fast path: bf16/fp8 pages, D 64/128, power-of-two pages holding at least
-  // the 64 / lanes-per-row rows a wave reads per pass (so they span at most two
-  // pages), page bytes addressable in 32 bits
-  const int row_bytes = g.D * (g.kv_dtype == DMS_FP8_E4M3 ? 1 : 2);
-  const int lpr = row_bytes / 16 >= 16 ? (cache->decode_lpr == 8 ? 8 : 16) : row_bytes / 16;
-  const bool fast = (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) &&
-                    g.Pshift >= 0 && (1 << g.Pshift) >= 64 / lpr &&
-                    cache->layout.v_pages - cache->layout.k_pages < (1ull << 32) && !cache->force_generic;
-  if (fast) {
+  if (fast_decode_ok(cache, nullptr)) {
     const bool fp8 = g.kv_dtype == DMS_FP8_E4M3;
     const int np = cache->decode_np > 0 ? cache->decode_np : 2;
     if (g.D == 128) s = fp8 ? launch_fast_d<128, true>(a, grid, np, st) : launch_fast_d<128, false>(a, grid, np, st);
@@ -974,4 +1125,59 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   }
   if (s) return s;
   return check_hip(hipGetLastError(), "dms_decode_attn launch");
+}
+
+extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden, const float* rms_gamma,
+                               const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,
+                               const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* stream) {
+  if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
+  const dms_config& c = cache->cfg;
+  const Geo& g = cache->geo;
+  if (!q_inout || !out || !k || !v || !offsets || !evict_out)
+    return fail(DMS_ERR_ARG, "q_inout, out, k, v, offsets and evict_out are required");
+  if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
+  if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
+  const bool linear = c.decide_mode == DMS_DECIDE_LINEAR;
+  if (linear && (!hidden || !rms_gamma || !W)) return fail(DMS_ERR_ARG, "hidden, rms_gamma and W are required");
+  uintptr_t al = reinterpret_cast<uintptr_t>(q_inout) | reinterpret_cast<uintptr_t>(k) |
+                 reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
+  if (linear)
+    al |= reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(rms_gamma) |
+          reinterpret_cast<uintptr_t>(W);
+  const bool fused = g.kv_dtype == DMS_BF16 && fast_decode_ok(cache, nullptr) && al % 16 == 0 &&
+                     (!linear || c.hidden % 8 == 0) && B * g.Hkv <= kMaxUnits;
+  hipStream_t st = as_stream(stream);
+  if (!fused) {
+    // fp8 pages and other shapes: the two calls in turn
+    int s = dms_decode_prepare(cache, seq_ids, hidden, rms_gamma, W, bias, offsets, q_inout, k, v, B, logits_out,
+                               evict_out, stream);
+    if (s) return s;
+    return dms_decode_attn(cache, seq_ids, q_inout, out, B, stream);
+  }
+  DecodeArgs a{cache->dev, g, seq_ids, q_inout, out, B, cache->decode_lpr};
+  AppendArgs ap{};
+  ap.d = cache->dev;
+  ap.g = g;
+  ap.seq_ids = seq_ids;
+  ap.k = k;
+  ap.v = v;
+  ap.evict = nullptr;
+  ap.B = B;
+  ap.T = 1;
+  ap.bias = bias;
+  ap.offsets = offsets;
+  ap.alpha = c.alpha_scale;
+  ap.eps = c.rms_eps;
+  ap.per_layer = c.alpha_per == DMS_ALPHA_PER_LAYER;
+  ap.disable = c.disable_eviction != 0;
+  ap.logits_out = logits_out;
+  ap.evict_out = evict_out;
+  PrepIn pin{static_cast<const uint16_t*>(hidden), rms_gamma, W, static_cast<uint16_t*>(q_inout), linear ? 0 : 1};
+  const int npairs = B * g.Hkv;
+  const int agrid = decode_grid_for(cache);
+  StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, npairs + agrid, linear ? 0 : 1};
+  const int s = g.D == 128 ? launch_step_d<128>(a, ap, pin, sa, npairs + agrid, st)
+                           : launch_step_d<64>(a, ap, pin, sa, npairs + agrid, st);
+  if (s) return s;
+  return check_hip(hipGetLastError(), "dms_decode_step launch");
 }

@@ -39,7 +39,7 @@ EXPORTS = (
     "dms_config_validate", "dms_cache_bytes", "dms_max_pages_per_seq", "dms_cache_create",
     "dms_cache_destroy", "dms_cache_config", "dms_decide", "dms_append_evict", "dms_decode_attn",
     "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
-    "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare",
+    "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
 )
 
 
@@ -95,6 +95,7 @@ def lib():
             "dms_append_evict": [vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_decode_attn": [vp, vp, vp, vp, i32, vp],
             "dms_decode_prepare": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
+            "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
             "dms_prefill_attn": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_seq_reset": [vp, vp, i32, vp],
             "dms_cache_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
@@ -236,6 +237,26 @@ def dms_decode_prepare(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, off
     return _check(lib().dms_decode_prepare(
         cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), hp, gp, wp, _ptr(bias, "bias", torch.float32, c.num_kv_heads),
         _ptr(offsets, "offsets", torch.float32, c.num_kv_heads), qp, _ptr(k, "k", ad, n), _ptr(v, "v", ad, n), B,
+        _ptr(logits_out, "logits_out", torch.float32, B * c.num_kv_heads),
+        _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads), _stream(stream)))
+
+
+def dms_decode_step(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, offsets, q_inout, k, v, out, B: int,
+                    logits_out, evict_out, stream=None) -> int:
+    c = cache.cfg
+    ad = cache.act_dtype
+    if c.decide_mode == DMS_DECIDE_LINEAR:
+        hp = _ptr(hidden, "hidden", ad, B * c.hidden)
+        gp = _ptr(rms_gamma, "rms_gamma", torch.float32, c.hidden)
+        wp = _ptr(W, "W", torch.float32, c.num_kv_heads * c.hidden)
+    else:
+        hp = gp = wp = None
+    nq = B * c.num_q_heads * c.head_dim
+    n = B * c.num_kv_heads * c.head_dim
+    return _check(lib().dms_decode_step(
+        cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), hp, gp, wp,
+        _ptr(bias, "bias", torch.float32, c.num_kv_heads), _ptr(offsets, "offsets", torch.float32, c.num_kv_heads),
+        _ptr(q_inout, "q_inout", ad, nq), _ptr(k, "k", ad, n), _ptr(v, "v", ad, n), _ptr(out, "out", ad, nq), B,
         _ptr(logits_out, "logits_out", torch.float32, B * c.num_kv_heads),
         _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads), _stream(stream)))
 

@@ -268,10 +268,12 @@ class Runner:
         self.sim.append(list(seqs), e_np, k_np, v_np)
         return stats
 
-    def decode_step(self, seqs: Sequence[int], positions: Sequence[int], check: bool = True, fused: bool = False):
+    def decode_step(self, seqs: Sequence[int], positions: Sequence[int], check: bool = True, fused: bool = False,
+                    step: bool = False):
         """decide -> append -> decode attention for one token per listed sequence.
 
-        fused=True runs decide + append as one dms_decode_prepare call."""
+        fused=True runs decide + append as one dms_decode_prepare call; step=True
+        runs the whole step as one dms_decode_step call."""
         torch, dms, wl, d = self.torch, self.dms, self.wl, self.prep.draw
         B = len(seqs)
         seq_dev = to_dev(np.asarray(seqs, np.int32), "i32")
@@ -281,18 +283,29 @@ class Runner:
         v_np = np.stack([self.row("v", b, t) for b, t in zip(seqs, positions)])[:, None]
         k_dev, v_dev = to_dev(k_np, wl.act_dtype), to_dev(v_np, wl.act_dtype)
         e_np = np.stack([self.prep.evict[b][:, t:t + 1] for b, t in zip(seqs, positions)])
-        if fused:
+        out = torch.empty(B * wl.Hq * wl.D, dtype=q_dev.dtype, device="cuda")
+        if fused or step:
             logits = torch.empty(B * wl.Hkv, dtype=torch.float32, device="cuda")
             evict = torch.empty(B * wl.Hkv, dtype=torch.uint8, device="cuda")
             h_dev = None
             if wl.decide == "linear":
                 h_dev = to_dev(np.stack([self.row("h", b, t) for b, t in zip(seqs, positions)]), wl.act_dtype)
-            dms.dms_decode_prepare(self.cache, seq_dev, h_dev, self.gamma, self.W, None, self.off, q_dev.view(-1),
-                                   k_dev, v_dev, B, logits, evict)
+            if step:
+                dms.dms_decode_step(self.cache, seq_dev, h_dev, self.gamma, self.W, None, self.off, q_dev.view(-1),
+                                    k_dev, v_dev, out, B, logits, evict)
+            else:
+                dms.dms_decode_prepare(self.cache, seq_dev, h_dev, self.gamma, self.W, None, self.off,
+                                       q_dev.view(-1), k_dev, v_dev, B, logits, evict)
             ref_l = np.stack([self.prep.logits[b][:, t] for b, t in zip(seqs, positions)])
             got_e = evict.cpu().numpy().reshape(B, wl.Hkv)
             assert np.array_equal(got_e, e_np[:, :, 0]), f"decisions differ at {np.argwhere(got_e != e_np[:, :, 0])[:5]}"
             np.testing.assert_allclose(logits.cpu().numpy().reshape(B, wl.Hkv), ref_l, atol=5e-3, rtol=0)
+            if wl.decide == "qneuron":
+                # the decision neuron is zeroed in place, nothing else changes
+                qz = from_dev(q_dev).reshape(B, wl.Hq, wl.D)
+                want = q_np.reshape(B, wl.Hq, wl.D).astype(np.float64).copy()
+                want[:, :: wl.g, -1] = 0.0
+                assert np.array_equal(qz, want), "q_inout after the decision"
         else:
             # decide works per (row, T=1); rows may sit at different positions
             if len(set(positions)) == 1:
@@ -304,8 +317,8 @@ class Runner:
                 evict = torch.cat(evs)
             dms.dms_append_evict(self.cache, seq_dev, k_dev, v_dev, evict, B, 1)
         self.sim.append(list(seqs), e_np, k_np, v_np)
-        out = torch.empty(B * wl.Hq * wl.D, dtype=q_dev.dtype, device="cuda")
-        dms.dms_decode_attn(self.cache, seq_dev, q_dev.view(-1), out, B)
+        if not step:
+            dms.dms_decode_attn(self.cache, seq_dev, q_dev.view(-1), out, B)
         if not check:
             return None
         got = from_dev(out).reshape(B, wl.Hq, wl.D)

@@ -1,0 +1,150 @@
+"""dms_decode_step (decision, append and attention of a decode token in one
+call) against the CPU oracle (needs an MI355X).
+
+Small bf16 layers with a short window (24) and small pages (16) so that, in a
+few dozen steps, tokens overwrite the slots of marked tokens in place, heads
+open pages from the shared pool, and sequences sit at different positions
+(log-uniform prompt lengths, rows given in a shuffled order).  Every step
+checks the decisions and logits, the attention output of every query head,
+and, bit for bit, the slot tables, page tables, ring, positions, free stack
+and page bytes.  Shapes cover GQA groups 1, 2, 4 and 8, head_dim 64 and 128,
+both decision sources, layer mode, and more than 64 (row, KV head) units.
+"""
+import numpy as np
+import pytest
+
+from learned_kv_cache_amd import synth
+from tests.harness import Runner, from_dev, log, prepare, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# name: (B, Hq, Hkv, D, decide, alpha_per)
+SHAPES = {
+    "g4_d128_linear": (3, 8, 2, 128, "linear", "head"),
+    "g2_d64_qneuron": (3, 8, 4, 64, "qneuron", "head"),
+    "g8_d64_linear_layer": (2, 16, 2, 64, "linear", "layer"),
+    "g1_d128_qneuron_80_units": (20, 4, 4, 128, "qneuron", "head"),
+}
+
+
+def _cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _workload(name, idx, **kw):
+    B, Hq, Hkv, D, decide, per = SHAPES[name]
+    args = dict(name=f"step_{name}", cfg_id=40 + idx, B=B, hidden=256, Hq=Hq, Hkv=Hkv, D=D, act_dtype="bf16",
+                kv_dtype="bf16", window=24, block=16, prefill=0, decode_steps=40, chunk=64,
+                p_range=(0.40, 0.70), ctx_range=(20, 150), decide=decide, alpha_per=per)
+    args.update(kw)
+    return synth.Workload(**args)
+
+
+def _fill(r, seqs):
+    """Each sequence's prompt, in chunks of up to 64, one sequence at a time."""
+    ctx = r.prep.draw.ctx
+    for b in seqs:
+        s = 0
+        while s < int(ctx[b]):
+            n = min(64, int(ctx[b]) - s)
+            r.prefill_chunk([b], s, n, attend=False)
+            s += n
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_step_ragged_positions(name):
+    _cuda()
+    wl = _workload(name, list(SHAPES).index(name))
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    ctx = prep.draw.ctx
+    seqs = list(np.random.default_rng(wl.cfg_id).permutation(wl.B))
+    _fill(r, seqs)
+    r.check_tables(pages=True)
+    log(f"{name}: prompts {[int(ctx[b]) for b in seqs]}")
+    worst = (0.0, 0.0)
+    for i in range(wl.decode_steps):
+        # every third step through the two-call path: both leave the same state
+        st = r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], step=i % 3 != 2, fused=i % 3 == 2)
+        worst = (max(worst[0], st[0]), max(worst[1], st[1]))
+        r.check_tables(pages=True)
+    assert r.dms.dms_cache_status(r.cache) == 0
+    log(f"{name}: worst err {worst}, stats {r.sim.stats()}")
+
+
+def test_step_from_empty_cache():
+    """Decode from position 0: heads whose only key is the current token, a page
+    opened every 16 steps, in-place reuse from step 24 on."""
+    _cuda()
+    wl = _workload("g4_d128_linear", 0, ctx_range=None, prefill=0, decode_steps=70, cfg_id=50)
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    seqs = [2, 0, 1]
+    for t in range(wl.decode_steps):
+        r.decode_step(seqs, [t] * 3, step=True)
+        r.check_tables(pages=True)
+    log(f"empty start: stats {r.sim.stats()}")
+
+
+def test_step_subset_of_rows_and_capacity():
+    """A call over some rows leaves the others alone; a row at its capacity is
+    flagged and not appended while the other rows proceed."""
+    torch = _cuda()
+    from learned_kv_cache_amd import dms
+    wl = _workload("g2_d64_qneuron", 1, ctx_range=None, prefill=0, decode_steps=12, cfg_id=51)
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    for t in range(4):
+        r.decode_step([1], [t], step=True)
+    for t in range(4):
+        r.decode_step([0, 2], [t, t], step=True)
+    r.check_tables(pages=True)
+    # row 1 runs to its capacity (12 tokens), then one more step over rows 1 and 0
+    for t in range(4, 12):
+        r.decode_step([1], [t], step=True)
+    r.check_tables(pages=True)
+    before = r.dms.dms_cache_dump(r.cache)
+    B = 2
+    ids = to_dev(np.array([1, 0], np.int32), "i32")
+    q = torch.randn(B * wl.Hq * wl.D, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B * wl.Hkv * wl.D, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ev = torch.empty(B * wl.Hkv, dtype=torch.uint8, device="cuda")
+    dms.dms_decode_step(r.cache, ids, None, None, None, None, r.off, q.clone(), k, k, out, B, None, ev)
+    assert dms.dms_cache_status(r.cache) & dms.DMS_DEV_CAPACITY
+    after = r.dms.dms_cache_dump(r.cache)
+    assert int(after["positions"][1]) == 12 and int(after["positions"][0]) == 5
+    assert np.array_equal(after["lengths"][1], before["lengths"][1])
+    # row 1's attention is over its 12-token cache as it stands: the same as dms_decode_attn's
+    ref = torch.empty_like(q)
+    qz = q.clone()
+    one = to_dev(np.array([1], np.int32), "i32")
+    qz1 = qz[: wl.Hq * wl.D].clone().view(wl.Hq, wl.D)
+    qz1[:: wl.g, -1] = 0
+    dms.dms_decode_attn(r.cache, one, qz1.reshape(-1), ref[: wl.Hq * wl.D], 1)
+    err = (from_dev(out[: wl.Hq * wl.D]) - from_dev(ref[: wl.Hq * wl.D]))
+    assert np.abs(err).max() <= 1e-2, np.abs(err).max()
+
+
+def test_step_bad_sequence_id():
+    torch = _cuda()
+    from learned_kv_cache_amd import dms
+    wl = _workload("g4_d128_linear", 0, ctx_range=None, prefill=0, decode_steps=4, cfg_id=52)
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    r.decode_step([0, 1], [0, 0], step=True)
+    ids = to_dev(np.array([0, 7], np.int32), "i32")
+    B = 2
+    h = torch.randn(B * wl.hidden, device="cuda").to(torch.bfloat16)
+    q = torch.randn(B * wl.Hq * wl.D, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B * wl.Hkv * wl.D, device="cuda").to(torch.bfloat16)
+    out = torch.full_like(q, 3.0)
+    ev = torch.empty(B * wl.Hkv, dtype=torch.uint8, device="cuda")
+    dms.dms_decode_step(r.cache, ids, h, r.gamma, r.W, None, r.off, q, k, k, out, B, None, ev)
+    assert dms.dms_cache_status(r.cache) & dms.DMS_DEV_BAD_SEQ
+    assert float(out[wl.Hq * wl.D:].float().abs().max()) == 0.0     # the bad row's heads have no keys
+    dump = r.dms.dms_cache_dump(r.cache)
+    assert int(dump["positions"][0]) == 2 and int(dump["positions"][1]) == 1

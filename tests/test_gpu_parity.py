@@ -22,9 +22,9 @@ def _cuda():
     return torch
 
 
-@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("path", ["unfused", "prepare", "step"])
 @pytest.mark.parametrize("mode", ["head", "layer", "disabled"])
-def test_tiny_prefill_then_decode_every_step(mode, fused):
+def test_tiny_prefill_then_decode_every_step(mode, path):
     _cuda()
     wl = synth.TINY
     if mode == "layer":
@@ -39,7 +39,7 @@ def test_tiny_prefill_then_decode_every_step(mode, fused):
     log(f"tiny {mode}: prefill err {st}")
     r.check_tables(pages=True)
     for t in range(64, 128):
-        r.decode_step([0], [t], fused=fused)
+        r.decode_step([0], [t], fused=path == "prepare", step=path == "step")
         r.check_tables(pages=True)
     log(f"tiny {mode}: decode ok, stats {r.sim.stats()}")
     if mode == "disabled":
@@ -77,7 +77,7 @@ def test_tiny_reset_and_reuse():
     r.check_tables(pages=True)
     for t in range(40, 50):
         r.decode_step([2, 0], [t, t], fused=t % 2 == 0)
-    r.decode_step([1], [80], fused=True)
+    r.decode_step([1], [80], step=True)
     r.check_tables(pages=True)
     assert r.dms.dms_cache_status(r.cache) == 0
 
@@ -135,7 +135,7 @@ def test_llama1b_prefill_8k_then_decode():
     r.check_tables(pages=True)
     worst = (0.0, 0.0)
     for i in range(wl.decode_steps):
-        st = r.decode_step([0], [8192 + i], fused=i % 2 == 1)
+        st = r.decode_step([0], [8192 + i], fused=i % 3 == 1, step=i % 3 == 2)
         worst = (max(worst[0], st[0]), max(worst[1], st[1]))
     r.check_tables()
     stats = r.dms.dms_cache_stats(r.cache)
@@ -157,7 +157,7 @@ def test_qwen8b_ctx8k_b8_decode():
     r.check_tables()
     worst = (0.0, 0.0)
     for i in range(wl.decode_steps):
-        st = r.decode_step(seqs, [8192 + i] * wl.B, fused=True)
+        st = r.decode_step(seqs, [8192 + i] * wl.B, fused=i % 2 == 1, step=i % 2 == 0)
         worst = (max(worst[0], st[0]), max(worst[1], st[1]))
         if i % 32 == 31:
             r.check_tables()
@@ -178,7 +178,7 @@ def test_qwen8b_prefill_32k_chunked(variant):
         log(f"prefill32k {variant}: chunk {s} err {st}")
     r.check_tables()
     for i in range(wl.decode_steps):
-        r.decode_step([0], [32768 + i], check=(i % 16 == 0), fused=i % 2 == 0)
+        r.decode_step([0], [32768 + i], check=(i % 16 == 0), fused=i % 3 == 0, step=i % 3 == 1)
     r.check_tables()
 
 
@@ -198,7 +198,8 @@ def test_qwen8b_fp8_serving_b64():
     r.check_tables()
     seqs = list(range(wl.B))
     for i in range(wl.decode_steps):
-        st = r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], check=(i % 32 == 0), fused=True)
+        st = r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], check=(i % 32 == 0), fused=i % 2 == 1,
+                           step=i % 2 == 0)
         if st:
             log(f"fp8 serving: step {i} err {st}")
     r.check_tables()

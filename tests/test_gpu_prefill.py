@@ -52,5 +52,5 @@ def test_prefill_shapes_ragged_chunks(name):
         s += n
     r.check_tables(pages=True)
     for i in range(wl.decode_steps):
-        r.decode_step(seqs, [s + i] * 2, fused=i % 2 == 1)
+        r.decode_step(seqs, [s + i] * 2, fused=i % 3 == 1, step=i % 3 == 2)
     r.check_tables(pages=True)
