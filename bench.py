@@ -8,14 +8,15 @@ every one of 36 layers (Qwen3-8B depth) is built separately, so one decode
 step streams ~1.7 GB of live K/V, far more than the 256 MB Infinity Cache.
 
 A step is one decode token for every sequence through all 36 layers: per layer
-dms_decode_prepare (RMSNorm + linear adapter + threshold, then delayed
-eviction with in-place slot reuse, one launch) -> dms_decode_attn.
-(--unfused: dms_decide -> dms_append_evict -> dms_decode_attn.)  Steps are
-captured as HIP graphs and replayed; inputs (hidden states, Q, K, V of every
-step) are resident in HBM before the timed region.
+one dms_decode_step launch (RMSNorm + linear adapter + threshold, delayed
+eviction with in-place slot reuse, and the attention over the live slots).
+(--path prepare: dms_decode_prepare -> dms_decode_attn; --path unfused:
+dms_decide -> dms_append_evict -> dms_decode_attn.)  Steps are captured as HIP
+graphs and replayed; inputs (hidden states, Q, K, V of every step) are
+resident in HBM before the timed region.
 
 Output: one JSON line (metric, value = decode tokens/s per layer, roofline of
-the decode-attention kernel, CPU-oracle baseline, prefill figures).
+the step's dominant kernel, CPU-oracle baseline, prefill figures).
 """
 from __future__ import annotations
 
@@ -50,7 +51,7 @@ def traffic_from_profiles(kind: str):
     with open(path) as fh:
         rec = json.load(fh)
     from learned_kv_cache_amd.counters import source_hash
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -120,10 +121,14 @@ def calibrate_and_fill(layer, wl, dms, torch):
         dms.dms_append_evict(layer.cache, None, k, v, ev, B, C)
 
 
-def decode_step(layers, s, wl, dms, fused=True):
+def decode_step(layers, s, wl, dms, path="step"):
     B = wl.B
     for L in layers:
-        if fused:
+        if path == "step":
+            dms.dms_decode_step(L.cache, None, L.h_dec[s], L.gamma, L.W, None, L.off, L.q_dec[s], L.k_dec[s],
+                                L.v_dec[s], L.out, B, None, L.evict)
+            continue
+        if path == "prepare":
             dms.dms_decode_prepare(L.cache, None, L.h_dec[s], L.gamma, L.W, None, L.off, None, L.k_dec[s],
                                    L.v_dec[s], B, None, L.evict)
         else:
@@ -162,7 +167,7 @@ def run_decode(args, dms, synth, torch):
         for s in range(S):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                decode_step(layers, s, wl, dms, fused=not args.unfused)
+                decode_step(layers, s, wl, dms, args.path)
             graphs.append(g)
         torch.cuda.synchronize()
         log(f"captured {S} step graphs")
@@ -171,7 +176,7 @@ def run_decode(args, dms, synth, torch):
         if graphs:
             graphs[s].replay()
         else:
-            decode_step(layers, s, wl, dms, fused=not args.unfused)
+            decode_step(layers, s, wl, dms, args.path)
 
     for s in range(args.warmup):
         step(s)
@@ -192,9 +197,10 @@ def run_decode(args, dms, synth, torch):
     tok_s_layer = wl.B * args.steps * args.layers / (elapsed_ms / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {tok_s_layer / 1e6:.3f} M tok/s/layer")
 
-    # Decode attention alone: one graph holding the dms_decode_attn calls of
-    # all layers (the cache state does not change), replayed; HIP events on the
-    # launch stream around the replays; average per call.
+    # Decode attention alone (context for the two-call paths): one graph
+    # holding the dms_decode_attn calls of all layers (the cache state does not
+    # change), replayed; HIP events on the launch stream around the replays;
+    # average per call.
     reps = args.attn_reps
     ga = torch.cuda.CUDAGraph()
     with torch.cuda.graph(ga):
@@ -219,8 +225,17 @@ def run_decode(args, dms, synth, torch):
     attn_gbs = attn_bytes / (attn_us * 1e-6) / 1e9
     mean_L = kv_live / (wl.B * wl.Hkv * 2 * row_bytes)
     step_bytes = kv_live_mid + qo_bytes
+    # one dms_decode_step launch: the live K/V after the append (the current
+    # token's row comes from the input), Q and O, the hidden state, the adapter
+    # row and gamma, the new K/V rows written into the pages, the page ids
+    pages_mid = float(np.mean([(a["pages_in_use"] + b["pages_in_use"]) / 2 for a, b in zip(live0, live1)]))
+    launch_bytes = (kv_live_mid + qo_bytes + wl.B * wl.hidden * 2 + wl.Hkv * wl.hidden * 4 + wl.hidden * 4
+                    + wl.B * wl.Hkv * 2 * row_bytes + pages_mid * 4)
+    layer_us = ms_per_step * 1e3 / args.layers
     stats = live1[0]
     return {
+        "launch_bytes": launch_bytes,
+        "launch_gbs": launch_bytes / (layer_us * 1e-6) / 1e9,
         "value": tok_s_layer,
         "ms_per_step": ms_per_step,
         "attn_us": attn_us,
@@ -394,7 +409,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying graphs")
-    ap.add_argument("--unfused", action="store_true", help="separate decide and append launches")
+    ap.add_argument("--path", choices=("step", "prepare", "unfused"), default="step",
+                    help="step: one dms_decode_step launch per layer; prepare: dms_decode_prepare -> "
+                         "dms_decode_attn; unfused: dms_decide -> dms_append_evict -> dms_decode_attn")
     ap.add_argument("--cpu-steps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -422,7 +439,19 @@ def main() -> int:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(args.cpu_steps)
         log(f"cpu baseline {cpu['value']:.1f} tok/s/layer in {cpu['seconds']:.1f}s")
-    traffic = traffic_from_profiles("decode_attn")
+    if args.path == "step":
+        traffic = traffic_from_profiles("decode_step")
+        roof = {"kernel": "decode_step_kernel (dms_decode_step)", "achieved": dec["launch_gbs"],
+                "algorithmic_bytes_per_launch": dec["launch_bytes"], "avg_launch_us": dec["layer_step_us"]}
+    else:
+        traffic = traffic_from_profiles("decode_attn")
+        roof = {"kernel": "decode_attn_fast_kernel (dms_decode_attn)", "achieved": dec["attn_gbs"],
+                "algorithmic_bytes_per_launch": dec["attn_bytes"], "avg_launch_us": dec["attn_us"]}
+    steps_desc = {
+        "step": "per layer: dms_decode_step (decide + append + attention, one launch)",
+        "prepare": "per layer: dms_decode_prepare (decide + append) -> dms_decode_attn",
+        "unfused": "per layer: dms_decide -> dms_append_evict -> dms_decode_attn",
+    }
     line = {
         "metric": METRIC,
         "value": dec["value"],
@@ -440,21 +469,22 @@ def main() -> int:
             "workload": "qwen3-8b_layer_ctx8k_b8_decode",
             "layers": args.layers, "batch": 8, "ctx": 8192, "hidden": 4096, "q_heads": 32, "kv_heads": 8,
             "head_dim": 128, "window": 512, "block": 256, "evict_fraction": [0.85, 0.92],
-            "step": ("per layer: dms_decide -> dms_append_evict -> dms_decode_attn" if args.unfused else
-                     "per layer: dms_decode_prepare (decide + append) -> dms_decode_attn"),
+            "step": steps_desc[args.path],
             "graphs": dec["graphs"], "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": "decode_attn (dms_decode_attn)",
+            "kernel": roof["kernel"],
             "bound": "hbm",
-            "achieved": dec["attn_gbs"],
+            "achieved": roof["achieved"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": dec["attn_gbs"] / HBM_PEAK_GBS,
+            "frac": roof["achieved"] / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": dec["attn_bytes"],
-            "avg_launch_us": dec["attn_us"],
+            "algorithmic_bytes_per_launch": roof["algorithmic_bytes_per_launch"],
+            "avg_launch_us": roof["avg_launch_us"],
         },
+        "attn_only": {"kernel": "decode_attn_fast_kernel (dms_decode_attn)", "avg_launch_us": dec["attn_us"],
+                      "achieved_gbs": dec["attn_gbs"], "algorithmic_bytes_per_launch": dec["attn_bytes"]},
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "layer_step_us": dec["layer_step_us"],
         "step_kv_gbs": dec["step_kv_gbs"],

@@ -61,6 +61,8 @@ typedef enum dms_status {
 #define DMS_DEV_POOL_EXHAUSTED 0x1  /* an append needed a page and the pool was empty */
 #define DMS_DEV_CAPACITY 0x2        /* an append would pass max_tokens_per_seq */
 #define DMS_DEV_BAD_SEQ 0x4         /* a sequence id outside [0, max_batch) */
+#define DMS_DEV_STEP_SYNC 0x8       /* a fused decode step gave up waiting for its attention workgroups;
+                                       the cache state is undefined (recreate the cache) */
 
 typedef enum dms_dtype { DMS_F32 = 0, DMS_BF16 = 1, DMS_FP8_E4M3 = 2 } dms_dtype;
 typedef enum dms_decide_mode { DMS_DECIDE_LINEAR = 0, DMS_DECIDE_QNEURON = 1 } dms_decide_mode;
@@ -221,7 +223,10 @@ int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, voi
  * of the attention, which takes the current token from k/v and masks the
  * slot it overwrites; the last workgroup to finish its reads of the shared
  * tables commits the append.  Other configurations call dms_decode_prepare,
- * then dms_decode_attn.  Device-side errors as in dms_append_evict.
+ * then dms_decode_attn.  Device-side errors as in dms_append_evict, and
+ * DMS_DEV_STEP_SYNC if the commit's bounded wait for the attention
+ * workgroups ran out (only when far more workgroups than the GPU holds at
+ * once queue behind it).
  */
 int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden, const float* rms_gamma,
                     const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,

@@ -7,8 +7,8 @@ by what it reads for a plain elementwise copy of known size that the same
 program runs at its end (`bench.py --copy-calib MiB`: torch.neg over a bf16
 tensor, which reads and writes that many bytes once).
 
-    python -m learned_kv_cache_amd.counters FETCH.csv WRITE.csv \
-        --kernel decode_attn_fast_kernel --copy-mib 1024 --out profiles/decode_attn_counters.json
+    python -m learned_kv_cache_amd.counters FETCH.csv WRITE.csv --kind decode_step \
+        --copy-mib 1024 --out profiles/decode_step_counters.json
 
 The record carries a hash of the kernel's sources; bench.py reports the
 traffic only while the hash matches the current sources.
@@ -26,14 +26,18 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "learned_kv_cache_amd", "csrc")
 
-# The sources that decide what the decode attention kernel does.
-DECODE_ATTN_SOURCES = ("decode_attn.hip", "dms_internal.h")
+# Per kind of record: the kernel (a substring of its name) and the sources
+# that decide what it does.
+KINDS = {
+    "decode_attn": ("decode_attn_fast_kernel", ("decode_attn.hip", "dms_internal.h")),
+    "decode_step": ("decode_step_kernel", ("decode_attn.hip", "decode_prep.h", "dms_internal.h")),
+}
 COPY_KERNEL = "neg_kernel"
 
 
-def source_hash(files=DECODE_ATTN_SOURCES) -> str:
+def source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for f in files:
+    for f in KINDS[kind][1]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -73,17 +77,19 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("fetch_csv")
     ap.add_argument("write_csv")
-    ap.add_argument("--kernel", default="decode_attn_fast_kernel")
+    ap.add_argument("--kind", choices=sorted(KINDS), default="decode_step")
     ap.add_argument("--copy-mib", type=float, default=1024.0)
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", action="append", default=[], help="command lines that made the CSVs")
     a = ap.parse_args(argv)
     kib = a.copy_mib * 1024.0
-    f = calibrated(a.fetch_csv, "FETCH_SIZE", a.kernel, kib)
-    w = calibrated(a.write_csv, "WRITE_SIZE", a.kernel, kib)
+    kernel = KINDS[a.kind][0]
+    f = calibrated(a.fetch_csv, "FETCH_SIZE", kernel, kib)
+    w = calibrated(a.write_csv, "WRITE_SIZE", kernel, kib)
     rec = {
-        "kernel": a.kernel,
-        "source_hash": source_hash(),
+        "kind": a.kind,
+        "kernel": kernel,
+        "source_hash": source_hash(a.kind),
         "fetch": f,
         "write": w,
         "hbm_bytes_per_launch": f["bytes_per_dispatch"] + w["bytes_per_dispatch"],

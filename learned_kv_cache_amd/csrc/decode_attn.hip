@@ -425,16 +425,17 @@ template <int NP, int NV>
 struct KvChunk {
   uint4 k[NP][NV];
   uint4 v[NP][NV];
-  int pg[NP];
+  float sk[NP], sv[NP];    // fp8 page scales of each pass's rows
 };
 
-// Issues the loads of passes [pass0, pass0 + NP) of a segment; rows at or past
-// `hi` are not loaded.
+// Issues the loads of passes [pass0, pass0 + NP) of a segment (rows at or
+// past `hi` load a stand-in row, masked by compute_chunk).
 // STEP: row `vrow` of the unit is the current token, read from the input rows
 // kin/vin (this lane's bytes) instead of a page.
 template <int D, int NP, bool FP8, int LPR, bool STEP = false>
 __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c, const uint8_t* __restrict__ kp,
-                                           const uint8_t* __restrict__ vp, int pt_reg, int first_page, int lo, int pass0,
+                                           const uint8_t* __restrict__ vp, const float* __restrict__ scales, int pt_reg,
+                                           int first_page, int lo, int pass0,
                                            int hi, int wave, int lane_row, int lane_col, int psh, int pmask,
                                            int vrow = -1, const uint8_t* kin = nullptr, const uint8_t* vin = nullptr) {
   constexpr int RB = D * (FP8 ? 1 : 2);
@@ -442,6 +443,8 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
   constexpr int NV = BPL / 16;
   constexpr int RG = 64 / LPR;
   constexpr int RPP = 4 * RG;
+  // page of the block's first row (live, so its bytes are finite)
+  const int pg_lo = __builtin_amdgcn_readlane(pt_reg, (lo >> psh) - first_page);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int r = lo + (pass0 + p) * RPP + wave * RG + lane_row;
@@ -451,22 +454,27 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
     const int rf = lo + (pass0 + p) * RPP + wave * RG;
     const int pf = __builtin_amdgcn_readlane(pt_reg, min((rf >> psh) - first_page, 63));
     const int pl = __builtin_amdgcn_readlane(pt_reg, min(((rf + RG - 1) >> psh) - first_page, 63));
-    c.pg[p] = ok ? (((r >> psh) == (rf >> psh)) ? pf : pl) : 0;
-    const uint32_t off = (static_cast<uint32_t>(c.pg[p]) * static_cast<uint32_t>(pmask + 1) +
-                          static_cast<uint32_t>(r & pmask)) * static_cast<uint32_t>(RB) +
+    // Every lane loads: a row past the end rereads the block's first row
+    // (STEP: the input row) and is masked in the compute.  Loads under a
+    // branch would make the compiler wait for this chunk's loads before
+    // computing the previous one.
+    const int pg = ok ? (((r >> psh) == (rf >> psh)) ? pf : pl) : pg_lo;
+    const int rr = ok ? r : lo;
+    if (FP8) {
+      // issued with the rows (a load issued later would be waited for with them)
+      c.sk[p] = scales[2 * pg];
+      c.sv[p] = scales[2 * pg + 1];
+    }
+    const uint32_t off = (static_cast<uint32_t>(pg) * static_cast<uint32_t>(pmask + 1) +
+                          static_cast<uint32_t>(rr & pmask)) * static_cast<uint32_t>(RB) +
                          static_cast<uint32_t>(lane_col * BPL);
-    const bool cur = STEP && r == vrow;
+    const bool cur = STEP && (r == vrow || !ok);
     const uint8_t* kb = cur ? kin : kp + off;
     const uint8_t* vb = cur ? vin : vp + off;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (ok) {
-        c.k[p][j] = *reinterpret_cast<const uint4*>(kb + 16 * j);
-        c.v[p][j] = *reinterpret_cast<const uint4*>(vb + 16 * j);
-      } else {
-        c.k[p][j] = make_uint4(0, 0, 0, 0);
-        c.v[p][j] = make_uint4(0, 0, 0, 0);
-      }
+      c.k[p][j] = *reinterpret_cast<const uint4*>(kb + 16 * j);
+      c.v[p][j] = *reinterpret_cast<const uint4*>(vb + 16 * j);
     }
   }
 }
@@ -474,8 +482,8 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
 // Online-softmax update with the rows of one chunk.
 // STEP: slot `skip` of the unit (the key the current token overwrites) is masked.
 template <int D, int G, int NP, bool FP8, int LPR, bool STEP = false>
-__device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c,
-                                              const float* __restrict__ scales, int lo, int pass0, int hi, int wave,
+__device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c, int lo,
+                                              int pass0, int hi, int wave,
                                               int lane_row, float scale_log2,
                                               const uint32_t (&qv)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2)) / 2],
                                               float (&m)[G], float (&l)[G],
@@ -498,8 +506,8 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
     sk[p] = scale_log2;
     sv[p] = 1.0f;
     if (FP8) {
-      sk[p] *= scales[2 * c.pg[p]];
-      sv[p] = scales[2 * c.pg[p] + 1];
+      sk[p] *= c.sk[p];
+      sv[p] = c.sv[p];
     }
   }
   float s[NP][G];
@@ -653,13 +661,19 @@ struct StepArgs {
   const uint8_t* k;        // [B][Hkv][D] bf16 rows of the current token
   const uint8_t* v;
   int npairs;              // workgroups of the prepare role (B * Hkv), placed first in the grid
-  int arrivals;            // npairs + attention workgroups: the commit waits for all of them
+  int groups;              // arrival groups of the attention workgroups (min(kArriveGroups, their count))
+  int agrid;               // attention workgroups
   int qneuron;             // the decision neuron (last element of each group's first query head) reads as zero
 };
+
+// Up to this many units (and at most half as many as workgroups) each unit
+// gets whole workgroups of its own.
+constexpr int kAlignedUnits = 512;
 
 template <int G, int D, bool STEP>
 struct FastLds {
   int start[kMaxUnits + 1];
+  int wstart[kAlignedUnits + 1];       // unit-aligned split: first workgroup of each unit
   int ext[STEP ? kMaxUnits : 1];    // STEP: -1 no current token, else 1 + the slot it overwrites (0: appended)
   int tmp[4];
   union {
@@ -704,13 +718,11 @@ __device__ __forceinline__ int unit_slots(const DecodeArgs& a, int u, int wg, in
 // attention of the fused decode step, run before the current token is in the
 // cache: each unit's rows are its live slots plus one more, the current
 // token, read from the input rows; the slot the token overwrites in place is
-// masked.  The same keys as after the append.  Once every workgroup has read
-// the lengths, positions and ring entries it works from, it arrives on the
-// step's counter; the last of the step's workgroups to arrive commits the
-// prepare role's tables (prep_commit).
+// masked.  The same keys as after the append.  Once a workgroup has read the
+// lengths, positions and ring entries it works from, it counts itself on its
+// arrival group; the prepare role's commit waits for all of them.
 template <int D, int G, int NP, bool FP8, int LPR, bool STEP>
-__device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const AppendArgs* ap, const PrepIn* pin,
-                                                      const StepArgs* sa, int wg, int grid,
+__device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const StepArgs* sa, int wg, int grid,
                                                       FastLds<G, D, STEP>& lds) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int RB = D * EB;
@@ -776,16 +788,46 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     __syncthreads();
   }
   if constexpr (STEP) {
-    // every read of state the commit changes is done: arrive
+    // every read of state the commit changes has returned (the values are in
+    // LDS): arrive, without waiting for the add to complete
     if (tid == 0)
-      lds.prep.last = __hip_atomic_fetch_add(d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      sa->arrivals - 1;
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(lds.prep.last)) prep_commit<DMS_BF16>(*ap, *pin, sa->npairs, lds.prep);
-    __syncthreads();
+      __hip_atomic_fetch_add(d.arrive + (wg % sa->groups) * kArriveStride, 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
   const int W = s_start[units];
   const int c = max((W + grid - 1) / grid, RPP);
+  // Few units: each unit gets 1 + floor(its share of the spare workgroups)
+  // workgroups of its own (at most one per RPP rows), so no workgroup spans
+  // two units (a second segment would repeat the setup and the merge).
+  // Otherwise the concatenated slots are cut into equal ranges.
+  const bool aligned = units <= kAlignedUnits && 2 * units <= grid;
+  int* s_wstart = lds.wstart;
+  if (aligned) {
+    const int spare = grid - units;
+    const int u0 = tid * 2;
+    int nw[2], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = u0 + i;
+      int n = 0;
+      if (u < units) {
+        const int wu = s_start[u + 1] - s_start[u];
+        if (wu > 0)
+          n = min(1 + static_cast<int>(static_cast<int64_t>(wu) * spare / W), max(1, wu / RPP));
+      }
+      nw[i] = n;
+      sum += n;
+    }
+    int tot;
+    int run = block_scan_256(sum, s_tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (u0 + i < units) s_wstart[u0 + i] = run;
+      run += nw[i];
+    }
+    if (tid == 0) s_wstart[units] = tot;
+    __syncthreads();
+  }
 
   // heads without live slots have no workgroup: workgroup 0 writes zeros
   if (wg == 0) {
@@ -797,15 +839,32 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     }
   }
 
-  int a0 = wg * c;
-  const int a1 = min(a0 + c, W);
-  if (a0 >= a1) return;
-  int lo_u = 0, hi_u = units - 1;
-  while (lo_u < hi_u) {
-    const int mid = (lo_u + hi_u + 1) >> 1;
-    if (s_start[mid] <= a0) lo_u = mid; else hi_u = mid - 1;
+  int a0, a1, u;
+  if (aligned) {
+    if (wg >= s_wstart[units]) return;
+    // the unit owning workgroup wg: the last u with s_wstart[u] <= wg (units without slots share starts)
+    int lo_u = 0, hi_u = units - 1;
+    while (lo_u < hi_u) {
+      const int mid = (lo_u + hi_u + 1) >> 1;
+      if (s_wstart[mid] <= wg) lo_u = mid; else hi_u = mid - 1;
+    }
+    u = lo_u;
+    const int k = wg - s_wstart[u], n = s_wstart[u + 1] - s_wstart[u];
+    const int wu = s_start[u + 1] - s_start[u];
+    a0 = s_start[u] + static_cast<int>(static_cast<int64_t>(k) * wu / n);
+    a1 = s_start[u] + static_cast<int>(static_cast<int64_t>(k + 1) * wu / n);
+  } else {
+    a0 = wg * c;
+    a1 = min(a0 + c, W);
+    if (a0 >= a1) return;
+    // unit holding slot a0: the last u with s_start[u] <= a0 (empty units share starts)
+    int lo_u = 0, hi_u = units - 1;
+    while (lo_u < hi_u) {
+      const int mid = (lo_u + hi_u + 1) >> 1;
+      if (s_start[mid] <= a0) lo_u = mid; else hi_u = mid - 1;
+    }
+    u = lo_u;
   }
-  int u = lo_u;
   bool first_seg = true;
   uint16_t* obase = static_cast<uint16_t*>(a.out);
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
@@ -863,21 +922,32 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       const int pt_reg = (pb + lane <= plast) ? pt[pb + lane] : 0;
       const int blo = max(lo, pb << psh), bhi = min(hi, (plast + 1) << psh);
       const int npass = (bhi - blo + RPP - 1) / RPP;
+      // The next chunk's loads are issued before the current chunk's compute,
+      // unconditionally and with no exit between them and their use (past
+      // the end they reread a stand-in row, and a trailing chunk past the end
+      // is computed fully masked): a load under a branch, or one that an exit
+      // leaves unused, is waited for or moved down to its use by the compiler.
+      // The scheduling barriers keep the written order: the counter of
+      // outstanding loads drains in issue order, so a chunk issued ahead of
+      // the one being waited for would be waited for too.
       KvChunk<NP, NV> ca, cb;
-      load_chunk<D, NP, FP8, LPR, STEP>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, 0, bhi, wave, lane_row, lane_col, psh,
-                                        pmask, vrow, kin, vin);
+      auto load = [&](KvChunk<NP, NV>& ch, int pass0) {
+        load_chunk<D, NP, FP8, LPR, STEP>(ch, d.k_pages, d.v_pages, d.scales, pt_reg, pb, blo, pass0, bhi, wave,
+                                          lane_row, lane_col, psh, pmask, vrow, kin, vin);
+      };
+      auto compute = [&](const KvChunk<NP, NV>& ch, int pass0) {
+        compute_chunk<D, G, NP, FP8, LPR, STEP>(ch, blo, pass0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o, skip);
+      };
+      load(ca, 0);
       for (int p0 = 0; p0 < npass; p0 += 2 * NP) {
-        if (p0 + NP < npass)
-          load_chunk<D, NP, FP8, LPR, STEP>(cb, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + NP, bhi, wave, lane_row,
-                                            lane_col, psh, pmask, vrow, kin, vin);
-        compute_chunk<D, G, NP, FP8, LPR, STEP>(ca, d.scales, blo, p0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o,
-                                                skip);
-        if (p0 + NP >= npass) break;
-        if (p0 + 2 * NP < npass)
-          load_chunk<D, NP, FP8, LPR, STEP>(ca, d.k_pages, d.v_pages, pt_reg, pb, blo, p0 + 2 * NP, bhi, wave,
-                                            lane_row, lane_col, psh, pmask, vrow, kin, vin);
-        compute_chunk<D, G, NP, FP8, LPR, STEP>(cb, d.scales, blo, p0 + NP, bhi, wave, lane_row, g.scale_log2, qv, m,
-                                                l, o, skip);
+        __builtin_amdgcn_sched_barrier(0);
+        load(cb, p0 + NP);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ca, p0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(ca, p0 + 2 * NP);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cb, p0 + NP);
       }
     }
     // per-column sums over the wave's rows go through LDS: lanes of the first
@@ -905,7 +975,11 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       for (int h = 0; h < G; ++h) lds.ml[wave][0][h][0] = m[h];
     }
     __syncthreads();
-    const int w0 = ustart / c, w1 = (uend - 1) / c;
+    // the unit's workgroups w0..w1 (concatenated split: w0's record is its
+    // second one when the unit starts inside w0's range)
+    const int w0 = aligned ? s_wstart[u] : ustart / c;
+    const int w1 = aligned ? s_wstart[u + 1] - 1 : (uend - 1) / c;
+    const int odd = (!aligned && ustart != w0 * c) ? 1 : 0;
     const bool split = w1 > w0;
     const int rec = 2 * wg + (first_seg ? 0 : 1);
     for (int idx = tid; idx < G * D; idx += 256) {
@@ -948,8 +1022,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       if (tid == 0) s_tmp[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
       __syncthreads();
       if (s_tmp[0]) {
-        merge_unit_records<D, G>(d.partials, w0, w1, (ustart != w0 * c) ? 1 : 0,
-                                 obase + (static_cast<size_t>(row) * g.Hq + kh * G) * D);
+        merge_unit_records<D, G>(d.partials, w0, w1, odd, obase + (static_cast<size_t>(row) * g.Hq + kh * G) * D);
         if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -965,28 +1038,58 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
 template <int D, int G, int NP, bool FP8, int LPR>
 __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
   __shared__ FastLds<G, D, false> lds;
-  decode_attn_fast_body<D, G, NP, FP8, LPR, false>(a, nullptr, nullptr, nullptr, blockIdx.x, gridDim.x, lds);
+  decode_attn_fast_body<D, G, NP, FP8, LPR, false>(a, nullptr, blockIdx.x, gridDim.x, lds);
 }
 
 // dms_decode_step: workgroups [0, npairs) prepare the current token of one
-// (row, KV head) pair each (decision, placement, plan record) and arrive on
-// the step's counter; the others run the attention (STEP).  The last arrival
-// commits.
+// (row, KV head) pair each (decision, placement, plan record); the others run
+// the attention (STEP).  The last pair to finish waits until every attention
+// workgroup has arrived (read the tables it works from), then commits.
 template <int D, int G, int NP, int LPR>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
   __shared__ FastLds<G, D, true> lds;
   if (static_cast<int>(blockIdx.x) < sa.npairs) {
-    prep_pair<DMS_BF16>(ap, pin, blockIdx.x, true, lds.prep);
+    PrepShared& sh = lds.prep;
+    prep_pair<DMS_BF16>(ap, pin, blockIdx.x, true, sh);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
-      lds.prep.last = __hip_atomic_fetch_add(ap.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) == sa.arrivals - 1;
+      sh.last = __hip_atomic_fetch_add(ap.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                sa.npairs - 1;
     __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(lds.prep.last)) prep_commit<DMS_BF16>(ap, pin, sa.npairs, lds.prep);
+    if (!__builtin_amdgcn_readfirstlane(sh.last)) return;
+    // the last pair commits once every attention workgroup has arrived: lane
+    // i of wave 0 polls group i (bounded; all of them are normally resident
+    // and arrive within their first microseconds)
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+      bool ok = true;
+      if (lane < sa.groups) {
+        const int want = sa.agrid / sa.groups + (lane < sa.agrid % sa.groups ? 1 : 0);
+        const int32_t* gc = ap.d.arrive + lane * kArriveStride;
+        for (int it = 0;; ++it) {
+          if (__hip_atomic_load(gc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+          if (it == kArriveSpinLimit) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      const bool all = __all(ok);
+      if (lane == 0) sh.n = all ? 1 : 0;
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(sh.n)) {
+      if (threadIdx.x == 0) set_status(ap.d.ctl, DMS_DEV_STEP_SYNC);
+      return;
+    }
+    prep_commit<DMS_BF16>(ap, pin, sa.npairs, sh);
+    if (threadIdx.x < sa.groups)
+      __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  decode_attn_fast_body<D, G, NP, false, LPR, true>(a, &ap, &pin, &sa, blockIdx.x - sa.npairs,
+  decode_attn_fast_body<D, G, NP, false, LPR, true>(a, &sa, blockIdx.x - sa.npairs,
                                                     gridDim.x - sa.npairs, lds);
 }
 
@@ -1175,7 +1278,9 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
   PrepIn pin{static_cast<const uint16_t*>(hidden), rms_gamma, W, static_cast<uint16_t*>(q_inout), linear ? 0 : 1};
   const int npairs = B * g.Hkv;
   const int agrid = decode_grid_for(cache);
-  StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, npairs + agrid, linear ? 0 : 1};
+  const int groups = std::min(kArriveGroups, agrid);
+  StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, groups, agrid,
+              linear ? 0 : 1};
   const int s = g.D == 128 ? launch_step_d<128>(a, ap, pin, sa, npairs + agrid, st)
                            : launch_step_d<64>(a, ap, pin, sa, npairs + agrid, st);
   if (s) return s;

@@ -64,6 +64,7 @@ int compute_layout(const dms_config& c, Layout* L) {
   L->chunk_slot = take(units * static_cast<size_t>(c.max_chunk) * sizeof(int32_t));
   L->chunk_info = take(units * 8 * sizeof(int32_t));
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
+  L->arrive = take(static_cast<size_t>(kArriveGroups) * kArriveStride * sizeof(int32_t));
   L->partial_records = 2 * kMaxDecodeGrid + kMaxUnits;
   L->partials = take(static_cast<size_t>(L->partial_records) * g * (D + 2) * sizeof(float));
   L->total = off;
@@ -117,6 +118,7 @@ __global__ void init_kernel(DevCache d, Geo g, int units) {
   for (int64_t i = i0; i < g.Bmax; i += n) d.pos[i] = 0;
   for (int64_t i = i0; i < kCtlWords; i += n) d.ctl[i] = (i == kCtlFreeCount) ? g.pool : 0;
   for (int64_t i = i0; i < static_cast<int64_t>(kMaxUnits) * 4; i += n) d.unit_info[i] = 0;
+  for (int64_t i = i0; i < static_cast<int64_t>(kArriveGroups) * kArriveStride; i += n) d.arrive[i] = 0;
   for (int64_t i = i0; i < static_cast<int64_t>(g.pool) * 2; i += n) {
     d.scales[i] = 1.0f;
     d.page_amax[i] = 0u;
@@ -259,6 +261,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.chunk_slot = reinterpret_cast<int32_t*>(base + L.chunk_slot);
   c->dev.chunk_info = reinterpret_cast<int32_t*>(base + L.chunk_info);
   c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
+  c->dev.arrive = reinterpret_cast<int32_t*>(base + L.arrive);
   c->dev.partials = reinterpret_cast<float*>(base + L.partials);
   Geo& g = c->geo;
   g.Bmax = cfg->max_batch;

@@ -20,6 +20,14 @@ constexpr int kCtlWords = 64;
 constexpr int kCtlFreeCount = 0;
 constexpr int kCtlStatus = 1;
 constexpr int kCtlPrepArrive = 2;    // arrival counter of the fused decode decision + append
+// Arrival counters of the fused decode step's attention workgroups: workgroup
+// i adds one to group i % kArriveGroups (an atomic whose result it does not
+// wait for); the committing workgroup polls the groups.  One counter per
+// 256-byte line, so the adds of different groups do not queue behind each
+// other.
+constexpr int kArriveGroups = 32;
+constexpr int kArriveStride = 64;    // int32 words between counters
+constexpr int kArriveSpinLimit = 1 << 18;   // polls (each a device-scope load and a short sleep)
 
 // Device pointers carved out of the caller's buffer (see compute_layout).
 struct DevCache {
@@ -39,6 +47,7 @@ struct DevCache {
   int32_t* chunk_slot;   // [Bmax*Hkv][max_chunk] slot of each chunk token
   int32_t* chunk_info;   // [Bmax*Hkv][8]
   int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
+  int32_t* arrive;       // [kArriveGroups][kArriveStride] decode step arrival counters (word 0 of each)
   float* partials;       // decode split partials
 };
 
@@ -52,7 +61,7 @@ struct Geo {
 
 struct Layout {
   size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, partials, total;
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, partials, total;
   int64_t partial_records;
 };
 

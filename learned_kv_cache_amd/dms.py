@@ -28,6 +28,7 @@ DMS_ERR_UNSUPPORTED = -6
 DMS_DEV_POOL_EXHAUSTED = 0x1
 DMS_DEV_CAPACITY = 0x2
 DMS_DEV_BAD_SEQ = 0x4
+DMS_DEV_STEP_SYNC = 0x8
 
 DMS_F32, DMS_BF16, DMS_FP8_E4M3 = 0, 1, 2
 DMS_DECIDE_LINEAR, DMS_DECIDE_QNEURON = 0, 1
