@@ -479,6 +479,9 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
   }
 }
 
+// Lazy-rescale threshold of the decode online softmax (log2 units).
+constexpr float kDecRescaleLog2 = 8.0f;
+
 // Online-softmax update with the rows of one chunk.
 // STEP: slot `skip` of the unit (the key the current token overwrites) is masked.
 template <int D, int G, int NP, bool FP8, int LPR, bool STEP = false>
@@ -541,14 +544,21 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
 #pragma unroll
     for (int p = 1; p < NP; ++p) mx = fmaxf(mx, s[p][h]);
     mx = cross_rows_max<LPR>(mx);
-    const float m_new = fmaxf(m[h], mx);
-    // a chunk whose wave has no row leaves the state as it is (wave-uniform)
-    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[h] - m_new);
-    const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
-    m[h] = m_new;
-    l[h] *= alpha;
+    // Lazy rescale: the reference max m moves only when a score passes it by
+    // more than 2^kDecRescaleLog2 (wave-uniform branch), so the weights
+    // exp2(s - m) stay below 2^kDecRescaleLog2, exact enough in fp32 and as
+    // packed bf16, and most chunks skip the rescale.  The first real score
+    // always moves m off -inf (alpha 0 on zero state).
+    if (__builtin_amdgcn_readfirstlane(__float_as_int(mx)) != __float_as_int(-INFINITY) &&
+        __builtin_amdgcn_readfirstlane(mx > m[h] + kDecRescaleLog2)) {
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);   // m = -inf gives 0
+      m[h] = mx;
+      l[h] *= alpha;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+    }
+    // no real score yet: subtract nothing (every weight is exp2(-inf) = 0)
+    const float msub = (m[h] == -INFINITY) ? 0.0f : m[h];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       pe[p][h] = __builtin_amdgcn_exp2f(s[p][h] - msub);   // -inf gives 0
@@ -796,14 +806,16 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
   }
   const int W = s_start[units];
   const int c = max((W + grid - 1) / grid, RPP);
-  // Few units: each unit gets 1 + floor(its share of the spare workgroups)
-  // workgroups of its own (at most one per RPP rows), so no workgroup spans
-  // two units (a second segment would repeat the setup and the merge).
-  // Otherwise the concatenated slots are cut into equal ranges.
+  // Few units: each unit gets workgroups of its own, ceil(slots / ca) of
+  // them for a cap of ca = ceil(W / (grid - units)) slots per workgroup (at
+  // most one per RPP rows), so no workgroup spans two units (a second
+  // segment would repeat the setup and the merge) and none holds more than
+  // ca slots; sum(ceil(slots / ca)) <= W / ca + units <= grid.  Otherwise the
+  // concatenated slots are cut into equal ranges.
   const bool aligned = units <= kAlignedUnits && 2 * units <= grid;
   int* s_wstart = lds.wstart;
   if (aligned) {
-    const int spare = grid - units;
+    const int ca = max(1, (W + (grid - units) - 1) / (grid - units));
     const int u0 = tid * 2;
     int nw[2], sum = 0;
 #pragma unroll
@@ -812,8 +824,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       int n = 0;
       if (u < units) {
         const int wu = s_start[u + 1] - s_start[u];
-        if (wu > 0)
-          n = min(1 + static_cast<int>(static_cast<int64_t>(wu) * spare / W), max(1, wu / RPP));
+        if (wu > 0) n = min((wu + ca - 1) / ca, max(1, wu / RPP));
       }
       nw[i] = n;
       sum += n;
@@ -1089,8 +1100,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendAr
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  decode_attn_fast_body<D, G, NP, false, LPR, true>(a, &sa, blockIdx.x - sa.npairs,
-                                                    gridDim.x - sa.npairs, lds);
+  decode_attn_fast_body<D, G, NP, false, LPR, true>(a, &sa, blockIdx.x - sa.npairs, sa.agrid, lds);
 }
 
 template <int D, int G, bool FP8, int NP>
