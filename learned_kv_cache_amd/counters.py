@@ -35,11 +35,22 @@ KINDS = {
 COPY_KERNEL = "neg_kernel"
 
 
+def _code_lines(text: str):
+    """The source without // comments and blank lines (edits to comments do
+    not change what the kernel does)."""
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            yield code
+
+
 def source_hash(kind: str) -> str:
     h = hashlib.sha256()
     for f in KINDS[kind][1]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            for line in _code_lines(fh.read()):
+                h.update(line.encode())
+                h.update(b"\n")
     return h.hexdigest()[:16]
 
 

@@ -8,15 +8,18 @@
 // replaces attention scoring with split-K grouped decode attention over
 // variable-length per-head live spans; this is that idea laid out for CDNA4:
 //
-// * Work balance: the live slots of all (row, KV head) units are concatenated
-//   and cut into one contiguous range per workgroup, so every workgroup
-//   streams the same number of bytes however ragged the heads are.  A range
-//   that spans a unit boundary emits one partial per unit.
+// * Work balance: with few (row, KV head) units each unit gets whole
+//   workgroups in proportion to its live slots (no workgroup spans two
+//   units); with many, the concatenated live slots are cut into one
+//   contiguous range per workgroup and a range spanning a unit boundary
+//   emits one partial per unit.  Either way every workgroup streams about the
+//   same number of bytes however ragged the heads are.
 // * One workgroup serves all g query heads of a KV head, so K/V are read once.
 // * Each lane loads 16 contiguous bytes of a K row and of a V row; LPR lanes
-//   cover one row, a wave covers 64/LPR rows per pass, NP passes are in flight.
-// * Online softmax per wave in base 2; waves merge through LDS; units split
-//   over several workgroups are merged by a second, small kernel.
+//   cover one row, a wave covers 64/LPR rows per pass, NP passes per chunk,
+//   chunks double-buffered.
+// * Online softmax per wave in base 2; waves merge through LDS; the last
+//   workgroup of a split unit merges the unit's partial records.
 #include "dms_internal.h"
 #include "decode_prep.h"
 
@@ -368,17 +371,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // Fast path for bf16 and fp8 pages (D = 64 or 128).
 //
 // Each lane owns 16 bytes of a row (8 bf16 or 16 fp8 elements), LPR lanes a
-// row, RG = 64 / LPR rows per wave and pass, 4 waves per workgroup.  Every
-// load of a round (NP passes) is issued before any arithmetic, so one
-// workgroup keeps NP * 4 * RG rows of K and V in flight.  Scores use the
-// packed bf16 dot product (fp8 codes are widened to bf16 exactly); the row sum
-// runs over LPR lanes with DPP; probabilities are rounded to bf16 for the
-// P.V dot products, accumulation is fp32.  A unit split over workgroups
-// leaves one partial per workgroup (records 2w and 2w+1: a workgroup's first
-// and last segment) that decode_merge_kernel combines.  (Merging inside the
-// kernel through a last-arrival counter needs a device-scope release per
-// workgroup, which writes back the whole L2 of its XCD; a second small launch
-// is far cheaper.)
+// row, RG = 64 / LPR rows per wave and pass, 4 waves per workgroup.  The
+// loads of a chunk (NP passes) are issued before the previous chunk's
+// arithmetic, so a wave keeps two chunks of K and V in flight.  Scores use
+// the packed bf16 dot product (fp8 codes are widened to bf16 exactly); the
+// row sum runs over LPR lanes with DPP; probabilities are rounded to bf16 for
+// the P.V dot products, accumulation is fp32.  A unit split over workgroups
+// leaves one partial record per workgroup and segment (records 2w and 2w+1:
+// a workgroup's first and second segment), written with device-scope stores
+// (coherent across XCDs without an L2 write-back, unlike a device-scope
+// release fence); the workgroup that completes the unit's arrival count
+// merges them.
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
