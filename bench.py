@@ -335,6 +335,56 @@ def run_prefill(args, dms, synth, torch, variant="qneuron"):
     return res
 
 
+def run_train_fwd(args, dms, torch):
+    """Training-mode forward (gate + soft-eviction attention) at the Qwen3-8B
+    layer shape: B = 2 sequences of T = 4096 tokens, window 512, gate logits
+    from N(0, 3) logits plus logistic noise at tau = 0.1; each call timed with
+    HIP events on the launch stream.  Useful work: 4 * D flops per (query
+    head, causal key) pair (training keeps every causal key)."""
+    B, T, Hq, Hkv, D, w = 2, 4096, 32, 8, 128, 512
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    q = torch.randn(B, T, Hq, D, generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B, T, Hkv, D, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(B, T, Hkv, D, generator=gen, device="cuda").to(torch.bfloat16)
+    logits = 3.0 * torch.randn(B, Hkv, T, generator=gen, device="cuda")
+    u = torch.rand(B, Hkv, T, generator=gen, device="cuda").clamp(1e-6, 1 - 1e-6)
+    noise = torch.log(u) - torch.log1p(-u)
+    y = torch.empty_like(logits)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, T, device="cuda")
+
+    def once():
+        dms.dms_train_gate(logits, noise, 0.1, y, None, None)
+        dms.dms_train_attn_fwd(q, k, v, y, out, lse, window=w)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(reps):
+        dms.dms_train_gate(logits, noise, 0.1, y, None, None)
+    e1.record()
+    for _ in range(reps):
+        dms.dms_train_attn_fwd(q, k, v, y, out, lse, window=w)
+    e2.record()
+    torch.cuda.synchronize()
+    gate_ms = e0.elapsed_time(e1) / reps
+    attn_ms = e1.elapsed_time(e2) / reps
+    useful = 4.0 * D * Hq * B * T * (T + 1) / 2
+    return {
+        "workload": "qwen3-8b_layer_train_fwd_b2_t4096_w512",
+        "attn_ms": attn_ms,
+        "gate_ms": gate_ms,
+        "useful_tflop": useful / 1e12,
+        "attn_tflops": useful / (attn_ms * 1e-3) / 1e12,
+        "frac_bf16_peak": useful / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "tok_s": B * T / ((attn_ms + gate_ms) * 1e-3),
+    }
+
+
 def cpu_baseline(steps: int):
     """The CPU oracle (float64 NumPy) on a bounded sample of the same decode
     workload: one layer, B = 8, 8192-token prompt, `steps` decode steps of
@@ -434,6 +484,11 @@ def main() -> int:
         for v, r in pre.items():
             log(f"prefill {v}: {r['ms_per_prompt']:.1f} ms per 32K prompt (decide {r['decide_ms']:.2f}, "
                 f"attention {r['attn_ms']:.2f} = {r['attn_tflops']:.1f} TFLOP/s, append {r['append_ms']:.2f} ms)")
+    train = None
+    if not args.no_prefill:
+        train = run_train_fwd(args, dms, torch)
+        log(f"training forward: {train['attn_ms']:.3f} ms attention = {train['attn_tflops']:.1f} TFLOP/s, "
+            f"gate {train['gate_ms'] * 1e3:.1f} us")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -494,6 +549,7 @@ def main() -> int:
         "dense_bf16_kv_bytes_per_layer": dec["dense_bf16_kv_bytes_per_layer"],
         "cache_cr": dec["cache_cr"],
         "prefill": pre,
+        "train_fwd": train,
     }
     print(json.dumps(line), flush=True)
     if args.copy_calib:

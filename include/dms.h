@@ -232,6 +232,36 @@ int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden
                     const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,
                     const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* stream);
 
+/* ---- training mode (walkthrough, Gumbel 噪声与可微门控 and 注意力 / 训练模式) ---- */
+
+/*
+ * Forward of the training-time gating: y = (logits + noise) / tau,
+ * probs = sigmoid(y), hard = 1 where probs > 1/2 (taken as y > 0), else 0
+ * (the forward value of the straight-through decision).  The noise (the
+ * Gumbel / logistic sample the trainer draws) is an input; NULL means none.
+ * All arrays are n device floats; any output may be NULL.  tau > 0.
+ */
+int dms_train_gate(const float* logits, const float* noise, float tau, int64_t n, float* y_out,
+                   float* probs_out, float* hard_out, void* stream);
+
+/*
+ * Forward of the training-mode attention (walkthrough, 训练模式): causal
+ * attention over the whole sequence in which key j keeps its score for
+ * queries closer than `window` and gets logsigmoid(-y[j]) added for queries
+ * at distance window or more (y = the key's gate logit, e.g. dms_train_gate's
+ * y_out; a re-indexing such as the pages' shift by one is the caller's).
+ * Non-causal keys get no weight (the pages' -50000 mask value).
+ *   q [B][T][Hq][D], k, v [B][T][Hkv][D] bf16 (16-byte aligned);
+ *   gate_logits [B][Hkv][T] f32; out [B][T][Hq][D] bf16;
+ *   lse [B][Hq][T] f32: natural log of the softmax normaliser per query
+ *   (what a backward pass needs).
+ * Query head h uses KV head h / (Hq / Hkv).  head_dim 64 or 128, Hq / Hkv in
+ * {1, 2, 4}; softmax_scale <= 0 means 1 / sqrt(head_dim).  Needs no cache.
+ */
+int dms_train_attn_fwd(int B, int T, int num_q_heads, int num_kv_heads, int head_dim, int window,
+                       float softmax_scale, const void* q, const void* k, const void* v,
+                       const float* gate_logits, void* out, float* lse, void* stream);
+
 /*
  * Prefill attention for one chunk of C new tokens per sequence (walkthrough,
  * 高级选项 Chunked Prefill, and the exact prefill with the eviction mask),

@@ -14,6 +14,8 @@
 // by latency (decode), not by arithmetic; it runs in fp32 on the vector ALUs.
 // Rounding the normalised activations to bf16 for a matrix-core product would
 // move logits by ~0.1, far more than the 1e-2 margin decisions are compared at.
+#include <algorithm>
+
 #include "dms_internal.h"
 
 namespace dms {
@@ -372,4 +374,40 @@ extern "C" int dms_decide(dms_cache* cache, const void* hidden, const float* rms
     else hipLaunchKernelGGL(decide_qneuron_kernel<uint16_t>, grid, block, 0, st, a);
   }
   return check_hip(hipGetLastError(), "dms_decide launch");
+}
+
+// ---------------------------------------------------------------------------
+// Training-time gating (walkthrough, Gumbel 噪声与可微门控): the decision logit
+// plus the caller's noise, over the temperature, through a sigmoid; the
+// straight-through decision's forward value is 1 where the probability
+// exceeds 1/2, i.e. where y > 0 (taken on y, so that no rounding of the
+// sigmoid near 1/2 decides it).
+
+namespace dms {
+
+__global__ __launch_bounds__(256) void train_gate_kernel(const float* __restrict__ logits,
+                                                         const float* __restrict__ noise, float inv_tau, int64_t n,
+                                                         float* __restrict__ y_out, float* __restrict__ probs_out,
+                                                         float* __restrict__ hard_out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float y = (logits[i] + (noise ? noise[i] : 0.0f)) * inv_tau;
+    if (y_out) y_out[i] = y;
+    if (probs_out) probs_out[i] = 1.0f / (1.0f + __expf(-y));
+    if (hard_out) hard_out[i] = y > 0.0f ? 1.0f : 0.0f;
+  }
+}
+
+}  // namespace dms
+
+extern "C" int dms_train_gate(const float* logits, const float* noise, float tau, int64_t n, float* y_out,
+                              float* probs_out, float* hard_out, void* stream) {
+  if (!logits) return fail(DMS_ERR_ARG, "logits is required");
+  if (n < 0) return fail(DMS_ERR_ARG, "n must be non-negative");
+  if (!(tau > 0.0f)) return fail(DMS_ERR_ARG, "tau must be positive");
+  if (n == 0) return DMS_OK;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(train_gate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream), logits,
+                     noise, 1.0f / tau, n, y_out, probs_out, hard_out);
+  return check_hip(hipGetLastError(), "dms_train_gate launch");
 }

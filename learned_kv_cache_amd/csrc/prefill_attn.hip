@@ -16,6 +16,8 @@
 //    first product already in the operand layout of the second and the
 //    softmax statistics of a column never leave its lane.
 //  * prefill_attn_generic_kernel: vector ALU, every dtype and head size.
+#include <cmath>
+
 #include "dms_internal.h"
 
 namespace dms {
@@ -30,6 +32,8 @@ struct PrefillArgs {
   const uint8_t* evict; // [B][Hkv][C]
   void* out;            // [B][C][Hq][D]
   int B, C;
+  const float* gate;    // training forward: [B][Hkv][C] gate logits of the keys (cache unused)
+  float* lse;           // training forward: [B][Hq][C] natural-log softmax normaliser per query
 };
 
 template <int KV>
@@ -237,7 +241,8 @@ struct PfShape {
   static constexpr int META_OFF = 2 * kPfKB * ROW;   // slot metadata of the block's cache keys
   static constexpr int LO_OFF = META_OFF + 4 * kPfKB;
   static constexpr int HI_OFF = LO_OFF + 4 * kPfKB;
-  static constexpr int BUF = HI_OFF + 4 * kPfKB;
+  static constexpr int PEN_OFF = HI_OFF + 4 * kPfKB;  // training forward: gate logit, then penalty / scale
+  static constexpr int BUF = PEN_OFF + 4 * kPfKB;
   static constexpr int DC = D / 8;            // 16-byte pieces per bf16 row
   static constexpr int STHREADS = kPfKB * DC; // register path: threads staging one K and one V piece each
   static_assert(NT == 2 && STHREADS <= kPfThreads, "shape");
@@ -325,9 +330,15 @@ __device__ __forceinline__ uint4 pf_bf16(const PfRaw& r) {
 typedef __attribute__((address_space(3))) void pf_lds_void;
 typedef __attribute__((address_space(1))) void pf_glb_void;
 
-template <int D, int G, bool FP8>
+// TRAIN: the training-mode forward (walkthrough, 训练模式): no cache, the
+// chunk is the whole sequence from position 0, every causal key stays, and a
+// key j gets the penalty logsigmoid(-y_j) added to its score for queries at
+// distance w or more (y = the key's gate logit); writes the per-query
+// log-sum-exp as well.
+template <int D, int G, bool FP8, bool TRAIN = false>
 __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillArgs a) {
   using S = PfShape<D, G, FP8>;
+  static_assert(!TRAIN || !FP8, "the training forward reads bf16 rows");
   // two key-block buffers as separate arrays: with the loop unrolled by two
   // each step's buffers are static, so loads into one are known not to alias
   // reads of the other
@@ -349,16 +360,22 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   const int pair = blockIdx.x % npairs;
   const int tb = ntb - 1 - static_cast<int>(blockIdx.x) / npairs;
   const int row = pair / g.Hkv, kh = pair % g.Hkv;
-  const int seq = a.seq_ids ? a.seq_ids[row] : row;
-  if (seq < 0 || seq >= g.Bmax) {   // uniform over the workgroup: no wave reaches a barrier
+  const int seq = (a.seq_ids && !TRAIN) ? a.seq_ids[row] : row;
+  if (!TRAIN && (seq < 0 || seq >= g.Bmax)) {   // uniform over the workgroup: no wave reaches a barrier
     if (tid == 0 && tb == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
     return;
   }
   const int unit = seq * g.Hkv + kh;
   PfSrc src;
-  src.pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
-  src.L = d.lengths[unit];
-  src.s0 = d.pos[seq];
+  if constexpr (TRAIN) {
+    src.pt = nullptr;
+    src.L = 0;
+    src.s0 = 0;
+  } else {
+    src.pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
+    src.L = d.lengths[unit];
+    src.s0 = d.pos[seq];
+  }
   const int tok0 = tb * S::TOKB;
   const int tok_end = min(tok0 + S::TOKB, a.C);
   src.nk = src.L + tok_end;
@@ -366,7 +383,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   const size_t chunk0 = (static_cast<size_t>(row) * a.C * g.Hkv + kh) * D * 2;
   src.kchunk = static_cast<const uint8_t*>(a.k) + chunk0;
   src.vchunk = static_cast<const uint8_t*>(a.v) + chunk0;
-  src.ev = a.evict + static_cast<int64_t>(pair) * a.C;
+  src.ev = TRAIN ? nullptr : a.evict + static_cast<int64_t>(pair) * a.C;
+  const float* gate = TRAIN ? a.gate + static_cast<int64_t>(pair) * a.C : nullptr;
   const int nblk = (src.nk + kPfKB - 1) / kPfKB;
 
   // ---- this wave's query columns: tile c = tg * HW + h
@@ -421,7 +439,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   const pf_bf16x8 ones = __builtin_bit_cast(pf_bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
   // ---- the unit's page table and the chunk's evict flags, once
-  {
+  if constexpr (!TRAIN) {
     const int npages = (src.L + g.P - 1) >> g.Pshift;   // <= kPfMaxPages (checked at launch)
     for (int i = tid; i < npages; i += kPfThreads) s_pt[i] = src.pt[i];
     for (int i = tid; i < tok_end; i += kPfThreads) s_ev[i] = src.ev[i];
@@ -433,11 +451,29 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   // ---- visibility intervals [lo, hi) of a block's keys, by lanes 0..31 of the
   // last wave; cache keys decode the slot metadata staged at META_OFF
   const bool vis_wave = wave == kPfWaves - 1;
+  // (TRAIN: [lo, hi) = [position, position + w): causal from lo, penalised
+  // from hi; the gate logit staged at PEN_OFF becomes logsigmoid(-y) / scale,
+  // so that adding it to the raw dot product adds logsigmoid(-y) to the
+  // scaled score)
   auto vis_write = [&](int blk, uint8_t* b, int meta) {
     if (vis_wave && lane < kPfKB) {
       const int kk = blk * kPfKB + lane;
       int lo, hi;
-      if (kk < src.L) {
+      if (TRAIN) {
+        float* pen = reinterpret_cast<float*>(b + S::PEN_OFF);
+        if (kk < src.nk) {
+          lo = kk;
+          hi = kk + g.w;
+          const float y = pen[lane];
+          // logsigmoid(-y) = -softplus(y), stable for either sign
+          const float ls = -(fmaxf(y, 0.0f) + log1pf(__expf(-fabsf(y))));
+          pen[lane] = ls * (1.4426950408889634f / g.scale_log2);
+        } else {
+          lo = kPfNoLimit;
+          hi = 0;
+          pen[lane] = 0.0f;
+        }
+      } else if (kk < src.L) {
         lo = meta & 0x7FFFFFFF;
         hi = meta < 0 ? lo + g.w : kPfNoLimit;
       } else if (kk < src.nk) {
@@ -462,7 +498,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
     const int lmax = max(max(max(lo0.x, lo0.y), max(lo0.z, lo0.w)), max(max(lo1.x, lo1.y), max(lo1.z, lo1.w)));
     const int hmin = min(min(min(hi0.x, hi0.y), min(hi0.z, hi0.w)), min(min(hi1.x, hi1.y), min(hi1.z, hi1.w)));
     const int hmax = max(max(max(hi0.x, hi0.y), max(hi0.z, hi0.w)), max(max(hi1.x, hi1.y), max(hi1.z, hi1.w)));
-    const bool lane_none = !lane_live || lmin > qmax || hmax <= qmin;
+    // (TRAIN: hi only starts the penalty, it hides nothing)
+    const bool lane_none = !lane_live || lmin > qmax || (!TRAIN && hmax <= qmin);
     const bool lane_all = !lane_live || (lmax <= qmin && hmin > qmax);
     if (__all(lane_none)) return;
     // S^T = K Q^T
@@ -481,13 +518,28 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
     if (!__all(lane_all)) {
       const int los[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
       const int his[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
+      if constexpr (TRAIN) {
+        const float4 pa = *reinterpret_cast<const float4*>(b + S::PEN_OFF + 16 * G4);
+        const float4 pb = *reinterpret_cast<const float4*>(b + S::PEN_OFF + 64 + 16 * G4);
+        const float pens[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-      for (int c = 0; c < S::NT; ++c) {
-        const int qp = qpos[c / S::HW];
+        for (int c = 0; c < S::NT; ++c) {
+          const int qp = qpos[c / S::HW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool vis = los[e] <= qp && qp < his[e];
-          s[e >> 2][c][e & 3] = vis ? s[e >> 2][c][e & 3] : -INFINITY;
+          for (int e = 0; e < 8; ++e) {
+            const float v = s[e >> 2][c][e & 3] + (qp >= his[e] ? pens[e] : 0.0f);
+            s[e >> 2][c][e & 3] = los[e] <= qp ? v : -INFINITY;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < S::NT; ++c) {
+          const int qp = qpos[c / S::HW];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool vis = los[e] <= qp && qp < his[e];
+            s[e >> 2][c][e & 3] = vis ? s[e >> 2][c][e & 3] : -INFINITY;
+          }
         }
       }
     }
@@ -569,7 +621,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
         __builtin_amdgcn_global_load_lds((const pf_glb_void*)(row_src(page, kb + r, isv) + 16 * c),
                                          (pf_lds_void*)(b + (isv ? S::V_OFF : 0) + w4 * 1024), 16, 0, 0);
       }
-      if (vis_wave && kb < src.L && lane < kPfKB) {
+      if (TRAIN && vis_wave && lane < kPfKB) {
+        __builtin_amdgcn_global_load_lds((const pf_glb_void*)(gate + min(kb + lane, src.nk - 1)),
+                                         (pf_lds_void*)(b + S::PEN_OFF), 4, 0, 0);
+      }
+      if (!TRAIN && vis_wave && kb < src.L && lane < kPfKB) {
         const int kc = min(kb + lane, src.L - 1);   // same page as kb
         __builtin_amdgcn_global_load_lds(
             (const pf_glb_void*)(d.slot_meta + (static_cast<int64_t>(page) << g.Pshift) + (kc & (g.P - 1))),
@@ -658,6 +714,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
     for (int h = 0; h < S::HW; ++h) {
       const int c = tg * S::HW + h;
       const float inv = 1.0f / lacc[c][0];
+      if (TRAIN && G4 == 0)   // natural log of sum_j exp(scaled score_j)
+        a.lse[(static_cast<size_t>(row) * g.Hq + head0 + h) * a.C + t] = (mb[c] + __log2f(lacc[c][0])) * 0.6931471805599453f;
       uint16_t* orow = obase + ((static_cast<size_t>(row) * a.C + t) * g.Hq + head0 + h) * D + 4 * G4;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) {
@@ -698,9 +756,66 @@ static int launch_mfma(const PrefillArgs& a, hipStream_t st) {
   return fp8 ? launch_mfma_d<64, true>(a, st) : launch_mfma_d<64, false>(a, st);
 }
 
+template <int D, int G>
+static void launch_train_dg(const PrefillArgs& a, hipStream_t st) {
+  using S = PfShape<D, G, false>;
+  const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
+  hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, false, true>), dim3(ntb * a.B * a.g.Hkv), dim3(kPfThreads), 0, st,
+                     a);
+}
+
+template <int D>
+static int launch_train_d(const PrefillArgs& a, hipStream_t st) {
+  switch (a.g.g) {
+    case 1: launch_train_dg<D, 1>(a, st); return DMS_OK;
+    case 2: launch_train_dg<D, 2>(a, st); return DMS_OK;
+    case 4: launch_train_dg<D, 4>(a, st); return DMS_OK;
+    default: return fail(DMS_ERR_UNSUPPORTED, "group size (1, 2 or 4)");
+  }
+}
+
 }  // namespace dms
 
 using namespace dms;
+
+extern "C" int dms_train_attn_fwd(int B, int T, int num_q_heads, int num_kv_heads, int head_dim, int window,
+                                  float softmax_scale, const void* q, const void* k, const void* v,
+                                  const float* gate_logits, void* out, float* lse, void* stream) {
+  if (!q || !k || !v || !gate_logits || !out || !lse) return fail(DMS_ERR_ARG, "q, k, v, gate_logits, out and lse are required");
+  if (B <= 0 || T <= 0) return fail(DMS_ERR_ARG, "B and T must be positive");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(DMS_ERR_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (head_dim != 64 && head_dim != 128) return fail(DMS_ERR_UNSUPPORTED, "head_dim (64 or 128)");
+  if (window <= 0) return fail(DMS_ERR_ARG, "window must be positive");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(gate_logits)) % 16 != 0)
+    return fail(DMS_ERR_ARG, "q, k, v, out and gate_logits must be 16-byte aligned");
+  Geo g{};
+  g.Bmax = B;
+  g.Hq = num_q_heads;
+  g.Hkv = num_kv_heads;
+  g.D = head_dim;
+  g.g = num_q_heads / num_kv_heads;
+  g.w = window;
+  g.kv_dtype = DMS_BF16;
+  g.Pshift = -1;
+  const float sc = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
+  g.scale_log2 = sc * 1.4426950408889634f;
+  PrefillArgs a{};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.B = B;
+  a.C = T;
+  a.gate = gate_logits;
+  a.lse = lse;
+  hipStream_t st = as_stream(stream);
+  const int s = head_dim == 128 ? launch_train_d<128>(a, st) : launch_train_d<64>(a, st);
+  if (s) return s;
+  return check_hip(hipGetLastError(), "dms_train_attn_fwd launch");
+}
 
 extern "C" int dms_prefill_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, const void* k,
                                 const void* v, const uint8_t* evict, void* out, int B, int C, void* stream) {
@@ -710,7 +825,7 @@ extern "C" int dms_prefill_attn(dms_cache* cache, const int32_t* seq_ids, const 
   if (B <= 0 || C <= 0) return fail(DMS_ERR_ARG, "B and C must be positive");
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
   if (C > g.max_chunk) return fail(DMS_ERR_CAPACITY, "C above max_chunk");
-  PrefillArgs a{cache->dev, g, seq_ids, q, k, v, evict, out, B, C};
+  PrefillArgs a{cache->dev, g, seq_ids, q, k, v, evict, out, B, C, nullptr, nullptr};
   hipStream_t st = as_stream(stream);
   int s;
   if (mfma_ok(g) && !cache->force_generic) {

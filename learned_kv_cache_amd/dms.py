@@ -41,6 +41,7 @@ EXPORTS = (
     "dms_cache_destroy", "dms_cache_config", "dms_decide", "dms_append_evict", "dms_decode_attn",
     "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
+    "dms_train_gate", "dms_train_attn_fwd",
 )
 
 
@@ -97,6 +98,8 @@ def lib():
             "dms_decode_attn": [vp, vp, vp, vp, i32, vp],
             "dms_decode_prepare": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
             "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
+            "dms_train_gate": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp],
+            "dms_train_attn_fwd": [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp],
             "dms_prefill_attn": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_seq_reset": [vp, vp, i32, vp],
             "dms_cache_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
@@ -260,6 +263,28 @@ def dms_decode_step(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, offset
         _ptr(q_inout, "q_inout", ad, nq), _ptr(k, "k", ad, n), _ptr(v, "v", ad, n), _ptr(out, "out", ad, nq), B,
         _ptr(logits_out, "logits_out", torch.float32, B * c.num_kv_heads),
         _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads), _stream(stream)))
+
+
+def dms_train_gate(logits, noise, tau: float, y_out=None, probs_out=None, hard_out=None, stream=None) -> int:
+    n = logits.numel()
+    return _check(lib().dms_train_gate(
+        _ptr(logits, "logits", torch.float32), _ptr(noise, "noise", torch.float32, n), ctypes.c_float(tau),
+        ctypes.c_int64(n), _ptr(y_out, "y_out", torch.float32, n), _ptr(probs_out, "probs_out", torch.float32, n),
+        _ptr(hard_out, "hard_out", torch.float32, n), _stream(stream)))
+
+
+def dms_train_attn_fwd(q, k, v, gate_logits, out, lse, *, window: int, softmax_scale: float = 0.0,
+                       stream=None) -> int:
+    """q [B, T, Hq, D], k/v [B, T, Hkv, D] bf16; gate_logits [B, Hkv, T] f32; out like q; lse [B, Hq, T] f32."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError("k and v must be [B, T, Hkv, D] like q")
+    return _check(lib().dms_train_attn_fwd(
+        B, T, Hq, Hkv, D, window, ctypes.c_float(softmax_scale), _ptr(q, "q", torch.bfloat16),
+        _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
+        _ptr(gate_logits, "gate_logits", torch.float32, B * Hkv * T), _ptr(out, "out", torch.bfloat16, q.numel()),
+        _ptr(lse, "lse", torch.float32, B * Hq * T), _stream(stream)))
 
 
 def dms_decode_attn(cache: DmsCache, seq_ids, q, out, B: int, stream=None) -> int:

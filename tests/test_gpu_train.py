@@ -1,0 +1,129 @@
+"""Training-mode forward (dms_train_gate, dms_train_attn_fwd) against the CPU
+oracle (needs an MI355X).
+
+Seeded bf16 Q/K/V (N(0, 1) rounded to bf16, the bits both sides use) and
+float32 gate logits.  Attention outputs within 2e-2 max / 2e-3 mean absolute
+error (bf16 inputs, bf16-rounded probabilities in P.V, fp32 accumulation);
+the log-sum-exp within 4e-3 absolute (its sum runs over the same bf16-rounded
+probabilities: at most 2^-9 relative).  Shapes: GQA 1/2/4, head_dim 64/128,
+ragged lengths (not multiples of the 32-key block or the token tiles),
+windows shorter than, equal to and longer than a block, penalties of both
+signs and the two extremes (nothing evicted, everything evicted).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dms_train_oracle as tor
+from tests.harness import from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = (2e-2, 2e-3)
+LSE_TOL = 4e-3
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _bf16(gen, shape):
+    from learned_kv_cache_amd import synth
+    return synth.as_dtype(gen.standard_normal(shape, dtype=np.float32), "bf16")
+
+
+def _run(torch, q, k, v, y, w):
+    from learned_kv_cache_amd import dms
+    B, T, Hq, D = q.shape
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    yd = to_dev(y, "f32")
+    out = torch.empty_like(qd)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device="cuda")
+    dms.dms_train_attn_fwd(qd, kd, vd, yd, out, lse, window=w)
+    torch.cuda.synchronize()
+    return from_dev(out), from_dev(lse)
+
+
+def _check(got_o, got_l, ref_o, ref_l, what):
+    err = np.abs(got_o - ref_o)
+    lerr = np.abs(got_l - ref_l)
+    log(f"{what}: out err max {err.max():.2e} mean {err.mean():.2e}; lse err max {lerr.max():.2e}")
+    assert err.max() <= OUT_TOL[0] and err.mean() <= OUT_TOL[1], (what, err.max(), err.mean())
+    assert lerr.max() <= LSE_TOL, (what, lerr.max())
+
+
+# (Hq, Hkv, D, T, window)
+SHAPES = [
+    (8, 2, 128, 333, 48),
+    (8, 4, 64, 1000, 200),
+    (4, 4, 128, 700, 32),
+    (8, 2, 64, 97, 512),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"hq{s[0]}_hkv{s[1]}_d{s[2]}_t{s[3]}_w{s[4]}" for s in SHAPES])
+def test_train_attn_fwd_shapes(shape):
+    torch = _torch()
+    Hq, Hkv, D, T, w = shape
+    gen = np.random.default_rng(SHAPES.index(shape) + 700)
+    B = 2
+    q, k, v = _bf16(gen, (B, T, Hq, D)), _bf16(gen, (B, T, Hkv, D)), _bf16(gen, (B, T, Hkv, D))
+    y = gen.normal(0.0, 3.0, (B, Hkv, T)).astype(np.float32)
+    got_o, got_l = _run(torch, q, k, v, y, w)
+    ref_o, ref_l = tor.train_attention(q, k, v, y, w)
+    _check(got_o, got_l, ref_o, ref_l, f"shape {shape}")
+
+
+@pytest.mark.parametrize("gate", [-40.0, 40.0])
+def test_train_attn_fwd_extremes(gate):
+    torch = _torch()
+    Hq, Hkv, D, T, w = 8, 2, 128, 300, 64
+    gen = np.random.default_rng(800)
+    B = 1
+    q, k, v = _bf16(gen, (B, T, Hq, D)), _bf16(gen, (B, T, Hkv, D)), _bf16(gen, (B, T, Hkv, D))
+    y = np.full((B, Hkv, T), gate, dtype=np.float32)
+    got_o, got_l = _run(torch, q, k, v, y, w)
+    ref_o, ref_l = tor.train_attention(q, k, v, y, w)
+    _check(got_o, got_l, ref_o, ref_l, f"gate {gate}")
+
+
+def test_train_attn_fwd_qwen8b_4k_sampled_rows():
+    """Qwen3-8B layer shape, T 4096, window 512: 48 sampled query rows per
+    sequence (the last 16 among them) against the oracle."""
+    torch = _torch()
+    Hq, Hkv, D, T, w = 32, 8, 128, 4096, 512
+    gen = np.random.default_rng(801)
+    B = 2
+    q, k, v = _bf16(gen, (B, T, Hq, D)), _bf16(gen, (B, T, Hkv, D)), _bf16(gen, (B, T, Hkv, D))
+    y = gen.normal(0.0, 3.0, (B, Hkv, T)).astype(np.float32)
+    got_o, got_l = _run(torch, q, k, v, y, w)
+    rows = np.unique(np.concatenate([gen.choice(T - 16, 32, replace=False), np.arange(T - 16, T)]))
+    ref_o, ref_l = tor.train_attention(q, k, v, y, w, rows=rows)
+    _check(got_o[:, rows], got_l[:, :, rows], ref_o, ref_l, "qwen8b T4096")
+
+
+def test_train_gate():
+    torch = _torch()
+    from learned_kv_cache_amd import dms
+    gen = np.random.default_rng(802)
+    n = 100_003
+    logits = gen.normal(0.0, 3.0, n).astype(np.float32)
+    noise = gen.logistic(0.0, 1.0, n).astype(np.float32)
+    tau = 0.1
+    ld, nd = to_dev(logits, "f32"), to_dev(noise, "f32")
+    y, p, h = (torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3))
+    dms.dms_train_gate(ld, nd, tau, y, p, h)
+    ry, rp, rh = tor.train_gate(logits.astype(np.float64), noise.astype(np.float64), tau)
+    gy, gp, gh = from_dev(y), from_dev(p), from_dev(h)
+    np.testing.assert_allclose(gy, ry, rtol=2e-6, atol=1e-6)
+    np.testing.assert_allclose(gp, rp, rtol=0, atol=2e-6)
+    clear = np.abs(ry) > 1e-4                      # the decision is not a rounding question
+    assert clear.mean() > 0.999
+    assert np.array_equal(gh[clear], rh[clear])
+    # no noise, tau 1: y equals the logits bit for bit
+    dms.dms_train_gate(ld, None, 1.0, y, None, None)
+    assert np.array_equal(from_dev(y), logits.astype(np.float64))
