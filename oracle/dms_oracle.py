@@ -438,6 +438,23 @@ class CacheSim:
         }
 
 
+def pages_needed_worst(sim: "CacheSim", b: int, n: int) -> int:
+    """Pool pages that appending n more tokens to sequence b takes when every
+    new token is kept (the most any decisions can take: a marked new token can
+    only save a slot later).  FastDMS post, subsystem table: admission by
+    compact KV capacity.  Simulated on a copy of the cache model; -1 when the
+    sequence would pass its capacity."""
+    import copy
+    if sim.pos[b] + n > sim.max_tokens:
+        return -1
+    trial = copy.deepcopy(sim)
+    trial.free = list(range(10 ** 9, 10 ** 9 - n * sim.Hkv - 1, -1))   # never runs dry
+    before = sum(len(trial.pages[b][k]) for k in range(sim.Hkv))
+    if n:
+        trial.append([b], np.zeros((1, sim.Hkv, n), dtype=np.uint8))
+    return sum(len(trial.pages[b][k]) for k in range(sim.Hkv)) - before
+
+
 def length_closed_form(e_row: np.ndarray, t: int, w: int) -> int:
     """Live slots of one head after token t: (t+1) - #{j <= t-w : e_j = 1}.
 

@@ -316,3 +316,59 @@ def test_fp8_page_scales_in_sim():
             assert (sk, sv) == sim.page_scale[page]
             kk = oracle.effective_kv(sim, 0, kh, k[0, :, kh], 0)[t]
             assert np.array_equal(oracle.fp8_roundtrip(kk, sk), kk)
+
+
+# ---------------------------------------------------------------------------
+# serving accounting: worst-case pages of a continuation
+
+def _random_sim(seed, w=6, P=4, Hkv=2, T=37, p=0.5):
+    rng = np.random.default_rng(seed)
+    sim = oracle.CacheSim(2, Hkv, w, P, 200, 400)
+    for b in range(2):
+        e = (rng.random((1, Hkv, T + 5 * b)) < p).astype(np.uint8)
+        sim.append([b], e)
+    return sim, rng
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pages_needed_worst_bounds_every_decision_and_is_reached(seed):
+    import copy
+    sim, rng = _random_sim(seed)
+    for b in range(2):
+        for n in (0, 1, 3, 6, 7, 13, 40):
+            worst = oracle.pages_needed_worst(sim, b, n)
+            for trial in range(8):
+                e = (rng.random((1, sim.Hkv, n)) < rng.random()).astype(np.uint8) if trial else \
+                    np.zeros((1, sim.Hkv, n), np.uint8)
+                s2 = copy.deepcopy(sim)
+                before = len(s2.free)
+                if n:
+                    s2.append([b], e)
+                taken = before - len(s2.free)
+                assert taken <= worst
+                if trial == 0:
+                    assert taken == worst            # all kept reaches the bound
+
+
+def test_pages_needed_worst_closed_form_without_marks():
+    sim = oracle.CacheSim(1, 3, 5, 4, 100, 100)
+    sim.append([0], np.zeros((1, 3, 11), np.uint8))     # nothing marked: no overwrite to come
+    for n in (0, 1, 5, 9, 30):
+        assert oracle.pages_needed_worst(sim, 0, n) == 3 * (math.ceil((11 + n) / 4) - math.ceil(11 / 4))
+
+
+def test_pages_needed_worst_hand_case():
+    # w = 4, P = 2, one head: positions 0..5 with marks 1,0,1,1,0,0 (t=4, 5 overwrite 0's slot... ):
+    # t=4 overwrites slot(0) (marked), t=5 takes a new slot (1 not marked) -> L = 5 after 6 tokens.
+    sim = oracle.CacheSim(1, 1, 4, 2, 100, 100)
+    sim.append([0], np.array([[[1, 0, 1, 1, 0, 0]]], np.uint8))
+    assert sim.L[0][0] == 5
+    # next tokens t = 6, 7, 8, 9 look at 2, 3, 4, 5: marked, marked, kept, kept -> 2 new slots for n = 4
+    # L 5 -> 7 slots: pages ceil(7/2) - ceil(5/2) = 4 - 3 = 1
+    assert oracle.pages_needed_worst(sim, 0, 4) == 1
+    # n = 2: both overwrite -> no new slot
+    assert oracle.pages_needed_worst(sim, 0, 2) == 0
+    # n = 6: t = 10, 11 look at the new tokens 6, 7 (worst case kept) -> 4 new slots: ceil(9/2) - 3 = 2
+    assert oracle.pages_needed_worst(sim, 0, 6) == 2
+    # capacity
+    assert oracle.pages_needed_worst(sim, 0, 95) == -1
