@@ -296,6 +296,33 @@ int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out);
  * realised compression; here tokens / live slots). */
 int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out);
 
+/* ---- serving accounting (FastDMS post, subsystem table: the scheduler admits
+ * requests by compact KV capacity, continuous batching accounts surviving
+ * tokens rather than logical length; walkthrough, 当前限制: interleaved
+ * prefill / generate turns on one sequence need no reset here) ---- */
+
+typedef struct dms_seq_info {
+  int32_t position;         /* tokens appended so far (logical length) */
+  int32_t live_slots;       /* surviving tokens: sum over KV heads of live slots */
+  int32_t max_head_slots;   /* largest per-head length */
+  int32_t pages;            /* pool pages the sequence holds */
+} dms_seq_info;
+
+/* Synchronises `stream`; per listed sequence (seq_ids host array of n ids, or
+ * NULL for 0..n-1) fills out[i] (host).  DMS_ERR_ARG for an id outside
+ * [0, max_batch). */
+int dms_seq_info_get(dms_cache* cache, const int32_t* seq_ids, int n, void* stream, dms_seq_info* out);
+
+/* Synchronises `stream`; the most pool pages that appending n_new[i] more
+ * tokens to sequence seq_ids[i] can take, whatever the new tokens' decisions:
+ * every new token is taken as kept, except that the first w of them
+ * overwrite in place the slots of already-marked tokens in the window
+ * (walkthrough, 推理模式).  pages_out[i] = -1 when the sequence would pass
+ * max_tokens_per_seq.  *free_pages (may be NULL) = pages left in the pool.
+ * Host arrays; admit when the sum of pages_out fits in *free_pages. */
+int dms_pages_needed(dms_cache* cache, const int32_t* seq_ids, const int32_t* n_new, int n, void* stream,
+                     int64_t* pages_out, int64_t* free_pages);
+
 /* Last error message of this thread ("" if none). */
 const char* dms_last_error(void);
 

@@ -391,4 +391,80 @@ int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out) {
   return DMS_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Serving accounting (FastDMS post, subsystem table: admission by compact KV
+// capacity, continuous-batching memory accounting by surviving tokens).
+
+int dms_seq_info_get(dms_cache* cache, const int32_t* seq_ids, int n, void* stream, dms_seq_info* out) {
+  if (!cache || !out || n < 0) return fail(DMS_ERR_ARG, "NULL argument or negative n");
+  const Geo& g = cache->geo;
+  std::vector<int32_t> len(static_cast<size_t>(g.Bmax) * g.Hkv), pos(g.Bmax);
+  dms_dump d;
+  std::memset(&d, 0, sizeof(d));
+  d.lengths = len.data();
+  d.positions = pos.data();
+  int s = dms_cache_dump(cache, stream, &d);
+  if (s) return s;
+  for (int i = 0; i < n; ++i) {
+    const int seq = seq_ids ? seq_ids[i] : i;
+    if (seq < 0 || seq >= g.Bmax) return fail(DMS_ERR_ARG, "sequence id outside [0, max_batch)");
+    dms_seq_info r{};
+    r.position = pos[seq];
+    for (int k = 0; k < g.Hkv; ++k) {
+      const int32_t L = len[static_cast<size_t>(seq) * g.Hkv + k];
+      r.live_slots += L;
+      r.max_head_slots = std::max(r.max_head_slots, L);
+      r.pages += (L + g.P - 1) / g.P;
+    }
+    out[i] = r;
+  }
+  return DMS_OK;
+}
+
+int dms_pages_needed(dms_cache* cache, const int32_t* seq_ids, const int32_t* n_new, int n, void* stream,
+                     int64_t* pages_out, int64_t* free_pages) {
+  if (!cache || !n_new || !pages_out || n < 0) return fail(DMS_ERR_ARG, "NULL argument or negative n");
+  const Geo& g = cache->geo;
+  const size_t units = static_cast<size_t>(g.Bmax) * g.Hkv;
+  std::vector<int32_t> len(units), pos(g.Bmax), ring(units * g.w);
+  int32_t freec = 0;
+  dms_dump d;
+  std::memset(&d, 0, sizeof(d));
+  d.lengths = len.data();
+  d.positions = pos.data();
+  d.ring = ring.data();
+  d.free_count = &freec;
+  int s = dms_cache_dump(cache, stream, &d);
+  if (s) return s;
+  for (int i = 0; i < n; ++i) {
+    const int seq = seq_ids ? seq_ids[i] : i;
+    if (seq < 0 || seq >= g.Bmax) return fail(DMS_ERR_ARG, "sequence id outside [0, max_batch)");
+    const int64_t m = n_new[i];
+    if (m < 0) return fail(DMS_ERR_ARG, "negative token count");
+    const int64_t t0 = pos[seq];
+    if (t0 + m > g.max_tokens) {
+      pages_out[i] = -1;   // beyond max_tokens_per_seq: the append would be refused
+      continue;
+    }
+    int64_t pages = 0;
+    for (int k = 0; k < g.Hkv; ++k) {
+      const size_t u = static_cast<size_t>(seq) * g.Hkv + k;
+      // new token t = t0 + j overwrites the slot of position t - w in place
+      // when that token was marked; for j < w that token is already in the
+      // ring (its mark is known), later ones are the new tokens (worst case:
+      // kept, so a new slot)
+      int64_t overwrites = 0;
+      for (int64_t j = 0; j < std::min<int64_t>(m, g.w); ++j) {
+        const int64_t p = t0 + j - g.w;
+        if (p >= 0 && ring[u * g.w + static_cast<size_t>(p % g.w)] < 0) ++overwrites;
+      }
+      const int64_t L = len[u], slots = L + (m - overwrites);
+      pages += (slots + g.P - 1) / g.P - (L + g.P - 1) / g.P;
+    }
+    pages_out[i] = pages;
+  }
+  if (free_pages) *free_pages = freec;
+  return DMS_OK;
+}
+
 }  // extern "C"

@@ -41,7 +41,7 @@ EXPORTS = (
     "dms_cache_destroy", "dms_cache_config", "dms_decide", "dms_append_evict", "dms_decode_attn",
     "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
-    "dms_train_gate", "dms_train_attn_fwd",
+    "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed",
 )
 
 
@@ -66,6 +66,11 @@ class dms_dump(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "lengths", "page_table", "slot_meta", "ring", "positions", "free_stack", "free_count",
         "k_pages", "v_pages", "page_scales")]
+
+
+class dms_seq_info(ctypes.Structure):
+    _fields_ = [("position", ctypes.c_int32), ("live_slots", ctypes.c_int32), ("max_head_slots", ctypes.c_int32),
+                ("pages", ctypes.c_int32)]
 
 
 class dms_stats(ctypes.Structure):
@@ -99,6 +104,8 @@ def lib():
             "dms_decode_prepare": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
             "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
             "dms_train_gate": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp],
+            "dms_seq_info_get": [vp, vp, i32, vp, ctypes.POINTER(dms_seq_info)],
+            "dms_pages_needed": [vp, vp, vp, i32, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
             "dms_train_attn_fwd": [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp],
             "dms_prefill_attn": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_seq_reset": [vp, vp, i32, vp],
@@ -285,6 +292,32 @@ def dms_train_attn_fwd(q, k, v, gate_logits, out, lse, *, window: int, softmax_s
         _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
         _ptr(gate_logits, "gate_logits", torch.float32, B * Hkv * T), _ptr(out, "out", torch.bfloat16, q.numel()),
         _ptr(lse, "lse", torch.float32, B * Hq * T), _stream(stream)))
+
+
+def _host_ids(seq_ids):
+    ids = (ctypes.c_int32 * len(seq_ids))(*[int(x) for x in seq_ids])
+    return ids
+
+
+def dms_seq_info_get(cache: DmsCache, seq_ids, stream=None):
+    """Per-sequence accounting (synchronises): list of dicts with position,
+    live_slots, max_head_slots, pages."""
+    n = len(seq_ids)
+    out = (dms_seq_info * n)()
+    _check(lib().dms_seq_info_get(cache.handle, _host_ids(seq_ids), n, _stream(stream), out))
+    return [{f: getattr(r, f) for f, _ in dms_seq_info._fields_} for r in out]
+
+
+def dms_pages_needed(cache: DmsCache, seq_ids, n_new, stream=None):
+    """Worst-case pool pages for appending n_new[i] tokens to seq_ids[i]
+    (synchronises).  Returns (pages list, free pages)."""
+    n = len(seq_ids)
+    pages = (ctypes.c_int64 * n)()
+    free = ctypes.c_int64(0)
+    counts = (ctypes.c_int32 * n)(*[int(x) for x in n_new])
+    _check(lib().dms_pages_needed(cache.handle, _host_ids(seq_ids), counts, n, _stream(stream), pages,
+                                  ctypes.byref(free)))
+    return list(pages), free.value
 
 
 def dms_decode_attn(cache: DmsCache, seq_ids, q, out, B: int, stream=None) -> int:
