@@ -159,7 +159,8 @@ def run_decode(args, dms, synth, torch):
         layers.append(L)
     torch.cuda.synchronize()
     for L in layers:
-        assert dms.dms_cache_status(L.cache) == 0
+        st = dms.dms_cache_status(L.cache)
+        assert st == 0, f"device status {st:#x}"
     log(f"{args.layers} layers filled with {wl.prefill} tokens x {wl.B} sequences in {time.time() - t0:.1f}s")
 
     graphs = []
@@ -192,7 +193,8 @@ def run_decode(args, dms, synth, torch):
     elapsed_ms = ev0.elapsed_time(ev1)
     live1 = [dms.dms_cache_stats(L.cache) for L in layers]
     for L in layers:
-        assert dms.dms_cache_status(L.cache) == 0
+        st = dms.dms_cache_status(L.cache)
+        assert st == 0, f"device status {st:#x}"
     ms_per_step = elapsed_ms / args.steps
     tok_s_layer = wl.B * args.steps * args.layers / (elapsed_ms / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {tok_s_layer / 1e6:.3f} M tok/s/layer")
