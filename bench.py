@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "DMS decode tok/s/layer + HBM GB/s vs peak, Qwen3-8B layer shape, ctx 8K, B=8"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
 
 
 def log(msg: str) -> None:
@@ -387,6 +388,56 @@ def run_train_fwd(args, dms, torch):
     }
 
 
+def run_kvzap(args, dms, torch):
+    """KVzap scorers at the KVzap-mlp page's Qwen3-8B shape (hidden 4096, inner
+    512, 8 KV heads) and the linear scorer (4096 -> 8), bf16 hidden states,
+    f32 weights: one 4096-token prefill chunk and one B = 8 decode step each,
+    timed with HIP events over repeated calls on the launch stream.  Work per
+    token: MLP 2 * 4096 * 512 + 2 * 512 * 8 flops; bytes: hidden 8 KB per
+    token, weights once per call (MLP 8 MB + 16 KB, linear 128 KB)."""
+    H, Hm, Hkv = 4096, 512, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(777)
+    W1 = torch.randn(Hm, H, generator=gen, device="cuda") / math.sqrt(H)
+    b1 = 0.1 * torch.randn(Hm, generator=gen, device="cuda")
+    W2 = torch.randn(Hkv, Hm, generator=gen, device="cuda") / math.sqrt(Hm)
+    b2 = torch.full((Hkv,), -4.0, device="cuda")
+    Wl = torch.randn(Hkv, H, generator=gen, device="cuda") / math.sqrt(H)
+    bl = torch.full((Hkv,), -4.0, device="cuda")
+    res = {"workload": "kvzap_qwen3-8b_h4096_inner512_kv8"}
+    for name, B, T in (("chunk4096", 1, 4096), ("decode_b8", 8, 1)):
+        h = torch.randn(B, T, H, generator=gen, device="cuda").to(torch.bfloat16)
+        ev = torch.empty(B * Hkv * T, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(B * Hkv * T, device="cuda")
+        ws = torch.empty(dms.dms_kvzap_workspace_bytes(B, T, Hkv, Hm), dtype=torch.uint8, device="cuda")
+        calls = {
+            "mlp": lambda: dms.dms_kvzap_score(h, W1, b1, ev, W2=W2, b2=b2, threshold=-4.0, scores_out=sc,
+                                               workspace=ws),
+            "linear": lambda: dms.dms_kvzap_score(h, Wl, bl, ev, threshold=-4.0, scores_out=sc),
+        }
+        for kind, fn in calls.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            reps = 50
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            N = B * T
+            flops = 2.0 * N * (H * Hm + Hm * Hkv) if kind == "mlp" else 2.0 * N * H * Hkv
+            wbytes = 4.0 * (Hm * H + Hkv * Hm) if kind == "mlp" else 4.0 * Hkv * H
+            nbytes = 2.0 * N * H + wbytes + 5.0 * N * Hkv
+            res[f"{kind}_{name}_us"] = us
+            res[f"{kind}_{name}_tflops"] = flops / (us * 1e-6) / 1e12
+            res[f"{kind}_{name}_gbs"] = nbytes / (us * 1e-6) / 1e9
+    res["mlp_chunk4096_frac_fp32_mfma_peak"] = res["mlp_chunk4096_tflops"] / FP32_PEAK_TFLOPS
+    return res
+
+
 def cpu_baseline(steps: int):
     """The CPU oracle (float64 NumPy) on a bounded sample of the same decode
     workload: one layer, B = 8, 8192-token prompt, `steps` decode steps of
@@ -491,6 +542,13 @@ def main() -> int:
         train = run_train_fwd(args, dms, torch)
         log(f"training forward: {train['attn_ms']:.3f} ms attention = {train['attn_tflops']:.1f} TFLOP/s, "
             f"gate {train['gate_ms'] * 1e3:.1f} us")
+    kvzap = None
+    if not args.no_prefill:
+        kvzap = run_kvzap(args, dms, torch)
+        log(f"kvzap: mlp chunk {kvzap['mlp_chunk4096_us']:.1f} us ({kvzap['mlp_chunk4096_tflops']:.1f} TFLOP/s), "
+            f"mlp decode {kvzap['mlp_decode_b8_us']:.1f} us ({kvzap['mlp_decode_b8_gbs']:.0f} GB/s), "
+            f"linear chunk {kvzap['linear_chunk4096_us']:.1f} us ({kvzap['linear_chunk4096_gbs']:.0f} GB/s), "
+            f"linear decode {kvzap['linear_decode_b8_us']:.1f} us")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -552,6 +610,7 @@ def main() -> int:
         "cache_cr": dec["cache_cr"],
         "prefill": pre,
         "train_fwd": train,
+        "kvzap": kvzap,
     }
     print(json.dumps(line), flush=True)
     if args.copy_calib:

@@ -296,6 +296,39 @@ int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out);
  * realised compression; here tokens / live slots). */
 int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out);
 
+/* ---- KVzap scorers ("动态内存稀疏化（DMS）策略：KVzap-linear-Llama-3.1-8B-Instruct的核心创新点",
+ * KVzap-linear的技术架构; "革命性LLM加速技术：NVIDIA KVzap-mlp-Qwen3-8B如何实现高效KV缓存修剪？",
+ * 模型架构 and 工作流程) ---- */
+
+/* Scores every token's KV pairs from the layer's hidden state and applies the
+ * pruning threshold, for B x T tokens:
+ *   linear (Hm == 0):  s[b][k][t] = W1[k] . h[b][t] + b1[k]
+ *   MLP    (Hm >  0):  s[b][k][t] = W2[k] . gelu(W1 . h[b][t] + b1) + b2[k]   (exact erf GELU)
+ *   evict[b][k][t] = s[b][k][t] < threshold   (the pages' default threshold is -4)
+ * The decisions feed dms_append_evict / dms_prefill_attn of a cache whose
+ * window is the pages' 128 tokens: a token with a score below the threshold
+ * leaves the cache once it is 128 positions old, the others stay.
+ *   hidden     device [B][T][H], float32 (act_dtype DMS_F32) or bfloat16 (DMS_BF16), 16-byte aligned
+ *   W1         device float32, linear [Hkv][H], MLP [Hm][H], 16-byte aligned
+ *   b1         device float32, linear [Hkv], MLP [Hm], or NULL (no bias)
+ *   W2, b2     device float32 [Hkv][Hm], [Hkv] (b2 may be NULL); MLP only, ignored for linear
+ *   scores_out device float32 [B][Hkv][T], or NULL
+ *   evict_out  device uint8 [B][Hkv][T]
+ *   workspace  MLP only: device memory of at least dms_kvzap_workspace_bytes(B, T, Hkv, Hm)
+ *              bytes, owned by the caller, overwritten (the inner-unit workgroups' shares of
+ *              the second layer, added in a fixed order: scores are deterministic); ignored
+ *              (may be NULL) for linear
+ * Limits: H a multiple of 32, 1 <= Hkv <= 16, Hm a multiple of 64
+ * (DMS_ERR_UNSUPPORTED otherwise).  Asynchronous on `stream`; needs no cache.
+ * DMS_ERR_ARG for NULL required pointers, negative sizes or a non-finite
+ * threshold; DMS_ERR_CAPACITY for a missing or short MLP workspace. */
+int dms_kvzap_score(int B, int T, int H, int Hkv, int Hm, int act_dtype, const void* hidden, const float* W1,
+                    const float* b1, const float* W2, const float* b2, float threshold, float* scores_out,
+                    uint8_t* evict_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dms_kvzap_score needs for B x T tokens (0 for Hm == 0). */
+int dms_kvzap_workspace_bytes(int B, int T, int Hkv, int Hm, size_t* bytes);
+
 /* ---- serving accounting (FastDMS post, subsystem table: the scheduler admits
  * requests by compact KV capacity, continuous batching accounts surviving
  * tokens rather than logical length; walkthrough, 当前限制: interleaved

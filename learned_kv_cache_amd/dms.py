@@ -41,7 +41,8 @@ EXPORTS = (
     "dms_cache_destroy", "dms_cache_config", "dms_decide", "dms_append_evict", "dms_decode_attn",
     "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
-    "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed",
+    "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed", "dms_kvzap_score",
+    "dms_kvzap_workspace_bytes",
 )
 
 
@@ -107,6 +108,9 @@ def lib():
             "dms_seq_info_get": [vp, vp, i32, vp, ctypes.POINTER(dms_seq_info)],
             "dms_pages_needed": [vp, vp, vp, i32, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
             "dms_train_attn_fwd": [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp],
+            "dms_kvzap_score": [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                ctypes.c_size_t, vp],
+            "dms_kvzap_workspace_bytes": [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)],
             "dms_prefill_attn": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_seq_reset": [vp, vp, i32, vp],
             "dms_cache_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
@@ -292,6 +296,44 @@ def dms_train_attn_fwd(q, k, v, gate_logits, out, lse, *, window: int, softmax_s
         _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
         _ptr(gate_logits, "gate_logits", torch.float32, B * Hkv * T), _ptr(out, "out", torch.bfloat16, q.numel()),
         _ptr(lse, "lse", torch.float32, B * Hq * T), _stream(stream)))
+
+
+def dms_kvzap_workspace_bytes(B: int, T: int, Hkv: int, Hm: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().dms_kvzap_workspace_bytes(B, T, Hkv, Hm, ctypes.byref(n)))
+    return n.value
+
+
+def dms_kvzap_score(hidden, W1, b1, evict_out, *, W2=None, b2=None, threshold: float = -4.0, scores_out=None,
+                    workspace=None, stream=None) -> int:
+    """KVzap scores and decisions.  hidden [B, T, H] f32 or bf16; linear: W1 [Hkv, H],
+    b1 [Hkv] or None; MLP (W2 given): W1 [Hm, H], b1 [Hm] or None, W2 [Hkv, Hm],
+    b2 [Hkv] or None.  evict_out uint8 and scores_out f32 (optional) are [B, Hkv, T].
+    The MLP needs a device workspace of dms_kvzap_workspace_bytes bytes (a uint8
+    tensor; allocated here when not given)."""
+    B, T, H = hidden.shape
+    if hidden.dtype == torch.float32:
+        act = DMS_F32
+    elif hidden.dtype == torch.bfloat16:
+        act = DMS_BF16
+    else:
+        raise ValueError("hidden must be float32 or bfloat16")
+    mlp = W2 is not None
+    Hkv = W2.shape[0] if mlp else W1.shape[0]
+    Hm = W1.shape[0] if mlp else 0
+    if W1.shape[1] != H or (mlp and W2.shape[1] != Hm):
+        raise ValueError("weight shapes do not match the hidden size")
+    n = B * Hkv * T
+    ws_bytes = dms_kvzap_workspace_bytes(B, T, Hkv, Hm)
+    if mlp and workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=hidden.device)
+    ws_ptr = _ptr(workspace, "workspace") if mlp else None
+    ws_len = workspace.numel() * workspace.element_size() if (mlp and workspace is not None) else 0
+    return _check(lib().dms_kvzap_score(
+        B, T, H, Hkv, Hm, act, _ptr(hidden, "hidden"), _ptr(W1, "W1", torch.float32, W1.shape[0] * H),
+        _ptr(b1, "b1", torch.float32, W1.shape[0]), _ptr(W2, "W2", torch.float32, Hkv * Hm if mlp else None),
+        _ptr(b2, "b2", torch.float32, Hkv), ctypes.c_float(threshold), _ptr(scores_out, "scores_out", torch.float32, n),
+        _ptr(evict_out, "evict_out", torch.uint8, n), ws_ptr, ctypes.c_size_t(ws_len), _stream(stream)))
 
 
 def _host_ids(seq_ids):
