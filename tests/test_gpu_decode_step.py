@@ -148,3 +148,34 @@ def test_step_bad_sequence_id():
     assert float(out[wl.Hq * wl.D:].float().abs().max()) == 0.0     # the bad row's heads have no keys
     dump = r.dms.dms_cache_dump(r.cache)
     assert int(dump["positions"][0]) == 2 and int(dump["positions"][1]) == 1
+
+
+def test_step_max_units():
+    """2048 (row, KV head) units, the most one call takes: 256 rows x 8 KV
+    heads, prompts of two lengths; the three decode paths in turn (the fused
+    step's commit then runs over eight batches of pairs, the attention's
+    prologue scans eight units per thread and splits the concatenated slots)."""
+    _cuda()
+    wl = synth.Workload(name="step_max_units", cfg_id=53, B=256, hidden=256, Hq=8, Hkv=8, D=64, act_dtype="bf16",
+                        kv_dtype="bf16", window=24, block=16, prefill=0, decode_steps=6, chunk=64,
+                        p_range=(0.40, 0.70), ctx_range=(20, 150), decide="linear", alpha_per="head")
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    ctx = prep.draw.ctx
+    seqs = list(range(wl.B))
+    # prompts through one chunk call per (start, length) group of rows
+    groups = {}
+    for b in seqs:
+        groups.setdefault(int(ctx[b]), []).append(b)
+    for n, rows in sorted(groups.items()):
+        s = 0
+        while s < n:
+            c = min(64, n - s)
+            r.prefill_chunk(rows, s, c, attend=False)
+            s += c
+    r.check_tables(pages=False)
+    for i in range(wl.decode_steps):
+        r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], step=i % 3 == 0, fused=i % 3 == 1)
+    r.check_tables(pages=True)
+    assert r.dms.dms_cache_status(r.cache) == 0
+    log(f"max units: stats {r.sim.stats()}")
