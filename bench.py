@@ -394,7 +394,8 @@ def run_kvzap(args, dms, torch):
     f32 weights: one 4096-token prefill chunk and one B = 8 decode step each,
     timed with HIP events over repeated calls on the launch stream.  Work per
     token: MLP 2 * 4096 * 512 + 2 * 512 * 8 flops; bytes: hidden 8 KB per
-    token, weights once per call (MLP 8 MB + 16 KB, linear 128 KB)."""
+    token, weights once per call (MLP 8 MB + 16 KB, linear 128 KB).  The calls
+    are replayed from a HIP graph (50 per replay): GPU time per call."""
     H, Hm, Hkv = 4096, 512, 8
     gen = torch.Generator(device="cuda")
     gen.manual_seed(777)
@@ -419,11 +420,17 @@ def run_kvzap(args, dms, torch):
             for _ in range(3):
                 fn()
             torch.cuda.synchronize()
+            # 50 calls captured in one graph, so that host launch costs stay out of the figure
             reps = 50
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    fn()
+            graph.replay()
+            torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(reps):
-                fn()
+            graph.replay()
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps

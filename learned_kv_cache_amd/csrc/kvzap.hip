@@ -90,6 +90,108 @@ __device__ __forceinline__ void reduce_scatter_step(float (&v)[64], int lane) {
 
 __device__ __forceinline__ void wave_reduce_scatter64(float (&v)[64], int lane) { reduce_scatter_step<64>(v, lane); }
 
+// The same for V <= 64 values (a power of two): afterwards every lane l
+// holds the wave sum of v[l % V] in v[0].
+template <int V, int C>
+__device__ __forceinline__ void reduce_scatter_v(float (&v)[V], int lane) {
+  if constexpr (C > 1) {
+    constexpr int H = C / 2;
+    const bool up = (lane & H) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float mine = up ? v[i + H] : v[i];
+      const float other = up ? v[i] : v[i + H];
+      v[i] = mine + __shfl_xor(other, H);
+    }
+    reduce_scatter_v<V, H>(v, lane);
+  }
+}
+template <int V>
+__device__ __forceinline__ void wave_sum_scatter(float (&v)[V], int lane) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "a power of two up to 64");
+  reduce_scatter_v<V, V>(v, lane);
+#pragma unroll
+  for (int o = V; o < 64; o <<= 1) v[0] += __shfl_xor(v[0], o);
+}
+
+template <typename ACT> __device__ __forceinline__ void load8(const ACT* p, float (&x)[8]) {
+  float a[4], b[4];
+  load4<ACT>(p, a);
+  load4<ACT>(p + 4, b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
+constexpr int kSmallThreads = 512;   // decode-size workgroups: 8 elements of H per thread and pass
+constexpr int kSmallTokens = 16;     // tokens per decode-size workgroup
+
+// Decode-size dot products: workgroup (x, y) takes R weight rows
+// [R x, R x + R) and tokens [16 y, 16 y + 16); thread t owns elements
+// [8t + 4096i, 8t + 4096i + 8) of H, all its loads of a pass issued
+// together (one round of loads per 4096 elements).  Returns, in lanes of
+// wave 0 ... (through LDS), the R x 16 sums.
+template <typename ACT, int R>
+__device__ __forceinline__ void small_dots(const KzArgs& a, const float* W, int nrows, int r0, int n0,
+                                           float (&s_red)[8][R * kSmallTokens]) {
+  constexpr int NT = kSmallTokens;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float acc[R * NT];
+#pragma unroll
+  for (int i = 0; i < R * NT; ++i) acc[i] = 0.0f;
+  for (int m = 8 * tid; m < a.H; m += 8 * kSmallThreads) {
+    float w[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r0 + r < nrows) {
+        load8<float>(W + static_cast<size_t>(r0 + r) * a.H + m, w[r]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[r][e] = 0.0f;
+      }
+    }
+    float x[NT][8];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n0 + n < a.N) {
+        load8<ACT>(static_cast<const ACT*>(a.hidden) + static_cast<size_t>(n0 + n) * a.H + m, x[n]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[n][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r * NT + n] = fmaf(w[r][e], x[n][e], acc[r * NT + n]);
+  }
+  wave_sum_scatter<R * NT>(acc, lane);
+  if (lane < R * NT) s_red[wave][lane] = acc[0];
+  __syncthreads();
+}
+
+// Linear scorer, up to 64 tokens: workgroup (k, y) takes head k and tokens [16 y, 16 y + 16).
+template <typename ACT>
+__global__ __launch_bounds__(kSmallThreads) void kz_linear_small_kernel(KzArgs a) {
+  __shared__ float s_red[8][kSmallTokens];
+  const int k = blockIdx.x, n0 = blockIdx.y * kSmallTokens;
+  small_dots<ACT, 1>(a, a.W1, a.Hkv, k, n0, s_red);
+  const int tid = threadIdx.x;
+  if (tid < kSmallTokens && n0 + tid < a.N) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) s += s_red[w][tid];
+    if (a.b1) s += a.b1[k];
+    const size_t o = out_index(a, n0 + tid, k);
+    if (a.scores) a.scores[o] = s;
+    a.evict[o] = s < a.thr ? 1 : 0;
+  }
+}
+
 // Linear scorer: TT tokens per 256-thread workgroup; thread t owns elements
 // [4t + 1024i, 4t + 1024i + 4) and keeps its W values in registers for the
 // TT tokens; waves reduce with shuffles, the four waves through LDS.
@@ -186,51 +288,27 @@ __global__ __launch_bounds__(256) void kz_finalize_wave_kernel(KzArgs a) {
   if (lane == 0) kz_store(a, i, s);
 }
 
-constexpr int kGemvTokens = 16;   // at most this many tokens on the decode-size path
+constexpr int kGemvTokens = 16;   // at most this many tokens on the MLP's decode-size path
 constexpr int kGemvUnits = 4;     // inner units per workgroup
 
-// MLP, N <= 16 tokens: workgroup blockIdx.x owns inner units
-// [4 blockIdx.x, 4 blockIdx.x + 4); thread t owns elements [4t + 1024i, +4)
-// of H for every token; W1 is read once over the grid.
+// MLP, N <= 16 tokens: workgroup x owns inner units [4x, 4x + 4) for all
+// tokens (one round of loads: W1 is read once over the grid), then writes
+// its share of the second layer.
 template <typename ACT>
-__global__ __launch_bounds__(256) void kz_mlp_gemv_kernel(KzArgs a) {
-  constexpr int NT = kGemvTokens, HP = kGemvUnits;
-  __shared__ float s_red[4][NT * HP];
+__global__ __launch_bounds__(kSmallThreads) void kz_mlp_gemv_kernel(KzArgs a) {
+  constexpr int NT = kSmallTokens, HP = kGemvUnits;
+  __shared__ float s_red[8][HP * NT];
   __shared__ float s_act[NT][HP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int u0 = blockIdx.x * HP;
-  float acc[NT * HP];
-#pragma unroll
-  for (int i = 0; i < NT * HP; ++i) acc[i] = 0.0f;
-  for (int m = 4 * tid; m < a.H; m += 1024) {
-    float4 w[HP];
-#pragma unroll
-    for (int j = 0; j < HP; ++j)
-      w[j] = u0 + j < a.Hm ? *reinterpret_cast<const float4*>(a.W1 + static_cast<size_t>(u0 + j) * a.H + m)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (n < a.N) load4<ACT>(static_cast<const ACT*>(a.hidden) + static_cast<size_t>(n) * a.H + m, x);
-#pragma unroll
-      for (int j = 0; j < HP; ++j) {
-        float& c = acc[n * HP + j];
-        c = fmaf(w[j].x, x[0], c);
-        c = fmaf(w[j].y, x[1], c);
-        c = fmaf(w[j].z, x[2], c);
-        c = fmaf(w[j].w, x[3], c);
-      }
-    }
-  }
-  static_assert(NT * HP == 64, "one value per lane after the reduce-scatter");
-  wave_reduce_scatter64(acc, lane);
-  s_red[wave][lane] = acc[0];
-  __syncthreads();
+  small_dots<ACT, HP>(a, a.W1, a.Hm, u0, 0, s_red);
   if (tid < NT * HP) {
-    const int n = tid / HP, j = tid % HP;
+    const int j = tid / NT, n = tid % NT;          // value index r * NT + n
     float act = 0.0f;
     if (n < a.N && u0 + j < a.Hm) {
-      float z = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+      float z = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) z += s_red[w][tid];
       if (a.b1) z += a.b1[u0 + j];
       act = gelu_erf(z);
     }
@@ -353,9 +431,9 @@ __global__ __launch_bounds__(256) void kz_mlp_mfma_kernel(KzArgs a) {
 template <typename ACT>
 int launch_kvzap(const KzArgs& a, hipStream_t st) {
   if (a.Hm == 0) {
-    if (a.N <= 64) {
-      if (a.Hkv <= 8) hipLaunchKernelGGL((kz_linear_kernel<ACT, 8, 1>), dim3(a.N), dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((kz_linear_kernel<ACT, 16, 1>), dim3(a.N), dim3(256), 0, st, a);
+    if (a.N <= 4 * kSmallTokens) {
+      hipLaunchKernelGGL((kz_linear_small_kernel<ACT>), dim3(a.Hkv, (a.N + kSmallTokens - 1) / kSmallTokens),
+                         dim3(kSmallThreads), 0, st, a);
     } else {
       if (a.Hkv <= 8) hipLaunchKernelGGL((kz_linear_kernel<ACT, 8, 8>), dim3((a.N + 7) / 8), dim3(256), 0, st, a);
       else hipLaunchKernelGGL((kz_linear_kernel<ACT, 16, 4>), dim3((a.N + 3) / 4), dim3(256), 0, st, a);
@@ -364,7 +442,7 @@ int launch_kvzap(const KzArgs& a, hipStream_t st) {
   }
   const int64_t total = static_cast<int64_t>(a.N) * a.Hkv;
   if (a.N <= kGemvTokens) {
-    hipLaunchKernelGGL((kz_mlp_gemv_kernel<ACT>), dim3(a.parts), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((kz_mlp_gemv_kernel<ACT>), dim3(a.parts), dim3(kSmallThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((kz_mlp_mfma_kernel<ACT>), dim3((a.N + kMfTok - 1) / kMfTok, a.parts), dim3(256), 0, st, a);
   }
