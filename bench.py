@@ -530,8 +530,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the DMS decode path has no multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the DMS decode path is timed on a single GPU", file=sys.stderr)
         return 2
     import torch
     from learned_kv_cache_amd import dms, synth
