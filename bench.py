@@ -67,7 +67,8 @@ class Layer:
         self.cache = dms.DmsCache(cfg)
         self.W = (torch.randn(Hkv, H, generator=gen, device="cuda") / math.sqrt(H)).contiguous()
         self.gamma = torch.ones(H, device="cuda")
-        self.p_h = 0.85 + 0.07 * torch.rand(Hkv, generator=gen, device="cuda")
+        lo, hi = wl.p_range
+        self.p_h = lo + (hi - lo) * torch.rand(Hkv, generator=gen, device="cuda")
         self.seed = 1_000_003 * (idx + 1)
         S = steps_total
         self.h_dec = torch.randn(S, B, H, generator=gen, device="cuda").to(torch.bfloat16)
@@ -122,6 +123,46 @@ def calibrate_and_fill(layer, wl, dms, torch):
         dms.dms_append_evict(layer.cache, None, k, v, ev, B, C)
 
 
+def calibrate_and_fill_ragged(layer, wl, ctx, dms, torch):
+    """As calibrate_and_fill, for prompts of per-sequence lengths ctx[b]:
+    each sequence's prompt goes in alone, in chunks of up to 4096 tokens
+    (each chunk's rows drawn from its own seed)."""
+    Hkv, C, H = wl.Hkv, wl.chunk, wl.hidden
+    zero = torch.zeros(Hkv, device="cuda")
+
+    def chunk(b, c0, n):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(layer.seed + 17 * c0 + 7919 * (b + 1))
+        h = torch.randn(1, n, H, generator=g, device="cuda").to(torch.bfloat16)
+        k = torch.randn(1, n, Hkv, wl.D, generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn(1, n, Hkv, wl.D, generator=g, device="cuda").to(torch.bfloat16)
+        return h, k, v
+
+    spans = [(b, c0, min(C, int(ctx[b]) - c0)) for b in range(wl.B) for c0 in range(0, int(ctx[b]), C)]
+    ev = torch.empty(Hkv * C, dtype=torch.uint8, device="cuda")
+    logits = []
+    for b, c0, n in spans:
+        h, _, _ = chunk(b, c0, n)
+        lg = torch.empty(1, Hkv, n, device="cuda")
+        dms.dms_decide(layer.cache, h, layer.gamma, layer.W, None, zero, None, 1, n, lg, ev[: Hkv * n])
+        logits.append(lg[0])
+    S = layer.h_dec.shape[0]
+    lg = torch.empty(S * wl.B, Hkv, 1, device="cuda")
+    evd = torch.empty(S * wl.B * Hkv, dtype=torch.uint8, device="cuda")
+    dms.dms_decide(layer.cache, layer.h_dec, layer.gamma, layer.W, None, zero, None, S * wl.B, 1, lg, evd)
+    logits.append(lg.permute(1, 0, 2).reshape(Hkv, -1))
+    allv = torch.cat(logits, dim=1)
+    srt, _ = torch.sort(allv, dim=1)
+    n_all = srt.shape[1]
+    kept = torch.round((1.0 - layer.p_h) * n_all).long().clamp(1, n_all - 1)
+    layer.off.copy_(0.5 * (srt.gather(1, (kept - 1)[:, None])[:, 0] + srt.gather(1, kept[:, None])[:, 0]))
+    for b, c0, n in spans:
+        h, k, v = chunk(b, c0, n)
+        seq = torch.tensor([b], dtype=torch.int32, device="cuda")
+        dms.dms_decide(layer.cache, h, layer.gamma, layer.W, None, layer.off, None, 1, n, None, ev[: Hkv * n])
+        dms.dms_append_evict(layer.cache, seq, k, v, ev[: Hkv * n], 1, n)
+
+
 def decode_step(layers, s, wl, dms, path="step"):
     B = wl.B
     for L in layers:
@@ -164,12 +205,19 @@ def run_decode(args, dms, synth, torch):
         assert st == 0, f"device status {st:#x}"
     log(f"{args.layers} layers filled with {wl.prefill} tokens x {wl.B} sequences in {time.time() - t0:.1f}s")
 
+    return time_decode(layers, wl, dms, torch, S, args.warmup, args.steps, args.path, args.attn_reps, args.eager)
+
+
+def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager=False):
+    """Replays `steps` timed decode steps (after `warmup`) over the layer
+    caches from one captured graph per step, then the attention alone; HIP
+    events on the launch stream; figures per layer step."""
     graphs = []
-    if not args.eager:
+    if not eager:
         for s in range(S):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                decode_step(layers, s, wl, dms, args.path)
+                decode_step(layers, s, wl, dms, path)
             graphs.append(g)
         torch.cuda.synchronize()
         log(f"captured {S} step graphs")
@@ -178,16 +226,16 @@ def run_decode(args, dms, synth, torch):
         if graphs:
             graphs[s].replay()
         else:
-            decode_step(layers, s, wl, dms, args.path)
+            decode_step(layers, s, wl, dms, path)
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
     live0 = [dms.dms_cache_stats(L.cache) for L in layers]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for s in range(args.warmup, S):
+    for s in range(warmup, S):
         step(s)
     ev1.record()
     torch.cuda.synchronize()
@@ -196,15 +244,15 @@ def run_decode(args, dms, synth, torch):
     for L in layers:
         st = dms.dms_cache_status(L.cache)
         assert st == 0, f"device status {st:#x}"
-    ms_per_step = elapsed_ms / args.steps
-    tok_s_layer = wl.B * args.steps * args.layers / (elapsed_ms / 1e3)
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {tok_s_layer / 1e6:.3f} M tok/s/layer")
+    ms_per_step = elapsed_ms / steps
+    tok_s_layer = wl.B * steps * len(layers) / (elapsed_ms / 1e3)
+    log(f"{wl.name}: timed {steps} steps: {ms_per_step:.3f} ms/step, {tok_s_layer / 1e6:.3f} M tok/s/layer")
 
     # Decode attention alone (context for the two-call paths): one graph
     # holding the dms_decode_attn calls of all layers (the cache state does not
     # change), replayed; HIP events on the launch stream around the replays;
     # average per call.
-    reps = args.attn_reps
+    reps = attn_reps
     ga = torch.cuda.CUDAGraph()
     with torch.cuda.graph(ga):
         for L in layers:
@@ -219,12 +267,14 @@ def run_decode(args, dms, synth, torch):
     torch.cuda.synchronize()
     attn_us = a0.elapsed_time(a1) * 1e3 / (reps * len(layers))
 
-    row_bytes = wl.D * 2
+    elem = 1 if wl.kv_dtype == "fp8" else 2
+    row_bytes = wl.D * elem
     kv_live = float(np.mean([s["bytes_live"] for s in live1]))          # K+V bytes the attention reads
     kv_live_mid = float(np.mean([(a["bytes_live"] + b["bytes_live"]) / 2 for a, b in zip(live0, live1)]))
     qo_bytes = 2 * wl.B * wl.Hq * wl.D * 2
     pages = float(np.mean([s["pages_in_use"] for s in live1]))
-    attn_bytes = kv_live + qo_bytes + pages * 4
+    scale_bytes = pages * 8 if wl.kv_dtype == "fp8" else 0.0
+    attn_bytes = kv_live + qo_bytes + pages * 4 + scale_bytes
     attn_gbs = attn_bytes / (attn_us * 1e-6) / 1e9
     mean_L = kv_live / (wl.B * wl.Hkv * 2 * row_bytes)
     step_bytes = kv_live_mid + qo_bytes
@@ -234,7 +284,7 @@ def run_decode(args, dms, synth, torch):
     pages_mid = float(np.mean([(a["pages_in_use"] + b["pages_in_use"]) / 2 for a, b in zip(live0, live1)]))
     launch_bytes = (kv_live_mid + qo_bytes + wl.B * wl.hidden * 2 + wl.Hkv * wl.hidden * 4 + wl.hidden * 4
                     + wl.B * wl.Hkv * 2 * row_bytes + pages_mid * 4)
-    layer_us = ms_per_step * 1e3 / args.layers
+    layer_us = ms_per_step * 1e3 / len(layers)
     stats = live1[0]
     return {
         "launch_bytes": launch_bytes,
@@ -245,14 +295,59 @@ def run_decode(args, dms, synth, torch):
         "attn_bytes": attn_bytes,
         "attn_gbs": attn_gbs,
         "mean_live_slots_per_head": mean_L,
-        "layer_step_us": ms_per_step * 1e3 / args.layers,
-        "step_kv_gbs": step_bytes * args.layers / (ms_per_step * 1e-3) / 1e9,
+        "layer_step_us": layer_us,
+        "step_kv_gbs": step_bytes * len(layers) / (ms_per_step * 1e-3) / 1e9,
         "kv_bytes_resident_per_layer": float(np.mean([s["bytes_allocated"] for s in live1])),
         "kv_bytes_live_per_layer": kv_live,
-        "dense_bf16_kv_bytes_per_layer": float(wl.B * wl.Hkv * (wl.prefill + S) * 2 * row_bytes),
+        "dense_bf16_kv_bytes_per_layer": float(wl.B * wl.Hkv * (wl.prefill + S) * 2 * wl.D * 2),
         "cache_cr": stats["cache_cr"],
         "graphs": bool(graphs),
     }
+
+
+def run_other_decode(dms, synth, torch, wl, n_layers, steps, warmup):
+    """A further decode configuration, reported beside the headline: wl's
+    layer shape and prompts (uniform, or per-sequence log-uniform lengths),
+    n_layers separate layer caches (enough to exceed the Infinity Cache),
+    the step path.  Returns the per-layer-step figures of time_decode."""
+    S = warmup + steps
+    if wl.ctx_range is None:
+        ctx = np.full(wl.B, wl.prefill)
+    else:
+        rng = np.random.default_rng(1000 + wl.cfg_id)
+        lo, hi = wl.ctx_range
+        ctx = np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), wl.B))).astype(np.int64)
+    max_tokens = int(ctx.max()) + S
+    pool_pages = int(sum(wl.Hkv * math.ceil((int(c) + S) / wl.block) for c in ctx))
+    cfg = dms.make_config(
+        max_batch=wl.B, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
+        window=wl.window, block_size=wl.block, max_tokens_per_seq=max_tokens, pool_pages=pool_pages,
+        max_chunk=wl.chunk, kv_dtype=wl.kv_dtype, decide_mode="linear", alpha_per="head")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + wl.cfg_id)
+    layers = []
+    t0 = time.time()
+    for i in range(n_layers):
+        L = Layer(i, cfg, wl, dms, torch, gen, S)
+        if wl.ctx_range is None:
+            calibrate_and_fill(L, wl, dms, torch)
+        else:
+            calibrate_and_fill_ragged(L, wl, ctx, dms, torch)
+        layers.append(L)
+    torch.cuda.synchronize()
+    for L in layers:
+        st = dms.dms_cache_status(L.cache)
+        assert st == 0, f"device status {st:#x}"
+    log(f"{wl.name}: {n_layers} layers filled (mean prompt {ctx.mean():.0f}) in {time.time() - t0:.1f}s")
+    r = time_decode(layers, wl, dms, torch, S, warmup, steps, "step", 10)
+    out = {"workload": wl.name, "layers": n_layers, "batch": wl.B, "kv_dtype": wl.kv_dtype,
+           "mean_prompt": float(ctx.mean()), "steps": steps}
+    out.update({k: r[k] for k in ("value", "layer_step_us", "attn_us", "attn_gbs", "attn_bytes",
+                                  "mean_live_slots_per_head", "kv_bytes_live_per_layer", "cache_cr")})
+    out["attn_frac_hbm_peak"] = r["attn_gbs"] / HBM_PEAK_GBS
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_prefill(args, dms, synth, torch, variant="qneuron"):
@@ -549,6 +644,16 @@ def main() -> int:
         train = run_train_fwd(args, dms, torch)
         log(f"training forward: {train['attn_ms']:.3f} ms attention = {train['attn_tflops']:.1f} TFLOP/s, "
             f"gate {train['gate_ms'] * 1e3:.1f} us")
+    others = None
+    if not args.no_prefill:
+        # Llama-3.2-1B has 16 layers; the fp8 serving figure rotates 4 layer caches
+        others = {
+            "llama1b_ctx8k_b1": run_other_decode(dms, synth, torch, synth.LLAMA1B_DECODE, 16, 64, 4),
+            "qwen8b_fp8kv_b64": run_other_decode(dms, synth, torch, synth.QWEN8B_FP8_SERVING, 4, 32, 4),
+        }
+        for k, r in others.items():
+            log(f"{k}: {r['layer_step_us']:.2f} us per layer step ({r['value'] / 1e6:.3f} M tok/s/layer), "
+                f"attention {r['attn_us']:.2f} us = {r['attn_gbs']:.0f} GB/s")
     kvzap = None
     if not args.no_prefill:
         kvzap = run_kvzap(args, dms, torch)
@@ -618,6 +723,7 @@ def main() -> int:
         "prefill": pre,
         "train_fwd": train,
         "kvzap": kvzap,
+        "other_decode": others,
     }
     print(json.dumps(line), flush=True)
     if args.copy_calib:

@@ -609,8 +609,9 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
 // Combines the partial records (m, l, o) of one unit's workgroups w0..w1 into
 // its bf16 output [G][D] (256 threads); the records are read with
 // device-scope atomic loads (written by workgroups on other XCDs).  The first workgroup's record is its
-// second segment when `odd`.  All loads of a batch of 8 records are issued
-// before any of them is used.
+// second segment when `odd`.  All loads of a batch of records (16, or 8
+// when a thread combines more than two outputs) are issued before any of
+// them is used.
 template <int D, int G>
 __device__ __forceinline__ void merge_unit_records(float* partials, int w0, int w1, int odd, uint16_t* out) {
   constexpr int PER = (G * D + 255) / 256;
@@ -622,10 +623,11 @@ __device__ __forceinline__ void merge_unit_records(float* partials, int w0, int 
     O[i] = 0.0f;
     L[i] = 0.0f;
   }
-  for (int b0 = 0; b0 < n; b0 += 8) {
-    float mv[8][PER], lv[8][PER], ov[8][PER];
+  constexpr int MB = PER <= 2 ? 16 : 8;   // records per batch of loads
+  for (int b0 = 0; b0 < n; b0 += MB) {
+    float mv[MB][PER], lv[MB][PER], ov[MB][PER];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < MB; ++j) {
       const int w = w0 + b0 + j;
       const int rec = (b0 + j == 0 && odd) ? 2 * w + 1 : 2 * w;
 #pragma unroll
@@ -648,13 +650,13 @@ __device__ __forceinline__ void merge_unit_records(float* partials, int w0, int 
     for (int i = 0; i < PER; ++i) {
       float mb = M[i];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mb = fmaxf(mb, mv[j][i]);
+      for (int j = 0; j < MB; ++j) mb = fmaxf(mb, mv[j][i]);
       if (mb == -INFINITY) continue;
       const float f0 = exp2f(M[i] - mb);
       O[i] *= f0;
       L[i] *= f0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < MB; ++j) {
         const float f = exp2f(mv[j][i] - mb);
         O[i] = fmaf(f, ov[j][i], O[i]);
         L[i] = fmaf(f, lv[j][i], L[i]);
@@ -682,6 +684,10 @@ struct StepArgs {
 // Up to this many units (and at most half as many as workgroups) each unit
 // gets whole workgroups of its own.
 constexpr int kAlignedUnits = 512;
+// ... at most this many: the merge of a unit's records then takes one batch
+// of loads (a few units with short contexts would otherwise spread over
+// dozens of workgroups whose merge costs more than their streaming saves).
+constexpr int kMaxSplit = 16;
 
 template <int G, int D, bool STEP>
 struct FastLds {
@@ -811,9 +817,9 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
   const int c = max((W + grid - 1) / grid, RPP);
   // Few units: each unit gets workgroups of its own, ceil(slots / ca) of
   // them for a cap of ca = ceil(W / (grid - units)) slots per workgroup (at
-  // most one per RPP rows), so no workgroup spans two units (a second
-  // segment would repeat the setup and the merge) and none holds more than
-  // ca slots; sum(ceil(slots / ca)) <= W / ca + units <= grid.  Otherwise the
+  // most one per RPP rows and kMaxSplit in all), so no workgroup spans two
+  // units (a second segment would repeat the setup and the merge);
+  // sum(ceil(slots / ca)) <= W / ca + units <= grid.  Otherwise the
   // concatenated slots are cut into equal ranges.
   const bool aligned = units <= kAlignedUnits && 2 * units <= grid;
   int* s_wstart = lds.wstart;
@@ -827,7 +833,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       int n = 0;
       if (u < units) {
         const int wu = s_start[u + 1] - s_start[u];
-        if (wu > 0) n = min((wu + ca - 1) / ca, max(1, wu / RPP));
+        if (wu > 0) n = min(min((wu + ca - 1) / ca, max(1, wu / RPP)), kMaxSplit);
       }
       nw[i] = n;
       sum += n;
