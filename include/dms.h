@@ -217,13 +217,17 @@ int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, voi
  * Arguments as in dms_decode_prepare; q_inout [B][Hq][D] is also the query of
  * the attention (QNEURON: its decision neuron is zeroed in place and plays no
  * part); out [B][Hq][D] act dtype.
- * bf16 pages (fast decode shapes, 16-byte aligned q_inout, k, v, out and,
- * LINEAR, hidden, rms_gamma, W with hidden a multiple of 8) run as one
- * launch: the workgroups that prepare a (row, KV head) pair run beside those
- * of the attention, which takes the current token from k/v and masks the
- * slot it overwrites; the last workgroup to finish its reads of the shared
- * tables commits the append.  Other configurations call dms_decode_prepare,
- * then dms_decode_attn.  Device-side errors as in dms_append_evict, and
+ * bf16 or fp8 pages (fast decode shapes, 16-byte aligned q_inout, k, v, out
+ * and, LINEAR, hidden, rms_gamma, W with hidden a multiple of 8) run as one
+ * launch when all of its workgroups (B * Hkv that prepare a (row, KV head)
+ * pair, plus the attention's) can be resident at once: the attention takes
+ * the current token from k/v (fp8: quantised with the scale its page has or
+ * gets, as the append stores it) and masks the slot it overwrites; the last
+ * preparing workgroup commits the append once every attention workgroup has
+ * read the shared tables.  Other configurations and larger steps call
+ * dms_decode_prepare, then dms_decode_attn (the environment variable
+ * DMS_DECODE_STEP_FUSE, read at cache creation, forces one (1) or two (0)
+ * launches).  Device-side errors as in dms_append_evict, and
  * DMS_DEV_STEP_SYNC if the commit's bounded wait for the attention
  * workgroups ran out (only when far more workgroups than the GPU holds at
  * once queue behind it).

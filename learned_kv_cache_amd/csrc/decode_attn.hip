@@ -434,7 +434,8 @@ struct KvChunk {
 // Issues the loads of passes [pass0, pass0 + NP) of a segment (rows at or
 // past `hi` load a stand-in row, masked by compute_chunk).
 // STEP: row `vrow` of the unit is the current token, read from the input rows
-// kin/vin (this lane's bytes) instead of a page.
+// kin/vin (this lane's bytes) instead of a page (fp8 pages: compute_chunk
+// substitutes its quantised codes).
 template <int D, int NP, bool FP8, int LPR, bool STEP = false>
 __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR / 16>& c, const uint8_t* __restrict__ kp,
                                            const uint8_t* __restrict__ vp, const float* __restrict__ scales, int pt_reg,
@@ -461,8 +462,13 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
     // (STEP: the input row) and is masked in the compute.  Loads under a
     // branch would make the compiler wait for this chunk's loads before
     // computing the previous one.
-    const int pg = ok ? (((r >> psh) == (rf >> psh)) ? pf : pl) : pg_lo;
-    const int rr = ok ? r : lo;
+    // (fp8: the current token's row and the rows past the end are
+    // substituted at compute time; the current token's page may not exist
+    // yet — a block can start at that row, leaving no live row and page id -1
+    // in pg_lo — so pool page 0 stands in for the address then)
+    const bool stand = !ok || (STEP && FP8 && r == vrow);
+    const int pg = stand ? ((STEP && FP8) ? max(pg_lo, 0) : pg_lo) : (((r >> psh) == (rf >> psh)) ? pf : pl);
+    const int rr = stand ? lo : r;
     if (FP8) {
       // issued with the rows (a load issued later would be waited for with them)
       c.sk[p] = scales[2 * pg];
@@ -471,7 +477,7 @@ __device__ __forceinline__ void load_chunk(KvChunk<NP, (D * (FP8 ? 1 : 2)) / LPR
     const uint32_t off = (static_cast<uint32_t>(pg) * static_cast<uint32_t>(pmask + 1) +
                           static_cast<uint32_t>(rr & pmask)) * static_cast<uint32_t>(RB) +
                          static_cast<uint32_t>(lane_col * BPL);
-    const bool cur = STEP && (r == vrow || !ok);
+    const bool cur = STEP && !FP8 && (r == vrow || !ok);
     const uint8_t* kb = cur ? kin : kp + off;
     const uint8_t* vb = cur ? vin : vp + off;
 #pragma unroll
@@ -494,7 +500,8 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
                                               const uint32_t (&qv)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2)) / 2],
                                               float (&m)[G], float (&l)[G],
                                               float (&o)[G][(D * (FP8 ? 1 : 2)) / LPR / 16 * (16 / (FP8 ? 1 : 2))],
-                                              int skip = -1) {
+                                              int skip = -1, int vrow = -1, const uint4* vk = nullptr,
+                                              const uint4* vv = nullptr, float vsk = 1.0f, float vsv = 1.0f) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int RB = D * EB;
   constexpr int BPL = RB / LPR;
@@ -505,15 +512,31 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
   constexpr int RPP = 4 * RG;
   bool ok[NP];
   float sk[NP], sv[NP];
+  // STEP with fp8 pages: the current token's row (row vrow) takes the codes
+  // and scales it will have once stored (vk, vv, vsk, vsv)
+  KvChunk<NP, NV> cc;
+  if constexpr (STEP && FP8) cc = c;
+  const KvChunk<NP, NV>& cu = (STEP && FP8) ? cc : c;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int r = lo + (pass0 + p) * RPP + wave * RG + lane_row;
     ok[p] = r < hi && (!STEP || r != skip);
+    if constexpr (STEP && FP8) {
+      // (rows past the end take the same codes: finite, and masked)
+      const bool vr = r == vrow || r >= hi;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        cc.k[p][j] = vr ? vk[j] : c.k[p][j];
+        cc.v[p][j] = vr ? vv[j] : c.v[p][j];
+      }
+      cc.sk[p] = vr ? vsk : c.sk[p];
+      cc.sv[p] = vr ? vsv : c.sv[p];
+    }
     sk[p] = scale_log2;
     sv[p] = 1.0f;
     if (FP8) {
-      sk[p] *= c.sk[p];
-      sv[p] = c.sv[p];
+      sk[p] *= cu.sk[p];
+      sv[p] = cu.sv[p];
     }
   }
   float s[NP][G];
@@ -522,7 +545,7 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
     uint32_t kw[QW];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const uint32_t raw[4] = {c.k[p][j].x, c.k[p][j].y, c.k[p][j].z, c.k[p][j].w};
+      const uint32_t raw[4] = {cu.k[p][j].x, cu.k[p][j].y, cu.k[p][j].z, cu.k[p][j].w};
       if (FP8) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) fp8x4_to_bf16(raw[t], kw[8 * j + 2 * t], kw[8 * j + 2 * t + 1]);
@@ -573,8 +596,8 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
     uint32_t va[QW], vb[QW];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const uint32_t ra[4] = {c.v[p][j].x, c.v[p][j].y, c.v[p][j].z, c.v[p][j].w};
-      const uint32_t rc[4] = {c.v[p + 1][j].x, c.v[p + 1][j].y, c.v[p + 1][j].z, c.v[p + 1][j].w};
+      const uint32_t ra[4] = {cu.v[p][j].x, cu.v[p][j].y, cu.v[p][j].z, cu.v[p][j].w};
+      const uint32_t rc[4] = {cu.v[p + 1][j].x, cu.v[p + 1][j].y, cu.v[p + 1][j].z, cu.v[p + 1][j].w};
       if (FP8) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -753,7 +776,6 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
   constexpr int NV = BPL / 16;
   static_assert(NP % 2 == 0, "passes are paired for the P.V dot products");
   static_assert(BPL % 16 == 0, "a lane loads whole 16-byte pieces");
-  static_assert(!STEP || !FP8, "the fused step reads bf16 input rows as cache rows");
 
   int* s_start = lds.start;
   int* s_tmp = lds.tmp;
@@ -906,9 +928,57 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
         vrow = uend - ustart - 1;
         skip = ext - 1;
       }
-      const size_t ro = (static_cast<size_t>(row) * g.Hkv + kh) * RB + lane_col * BPL;
+      // (the input rows are bf16: 2 bytes per element whatever the pages hold)
+      const size_t ro = (static_cast<size_t>(row) * g.Hkv + kh) * (D * 2) + lane_col * (BPL * 2 / EB);
       kin = sa->k + ro;
       vin = sa->v + ro;
+    }
+    // fp8 pages: the current token's codes and scales as the append stores
+    // them — in place or in the current page with that page's scales, in a
+    // new page with scales from the row's own largest magnitudes
+    uint4 vk[NV], vv[NV];
+    float vsk = 1.0f, vsv = 1.0f;
+    if constexpr (STEP && FP8) {
+      static_assert(NV == 1 && BPL == 16, "fp8 step: 16 codes (32 input bytes) per lane");
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        vk[j] = make_uint4(0, 0, 0, 0);
+        vv[j] = make_uint4(0, 0, 0, 0);
+      }
+      if (vrow >= 0) {
+        const uint4 k0 = *reinterpret_cast<const uint4*>(kin), k1 = *reinterpret_cast<const uint4*>(kin + 16);
+        const uint4 v0 = *reinterpret_cast<const uint4*>(vin), v1 = *reinterpret_cast<const uint4*>(vin + 16);
+        const float mk = piece_row_max(fmaxf(piece_amax(k0, true), piece_amax(k1, true)), LPR);
+        const float mv = piece_row_max(fmaxf(piece_amax(v0, true), piece_amax(v1, true)), LPR);
+        const int L = uend - ustart - 1;
+        if (skip < 0 && (L & pmask) == 0) {
+          vsk = page_scale_from_amax(mk);
+          vsv = page_scale_from_amax(mv);
+        } else {
+          const int page = skip >= 0 ? pt[skip >> psh] : d.cur_page[static_cast<int64_t>(seq) * g.Hkv + kh];
+          vsk = d.scales[2 * page];
+          vsv = d.scales[2 * page + 1];
+        }
+        const float ik = 1.0f / vsk, iv = 1.0f / vsv;
+        auto codes = [](const uint4& a, const uint4& b, float inv) {
+          const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          uint32_t out[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t bits = w[2 * q + (e >> 1)];
+              const float x = __uint_as_float((e & 1) ? (bits & 0xFFFF0000u) : (bits << 16));
+              word |= static_cast<uint32_t>(f32_to_e4m3(x * inv)) << (8 * e);
+            }
+            out[q] = word;
+          }
+          return make_uint4(out[0], out[1], out[2], out[3]);
+        };
+        vk[0] = codes(k0, k1, ik);
+        vv[0] = codes(v0, v1, iv);
+      }
     }
 
     uint32_t qv[G][QW];
@@ -956,7 +1026,8 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
                                           lane_row, lane_col, psh, pmask, vrow, kin, vin);
       };
       auto compute = [&](const KvChunk<NP, NV>& ch, int pass0) {
-        compute_chunk<D, G, NP, FP8, LPR, STEP>(ch, blo, pass0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o, skip);
+        compute_chunk<D, G, NP, FP8, LPR, STEP>(ch, blo, pass0, bhi, wave, lane_row, g.scale_log2, qv, m, l, o, skip,
+                                                vrow, vk, vv, vsk, vsv);
       };
       load(ca, 0);
       for (int p0 = 0; p0 < npass; p0 += 2 * NP) {
@@ -1065,12 +1136,13 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
 // (row, KV head) pair each (decision, placement, plan record); the others run
 // the attention (STEP).  The last pair to finish waits until every attention
 // workgroup has arrived (read the tables it works from), then commits.
-template <int D, int G, int NP, int LPR>
+template <int D, int G, int NP, bool FP8, int LPR>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
+  constexpr int KV = FP8 ? DMS_FP8_E4M3 : DMS_BF16;
   __shared__ FastLds<G, D, true> lds;
   if (static_cast<int>(blockIdx.x) < sa.npairs) {
     PrepShared& sh = lds.prep;
-    prep_pair<DMS_BF16>(ap, pin, blockIdx.x, true, sh);
+    prep_pair<KV>(ap, pin, blockIdx.x, true, sh);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
@@ -1104,12 +1176,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendAr
       if (threadIdx.x == 0) set_status(ap.d.ctl, DMS_DEV_STEP_SYNC);
       return;
     }
-    prep_commit<DMS_BF16>(ap, pin, sa.npairs, sh);
+    prep_commit<KV>(ap, pin, sa.npairs, sh);
     if (threadIdx.x < sa.groups)
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  decode_attn_fast_body<D, G, NP, false, LPR, true>(a, &sa, blockIdx.x - sa.npairs, sa.agrid, lds);
+  decode_attn_fast_body<D, G, NP, FP8, LPR, true>(a, &sa, blockIdx.x - sa.npairs, sa.agrid, lds);
 }
 
 template <int D, int G, bool FP8, int NP>
@@ -1178,30 +1250,34 @@ static int launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
   }
 }
 
+// The one-launch step kernel of a cache's shape: fp8 rows of D bytes take
+// 16 bytes (16 codes) per lane; bf16 rows 16 lanes per row of 128 (8 on request).
+using StepKernel = void (*)(DecodeArgs, AppendArgs, PrepIn, StepArgs);
+
 template <int D, int G>
-static void launch_step_dg(const DecodeArgs& a, const AppendArgs& ap, const PrepIn& pin, const StepArgs& sa, int grid,
-                           hipStream_t st) {
+static StepKernel step_kernel_dg(const Geo& g, int lanes_per_row) {
+  if (g.kv_dtype == DMS_FP8_E4M3) return decode_step_kernel<D, G, 2, true, D / 16>;
   constexpr int RB = D * 2;
   constexpr int LPR1 = RB / 16 >= 16 ? 16 : RB / 16;
   if constexpr (RB / 16 >= 16) {
-    if (a.lanes_per_row == 8) {
-      hipLaunchKernelGGL((decode_step_kernel<D, G, 2, 8>), dim3(grid), dim3(256), 0, st, a, ap, pin, sa);
-      return;
-    }
+    if (lanes_per_row == 8) return decode_step_kernel<D, G, 2, false, 8>;
   }
-  hipLaunchKernelGGL((decode_step_kernel<D, G, 2, LPR1>), dim3(grid), dim3(256), 0, st, a, ap, pin, sa);
+  return decode_step_kernel<D, G, 2, false, LPR1>;
 }
 
 template <int D>
-static int launch_step_d(const DecodeArgs& a, const AppendArgs& ap, const PrepIn& pin, const StepArgs& sa, int grid,
-                         hipStream_t st) {
-  switch (a.g.g) {
-    case 1: launch_step_dg<D, 1>(a, ap, pin, sa, grid, st); return DMS_OK;
-    case 2: launch_step_dg<D, 2>(a, ap, pin, sa, grid, st); return DMS_OK;
-    case 4: launch_step_dg<D, 4>(a, ap, pin, sa, grid, st); return DMS_OK;
-    case 8: launch_step_dg<D, 8>(a, ap, pin, sa, grid, st); return DMS_OK;
-    default: return fail(DMS_ERR_UNSUPPORTED, "group size");
+static StepKernel step_kernel_d(const Geo& g, int lanes_per_row) {
+  switch (g.g) {
+    case 1: return step_kernel_dg<D, 1>(g, lanes_per_row);
+    case 2: return step_kernel_dg<D, 2>(g, lanes_per_row);
+    case 4: return step_kernel_dg<D, 4>(g, lanes_per_row);
+    case 8: return step_kernel_dg<D, 8>(g, lanes_per_row);
+    default: return nullptr;
   }
+}
+
+static StepKernel step_kernel(const Geo& g, int lanes_per_row) {
+  return g.D == 128 ? step_kernel_d<128>(g, lanes_per_row) : step_kernel_d<64>(g, lanes_per_row);
 }
 
 // The fast decode attention applies: bf16/fp8 pages, D 64/128, power-of-two
@@ -1266,11 +1342,28 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
   if (linear)
     al |= reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(rms_gamma) |
           reinterpret_cast<uintptr_t>(W);
-  const bool fused = g.kv_dtype == DMS_BF16 && fast_decode_ok(cache, nullptr) && al % 16 == 0 &&
-                     (!linear || c.hidden % 8 == 0) && B * g.Hkv <= kMaxUnits;
+  const int npairs = B * g.Hkv;
+  const int agrid = decode_grid_for(cache);
+  bool fused = cache->step_fuse != 0 && fast_decode_ok(cache, nullptr) && al % 16 == 0 &&
+               (!linear || c.hidden % 8 == 0) && npairs <= kMaxUnits;
+  StepKernel kern = fused ? step_kernel(g, cache->decode_lpr) : nullptr;
+  if (!kern) fused = false;
+  if (fused && cache->step_fuse < 0) {
+    // One launch only when every workgroup can be resident at once: else the
+    // attention workgroups wait for whole prepare workgroups to leave, and
+    // the two calls in turn are faster.
+    if (cache->step_blocks_per_cu < 0) {
+      int n = 0;
+      if (check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kern), 256, 0),
+                    "step kernel occupancy"))
+        return DMS_ERR_HIP;
+      cache->step_blocks_per_cu = n;
+    }
+    fused = npairs + agrid <= cache->step_blocks_per_cu * cache->num_cus;
+  }
   hipStream_t st = as_stream(stream);
   if (!fused) {
-    // fp8 pages and other shapes: the two calls in turn
+    // other shapes, or a step too large for one resident launch: the two calls in turn
     int s = dms_decode_prepare(cache, seq_ids, hidden, rms_gamma, W, bias, offsets, q_inout, k, v, B, logits_out,
                                evict_out, stream);
     if (s) return s;
@@ -1295,13 +1388,9 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
   ap.logits_out = logits_out;
   ap.evict_out = evict_out;
   PrepIn pin{static_cast<const uint16_t*>(hidden), rms_gamma, W, static_cast<uint16_t*>(q_inout), linear ? 0 : 1};
-  const int npairs = B * g.Hkv;
-  const int agrid = decode_grid_for(cache);
   const int groups = std::min(kArriveGroups, agrid);
   StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, groups, agrid,
               linear ? 0 : 1};
-  const int s = g.D == 128 ? launch_step_d<128>(a, ap, pin, sa, npairs + agrid, st)
-                           : launch_step_d<64>(a, ap, pin, sa, npairs + agrid, st);
-  if (s) return s;
+  hipLaunchKernelGGL(kern, dim3(npairs + agrid), dim3(256), 0, st, a, ap, pin, sa);
   return check_hip(hipGetLastError(), "dms_decode_step launch");
 }

@@ -298,6 +298,9 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   if (const char* e = std::getenv("DMS_DECODE_LPR")) c->decode_lpr = std::atoi(e);
   const char* fg = std::getenv("DMS_GENERIC_KERNELS");
   c->force_generic = fg && fg[0] == '1';
+  c->step_fuse = -1;
+  if (const char* e = std::getenv("DMS_DECODE_STEP_FUSE")) c->step_fuse = std::atoi(e) ? 1 : 0;
+  c->step_blocks_per_cu = -1;
   const int units = cfg->max_batch * cfg->num_kv_heads;
   hipLaunchKernelGGL(init_kernel, dim3(256), dim3(256), 0, as_stream(stream), c->dev, g, units);
   if ((s = check_hip(hipGetLastError(), "init_kernel launch"))) { delete c; return s; }

@@ -78,6 +78,9 @@ struct dms_cache {
   int decode_np;         // passes in flight per round of the decode kernel (DMS_DECODE_NP; 0: default)
   int decode_lpr;        // lanes per row of the decode kernel (DMS_DECODE_LPR; 0: default)
   bool force_generic;    // DMS_GENERIC_KERNELS=1: vector-ALU decode and prefill attention kernels only
+  int step_fuse;         // dms_decode_step in one launch: -1 when all its workgroups fit at once (default),
+                         // 0 never, 1 always (DMS_DECODE_STEP_FUSE)
+  int step_blocks_per_cu;  // resident workgroups per CU of the one-launch step kernel (-1: not queried yet)
 };
 
 namespace dms {

@@ -7,8 +7,11 @@ open pages from the shared pool, and sequences sit at different positions
 (log-uniform prompt lengths, rows given in a shuffled order).  Every step
 checks the decisions and logits, the attention output of every query head,
 and, bit for bit, the slot tables, page tables, ring, positions, free stack
-and page bytes.  Shapes cover GQA groups 1, 2, 4 and 8, head_dim 64 and 128,
-both decision sources, layer mode, and more than 64 (row, KV head) units.
+and page bytes (fp8 pages: codes and per-page scales, the current token's
+row quantised by the attention exactly as the append stores it, in place,
+into the current page or as the first row of a new page).  Shapes cover GQA
+groups 1, 2, 4 and 8, head_dim 64 and 128, bf16 and fp8 pages, both decision
+sources, layer mode, and more than 64 (row, KV head) units.
 """
 import numpy as np
 import pytest
@@ -18,13 +21,23 @@ from tests.harness import Runner, from_dev, log, prepare, to_dev
 
 pytestmark = pytest.mark.gpu
 
-# name: (B, Hq, Hkv, D, decide, alpha_per)
+# name: (B, Hq, Hkv, D, decide, alpha_per, kv_dtype)
 SHAPES = {
-    "g4_d128_linear": (3, 8, 2, 128, "linear", "head"),
-    "g2_d64_qneuron": (3, 8, 4, 64, "qneuron", "head"),
-    "g8_d64_linear_layer": (2, 16, 2, 64, "linear", "layer"),
-    "g1_d128_qneuron_80_units": (20, 4, 4, 128, "qneuron", "head"),
+    "g4_d128_linear": (3, 8, 2, 128, "linear", "head", "bf16"),
+    "g2_d64_qneuron": (3, 8, 4, 64, "qneuron", "head", "bf16"),
+    "g8_d64_linear_layer": (2, 16, 2, 64, "linear", "layer", "bf16"),
+    "g1_d128_qneuron_80_units": (20, 4, 4, 128, "qneuron", "head", "bf16"),
+    "g4_d128_linear_fp8": (3, 8, 2, 128, "linear", "head", "fp8"),
+    "g2_d64_qneuron_fp8": (3, 8, 4, 64, "qneuron", "head", "fp8"),
 }
+
+
+@pytest.fixture(autouse=True)
+def _one_launch(monkeypatch):
+    """Every step=True call here runs the one-launch kernel, also where the
+    default would take the two calls (a step too large for one resident
+    launch); the caches read the setting when they are created."""
+    monkeypatch.setenv("DMS_DECODE_STEP_FUSE", "1")
 
 
 def _cuda():
@@ -35,9 +48,9 @@ def _cuda():
 
 
 def _workload(name, idx, **kw):
-    B, Hq, Hkv, D, decide, per = SHAPES[name]
+    B, Hq, Hkv, D, decide, per, kv = SHAPES[name]
     args = dict(name=f"step_{name}", cfg_id=40 + idx, B=B, hidden=256, Hq=Hq, Hkv=Hkv, D=D, act_dtype="bf16",
-                kv_dtype="bf16", window=24, block=16, prefill=0, decode_steps=40, chunk=64,
+                kv_dtype=kv, window=24, block=16, prefill=0, decode_steps=40, chunk=64,
                 p_range=(0.40, 0.70), ctx_range=(20, 150), decide=decide, alpha_per=per)
     args.update(kw)
     return synth.Workload(**args)
@@ -179,3 +192,25 @@ def test_step_max_units():
     r.check_tables(pages=True)
     assert r.dms.dms_cache_status(r.cache) == 0
     log(f"max units: stats {r.sim.stats()}")
+
+
+def test_step_fp8_concatenated_split():
+    """fp8 pages, 320 (row, KV head) units: the attention cuts the
+    concatenated slots into equal ranges, so some workgroups' ranges start at
+    the current token's row — also when that token opens a new page (pages of
+    16).  Regression case: such a range has no stored row to stand in for its
+    masked lanes."""
+    _cuda()
+    wl = synth.Workload(name="step_fp8_concat", cfg_id=54, B=40, hidden=256, Hq=8, Hkv=8, D=128, act_dtype="bf16",
+                        kv_dtype="fp8", window=24, block=16, prefill=0, decode_steps=24, chunk=64,
+                        p_range=(0.40, 0.70), ctx_range=(20, 80), decide="linear", alpha_per="head")
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    ctx = prep.draw.ctx
+    seqs = list(range(wl.B))
+    _fill(r, seqs)
+    r.check_tables(pages=True)
+    for i in range(wl.decode_steps):
+        r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], step=True)
+    r.check_tables(pages=True)
+    assert r.dms.dms_cache_status(r.cache) == 0
