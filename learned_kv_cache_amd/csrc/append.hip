@@ -407,30 +407,57 @@ __global__ __launch_bounds__(1024) void chunk_alloc_kernel(AppendArgs a) {
 
 constexpr int kTokPerWG = 16;   // tokens per workgroup of the write/amax kernels (one wave per token)
 
-// fp8 only: largest magnitude written into each freshly opened page.
+// fp8 only: largest magnitude written into each freshly opened page.  The
+// workgroup's tokens (consecutive, so mostly in one page) are folded per page
+// in LDS first: one atomic per (workgroup, page) instead of one per token
+// (a page's 256 tokens queued on the same two words otherwise).
 template <typename ACT>
 __global__ __launch_bounds__(kTokPerWG * 64) void chunk_amax_kernel(AppendArgs a) {
+  __shared__ int s_page[kTokPerWG];
+  __shared__ float s_mk[kTokPerWG], s_mv[kTokPerWG];
   const DevCache& d = a.d;
   const Geo& g = a.g;
   const int pair = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int tt = blockIdx.x * kTokPerWG + (threadIdx.x >> 6);
-  if (tt >= a.T) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tt = blockIdx.x * kTokPerWG + wave;
   const int32_t* info = d.chunk_info + static_cast<int64_t>(pair) * 8;
-  if (!info[0]) return;
-  const uint8_t* ev = a.evict + static_cast<int64_t>(pair) * a.T;
-  if (ev[tt] && tt + g.w < a.T) return;            // overwritten later in this chunk
-  const int slot = d.chunk_slot[static_cast<int64_t>(pair) * g.max_chunk + tt];
-  if (slot / g.P < info[4]) return;                 // page opened by an earlier call
-  const int row = pair / g.Hkv, kh = pair % g.Hkv;
-  const int seq = a.seq_ids ? a.seq_ids[row] : row;
-  const int page = d.page_table[(static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp + slot / g.P];
-  const size_t src = ((static_cast<size_t>(row) * a.T + tt) * g.Hkv + kh) * g.D;
-  const float mk = row_amax<ACT>(static_cast<const ACT*>(a.k) + src, g.D, lane);
-  const float mv = row_amax<ACT>(static_cast<const ACT*>(a.v) + src, g.D, lane);
+  int page = -1;
+  float mk = 0.0f, mv = 0.0f;
+  // (waves with no freshly written row keep page -1 and still meet the barrier)
+  if (tt < a.T && info[0]) {
+    const uint8_t* ev = a.evict + static_cast<int64_t>(pair) * a.T;
+    const int slot = d.chunk_slot[static_cast<int64_t>(pair) * g.max_chunk + tt];
+    // skipped: rows overwritten later in this chunk, and pages opened by an earlier call
+    if (!(ev[tt] && tt + g.w < a.T) && slot / g.P >= info[4]) {
+      const int row = pair / g.Hkv, kh = pair % g.Hkv;
+      const int seq = a.seq_ids ? a.seq_ids[row] : row;
+      page = d.page_table[(static_cast<int64_t>(seq) * g.Hkv + kh) * g.maxp + slot / g.P];
+      const size_t src = ((static_cast<size_t>(row) * a.T + tt) * g.Hkv + kh) * g.D;
+      mk = row_amax<ACT>(static_cast<const ACT*>(a.k) + src, g.D, lane);
+      mv = row_amax<ACT>(static_cast<const ACT*>(a.v) + src, g.D, lane);
+    }
+  }
   if (lane == 0) {
-    atomicMax(d.page_amax + 2 * page, __float_as_uint(mk));
-    atomicMax(d.page_amax + 2 * page + 1, __float_as_uint(mv));
+    s_page[wave] = page;
+    s_mk[wave] = mk;
+    s_mv[wave] = mv;
+  }
+  __syncthreads();
+  if (threadIdx.x < kTokPerWG) {
+    const int i = threadIdx.x, pg = s_page[i];
+    bool first = pg >= 0;
+    for (int j = 0; j < i; ++j) first = first && s_page[j] != pg;
+    if (first) {
+      float k2 = 0.0f, v2 = 0.0f;
+      for (int j = i; j < kTokPerWG; ++j) {
+        if (s_page[j] == pg) {
+          k2 = fmaxf(k2, s_mk[j]);
+          v2 = fmaxf(v2, s_mv[j]);
+        }
+      }
+      atomicMax(d.page_amax + 2 * pg, __float_as_uint(k2));
+      atomicMax(d.page_amax + 2 * pg + 1, __float_as_uint(v2));
+    }
   }
 }
 
