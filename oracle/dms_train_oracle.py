@@ -23,6 +23,10 @@ Readings (listed in the design notes as well):
   taken as [y > 0] (the same set, without a rounding of the sigmoid deciding).
 * T3 — the window test is q_idx - k_idx < w, as at inference (R1).
 
+Backward: ``train_attention_backward`` (the gradients of the forward for an
+upstream output gradient; pinned by central finite differences of
+``train_attention`` and by torch autograd of a torch restatement).
+
 Pins: ``tests/test_train_oracle_pins.py``.
 """
 from __future__ import annotations
@@ -101,3 +105,55 @@ def train_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, y: np.ndarray, 
             out[b, :, h] = (e @ v[b, :, kv]) / den
             lse[b, h] = (mx + np.log(den))[:, 0]
     return out, lse
+
+
+def train_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, y: np.ndarray, w: int,
+                             dout: np.ndarray, scale: Optional[float] = None):
+    """Gradients of the training-mode attention (walkthrough, 训练模式) for an
+    upstream gradient dout of its output.
+
+    With s_ij the modified score and P = softmax_j(s): dP = dO V^T,
+    dS = P * (dP - rowsum(dO * O)), dq_i = scale * sum_j dS_ij k_j,
+    dk_j = scale * sum_i dS_ij q_i, dv_j = sum_i P_ij dO_i (the last two summed
+    over the query heads that share the KV head), and, as key j's penalty
+    logsigmoid(-y_j) enters every score with i - j >= w (i >= j),
+    dy_j = -sigmoid(y_j) * sum over those (i, head) of dS_ij.  The -50000
+    entries are constants.
+
+    Shapes as in train_attention; dout like q.  Returns (dq, dk, dv, dy),
+    float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(T)
+    q_idx = rows[:, None]
+    k_idx = rows[None, :]
+    penalised = ((q_idx >= k_idx) & (q_idx - k_idx >= w)).astype(np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dy = np.zeros_like(y)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // g
+            pen = logsigmoid(-y[b, kv])
+            s = _scored(q[b, :, h], k[b, :, kv], pen, rows, w, scale)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            o = p @ v[b, :, kv]
+            dp = dout[b, :, h] @ v[b, :, kv].T
+            delta = (dout[b, :, h] * o).sum(axis=1, keepdims=True)
+            ds = p * (dp - delta)
+            dq[b, :, h] = scale * (ds @ k[b, :, kv])
+            dk[b, :, kv] += scale * (ds.T @ q[b, :, h])
+            dv[b, :, kv] += p.T @ dout[b, :, h]
+            dy[b, kv] += (ds * penalised).sum(axis=0)
+    dy *= -1.0 / (1.0 + np.exp(-y))
+    return dq, dk, dv, dy

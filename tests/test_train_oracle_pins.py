@@ -146,3 +146,69 @@ def test_rows_subset_equals_full():
     o2, l2 = tor.train_attention(q, k, v, y, w, rows=rows)
     np.testing.assert_array_equal(o2, out[:, rows])
     np.testing.assert_array_equal(l2, lse[:, :, rows])
+
+
+def _loss(q, k, v, y, w, dout, scale=None):
+    out, _ = tor.train_attention(q, k, v, y, w, scale=scale)
+    return float((out * dout).sum())
+
+
+def test_backward_matches_central_differences():
+    B, T, Hq, Hkv, D, w = 1, 9, 4, 2, 4, 3
+    q, k, v = _inputs(B, T, Hq, Hkv, D)
+    y = RNG.normal(0, 1.5, (B, Hkv, T))
+    dout = RNG.standard_normal((B, T, Hq, D))
+    dq, dk, dv, dy = tor.train_attention_backward(q, k, v, y, w, dout)
+    eps = 1e-6
+    for name, x, gr in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("y", y, dy)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v, "y": y}
+            args[name] = xp
+            fp = _loss(args["q"], args["k"], args["v"], args["y"], w, dout)
+            args[name] = xm
+            fm = _loss(args["q"], args["k"], args["v"], args["y"], w, dout)
+            num[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(gr, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_matches_torch_autograd():
+    B, T, Hq, Hkv, D, w = 2, 21, 4, 2, 8, 5
+    q, k, v = _inputs(B, T, Hq, Hkv, D)
+    y = RNG.normal(0, 2, (B, Hkv, T))
+    dout = RNG.standard_normal((B, T, Hq, D))
+    scale = 1.0 / math.sqrt(D)
+    tq, tk, tv, ty = (torch.tensor(x, requires_grad=True) for x in (q, k, v, y))
+    g = Hq // Hkv
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    outs = []
+    for b in range(B):
+        per_head = []
+        for h in range(Hq):
+            kv = h // g
+            s = scale * tq[b, :, h] @ tk[b, :, kv].T
+            pen = F.logsigmoid(-ty[b, kv])[None, :].expand(T, T)
+            s = torch.where(i - j >= w, s + pen, s)
+            s = torch.where(j > i, torch.full_like(s, -50000.0), s)
+            per_head.append(torch.softmax(s, dim=-1) @ tv[b, :, kv])
+        outs.append(torch.stack(per_head, dim=1))
+    out = torch.stack(outs)
+    (out * torch.from_numpy(dout)).sum().backward()
+    dq, dk, dv, dy = tor.train_attention_backward(q, k, v, y, w, dout)
+    for name, got, ref in (("q", dq, tq.grad), ("k", dk, tk.grad), ("v", dv, tv.grad), ("y", dy, ty.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_backward_no_penalty_region_gives_zero_gate_gradient():
+    B, T, Hq, Hkv, D = 1, 12, 2, 1, 4
+    q, k, v = _inputs(B, T, Hq, Hkv, D)
+    y = RNG.normal(0, 2, (B, Hkv, T))
+    dout = RNG.standard_normal((B, T, Hq, D))
+    _, _, _, dy = tor.train_attention_backward(q, k, v, y, T, dout)     # window covers every pair
+    assert np.array_equal(dy, np.zeros_like(dy))
