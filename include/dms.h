@@ -300,6 +300,31 @@ int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out);
  * realised compression; here tokens / live slots). */
 int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out);
 
+/*
+ * Backward of dms_train_attn_fwd (walkthrough, 训练模式): given the forward's
+ * inputs, its output `out` and log-sum-exp `lse`, and the output gradient
+ * `dout`, writes
+ *   dq [B][T][Hq][D], dk, dv [B][T][Hkv][D]   float32 (dk, dv summed over the
+ *                                               query heads of each KV head)
+ *   dgate [B][Hkv][T] float32: the gradient of the gate logits y, through
+ *                      the penalty logsigmoid(-y) of the scores at distance
+ *                      >= window: -sigmoid(y_j) * sum of those scores' gradients.
+ * q, k, v, out, dout bf16 in the forward's layouts (8-byte aligned);
+ * gate_logits [B][Hkv][T] and lse [B][Hq][T] float32 as given to / returned
+ * by the forward.  workspace: device memory of at least
+ * dms_train_attn_bwd_workspace_bytes bytes (overwritten).  head_dim 64 or
+ * 128, Hq / Hkv in {1, 2, 4}; softmax_scale <= 0 means 1 / sqrt(head_dim).
+ * DMS_ERR_ARG for NULL tensors or bad sizes, DMS_ERR_CAPACITY for a short
+ * workspace.  Needs no cache.
+ */
+int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_heads, int head_dim, int window,
+                       float softmax_scale, const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* gate_logits, const float* lse, void* dq, void* dk,
+                       void* dv, float* dgate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of dms_train_attn_bwd (one float per query row and head). */
+int dms_train_attn_bwd_workspace_bytes(int B, int T, int num_q_heads, size_t* bytes);
+
 /* ---- KVzap scorers ("动态内存稀疏化（DMS）策略：KVzap-linear-Llama-3.1-8B-Instruct的核心创新点",
  * KVzap-linear的技术架构; "革命性LLM加速技术：NVIDIA KVzap-mlp-Qwen3-8B如何实现高效KV缓存修剪？",
  * 模型架构 and 工作流程) ---- */

@@ -22,7 +22,7 @@ OUT = os.path.join(PKG, "libdms.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("DMS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["dms_host.hip", "decide.hip", "append.hip", "decode_attn.hip", "prefill_attn.hip", "kvzap.hip"]
+SOURCES = ["dms_host.hip", "decide.hip", "append.hip", "decode_attn.hip", "prefill_attn.hip", "kvzap.hip", "train_bwd.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -42,7 +42,7 @@ EXPORTS = (
     "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
     "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed", "dms_kvzap_score",
-    "dms_kvzap_workspace_bytes",
+    "dms_kvzap_workspace_bytes", "dms_train_attn_bwd", "dms_train_attn_bwd_workspace_bytes",
 )
 
 
@@ -111,6 +111,9 @@ def lib():
             "dms_kvzap_score": [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                 ctypes.c_size_t, vp],
             "dms_kvzap_workspace_bytes": [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)],
+            "dms_train_attn_bwd": [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   vp, vp, vp, ctypes.c_size_t, vp],
+            "dms_train_attn_bwd_workspace_bytes": [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)],
             "dms_prefill_attn": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_seq_reset": [vp, vp, i32, vp],
             "dms_cache_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
@@ -296,6 +299,30 @@ def dms_train_attn_fwd(q, k, v, gate_logits, out, lse, *, window: int, softmax_s
         _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
         _ptr(gate_logits, "gate_logits", torch.float32, B * Hkv * T), _ptr(out, "out", torch.bfloat16, q.numel()),
         _ptr(lse, "lse", torch.float32, B * Hq * T), _stream(stream)))
+
+
+def dms_train_attn_bwd(q, k, v, out, dout, gate_logits, lse, dq, dk, dv, dgate, *, window: int,
+                       softmax_scale: float = 0.0, workspace=None, stream=None) -> int:
+    """Gradients of dms_train_attn_fwd.  q, out, dout [B, T, Hq, D] and k, v
+    [B, T, Hkv, D] bf16; gate_logits [B, Hkv, T] and lse [B, Hq, T] f32; dq,
+    dk, dv f32 like q, k, v; dgate f32 like gate_logits.  workspace: a device
+    uint8 tensor of dms_train_attn_bwd_workspace_bytes bytes (allocated here
+    when not given)."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    n = ctypes.c_size_t()
+    _check(lib().dms_train_attn_bwd_workspace_bytes(B, T, Hq, ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(1, n.value), dtype=torch.uint8, device=q.device)
+    nq, nk = B * T * Hq * D, B * T * Hkv * D
+    return _check(lib().dms_train_attn_bwd(
+        B, T, Hq, Hkv, D, window, ctypes.c_float(softmax_scale), _ptr(q, "q", torch.bfloat16, nq),
+        _ptr(k, "k", torch.bfloat16, nk), _ptr(v, "v", torch.bfloat16, nk), _ptr(out, "out", torch.bfloat16, nq),
+        _ptr(dout, "dout", torch.bfloat16, nq), _ptr(gate_logits, "gate_logits", torch.float32, B * Hkv * T),
+        _ptr(lse, "lse", torch.float32, B * Hq * T), _ptr(dq, "dq", torch.float32, nq),
+        _ptr(dk, "dk", torch.float32, nk), _ptr(dv, "dv", torch.float32, nk),
+        _ptr(dgate, "dgate", torch.float32, B * Hkv * T), _ptr(workspace, "workspace"),
+        ctypes.c_size_t(workspace.numel()), _stream(stream)))
 
 
 def dms_kvzap_workspace_bytes(B: int, T: int, Hkv: int, Hm: int) -> int:

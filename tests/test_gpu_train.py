@@ -2,7 +2,9 @@
 oracle (needs an MI355X).
 
 Seeded bf16 Q/K/V (N(0, 1) rounded to bf16, the bits both sides use) and
-float32 gate logits.  Attention outputs within 2e-2 max / 2e-3 mean absolute
+float32 gate logits; the backward also takes a bf16 output gradient and is
+checked against the oracle's float64 gradients (dq, dk, dv and the gate
+logits') relative to each tensor's largest entry.  Attention outputs within 2e-2 max / 2e-3 mean absolute
 error (bf16 inputs, bf16-rounded probabilities in P.V, fp32 accumulation);
 the log-sum-exp within 4e-3 absolute (its sum runs over the same bf16-rounded
 probabilities: at most 2^-9 relative).  Shapes: GQA 1/2/4, head_dim 64/128,
@@ -127,3 +129,57 @@ def test_train_gate():
     # no noise, tau 1: y equals the logits bit for bit
     dms.dms_train_gate(ld, None, 1.0, y, None, None)
     assert np.array_equal(from_dev(y), logits.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# backward
+
+def _bwd(torch, q, k, v, y, w, dout):
+    from learned_kv_cache_amd import dms
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, dout))
+    yd = to_dev(y, "f32")
+    out = torch.empty_like(qd)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device="cuda")
+    dms.dms_train_attn_fwd(qd, kd, vd, yd, out, lse, window=w)
+    dq = torch.empty(B, T, Hq, D, dtype=torch.float32, device="cuda")
+    dk = torch.empty(B, T, Hkv, D, dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    dy = torch.empty(B, Hkv, T, dtype=torch.float32, device="cuda")
+    dms.dms_train_attn_bwd(qd, kd, vd, out, dod, yd, lse, dq, dk, dv, dy, window=w)
+    torch.cuda.synchronize()
+    return [from_dev(x) for x in (dq, dk, dv, dy)]
+
+
+# Gradient tolerance, relative to the largest reference entry of each tensor:
+# the products take bf16 operands (P, dS, and the bf16 forward output in
+# delta = rowsum(dO * O)), each rounded to 2^-9 relative, so an entry's error
+# is a few 2^-9 of the magnitudes summed into it: 2e-2 of the tensor's
+# largest entry at most, 2e-3 on average.
+GRAD_TOL = (2e-2, 2e-3)
+
+BWD_SHAPES = [
+    (8, 2, 128, 333, 48),
+    (8, 4, 64, 200, 16),
+    (4, 4, 128, 130, 32),
+    (8, 2, 64, 97, 512),
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=[f"hq{s[0]}_hkv{s[1]}_d{s[2]}_t{s[3]}_w{s[4]}" for s in BWD_SHAPES])
+def test_train_attn_bwd_shapes(shape):
+    torch = _torch()
+    Hq, Hkv, D, T, w = shape
+    gen = np.random.default_rng(BWD_SHAPES.index(shape) + 900)
+    B = 2
+    q, k, v = _bf16(gen, (B, T, Hq, D)), _bf16(gen, (B, T, Hkv, D)), _bf16(gen, (B, T, Hkv, D))
+    y = gen.normal(0.0, 3.0, (B, Hkv, T)).astype(np.float32)
+    dout = _bf16(gen, (B, T, Hq, D))
+    got = _bwd(torch, q, k, v, y, w, dout)
+    ref = tor.train_attention_backward(q, k, v, y, w, dout)
+    for name, g_, r_ in zip(("dq", "dk", "dv", "dgate"), got, ref):
+        scale = float(np.abs(r_).max())          # 0 for the gate when the window covers every pair
+        err = np.abs(g_ - r_)
+        log(f"bwd {shape} {name}: max |ref| {scale:.3g}, err max {err.max():.2e} mean {err.mean():.2e}")
+        assert err.max() <= GRAD_TOL[0] * scale and err.mean() <= GRAD_TOL[1] * scale, (shape, name)
