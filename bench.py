@@ -438,7 +438,10 @@ def run_train_fwd(args, dms, torch):
     layer shape: B = 2 sequences of T = 4096 tokens, window 512, gate logits
     from N(0, 3) logits plus logistic noise at tau = 0.1; each call timed with
     HIP events on the launch stream.  Useful work: 4 * D flops per (query
-    head, causal key) pair (training keeps every causal key)."""
+    head, causal key) pair (training keeps every causal key).  The backward
+    (dq, dk, dv and the gate-logit gradient from a seeded N(0, 1) output
+    gradient) is timed the same way; its useful work is the five products of
+    the softmax backward, 10 * D flops per pair."""
     B, T, Hq, Hkv, D, w = 2, 4096, 32, 8, 128, 512
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4242)
@@ -472,6 +475,27 @@ def run_train_fwd(args, dms, torch):
     gate_ms = e0.elapsed_time(e1) / reps
     attn_ms = e1.elapsed_time(e2) / reps
     useful = 4.0 * D * Hq * B * T * (T + 1) / 2
+
+    dout = torch.randn(B, T, Hq, D, generator=gen, device="cuda").to(torch.bfloat16)
+    dq = torch.empty(q.shape, device="cuda")
+    dk, dv = torch.empty(k.shape, device="cuda"), torch.empty(v.shape, device="cuda")
+    dy = torch.empty_like(logits)
+    ws = torch.empty(dms.dms_train_attn_bwd_workspace_bytes(B, T, Hq), dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        dms.dms_train_attn_bwd(q, k, v, out, dout, y, lse, dq, dk, dv, dy, window=w, workspace=ws)
+
+    for _ in range(3):
+        bwd()
+    torch.cuda.synchronize()
+    b0, b1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    b0.record()
+    for _ in range(reps):
+        bwd()
+    b1.record()
+    torch.cuda.synchronize()
+    bwd_ms = b0.elapsed_time(b1) / reps
+    useful_bwd = 2.5 * useful
     return {
         "workload": "qwen3-8b_layer_train_fwd_b2_t4096_w512",
         "attn_ms": attn_ms,
@@ -480,6 +504,10 @@ def run_train_fwd(args, dms, torch):
         "attn_tflops": useful / (attn_ms * 1e-3) / 1e12,
         "frac_bf16_peak": useful / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "tok_s": B * T / ((attn_ms + gate_ms) * 1e-3),
+        "bwd_ms": bwd_ms,
+        "bwd_useful_tflop": useful_bwd / 1e12,
+        "bwd_tflops": useful_bwd / (bwd_ms * 1e-3) / 1e12,
+        "bwd_frac_bf16_peak": useful_bwd / (bwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     }
 
 
@@ -643,7 +671,8 @@ def main() -> int:
     if not args.no_prefill:
         train = run_train_fwd(args, dms, torch)
         log(f"training forward: {train['attn_ms']:.3f} ms attention = {train['attn_tflops']:.1f} TFLOP/s, "
-            f"gate {train['gate_ms'] * 1e3:.1f} us")
+            f"gate {train['gate_ms'] * 1e3:.1f} us; backward {train['bwd_ms']:.3f} ms = "
+            f"{train['bwd_tflops']:.1f} TFLOP/s")
     others = None
     if not args.no_prefill:
         # Llama-3.2-1B has 16 layers; the fp8 serving figure rotates 4 layer caches

@@ -309,7 +309,7 @@ int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out);
  *   dgate [B][Hkv][T] float32: the gradient of the gate logits y, through
  *                      the penalty logsigmoid(-y) of the scores at distance
  *                      >= window: -sigmoid(y_j) * sum of those scores' gradients.
- * q, k, v, out, dout bf16 in the forward's layouts (8-byte aligned);
+ * q, k, v, out, dout bf16 in the forward's layouts (16-byte aligned);
  * gate_logits [B][Hkv][T] and lse [B][Hq][T] float32 as given to / returned
  * by the forward.  workspace: device memory of at least
  * dms_train_attn_bwd_workspace_bytes bytes (overwritten).  head_dim 64 or

@@ -11,18 +11,24 @@
 //
 // Three kernels: delta (one wave per query row and head); dk/dv/dy, one
 // workgroup per 64 keys of a (sequence, KV head), each wave owning 16 keys
-// whose K and V fragments stay in registers while it walks the causal query
-// blocks of its group's heads; dq, one workgroup per 64 queries of a
-// (sequence, query head), each wave owning 16 queries whose Q and dO
-// fragments stay in registers while it walks their causal key blocks.  The
-// four products of a 16 x 16 block run on bf16 16x16x16 matrix cores (fp32
-// accumulation); P and dS are rounded to bf16 as products' operands, as in
-// the forward.  Layout of a 16x16x16 product D = A B: lane l supplies
-// A[l % 16][4 (l / 16) + 0..3] and B[4 (l / 16) + 0..3][l % 16] and holds
-// D[4 (l / 16) + v][l % 16] in element v, so the scores of S = Q K^T
-// (rows queries, columns keys) are, lane by lane, the A operand of
-// dV = P^T dO and dK = dS^T Q, and those of S^T = K Q^T the A operand of
-// dQ = dS K.
+// whose K and V fragments stay in registers while the workgroup stages the
+// Q and dO rows of each 64-query tile (for every query head of the group) in
+// LDS; dq, one workgroup per 64 queries of a (sequence, query head), each
+// wave owning 16 queries whose Q and dO fragments stay in registers while the
+// workgroup stages the K and V rows of each causal 64-key tile.  All products
+// run on bf16 16x16x32 matrix cores (fp32 accumulation) over 32-row blocks;
+// P and dS are rounded to bf16 as operands, as in the forward.
+//
+// 16x16x32 operand layout (lane l, g = l / 16, i = 0..7): lane l supplies
+// A[l % 16][8 g + i] and B[8 g + i][l % 16] and holds D[4 g + v][l % 16] in
+// element v.  Two 16-row score blocks (rows 0..15 and 16..31 of a 32-row
+// block) leave lane l the rows 4 g + v and 16 + 4 g + v of its column; with
+// the contraction index k = 8 g + i read as row (i < 4 ? 4 g + i :
+// 16 + 4 g + i - 4), those eight values are the lane's A operand of the next
+// product (P^T dO and dS^T Q in dk/dv, dS K in dq), and the matching B
+// operand, four rows at one column twice, comes from the transposing LDS
+// read ds_read_b64_tr_b16 (within 16 lanes, lane j receives element j of
+// each of the four 16-element rows the group addresses).
 #include <algorithm>
 #include <cmath>
 
@@ -55,16 +61,30 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
-__device__ __forceinline__ short to_bf16(float f) {
-  return static_cast<short>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
+typedef __bf16 tb_bf8 __attribute__((ext_vector_type(8)));
+typedef float tb_f8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) tb_s4 tb_lds_s4;
+
+// 8 consecutive bf16 at p (16-byte aligned); zeros when !ok
+__device__ __forceinline__ tb_bf8 load8(const uint16_t* p, bool ok) {
+  if (!ok) return __builtin_bit_cast(tb_bf8, make_uint4(0u, 0u, 0u, 0u));
+  return *reinterpret_cast<const tb_bf8*>(p);
 }
 
-// 4 consecutive bf16 at p (8-byte aligned) as an MFMA operand; zeros when !ok
-__device__ __forceinline__ tb_s4 frag4(const uint16_t* p, bool ok) {
-  if (!ok) return tb_s4{0, 0, 0, 0};
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  return tb_s4{static_cast<short>(u.x & 0xFFFF), static_cast<short>(u.x >> 16), static_cast<short>(u.y & 0xFFFF),
-               static_cast<short>(u.y >> 16)};
+// the eight products' operands of a 32-row block, rounded to bf16
+__device__ __forceinline__ tb_bf8 pack8(const float* x) {
+  const tb_f8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, tb_bf8);
+}
+
+// B operand of a 32-row contraction at LDS column c: rows r and r + 16 of
+// the lane's group (see the layout note above); p points at row r's column
+// c + 4 (l16 & 3) with r = 4 g + (l16 >> 2) relative to the block.
+template <int LD>
+__device__ __forceinline__ tb_bf8 lds_cols8(const uint16_t* p) {
+  const tb_s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tb_lds_s4*)(p));
+  const tb_s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tb_lds_s4*)(p + 16 * LD));
+  return __builtin_bit_cast(tb_bf8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // logsigmoid(-y) = -softplus(y), stable for either sign
@@ -87,92 +107,135 @@ __global__ __launch_bounds__(256) void train_bwd_delta_kernel(BwdArgs a, int D) 
   }
 }
 
-// Workgroup (tile, pair): keys [64 tile, 64 tile + 64) of (b, kv); wave w
-// owns keys k0 = 64 tile + 16 w .. + 16.
+// Rows [r0, r0 + 64) of one head of a [B][T][H][D] bf16 tensor into LDS rows
+// of stride D + 16 elements (16-byte chunks; rows past T are zero).  With
+// rows of 2 D + 32 bytes both the 16-byte row reads and the transposing
+// column reads are free of bank conflicts.
+template <int D>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int b, int r0, int T, int H, int h) {
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int LD = D + 16;
+#pragma unroll
+  for (int it = 0; it < 64 * CH / 256; ++it) {
+    const int c = threadIdx.x + 256 * it;
+    const int row = c / CH, col = (c % CH) * 8;
+    const int t = r0 + row;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (t < T) val = *reinterpret_cast<const uint4*>(src + ((static_cast<size_t>(b) * T + t) * H + h) * D + col);
+    *reinterpret_cast<uint4*>(dst + row * LD + col) = val;
+  }
+}
+
+// Workgroup (pair, tile): keys [64 tile, 64 tile + 64) of (b, kv); wave w
+// owns keys k0 = 64 tile + 16 w .. + 16.  Per query tile of 64 rows and query
+// head of the group, the workgroup stages the Q and dO rows (and their lse,
+// delta) in LDS once; each wave then takes the two 32-query blocks.  Tiles
+// with the most causal queries (low tile index) are dispatched first.
 template <int D, int G>
 __global__ __launch_bounds__(256) void train_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int KS = D / 16;
+  constexpr int K32 = D / 32;               // k-steps of S and dP over head_dim
+  constexpr int DT = D / 16;                // 16-column tiles of dK and dV
+  constexpr int LD = D + 16;
+  __shared__ __align__(16) uint16_t sQ[64 * LD];
+  __shared__ __align__(16) uint16_t sO[64 * LD];
+  __shared__ float sL[64], sDl[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, l4 = lane >> 4;
-  const int pair = blockIdx.y, b = pair / a.Hkv, kv = pair % a.Hkv;
-  const int k0 = blockIdx.x * 64 + wave * 16;
-  if (k0 >= a.T) return;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int pair = blockIdx.x, b = pair / a.Hkv, kv = pair % a.Hkv;
+  const int kt0 = blockIdx.y * 64;
+  const int k0 = kt0 + wave * 16;
   const int key = k0 + l16;                 // this lane's key (column of S)
   const bool key_ok = key < a.T;
   // K and V fragments of the wave's keys (B operands of S = Q K^T, dP = dO V^T)
-  tb_s4 kf[KS], vf[KS];
+  tb_bf8 kf[K32], vf[K32];
   const size_t krow = ((static_cast<size_t>(b) * a.T + (key_ok ? key : 0)) * a.Hkv + kv) * D;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = frag4(a.k + krow + 16 * ks + 4 * l4, key_ok);
-    vf[ks] = frag4(a.v + krow + 16 * ks + 4 * l4, key_ok);
+  for (int ks = 0; ks < K32; ++ks) {
+    kf[ks] = load8(a.k + krow + 32 * ks + 8 * g, key_ok);
+    vf[ks] = load8(a.v + krow + 32 * ks + 8 * g, key_ok);
   }
   const float yk = key_ok ? a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] : 0.0f;
-  const float pen = penalty(yk);
-  tb_f4 dk[KS], dv[KS];
+  const float pen2 = penalty(yk) * kLog2e;
+  tb_f4 dk[DT], dv[DT];
 #pragma unroll
-  for (int dt = 0; dt < KS; ++dt) {
+  for (int dt = 0; dt < DT; ++dt) {
     dk[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
     dv[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
   }
   float dyacc = 0.0f;
   const float sl2 = a.scale * kLog2e;
-  for (int i0 = (k0 / 16) * 16; i0 < a.T; i0 += 16) {
+  for (int qb = kt0; qb < a.T; qb += 64) {
 #pragma unroll 1
     for (int hh = 0; hh < G; ++hh) {
       const int h = kv * G + hh;
-      // A operands: Q and dO rows of query i0 + l16
-      const int qa = i0 + l16;
-      const bool qa_ok = qa < a.T;
-      const size_t qrow = ((static_cast<size_t>(b) * a.T + (qa_ok ? qa : 0)) * a.Hq + h) * D;
-      tb_f4 s = tb_f4{0.f, 0.f, 0.f, 0.f}, dp = tb_f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(a.q + qrow + 16 * ks + 4 * l4, qa_ok), kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(a.dout + qrow + 16 * ks + 4 * l4, qa_ok), vf[ks], dp, 0,
-                                                      0, 0);
+      __syncthreads();                      // previous tile fully read
+      stage_rows<D>(sQ, a.q, b, qb, a.T, a.Hq, h);
+      stage_rows<D>(sO, a.dout, b, qb, a.T, a.Hq, h);
+      if (threadIdx.x < 128) {
+        const int r = threadIdx.x & 63, t = qb + r;
+        const int64_t li = (static_cast<int64_t>(b) * a.Hq + h) * a.T + t;
+        if (threadIdx.x < 64) sL[r] = t < a.T ? a.lse[li] * kLog2e : 0.0f;
+        else sDl[r] = t < a.T ? a.delta[li] : 0.0f;
       }
-      // element e: query i0 + 4 l4 + e, key `key`
-      short pa[4], da[4];
+      __syncthreads();
+#pragma unroll 1
+      for (int blk = 0; blk < 2; ++blk) {
+        const int i0 = qb + 32 * blk;
+        if (i0 >= a.T || k0 >= a.T) break;
+        if (i0 + 31 < k0) continue;         // every query of the block precedes the wave's keys
+        tb_f4 s[2], dp[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qi = i0 + 4 * l4 + e;
-        float p = 0.0f, ds = 0.0f;
-        if (qi < a.T && key_ok && qi >= key) {
-          const int64_t li = (static_cast<int64_t>(b) * a.Hq + h) * a.T + qi;
-          const bool penalised = qi - key >= a.w;
-          const float x = s[e] * sl2 + (penalised ? pen * kLog2e : 0.0f) - a.lse[li] * kLog2e;
-          p = __builtin_amdgcn_exp2f(x);
-          ds = p * (dp[e] - a.delta[li]);
-          if (penalised) dyacc += ds;
+        for (int c = 0; c < 2; ++c) {
+          const uint16_t* qr = sQ + (32 * blk + 16 * c + l16) * LD + 8 * g;
+          const uint16_t* orow = sO + (32 * blk + 16 * c + l16) * LD + 8 * g;
+          s[c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+          dp[c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < K32; ++ks) {
+            s[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const tb_bf8*>(qr + 32 * ks), kf[ks],
+                                                           s[c], 0, 0, 0);
+            dp[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const tb_bf8*>(orow + 32 * ks), vf[ks],
+                                                            dp[c], 0, 0, 0);
+          }
         }
-        pa[e] = to_bf16(p);
-        da[e] = to_bf16(ds);
-      }
-      const tb_s4 pA = tb_s4{pa[0], pa[1], pa[2], pa[3]}, dA = tb_s4{da[0], da[1], da[2], da[3]};
-      // dV += P^T dO, dK += dS^T Q: B operands dO / Q [query 4 l4 + e][d 16 dt + l16]
+        // element (c, e): query i0 + 16 c + 4 g + e, key `key`
+        float p[8], ds[8];
 #pragma unroll
-      for (int dt = 0; dt < KS; ++dt) {
-        short ob[4], qb[4];
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qi = i0 + 4 * l4 + e;
-          const bool ok = qi < a.T;
-          const size_t r = ((static_cast<size_t>(b) * a.T + (ok ? qi : 0)) * a.Hq + h) * D + 16 * dt + l16;
-          ob[e] = ok ? static_cast<short>(a.dout[r]) : 0;
-          qb[e] = ok ? static_cast<short>(a.q[r]) : 0;
+          for (int e = 0; e < 4; ++e) {
+            const int rr = 32 * blk + 16 * c + 4 * g + e;
+            const int qi = qb + rr;
+            float pv = 0.0f, dsv = 0.0f;
+            if (qi < a.T && key_ok && qi >= key) {
+              const bool penalised = qi - key >= a.w;
+              pv = __builtin_amdgcn_exp2f(s[c][e] * sl2 + (penalised ? pen2 : 0.0f) - sL[rr]);
+              dsv = pv * (dp[c][e] - sDl[rr]);
+              if (penalised) dyacc += dsv;
+            }
+            p[4 * c + e] = pv;
+            ds[4 * c + e] = dsv;
+          }
         }
-        dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pA, tb_s4{ob[0], ob[1], ob[2], ob[3]}, dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dA, tb_s4{qb[0], qb[1], qb[2], qb[3]}, dk[dt], 0, 0, 0);
+        const tb_bf8 pA = pack8(p), dA = pack8(ds);
+        // dV += P^T dO, dK += dS^T Q: B operands dO / Q at rows (query)
+        // 4 g + i and 16 + 4 g + i of the block, column 16 dt + l16
+        const int cofs = (32 * blk + 4 * g + (l16 >> 2)) * LD + 4 * (l16 & 3);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pA, lds_cols8<LD>(sO + cofs + 16 * dt), dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dA, lds_cols8<LD>(sQ + cofs + 16 * dt), dk[dt], 0, 0, 0);
+        }
       }
     }
   }
-  // dK, dV: element v of tile dt is key k0 + 4 l4 + v, dim 16 dt + l16
+  if (k0 >= a.T) return;
+  // dK, dV: element v of tile dt is key k0 + 4 g + v, dim 16 dt + l16
 #pragma unroll
-  for (int dt = 0; dt < KS; ++dt) {
+  for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int kk = k0 + 4 * l4 + e;
+      const int kk = k0 + 4 * g + e;
       if (kk < a.T) {
         const size_t r = ((static_cast<size_t>(b) * a.T + kk) * a.Hkv + kv) * D + 16 * dt + l16;
         a.dk[r] = dk[dt][e] * a.scale;
@@ -183,85 +246,108 @@ __global__ __launch_bounds__(256) void train_bwd_dkdv_kernel(BwdArgs a) {
   // dy: this lane's key summed over the four query groups (lanes l16 + 16 m)
   dyacc += __shfl_xor(dyacc, 16);
   dyacc += __shfl_xor(dyacc, 32);
-  if (l4 == 0 && key_ok) {
+  if (g == 0 && key_ok) {
     const float sig = 1.0f / (1.0f + __expf(-yk));
     a.dy[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] = -sig * dyacc;
   }
 }
 
-// Workgroup (tile, row): queries [64 tile, 64 tile + 64) of (b, h); wave w
-// owns queries q0 = 64 tile + 16 w .. + 16.
+// Workgroup (row, tile): queries [64 tile, 64 tile + 64) of (b, h); wave w
+// owns queries q0 = 64 tile + 16 w .. + 16.  Per key tile of 64 rows the
+// workgroup stages the K and V rows (and the keys' penalties) in LDS; each
+// wave takes the 32-key blocks that are causal for it.  Tiles with the most
+// keys (high tile index) are dispatched first.
 template <int D, int G>
 __global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
-  constexpr int KS = D / 16;
+  constexpr int K32 = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int LD = D + 16;
+  __shared__ __align__(16) uint16_t sK[64 * LD];
+  __shared__ __align__(16) uint16_t sV[64 * LD];
+  __shared__ float sP[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, l4 = lane >> 4;
-  const int row = blockIdx.y, b = row / a.Hq, h = row % a.Hq, kv = h / G;
-  const int q0 = blockIdx.x * 64 + wave * 16;
-  if (q0 >= a.T) return;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int row = blockIdx.x, b = row / a.Hq, h = row % a.Hq, kv = h / G;
+  const int qt0 = (static_cast<int>(gridDim.y) - 1 - static_cast<int>(blockIdx.y)) * 64;
+  const int q0 = qt0 + wave * 16;
   const int qi = q0 + l16;                  // this lane's query (column of S^T)
   const bool q_ok = qi < a.T;
+  // Q and dO fragments of the wave's queries (B operands of S^T = K Q^T, dP^T = V dO^T)
   const size_t qrow = ((static_cast<size_t>(b) * a.T + (q_ok ? qi : 0)) * a.Hq + h) * D;
-  tb_s4 qf[KS], of[KS];
+  tb_bf8 qf[K32], of[K32];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = frag4(a.q + qrow + 16 * ks + 4 * l4, q_ok);
-    of[ks] = frag4(a.dout + qrow + 16 * ks + 4 * l4, q_ok);
+  for (int ks = 0; ks < K32; ++ks) {
+    qf[ks] = load8(a.q + qrow + 32 * ks + 8 * g, q_ok);
+    of[ks] = load8(a.dout + qrow + 32 * ks + 8 * g, q_ok);
   }
   const int64_t li = (static_cast<int64_t>(b) * a.Hq + h) * a.T + (q_ok ? qi : 0);
   const float lse2 = q_ok ? a.lse[li] * kLog2e : 0.0f;
   const float dlt = q_ok ? a.delta[li] : 0.0f;
-  tb_f4 dq[KS];
+  tb_f4 dq[DT];
 #pragma unroll
-  for (int dt = 0; dt < KS; ++dt) dq[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale * kLog2e;
-  const int kend = min(a.T, q0 + 16);
-  for (int j0 = 0; j0 < kend; j0 += 16) {
-    // A operands: K and V rows of key j0 + l16
-    const int ka = j0 + l16;
-    const bool ka_ok = ka < a.T;
-    const size_t krow = ((static_cast<size_t>(b) * a.T + (ka_ok ? ka : 0)) * a.Hkv + kv) * D;
-    tb_f4 s = tb_f4{0.f, 0.f, 0.f, 0.f}, dp = tb_f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(a.k + krow + 16 * ks + 4 * l4, ka_ok), qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(a.v + krow + 16 * ks + 4 * l4, ka_ok), of[ks], dp, 0, 0, 0);
+  const int kend = min(a.T, qt0 + 64);
+  for (int kb = 0; kb < kend; kb += 64) {
+    __syncthreads();                        // previous tile fully read
+    stage_rows<D>(sK, a.k, b, kb, a.T, a.Hkv, kv);
+    stage_rows<D>(sV, a.v, b, kb, a.T, a.Hkv, kv);
+    if (threadIdx.x < 64) {
+      const int t = kb + threadIdx.x;
+      sP[threadIdx.x] = t < a.T ? penalty(a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + t]) * kLog2e : 0.0f;
     }
-    // element e: key j0 + 4 l4 + e, query qi
-    short da[4];
+    __syncthreads();
+#pragma unroll 1
+    for (int blk = 0; blk < 2; ++blk) {
+      const int j0 = kb + 32 * blk;
+      if (j0 >= a.T || j0 > q0 + 15 || q0 >= a.T) break;   // keys past every query of the wave
+      tb_f4 s[2], dp[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kj = j0 + 4 * l4 + e;
-      float ds = 0.0f;
-      if (q_ok && kj < a.T && kj <= qi) {
-        const bool penalised = qi - kj >= a.w;
-        float x = s[e] * sl2 - lse2;
-        if (penalised) x += penalty(a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + kj]) * kLog2e;
-        const float p = __builtin_amdgcn_exp2f(x);
-        ds = p * (dp[e] - dlt);
+      for (int c = 0; c < 2; ++c) {
+        const uint16_t* kr = sK + (32 * blk + 16 * c + l16) * LD + 8 * g;
+        const uint16_t* vr = sV + (32 * blk + 16 * c + l16) * LD + 8 * g;
+        s[c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+        dp[c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < K32; ++ks) {
+          s[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const tb_bf8*>(kr + 32 * ks), qf[ks], s[c],
+                                                         0, 0, 0);
+          dp[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const tb_bf8*>(vr + 32 * ks), of[ks],
+                                                          dp[c], 0, 0, 0);
+        }
       }
-      da[e] = to_bf16(ds);
-    }
-    const tb_s4 dA = tb_s4{da[0], da[1], da[2], da[3]};
-    // dQ += dS K: B operand K [key 4 l4 + e][d 16 dt + l16]
+      // element (c, e): key j0 + 16 c + 4 g + e, query qi
+      float ds[8];
 #pragma unroll
-    for (int dt = 0; dt < KS; ++dt) {
-      short kb[4];
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kj = j0 + 4 * l4 + e;
-        const bool ok = kj < a.T;
-        kb[e] = ok ? static_cast<short>(a.k[((static_cast<size_t>(b) * a.T + kj) * a.Hkv + kv) * D + 16 * dt + l16]) : 0;
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 32 * blk + 16 * c + 4 * g + e;
+          const int kj = kb + rr;
+          float dsv = 0.0f;
+          if (q_ok && kj < a.T && kj <= qi) {
+            const float pv = __builtin_amdgcn_exp2f(s[c][e] * sl2 - lse2 + (qi - kj >= a.w ? sP[rr] : 0.0f));
+            dsv = pv * (dp[c][e] - dlt);
+          }
+          ds[4 * c + e] = dsv;
+        }
       }
-      dq[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dA, tb_s4{kb[0], kb[1], kb[2], kb[3]}, dq[dt], 0, 0, 0);
+      const tb_bf8 dA = pack8(ds);
+      // dQ += dS K: B operand K at rows (key) 4 g + i and 16 + 4 g + i of the
+      // block, column 16 dt + l16
+      const int cofs = (32 * blk + 4 * g + (l16 >> 2)) * LD + 4 * (l16 & 3);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dA, lds_cols8<LD>(sK + cofs + 16 * dt), dq[dt], 0, 0, 0);
     }
   }
-  // element v of tile dt: query q0 + 4 l4 + v, dim 16 dt + l16
+  if (q0 >= a.T) return;
+  // element v of tile dt: query q0 + 4 g + v, dim 16 dt + l16
 #pragma unroll
-  for (int dt = 0; dt < KS; ++dt) {
+  for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int qq = q0 + 4 * l4 + e;
+      const int qq = q0 + 4 * g + e;
       if (qq < a.T) a.dq[((static_cast<size_t>(b) * a.T + qq) * a.Hq + h) * D + 16 * dt + l16] = dq[dt][e] * a.scale;
     }
   }
@@ -270,8 +356,8 @@ __global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
 template <int D, int G>
 void launch_bwd(const BwdArgs& a, hipStream_t st) {
   const int tiles = (a.T + 63) / 64;
-  hipLaunchKernelGGL((train_bwd_dkdv_kernel<D, G>), dim3(tiles, a.B * a.Hkv), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((train_bwd_dq_kernel<D, G>), dim3(tiles, a.B * a.Hq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((train_bwd_dkdv_kernel<D, G>), dim3(a.B * a.Hkv, tiles), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((train_bwd_dq_kernel<D, G>), dim3(a.B * a.Hq, tiles), dim3(256), 0, st, a);
 }
 
 template <int D>
@@ -310,7 +396,7 @@ extern "C" int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_head
     return fail(DMS_ERR_CAPACITY, "workspace smaller than dms_train_attn_bwd_workspace_bytes");
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(dout);
-  if (al % 8) return fail(DMS_ERR_UNSUPPORTED, "q, k, v and dout must be 8-byte aligned");
+  if (al % 16) return fail(DMS_ERR_UNSUPPORTED, "q, k, v and dout must be 16-byte aligned");
   BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

@@ -301,6 +301,12 @@ def dms_train_attn_fwd(q, k, v, gate_logits, out, lse, *, window: int, softmax_s
         _ptr(lse, "lse", torch.float32, B * Hq * T), _stream(stream)))
 
 
+def dms_train_attn_bwd_workspace_bytes(B: int, T: int, Hq: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().dms_train_attn_bwd_workspace_bytes(B, T, Hq, ctypes.byref(n)))
+    return n.value
+
+
 def dms_train_attn_bwd(q, k, v, out, dout, gate_logits, lse, dq, dk, dv, dgate, *, window: int,
                        softmax_scale: float = 0.0, workspace=None, stream=None) -> int:
     """Gradients of dms_train_attn_fwd.  q, out, dout [B, T, Hq, D] and k, v
@@ -310,10 +316,9 @@ def dms_train_attn_bwd(q, k, v, out, dout, gate_logits, lse, dq, dk, dv, dgate, 
     when not given)."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    n = ctypes.c_size_t()
-    _check(lib().dms_train_attn_bwd_workspace_bytes(B, T, Hq, ctypes.byref(n)))
     if workspace is None:
-        workspace = torch.empty(max(1, n.value), dtype=torch.uint8, device=q.device)
+        n = dms_train_attn_bwd_workspace_bytes(B, T, Hq)
+        workspace = torch.empty(max(1, n), dtype=torch.uint8, device=q.device)
     nq, nk = B * T * Hq * D, B * T * Hkv * D
     return _check(lib().dms_train_attn_bwd(
         B, T, Hq, Hkv, D, window, ctypes.c_float(softmax_scale), _ptr(q, "q", torch.bfloat16, nq),
