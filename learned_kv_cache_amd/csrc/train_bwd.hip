@@ -9,7 +9,7 @@
 //   query heads of their group),
 //   dy_j = -sigmoid(y_j) * sum of dS_ij over the penalised pairs (i - j >= w).
 //
-// Three kernels: delta (one wave per query row and head); dk/dv/dy, one
+// Three kernels: delta (D / 8 lanes per query row and head); dk/dv/dy, one
 // workgroup per 64 keys of a (sequence, KV head), each wave owning 16 keys
 // whose K and V fragments stay in registers while the workgroup stages the
 // Q and dO rows of each 64-query tile (for every query head of the group) in
@@ -90,16 +90,28 @@ __device__ __forceinline__ tb_bf8 lds_cols8(const uint16_t* p) {
 // logsigmoid(-y) = -softplus(y), stable for either sign
 __device__ __forceinline__ float penalty(float yv) { return -(fmaxf(yv, 0.0f) + log1pf(__expf(-fabsf(yv)))); }
 
-__global__ __launch_bounds__(256) void train_bwd_delta_kernel(BwdArgs a, int D) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);   // (b, t, h) row of O
+// delta of one (b, t, h) row per D / 8 lanes: 16-byte loads of dO and O,
+// products summed in fp32, then over the row's lanes by xor shuffles.
+template <int D>
+__global__ __launch_bounds__(256) void train_bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;                // lanes per row
+  const int64_t r = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / LPR;   // (b, t, h) row of O
+  const int part = threadIdx.x % LPR;
   const int64_t rows = static_cast<int64_t>(a.B) * a.T * a.Hq;
-  if (r >= rows) return;
   float s = 0.0f;
-  for (int d = lane; d < D; d += 64) s = fmaf(bf(a.dout[r * D + d]), bf(a.o[r * D + d]), s);
+  if (r < rows) {
+    const uint4 x = *reinterpret_cast<const uint4*>(a.dout + r * D + 8 * part);
+    const uint4 y = *reinterpret_cast<const uint4*>(a.o + r * D + 8 * part);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) {
+    for (int j = 0; j < 4; ++j) {
+      s = fmaf(bf(static_cast<uint16_t>(xs[j] & 0xFFFF)), bf(static_cast<uint16_t>(ys[j] & 0xFFFF)), s);
+      s = fmaf(bf(static_cast<uint16_t>(xs[j] >> 16)), bf(static_cast<uint16_t>(ys[j] >> 16)), s);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (r < rows && part == 0) {
     const int h = static_cast<int>(r % a.Hq);
     const int64_t bt = r / a.Hq;
     const int t = static_cast<int>(bt % a.T), b = static_cast<int>(bt / a.T);
@@ -107,24 +119,36 @@ __global__ __launch_bounds__(256) void train_bwd_delta_kernel(BwdArgs a, int D) 
   }
 }
 
-// Rows [r0, r0 + 64) of one head of a [B][T][H][D] bf16 tensor into LDS rows
-// of stride D + 16 elements (16-byte chunks; rows past T are zero).  With
-// rows of 2 D + 32 bytes both the 16-byte row reads and the transposing
-// column reads are free of bank conflicts.
+// Rows [r0, r0 + 64) of one head of a [B][T][H][D] bf16 tensor, staged in
+// two steps so that the next tile's global loads run under the current
+// tile's products: fetch_rows reads this thread's 16-byte chunks into
+// registers (rows past T are zero), put_rows writes them to LDS rows of
+// stride D + 16 elements.  With rows of 2 D + 32 bytes both the 16-byte row
+// reads and the transposing column reads are free of bank conflicts.
 template <int D>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int b, int r0, int T, int H, int h) {
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int LD = D + 16;
+struct TileRows {
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int LD = D + 16;
+  static constexpr int NIT = 64 * CH / 256; // chunks per thread
+  uint4 r[NIT];
+  __device__ __forceinline__ void fetch(const uint16_t* src, int b, int r0, int T, int H, int h) {
 #pragma unroll
-  for (int it = 0; it < 64 * CH / 256; ++it) {
-    const int c = threadIdx.x + 256 * it;
-    const int row = c / CH, col = (c % CH) * 8;
-    const int t = r0 + row;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (t < T) val = *reinterpret_cast<const uint4*>(src + ((static_cast<size_t>(b) * T + t) * H + h) * D + col);
-    *reinterpret_cast<uint4*>(dst + row * LD + col) = val;
+    for (int it = 0; it < NIT; ++it) {
+      const int c = threadIdx.x + 256 * it;
+      const int t = r0 + c / CH;
+      r[it] = t < T ? *reinterpret_cast<const uint4*>(src + ((static_cast<size_t>(b) * T + t) * H + h) * D +
+                                                       (c % CH) * 8)
+                    : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
-}
+  __device__ __forceinline__ void put(uint16_t* dst) const {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = threadIdx.x + 256 * it;
+      *reinterpret_cast<uint4*>(dst + (c / CH) * LD + (c % CH) * 8) = r[it];
+    }
+  }
+};
 
 // Workgroup (pair, tile): keys [64 tile, 64 tile + 64) of (b, kv); wave w
 // owns keys k0 = 64 tile + 16 w .. + 16.  Per query tile of 64 rows and query
@@ -164,20 +188,35 @@ __global__ __launch_bounds__(256) void train_bwd_dkdv_kernel(BwdArgs a) {
   }
   float dyacc = 0.0f;
   const float sl2 = a.scale * kLog2e;
-  for (int qb = kt0; qb < a.T; qb += 64) {
-#pragma unroll 1
-    for (int hh = 0; hh < G; ++hh) {
-      const int h = kv * G + hh;
-      __syncthreads();                      // previous tile fully read
-      stage_rows<D>(sQ, a.q, b, qb, a.T, a.Hq, h);
-      stage_rows<D>(sO, a.dout, b, qb, a.T, a.Hq, h);
-      if (threadIdx.x < 128) {
-        const int r = threadIdx.x & 63, t = qb + r;
-        const int64_t li = (static_cast<int64_t>(b) * a.Hq + h) * a.T + t;
-        if (threadIdx.x < 64) sL[r] = t < a.T ? a.lse[li] * kLog2e : 0.0f;
-        else sDl[r] = t < a.T ? a.delta[li] : 0.0f;
-      }
-      __syncthreads();
+  // tiles in the order (query tile, head of the group); the next one's rows
+  // are fetched into registers while the current one is computed
+  TileRows<D> nq, no;
+  float nrow = 0.0f;                        // lse (threads 0..63) or delta (64..127) of the next tile
+  auto fetch = [&](int qb, int h) {
+    nq.fetch(a.q, b, qb, a.T, a.Hq, h);
+    no.fetch(a.dout, b, qb, a.T, a.Hq, h);
+    if (threadIdx.x < 128) {
+      const int t = qb + (threadIdx.x & 63);
+      const int64_t li = (static_cast<int64_t>(b) * a.Hq + h) * a.T + t;
+      nrow = t >= a.T ? 0.0f : threadIdx.x < 64 ? a.lse[li] * kLog2e : a.delta[li];
+    }
+  };
+  int nqb = kt0, nhh = 0;
+  if (nqb < a.T) fetch(nqb, kv * G);
+  while (nqb < a.T) {
+    const int qb = nqb;
+    __syncthreads();                        // previous tile fully read
+    nq.put(sQ);
+    no.put(sO);
+    if (threadIdx.x < 64) sL[threadIdx.x] = nrow;
+    else if (threadIdx.x < 128) sDl[threadIdx.x - 64] = nrow;
+    __syncthreads();
+    if (++nhh == G) {
+      nhh = 0;
+      nqb += 64;
+    }
+    if (nqb < a.T) fetch(nqb, kv * G + nhh);
+    {
 #pragma unroll 1
       for (int blk = 0; blk < 2; ++blk) {
         const int i0 = qb + 32 * blk;
@@ -288,15 +327,25 @@ __global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) dq[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale * kLog2e;
   const int kend = min(a.T, qt0 + 64);
+  // the next key tile's rows are fetched into registers while the current
+  // one is computed
+  TileRows<D> nk, nv;
+  float npen = 0.0f;                        // threads 0..63: the next tile's key penalties
+  auto fetch = [&](int kb) {
+    nk.fetch(a.k, b, kb, a.T, a.Hkv, kv);
+    nv.fetch(a.v, b, kb, a.T, a.Hkv, kv);
+    const int t = kb + threadIdx.x;
+    if (threadIdx.x < 64)
+      npen = t < a.T ? penalty(a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + t]) * kLog2e : 0.0f;
+  };
+  if (kend > 0) fetch(0);
   for (int kb = 0; kb < kend; kb += 64) {
     __syncthreads();                        // previous tile fully read
-    stage_rows<D>(sK, a.k, b, kb, a.T, a.Hkv, kv);
-    stage_rows<D>(sV, a.v, b, kb, a.T, a.Hkv, kv);
-    if (threadIdx.x < 64) {
-      const int t = kb + threadIdx.x;
-      sP[threadIdx.x] = t < a.T ? penalty(a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + t]) * kLog2e : 0.0f;
-    }
+    nk.put(sK);
+    nv.put(sV);
+    if (threadIdx.x < 64) sP[threadIdx.x] = npen;
     __syncthreads();
+    if (kb + 64 < kend) fetch(kb + 64);
 #pragma unroll 1
     for (int blk = 0; blk < 2; ++blk) {
       const int j0 = kb + 32 * blk;
@@ -396,7 +445,8 @@ extern "C" int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_head
     return fail(DMS_ERR_CAPACITY, "workspace smaller than dms_train_attn_bwd_workspace_bytes");
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(dout);
-  if (al % 16) return fail(DMS_ERR_UNSUPPORTED, "q, k, v and dout must be 16-byte aligned");
+  if ((al | reinterpret_cast<uintptr_t>(out)) % 16)
+    return fail(DMS_ERR_UNSUPPORTED, "q, k, v, out and dout must be 16-byte aligned");
   BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -418,8 +468,10 @@ extern "C" int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_head
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
   hipStream_t st = as_stream(stream);
   const int64_t rows = static_cast<int64_t>(B) * T * num_q_heads;
-  hipLaunchKernelGGL(train_bwd_delta_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st, a,
-                     head_dim);
+  const int64_t rows_per_block = 256 / (head_dim / 8);
+  const dim3 dgrid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  if (head_dim == 128) hipLaunchKernelGGL(train_bwd_delta_kernel<128>, dgrid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(train_bwd_delta_kernel<64>, dgrid, dim3(256), 0, st, a);
   const int g = num_q_heads / num_kv_heads;
   const int s = head_dim == 128 ? launch_bwd_d<128>(a, g, st) : launch_bwd_d<64>(a, g, st);
   if (s) return s;
