@@ -183,3 +183,29 @@ def test_train_attn_bwd_shapes(shape):
         err = np.abs(g_ - r_)
         log(f"bwd {shape} {name}: max |ref| {scale:.3g}, err max {err.max():.2e} mean {err.mean():.2e}")
         assert err.max() <= GRAD_TOL[0] * scale and err.mean() <= GRAD_TOL[1] * scale, (shape, name)
+
+
+def test_train_attn_bwd_qwen3_8b_shape_groups():
+    """The benchmarked shape (Qwen3-8B layer: B 2, T 4096, 32 query and 8 KV
+    heads, D 128, window 512) in the launch configuration the benchmark times;
+    every entry of two KV groups (the first sequence's first group and the
+    second sequence's last) against the oracle run on those groups alone."""
+    torch = _torch()
+    B, T, Hq, Hkv, D, w = 2, 4096, 32, 8, 128, 512
+    G = Hq // Hkv
+    gen = np.random.default_rng(4096)
+    q, k, v = _bf16(gen, (B, T, Hq, D)), _bf16(gen, (B, T, Hkv, D)), _bf16(gen, (B, T, Hkv, D))
+    y = gen.normal(0.0, 3.0, (B, Hkv, T)).astype(np.float32)
+    dout = _bf16(gen, (B, T, Hq, D))
+    got = _bwd(torch, q, k, v, y, w, dout)
+    for b, kv in ((0, 0), (1, Hkv - 1)):
+        hs, ks = slice(kv * G, (kv + 1) * G), slice(kv, kv + 1)
+        ref = tor.train_attention_backward(q[b:b + 1, :, hs], k[b:b + 1, :, ks], v[b:b + 1, :, ks],
+                                           y[b:b + 1, ks], w, dout[b:b + 1, :, hs])
+        mine = (got[0][b:b + 1, :, hs], got[1][b:b + 1, :, ks], got[2][b:b + 1, :, ks], got[3][b:b + 1, ks])
+        for name, g_, r_ in zip(("dq", "dk", "dv", "dgate"), mine, ref):
+            scale = float(np.abs(r_).max())
+            err = np.abs(g_ - r_)
+            log(f"bwd full shape (b {b}, kv {kv}) {name}: max |ref| {scale:.3g}, err max {err.max():.2e} "
+                f"mean {err.mean():.2e}")
+            assert err.max() <= GRAD_TOL[0] * scale and err.mean() <= GRAD_TOL[1] * scale, (b, kv, name)
