@@ -94,3 +94,55 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(dms, "_LIB_PATH", os.path.join(ROOT, "no_such_lib.so"))
     with pytest.raises(RuntimeError, match="not built"):
         dms.lib()
+
+
+def test_training_scorer_and_accounting_arguments_fail_before_any_launch():
+    """Argument checks of the training, KVzap and accounting entry points run
+    on the host before any HIP call (placeholder addresses are never
+    dereferenced: every call below fails a check or has nothing to do)."""
+    L = dms.lib()
+    vp = ctypes.c_void_p
+    a16 = vp(4096)                      # 16-byte aligned placeholder
+    a8 = vp(4096 + 8)                   # 8-byte aligned only
+    f = ctypes.c_float(0.0)
+    # training forward
+    assert L.dms_train_attn_fwd(1, 8, 4, 2, 128, 4, f, None, a16, a16, a16, a16, a16, None) == dms.DMS_ERR_ARG
+    assert L.dms_train_attn_fwd(1, 8, 4, 3, 128, 4, f, a16, a16, a16, a16, a16, a16, None) == dms.DMS_ERR_ARG
+    assert L.dms_train_attn_fwd(1, 8, 4, 2, 96, 4, f, a16, a16, a16, a16, a16, a16, None) == dms.DMS_ERR_UNSUPPORTED
+    assert L.dms_train_attn_fwd(1, 8, 4, 2, 128, 0, f, a16, a16, a16, a16, a16, a16, None) == dms.DMS_ERR_ARG
+    assert L.dms_train_attn_fwd(1, 8, 4, 2, 128, 4, f, a8, a16, a16, a16, a16, a16, None) == dms.DMS_ERR_ARG
+    # training backward and its workspace size
+    n = ctypes.c_size_t()
+    assert L.dms_train_attn_bwd_workspace_bytes(2, 10, 4, ctypes.byref(n)) == dms.DMS_OK and n.value == 2 * 10 * 4 * 4
+    assert L.dms_train_attn_bwd_workspace_bytes(2, 10, 0, ctypes.byref(n)) == dms.DMS_ERR_ARG
+    t11 = [a16] * 11                    # q k v out dout y lse dq dk dv dgate
+    ws = (a16, ctypes.c_size_t(1 << 20))
+    assert L.dms_train_attn_bwd(-1, 8, 4, 2, 128, 4, f, *t11, *ws, None) == dms.DMS_ERR_ARG
+    assert L.dms_train_attn_bwd(1, 8, 4, 3, 128, 4, f, *t11, *ws, None) == dms.DMS_ERR_ARG
+    assert L.dms_train_attn_bwd(1, 8, 4, 2, 96, 4, f, *t11, *ws, None) == dms.DMS_ERR_UNSUPPORTED
+    assert L.dms_train_attn_bwd(0, 8, 4, 2, 128, 4, f, *([None] * 11), None, ctypes.c_size_t(0), None) == dms.DMS_OK
+    assert L.dms_train_attn_bwd(1, 8, 4, 2, 128, 4, f, *t11[:5], None, *t11[6:], *ws, None) == dms.DMS_ERR_ARG
+    assert L.dms_train_attn_bwd(1, 8, 4, 2, 128, 4, f, *t11, a16, ctypes.c_size_t(8 * 4 * 4 - 1), None) == \
+        dms.DMS_ERR_CAPACITY
+    assert L.dms_train_attn_bwd(1, 8, 4, 2, 128, 4, f, a8, *t11[1:], *ws, None) == dms.DMS_ERR_UNSUPPORTED
+    # KVzap scorers
+    assert L.dms_kvzap_workspace_bytes(1, 8, 0, 512, ctypes.byref(n)) == dms.DMS_ERR_ARG
+    thr = ctypes.c_float(-4.0)
+    kz = lambda B, T, H, Hkv, Hm, dt, h, W1, W2, th, ev, wsb: L.dms_kvzap_score(  # noqa: E731
+        B, T, H, Hkv, Hm, dt, h, W1, None, W2, None, th, None, ev, a16, ctypes.c_size_t(wsb), None)
+    assert kz(0, 8, 4096, 8, 512, dms.DMS_BF16, None, None, None, thr, None, 0) == dms.DMS_OK
+    assert kz(1, 8, 4096, 8, 512, dms.DMS_BF16, None, a16, a16, thr, a16, 1 << 20) == dms.DMS_ERR_ARG
+    assert kz(1, 8, 4096, 8, 512, dms.DMS_FP8_E4M3, a16, a16, a16, thr, a16, 1 << 20) == dms.DMS_ERR_UNSUPPORTED
+    assert kz(1, 8, 4096, 17, 512, dms.DMS_BF16, a16, a16, a16, thr, a16, 1 << 20) == dms.DMS_ERR_UNSUPPORTED
+    assert kz(1, 8, 4016, 8, 512, dms.DMS_BF16, a16, a16, a16, thr, a16, 1 << 20) == dms.DMS_ERR_UNSUPPORTED
+    assert kz(1, 8, 4096, 8, 500, dms.DMS_BF16, a16, a16, a16, thr, a16, 1 << 20) == dms.DMS_ERR_UNSUPPORTED
+    assert kz(1, 8, 4096, 8, 512, dms.DMS_BF16, a8, a16, a16, thr, a16, 1 << 20) == dms.DMS_ERR_UNSUPPORTED
+    assert kz(1, 8, 4096, 8, 512, dms.DMS_BF16, a16, a16, a16, ctypes.c_float(float("nan")), a16, 1 << 20) == \
+        dms.DMS_ERR_ARG
+    assert kz(1, 8, 4096, 8, 512, dms.DMS_BF16, a16, a16, None, thr, a16, 1 << 20) == dms.DMS_ERR_ARG
+    assert kz(1, 8, 4096, 8, 512, dms.DMS_BF16, a16, a16, a16, thr, a16, 0) == dms.DMS_ERR_CAPACITY
+    # serving accounting without a cache
+    info = dms.dms_seq_info()
+    assert L.dms_seq_info_get(None, None, 1, None, ctypes.byref(info)) == dms.DMS_ERR_ARG
+    p, fr = ctypes.c_int64(), ctypes.c_int64()
+    assert L.dms_pages_needed(None, None, a16, 1, None, ctypes.byref(p), ctypes.byref(fr)) == dms.DMS_ERR_ARG
