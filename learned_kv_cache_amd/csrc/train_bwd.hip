@@ -58,6 +58,7 @@ struct BwdArgs {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBwdKeyGroups = 1;          // 16-key groups per wave in the dk/dv kernel
 
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
@@ -150,43 +151,54 @@ struct TileRows {
   }
 };
 
-// Workgroup (pair, tile): keys [64 tile, 64 tile + 64) of (b, kv); wave w
-// owns keys k0 = 64 tile + 16 w .. + 16.  Per query tile of 64 rows and query
+// Workgroup (pair, tile): keys [64 KG tile, 64 KG (tile + 1)) of (b, kv);
+// wave w owns the 16 KG keys from k0 = 64 KG tile + 16 KG w, in KG groups of
+// 16 that share every LDS operand read.  Per query tile of 64 rows and query
 // head of the group, the workgroup stages the Q and dO rows (and their lse,
 // delta) in LDS once; each wave then takes the two 32-query blocks.  Tiles
 // with the most causal queries (low tile index) are dispatched first.
-template <int D, int G>
-__global__ __launch_bounds__(256) void train_bwd_dkdv_kernel(BwdArgs a) {
+template <int D, int G, int KG>
+__global__ __launch_bounds__(256, KG == 1 ? 2 : 1) void train_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int K32 = D / 32;               // k-steps of S and dP over head_dim
   constexpr int DT = D / 16;                // 16-column tiles of dK and dV
   constexpr int LD = D + 16;
   __shared__ __align__(16) uint16_t sQ[64 * LD];
   __shared__ __align__(16) uint16_t sO[64 * LD];
-  __shared__ float sL[64], sDl[64];
+  __shared__ __align__(16) float sL[64];
+  __shared__ __align__(16) float sDl[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int pair = blockIdx.x, b = pair / a.Hkv, kv = pair % a.Hkv;
-  const int kt0 = blockIdx.y * 64;
-  const int k0 = kt0 + wave * 16;
-  const int key = k0 + l16;                 // this lane's key (column of S)
-  const bool key_ok = key < a.T;
-  // K and V fragments of the wave's keys (B operands of S = Q K^T, dP = dO V^T)
-  tb_bf8 kf[K32], vf[K32];
-  const size_t krow = ((static_cast<size_t>(b) * a.T + (key_ok ? key : 0)) * a.Hkv + kv) * D;
+  const int kt0 = blockIdx.y * 64 * KG;
+  const int k0 = kt0 + wave * 16 * KG;
+  // K and V fragments of the wave's keys (B operands of S = Q K^T, dP = dO V^T);
+  // lane column l16 of group kg is key k0 + 16 kg + l16
+  tb_bf8 kf[KG][K32], vf[KG][K32];
+  float pen2[KG], yk[KG];
 #pragma unroll
-  for (int ks = 0; ks < K32; ++ks) {
-    kf[ks] = load8(a.k + krow + 32 * ks + 8 * g, key_ok);
-    vf[ks] = load8(a.v + krow + 32 * ks + 8 * g, key_ok);
-  }
-  const float yk = key_ok ? a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] : 0.0f;
-  const float pen2 = penalty(yk) * kLog2e;
-  tb_f4 dk[DT], dv[DT];
+  for (int kg = 0; kg < KG; ++kg) {
+    const int key = k0 + 16 * kg + l16;
+    const bool ok = key < a.T;
+    const size_t krow = ((static_cast<size_t>(b) * a.T + (ok ? key : 0)) * a.Hkv + kv) * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dk[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
-    dv[dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < K32; ++ks) {
+      kf[kg][ks] = load8(a.k + krow + 32 * ks + 8 * g, ok);
+      vf[kg][ks] = load8(a.v + krow + 32 * ks + 8 * g, ok);
+    }
+    yk[kg] = ok ? a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] : 0.0f;
+    pen2[kg] = penalty(yk[kg]) * kLog2e;
   }
-  float dyacc = 0.0f;
+  tb_f4 dk[KG][DT], dv[KG][DT];
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dk[kg][dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
+      dv[kg][dt] = tb_f4{0.f, 0.f, 0.f, 0.f};
+    }
+  float dyacc[KG];
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg) dyacc[kg] = 0.0f;
   const float sl2 = a.scale * kLog2e;
   // tiles in the order (query tile, head of the group); the next one's rows
   // are fetched into registers while the current one is computed
@@ -216,78 +228,129 @@ __global__ __launch_bounds__(256) void train_bwd_dkdv_kernel(BwdArgs a) {
       nqb += 64;
     }
     if (nqb < a.T) fetch(nqb, kv * G + nhh);
-    {
 #pragma unroll 1
-      for (int blk = 0; blk < 2; ++blk) {
-        const int i0 = qb + 32 * blk;
-        if (i0 >= a.T || k0 >= a.T) break;
-        if (i0 + 31 < k0) continue;         // every query of the block precedes the wave's keys
-        tb_f4 s[2], dp[2];
+    for (int blk = 0; blk < 2; ++blk) {
+      const int i0 = qb + 32 * blk;
+      if (i0 >= a.T || k0 >= a.T) break;
+      if (i0 + 31 < k0) continue;           // every query of the block precedes the wave's keys
+      tb_f4 s[KG][2], dp[KG][2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint16_t* qr = sQ + (32 * blk + 16 * c + l16) * LD + 8 * g;
-          const uint16_t* orow = sO + (32 * blk + 16 * c + l16) * LD + 8 * g;
-          s[c] = tb_f4{0.f, 0.f, 0.f, 0.f};
-          dp[c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 2; ++c) {
+        const uint16_t* qr = sQ + (32 * blk + 16 * c + l16) * LD + 8 * g;
+        const uint16_t* orow = sO + (32 * blk + 16 * c + l16) * LD + 8 * g;
 #pragma unroll
-          for (int ks = 0; ks < K32; ++ks) {
-            s[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const tb_bf8*>(qr + 32 * ks), kf[ks],
-                                                           s[c], 0, 0, 0);
-            dp[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const tb_bf8*>(orow + 32 * ks), vf[ks],
-                                                            dp[c], 0, 0, 0);
+        for (int kg = 0; kg < KG; ++kg) {
+          s[kg][c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+          dp[kg][c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < K32; ++ks) {
+          const tb_bf8 qa = *reinterpret_cast<const tb_bf8*>(qr + 32 * ks);
+          const tb_bf8 oa = *reinterpret_cast<const tb_bf8*>(orow + 32 * ks);
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg) {
+            s[kg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kg][ks], s[kg][c], 0, 0, 0);
+            dp[kg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kg][ks], dp[kg][c], 0, 0, 0);
           }
         }
-        // element (c, e): query i0 + 16 c + 4 g + e, key `key`
-        float p[8], ds[8];
+      }
+      // element (c, e) of group kg: query i0 + 16 c + 4 g + e, key k0 + 16 kg + l16.
+      // A block with every query after every key of the wave, inside T, and
+      // all of its pairs either inside the window or past it takes no
+      // per-element test (the wave agrees on the branch).
+      const int klast = k0 + 16 * KG - 1;
+      const bool inside = i0 + 31 < a.T && klast < a.T && i0 >= klast;
+      const bool pen_all = i0 - klast >= a.w, pen_none = i0 + 31 - k0 < a.w;
+      tb_bf8 pA[KG], dA[KG];
+      if (inside && (pen_all || pen_none)) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int kg = 0; kg < KG; ++kg) {
+          const float pb = pen_all ? pen2[kg] : 0.0f;
+          float p[8], ds[8], dsum = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int rr = 32 * blk + 16 * c + 4 * g + e;
-            const int qi = qb + rr;
-            float pv = 0.0f, dsv = 0.0f;
-            if (qi < a.T && key_ok && qi >= key) {
-              const bool penalised = qi - key >= a.w;
-              pv = __builtin_amdgcn_exp2f(s[c][e] * sl2 + (penalised ? pen2 : 0.0f) - sL[rr]);
-              dsv = pv * (dp[c][e] - sDl[rr]);
-              if (penalised) dyacc += dsv;
+          for (int c = 0; c < 2; ++c) {
+            const float4 L4 = *reinterpret_cast<const float4*>(sL + 32 * blk + 16 * c + 4 * g);
+            const float4 D4 = *reinterpret_cast<const float4*>(sDl + 32 * blk + 16 * c + 4 * g);
+            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(fmaf(s[kg][c][e], sl2, pb - Lr[e]));
+              const float dsv = pv * (dp[kg][c][e] - Dr[e]);
+              dsum += dsv;
+              p[4 * c + e] = pv;
+              ds[4 * c + e] = dsv;
             }
-            p[4 * c + e] = pv;
-            ds[4 * c + e] = dsv;
           }
+          if (pen_all) dyacc[kg] += dsum;
+          pA[kg] = pack8(p);
+          dA[kg] = pack8(ds);
         }
-        const tb_bf8 pA = pack8(p), dA = pack8(ds);
-        // dV += P^T dO, dK += dS^T Q: B operands dO / Q at rows (query)
-        // 4 g + i and 16 + 4 g + i of the block, column 16 dt + l16
-        const int cofs = (32 * blk + 4 * g + (l16 >> 2)) * LD + 4 * (l16 & 3);
+      } else {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pA, lds_cols8<LD>(sO + cofs + 16 * dt), dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dA, lds_cols8<LD>(sQ + cofs + 16 * dt), dk[dt], 0, 0, 0);
+        for (int kg = 0; kg < KG; ++kg) {
+          const int key = k0 + 16 * kg + l16;
+          float p[8], ds[8];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rr = 32 * blk + 16 * c + 4 * g + e;
+              const int qi = qb + rr;
+              float pv = 0.0f, dsv = 0.0f;
+              if (qi < a.T && key < a.T && qi >= key) {
+                const bool penalised = qi - key >= a.w;
+                pv = __builtin_amdgcn_exp2f(s[kg][c][e] * sl2 + (penalised ? pen2[kg] : 0.0f) - sL[rr]);
+                dsv = pv * (dp[kg][c][e] - sDl[rr]);
+                if (penalised) dyacc[kg] += dsv;
+              }
+              p[4 * c + e] = pv;
+              ds[4 * c + e] = dsv;
+            }
+          }
+          pA[kg] = pack8(p);
+          dA[kg] = pack8(ds);
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q: B operands dO / Q at rows (query)
+      // 4 g + i and 16 + 4 g + i of the block, column 16 dt + l16
+      const int cofs = (32 * blk + 4 * g + (l16 >> 2)) * LD + 4 * (l16 & 3);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const tb_bf8 ob = lds_cols8<LD>(sO + cofs + 16 * dt);
+        const tb_bf8 qb8 = lds_cols8<LD>(sQ + cofs + 16 * dt);
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg) {
+          dv[kg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pA[kg], ob, dv[kg][dt], 0, 0, 0);
+          dk[kg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dA[kg], qb8, dk[kg][dt], 0, 0, 0);
         }
       }
     }
   }
   if (k0 >= a.T) return;
-  // dK, dV: element v of tile dt is key k0 + 4 g + v, dim 16 dt + l16
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int kg = 0; kg < KG; ++kg) {
+    // dK, dV: element v of tile dt is key k0 + 16 kg + 4 g + v, dim 16 dt + l16
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kk = k0 + 4 * g + e;
-      if (kk < a.T) {
-        const size_t r = ((static_cast<size_t>(b) * a.T + kk) * a.Hkv + kv) * D + 16 * dt + l16;
-        a.dk[r] = dk[dt][e] * a.scale;
-        a.dv[r] = dv[dt][e];
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = k0 + 16 * kg + 4 * g + e;
+        if (kk < a.T) {
+          const size_t r = ((static_cast<size_t>(b) * a.T + kk) * a.Hkv + kv) * D + 16 * dt + l16;
+          a.dk[r] = dk[kg][dt][e] * a.scale;
+          a.dv[r] = dv[kg][dt][e];
+        }
       }
     }
-  }
-  // dy: this lane's key summed over the four query groups (lanes l16 + 16 m)
-  dyacc += __shfl_xor(dyacc, 16);
-  dyacc += __shfl_xor(dyacc, 32);
-  if (g == 0 && key_ok) {
-    const float sig = 1.0f / (1.0f + __expf(-yk));
-    a.dy[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] = -sig * dyacc;
+    // dy: this lane's key summed over the four query groups (lanes l16 + 16 m)
+    float d = dyacc[kg];
+    d += __shfl_xor(d, 16);
+    d += __shfl_xor(d, 32);
+    const int key = k0 + 16 * kg + l16;
+    if (g == 0 && key < a.T) {
+      const float sig = 1.0f / (1.0f + __expf(-yk[kg]));
+      a.dy[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] = -sig * d;
+    }
   }
 }
 
@@ -303,7 +366,7 @@ __global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
   constexpr int LD = D + 16;
   __shared__ __align__(16) uint16_t sK[64 * LD];
   __shared__ __align__(16) uint16_t sV[64 * LD];
-  __shared__ float sP[64];
+  __shared__ __align__(16) float sP[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int row = blockIdx.x, b = row / a.Hq, h = row % a.Hq, kv = h / G;
@@ -365,20 +428,38 @@ __global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
                                                           dp[c], 0, 0, 0);
         }
       }
-      // element (c, e): key j0 + 16 c + 4 g + e, query qi
+      // element (c, e): key j0 + 16 c + 4 g + e, query qi.  A block with
+      // every key before every query of the wave, inside T, and all of its
+      // pairs either inside the window or past it takes no per-element test.
+      const bool inside = j0 + 31 < a.T && q0 + 15 < a.T && j0 + 31 <= q0;
+      const bool pen_all = q0 - (j0 + 31) >= a.w, pen_none = q0 + 15 - j0 < a.w;
       float ds[8];
+      if (inside && (pen_all || pen_none)) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 2; ++c) {
+          const float4 P4 = pen_all ? *reinterpret_cast<const float4*>(sP + 32 * blk + 16 * c + 4 * g)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float Pr[4] = {P4.x, P4.y, P4.z, P4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 32 * blk + 16 * c + 4 * g + e;
-          const int kj = kb + rr;
-          float dsv = 0.0f;
-          if (q_ok && kj < a.T && kj <= qi) {
-            const float pv = __builtin_amdgcn_exp2f(s[c][e] * sl2 - lse2 + (qi - kj >= a.w ? sP[rr] : 0.0f));
-            dsv = pv * (dp[c][e] - dlt);
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[c][e], sl2, Pr[e] - lse2));
+            ds[4 * c + e] = pv * (dp[c][e] - dlt);
           }
-          ds[4 * c + e] = dsv;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rr = 32 * blk + 16 * c + 4 * g + e;
+            const int kj = kb + rr;
+            float dsv = 0.0f;
+            if (q_ok && kj < a.T && kj <= qi) {
+              const float pv = __builtin_amdgcn_exp2f(s[c][e] * sl2 - lse2 + (qi - kj >= a.w ? sP[rr] : 0.0f));
+              dsv = pv * (dp[c][e] - dlt);
+            }
+            ds[4 * c + e] = dsv;
+          }
         }
       }
       const tb_bf8 dA = pack8(ds);
@@ -404,8 +485,10 @@ __global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
 
 template <int D, int G>
 void launch_bwd(const BwdArgs& a, hipStream_t st) {
+  constexpr int KG = kBwdKeyGroups;
   const int tiles = (a.T + 63) / 64;
-  hipLaunchKernelGGL((train_bwd_dkdv_kernel<D, G>), dim3(a.B * a.Hkv, tiles), dim3(256), 0, st, a);
+  const int ktiles = (a.T + 64 * KG - 1) / (64 * KG);
+  hipLaunchKernelGGL((train_bwd_dkdv_kernel<D, G, KG>), dim3(a.B * a.Hkv, ktiles), dim3(256), 0, st, a);
   hipLaunchKernelGGL((train_bwd_dq_kernel<D, G>), dim3(a.B * a.Hq, tiles), dim3(256), 0, st, a);
 }
 
