@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256, KG == 1 ? 2 : 1) void train_bwd_dkdv_kernel(Bw
 // wave takes the 32-key blocks that are causal for it.  Tiles with the most
 // keys (high tile index) are dispatched first.
 template <int D, int G>
-__global__ __launch_bounds__(256) void train_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void train_bwd_dq_kernel(BwdArgs a) {
   constexpr int K32 = D / 32;
   constexpr int DT = D / 16;
   constexpr int LD = D + 16;
