@@ -522,13 +522,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
         const float4 pa = *reinterpret_cast<const float4*>(b + S::PEN_OFF + 16 * G4);
         const float4 pb = *reinterpret_cast<const float4*>(b + S::PEN_OFF + 64 + 16 * G4);
         const float pens[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        // every pair causal and past the window (most blocks of a long
+        // sequence): the penalty alone, without per-element tests
+        const bool lane_pen = !lane_live || (lmax <= qmin && hmax <= qmin);
+        if (__all(lane_pen)) {
 #pragma unroll
-        for (int c = 0; c < S::NT; ++c) {
-          const int qp = qpos[c / S::HW];
+          for (int c = 0; c < S::NT; ++c)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = s[e >> 2][c][e & 3] + (qp >= his[e] ? pens[e] : 0.0f);
-            s[e >> 2][c][e & 3] = los[e] <= qp ? v : -INFINITY;
+            for (int e = 0; e < 8; ++e) s[e >> 2][c][e & 3] += pens[e];
+        } else {
+#pragma unroll
+          for (int c = 0; c < S::NT; ++c) {
+            const int qp = qpos[c / S::HW];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = s[e >> 2][c][e & 3] + (qp >= his[e] ? pens[e] : 0.0f);
+              s[e >> 2][c][e & 3] = los[e] <= qp ? v : -INFINITY;
+            }
           }
         }
       } else {
