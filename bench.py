@@ -508,6 +508,9 @@ def run_train_fwd(args, dms, torch):
         "bwd_useful_tflop": useful_bwd / 1e12,
         "bwd_tflops": useful_bwd / (bwd_ms * 1e-3) / 1e12,
         "bwd_frac_bf16_peak": useful_bwd / (bwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        # one layer's attention training step: gate, forward and backward
+        "step_ms": gate_ms + attn_ms + bwd_ms,
+        "step_tok_s": B * T / ((gate_ms + attn_ms + bwd_ms) * 1e-3),
     }
 
 
@@ -672,7 +675,7 @@ def main() -> int:
         train = run_train_fwd(args, dms, torch)
         log(f"training forward: {train['attn_ms']:.3f} ms attention = {train['attn_tflops']:.1f} TFLOP/s, "
             f"gate {train['gate_ms'] * 1e3:.1f} us; backward {train['bwd_ms']:.3f} ms = "
-            f"{train['bwd_tflops']:.1f} TFLOP/s")
+            f"{train['bwd_tflops']:.1f} TFLOP/s; step {train['step_ms']:.3f} ms = {train['step_tok_s'] / 1e6:.2f} M tok/s")
     others = None
     if not args.no_prefill:
         # Llama-3.2-1B has 16 layers; the fp8 serving figure rotates 4 layer caches

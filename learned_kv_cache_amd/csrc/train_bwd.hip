@@ -122,9 +122,9 @@ __global__ __launch_bounds__(256) void train_bwd_delta_kernel(BwdArgs a) {
 
 // Rows [r0, r0 + 64) of one head of a [B][T][H][D] bf16 tensor, staged in
 // two steps so that the next tile's global loads run under the current
-// tile's products: fetch_rows reads this thread's 16-byte chunks into
-// registers (rows past T are zero), put_rows writes them to LDS rows of
-// stride D + 16 elements.  With rows of 2 D + 32 bytes both the 16-byte row
+// tile's products: fetch reads this thread's 16-byte chunks into registers
+// (rows past T are zero), put writes them to LDS rows of stride D + 16
+// elements.  With rows of 2 D + 32 bytes both the 16-byte row
 // reads and the transposing column reads are free of bank conflicts.
 template <int D>
 struct TileRows {
