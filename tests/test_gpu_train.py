@@ -134,7 +134,7 @@ def test_train_gate():
 # ---------------------------------------------------------------------------
 # backward
 
-def _bwd(torch, q, k, v, y, w, dout):
+def _bwd(torch, q, k, v, y, w, dout, scale=0.0):
     from learned_kv_cache_amd import dms
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -142,12 +142,12 @@ def _bwd(torch, q, k, v, y, w, dout):
     yd = to_dev(y, "f32")
     out = torch.empty_like(qd)
     lse = torch.empty(B, Hq, T, dtype=torch.float32, device="cuda")
-    dms.dms_train_attn_fwd(qd, kd, vd, yd, out, lse, window=w)
+    dms.dms_train_attn_fwd(qd, kd, vd, yd, out, lse, window=w, softmax_scale=scale)
     dq = torch.empty(B, T, Hq, D, dtype=torch.float32, device="cuda")
     dk = torch.empty(B, T, Hkv, D, dtype=torch.float32, device="cuda")
     dv = torch.empty_like(dk)
     dy = torch.empty(B, Hkv, T, dtype=torch.float32, device="cuda")
-    dms.dms_train_attn_bwd(qd, kd, vd, out, dod, yd, lse, dq, dk, dv, dy, window=w)
+    dms.dms_train_attn_bwd(qd, kd, vd, out, dod, yd, lse, dq, dk, dv, dy, window=w, softmax_scale=scale)
     torch.cuda.synchronize()
     return [from_dev(x) for x in (dq, dk, dv, dy)]
 
@@ -158,6 +158,18 @@ def _bwd(torch, q, k, v, y, w, dout):
 # is a few 2^-9 of the magnitudes summed into it: 2e-2 of the tensor's
 # largest entry at most, 2e-3 on average.
 GRAD_TOL = (2e-2, 2e-3)
+# The largest reference entry is taken as at least GRAD_FLOOR: where every
+# exact gradient vanishes (one token: P = 1 so dS = dP - delta = 0; a window
+# covering every pair: no gate gradient), what is left is fp32 rounding of
+# dP and delta (magnitudes below 16, so about 1e-6), far below 2e-2 * 5e-3.
+GRAD_FLOOR = 5e-3
+
+
+def _grad_check(what, name, got, ref, floor=GRAD_FLOOR):
+    scale = max(float(np.abs(ref).max()), floor)
+    err = np.abs(got - ref)
+    log(f"{what} {name}: max |ref| {float(np.abs(ref).max()):.3g}, err max {err.max():.2e} mean {err.mean():.2e}")
+    assert err.max() <= GRAD_TOL[0] * scale and err.mean() <= GRAD_TOL[1] * scale, (what, name)
 
 BWD_SHAPES = [
     (8, 2, 128, 333, 48),
@@ -179,10 +191,39 @@ def test_train_attn_bwd_shapes(shape):
     got = _bwd(torch, q, k, v, y, w, dout)
     ref = tor.train_attention_backward(q, k, v, y, w, dout)
     for name, g_, r_ in zip(("dq", "dk", "dv", "dgate"), got, ref):
-        scale = float(np.abs(r_).max())          # 0 for the gate when the window covers every pair
-        err = np.abs(g_ - r_)
-        log(f"bwd {shape} {name}: max |ref| {scale:.3g}, err max {err.max():.2e} mean {err.mean():.2e}")
-        assert err.max() <= GRAD_TOL[0] * scale and err.mean() <= GRAD_TOL[1] * scale, (shape, name)
+        _grad_check(f"bwd {shape}", name, g_, r_)
+
+
+# degenerate and small cases: one token; a window of one (every pair off the
+# diagonal penalised); fewer tokens than one 16-row block; a non-default
+# softmax scale; penalties at both extremes (nothing and everything evicted)
+BWD_EDGE = [
+    # (Hq, Hkv, D, T, w, scale, y mean)
+    (2, 2, 64, 1, 1, 0.0, 0.0),
+    (4, 1, 128, 17, 1, 0.0, 0.0),
+    (1, 1, 64, 5, 3, 0.0, 0.0),
+    (4, 2, 128, 70, 8, 0.05, 0.0),
+    (4, 2, 64, 90, 8, 0.0, -30.0),
+    (4, 2, 64, 90, 8, 0.0, 30.0),
+]
+
+
+@pytest.mark.parametrize("case", BWD_EDGE, ids=[f"hq{c[0]}_hkv{c[1]}_d{c[2]}_t{c[3]}_w{c[4]}_s{c[5]}_y{c[6]}"
+                                               for c in BWD_EDGE])
+def test_train_attn_bwd_edge_cases(case):
+    torch = _torch()
+    Hq, Hkv, D, T, w, scale, ym = case
+    gen = np.random.default_rng(BWD_EDGE.index(case) + 950)
+    B = 2
+    q, k, v = _bf16(gen, (B, T, Hq, D)), _bf16(gen, (B, T, Hkv, D)), _bf16(gen, (B, T, Hkv, D))
+    y = (ym + gen.normal(0.0, 3.0, (B, Hkv, T))).astype(np.float32)
+    dout = _bf16(gen, (B, T, Hq, D))
+    got = _bwd(torch, q, k, v, y, w, dout, scale)
+    ref = tor.train_attention_backward(q, k, v, y, w, dout, scale=scale if scale > 0 else None)
+    for name, g_, r_ in zip(("dq", "dk", "dv", "dgate"), got, ref):
+        # at the extreme penalties the gate gradient is ~1e-9 (sigmoid(-30),
+        # or P ~ e^-30): checked against its own scale, with no floor
+        _grad_check(f"bwd edge {case}", name, g_, r_, 0.0 if name == "dgate" and ym != 0.0 else GRAD_FLOOR)
 
 
 def test_train_attn_bwd_qwen3_8b_shape_groups():
@@ -204,8 +245,4 @@ def test_train_attn_bwd_qwen3_8b_shape_groups():
                                            y[b:b + 1, ks], w, dout[b:b + 1, :, hs])
         mine = (got[0][b:b + 1, :, hs], got[1][b:b + 1, :, ks], got[2][b:b + 1, :, ks], got[3][b:b + 1, ks])
         for name, g_, r_ in zip(("dq", "dk", "dv", "dgate"), mine, ref):
-            scale = float(np.abs(r_).max())
-            err = np.abs(g_ - r_)
-            log(f"bwd full shape (b {b}, kv {kv}) {name}: max |ref| {scale:.3g}, err max {err.max():.2e} "
-                f"mean {err.mean():.2e}")
-            assert err.max() <= GRAD_TOL[0] * scale and err.mean() <= GRAD_TOL[1] * scale, (b, kv, name)
+            _grad_check(f"bwd full shape (b {b}, kv {kv})", name, g_, r_)
