@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, KG == 1 ? 2 : 1) void train_bwd_dkdv_kernel(Bw
       nqb += 64;
     }
     if (nqb < a.T) fetch(nqb, kv * G + nhh);
-#pragma unroll 1
+#pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int i0 = qb + 32 * blk;
       if (i0 >= a.T || k0 >= a.T) break;
