@@ -133,21 +133,23 @@ struct TileRows {
   static constexpr int NIT = 64 * CH / 256; // chunks per thread
   uint4 r[NIT];
   __device__ __forceinline__ void fetch(const uint16_t* src, int b, int r0, int T, int H, int h) {
+    // row r0 + row of head h is base + row * stride; this thread's rows are
+    // threadIdx.x / CH + (256 / CH) it, its column (threadIdx.x % CH) * 8
+    const size_t stride = static_cast<size_t>(H) * D;
+    const int row0 = threadIdx.x / CH;
+    const uint16_t* p = src + (static_cast<size_t>(b) * T + r0 + row0) * stride + static_cast<size_t>(h) * D +
+                        (threadIdx.x % CH) * 8;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int c = threadIdx.x + 256 * it;
-      const int t = r0 + c / CH;
-      r[it] = t < T ? *reinterpret_cast<const uint4*>(src + ((static_cast<size_t>(b) * T + t) * H + h) * D +
-                                                       (c % CH) * 8)
-                    : make_uint4(0u, 0u, 0u, 0u);
+      const int row = row0 + (256 / CH) * it;
+      r[it] = r0 + row < T ? *reinterpret_cast<const uint4*>(p + static_cast<size_t>((256 / CH) * it) * stride)
+                           : make_uint4(0u, 0u, 0u, 0u);
     }
   }
   __device__ __forceinline__ void put(uint16_t* dst) const {
+    uint16_t* p = dst + (threadIdx.x / CH) * LD + (threadIdx.x % CH) * 8;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int c = threadIdx.x + 256 * it;
-      *reinterpret_cast<uint4*>(dst + (c / CH) * LD + (c % CH) * 8) = r[it];
-    }
+    for (int it = 0; it < NIT; ++it) *reinterpret_cast<uint4*>(p + (256 / CH) * it * LD) = r[it];
   }
 };
 
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(256, 3) void train_bwd_dq_kernel(BwdArgs a) {
     if (threadIdx.x < 64) sP[threadIdx.x] = npen;
     __syncthreads();
     if (kb + 64 < kend) fetch(kb + 64);
-#pragma unroll 1
+#pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int j0 = kb + 32 * blk;
       if (j0 >= a.T || j0 > q0 + 15 || q0 >= a.T) break;   // keys past every query of the wave
