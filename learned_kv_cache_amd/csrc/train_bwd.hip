@@ -230,20 +230,24 @@ __global__ __launch_bounds__(256, KG == 1 ? 2 : 1) void train_bwd_dkdv_kernel(Bw
       nqb += 64;
     }
     if (nqb < a.T) fetch(nqb, kv * G + nhh);
+    // both blocks' score products first, so that the second block's run on
+    // the matrix cores while the first block's P and dS are formed
+    bool act[2];
+    tb_f4 sb[2][KG][2], dpb[2][KG][2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int i0 = qb + 32 * blk;
-      if (i0 >= a.T || k0 >= a.T) break;
-      if (i0 + 31 < k0) continue;           // every query of the block precedes the wave's keys
-      tb_f4 s[KG][2], dp[KG][2];
+      // skipped: past T, or every query of the block before the wave's keys
+      act[blk] = i0 < a.T && k0 < a.T && i0 + 31 >= k0;
+      if (!act[blk]) continue;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const uint16_t* qr = sQ + (32 * blk + 16 * c + l16) * LD + 8 * g;
         const uint16_t* orow = sO + (32 * blk + 16 * c + l16) * LD + 8 * g;
 #pragma unroll
         for (int kg = 0; kg < KG; ++kg) {
-          s[kg][c] = tb_f4{0.f, 0.f, 0.f, 0.f};
-          dp[kg][c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+          sb[blk][kg][c] = tb_f4{0.f, 0.f, 0.f, 0.f};
+          dpb[blk][kg][c] = tb_f4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int ks = 0; ks < K32; ++ks) {
@@ -251,11 +255,18 @@ __global__ __launch_bounds__(256, KG == 1 ? 2 : 1) void train_bwd_dkdv_kernel(Bw
           const tb_bf8 oa = *reinterpret_cast<const tb_bf8*>(orow + 32 * ks);
 #pragma unroll
           for (int kg = 0; kg < KG; ++kg) {
-            s[kg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kg][ks], s[kg][c], 0, 0, 0);
-            dp[kg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kg][ks], dp[kg][c], 0, 0, 0);
+            sb[blk][kg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kg][ks], sb[blk][kg][c], 0, 0, 0);
+            dpb[blk][kg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kg][ks], dpb[blk][kg][c], 0, 0, 0);
           }
         }
       }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      if (!act[blk]) continue;
+      const int i0 = qb + 32 * blk;
+      const auto& s = sb[blk];
+      const auto& dp = dpb[blk];
       // element (c, e) of group kg: query i0 + 16 c + 4 g + e, key k0 + 16 kg + l16.
       // A block with every query after every key of the wave, inside T, and
       // all of its pairs either inside the window or past it takes no
