@@ -322,7 +322,8 @@ int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_heads, int head
                        const void* dout, const float* gate_logits, const float* lse, void* dq, void* dk,
                        void* dv, float* dgate, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of dms_train_attn_bwd (one float per query row and head). */
+/* Workspace bytes of dms_train_attn_bwd (two floats per query row and head: the
+ * rows' rowsum(dO * O), then the keys' penalties). */
 int dms_train_attn_bwd_workspace_bytes(int B, int T, int num_q_heads, size_t* bytes);
 
 /* ---- KVzap scorers ("动态内存稀疏化（DMS）策略：KVzap-linear-Llama-3.1-8B-Instruct的核心创新点",

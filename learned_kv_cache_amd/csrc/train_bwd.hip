@@ -9,7 +9,8 @@
 //   query heads of their group),
 //   dy_j = -sigmoid(y_j) * sum of dS_ij over the penalised pairs (i - j >= w).
 //
-// Three kernels: delta (D / 8 lanes per query row and head); dk/dv/dy, one
+// Three kernels: delta (D / 8 lanes per query row and head; it also turns
+// each gate logit into its penalty logsigmoid(-y) once); dk/dv/dy, one
 // workgroup per 64 keys of a (sequence, KV head), each wave owning 16 keys
 // whose K and V fragments stay in registers while the workgroup stages the
 // Q and dO rows of each 64-query tile (for every query head of the group) in
@@ -49,6 +50,7 @@ struct BwdArgs {
   const float* y;         // gate logits [B][Hkv][T]
   const float* lse;       // forward log-sum-exp [B][Hq][T]
   float* delta;           // [B][Hq][T] (written by the first kernel)
+  float* pen;             // [B][Hkv][T]: logsigmoid(-y) * log2(e) (written by the first kernel)
   float* dq;              // [B][T][Hq][D] f32
   float* dk;              // [B][T][Hkv][D] f32
   float* dv;
@@ -112,6 +114,9 @@ __global__ __launch_bounds__(256) void train_bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  // the keys' penalties, once per (b, kv, t), for the two gradient kernels
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid < static_cast<int64_t>(a.B) * a.Hkv * a.T) a.pen[gid] = penalty(a.y[gid]) * kLog2e;
   if (r < rows && part == 0) {
     const int h = static_cast<int>(r % a.Hq);
     const int64_t bt = r / a.Hq;
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(256, KG == 1 ? 2 : 1) void train_bwd_dkdv_kernel(Bw
       vf[kg][ks] = load8(a.v + krow + 32 * ks + 8 * g, ok);
     }
     yk[kg] = ok ? a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] : 0.0f;
-    pen2[kg] = penalty(yk[kg]) * kLog2e;
+    pen2[kg] = ok ? a.pen[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + key] : 0.0f;
   }
   tb_f4 dk[KG][DT], dv[KG][DT];
 #pragma unroll
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(256, 3) void train_bwd_dq_kernel(BwdArgs a) {
     nv.fetch(a.v, b, kb, a.T, a.Hkv, kv);
     const int t = kb + threadIdx.x;
     if (threadIdx.x < 64)
-      npen = t < a.T ? penalty(a.y[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + t]) * kLog2e : 0.0f;
+      npen = t < a.T ? a.pen[(static_cast<int64_t>(b) * a.Hkv + kv) * a.T + t] : 0.0f;
   };
   if (kend > 0) fetch(0);
   for (int kb = 0; kb < kend; kb += 64) {
@@ -522,7 +527,7 @@ using namespace dms;
 
 extern "C" int dms_train_attn_bwd_workspace_bytes(int B, int T, int num_q_heads, size_t* bytes) {
   if (!bytes || B < 0 || T < 0 || num_q_heads <= 0) return fail(DMS_ERR_ARG, "bad sizes or NULL bytes");
-  *bytes = static_cast<size_t>(B) * T * num_q_heads * sizeof(float);
+  *bytes = 2 * static_cast<size_t>(B) * T * num_q_heads * sizeof(float);   // delta, then the key penalties
   return DMS_OK;
 }
 
@@ -536,7 +541,7 @@ extern "C" int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_head
   if (B == 0 || T == 0) return DMS_OK;
   if (!q || !k || !v || !out || !dout || !gate_logits || !lse || !dq || !dk || !dv || !dgate)
     return fail(DMS_ERR_ARG, "every tensor argument is required");
-  const size_t need = static_cast<size_t>(B) * T * num_q_heads * sizeof(float);
+  const size_t need = 2 * static_cast<size_t>(B) * T * num_q_heads * sizeof(float);
   if (!workspace || workspace_bytes < need)
     return fail(DMS_ERR_CAPACITY, "workspace smaller than dms_train_attn_bwd_workspace_bytes");
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
@@ -552,6 +557,7 @@ extern "C" int dms_train_attn_bwd(int B, int T, int num_q_heads, int num_kv_head
   a.y = gate_logits;
   a.lse = lse;
   a.delta = static_cast<float*>(workspace);
+  a.pen = a.delta + static_cast<size_t>(B) * T * num_q_heads;   // Hkv <= Hq keys per (b, t)
   a.dq = static_cast<float*>(dq);
   a.dk = static_cast<float*>(dk);
   a.dv = static_cast<float*>(dv);

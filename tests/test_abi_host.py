@@ -113,7 +113,7 @@ def test_training_scorer_and_accounting_arguments_fail_before_any_launch():
     assert L.dms_train_attn_fwd(1, 8, 4, 2, 128, 4, f, a8, a16, a16, a16, a16, a16, None) == dms.DMS_ERR_ARG
     # training backward and its workspace size
     n = ctypes.c_size_t()
-    assert L.dms_train_attn_bwd_workspace_bytes(2, 10, 4, ctypes.byref(n)) == dms.DMS_OK and n.value == 2 * 10 * 4 * 4
+    assert L.dms_train_attn_bwd_workspace_bytes(2, 10, 4, ctypes.byref(n)) == dms.DMS_OK and n.value == 2 * 2 * 10 * 4 * 4
     assert L.dms_train_attn_bwd_workspace_bytes(2, 10, 0, ctypes.byref(n)) == dms.DMS_ERR_ARG
     t11 = [a16] * 11                    # q k v out dout y lse dq dk dv dgate
     ws = (a16, ctypes.c_size_t(1 << 20))
