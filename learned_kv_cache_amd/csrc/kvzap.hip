@@ -192,38 +192,36 @@ __global__ __launch_bounds__(kSmallThreads) void kz_linear_small_kernel(KzArgs a
   }
 }
 
-// Linear scorer: TT tokens per 256-thread workgroup; thread t owns elements
-// [4t + 1024i, 4t + 1024i + 4) and keeps its W values in registers for the
-// TT tokens; waves reduce with shuffles, the four waves through LDS.
-// HKV bounds the heads (a.Hkv <= HKV).
-template <typename ACT, int HKV, int TT>
-__global__ __launch_bounds__(256) void kz_linear_kernel(KzArgs a) {
-  __shared__ float s_red[4][TT][HKV];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok0 = blockIdx.x * TT;
-  float acc[TT * HKV];
-#pragma unroll
-  for (int i = 0; i < TT * HKV; ++i) acc[i] = 0.0f;
-  for (int m = 4 * tid; m < a.H; m += 1024) {
-    float4 w[HKV];
-#pragma unroll
-    for (int k = 0; k < HKV; ++k)
-      w[k] = k < a.Hkv ? *reinterpret_cast<const float4*>(a.W1 + static_cast<size_t>(k) * a.H + m)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (tok0 + t < a.N) load4<ACT>(static_cast<const ACT*>(a.hidden) + static_cast<size_t>(tok0 + t) * a.H + m, x);
-#pragma unroll
-      for (int k = 0; k < HKV; ++k) {
-        float& c = acc[t * HKV + k];
-        c = fmaf(w[k].x, x[0], c);
-        c = fmaf(w[k].y, x[1], c);
-        c = fmaf(w[k].z, x[2], c);
-        c = fmaf(w[k].w, x[3], c);
-      }
-    }
+// Four activations as loaded (bf16 pairs or f32), widened to f32 later.
+template <typename ACT> struct Raw4;
+template <> struct Raw4<float> {
+  typedef float4 T;
+  __device__ static T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static void widen(const T& v, float (&x)[4]) {
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
   }
+};
+template <> struct Raw4<uint16_t> {
+  typedef uint2 T;
+  __device__ static T zero() { return make_uint2(0u, 0u); }
+  __device__ static void widen(const T& v, float (&x)[4]) {
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  }
+};
+
+// The linear scorers' last step: each wave's TT x HKV partial dot products
+// summed over its lanes, the four waves' sums through LDS, then bias,
+// score and threshold for token tok0 + t and head k (one thread each).
+template <int HKV, int TT>
+__device__ __forceinline__ void kz_linear_finish(float (&acc)[TT * HKV], float (&s_red)[4][TT][HKV],
+                                                 const KzArgs& a, int tok0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if constexpr (TT * HKV == 64) {
     wave_reduce_scatter64(acc, lane);
     (&s_red[wave][0][0])[lane] = acc[0];
@@ -248,6 +246,92 @@ __global__ __launch_bounds__(256) void kz_linear_kernel(KzArgs a) {
   const size_t o = out_index(a, tok, k);
   if (a.scores) a.scores[o] = s;
   a.evict[o] = s < a.thr ? 1 : 0;
+}
+
+// Linear scorer: TT tokens per 256-thread workgroup; thread t owns elements
+// [4t + 1024i, 4t + 1024i + 4) and keeps its W values in registers for the
+// TT tokens; waves reduce with shuffles, the four waves through LDS.
+// HKV bounds the heads (a.Hkv <= HKV).
+template <typename ACT, int HKV, int TT>
+__global__ __launch_bounds__(256) void kz_linear_kernel(KzArgs a) {
+  __shared__ float s_red[4][TT][HKV];
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * TT;
+  float acc[TT * HKV];
+#pragma unroll
+  for (int i = 0; i < TT * HKV; ++i) acc[i] = 0.0f;
+  for (int m = 4 * tid; m < a.H; m += 1024) {
+    float4 w[HKV];
+#pragma unroll
+    for (int k = 0; k < HKV; ++k)
+      w[k] = k < a.Hkv ? *reinterpret_cast<const float4*>(a.W1 + static_cast<size_t>(k) * a.H + m)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (tok0 + t < a.N) load4<ACT>(static_cast<const ACT*>(a.hidden) + static_cast<size_t>(tok0 + t) * a.H + m, x);
+#pragma unroll
+      for (int k = 0; k < HKV; ++k) {
+        float& c = acc[t * HKV + k];
+        c = fmaf(w[k].x, x[0], c);
+        c = fmaf(w[k].y, x[1], c);
+        c = fmaf(w[k].z, x[2], c);
+        c = fmaf(w[k].w, x[3], c);
+      }
+    }
+  }
+  kz_linear_finish<HKV, TT>(acc, s_red, a, tok0);
+}
+
+// Linear scorer for H <= 1024 NS: as kz_linear_kernel, but every slab's
+// hidden-state loads are issued before the first product, so a thread's rows
+// arrive after one memory latency instead of one per slab (the grid holds
+// only a few waves per SIMD to hide them).
+template <typename ACT, int HKV, int TT, int NS>
+__global__ __launch_bounds__(256) void kz_linear_pre_kernel(KzArgs a) {
+  __shared__ float s_red[4][TT][HKV];
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * TT;
+  typedef typename Raw4<ACT>::T R;
+  R raw[NS][TT];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int m = 4 * tid + 1024 * sl;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      raw[sl][t] = (m < a.H && tok0 + t < a.N)
+                       ? *reinterpret_cast<const R*>(static_cast<const ACT*>(a.hidden) +
+                                                     static_cast<size_t>(tok0 + t) * a.H + m)
+                       : Raw4<ACT>::zero();
+  }
+  float acc[TT * HKV];
+#pragma unroll
+  for (int i = 0; i < TT * HKV; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int m = 4 * tid + 1024 * sl;
+    if (m < a.H) {
+      float4 w[HKV];
+#pragma unroll
+      for (int k = 0; k < HKV; ++k)
+        w[k] = k < a.Hkv ? *reinterpret_cast<const float4*>(a.W1 + static_cast<size_t>(k) * a.H + m)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        float x[4];
+        Raw4<ACT>::widen(raw[sl][t], x);
+#pragma unroll
+        for (int k = 0; k < HKV; ++k) {
+          float& c = acc[t * HKV + k];
+          c = fmaf(w[k].x, x[0], c);
+          c = fmaf(w[k].y, x[1], c);
+          c = fmaf(w[k].z, x[2], c);
+          c = fmaf(w[k].w, x[3], c);
+        }
+      }
+    }
+  }
+  kz_linear_finish<HKV, TT>(acc, s_red, a, tok0);
 }
 
 // MLP: s = b2 + the inner-unit workgroups' shares (a fixed order of
@@ -435,8 +519,14 @@ int launch_kvzap(const KzArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((kz_linear_small_kernel<ACT>), dim3(a.Hkv, (a.N + kSmallTokens - 1) / kSmallTokens),
                          dim3(kSmallThreads), 0, st, a);
     } else {
-      if (a.Hkv <= 8) hipLaunchKernelGGL((kz_linear_kernel<ACT, 8, 8>), dim3((a.N + 7) / 8), dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((kz_linear_kernel<ACT, 16, 4>), dim3((a.N + 3) / 4), dim3(256), 0, st, a);
+      if (a.H <= 4096) {
+        if (a.Hkv <= 8) hipLaunchKernelGGL((kz_linear_pre_kernel<ACT, 8, 8, 4>), dim3((a.N + 7) / 8), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((kz_linear_pre_kernel<ACT, 16, 4, 4>), dim3((a.N + 3) / 4), dim3(256), 0, st, a);
+      } else if (a.Hkv <= 8) {
+        hipLaunchKernelGGL((kz_linear_kernel<ACT, 8, 8>), dim3((a.N + 7) / 8), dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((kz_linear_kernel<ACT, 16, 4>), dim3((a.N + 3) / 4), dim3(256), 0, st, a);
+      }
     }
     return check_hip(hipGetLastError(), "kz_linear_kernel launch");
   }

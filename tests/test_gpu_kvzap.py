@@ -94,16 +94,18 @@ def _check(got_s, got_e, ref, what):
         assert 0.2 < frac < 0.8
 
 
-# (B, T, Hkv, dtype)
-LINEAR = [(1, 1, 8, "bf16"), (2, 37, 8, "bf16"), (3, 700, 8, "bf16"), (1, 2100, 16, "bf16"), (2, 45, 3, "f32"),
-          (1, 333, 16, "f32")]
+# (B, T, Hkv, dtype, H): H 4096 as on the pages; 2080 ends in a partial
+# 1024-element slab; 5120 is past the four slabs whose rows are loaded
+# before the first product (the per-slab kernel)
+LINEAR = [(1, 1, 8, "bf16", 4096), (2, 37, 8, "bf16", 4096), (3, 700, 8, "bf16", 4096), (1, 2100, 16, "bf16", 4096),
+          (2, 45, 3, "f32", 4096), (1, 333, 16, "f32", 4096), (2, 300, 8, "bf16", 2080), (1, 200, 16, "f32", 2080),
+          (2, 150, 8, "bf16", 5120), (1, 90, 16, "f32", 5120)]
 
 
-@pytest.mark.parametrize("case", LINEAR, ids=[f"b{c[0]}_t{c[1]}_hkv{c[2]}_{c[3]}" for c in LINEAR])
+@pytest.mark.parametrize("case", LINEAR, ids=[f"b{c[0]}_t{c[1]}_hkv{c[2]}_{c[3]}_h{c[4]}" for c in LINEAR])
 def test_kvzap_linear(case):
     torch = _torch()
-    B, T, Hkv, dtype = case
-    H = 4096
+    B, T, Hkv, dtype, H = case
     gen = np.random.default_rng(900 + LINEAR.index(case))
     h = _hidden(gen, (B, T, H), dtype)
     W1, _, _, _ = _weights(gen, H, Hkv, 0)
