@@ -9,7 +9,9 @@ Scores within 2e-4 absolute of the float64 oracle (fp32 accumulation over
 H = 4096 terms of unit-scale products: ~1e-5); decisions equal wherever the
 oracle's score is more than 1e-3 from the threshold (at least 99.5% of them).
 Shapes: linear with 3, 8 and 16 heads, bf16 and f32 hidden states, 1 to 2100
-tokens (both workgroup shapes, ragged tails); the MLP 4096 -> 512 -> 8 of the
+tokens (both workgroup shapes, ragged tails), hidden sizes 4096, 2080 (a
+partial last slab of 1024 elements) and 5120 (past the slabs whose rows load
+before the first product); the MLP 4096 -> 512 -> 8 of the
 KVzap-mlp page at 1, 8, 16 tokens (the decode-size path), 17 and 600 tokens
 and a 4096-token prefill chunk (the matrix-core path, ragged token tiles);
 MLP scores are bit-identical from one call to the next.
