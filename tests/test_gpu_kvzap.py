@@ -11,7 +11,8 @@ oracle's score is more than 1e-3 from the threshold (at least 99.5% of them).
 Shapes: linear with 3, 8 and 16 heads, bf16 and f32 hidden states, 1 to 2100
 tokens (both workgroup shapes, ragged tails), hidden sizes 4096, 2080 (a
 partial last slab of 1024 elements) and 5120 (past the slabs whose rows load
-before the first product); the MLP 4096 -> 512 -> 8 of the
+before the first product); the MLP 2080 -> 192 -> 8 at 4, 70 and 300 tokens
+(ragged 32-column stages, three 64-unit groups) and the MLP 4096 -> 512 -> 8 of the
 KVzap-mlp page at 1, 8, 16 tokens (the decode-size path), 17 and 600 tokens
 and a 4096-token prefill chunk (the matrix-core path, ragged token tiles);
 MLP scores are bit-identical from one call to the next.
@@ -101,7 +102,7 @@ def _check(got_s, got_e, ref, what):
 # before the first product (the per-slab kernel)
 LINEAR = [(1, 1, 8, "bf16", 4096), (2, 37, 8, "bf16", 4096), (3, 700, 8, "bf16", 4096), (1, 2100, 16, "bf16", 4096),
           (2, 45, 3, "f32", 4096), (1, 333, 16, "f32", 4096), (2, 300, 8, "bf16", 2080), (1, 200, 16, "f32", 2080),
-          (2, 150, 8, "bf16", 5120), (1, 90, 16, "f32", 5120)]
+          (2, 150, 8, "bf16", 5120), (1, 90, 16, "f32", 5120), (1, 5, 8, "bf16", 2080)]
 
 
 @pytest.mark.parametrize("case", LINEAR, ids=[f"b{c[0]}_t{c[1]}_hkv{c[2]}_{c[3]}_h{c[4]}" for c in LINEAR])
@@ -117,16 +118,20 @@ def test_kvzap_linear(case):
     _check(got_s, got_e, kz.scores_linear(h, W1, b1), f"linear {case}")
 
 
-# (B, T, dtype)
-MLP = [(1, 1, "bf16"), (8, 1, "bf16"), (2, 8, "bf16"), (1, 17, "bf16"), (2, 300, "bf16"), (1, 4096, "bf16"),
-       (3, 5, "f32"), (1, 100, "f32")]
+# (B, T, dtype, H, Hm): the KVzap-mlp page's 4096 -> 512 -> 8, and a hidden
+# size of 2080 with an inner width of 192 (neither a power of two: ragged
+# 32-column stages of h, three 64-unit groups)
+MLP = [(1, 1, "bf16", 4096, 512), (8, 1, "bf16", 4096, 512), (2, 8, "bf16", 4096, 512),
+       (1, 17, "bf16", 4096, 512), (2, 300, "bf16", 4096, 512), (1, 4096, "bf16", 4096, 512),
+       (3, 5, "f32", 4096, 512), (1, 100, "f32", 4096, 512), (2, 4, "bf16", 2080, 192),
+       (2, 150, "bf16", 2080, 192), (1, 70, "f32", 2080, 192)]
 
 
-@pytest.mark.parametrize("case", MLP, ids=[f"b{c[0]}_t{c[1]}_{c[2]}" for c in MLP])
+@pytest.mark.parametrize("case", MLP, ids=[f"b{c[0]}_t{c[1]}_{c[2]}_h{c[3]}_m{c[4]}" for c in MLP])
 def test_kvzap_mlp(case):
     torch = _torch()
-    B, T, dtype = case
-    H, Hm, Hkv = 4096, 512, 8
+    B, T, dtype, H, Hm = case
+    Hkv = 8
     gen = np.random.default_rng(950 + MLP.index(case))
     h = _hidden(gen, (B, T, H), dtype)
     W1, b1, W2, _ = _weights(gen, H, Hkv, Hm)
