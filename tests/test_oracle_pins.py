@@ -372,3 +372,126 @@ def test_pages_needed_worst_hand_case():
     assert oracle.pages_needed_worst(sim, 0, 6) == 2
     # capacity
     assert oracle.pages_needed_worst(sim, 0, 95) == -1
+
+
+def _rows(mags, D=4):
+    """[T, D] rows whose largest magnitude is mags[t] (held by one element, the
+    others smaller), alternating signs so the amax is taken over |x|."""
+    out = np.zeros((len(mags), D))
+    for t, m in enumerate(mags):
+        out[t] = [m * 0.25, -m * 0.5, (-1) ** t * m, m * 0.125]
+    return out
+
+
+def test_fp8_page_scale_rule_hand_worked():
+    _check_fp8_page_scale_rule(oracle.CacheSim)
+
+
+def _check_fp8_page_scale_rule(sim_cls):
+    """Which values set a fresh page's K and V scale (reading R19; the pages only say
+    FP8 storage follows eviction — FastDMS post, FP8 compact KV).
+
+    Window 3, block 2, one sequence, two heads.  First call, six tokens; head 0
+    marks token 0 only:
+      t0 -> slot 0 (opens page 0), t1 -> slot 1, t2 -> slot 2 (opens page 1),
+      t3 overwrites slot 0 in place (token 0 was marked), t4 -> slot 3,
+      t5 -> slot 4 (opens page 2).
+    Final occupants: page 0 = {t3, t1}, page 1 = {t2, t4}, page 2 = {t5}.
+    Token 0 was written and overwritten inside the call, so its huge K (1000)
+    must not set page 0's scale.  Head 1 keeps everything: pages 3, 4, 5.
+    Scale = 4 * (smallest power of two s with amax <= 448 s):
+      page 0: K amax max(3, 10) = 10   -> s 2^-5 -> 2^-3;  V amax max(200, 1) = 200 -> 2^-1 -> 2
+              (with token 0 counted K would be 16; with K and V swapped K would be 2)
+      page 1: K amax 0.7 -> 2^-9 -> 2^-7;                 V amax 50 -> 2^-3 -> 2^-1
+      page 2: K amax 448 -> 1 -> 4 (exactly at the bound); V amax 448.01 -> 2 -> 8
+      head 1: K amax 1 -> 2^-8 -> 2^-6;                   V amax 2 -> 2^-7 -> 2^-5
+    Second call (one token, t6, head 0): token 3 (w back) is kept, so t6 takes
+    slot 5 of page 2 and reuses page 2's scales (4, 8) although its K is 5000
+    (saturates); head 1 opens page 6 in that call.  Third call (t7): head 0's
+    slot 6 opens page 7, with scales from t7 alone.
+    """
+    w, P, Hkv, D = 3, 2, 2, 4
+    sim = sim_cls(1, Hkv, w, P, max_tokens=16, pool_pages=32, fp8=True)
+    k = np.zeros((1, 6, Hkv, D))
+    v = np.zeros((1, 6, Hkv, D))
+    k[0, :, 0] = _rows([1000.0, 3.0, 0.3, 10.0, 0.7, 448.0])
+    v[0, :, 0] = _rows([0.5, 200.0, 50.0, 1.0, 5.0, 448.01])
+    k[0, :, 1] = _rows([1.0] * 6)
+    v[0, :, 1] = _rows([2.0] * 6)
+    e = np.zeros((1, Hkv, 6), np.uint8)
+    e[0, 0, 0] = 1
+    sim.append([0], e, k, v)
+    assert sim.pages[0][0] == [0, 1, 2] and sim.pages[0][1] == [3, 4, 5]
+    assert sim.slot_table(0, 0).tolist() == [3, 1, 2, 4, 5]
+    assert sim.page_scale[0] == (2.0 ** -3, 2.0)
+    assert sim.page_scale[1] == (2.0 ** -7, 0.5)
+    assert sim.page_scale[2] == (4.0, 8.0)
+    for pg in (3, 4, 5):
+        assert sim.page_scale[pg] == (2.0 ** -6, 2.0 ** -5)
+    # what attention reads: K through the K scale, V through the V scale
+    kk = oracle.effective_kv(sim, 0, 0, k[0, :, 0], 0)
+    vv = oracle.effective_kv(sim, 0, 0, v[0, :, 0], 1)
+    # t1's V element -200 / 2 = -100 lies halfway between the e4m3 values 96 and 104:
+    # ties go to the even code (96), so the stored value is -192; with the K scale
+    # (1/8) it would saturate at -448 / 8 = -56.
+    assert vv[1, 2] == -192.0
+    # t3's K element 10 / 2^-3 = 80 is exact in e4m3
+    assert kk[3, 2] == -10.0
+    # t2's K element 0.3 through 2^-7: 38.4 -> nearest e4m3 value 40 -> 0.3125
+    # (through page 1's V scale 1/2 it would be 0.3 / 0.5 = 0.6 -> 0.625 * 0.5 = 0.3125 too,
+    # which is why the V check above carries the swap test)
+    assert kk[2, 2] == 0.3125
+    # second call: t6 into slot 5 of page 2 with page 2's scales, K saturates at 448 * 4
+    k6 = np.zeros((1, 1, Hkv, D))
+    v6 = np.zeros((1, 1, Hkv, D))
+    k6[0, 0, 0] = _rows([5000.0])[0]
+    v6[0, 0, 0] = _rows([1.0])[0]
+    k6[0, 0, 1] = _rows([1.0])[0]
+    v6[0, 0, 1] = _rows([2.0])[0]
+    sim.append([0], np.zeros((1, Hkv, 1), np.uint8), k6, v6)
+    assert sim.slot_of[0][0][6] == 5 and sim.pages[0][0] == [0, 1, 2]
+    assert sim.page_scale[2] == (4.0, 8.0)
+    assert sim.tok_scale[0][0][6] == (4.0, 8.0)
+    # head 1 opened page 6 (slot 6 of a kept-everything head) from its own values
+    assert sim.pages[0][1] == [3, 4, 5, 6] and sim.page_scale[6] == (2.0 ** -6, 2.0 ** -5)
+    full_k = np.concatenate([k[0, :, 0], k6[0, :, 0]])
+    assert oracle.effective_kv(sim, 0, 0, full_k, 0)[6, 2] == 1792.0
+    # third call: t7 takes slot 6 of head 0, opening page 7, scales from t7 alone
+    k7 = np.zeros((1, 1, Hkv, D))
+    v7 = np.zeros((1, 1, Hkv, D))
+    k7[0, 0, 0] = _rows([0.05])[0]
+    v7[0, 0, 0] = _rows([9.0])[0]
+    k7[0, 0, 1] = _rows([1.0])[0]
+    v7[0, 0, 1] = _rows([2.0])[0]
+    sim.append([0], np.zeros((1, Hkv, 1), np.uint8), k7, v7)
+    assert sim.pages[0][0] == [0, 1, 2, 7]
+    # 0.05 / 448 -> s 2^-13 -> 2^-11;  9 / 448 -> 2^-5 -> 2^-3
+    assert sim.page_scale[7] == (2.0 ** -11, 2.0 ** -3)
+
+
+class _AllWrittenAmax(oracle.CacheSim):
+    """Planted mistake: a fresh page's amax over every token the call placed in
+    it, including those overwritten later in the same call."""
+
+    def _set_scales(self, seq_ids, new_pages, written, k, v):
+        T = k.shape[1]
+        every = []
+        for row, b in enumerate(seq_ids):
+            s0 = self.pos[b] - T
+            for kh in range(self.Hkv):
+                for t in range(s0, s0 + T):
+                    every.append((row, b, kh, t, self.slot_of[b][kh][t]))
+        super()._set_scales(seq_ids, new_pages, every, k, v)
+
+
+class _SwappedKV(oracle.CacheSim):
+    """Planted mistake: K and V amax exchanged."""
+
+    def _set_scales(self, seq_ids, new_pages, written, k, v):
+        super()._set_scales(seq_ids, new_pages, written, v, k)
+
+
+@pytest.mark.parametrize("mutant", [_AllWrittenAmax, _SwappedKV])
+def test_fp8_page_scale_pin_rejects_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        _check_fp8_page_scale_rule(mutant)
