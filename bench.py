@@ -163,12 +163,14 @@ def calibrate_and_fill_ragged(layer, wl, ctx, dms, torch):
         dms.dms_append_evict(layer.cache, seq, k, v, ev[: Hkv * n], 1, n)
 
 
-def decode_step(layers, s, wl, dms, path="step"):
+def decode_step(layers, s, wl, dms, path, ws):
+    """One decode step over every layer; `ws` is the decode workspace all
+    layers share (their calls run in stream order)."""
     B = wl.B
     for L in layers:
         if path == "step":
             dms.dms_decode_step(L.cache, None, L.h_dec[s], L.gamma, L.W, None, L.off, L.q_dec[s], L.k_dec[s],
-                                L.v_dec[s], L.out, B, None, L.evict)
+                                L.v_dec[s], L.out, B, None, L.evict, workspace=ws)
             continue
         if path == "prepare":
             dms.dms_decode_prepare(L.cache, None, L.h_dec[s], L.gamma, L.W, None, L.off, None, L.k_dec[s],
@@ -176,7 +178,7 @@ def decode_step(layers, s, wl, dms, path="step"):
         else:
             dms.dms_decide(L.cache, L.h_dec[s], L.gamma, L.W, None, L.off, None, B, 1, None, L.evict)
             dms.dms_append_evict(L.cache, None, L.k_dec[s], L.v_dec[s], L.evict, B, 1)
-        dms.dms_decode_attn(L.cache, None, L.q_dec[s], L.out, B)
+        dms.dms_decode_attn(L.cache, None, L.q_dec[s], L.out, B, workspace=ws)
 
 
 # ---------------------------------------------------------------------------
@@ -212,12 +214,13 @@ def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager
     """Replays `steps` timed decode steps (after `warmup`) over the layer
     caches from one captured graph per step, then the attention alone; HIP
     events on the launch stream; figures per layer step."""
+    ws = dms.decode_workspace(layers[0].cache.cfg, wl.B)
     graphs = []
     if not eager:
         for s in range(S):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                decode_step(layers, s, wl, dms, path)
+                decode_step(layers, s, wl, dms, path, ws)
             graphs.append(g)
         torch.cuda.synchronize()
         log(f"captured {S} step graphs")
@@ -226,7 +229,7 @@ def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager
         if graphs:
             graphs[s].replay()
         else:
-            decode_step(layers, s, wl, dms, path)
+            decode_step(layers, s, wl, dms, path, ws)
 
     for s in range(warmup):
         step(s)
@@ -256,7 +259,7 @@ def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager
     ga = torch.cuda.CUDAGraph()
     with torch.cuda.graph(ga):
         for L in layers:
-            dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B)
+            dms.dms_decode_attn(L.cache, None, L.q_dec[S - 1], L.out, wl.B, workspace=ws)
     ga.replay()
     torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -593,7 +596,8 @@ def cpu_baseline(steps: int):
         pre.append(lg[0])
     off = np.array([synth.offset_for_fraction(np.concatenate([p[k] for p in pre]), d.p_h[k]) for k in range(Hkv)])
     e_hist = [(p - off[:, None] > 0).astype(np.uint8) for p in pre]
-    sim = oracle.CacheSim(B, Hkv, wl.window, wl.block, wl.prefill + steps, B * Hkv * 64)
+    steps = min(steps, wl.decode_steps)
+    sim = oracle.CacheSim(B, Hkv, wl.window, wl.block, wl.prefill + wl.decode_steps, B * Hkv * 64)
     for s in range(0, wl.prefill, wl.chunk):
         sim.append(list(range(B)), np.stack([e[:, s:s + wl.chunk] for e in e_hist]))
     K = [d.tensor("k", b, keep=True) for b in range(B)]
@@ -611,6 +615,22 @@ def cpu_baseline(steps: int):
             e_hist[b] = np.concatenate([e_hist[b], e[b]], axis=1)
             oracle.attention_rows(qd[b][i][None], K[b][: t + 1], V[b][: t + 1], e_hist[b], wl.window, [t], scale)
     dt = time.perf_counter() - t0
+    # the same loop with BLAS held to one thread, on a quarter of the steps
+    from threadpoolctl import threadpool_limits
+    steps1 = min(max(4, steps // 4), wl.decode_steps - steps)
+    sim1 = __import__("copy").deepcopy(sim)
+    e1 = [x.copy() for x in e_hist]
+    with threadpool_limits(1):
+        t1 = time.perf_counter()
+        for i in range(steps, steps + steps1):
+            t = wl.prefill + i
+            h = np.stack([hd[b][i] for b in range(B)])[:, None]
+            _, e = oracle.decide_linear(h, d.gamma, d.W, off, alpha_scale=wl.alpha_scale, eps=1e-6)
+            sim1.append(list(range(B)), e)
+            for b in range(B):
+                e1[b] = np.concatenate([e1[b], e[b]], axis=1)
+                oracle.attention_rows(qd[b][i][None], K[b][: t + 1], V[b][: t + 1], e1[b], wl.window, [t], scale)
+        dt1 = max(time.perf_counter() - t1, 1e-9)
     return {
         "value": B * steps / dt,
         "unit": "tok/s/layer",
@@ -620,7 +640,46 @@ def cpu_baseline(steps: int):
                   f"decide + cache simulation + masked attention); prompt state built untimed",
         "seconds": dt,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "blas_threads": blas_threads,
+        "one_thread": {"value": B * steps1 / dt1 if steps1 > 0 else None, "steps": steps1, "seconds": dt1,
+                       "blas_threads": 1},
     }
+
+
+def measure_peaks(dms, torch) -> dict:
+    """The box's own rates (libdms_probe): a streaming read of a 4 GiB buffer
+    (16 times the Infinity Cache) with a few launch shapes, best of them, and a
+    dense bf16 matrix-core loop (8 independent 16x16x32 products per wave,
+    8 waves per CU); HIP events on the launch stream around repeated calls."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(8 * cus * 8, dtype=torch.int32, device="cuda")
+    best = (0.0, None)
+    for grid, unroll in ((cus * 4, 8), (cus * 8, 8), (cus * 4, 16), (cus * 8, 16)):
+        dms.probe_read(buf, grid, unroll, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            nbytes = dms.probe_read(buf, grid, unroll, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if gbs > best[0]:
+            best = (gbs, {"grid": grid, "unroll": unroll, "bytes": nbytes})
+    del buf
+    grid, iters = 2 * cus, 20000
+    dms.probe_mfma_bf16(grid, 200, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = sum(dms.probe_mfma_bf16(grid, iters, sink) for _ in range(5))
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"hbm_read_gbs": best[0], "hbm_read_shape": best[1], "bf16_mfma_tflops": tflops,
+            "hbm_nominal_gbs": HBM_PEAK_GBS, "bf16_nominal_tflops": BF16_PEAK_TFLOPS, "compute_units": cus}
 
 
 def copy_calibration(mib: int, torch) -> None:
@@ -651,6 +710,7 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM / bf16 peak probes")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="end with a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -693,6 +753,18 @@ def main() -> int:
             f"mlp decode {kvzap['mlp_decode_b8_us']:.1f} us ({kvzap['mlp_decode_b8_gbs']:.0f} GB/s), "
             f"linear chunk {kvzap['linear_chunk4096_us']:.1f} us ({kvzap['linear_chunk4096_gbs']:.0f} GB/s), "
             f"linear decode {kvzap['linear_decode_b8_us']:.1f} us")
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(dms, torch)
+        log(f"peaks: HBM read {peaks['hbm_read_gbs']:.0f} GB/s {peaks['hbm_read_shape']}, "
+            f"bf16 matrix cores {peaks['bf16_mfma_tflops']:.0f} TFLOP/s")
+        for r in (pre or {}).values():
+            r["frac_bf16_measured"] = r["attn_tflops"] / peaks["bf16_mfma_tflops"]
+        if train:
+            train["frac_bf16_measured"] = train["attn_tflops"] / peaks["bf16_mfma_tflops"]
+            train["bwd_frac_bf16_measured"] = train["bwd_tflops"] / peaks["bf16_mfma_tflops"]
+        for r in (others or {}).values():
+            r["attn_frac_hbm_measured"] = r["attn_gbs"] / peaks["hbm_read_gbs"]
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -739,12 +811,17 @@ def main() -> int:
             "unit": "GB/s",
             "frac": roof["achieved"] / HBM_PEAK_GBS,
             "traffic": traffic,
+            "peak_measured": None if peaks is None else peaks["hbm_read_gbs"],
+            "frac_measured": None if peaks is None else roof["achieved"] / peaks["hbm_read_gbs"],
             "algorithmic_bytes_per_launch": roof["algorithmic_bytes_per_launch"],
             "avg_launch_us": roof["avg_launch_us"],
         },
         "attn_only": {"kernel": "decode_attn_fast_kernel (dms_decode_attn)", "avg_launch_us": dec["attn_us"],
                       "achieved_gbs": dec["attn_gbs"], "algorithmic_bytes_per_launch": dec["attn_bytes"]},
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "cpu_baseline_detail": None if cpu is None else {k: cpu[k] for k in ("host_cpus", "blas_threads", "seconds",
+                                                                             "one_thread")},
+        "peaks": peaks,
         "layer_step_us": dec["layer_step_us"],
         "step_kv_gbs": dec["step_kv_gbs"],
         "mean_live_slots_per_head": dec["mean_live_slots_per_head"],

@@ -61,8 +61,11 @@ typedef enum dms_status {
 #define DMS_DEV_POOL_EXHAUSTED 0x1  /* an append needed a page and the pool was empty */
 #define DMS_DEV_CAPACITY 0x2        /* an append would pass max_tokens_per_seq */
 #define DMS_DEV_BAD_SEQ 0x4         /* a sequence id outside [0, max_batch) */
-#define DMS_DEV_STEP_SYNC 0x8       /* a fused decode step gave up waiting for its attention workgroups;
-                                       the cache state is undefined (recreate the cache) */
+#define DMS_DEV_STEP_SYNC 0x8       /* a one-launch decode step gave up waiting for its attention
+                                       workgroups and did not commit: positions, lengths, ring and
+                                       page tables are as before the call, but the rows it would have
+                                       placed may already be written; clear the status
+                                       (dms_cache_clear_status), then repeat the same step */
 
 typedef enum dms_dtype { DMS_F32 = 0, DMS_BF16 = 1, DMS_FP8_E4M3 = 2 } dms_dtype;
 typedef enum dms_decide_mode { DMS_DECIDE_LINEAR = 0, DMS_DECIDE_QNEURON = 1 } dms_decide_mode;
@@ -122,8 +125,21 @@ typedef struct dms_stats {
  * size or dtype, a bad enum, or a nonpositive size. */
 int dms_config_validate(const dms_config* cfg);
 
-/* Bytes of the single device buffer a cache with this configuration needs. */
+/* Bytes of the single device buffer a cache with this configuration needs
+ * (walkthrough, 高级选项 预分配: the cache is preallocated for
+ * dms_preallocate_for_tokens positions, here max_tokens_per_seq per sequence,
+ * with pool_pages pages shared by all sequences and heads).  It holds the K/V
+ * pages, the fp8 scales, the slot/page/ring tables, the free-page stack and
+ * small control words; decode scratch is the caller's workspace
+ * (dms_decode_workspace_bytes), not part of the cache. */
 int dms_cache_bytes(const dms_config* cfg, size_t* bytes);
+
+/* Bytes of the workspace dms_decode_attn and dms_decode_step need for a call
+ * of B rows on the current device: the partial (o, max, sum) records of the
+ * (row, KV head) units whose live slots are split over several workgroups
+ * (two per attention workgroup plus one per unit, Hq / Hkv * (head_dim + 2)
+ * floats each).  DMS_ERR_ARG for B outside [1, max_batch]. */
+int dms_decode_workspace_bytes(const dms_config* cfg, int B, size_t* bytes);
 
 /* Pages a sequence may hold per KV head: ceil(max_tokens_per_seq / block_size). */
 int dms_max_pages_per_seq(const dms_config* cfg, int32_t* pages);
@@ -132,8 +148,9 @@ int dms_max_pages_per_seq(const dms_config* cfg, int32_t* pages);
  * Creates a cache inside dev_buf (device memory of at least
  * dms_cache_bytes(cfg), 256-byte aligned, owned by the caller and kept alive
  * until dms_cache_destroy) and initialises it on `stream`: every sequence
- * empty, the free stack ordered so pops return pages 0, 1, 2, ..., status 0.
- * The host handle (*out) owns no device memory.
+ * empty, the free stack ordered so pops return pages 0, 1, 2, ..., status 0
+ * (walkthrough, 高级选项 预分配: all cache memory is reserved up front; no call
+ * allocates afterwards).  The host handle (*out) owns no device memory.
  */
 int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* stream, dms_cache** out);
 
@@ -204,9 +221,14 @@ int dms_decode_prepare(dms_cache* cache, const int32_t* seq_ids, const void* hid
  *   exactly the visible keys, so no mask is applied.
  * q [B][Hq][D], out [B][Hq][D] act dtype; seq_ids as in dms_append_evict.
  * A head with no live slot gets zeros.  fp32 accumulation.
+ * workspace: device memory of at least dms_decode_workspace_bytes(cfg, B)
+ * bytes, 256-byte aligned, owned by the caller, overwritten (no contents are
+ * kept between calls, so one workspace can serve every layer's cache in turn
+ * on one stream; calls that overlap in time need workspaces of their own).
+ * DMS_ERR_CAPACITY for a missing or short workspace, before any launch.
  */
 int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, void* out, int B,
-                    void* stream);
+                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * A layer's whole decode step in one call: the decision and append of
@@ -227,14 +249,17 @@ int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, voi
  * read the shared tables.  Other configurations and larger steps call
  * dms_decode_prepare, then dms_decode_attn (the environment variable
  * DMS_DECODE_STEP_FUSE, read at cache creation, forces one (1) or two (0)
- * launches).  Device-side errors as in dms_append_evict, and
- * DMS_DEV_STEP_SYNC if the commit's bounded wait for the attention
- * workgroups ran out (only when far more workgroups than the GPU holds at
- * once queue behind it).
+ * launches).  workspace / ws_bytes as in dms_decode_attn.  Device-side
+ * errors as in dms_append_evict, and DMS_DEV_STEP_SYNC if the commit's
+ * bounded wait for the attention workgroups ran out (only when far more
+ * workgroups than the GPU holds at once queue behind it; the environment
+ * variable DMS_STEP_SPIN_LIMIT, read at every call, sets the bound in polls,
+ * 0 giving up at once).
  */
 int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden, const float* rms_gamma,
                     const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,
-                    const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* stream);
+                    const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* workspace,
+                    size_t ws_bytes, void* stream);
 
 /* ---- training mode (walkthrough, Gumbel 噪声与可微门控 and 注意力 / 训练模式) ---- */
 
@@ -290,7 +315,8 @@ int dms_seq_reset(dms_cache* cache, const int32_t* seq_ids, int n, void* stream)
 /* Synchronises `stream` and returns the sticky device status bits in *device_status. */
 int dms_cache_status(dms_cache* cache, void* stream, int32_t* device_status);
 
-/* Clears the sticky device status word (asynchronous). */
+/* Clears the sticky device status word and resets the one-launch decode
+ * step's arrival counters (asynchronous). */
 int dms_cache_clear_status(dms_cache* cache, void* stream);
 
 /* Synchronises `stream` and copies the tables into host buffers. */

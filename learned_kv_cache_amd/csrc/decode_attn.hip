@@ -20,6 +20,9 @@
 //   chunks double-buffered.
 // * Online softmax per wave in base 2; waves merge through LDS; the last
 //   workgroup of a split unit merges the unit's partial records.
+#include <algorithm>
+#include <cstdlib>
+
 #include "dms_internal.h"
 #include "decode_prep.h"
 
@@ -33,6 +36,7 @@ struct DecodeArgs {
   void* out;
   int B;
   int lanes_per_row;   // fast kernel row layout (8 or 16 lanes per bf16 row of 128)
+  float* partials;     // caller's workspace: partial (o, m, l) records of split units
 };
 
 template <int KV> struct KvTraits;
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
         store_act<ACT>(obase, (static_cast<size_t>(row) * g.Hq + kh * G + h) * D + dd, lv > 0.0f ? ov / lv : 0.0f);
       } else {
         const int rec = s_pbase[u] + (blockIdx.x - s_start[u] / c);
-        float* pr = d.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
+        float* pr = a.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
         pr[dd] = ov;
         if (dd == 0) {
           pr[D] = M;
@@ -352,10 +356,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     float res = 0.0f;
     if (n > 1) {
       float M = -INFINITY;
-      for (int i = 0; i < n; ++i) M = fmaxf(M, a.d.partials[(static_cast<int64_t>(pb + i) * G + h) * (D + 2) + D]);
+      for (int i = 0; i < n; ++i) M = fmaxf(M, a.partials[(static_cast<int64_t>(pb + i) * G + h) * (D + 2) + D]);
       float ov = 0.0f, lv = 0.0f;
       for (int i = 0; i < n; ++i) {
-        const float* pr = a.d.partials + (static_cast<int64_t>(pb + i) * G + h) * (D + 2);
+        const float* pr = a.partials + (static_cast<int64_t>(pb + i) * G + h) * (D + 2);
         if (pr[D] == -INFINITY) continue;
         const float f = exp2f(pr[D] - M);
         ov += f * pr[dd];
@@ -702,6 +706,7 @@ struct StepArgs {
   int groups;              // arrival groups of the attention workgroups (min(kArriveGroups, their count))
   int agrid;               // attention workgroups
   int qneuron;             // the decision neuron (last element of each group's first query head) reads as zero
+  int spin_limit;          // polls of the commit's wait before it gives up (0: give up at once)
 };
 
 // Up to this many units (and at most half as many as workgroups) each unit
@@ -1091,7 +1096,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
         obase[(static_cast<size_t>(row) * g.Hq + kh * G + h) * D + dd] = f32_to_bf16(lv > 0.0f ? ov / lv : 0.0f);
       } else {
         // device-coherent stores (no L2 write-back of the XCD needed)
-        float* pr = d.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
+        float* pr = a.partials + (static_cast<int64_t>(rec) * G + h) * (D + 2);
         __hip_atomic_store(pr + dd, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (dd == 0) {
           __hip_atomic_store(pr + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1113,7 +1118,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       if (tid == 0) s_tmp[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
       __syncthreads();
       if (s_tmp[0]) {
-        merge_unit_records<D, G>(d.partials, w0, w1, odd, obase + (static_cast<size_t>(row) * g.Hq + kh * G) * D);
+        merge_unit_records<D, G>(a.partials, w0, w1, odd, obase + (static_cast<size_t>(row) * g.Hq + kh * G) * D);
         if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -1160,11 +1165,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendAr
         const int want = sa.agrid / sa.groups + (lane < sa.agrid % sa.groups ? 1 : 0);
         const int32_t* gc = ap.d.arrive + lane * kArriveStride;
         for (int it = 0;; ++it) {
-          if (__hip_atomic_load(gc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
-          if (it == kArriveSpinLimit) {
+          if (it >= sa.spin_limit) {
             ok = false;
             break;
           }
+          if (__hip_atomic_load(gc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
           __builtin_amdgcn_s_sleep(2);
         }
       }
@@ -1173,6 +1178,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendAr
     }
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(sh.n)) {
+      // no commit: the tables are as before the call (the pairs wrote only
+      // their K/V rows and slot metadata); the arrival counters are reset by
+      // dms_cache_clear_status, once every workgroup of this launch is done
       if (threadIdx.x == 0) set_status(ap.d.ctl, DMS_DEV_STEP_SYNC);
       return;
     }
@@ -1297,17 +1305,30 @@ static bool fast_decode_ok(const dms_cache* cache, int* lpr_out) {
 
 using namespace dms;
 
+// Checks the caller's decode workspace against what a call of B rows needs.
+static int check_workspace(const dms_cache* cache, int B, const void* workspace, size_t ws_bytes) {
+  const Geo& g = cache->geo;
+  const size_t need = decode_workspace_bytes(decode_grid_for(cache), B * g.Hkv, g.g, g.D);
+  if (!workspace || ws_bytes < need)
+    return fail(DMS_ERR_CAPACITY, "decode workspace missing or smaller than dms_decode_workspace_bytes (" +
+                                      std::to_string(need) + " bytes)");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(DMS_ERR_ARG, "decode workspace must be 256-byte aligned");
+  return DMS_OK;
+}
+
 extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, void* out, int B,
-                               void* stream) {
+                               void* workspace, size_t ws_bytes, void* stream) {
   if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
   if (!q || !out) return fail(DMS_ERR_ARG, "q and out are required");
   const Geo& g = cache->geo;
   if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
-  DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr};
+  int s = check_workspace(cache, B, workspace, ws_bytes);
+  if (s) return s;
+  DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr, static_cast<float*>(workspace)};
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
-  int s;
   if (fast_decode_ok(cache, nullptr)) {
     const bool fp8 = g.kv_dtype == DMS_FP8_E4M3;
     const int np = cache->decode_np > 0 ? cache->decode_np : 2;
@@ -1327,7 +1348,8 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
 
 extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden, const float* rms_gamma,
                                const float* W, const float* bias, const float* offsets, void* q_inout, const void* k,
-                               const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* stream) {
+                               const void* v, void* out, int B, float* logits_out, uint8_t* evict_out,
+                               void* workspace, size_t ws_bytes, void* stream) {
   if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
   const dms_config& c = cache->cfg;
   const Geo& g = cache->geo;
@@ -1335,6 +1357,7 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
     return fail(DMS_ERR_ARG, "q_inout, out, k, v, offsets and evict_out are required");
   if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
+  if (int s = check_workspace(cache, B, workspace, ws_bytes)) return s;
   const bool linear = c.decide_mode == DMS_DECIDE_LINEAR;
   if (linear && (!hidden || !rms_gamma || !W)) return fail(DMS_ERR_ARG, "hidden, rms_gamma and W are required");
   uintptr_t al = reinterpret_cast<uintptr_t>(q_inout) | reinterpret_cast<uintptr_t>(k) |
@@ -1367,9 +1390,9 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
     int s = dms_decode_prepare(cache, seq_ids, hidden, rms_gamma, W, bias, offsets, q_inout, k, v, B, logits_out,
                                evict_out, stream);
     if (s) return s;
-    return dms_decode_attn(cache, seq_ids, q_inout, out, B, stream);
+    return dms_decode_attn(cache, seq_ids, q_inout, out, B, workspace, ws_bytes, stream);
   }
-  DecodeArgs a{cache->dev, g, seq_ids, q_inout, out, B, cache->decode_lpr};
+  DecodeArgs a{cache->dev, g, seq_ids, q_inout, out, B, cache->decode_lpr, static_cast<float*>(workspace)};
   AppendArgs ap{};
   ap.d = cache->dev;
   ap.g = g;
@@ -1389,8 +1412,13 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
   ap.evict_out = evict_out;
   PrepIn pin{static_cast<const uint16_t*>(hidden), rms_gamma, W, static_cast<uint16_t*>(q_inout), linear ? 0 : 1};
   const int groups = std::min(kArriveGroups, agrid);
+  // DMS_STEP_SPIN_LIMIT (read at every call): the commit's bounded wait, in
+  // polls; 0 makes it give up at once (a host-side way to exercise the
+  // DMS_DEV_STEP_SYNC path with every kernel exiting normally)
+  int spin = kArriveSpinLimit;
+  if (const char* e = std::getenv("DMS_STEP_SPIN_LIMIT")) spin = std::max(0, std::atoi(e));
   StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, groups, agrid,
-              linear ? 0 : 1};
+              linear ? 0 : 1, spin};
   hipLaunchKernelGGL(kern, dim3(npairs + agrid), dim3(256), 0, st, a, ap, pin, sa);
   return check_hip(hipGetLastError(), "dms_decode_step launch");
 }

@@ -41,7 +41,6 @@ int compute_layout(const dms_config& c, Layout* L) {
   const size_t D = static_cast<size_t>(c.head_dim);
   const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
   const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + P - 1) / P;
-  const size_t g = static_cast<size_t>(c.num_q_heads / c.num_kv_heads);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -65,8 +64,6 @@ int compute_layout(const dms_config& c, Layout* L) {
   L->chunk_info = take(units * 8 * sizeof(int32_t));
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
   L->arrive = take(static_cast<size_t>(kArriveGroups) * kArriveStride * sizeof(int32_t));
-  L->partial_records = 2 * kMaxDecodeGrid + kMaxUnits;
-  L->partials = take(static_cast<size_t>(L->partial_records) * g * (D + 2) * sizeof(float));
   L->total = off;
   return DMS_OK;
 }
@@ -103,6 +100,17 @@ static int validate(const dms_config* c) {
 }
 
 int decode_grid_for(const dms_cache* c) { return c->decode_grid; }
+
+int decode_grid_default(int cus) {
+  int grid = 2 * cus;
+  if (const char* e = std::getenv("DMS_DECODE_WGS")) grid = std::atoi(e);
+  return std::max(1, std::min(grid, kMaxDecodeGrid));
+}
+
+size_t decode_workspace_bytes(int grid, int units, int g, int D) {
+  const size_t records = 2 * static_cast<size_t>(grid) + static_cast<size_t>(units);
+  return align256(records * static_cast<size_t>(g) * (D + 2) * sizeof(float));
+}
 
 // Fills the control words, the free stack (pops return 0, 1, 2, ...), empty
 // lengths/positions, unused page-table entries and zero decode counters.
@@ -196,7 +204,17 @@ __global__ __launch_bounds__(1024) void reset_kernel(DevCache d, Geo g, const in
   if (tid == 0) d.ctl[kCtlFreeCount] = min(g.pool, s_free + s_base);
 }
 
-__global__ void clear_status_kernel(int32_t* ctl) { ctl[kCtlStatus] = 0; }
+// Clears the status word and the one-launch decode step's arrival counters
+// (left set when a step's commit gave up waiting; every workgroup of that
+// launch has finished before this kernel runs).
+__global__ void clear_status_kernel(int32_t* ctl, int32_t* arrive) {
+  const int i = threadIdx.x;
+  if (i == 0) {
+    ctl[kCtlStatus] = 0;
+    ctl[kCtlPrepArrive] = 0;
+  }
+  if (i < kArriveGroups) arrive[i * kArriveStride] = 0;
+}
 
 }  // namespace dms
 
@@ -219,6 +237,21 @@ int dms_cache_bytes(const dms_config* cfg, size_t* bytes) {
   Layout L;
   compute_layout(*cfg, &L);
   *bytes = L.total;
+  return DMS_OK;
+}
+
+int dms_decode_workspace_bytes(const dms_config* cfg, int B, size_t* bytes) {
+  if (!bytes) return fail(DMS_ERR_ARG, "bytes is NULL");
+  int s = validate(cfg);
+  if (s) return s;
+  if (B <= 0 || B > cfg->max_batch) return fail(DMS_ERR_ARG, "B must be in [1, max_batch]");
+  int dev = 0, cus = 256;
+  if ((s = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return s;
+  if ((s = check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                     "hipDeviceGetAttribute")))
+    return s;
+  *bytes = decode_workspace_bytes(decode_grid_default(cus), B * cfg->num_kv_heads,
+                                  cfg->num_q_heads / cfg->num_kv_heads, cfg->head_dim);
   return DMS_OK;
 }
 
@@ -262,7 +295,6 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.chunk_info = reinterpret_cast<int32_t*>(base + L.chunk_info);
   c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
   c->dev.arrive = reinterpret_cast<int32_t*>(base + L.arrive);
-  c->dev.partials = reinterpret_cast<float*>(base + L.partials);
   Geo& g = c->geo;
   g.Bmax = cfg->max_batch;
   g.Hq = cfg->num_q_heads;
@@ -289,9 +321,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   if ((s = check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
                      "hipDeviceGetAttribute"))) { delete c; return s; }
   c->num_cus = cus;
-  int grid = 2 * cus;
-  if (const char* e = std::getenv("DMS_DECODE_WGS")) grid = std::atoi(e);
-  c->decode_grid = std::max(1, std::min(grid, kMaxDecodeGrid));
+  c->decode_grid = decode_grid_default(cus);
   c->decode_np = 0;
   if (const char* e = std::getenv("DMS_DECODE_NP")) c->decode_np = std::atoi(e);
   c->decode_lpr = 0;
@@ -337,7 +367,7 @@ int dms_cache_status(dms_cache* cache, void* stream, int32_t* device_status) {
 
 int dms_cache_clear_status(dms_cache* cache, void* stream) {
   if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
-  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(1), 0, as_stream(stream), cache->dev.ctl);
+  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, as_stream(stream), cache->dev.ctl, cache->dev.arrive);
   return check_hip(hipGetLastError(), "clear_status_kernel launch");
 }
 

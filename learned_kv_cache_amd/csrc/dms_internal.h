@@ -48,7 +48,6 @@ struct DevCache {
   int32_t* chunk_info;   // [Bmax*Hkv][8]
   int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
   int32_t* arrive;       // [kArriveGroups][kArriveStride] decode step arrival counters (word 0 of each)
-  float* partials;       // decode split partials
 };
 
 // Geometry shared by every kernel of one cache.
@@ -61,8 +60,7 @@ struct Geo {
 
 struct Layout {
   size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, partials, total;
-  int64_t partial_records;
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, total;
 };
 
 }  // namespace dms
@@ -91,6 +89,13 @@ int check_hip(hipError_t e, const char* what);
 int kv_elem_bytes(int kv_dtype);
 int compute_layout(const dms_config& c, Layout* L);
 int decode_grid_for(const dms_cache* c);
+// Decode attention workgroups on a device with `cus` compute units (2 per CU,
+// or DMS_DECODE_WGS), capped at kMaxDecodeGrid.
+int decode_grid_default(int cus);
+// Partial records of one decode call: two per attention workgroup (its first
+// and last unit segment may be split units) plus one per (row, KV head) unit
+// (the generic kernel's records per unit), each G * (D + 2) floats.
+size_t decode_workspace_bytes(int grid, int units, int g, int D);
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 

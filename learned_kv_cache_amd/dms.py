@@ -15,7 +15,11 @@ import numpy as np
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdms.so")
+_PROBE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdms_probe.so")
 _lib = None
+_probe = None
+
+PROBE_EXPORTS = ("dms_probe_read", "dms_probe_read_bytes", "dms_probe_mfma_bf16", "dms_probe_mfma_bf16_flops")
 
 DMS_OK = 0
 DMS_ERR_ARG = -1
@@ -43,6 +47,7 @@ EXPORTS = (
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
     "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed", "dms_kvzap_score",
     "dms_kvzap_workspace_bytes", "dms_train_attn_bwd", "dms_train_attn_bwd_workspace_bytes",
+    "dms_decode_workspace_bytes",
 )
 
 
@@ -101,9 +106,10 @@ def lib():
             "dms_cache_config": [vp, cfgp],
             "dms_decide": [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp],
             "dms_append_evict": [vp, vp, vp, vp, vp, i32, i32, vp],
-            "dms_decode_attn": [vp, vp, vp, vp, i32, vp],
+            "dms_decode_attn": [vp, vp, vp, vp, i32, vp, sz, vp],
+            "dms_decode_workspace_bytes": [cfgp, i32, ctypes.POINTER(sz)],
             "dms_decode_prepare": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
-            "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
+            "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
             "dms_train_gate": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp],
             "dms_seq_info_get": [vp, vp, i32, vp, ctypes.POINTER(dms_seq_info)],
             "dms_pages_needed": [vp, vp, vp, i32, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
@@ -129,6 +135,43 @@ def lib():
         L.dms_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def probe_lib():
+    """Loads libdms_probe.so (include/dms_probe.h: HBM read and bf16 matrix-core rate probes)."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(_PROBE_PATH):
+            raise RuntimeError(f"{_PROBE_PATH} is not built; run `python -m learned_kv_cache_amd.build`")
+        L = ctypes.CDLL(_PROBE_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.dms_probe_read.argtypes = [vp, sz, i32, i32, vp, vp]
+        L.dms_probe_read.restype = ctypes.c_int
+        L.dms_probe_read_bytes.argtypes = [sz, i32, i32]
+        L.dms_probe_read_bytes.restype = sz
+        L.dms_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+        L.dms_probe_mfma_bf16.restype = ctypes.c_int
+        L.dms_probe_mfma_bf16_flops.argtypes = [i32, i32]
+        L.dms_probe_mfma_bf16_flops.restype = ctypes.c_double
+        _probe = L
+    return _probe
+
+
+def probe_read(buf: torch.Tensor, grid: int, unroll: int, sink: torch.Tensor, stream=None) -> int:
+    """One streaming read of `buf` (dms_probe_read); returns the bytes read."""
+    L = probe_lib()
+    nbytes = buf.numel() * buf.element_size()
+    if L.dms_probe_read(_ptr(buf, "buf"), nbytes, grid, unroll, _ptr(sink, "sink"), _stream(stream)) != 0:
+        raise RuntimeError("dms_probe_read failed")
+    return int(L.dms_probe_read_bytes(nbytes, grid, unroll))
+
+
+def probe_mfma_bf16(grid: int, iters: int, sink: torch.Tensor, stream=None) -> float:
+    """One bf16 matrix-core loop (dms_probe_mfma_bf16); returns its flops."""
+    L = probe_lib()
+    if L.dms_probe_mfma_bf16(grid, iters, _ptr(sink, "sink"), _stream(stream)) != 0:
+        raise RuntimeError("dms_probe_mfma_bf16 failed")
+    return float(L.dms_probe_mfma_bf16_flops(grid, iters))
 
 
 def _check(status: int) -> int:
@@ -157,6 +200,29 @@ def dms_cache_bytes(cfg: dms_config) -> int:
     n = ctypes.c_size_t()
     _check(lib().dms_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def dms_decode_workspace_bytes(cfg: dms_config, B: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().dms_decode_workspace_bytes(ctypes.byref(cfg), B, ctypes.byref(n)))
+    return n.value
+
+
+def decode_workspace(cfg: dms_config, B: int, device: str = "cuda") -> torch.Tensor:
+    """A device uint8 tensor of dms_decode_workspace_bytes(cfg, B) bytes (torch's
+    allocator returns 256-byte aligned blocks).  One can serve every cache of a
+    stream in turn."""
+    return torch.empty(dms_decode_workspace_bytes(cfg, B), dtype=torch.uint8, device=device)
+
+
+def _ws(cache: "DmsCache", workspace, B: int):
+    """(pointer, bytes) of the caller's decode workspace, or of the cache's own
+    one (allocated on first use, for B = max_batch) when none is given."""
+    if workspace is None:
+        if cache.workspace is None:
+            cache.workspace = decode_workspace(cache.cfg, cache.cfg.max_batch)
+        workspace = cache.workspace
+    return _ptr(workspace, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size())
 
 
 def dms_max_pages_per_seq(cfg: dms_config) -> int:
@@ -198,6 +264,7 @@ class DmsCache:
         _check(lib().dms_cache_create(ctypes.byref(cfg), self._base, nbytes, _stream(stream), ctypes.byref(h)))
         self.handle = h
         self.act_dtype = torch.float32 if cfg.kv_dtype == DMS_F32 else torch.bfloat16
+        self.workspace = None   # decode workspace used when a call passes none
 
     def close(self):
         if self.handle:
@@ -260,7 +327,7 @@ def dms_decode_prepare(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, off
 
 
 def dms_decode_step(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, offsets, q_inout, k, v, out, B: int,
-                    logits_out, evict_out, stream=None) -> int:
+                    logits_out, evict_out, workspace=None, stream=None) -> int:
     c = cache.cfg
     ad = cache.act_dtype
     if c.decide_mode == DMS_DECIDE_LINEAR:
@@ -276,7 +343,7 @@ def dms_decode_step(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, offset
         _ptr(bias, "bias", torch.float32, c.num_kv_heads), _ptr(offsets, "offsets", torch.float32, c.num_kv_heads),
         _ptr(q_inout, "q_inout", ad, nq), _ptr(k, "k", ad, n), _ptr(v, "v", ad, n), _ptr(out, "out", ad, nq), B,
         _ptr(logits_out, "logits_out", torch.float32, B * c.num_kv_heads),
-        _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads), _stream(stream)))
+        _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads), *_ws(cache, workspace, B), _stream(stream)))
 
 
 def dms_train_gate(logits, noise, tau: float, y_out=None, probs_out=None, hard_out=None, stream=None) -> int:
@@ -394,12 +461,12 @@ def dms_pages_needed(cache: DmsCache, seq_ids, n_new, stream=None):
     return list(pages), free.value
 
 
-def dms_decode_attn(cache: DmsCache, seq_ids, q, out, B: int, stream=None) -> int:
+def dms_decode_attn(cache: DmsCache, seq_ids, q, out, B: int, workspace=None, stream=None) -> int:
     c = cache.cfg
     n = B * c.num_q_heads * c.head_dim
     return _check(lib().dms_decode_attn(
         cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), _ptr(q, "q", cache.act_dtype, n),
-        _ptr(out, "out", cache.act_dtype, n), B, _stream(stream)))
+        _ptr(out, "out", cache.act_dtype, n), B, *_ws(cache, workspace, B), _stream(stream)))
 
 
 def dms_prefill_attn(cache: DmsCache, seq_ids, q, k, v, evict, out, B: int, C: int, stream=None) -> int:

@@ -465,17 +465,19 @@ def length_closed_form(e_row: np.ndarray, t: int, w: int) -> int:
     return (t + 1) - int(np.sum(np.asarray(e_row[: max(0, t - w + 1)]) != 0))
 
 
-def effective_kv(sim: CacheSim, b: int, kh: int, x: np.ndarray, which: int) -> np.ndarray:
+def effective_kv(sim: CacheSim, b: int, kh: int, x: np.ndarray, which: int, t0: int = 0) -> np.ndarray:
     """Values attention reads for one head's tokens: raw, or fp8-rounded with their page scale.
 
-    x: [T, D] raw values of positions 0..T-1; which: 0 for K, 1 for V.  Tokens
-    never written (overwritten inside the call that appended them) keep their
-    raw value; they are never visible from later calls.
+    x: [T, D] raw values of positions t0..t0+T-1; which: 0 for K, 1 for V.
+    Tokens never written (overwritten inside the call that appended them) keep
+    their raw value; they are never visible from later calls.  A token's scale
+    is fixed when the call that appends it ends, so a range can be taken once.
     """
     x = np.asarray(x, dtype=np.float64)
     if not sim.fp8:
         return x
-    sc = np.array([s[which] if s is not None else np.nan for s in sim.tok_scale[b][kh][: x.shape[0]]])
+    sc = np.array([s[which] if s is not None else np.nan
+                   for s in sim.tok_scale[b][kh][t0: t0 + x.shape[0]]])
     if len(sc) < x.shape[0]:
         sc = np.concatenate([sc, np.full(x.shape[0] - len(sc), np.nan)])
     written = ~np.isnan(sc)

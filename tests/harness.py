@@ -17,6 +17,7 @@ import time
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 import oracle
 from learned_kv_cache_amd import synth
@@ -58,8 +59,10 @@ def prepare(wl: synth.Workload, run_id: int = 0, max_rounds: int = 50) -> Prepar
     d = synth.draw(wl, run_id)
     B, Hkv = wl.B, wl.Hkv
     pre = _pre_offset_linear if wl.decide == "linear" else _pre_offset_qneuron
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    with cf.ThreadPoolExecutor(max_workers=workers) as ex:       # numpy releases the GIL
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), B))
+    # numpy leaves the GIL in its products; one BLAS thread per worker (nested
+    # BLAS threads in each of many workers oversubscribe the cores badly)
+    with threadpool_limits(1 if workers > 1 else None), cf.ThreadPoolExecutor(max_workers=workers) as ex:
         u = list(ex.map(lambda b: pre(d, b), range(B)))
     if wl.fixed_offset is not None:
         off = np.full(Hkv, wl.fixed_offset)
@@ -163,6 +166,7 @@ class Runner:
         self.off = to_dev(prep.offsets, "f32")
         self.scale = 1.0 / np.sqrt(wl.D)
         self._dec: Dict = {}                                  # cached decode rows per (tensor, sequence)
+        self._kv64: Dict = {}                                 # per sequence [K, V float64 as read, fp8 positions done]
         self.torch = torch
 
     # -- decisions ----------------------------------------------------------
@@ -211,23 +215,48 @@ class Runner:
 
     # -- oracle attention ------------------------------------------------------
     def kv_view(self, b: int, upto: int, raw_from: Optional[int] = None):
-        """K, V [upto, Hkv, D] as attention reads them: fp8-rounded where stored
-        (positions < raw_from), raw from raw_from on."""
-        d = self.prep.draw
-        K = d.tensor("k", b, keep=True)[:upto].astype(np.float64)
-        V = d.tensor("v", b, keep=True)[:upto].astype(np.float64)
+        """K, V [upto, Hkv, D] float64 as attention reads them: fp8-rounded where
+        stored (positions < raw_from), raw from raw_from on.  Held per sequence
+        and returned as views: the fp8 view of a position is fixed once the
+        call that appended it has ended, so it is computed once per position."""
+        ent = self._kv64.get(b)
+        if ent is None:
+            d = self.prep.draw
+            ent = self._kv64[b] = [d.tensor("k", b).astype(np.float64), d.tensor("v", b).astype(np.float64), 0]
+        K, V, done = ent
         if self.sim.fp8:
-            lim = upto if raw_from is None else raw_from
-            for kh in range(self.wl.Hkv):
-                K[:lim, kh] = oracle.effective_kv(self.sim, b, kh, K[:lim, kh], 0)
-                V[:lim, kh] = oracle.effective_kv(self.sim, b, kh, V[:lim, kh], 1)
-        return K, V
+            lim = upto if raw_from is None else min(raw_from, upto)
+            if lim > done:
+                for kh in range(self.wl.Hkv):
+                    K[done:lim, kh] = oracle.effective_kv(self.sim, b, kh, K[done:lim, kh], 0, t0=done)
+                    V[done:lim, kh] = oracle.effective_kv(self.sim, b, kh, V[done:lim, kh], 1, t0=done)
+                ent[2] = lim
+        return K[:upto], V[:upto]
 
     def oracle_rows(self, b: int, q_rows: np.ndarray, rows: np.ndarray, raw_from: Optional[int] = None):
+        """The oracle's attention at query positions `rows` (any order); many
+        rows are split into blocks computed in parallel threads (numpy leaves
+        the GIL in its products and element-wise passes)."""
+        rows = np.asarray(rows)
         upto = int(rows.max()) + 1
         K, V = self.kv_view(b, upto, raw_from)
         e = self.prep.evict[b][:, :upto]
-        return oracle.attention_rows(q_rows, K, V, e, self.wl.window, rows, self.scale)
+        if rows.size <= 64:
+            return oracle.attention_rows(q_rows, K, V, e, self.wl.window, rows, self.scale)
+        order = np.argsort(rows, kind="stable")
+        blocks = np.array_split(order, -(-rows.size // 64))
+
+        def one(ix):
+            top = int(rows[ix].max()) + 1
+            return ix, oracle.attention_rows(q_rows[ix], K[:top], V[:top], e[:, :top], self.wl.window, rows[ix],
+                                             self.scale)
+
+        out = np.empty(q_rows.shape, dtype=np.float64)
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), len(blocks)))
+        with threadpool_limits(1), cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            for ix, o in ex.map(one, blocks):
+                out[ix] = o
+        return out
 
     # -- steps -------------------------------------------------------------------
     def prefill_chunk(self, seqs: Sequence[int], s: int, C: int, check_rows: Optional[int] = None,
@@ -322,14 +351,19 @@ class Runner:
         if not check:
             return None
         got = from_dev(out).reshape(B, wl.Hq, wl.D)
-        errs = []
-        for i, (b, t) in enumerate(zip(seqs, positions)):
+
+        def one(i):
+            b, t = seqs[i], positions[i]
             qz = q_np[i].astype(np.float64).copy()
             if wl.decide == "qneuron":
                 qz[:: wl.g, -1] = 0.0
-            ref = self.oracle_rows(b, qz[None], np.array([t]))[0]
-            errs.append(np.abs(got[i] - ref))
-        err = np.stack(errs)
+            return np.abs(got[i] - self.oracle_rows(b, qz[None], np.array([t]))[0])
+
+        for i, b in enumerate(seqs):             # fp8 views are extended here, before the threads read them
+            self.kv_view(b, positions[i] + 1)
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), B))
+        with threadpool_limits(1 if workers > 1 else None), cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            err = np.stack(list(ex.map(one, range(B))))
         stats = (float(err.max()), float(err.mean()))
         mx, mn = tolerance(wl)
         assert stats[0] <= mx and stats[1] <= mn, f"decode attention error {stats} at positions {positions[:4]}"

@@ -26,6 +26,19 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(dms.EXPORTS)
 
 
+def test_probe_library_exports_its_header():
+    text = open(os.path.join(ROOT, "include", "dms_probe.h")).read()
+    names = sorted(set(re.findall(r"^(?:int|size_t|double)\s+(dms_\w+)\(", text, flags=re.M)))
+    assert set(names) == set(dms.PROBE_EXPORTS)
+    L = ctypes.CDLL(os.path.join(os.path.dirname(dms.library_path()), "libdms_probe.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    P = dms.probe_lib()
+    assert P.dms_probe_read(None, 1 << 20, 4, 8, None, None) == -1          # refused before any launch
+    assert P.dms_probe_read_bytes(10 * 4096 * 16 + 5, 4, 4) == 10 * 4096 * 16
+    assert P.dms_probe_mfma_bf16_flops(2, 3) == 2 * 4 * 8 * 3 * 16 * 16 * 32 * 2
+
+
 def base(**kw):
     c = dict(max_batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, hidden=256, window=16, block_size=8,
              max_tokens_per_seq=100, pool_pages=32, max_chunk=64)
@@ -78,7 +91,7 @@ def test_null_arguments_fail_before_any_launch():
     assert L.dms_cache_bytes(None, None) == dms.DMS_ERR_ARG
     assert L.dms_decide(None, None, None, None, None, None, None, 1, 1, None, None, None) == dms.DMS_ERR_ARG
     assert L.dms_append_evict(None, None, None, None, None, 1, 1, None) == dms.DMS_ERR_ARG
-    assert L.dms_decode_attn(None, None, None, None, 1, None) == dms.DMS_ERR_ARG
+    assert L.dms_decode_attn(None, None, None, None, 1, None, 0, None) == dms.DMS_ERR_ARG
     assert L.dms_prefill_attn(None, None, None, None, None, None, None, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_seq_reset(None, None, 1, None) == dms.DMS_ERR_ARG
     cfg = base()
@@ -87,6 +100,22 @@ def test_null_arguments_fail_before_any_launch():
     assert L.dms_cache_create(ctypes.byref(cfg), ctypes.c_void_p(256), 16, None, ctypes.byref(out)) == \
         dms.DMS_ERR_CAPACITY
     assert b"smaller" in L.dms_last_error()
+
+
+def test_cache_holds_no_decode_scratch():
+    """The Qwen3-8B decode layer (B 8, 8K prompt + 136 steps, block 256): the
+    cache buffer is the K/V pages plus tables a few MB in size; the decode
+    partial records live in the caller's workspace (dms_decode_workspace_bytes)."""
+    P, D, B, Hkv = 256, 128, 8, 8
+    max_tokens = 8192 + 136
+    pool = B * Hkv * -(-max_tokens // P)
+    cfg = dms.make_config(max_batch=B, num_q_heads=32, num_kv_heads=Hkv, head_dim=D, hidden=4096, window=512,
+                          block_size=P, max_tokens_per_seq=max_tokens, pool_pages=pool, max_chunk=4096)
+    pages = 2 * pool * P * D * 2
+    slot_meta = pool * P * 4
+    chunk_slot = B * Hkv * 4096 * 4
+    overhead = dms.dms_cache_bytes(cfg) - pages
+    assert slot_meta + chunk_slot <= overhead < slot_meta + chunk_slot + (1 << 20)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -13,9 +13,12 @@ into the current page or as the first row of a new page).  Shapes cover GQA
 groups 1, 2, 4 and 8, head_dim 64 and 128, bf16 and fp8 pages, both decision
 sources, layer mode, and more than 64 (row, KV head) units.
 """
+import copy
+
 import numpy as np
 import pytest
 
+import oracle
 from learned_kv_cache_amd import synth
 from tests.harness import Runner, from_dev, log, prepare, to_dev
 
@@ -131,15 +134,25 @@ def test_step_subset_of_rows_and_capacity():
     after = r.dms.dms_cache_dump(r.cache)
     assert int(after["positions"][1]) == 12 and int(after["positions"][0]) == 5
     assert np.array_equal(after["lengths"][1], before["lengths"][1])
-    # row 1's attention is over its 12-token cache as it stands: the same as dms_decode_attn's
-    ref = torch.empty_like(q)
-    qz = q.clone()
-    one = to_dev(np.array([1], np.int32), "i32")
-    qz1 = qz[: wl.Hq * wl.D].clone().view(wl.Hq, wl.D)
-    qz1[:: wl.g, -1] = 0
-    dms.dms_decode_attn(r.cache, one, qz1.reshape(-1), ref[: wl.Hq * wl.D], 1)
-    err = (from_dev(out[: wl.Hq * wl.D]) - from_dev(ref[: wl.Hq * wl.D]))
-    assert np.abs(err).max() <= 1e-2, np.abs(err).max()
+    # against the oracle: row 1 attends over its 12-token cache as it stands
+    # (positions 0..11, the visible set of a query at position 11); row 0
+    # appended its token at position 4, so it attends over positions 0..4
+    # (all inside the window), the last with this call's k (= v) row
+    q_np = from_dev(q).reshape(B, wl.Hq, wl.D)
+    q_np[:, :: wl.g, -1] = 0.0                       # the decision neuron plays no part
+    k_np = from_dev(k).reshape(B, wl.Hkv, wl.D)
+    got = from_dev(out).reshape(B, wl.Hq, wl.D)
+    mx, mn = 2e-2, 2e-3
+    K1, V1 = r.kv_view(1, 12)
+    ref1 = oracle.attention_rows(q_np[0][None], K1, V1, prep.evict[1][:, :12], wl.window, [11], r.scale)[0]
+    K0, V0 = r.kv_view(0, 4)
+    K0 = np.concatenate([K0, k_np[1][None]])
+    V0 = np.concatenate([V0, k_np[1][None]])
+    ref0 = oracle.attention_rows(q_np[1][None], K0, V0, np.zeros((wl.Hkv, 5), np.uint8), wl.window, [4],
+                                 r.scale)[0]
+    for g_, ref in ((got[0], ref1), (got[1], ref0)):
+        err = np.abs(g_ - ref)
+        assert err.max() <= mx and err.mean() <= mn, (err.max(), err.mean())
 
 
 def test_step_bad_sequence_id():
@@ -214,3 +227,79 @@ def test_step_fp8_concatenated_split():
         r.decode_step(seqs, [int(ctx[b]) + i for b in seqs], step=True)
     r.check_tables(pages=True)
     assert r.dms.dms_cache_status(r.cache) == 0
+
+
+def test_step_gives_up_and_recovers(monkeypatch):
+    """The commit's bounded wait made to give up from the host
+    (DMS_STEP_SPIN_LIMIT=0, every kernel still exits normally): the status
+    bit is set and no table changes; after dms_cache_clear_status the same
+    step, repeated, commits and the cache equals the oracle's (which saw the
+    step once), and later steps go on normally."""
+    _cuda()
+    from learned_kv_cache_amd import dms
+    wl = _workload("g4_d128_linear", 0, ctx_range=None, prefill=0, decode_steps=34, cfg_id=56)
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    seqs = [0, 2, 1]
+    for t in range(30):                               # past the window of 24: in-place reuse happens
+        r.decode_step(seqs, [t] * 3, step=True)
+    r.check_tables(pages=True)
+    saved = copy.deepcopy(r.sim)
+    monkeypatch.setenv("DMS_STEP_SPIN_LIMIT", "0")
+    r.decode_step(seqs, [30] * 3, step=True, check=False)     # decisions still checked
+    assert dms.dms_cache_status(r.cache) == dms.DMS_DEV_STEP_SYNC
+    r.sim = saved                                     # the step did not commit
+    # positions, lengths, page tables, ring and pool as before the call (slot
+    # metadata and rows of the slots it would have taken may be written)
+    dump = dms.dms_cache_dump(r.cache)
+    assert np.array_equal(dump["positions"], np.asarray(saved.pos, np.int32))
+    assert np.array_equal(dump["lengths"], np.asarray(saved.L, np.int32))
+    assert int(dump["free_count"][0]) == len(saved.free)
+    for b in seqs:
+        for kh in range(wl.Hkv):
+            assert list(dump["page_table"][b, kh][: len(saved.pages[b][kh])]) == saved.pages[b][kh]
+            for t, (slot, e) in saved.ring(b, kh).items():
+                assert int(dump["ring"][b, kh, t % wl.window]) & 0xFFFFFFFF == slot | (e << 31)
+    monkeypatch.delenv("DMS_STEP_SPIN_LIMIT")
+    dms.dms_cache_clear_status(r.cache)
+    assert dms.dms_cache_status(r.cache) == 0
+    for t in range(30, 34):
+        r.decode_step(seqs, [t] * 3, step=True)
+        r.check_tables(pages=True)
+    assert dms.dms_cache_status(r.cache) == 0
+
+
+def test_decode_workspace_is_checked():
+    """dms_decode_workspace_bytes gives two partial records per attention
+    workgroup plus one per (row, KV head) unit; a missing or short workspace
+    is refused before any launch, and an exact one works."""
+    torch = _cuda()
+    from learned_kv_cache_amd import dms
+    wl = _workload("g4_d128_linear", 0, ctx_range=None, prefill=0, decode_steps=4, cfg_id=57)
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    B = 3
+    n = dms.dms_decode_workspace_bytes(r.cfg, B)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rec = wl.g * (wl.D + 2) * 4
+    want = (2 * 2 * cus + B * wl.Hkv) * rec
+    assert want <= n < want + 256
+    with pytest.raises(dms.DmsError):
+        dms.dms_decode_workspace_bytes(r.cfg, 0)
+    r.decode_step([0, 1, 2], [0] * 3, step=True)
+    q = torch.zeros(B * wl.Hq * wl.D, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    short = torch.empty(n - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dms.DmsError) as ei:
+        dms.dms_decode_attn(r.cache, None, q, out, B, workspace=short)
+    assert ei.value.status == dms.DMS_ERR_CAPACITY
+    k = torch.zeros(B * wl.Hkv * wl.D, dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty(B * wl.Hkv, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(B * wl.hidden, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dms.DmsError) as ei:
+        dms.dms_decode_step(r.cache, None, h, r.gamma, r.W, None, r.off, q, k, k, out, B, None, ev, workspace=short)
+    assert ei.value.status == dms.DMS_ERR_CAPACITY
+    r.check_tables(pages=True)                        # neither call touched the cache
+    exact = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dms.dms_decode_attn(r.cache, None, q, out, B, workspace=exact)
+    assert dms.dms_cache_status(r.cache) == 0
