@@ -231,6 +231,23 @@ int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const void* q, voi
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dms_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that must not call hipMalloc
+ * or bring a workspace): the same kernels and results, with the partial
+ * records in a static 8 MiB array held by each GPU for the life of the
+ * process, instead of a caller workspace.  Calls no allocating routine.
+ * Arguments as in dms_decode_attn; the cache's device must be current.
+ * DMS_ERR_CAPACITY (before any launch) when the call needs more than 8 MiB of
+ * records (dms_decode_workspace_bytes(cfg, B) > 8 MiB: with head_dim 128 at
+ * the default 512 workgroups, 4 query heads per KV head fit every call of up
+ * to 2048 (row, KV head) units, 8 query heads up to about 990).  All calls on
+ * one GPU share the array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued.
+ */
+int dms_decode_attn_noalloc(dms_cache* cache, const int32_t* seq_ids, const void* q, void* out, int B,
+                            void* stream);
+
+/*
  * A layer's whole decode step in one call: the decision and append of
  * dms_decode_prepare and the attention of dms_decode_attn for one token per
  * row (walkthrough, 推理模式, and the FastDMS post's fused decode path).

@@ -22,6 +22,7 @@
 //   workgroup of a split unit merges the unit's partial records.
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 
 #include "dms_internal.h"
 #include "decode_prep.h"
@@ -1301,6 +1302,36 @@ static bool fast_decode_ok(const dms_cache* cache, int* lpr_out) {
          !cache->force_generic;
 }
 
+// ---- decode attention without an allocation ------------------------------
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops that must not call hipMalloc): dms_decode_attn_noalloc runs the same
+// kernels with their partial records in this file-scope device array, of
+// which each GPU holds its own copy for the life of the process.  Nothing in
+// it has to start at zero (every record is written before it is read within
+// a call).  Its device address is looked up once per device and kept; host
+// code passes that address, never the array's name.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxScratchDevices];
+
+// The scratch array's address on device `dev` (which must be current).
+static int noalloc_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(DMS_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const int s = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (s) return s;
+    if (!p) return fail(DMS_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DMS_OK;
+}
+
 }  // namespace dms
 
 using namespace dms;
@@ -1421,4 +1452,25 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
               linear ? 0 : 1, spin};
   hipLaunchKernelGGL(kern, dim3(npairs + agrid), dim3(256), 0, st, a, ap, pin, sa);
   return check_hip(hipGetLastError(), "dms_decode_step launch");
+}
+
+extern "C" int dms_decode_attn_noalloc(dms_cache* cache, const int32_t* seq_ids, const void* q, void* out, int B,
+                                       void* stream) {
+  if (!cache) return fail(DMS_ERR_ARG, "cache is NULL");
+  if (!q || !out) return fail(DMS_ERR_ARG, "q and out are required");
+  const Geo& g = cache->geo;
+  if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
+  if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
+  const size_t need = decode_workspace_bytes(decode_grid_for(cache), B * g.Hkv, g.g, g.D);
+  if (need > kNoAllocScratchBytes)
+    return fail(DMS_ERR_CAPACITY, "this call needs " + std::to_string(need) +
+                                      " bytes of decode scratch, above the static 8 MiB of dms_decode_attn_noalloc "
+                                      "(use dms_decode_attn with a workspace)");
+  int dev = -1;
+  int s = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (s) return s;
+  if (dev != cache->device) return fail(DMS_ERR_ARG, "the cache's device must be the current device");
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(dev, &ws))) return s;
+  return dms_decode_attn(cache, seq_ids, q, out, B, ws, kNoAllocScratchBytes, stream);
 }

@@ -47,7 +47,7 @@ EXPORTS = (
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
     "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed", "dms_kvzap_score",
     "dms_kvzap_workspace_bytes", "dms_train_attn_bwd", "dms_train_attn_bwd_workspace_bytes",
-    "dms_decode_workspace_bytes",
+    "dms_decode_workspace_bytes", "dms_decode_attn_noalloc",
 )
 
 
@@ -108,6 +108,7 @@ def lib():
             "dms_append_evict": [vp, vp, vp, vp, vp, i32, i32, vp],
             "dms_decode_attn": [vp, vp, vp, vp, i32, vp, sz, vp],
             "dms_decode_workspace_bytes": [cfgp, i32, ctypes.POINTER(sz)],
+            "dms_decode_attn_noalloc": [vp, vp, vp, vp, i32, vp],
             "dms_decode_prepare": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
             "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
             "dms_train_gate": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp],
@@ -467,6 +468,15 @@ def dms_decode_attn(cache: DmsCache, seq_ids, q, out, B: int, workspace=None, st
     return _check(lib().dms_decode_attn(
         cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), _ptr(q, "q", cache.act_dtype, n),
         _ptr(out, "out", cache.act_dtype, n), B, *_ws(cache, workspace, B), _stream(stream)))
+
+
+def dms_decode_attn_noalloc(cache: DmsCache, seq_ids, q, out, B: int, stream=None) -> int:
+    """dms_decode_attn with the library's static per-device scratch (no workspace, no allocation)."""
+    c = cache.cfg
+    n = B * c.num_q_heads * c.head_dim
+    return _check(lib().dms_decode_attn_noalloc(
+        cache.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), _ptr(q, "q", cache.act_dtype, n),
+        _ptr(out, "out", cache.act_dtype, n), B, _stream(stream)))
 
 
 def dms_prefill_attn(cache: DmsCache, seq_ids, q, k, v, evict, out, B: int, C: int, stream=None) -> int:
