@@ -78,6 +78,67 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# A build of the library with the host code under the address and
+# undefined-behaviour sanitizers (device code unoptimised: it is never run),
+# for the host-side tests on a machine without a GPU; kept out of the package.
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_OUT = os.path.join(SAN_DIR, "libdms_san.so")
+SAN_FLAGS = [
+    f"--offload-arch={ARCH}", "-O1", "-Xarch_device", "-O0", "-g", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def sanitized_stale() -> bool:
+    if not os.path.exists(SAN_OUT):
+        return True
+    t = os.path.getmtime(SAN_OUT)
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    return any(os.path.getmtime(f) > t for f in srcs)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(SAN_DIR, exist_ok=True)
+
+    def one(src: str) -> str:
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = SAN_OUT + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_OUT)
+    if verbose:
+        print(f"built {SAN_OUT}")
+    return SAN_OUT
+
+
+def asan_runtime() -> str:
+    """The compiler's address-sanitizer runtime (to preload into a process
+    that is not itself instrumented)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for cand in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if cand and os.path.exists(cand):
+            r = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("address-sanitizer runtime not found")
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -23,80 +23,10 @@ int check_hip(hipError_t e, const char* what) {
   return fail(DMS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int kv_elem_bytes(int kv_dtype) {
-  switch (kv_dtype) {
-    case DMS_F32: return 4;
-    case DMS_BF16: return 2;
-    case DMS_FP8_E4M3: return 1;
-    default: return 0;
-  }
-}
-
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-int compute_layout(const dms_config& c, Layout* L) {
-  const size_t elem = static_cast<size_t>(kv_elem_bytes(c.kv_dtype));
-  const size_t pool = static_cast<size_t>(c.pool_pages);
-  const size_t P = static_cast<size_t>(c.block_size);
-  const size_t D = static_cast<size_t>(c.head_dim);
-  const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
-  const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + P - 1) / P;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off = align256(off + bytes);
-    return at;
-  };
-  L->k_pages = take(pool * P * D * elem);
-  L->v_pages = take(pool * P * D * elem);
-  L->scales = take(pool * 2 * sizeof(float));
-  L->page_amax = take(pool * 2 * sizeof(uint32_t));
-  L->slot_meta = take(pool * P * sizeof(int32_t));
-  L->page_table = take(units * maxp * sizeof(int32_t));
-  L->lengths = take(units * sizeof(int32_t));
-  L->ring = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
-  L->ring_row = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
-  L->cur_page = take(units * sizeof(int32_t));
-  L->pos = take(static_cast<size_t>(c.max_batch) * sizeof(int32_t));
-  L->free_stack = take(pool * sizeof(int32_t));
-  L->ctl = take(kCtlWords * sizeof(int32_t));
-  L->chunk_slot = take(units * static_cast<size_t>(c.max_chunk) * sizeof(int32_t));
-  L->chunk_info = take(units * 8 * sizeof(int32_t));
-  L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
-  L->arrive = take(static_cast<size_t>(kArriveGroups) * kArriveStride * sizeof(int32_t));
-  L->total = off;
-  return DMS_OK;
-}
-
 static int validate(const dms_config* c) {
-  if (!c) return fail(DMS_ERR_ARG, "config is NULL");
-  if (c->max_batch <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
-      c->hidden <= 0 || c->max_tokens_per_seq <= 0 || c->pool_pages <= 0 || c->max_chunk <= 0)
-    return fail(DMS_ERR_CONFIG, "sizes must be positive");
-  if (c->block_size <= 0) return fail(DMS_ERR_CONFIG, "block_size must be > 0");
-  if (c->window <= c->block_size) return fail(DMS_ERR_CONFIG, "window must be greater than block_size");
-  if (c->num_q_heads % c->num_kv_heads != 0)
-    return fail(DMS_ERR_CONFIG, "num_q_heads must be a multiple of num_kv_heads");
-  const int g = c->num_q_heads / c->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8) return fail(DMS_ERR_CONFIG, "group size must be 1, 2, 4 or 8");
-  if (c->num_kv_heads > 16) return fail(DMS_ERR_CONFIG, "num_kv_heads must be <= 16");
-  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
-    return fail(DMS_ERR_CONFIG, "head_dim must be 32, 64 or 128");
-  if (c->hidden % 4 != 0) return fail(DMS_ERR_CONFIG, "hidden must be a multiple of 4");
-  if (kv_elem_bytes(c->kv_dtype) == 0) return fail(DMS_ERR_CONFIG, "bad kv_dtype");
-  if (c->decide_mode != DMS_DECIDE_LINEAR && c->decide_mode != DMS_DECIDE_QNEURON)
-    return fail(DMS_ERR_CONFIG, "bad decide_mode");
-  if (c->alpha_per != DMS_ALPHA_PER_HEAD && c->alpha_per != DMS_ALPHA_PER_LAYER)
-    return fail(DMS_ERR_CONFIG, "alpha_per must be head or layer");
-  if (c->max_chunk > kMaxChunk) return fail(DMS_ERR_CONFIG, "max_chunk above 8192");
-  if (static_cast<int64_t>(c->max_batch) * c->num_kv_heads > kMaxUnits)
-    return fail(DMS_ERR_CONFIG, "max_batch * num_kv_heads above 2048");
-  if (!(c->alpha_scale == c->alpha_scale) || !(c->rms_eps >= 0.0f) || !(c->softmax_scale >= 0.0f))
-    return fail(DMS_ERR_CONFIG, "alpha_scale, rms_eps and softmax_scale must be finite, eps and scale >= 0");
-  if (static_cast<int64_t>(c->pool_pages) * c->block_size >= (1ll << 31))
-    return fail(DMS_ERR_CONFIG, "pool_pages * block_size must stay below 2^31");
-  if (c->max_tokens_per_seq >= (1 << 30)) return fail(DMS_ERR_CONFIG, "max_tokens_per_seq too large");
-  return DMS_OK;
+  int status = DMS_OK;
+  const char* why = config_error(c, &status);
+  return why ? fail(status, why) : DMS_OK;
 }
 
 int decode_grid_for(const dms_cache* c) { return c->decode_grid; }
@@ -408,19 +338,8 @@ int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out) {
   d.positions = pos.data();
   int s = dms_cache_dump(cache, stream, &d);
   if (s) return s;
-  int64_t tokens = 0, live = 0, pages = 0;
-  for (int b = 0; b < g.Bmax; ++b) tokens += static_cast<int64_t>(pos[b]) * g.Hkv;
-  for (int32_t L : len) {
-    live += L;
-    pages += (L + g.P - 1) / g.P;
-  }
-  const int64_t row_bytes = static_cast<int64_t>(g.D) * kv_elem_bytes(g.kv_dtype);
-  out->tokens = tokens;
-  out->live_slots = live;
-  out->pages_in_use = pages;
-  out->bytes_live = live * row_bytes * 2;
-  out->bytes_allocated = pages * g.P * row_bytes * 2;
-  out->cache_cr = live ? static_cast<double>(tokens) / static_cast<double>(live) : 0.0;
+  stats_from_tables(g.Bmax, g.Hkv, g.P, static_cast<int64_t>(g.D) * kv_elem_bytes(g.kv_dtype), len.data(),
+                    pos.data(), out);
   return DMS_OK;
 }
 
@@ -441,15 +360,7 @@ int dms_seq_info_get(dms_cache* cache, const int32_t* seq_ids, int n, void* stre
   for (int i = 0; i < n; ++i) {
     const int seq = seq_ids ? seq_ids[i] : i;
     if (seq < 0 || seq >= g.Bmax) return fail(DMS_ERR_ARG, "sequence id outside [0, max_batch)");
-    dms_seq_info r{};
-    r.position = pos[seq];
-    for (int k = 0; k < g.Hkv; ++k) {
-      const int32_t L = len[static_cast<size_t>(seq) * g.Hkv + k];
-      r.live_slots += L;
-      r.max_head_slots = std::max(r.max_head_slots, L);
-      r.pages += (L + g.P - 1) / g.P;
-    }
-    out[i] = r;
+    out[i] = seq_info_from_tables(seq, g.Hkv, g.P, len.data(), pos.data());
   }
   return DMS_OK;
 }
@@ -474,27 +385,8 @@ int dms_pages_needed(dms_cache* cache, const int32_t* seq_ids, const int32_t* n_
     if (seq < 0 || seq >= g.Bmax) return fail(DMS_ERR_ARG, "sequence id outside [0, max_batch)");
     const int64_t m = n_new[i];
     if (m < 0) return fail(DMS_ERR_ARG, "negative token count");
-    const int64_t t0 = pos[seq];
-    if (t0 + m > g.max_tokens) {
-      pages_out[i] = -1;   // beyond max_tokens_per_seq: the append would be refused
-      continue;
-    }
-    int64_t pages = 0;
-    for (int k = 0; k < g.Hkv; ++k) {
-      const size_t u = static_cast<size_t>(seq) * g.Hkv + k;
-      // new token t = t0 + j overwrites the slot of position t - w in place
-      // when that token was marked; for j < w that token is already in the
-      // ring (its mark is known), later ones are the new tokens (worst case:
-      // kept, so a new slot)
-      int64_t overwrites = 0;
-      for (int64_t j = 0; j < std::min<int64_t>(m, g.w); ++j) {
-        const int64_t p = t0 + j - g.w;
-        if (p >= 0 && ring[u * g.w + static_cast<size_t>(p % g.w)] < 0) ++overwrites;
-      }
-      const int64_t L = len[u], slots = L + (m - overwrites);
-      pages += (slots + g.P - 1) / g.P - (L + g.P - 1) / g.P;
-    }
-    pages_out[i] = pages;
+    // beyond max_tokens_per_seq (-1): the append would be refused
+    pages_out[i] = worst_pages_for_seq(seq, m, g.Hkv, g.w, g.P, g.max_tokens, len.data(), pos.data(), ring.data());
   }
   if (free_pages) *free_pages = freec;
   return DMS_OK;

@@ -10,23 +10,13 @@
 #include <string>
 
 #include "dms.h"
+#include "host_logic.h"
 
 namespace dms {
 
-constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
-constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
-constexpr int kMaxDecodeGrid = 2048;   // workgroups of the decode attention kernel
-constexpr int kCtlWords = 64;
 constexpr int kCtlFreeCount = 0;
 constexpr int kCtlStatus = 1;
 constexpr int kCtlPrepArrive = 2;    // arrival counter of the fused decode decision + append
-// Arrival counters of the fused decode step's attention workgroups: workgroup
-// i adds one to group i % kArriveGroups (an atomic whose result it does not
-// wait for); the committing workgroup polls the groups.  One counter per
-// 256-byte line, so the adds of different groups do not queue behind each
-// other.
-constexpr int kArriveGroups = 32;
-constexpr int kArriveStride = 64;    // int32 words between counters
 constexpr int kArriveSpinLimit = 1 << 18;   // polls (each a device-scope load and a short sleep)
 
 // Device pointers carved out of the caller's buffer (see compute_layout).
@@ -58,11 +48,6 @@ struct Geo {
   float scale_log2;      // softmax scale * log2(e)
 };
 
-struct Layout {
-  size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, total;
-};
-
 }  // namespace dms
 
 struct dms_cache {
@@ -86,8 +71,6 @@ namespace dms {
 // Error reporting (thread-local message).
 int fail(int status, const std::string& msg);
 int check_hip(hipError_t e, const char* what);
-int kv_elem_bytes(int kv_dtype);
-int compute_layout(const dms_config& c, Layout* L);
 int decode_grid_for(const dms_cache* c);
 // Decode attention workgroups on a device with `cus` compute units (2 per CU,
 // or DMS_DECODE_WGS), capped at kMaxDecodeGrid.

@@ -1,0 +1,171 @@
+// Host-side logic of the DMS C ABI that needs no GPU: configuration checks,
+// the layout of the single cache buffer, and the statistics and serving
+// accounting computed from host copies of the cache tables.  Plain C++17 (no
+// HIP), so that it can also be built and checked on its own, under the
+// address and undefined-behaviour sanitizers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "dms.h"
+
+namespace dms {
+
+constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
+constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
+constexpr int kMaxDecodeGrid = 2048;   // workgroups of the decode attention kernel
+constexpr int kCtlWords = 64;
+// Arrival counters of the fused decode step's attention workgroups: workgroup
+// i adds one to group i % kArriveGroups (an atomic whose result it does not
+// wait for); the committing workgroup polls the groups.  One counter per
+// 256-byte line, so the adds of different groups do not queue behind each
+// other.
+constexpr int kArriveGroups = 32;
+constexpr int kArriveStride = 64;      // int32 words between counters
+
+// Byte offsets of the regions carved out of one cache buffer.
+struct Layout {
+  size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+inline int kv_elem_bytes(int kv_dtype) {
+  switch (kv_dtype) {
+    case DMS_F32: return 4;
+    case DMS_BF16: return 2;
+    case DMS_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+// nullptr when the configuration is valid; otherwise the reason, with the
+// status code in *status (walkthrough, Qwen3ConfigDMS hard constraints:
+// block_size > 0 and window > block_size; the rest are this library's limits).
+inline const char* config_error(const dms_config* c, int* status) {
+  *status = DMS_ERR_CONFIG;
+  if (!c) {
+    *status = DMS_ERR_ARG;
+    return "config is NULL";
+  }
+  if (c->max_batch <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->hidden <= 0 ||
+      c->max_tokens_per_seq <= 0 || c->pool_pages <= 0 || c->max_chunk <= 0)
+    return "sizes must be positive";
+  if (c->block_size <= 0) return "block_size must be > 0";
+  if (c->window <= c->block_size) return "window must be greater than block_size";
+  if (c->num_q_heads % c->num_kv_heads != 0) return "num_q_heads must be a multiple of num_kv_heads";
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return "group size must be 1, 2, 4 or 8";
+  if (c->num_kv_heads > 16) return "num_kv_heads must be <= 16";
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 32, 64 or 128";
+  if (c->hidden % 4 != 0) return "hidden must be a multiple of 4";
+  if (kv_elem_bytes(c->kv_dtype) == 0) return "bad kv_dtype";
+  if (c->decide_mode != DMS_DECIDE_LINEAR && c->decide_mode != DMS_DECIDE_QNEURON) return "bad decide_mode";
+  if (c->alpha_per != DMS_ALPHA_PER_HEAD && c->alpha_per != DMS_ALPHA_PER_LAYER) return "alpha_per must be head or layer";
+  if (c->max_chunk > kMaxChunk) return "max_chunk above 8192";
+  if (static_cast<int64_t>(c->max_batch) * c->num_kv_heads > kMaxUnits) return "max_batch * num_kv_heads above 2048";
+  if (!(c->alpha_scale == c->alpha_scale) || !(c->rms_eps >= 0.0f) || !(c->softmax_scale >= 0.0f))
+    return "alpha_scale, rms_eps and softmax_scale must be finite, eps and scale >= 0";
+  if (static_cast<int64_t>(c->pool_pages) * c->block_size >= (1ll << 31))
+    return "pool_pages * block_size must stay below 2^31";
+  if (c->max_tokens_per_seq >= (1 << 30)) return "max_tokens_per_seq too large";
+  *status = DMS_OK;
+  return nullptr;
+}
+
+// The regions of one cache buffer, each 256-byte aligned, in this order (the
+// configuration must be valid).
+inline void compute_layout(const dms_config& c, Layout* L) {
+  const size_t elem = static_cast<size_t>(kv_elem_bytes(c.kv_dtype));
+  const size_t pool = static_cast<size_t>(c.pool_pages);
+  const size_t P = static_cast<size_t>(c.block_size);
+  const size_t D = static_cast<size_t>(c.head_dim);
+  const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
+  const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + P - 1) / P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->k_pages = take(pool * P * D * elem);
+  L->v_pages = take(pool * P * D * elem);
+  L->scales = take(pool * 2 * sizeof(float));
+  L->page_amax = take(pool * 2 * sizeof(uint32_t));
+  L->slot_meta = take(pool * P * sizeof(int32_t));
+  L->page_table = take(units * maxp * sizeof(int32_t));
+  L->lengths = take(units * sizeof(int32_t));
+  L->ring = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
+  L->ring_row = take(units * static_cast<size_t>(c.window) * sizeof(int32_t));
+  L->cur_page = take(units * sizeof(int32_t));
+  L->pos = take(static_cast<size_t>(c.max_batch) * sizeof(int32_t));
+  L->free_stack = take(pool * sizeof(int32_t));
+  L->ctl = take(kCtlWords * sizeof(int32_t));
+  L->chunk_slot = take(units * static_cast<size_t>(c.max_chunk) * sizeof(int32_t));
+  L->chunk_info = take(units * 8 * sizeof(int32_t));
+  L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
+  L->arrive = take(static_cast<size_t>(kArriveGroups) * kArriveStride * sizeof(int32_t));
+  L->total = off;
+}
+
+// Occupancy from the per-head lengths [Bmax][Hkv] and positions [Bmax]
+// (walkthrough, 损失函数与压缩比调度: realised compression, here tokens / live
+// slots).
+inline void stats_from_tables(int Bmax, int Hkv, int P, int64_t row_bytes, const int32_t* len, const int32_t* pos,
+                              dms_stats* out) {
+  int64_t tokens = 0, live = 0, pages = 0;
+  for (int b = 0; b < Bmax; ++b) tokens += static_cast<int64_t>(pos[b]) * Hkv;
+  for (int64_t i = 0; i < static_cast<int64_t>(Bmax) * Hkv; ++i) {
+    live += len[i];
+    pages += (len[i] + P - 1) / P;
+  }
+  out->tokens = tokens;
+  out->live_slots = live;
+  out->pages_in_use = pages;
+  out->bytes_live = live * row_bytes * 2;
+  out->bytes_allocated = pages * P * row_bytes * 2;
+  out->cache_cr = live ? static_cast<double>(tokens) / static_cast<double>(live) : 0.0;
+}
+
+// Footprint of sequence seq (FastDMS post, subsystem table: memory accounting
+// by surviving tokens).
+inline dms_seq_info seq_info_from_tables(int seq, int Hkv, int P, const int32_t* len, const int32_t* pos) {
+  dms_seq_info r{};
+  r.position = pos[seq];
+  for (int k = 0; k < Hkv; ++k) {
+    const int32_t L = len[static_cast<size_t>(seq) * Hkv + k];
+    r.live_slots += L;
+    if (L > r.max_head_slots) r.max_head_slots = L;
+    r.pages += (L + P - 1) / P;
+  }
+  return r;
+}
+
+// The most pool pages that appending n more tokens to sequence seq can take
+// (FastDMS post, subsystem table: admission by compact capacity): every new
+// token kept, except that the first w of them overwrite in place the slots of
+// already-marked tokens in the window (walkthrough, 推理模式); -1 past
+// max_tokens.  len [Bmax][Hkv], pos [Bmax], ring [Bmax][Hkv][w] (slot |
+// evict << 31 of position p at p % w).
+inline int64_t worst_pages_for_seq(int seq, int64_t n, int Hkv, int w, int P, int max_tokens, const int32_t* len,
+                                   const int32_t* pos, const int32_t* ring) {
+  const int64_t t0 = pos[seq];
+  if (t0 + n > max_tokens) return -1;
+  int64_t pages = 0;
+  for (int k = 0; k < Hkv; ++k) {
+    const size_t u = static_cast<size_t>(seq) * Hkv + k;
+    int64_t overwrites = 0;
+    const int64_t first = n < w ? n : w;
+    for (int64_t j = 0; j < first; ++j) {
+      const int64_t p = t0 + j - w;
+      if (p >= 0 && ring[u * w + static_cast<size_t>(p % w)] < 0) ++overwrites;
+    }
+    const int64_t L = len[u], slots = L + (n - overwrites);
+    pages += (slots + P - 1) / P - (L + P - 1) / P;
+  }
+  return pages;
+}
+
+}  // namespace dms

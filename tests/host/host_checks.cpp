@@ -1,0 +1,208 @@
+// Host-side checks of the DMS library's pure C++ logic (host_logic.h), built
+// with the address and undefined-behaviour sanitizers by
+// tests/test_host_sanitizers.py: configuration checks, the cache buffer's
+// layout, statistics and the serving accounting (worst-case pages of a
+// continuation against a brute-force replay of the slot rule).
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "host_logic.h"
+
+using namespace dms;
+
+static int g_fail = 0;
+#define CHECK(cond)                                                      \
+  do {                                                                   \
+    if (!(cond)) {                                                       \
+      std::fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #cond); \
+      ++g_fail;                                                          \
+    }                                                                    \
+  } while (0)
+
+static dms_config base() {
+  dms_config c{};
+  c.max_batch = 2;
+  c.num_q_heads = 8;
+  c.num_kv_heads = 2;
+  c.head_dim = 64;
+  c.hidden = 256;
+  c.window = 16;
+  c.block_size = 8;
+  c.max_tokens_per_seq = 100;
+  c.pool_pages = 32;
+  c.max_chunk = 64;
+  c.kv_dtype = DMS_BF16;
+  c.decide_mode = DMS_DECIDE_LINEAR;
+  c.alpha_per = DMS_ALPHA_PER_HEAD;
+  c.alpha_scale = 100.0f;
+  c.rms_eps = 1e-6f;
+  return c;
+}
+
+static void check_config() {
+  int st = -99;
+  dms_config c = base();
+  CHECK(config_error(&c, &st) == nullptr && st == DMS_OK);
+  CHECK(config_error(nullptr, &st) != nullptr && st == DMS_ERR_ARG);
+  struct Case {
+    void (*edit)(dms_config&);
+    const char* msg;
+  };
+  const Case cases[] = {
+      {[](dms_config& x) { x.block_size = 0; }, "block_size"},
+      {[](dms_config& x) { x.window = 8; }, "window must be greater"},
+      {[](dms_config& x) { x.num_q_heads = 6; x.num_kv_heads = 4; }, "multiple"},
+      {[](dms_config& x) { x.num_q_heads = 24; }, "group size"},
+      {[](dms_config& x) { x.head_dim = 96; }, "head_dim"},
+      {[](dms_config& x) { x.hidden = 130; }, "hidden"},
+      {[](dms_config& x) { x.max_chunk = 10000; }, "max_chunk"},
+      {[](dms_config& x) { x.max_batch = 0; }, "positive"},
+      {[](dms_config& x) { x.max_batch = 300; x.num_kv_heads = 8; x.num_q_heads = 32; }, "2048"},
+      {[](dms_config& x) { x.kv_dtype = 7; }, "kv_dtype"},
+      {[](dms_config& x) { x.alpha_per = 2; }, "alpha_per"},
+      {[](dms_config& x) { x.decide_mode = 5; }, "decide_mode"},
+      {[](dms_config& x) { x.rms_eps = -1.0f; }, "eps"},
+      {[](dms_config& x) { x.alpha_scale = NAN; }, "finite"},
+      {[](dms_config& x) { x.pool_pages = 1 << 28; }, "2^31"},
+      {[](dms_config& x) { x.max_tokens_per_seq = 1 << 30; }, "too large"},
+      {[](dms_config& x) { x.num_kv_heads = 32; x.num_q_heads = 32; }, "<= 16"},
+  };
+  for (const Case& k : cases) {
+    dms_config x = base();
+    k.edit(x);
+    const char* why = config_error(&x, &st);
+    CHECK(why != nullptr && st == DMS_ERR_CONFIG && std::strstr(why, k.msg) != nullptr);
+  }
+}
+
+static void check_layout() {
+  std::mt19937 rng(12345);
+  auto pick = [&](std::initializer_list<int> v) { return *(v.begin() + rng() % v.size()); };
+  for (int it = 0; it < 2000; ++it) {
+    dms_config c = base();
+    c.num_kv_heads = pick({1, 2, 4, 8, 16});
+    c.num_q_heads = c.num_kv_heads * pick({1, 2, 4, 8});
+    c.max_batch = 1 + static_cast<int>(rng() % (kMaxUnits / c.num_kv_heads));
+    c.head_dim = pick({32, 64, 128});
+    c.block_size = pick({1, 7, 16, 256, 1000});
+    c.window = c.block_size + 1 + static_cast<int>(rng() % 600);
+    c.max_tokens_per_seq = 1 + static_cast<int>(rng() % 40000);
+    c.pool_pages = 1 + static_cast<int>(rng() % 5000);
+    c.max_chunk = 1 + static_cast<int>(rng() % kMaxChunk);
+    c.kv_dtype = pick({DMS_F32, DMS_BF16, DMS_FP8_E4M3});
+    int st;
+    if (config_error(&c, &st)) continue;
+    Layout L;
+    compute_layout(c, &L);
+    const size_t off[] = {L.k_pages, L.v_pages, L.scales, L.page_amax, L.slot_meta, L.page_table, L.lengths, L.ring,
+                          L.ring_row, L.cur_page, L.pos, L.free_stack, L.ctl, L.chunk_slot, L.chunk_info,
+                          L.unit_info, L.arrive, L.total};
+    const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
+    const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + c.block_size - 1) / c.block_size;
+    const size_t pool = c.pool_pages, P = c.block_size;
+    const size_t need[] = {pool * P * c.head_dim * kv_elem_bytes(c.kv_dtype),
+                           pool * P * c.head_dim * kv_elem_bytes(c.kv_dtype),
+                           pool * 8, pool * 8, pool * P * 4, units * maxp * 4, units * 4,
+                           units * c.window * 4, units * c.window * 4, units * 4, static_cast<size_t>(c.max_batch) * 4,
+                           pool * 4, kCtlWords * 4, units * c.max_chunk * 4, units * 32, kMaxUnits * 16,
+                           kArriveGroups * kArriveStride * 4};
+    CHECK(L.k_pages == 0);
+    for (int r = 0; r < 17; ++r) {
+      CHECK(off[r] % 256 == 0);
+      CHECK(off[r + 1] >= off[r] + need[r]);          // no region overlaps the next
+      CHECK(off[r + 1] - off[r] < need[r] + 256);     // and no more than alignment in between
+    }
+  }
+}
+
+static void check_stats_and_info() {
+  std::mt19937 rng(7);
+  for (int it = 0; it < 200; ++it) {
+    const int Bmax = 1 + rng() % 40, Hkv = 1 + rng() % 16, P = 1 + rng() % 300;
+    std::vector<int32_t> len(static_cast<size_t>(Bmax) * Hkv), pos(Bmax);
+    for (auto& v : pos) v = rng() % 20000;
+    for (int b = 0; b < Bmax; ++b)
+      for (int k = 0; k < Hkv; ++k) len[b * Hkv + k] = pos[b] ? static_cast<int32_t>(rng() % (pos[b] + 1)) : 0;
+    dms_stats s;
+    const int64_t rb = 256;
+    stats_from_tables(Bmax, Hkv, P, rb, len.data(), pos.data(), &s);
+    int64_t tok = 0, live = 0, pages = 0;
+    for (int b = 0; b < Bmax; ++b) {
+      tok += static_cast<int64_t>(pos[b]) * Hkv;
+      const dms_seq_info si = seq_info_from_tables(b, Hkv, P, len.data(), pos.data());
+      int64_t sl = 0, sp = 0, mx = 0;
+      for (int k = 0; k < Hkv; ++k) {
+        const int64_t L = len[b * Hkv + k];
+        sl += L;
+        sp += (L + P - 1) / P;
+        mx = L > mx ? L : mx;
+      }
+      CHECK(si.position == pos[b] && si.live_slots == sl && si.pages == sp && si.max_head_slots == mx);
+      live += sl;
+      pages += sp;
+    }
+    CHECK(s.tokens == tok && s.live_slots == live && s.pages_in_use == pages);
+    CHECK(s.bytes_live == live * rb * 2 && s.bytes_allocated == pages * P * rb * 2);
+    CHECK(live == 0 ? s.cache_cr == 0.0 : std::fabs(s.cache_cr - double(tok) / double(live)) < 1e-12);
+  }
+}
+
+// Replays the slot rule (a token w positions after a marked one takes its
+// slot in place, any other token a new slot) over a random history of one
+// head, then appends n kept tokens; returns the pages the continuation adds.
+static void replay(int w, int P, const std::vector<int>& marks, int n, int32_t* len_out, std::vector<int32_t>* ring,
+                   int64_t* pages_added) {
+  const int t0 = static_cast<int>(marks.size());
+  std::vector<int> slot(t0 + n), mark(marks);
+  mark.resize(t0 + n, 0);
+  int64_t L = 0;
+  for (int t = 0; t < t0 + n; ++t) {
+    if (t >= w && mark[t - w]) slot[t] = slot[t - w];
+    else slot[t] = static_cast<int>(L++);
+    if (t == t0 - 1) *len_out = static_cast<int32_t>(L);
+  }
+  if (t0 == 0) *len_out = 0;
+  ring->assign(w, 0);
+  for (int t = (t0 > w ? t0 - w : 0); t < t0; ++t)
+    (*ring)[t % w] = static_cast<int32_t>(static_cast<uint32_t>(slot[t]) | (static_cast<uint32_t>(mark[t]) << 31));
+  const int64_t L0 = *len_out;
+  *pages_added = (L + P - 1) / P - (L0 + P - 1) / P;
+}
+
+static void check_worst_pages() {
+  std::mt19937 rng(99);
+  for (int it = 0; it < 3000; ++it) {
+    const int P = 1 + rng() % 8;
+    const int w = P + 1 + rng() % 9;
+    const int t0 = rng() % 60, n = rng() % 40;
+    const double p = (rng() % 100) / 100.0;
+    std::vector<int> marks(t0);
+    for (auto& m : marks) m = (rng() % 1000) < p * 1000 ? 1 : 0;
+    int32_t len = 0;
+    std::vector<int32_t> ring;
+    int64_t want = 0;
+    replay(w, P, marks, n, &len, &ring, &want);
+    const int32_t pos = t0;
+    const int max_tokens = t0 + n + static_cast<int>(rng() % 3);
+    CHECK(worst_pages_for_seq(0, n, 1, w, P, max_tokens, &len, &pos, ring.data()) == want);
+    CHECK(worst_pages_for_seq(0, n, 1, w, P, t0 + n - 1, &len, &pos, ring.data()) == -1);   // one past capacity
+  }
+}
+
+int main() {
+  check_config();
+  check_layout();
+  check_stats_and_info();
+  check_worst_pages();
+  if (g_fail) {
+    std::fprintf(stderr, "%d checks failed\n", g_fail);
+    return 1;
+  }
+  std::printf("host checks ok\n");
+  return 0;
+}
