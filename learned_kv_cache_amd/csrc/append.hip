@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kAppThreads) void append_decode_kernel(AppendArgs a
   const int npairs = a.B * g.Hkv;
   const int in_row_bytes = g.D * static_cast<int>(sizeof(ACT));
   const int ppr = in_row_bytes / 16;                       // 16-byte pieces per row
+  if (blockIdx.x == 0 && tid == 0) plan_invalidate(d);
   const int page_row_bytes = g.D * (KV == DMS_F32 ? 4 : (KV == DMS_BF16 ? 2 : 1));
   if (tid == 0) {
     s_free = d.ctl[kCtlFreeCount];
@@ -242,6 +243,7 @@ template <int KV>
 __global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(AppendArgs a, PrepIn in) {
   __shared__ PrepShared sh;
   const int npairs = a.B * a.g.Hkv;
+  if (blockIdx.x == 0 && threadIdx.x == 0) plan_invalidate(a.d);
   prep_pair<KV>(a, in, blockIdx.x, false, sh);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -273,6 +275,7 @@ __global__ __launch_bounds__(1024) void chunk_plan_kernel(AppendArgs a) {
   const int pair = blockIdx.x;
   const int row = pair / g.Hkv, kh = pair % g.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (pair == 0 && tid == 0) plan_invalidate(d);
   int32_t* info = d.chunk_info + static_cast<int64_t>(pair) * 8;
   const int seq = a.seq_ids ? a.seq_ids[row] : row;
   if (seq < 0 || seq >= g.Bmax) {

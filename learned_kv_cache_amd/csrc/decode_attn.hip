@@ -762,6 +762,21 @@ __device__ __forceinline__ int unit_slots(const DecodeArgs& a, int u, int wg, in
   return L;
 }
 
+// The decode plan (fused step): the kernel variant a plan was split for, and
+// where its rows and records start.
+template <int D, int G, bool FP8, int LPR>
+__device__ __forceinline__ constexpr int plan_variant() {
+  return D | (G << 8) | ((FP8 ? 1 : 0) << 12) | (LPR << 16) | (1 << 24);
+}
+__device__ __forceinline__ int32_t* plan_rows(const DevCache& d) { return d.plan + kPlanHeader; }
+__device__ __forceinline__ int32_t* plan_records(const DevCache& d, const Geo& g) {
+  return d.plan + kPlanHeader + ((g.Bmax + 63) & ~63);
+}
+// record words
+constexpr int kRecUnit = 0, kRecLo = 1, kRecHi = 2, kRecRows = 3, kRecExt = 4, kRecW0 = 5, kRecW1 = 6,
+              kRecScalePage = 7, kRecNpages = 8, kRecPages = 9;
+constexpr int kRecMaxPages = kPlanRec - kRecPages;
+
 // The attention of dms_decode_attn (workgroup wg of `grid`).  STEP: the
 // attention of the fused decode step, run before the current token is in the
 // cache: each unit's rows are its live slots plus one more, the current
@@ -785,12 +800,64 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
 
   int* s_start = lds.start;
   int* s_tmp = lds.tmp;
+  int* s_wstart = lds.wstart;
   const DevCache& d = a.d;
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lane_row = lane / LPR, lane_col = lane % LPR;
   const int units = a.B * g.Hkv;
 
+  // STEP: the plan the previous step's commit left, when it was made for this
+  // kernel, grid, batch and row-to-sequence mapping and nothing has changed
+  // the cache since (every other call that does clears it).  It gives this
+  // workgroup's unit, row range, page ids and the next token's placement in
+  // one load, in place of the length, position and ring reads, the scans
+  // and the page-table read.
+  bool use_plan = false;
+  int p_u = 0, p_lo = 0, p_hi = 0, p_rows = 0, p_ext = -1, p_w0 = 0, p_w1 = 0, p_spage = -1, p_np = -1, p_page = 0;
+  if constexpr (STEP) {
+    if (grid <= kPlanMaxWgs) {
+      const int32_t* P = d.plan;
+      const int32_t* rec = plan_records(d, g) + static_cast<int64_t>(wg) * kPlanRec;
+      const int rv = rec[lane & (kPlanRec - 1)];
+      p_page = rec[kRecPages + min(lane, kRecMaxPages - 1)];
+      const int nrec = P[kPlanNrec];
+      int bad = !(P[kPlanValid] == 1 && P[kPlanB] == a.B && P[kPlanGrid] == grid &&
+                  P[kPlanSeqNull] == (a.seq_ids == nullptr ? 1 : 0) &&
+                  P[kPlanVariant] == plan_variant<D, G, FP8, LPR>());
+      for (int r = tid; r < a.B; r += 256)
+        if ((a.seq_ids ? a.seq_ids[r] : r) != plan_rows(d)[r]) bad = 1;
+      use_plan = !__syncthreads_or(bad);
+      if (use_plan) {
+        p_u = __builtin_amdgcn_readlane(rv, kRecUnit);
+        p_lo = __builtin_amdgcn_readlane(rv, kRecLo);
+        p_hi = __builtin_amdgcn_readlane(rv, kRecHi);
+        p_rows = __builtin_amdgcn_readlane(rv, kRecRows);
+        p_ext = __builtin_amdgcn_readlane(rv, kRecExt);
+        p_w0 = __builtin_amdgcn_readlane(rv, kRecW0);
+        p_w1 = __builtin_amdgcn_readlane(rv, kRecW1);
+        p_spage = __builtin_amdgcn_readlane(rv, kRecScalePage);
+        p_np = __builtin_amdgcn_readlane(rv, kRecNpages);
+        // every plan word this workgroup uses has arrived (the commit
+        // rewrites the plan once all have arrived), and nothing it reads
+        // later can change: arrive
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        if (tid == 0)
+          __hip_atomic_fetch_add(d.arrive + (wg % sa->groups) * kArriveStride, 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (wg >= nrec) return;
+      }
+    }
+  }
+
+  int W = 0, c = 0;
+  bool aligned = true;
+  int a0, a1, u;
+  if (use_plan) {
+    u = p_u;
+    a0 = p_lo;
+    a1 = p_hi;
+  } else {
   // -- unit prefix (live slots of every (row, KV head), concatenated) --------
   if (units <= 64) {
     if (wave == 0) {
@@ -841,16 +908,15 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       __hip_atomic_fetch_add(d.arrive + (wg % sa->groups) * kArriveStride, 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
-  const int W = s_start[units];
-  const int c = max((W + grid - 1) / grid, RPP);
+  W = s_start[units];
+  c = max((W + grid - 1) / grid, RPP);
   // Few units: each unit gets workgroups of its own, ceil(slots / ca) of
   // them for a cap of ca = ceil(W / (grid - units)) slots per workgroup (at
   // most one per RPP rows and kMaxSplit in all), so no workgroup spans two
   // units (a second segment would repeat the setup and the merge);
   // sum(ceil(slots / ca)) <= W / ca + units <= grid.  Otherwise the
   // concatenated slots are cut into equal ranges.
-  const bool aligned = units <= kAlignedUnits && 2 * units <= grid;
-  int* s_wstart = lds.wstart;
+  aligned = units <= kAlignedUnits && 2 * units <= grid;
   if (aligned) {
     const int ca = max(1, (W + (grid - units) - 1) / (grid - units));
     const int u0 = tid * 2;
@@ -877,17 +943,19 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     __syncthreads();
   }
 
-  // heads without live slots have no workgroup: workgroup 0 writes zeros
-  if (wg == 0) {
-    uint16_t* ob = static_cast<uint16_t*>(a.out);
-    for (int uu = 0; uu < units; ++uu) {
+  // heads without live slots have no workgroup: the last workgroup writes
+  // their zeros (a thread per unit; it is the one most often left without
+  // slots of its own, and no merge waits for it)
+  if (wg == grid - 1) {
+    uint4* ob = static_cast<uint4*>(a.out);
+    for (int uu = tid; uu < units; uu += 256) {
       if (s_start[uu + 1] != s_start[uu]) continue;
       const int row = uu / g.Hkv, kh = uu % g.Hkv;
-      for (int idx = tid; idx < G * D; idx += 256) ob[(static_cast<size_t>(row) * g.Hq + kh * G) * D + idx] = 0;
+      uint4* dst = ob + (static_cast<size_t>(row) * g.Hq + kh * G) * D / 8;
+      for (int i = 0; i < G * D / 8; ++i) dst[i] = make_uint4(0, 0, 0, 0);
     }
   }
 
-  int a0, a1, u;
   if (aligned) {
     if (wg >= s_wstart[units]) return;
     // the unit owning workgroup wg: the last u with s_wstart[u] <= wg (units without slots share starts)
@@ -913,13 +981,14 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     }
     u = lo_u;
   }
+  }
   bool first_seg = true;
   uint16_t* obase = static_cast<uint16_t*>(a.out);
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
   const int psh = g.Pshift, pmask = g.P - 1;
 
   while (a0 < a1) {
-    const int ustart = s_start[u], uend = s_start[u + 1];
+    const int ustart = use_plan ? 0 : s_start[u], uend = use_plan ? p_rows : s_start[u + 1];
     const int seg_end = min(a1, uend);
     const int lo = a0 - ustart, hi = seg_end - ustart;
     const int row = u / g.Hkv, kh = u % g.Hkv;
@@ -929,7 +998,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     const uint8_t* kin = nullptr;
     const uint8_t* vin = nullptr;
     if constexpr (STEP) {
-      const int ext = lds.ext[u];
+      const int ext = use_plan ? p_ext : lds.ext[u];
       if (ext >= 0) {
         vrow = uend - ustart - 1;
         skip = ext - 1;
@@ -961,7 +1030,8 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
           vsk = page_scale_from_amax(mk);
           vsv = page_scale_from_amax(mv);
         } else {
-          const int page = skip >= 0 ? pt[skip >> psh] : d.cur_page[static_cast<int64_t>(seq) * g.Hkv + kh];
+          const int page = use_plan ? p_spage
+                                    : skip >= 0 ? pt[skip >> psh] : d.cur_page[static_cast<int64_t>(seq) * g.Hkv + kh];
           vsk = d.scales[2 * page];
           vsv = d.scales[2 * page + 1];
         }
@@ -1015,7 +1085,8 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     // flight while chunk i is computed
     for (int pb = lo >> psh; pb <= (hi - 1) >> psh; pb += 64) {
       const int plast = min((hi - 1) >> psh, pb + 63);
-      const int pt_reg = (pb + lane <= plast) ? pt[pb + lane] : 0;
+      const bool from_plan = use_plan && p_np > 0;       // the range's pages (at most kRecMaxPages) are in the record
+      const int pt_reg = from_plan ? (lane < p_np ? p_page : 0) : (pb + lane <= plast) ? pt[pb + lane] : 0;
       const int blo = max(lo, pb << psh), bhi = min(hi, (plast + 1) << psh);
       const int npass = (bhi - blo + RPP - 1) / RPP;
       // The next chunk's loads are issued before the current chunk's compute,
@@ -1074,8 +1145,8 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
     __syncthreads();
     // the unit's workgroups w0..w1 (concatenated split: w0's record is its
     // second one when the unit starts inside w0's range)
-    const int w0 = aligned ? s_wstart[u] : ustart / c;
-    const int w1 = aligned ? s_wstart[u + 1] - 1 : (uend - 1) / c;
+    const int w0 = use_plan ? p_w0 : aligned ? s_wstart[u] : ustart / c;
+    const int w1 = use_plan ? p_w1 : aligned ? s_wstart[u + 1] - 1 : (uend - 1) / c;
     const int odd = (!aligned && ustart != w0 * c) ? 1 : 0;
     const bool split = w1 > w0;
     const int rec = 2 * wg + (first_seg ? 0 : 1);
@@ -1124,6 +1195,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       }
     }
     __syncthreads();
+    if (use_plan) break;
     first_seg = false;
     a0 = seg_end;
     ++u;
@@ -1136,6 +1208,139 @@ template <int D, int G, int NP, bool FP8, int LPR>
 __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
   __shared__ FastLds<G, D, false> lds;
   decode_attn_fast_body<D, G, NP, FP8, LPR, false>(a, nullptr, blockIdx.x, gridDim.x, lds);
+}
+
+// The next step's plan, built by the committing workgroup once its commit's
+// stores are complete: for each pair of this call, its rows at the next step
+// (live slots after the commit plus the next token) and the next token's
+// placement (in place over the slot of position t + 1 - w when that token was
+// marked, else appended), split over the attention workgroups by the rule the
+// attention uses, one record per workgroup.  Only when the next step can use
+// it: every pair placed with room for one more token, no device error, units
+// split one per workgroup, at most kPlanMaxWgs workgroups; else the plan is
+// marked invalid.  Sequence ids of one call are distinct, so no unit has two
+// pairs.
+template <int D, int G, bool FP8, int LPR>
+__device__ void plan_build(const DecodeArgs& a, const StepArgs& sa, FastLds<G, D, true>& lds) {
+  constexpr int RPP = 4 * (64 / LPR);
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x;
+  const int units = sa.npairs, grid = sa.agrid;
+  const int psh = g.Pshift, pmask = g.P - 1;
+  int* s_start = lds.start;
+  int* s_wstart = lds.wstart;
+  int* s_tmp = lds.tmp;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const bool shape_ok = units <= kAlignedUnits && 2 * units <= grid && grid <= kPlanMaxWgs;
+  int bad = shape_ok ? 0 : 1;
+  if (tid == 0 && __hip_atomic_load(d.ctl + kCtlStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) bad = 1;
+  // rows of the next step per pair (two per thread, as the attention's split scan)
+  int rows[2] = {0, 0};
+  if (shape_ok) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = 2 * tid + i;
+      if (p >= units) continue;
+      const int32_t* pl = d.chunk_info + static_cast<int64_t>(p) * 8;
+      const int kind = __hip_atomic_load(pl + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int unit = __hip_atomic_load(pl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int t = __hip_atomic_load(pl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int slot = __hip_atomic_load(pl + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int app = __hip_atomic_load(pl + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int len = __hip_atomic_load(pl + 7, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int t1 = t + 1;
+      if (kind == kPlanNone || t1 + 1 > g.max_tokens) bad = 1;
+      int ext = 0;
+      if (t1 >= g.w) {
+        // position t + 1 - w: its ring entry predates this call
+        const int rv = d.ring[static_cast<int64_t>(unit) * g.w + t1 % g.w];
+        if (rv < 0) ext = (rv & 0x7FFFFFFF) + 1;
+      }
+      lds.ext[p] = ext;
+      rows[i] = (app ? slot + 1 : len) + 1;
+    }
+  }
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) plan_invalidate(d);
+    return;
+  }
+  int W;
+  int run = block_scan_256(rows[0] + rows[1], s_tmp, &W);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (2 * tid + i < units) s_start[2 * tid + i] = run;
+    run += rows[i];
+  }
+  if (tid == 0) s_start[units] = W;
+  __syncthreads();
+  const int ca = max(1, (W + (grid - units) - 1) / (grid - units));
+  int nw[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int wu = rows[i];
+    if (2 * tid + i < units && wu > 0) nw[i] = min(min((wu + ca - 1) / ca, max(1, wu / RPP)), kMaxSplit);
+  }
+  int tot;
+  run = block_scan_256(nw[0] + nw[1], s_tmp, &tot);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (2 * tid + i < units) s_wstart[2 * tid + i] = run;
+    run += nw[i];
+  }
+  if (tid == 0) s_wstart[units] = tot;
+  __syncthreads();
+  int32_t* recs = plan_records(d, g);
+  for (int j = tid; j < tot; j += 256) {
+    int lo_u = 0, hi_u = units - 1;
+    while (lo_u < hi_u) {
+      const int mid = (lo_u + hi_u + 1) >> 1;
+      if (s_wstart[mid] <= j) lo_u = mid; else hi_u = mid - 1;
+    }
+    const int u = lo_u;
+    const int k = j - s_wstart[u], n = s_wstart[u + 1] - s_wstart[u];
+    const int wu = s_start[u + 1] - s_start[u];
+    const int lo = static_cast<int>(static_cast<int64_t>(k) * wu / n);
+    const int hi = static_cast<int>(static_cast<int64_t>(k + 1) * wu / n);
+    const int unit = __hip_atomic_load(d.chunk_info + static_cast<int64_t>(u) * 8 + 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t* pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
+    const int ext = lds.ext[u];
+    int spage = -1;
+    if (FP8) {
+      // the page whose scales the next token takes (-1: it opens a page)
+      if (ext > 0) spage = __hip_atomic_load(pt + ((ext - 1) >> psh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (((wu - 1) & pmask) != 0)
+        spage = __hip_atomic_load(d.cur_page + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int p0 = lo >> psh;
+    int np = ((hi - 1) >> psh) - p0 + 1;
+    if (np > kRecMaxPages) np = -1;
+    int32_t* r = recs + static_cast<int64_t>(j) * kPlanRec;
+    r[kRecUnit] = u;
+    r[kRecLo] = lo;
+    r[kRecHi] = hi;
+    r[kRecRows] = wu;
+    r[kRecExt] = ext;
+    r[kRecW0] = s_wstart[u];
+    r[kRecW1] = s_wstart[u + 1] - 1;
+    r[kRecScalePage] = spage;
+    r[kRecNpages] = np;
+    for (int i = 0; i < np; ++i)
+      r[kRecPages + i] = __hip_atomic_load(pt + p0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int rr = tid; rr < a.B; rr += 256) plan_rows(d)[rr] = a.seq_ids ? a.seq_ids[rr] : rr;
+  if (tid == 0) {
+    d.plan[kPlanB] = a.B;
+    d.plan[kPlanGrid] = grid;
+    d.plan[kPlanSeqNull] = a.seq_ids == nullptr ? 1 : 0;
+    d.plan[kPlanVariant] = plan_variant<D, G, FP8, LPR>();
+    d.plan[kPlanNrec] = tot;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) d.plan[kPlanValid] = 1;
 }
 
 // dms_decode_step: workgroups [0, npairs) prepare the current token of one
@@ -1186,6 +1391,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendAr
       return;
     }
     prep_commit<KV>(ap, pin, sa.npairs, sh);
+    plan_build<D, G, FP8, LPR>(a, sa, lds);
     if (threadIdx.x < sa.groups)
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
@@ -1360,7 +1566,9 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr, static_cast<float*>(workspace)};
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
-  if (fast_decode_ok(cache, nullptr)) {
+  // the fast kernels read q and write out in 16-byte pieces
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16 == 0;
+  if (fast_decode_ok(cache, nullptr) && aligned16) {
     const bool fp8 = g.kv_dtype == DMS_FP8_E4M3;
     const int np = cache->decode_np > 0 ? cache->decode_np : 2;
     if (g.D == 128) s = fp8 ? launch_fast_d<128, true>(a, grid, np, st) : launch_fast_d<128, false>(a, grid, np, st);

@@ -121,7 +121,7 @@ struct PrepShared {
   int q[kPrepThreads], dst[kPrepThreads], page[kPrepThreads];
 };
 
-// plan record kinds (chunk_info[pair][0..6]: kind, unit, t, slot, e, dst, appended)
+// plan record kinds (chunk_info[pair][0..7]: kind, unit, t, slot, e, dst, appended, length before)
 constexpr int kPlanNone = 0;      // nothing to do (bad sequence id, capacity)
 constexpr int kPlanDone = 1;      // the pair's workgroup wrote everything
 constexpr int kPlanTables = 2;    // K/V row and slot metadata written; length and ring entry left to the commit
@@ -277,9 +277,9 @@ __device__ __forceinline__ void prep_pair(const AppendArgs& a, const PrepIn& in,
   if (tid == 0) {
     const int kind = !valid ? kPlanNone : new_page ? kPlanNewPage : defer_tables ? kPlanTables : kPlanDone;
     int32_t* pl = d.chunk_info + static_cast<int64_t>(p) * 8;
-    const int vals[7] = {kind, unit, t, slot, e, dst, appended};
+    const int vals[8] = {kind, unit, t, slot, e, dst, appended, len};
 #pragma unroll
-    for (int i = 0; i < 7; ++i) __hip_atomic_store(pl + i, vals[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 8; ++i) __hip_atomic_store(pl + i, vals[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -57,6 +57,7 @@ __global__ void init_kernel(DevCache d, Geo g, int units) {
   for (int64_t i = i0; i < kCtlWords; i += n) d.ctl[i] = (i == kCtlFreeCount) ? g.pool : 0;
   for (int64_t i = i0; i < static_cast<int64_t>(kMaxUnits) * 4; i += n) d.unit_info[i] = 0;
   for (int64_t i = i0; i < static_cast<int64_t>(kArriveGroups) * kArriveStride; i += n) d.arrive[i] = 0;
+  if (i0 == 0) plan_invalidate(d);
   for (int64_t i = i0; i < static_cast<int64_t>(g.pool) * 2; i += n) {
     d.scales[i] = 1.0f;
     d.page_amax[i] = 0u;
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(1024) void reset_kernel(DevCache d, Geo g, const in
   const int tid = threadIdx.x;
   const int npairs = n * g.Hkv;
   if (tid == 0) {
+    plan_invalidate(d);
     s_free = d.ctl[kCtlFreeCount];
     s_base = 0;
   }
@@ -225,6 +227,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.chunk_info = reinterpret_cast<int32_t*>(base + L.chunk_info);
   c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
   c->dev.arrive = reinterpret_cast<int32_t*>(base + L.arrive);
+  c->dev.plan = reinterpret_cast<int32_t*>(base + L.plan);
   Geo& g = c->geo;
   g.Bmax = cfg->max_batch;
   g.Hq = cfg->num_q_heads;

@@ -38,7 +38,13 @@ struct DevCache {
   int32_t* chunk_info;   // [Bmax*Hkv][8]
   int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
   int32_t* arrive;       // [kArriveGroups][kArriveStride] decode step arrival counters (word 0 of each)
+  int32_t* plan;         // decode plan of the fused step: [kPlanHeader] header, [Bmax] rows, [kPlanMaxWgs][kPlanRec]
 };
+
+// Decode plan header words (plan[0] = 1 marks the plan valid; every other
+// call that changes lengths, positions, ring entries or page tables clears it).
+constexpr int kPlanValid = 0, kPlanB = 1, kPlanGrid = 2, kPlanSeqNull = 3, kPlanVariant = 4, kPlanNrec = 5;
+__device__ __forceinline__ void plan_invalidate(const DevCache& d) { d.plan[kPlanValid] = 0; }
 
 // Geometry shared by every kernel of one cache.
 struct Geo {

@@ -23,11 +23,17 @@ constexpr int kCtlWords = 64;
 // other.
 constexpr int kArriveGroups = 32;
 constexpr int kArriveStride = 64;      // int32 words between counters
+// Decode plan of the fused step (written by one step's commit for the next):
+// a header, the sequence id of each batch row, and one record per attention
+// workgroup; used only for launches of at most kPlanMaxWgs workgroups.
+constexpr int kPlanHeader = 64;        // int32 words
+constexpr int kPlanMaxWgs = 1024;
+constexpr int kPlanRec = 16;           // int32 words per workgroup record
 
 // Byte offsets of the regions carved out of one cache buffer.
 struct Layout {
   size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, total;
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, plan, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -75,6 +81,12 @@ inline const char* config_error(const dms_config* c, int* status) {
   return nullptr;
 }
 
+// int32 words of the decode plan region: header, rows (rounded up to 64), records.
+inline size_t plan_words(int Bmax) {
+  return static_cast<size_t>(kPlanHeader) + ((static_cast<size_t>(Bmax) + 63) & ~static_cast<size_t>(63)) +
+         static_cast<size_t>(kPlanMaxWgs) * kPlanRec;
+}
+
 // The regions of one cache buffer, each 256-byte aligned, in this order (the
 // configuration must be valid).
 inline void compute_layout(const dms_config& c, Layout* L) {
@@ -107,6 +119,7 @@ inline void compute_layout(const dms_config& c, Layout* L) {
   L->chunk_info = take(units * 8 * sizeof(int32_t));
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
   L->arrive = take(static_cast<size_t>(kArriveGroups) * kArriveStride * sizeof(int32_t));
+  L->plan = take(plan_words(c.max_batch) * sizeof(int32_t));
   L->total = off;
 }
 

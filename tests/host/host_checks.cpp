@@ -101,7 +101,7 @@ static void check_layout() {
     compute_layout(c, &L);
     const size_t off[] = {L.k_pages, L.v_pages, L.scales, L.page_amax, L.slot_meta, L.page_table, L.lengths, L.ring,
                           L.ring_row, L.cur_page, L.pos, L.free_stack, L.ctl, L.chunk_slot, L.chunk_info,
-                          L.unit_info, L.arrive, L.total};
+                          L.unit_info, L.arrive, L.plan, L.total};
     const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
     const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + c.block_size - 1) / c.block_size;
     const size_t pool = c.pool_pages, P = c.block_size;
@@ -110,9 +110,9 @@ static void check_layout() {
                            pool * 8, pool * 8, pool * P * 4, units * maxp * 4, units * 4,
                            units * c.window * 4, units * c.window * 4, units * 4, static_cast<size_t>(c.max_batch) * 4,
                            pool * 4, kCtlWords * 4, units * c.max_chunk * 4, units * 32, kMaxUnits * 16,
-                           kArriveGroups * kArriveStride * 4};
+                           kArriveGroups * kArriveStride * 4, plan_words(c.max_batch) * 4};
     CHECK(L.k_pages == 0);
-    for (int r = 0; r < 17; ++r) {
+    for (int r = 0; r < 18; ++r) {
       CHECK(off[r] % 256 == 0);
       CHECK(off[r + 1] >= off[r] + need[r]);          // no region overlaps the next
       CHECK(off[r + 1] - off[r] < need[r] + 256);     // and no more than alignment in between

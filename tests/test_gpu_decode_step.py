@@ -105,6 +105,52 @@ def test_step_from_empty_cache():
     log(f"empty start: stats {r.sim.stats()}")
 
 
+def test_step_plan_reuse_and_invalidation():
+    """A step leaves the next step a plan of its split (rows, page ids and the
+    next token's placement per attention workgroup).  Steps in a row use it;
+    every other call that changes the cache (an append through dms_decide +
+    dms_append_evict, dms_decode_prepare, a chunk append, a reset) leaves the
+    next step to plan afresh, and so do another row order and fewer rows.
+    Every step is checked against the oracle, the tables after each phase."""
+    _cuda()
+    from learned_kv_cache_amd import dms
+    wl = _workload("g4_d128_linear", 0, cfg_id=52, decode_steps=48)
+    prep = prepare(wl)
+    r = Runner(prep, max_chunk=64)
+    ctx = prep.draw.ctx
+    seqs = [2, 0, 1]
+    _fill(r, seqs)
+    pos = {b: int(ctx[b]) for b in seqs}
+
+    def step(rows, n=1, **kw):
+        for _ in range(n):
+            r.decode_step(rows, [pos[b] for b in rows], **kw)
+            for b in rows:
+                pos[b] += 1
+
+    step(seqs, 3, step=True)
+    step(seqs, step=False)                      # decide + append + attention
+    step(seqs, 2, step=True)
+    step(seqs, fused=True)                      # dms_decode_prepare + attention
+    step(seqs, 2, step=True)
+    r.check_tables(pages=True)
+    step([0, 1, 2], 2, step=True)               # another row order, same batch
+    step([1, 2], 2, step=True)                  # fewer rows
+    step([0, 1, 2], step=True)
+    r.prefill_chunk([1], pos[1], 5, attend=False)
+    pos[1] += 5
+    step([0, 1, 2], 2, step=True)
+    r.check_tables(pages=True)
+    # a reset right after a step over the same rows: sequence 0 starts again
+    # from position 0
+    dms.dms_seq_reset(r.cache, to_dev(np.array([0], np.int32), "i32"), 1)
+    r.sim.reset([0])
+    pos[0] = 0
+    step([0, 1, 2], 3, step=True)
+    r.check_tables(pages=True)
+    assert r.dms.dms_cache_status(r.cache) == 0
+
+
 def test_step_subset_of_rows_and_capacity():
     """A call over some rows leaves the others alone; a row at its capacity is
     flagged and not appended while the other rows proceed."""

@@ -136,7 +136,9 @@ def test_llama1b_prefill_8k_then_decode():
     r.check_tables(pages=True)
     worst = (0.0, 0.0)
     for i in range(wl.decode_steps):
-        st = r.decode_step([0], [8192 + i], fused=i % 3 == 1, step=i % 3 == 2)
+        # the three paths in turn; the second of two one-launch steps runs on the
+        # plan the first left
+        st = r.decode_step([0], [8192 + i], fused=i % 4 == 1, step=i % 4 >= 2)
         worst = (max(worst[0], st[0]), max(worst[1], st[1]))
     r.check_tables()
     stats = r.dms.dms_cache_stats(r.cache)
@@ -159,7 +161,9 @@ def test_qwen8b_ctx8k_b8_decode():
     r.check_tables()
     worst = (0.0, 0.0)
     for i in range(wl.decode_steps):
-        st = r.decode_step(seqs, [8192 + i] * wl.B, fused=i % 2 == 1, step=i % 2 == 0)
+        # runs of three one-launch steps (the second and third on the plan the one
+        # before left), then decide + append in one call and the attention
+        st = r.decode_step(seqs, [8192 + i] * wl.B, fused=i % 4 == 3, step=i % 4 != 3)
         worst = (max(worst[0], st[0]), max(worst[1], st[1]))
         if i % 32 == 31:
             r.check_tables()
