@@ -38,6 +38,7 @@ struct DecodeArgs {
   int B;
   int lanes_per_row;   // fast kernel row layout (8 or 16 lanes per bf16 row of 128)
   float* partials;     // caller's workspace: partial (o, m, l) records of split units
+  int mfma;            // bf16 pages: the matrix-core variant of the fast kernel
 };
 
 template <int KV> struct KvTraits;
@@ -634,6 +635,172 @@ __device__ __forceinline__ void compute_chunk(const KvChunk<NP, (D * (FP8 ? 1 : 
 }
 
 
+// ---------------------------------------------------------------------------
+// Matrix-core variant (bf16 pages, D = 64 or 128, pages of at least 16 rows).
+//
+// A wave takes 16-row tiles of its segment, aligned to 16 rows of the unit so
+// that a tile lies in one page.  The tile's scores for the group's G query
+// heads come from v_mfma_f32_16x16x32_bf16 with the 16 keys as rows (A: lane
+// (g, n) = (lane / 16, lane % 16) holds the 8 elements 32s + 8g.. of key n's
+// row, loaded from the page) and the heads as columns (B: the same elements of
+// query head n, zero from head G on); lane (g, n) is left the scores of keys
+// 4g..4g+3 for head n.  The max over the tile's keys is a reduction over the
+// four 16-lane rows.  The P.V products run on the vector ALU over coalesced V
+// loads (whole rows per load): lane (g, s, c) holds 16-byte piece c of the V
+// rows of keys of its row group g, takes head h's probabilities from lane
+// (g, h) by a row broadcast, and accumulates o[h][8c..8c+8] with packed bf16
+// dot products over key pairs.  Per 16 keys that is D / 32 matrix products
+// and about (G + 2) * 16 vector instructions, against G * D / 4 packed dot
+// products and the per-row reductions of the lane-per-row-piece kernel.
+
+typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mf_f32x4 __attribute__((ext_vector_type(4)));
+
+// max / sum of lane l and lane l ^ 32 (resp. l ^ 16): the swap builtins
+// return the pair (own, partner) in a lane-independent order.
+__device__ __forceinline__ float mf_max_x32(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float mf_max_x16(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float mf_sum_x32(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float mf_sum_x16(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// lane h of each 16-lane row, to every lane of the row (row_newbcast:h)
+template <int H>
+__device__ __forceinline__ uint32_t mf_row_bcast(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x150 + H, 0xF, 0xF, false));
+}
+
+template <int D>
+struct MfTile {
+  static constexpr int KS = D / 32;                // k-steps of the score product
+  static constexpr int NVI = D == 128 ? 4 : 2;     // V loads per tile
+  uint4 k[KS];
+  uint4 v[NVI];
+};
+
+// Issues the loads of tile t of a page block (clamped to its last tile, nt
+// tiles from row t0): K in the matrix-core layout, V as whole rows.  Rows past
+// `hi` read the tile's first row instead (finite: a live row or, STEP, the
+// current token's input row) and are masked; STEP: row `vrow` is the current
+// token, read from the input rows kin0 / vin0.
+template <int D, bool STEP>
+__device__ __forceinline__ void mf_load(MfTile<D>& b, int t, int nt, int t0, int pb, int pt_reg,
+                                        const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp, int hi,
+                                        int psh, int pmask, int vrow, const uint8_t* kin0, const uint8_t* vin0,
+                                        int lane) {
+  constexpr int RB = D * 2, VL = D / 8, RPG = 16 / VL;
+  const int tb = t0 + 16 * min(t, nt - 1);
+  const int page = __builtin_amdgcn_readlane(pt_reg, (tb >> psh) - pb);
+  const uint32_t prow = static_cast<uint32_t>(page) * static_cast<uint32_t>(pmask + 1);
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const bool tb_in = STEP && tb == vrow;
+  {
+    const int r = tb + n16;
+    const bool past = r >= hi;
+    const bool in = STEP && (past ? tb_in : r == vrow);
+    const int rr = past ? tb : r;
+    const uint8_t* base = in ? kin0 : kp + (prow + static_cast<uint32_t>(rr & pmask)) * static_cast<uint32_t>(RB);
+#pragma unroll
+    for (int s = 0; s < MfTile<D>::KS; ++s) b.k[s] = *reinterpret_cast<const uint4*>(base + (32 * s + 8 * g4) * 2);
+  }
+  const int vs = (lane & 15) / VL, vc = lane % VL;
+#pragma unroll
+  for (int j = 0; j < MfTile<D>::NVI; ++j) {
+    const int r = tb + 4 * g4 + RPG * j + vs;
+    const bool past = r >= hi;
+    const bool in = STEP && (past ? tb_in : r == vrow);
+    const int rr = past ? tb : r;
+    const uint8_t* base = in ? vin0 : vp + (prow + static_cast<uint32_t>(rr & pmask)) * static_cast<uint32_t>(RB);
+    b.v[j] = *reinterpret_cast<const uint4*>(base + 16 * vc);
+  }
+}
+
+// o[8] += P (bf16 pair: keys a, b) . (V rows a, b), 8 elements
+__device__ __forceinline__ void mf_pv_pair(const uint4& va, const uint4& vb, uint32_t P, float* o) {
+  const uint32_t x[4] = {va.x, va.y, va.z, va.w};
+  const uint32_t y[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo2 = __builtin_amdgcn_perm(y[w], x[w], 0x05040100u);
+    const uint32_t hi2 = __builtin_amdgcn_perm(y[w], x[w], 0x07060302u);
+    o[2 * w] = dot2(P, lo2, o[2 * w]);
+    o[2 * w + 1] = dot2(P, hi2, o[2 * w + 1]);
+  }
+}
+
+template <int D, int G, int H>
+__device__ __forceinline__ void mf_pv_head(const MfTile<D>& b, uint32_t pa, uint32_t pb, bool vs1, float (&o)[G][8]) {
+  if constexpr (H < G) {
+    const uint32_t Pa = mf_row_bcast<H>(pa), Pb = mf_row_bcast<H>(pb);
+    if constexpr (D == 128) {
+      mf_pv_pair(b.v[0], b.v[1], Pa, o[H]);
+      mf_pv_pair(b.v[2], b.v[3], Pb, o[H]);
+    } else {
+      mf_pv_pair(b.v[0], b.v[1], vs1 ? Pb : Pa, o[H]);
+    }
+    mf_pv_head<D, G, H + 1>(b, pa, pb, vs1, o);
+  }
+}
+
+// Online-softmax update with tile t: m (running max, base 2) and lsum are
+// lane (g, n)'s for head n (lsum over the keys of its row group); o[h][e] is
+// lane (g, s, c)'s partial for element 8c + e of head h.
+template <int D, int G, bool STEP>
+__device__ __forceinline__ void mf_compute(const MfTile<D>& b, int t, int t0, int lo, int hi, int skip,
+                                           float scale_log2, const uint4 (&qb)[D / 32], float& m, float& lsum,
+                                           float (&o)[G][8], int lane) {
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int tb = t0 + 16 * t;
+  mf_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < MfTile<D>::KS; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, b.k[s]),
+                                                  __builtin_bit_cast(mf_bf16x8, qb[s]), acc, 0, 0, 0);
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tb + 4 * g4 + i;
+    const bool ok = n16 < G && r >= lo && r < hi && (!STEP || r != skip);
+    sc[i] = ok ? acc[i] * scale_log2 : -INFINITY;
+  }
+  float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  tmax = mf_max_x16(mf_max_x32(tmax));
+  // lazy rescale (see compute_chunk); every lane of head n moves together
+  const bool need = tmax > m + kDecRescaleLog2;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;   // m = -inf gives 0
+    if (need) m = tmax;
+    lsum *= alpha;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ah = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= ah;
+    }
+  }
+  const float msub = (m == -INFINITY) ? 0.0f : m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - msub);   // -inf gives 0
+  lsum += (p[0] + p[1]) + (p[2] + p[3]);
+  // key pairs of the P.V products: (0, 1), (2, 3) for D = 128 (a lane's V rows
+  // are keys 4g..4g+3); (0, 2), (1, 3) for D = 64 (keys 4g + s, 4g + 2 + s)
+  const uint32_t pa = D == 128 ? pack_bf16(p[0], p[1]) : pack_bf16(p[0], p[2]);
+  const uint32_t pb = D == 128 ? pack_bf16(p[2], p[3]) : pack_bf16(p[1], p[3]);
+  mf_pv_head<D, G, 0>(b, pa, pb, (lane & 15) >= 8, o);
+}
+
 // Combines the partial records (m, l, o) of one unit's workgroups w0..w1 into
 // its bf16 output [G][D] (256 threads); the records are read with
 // device-scope atomic loads (written by workgroups on other XCDs).  The first workgroup's record is its
@@ -762,11 +929,100 @@ __device__ __forceinline__ int unit_slots(const DecodeArgs& a, int u, int wg, in
   return L;
 }
 
+// One wave's share of a segment (rows [lo, hi) of unit (row, kh)) on the
+// matrix cores: the wave takes tiles wave, wave + 4, ... of each page block,
+// keeps NB = 2 tiles in flight, and leaves its (m, l, o) in entry 0 of the
+// workgroup's LDS rows (m, l of head h from lane h, o from the lanes of row
+// group 0).
+template <int D, int G, bool STEP>
+__device__ __forceinline__ void mf_segment(const DecodeArgs& a, const StepArgs* sa, FastLds<G, D, STEP>& lds,
+                                           bool use_plan, int p_np, int p_page, const int32_t* pt, int row, int kh,
+                                           int lo, int hi, int vrow, int skip, int wave, int lane) {
+  constexpr int KS = D / 32, VL = D / 8;
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int psh = g.Pshift, pmask = g.P - 1;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  // query rows as the B operand: lane (g, n) holds elements 32s + 8g.. of head n
+  uint4 qb[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<size_t>(row) * g.Hq + kh * G + min(n16, G - 1)) * D + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qb[s] = n16 < G ? *reinterpret_cast<const uint4*>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+    // the decision neuron (element D - 1 of the group's first head) plays no
+    // part in attention (the commit zeroes it in memory)
+    if (STEP && sa->qneuron && n16 == 0 && g4 == 3) qb[KS - 1].w &= 0xFFFFu;
+  }
+  const uint8_t* kin0 = nullptr;
+  const uint8_t* vin0 = nullptr;
+  if constexpr (STEP) {
+    const size_t ro = (static_cast<size_t>(row) * g.Hkv + kh) * (D * 2);
+    kin0 = sa->k + ro;
+    vin0 = sa->v + ro;
+  }
+  float m = -INFINITY, lsum = 0.0f;
+  float o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+  for (int pb = lo >> psh; pb <= (hi - 1) >> psh; pb += 64) {
+    const int plast = min((hi - 1) >> psh, pb + 63);
+    const bool from_plan = use_plan && p_np > 0;
+    const int pt_reg = from_plan ? (lane < p_np ? p_page : 0) : (pb + lane <= plast) ? pt[pb + lane] : 0;
+    const int blo = max(lo, pb << psh), bhi = min(hi, (plast + 1) << psh);
+    const int t0 = blo & ~15;
+    const int nt = (bhi - t0 + 15) >> 4;
+    // loads one tile ahead, unconditionally (past the block's end they reread
+    // its last tile), in written order (see the lane-per-row-piece kernel)
+    MfTile<D> ta, tb;
+    auto load = [&](MfTile<D>& b, int t) {
+      mf_load<D, STEP>(b, t, nt, t0, pb, pt_reg, d.k_pages, d.v_pages, hi, psh, pmask, vrow, kin0, vin0, lane);
+    };
+    auto compute = [&](const MfTile<D>& b, int t) {
+      mf_compute<D, G, STEP>(b, t, t0, lo, hi, skip, g.scale_log2, qb, m, lsum, o, lane);
+    };
+    load(ta, wave);
+    for (int t = wave; t < nt; t += 8) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(tb, t + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ta, t);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ta, t + 8);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 4 < nt) compute(tb, t + 4);
+    }
+  }
+  // sums over the row groups (and, D = 64, the two rows of a group)
+  lsum = mf_sum_x16(mf_sum_x32(lsum));
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = mf_sum_x16(mf_sum_x32(o[h][e]));
+      if (VL == 8) x += dpp_f<0x128, 0xF>(x, 0.0f);   // row_ror:8
+      o[h][e] = x;
+    }
+  if (lane < VL) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lds.o[wave][0][h][8 * lane + e] = o[h][e];
+  }
+  if (lane < G) {
+    lds.ml[wave][0][lane][0] = m;
+    lds.ml[wave][0][lane][1] = lsum;
+  }
+}
+
 // The decode plan (fused step): the kernel variant a plan was split for, and
 // where its rows and records start.
-template <int D, int G, bool FP8, int LPR>
+template <int D, int G, bool FP8, int LPR, bool MF>
 __device__ __forceinline__ constexpr int plan_variant() {
-  return D | (G << 8) | ((FP8 ? 1 : 0) << 12) | (LPR << 16) | (1 << 24);
+  return D | (G << 8) | ((FP8 ? 1 : 0) << 12) | ((MF ? 1 : 0) << 13) | (LPR << 16) | (1 << 24);
 }
 __device__ __forceinline__ int32_t* plan_rows(const DevCache& d) { return d.plan + kPlanHeader; }
 __device__ __forceinline__ int32_t* plan_records(const DevCache& d, const Geo& g) {
@@ -784,7 +1040,7 @@ constexpr int kRecMaxPages = kPlanRec - kRecPages;
 // masked.  The same keys as after the append.  Once a workgroup has read the
 // lengths, positions and ring entries it works from, it counts itself on its
 // arrival group; the prepare role's commit waits for all of them.
-template <int D, int G, int NP, bool FP8, int LPR, bool STEP>
+template <int D, int G, int NP, bool FP8, int LPR, bool STEP, bool MF = false>
 __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const StepArgs* sa, int wg, int grid,
                                                       FastLds<G, D, STEP>& lds) {
   constexpr int EB = FP8 ? 1 : 2;
@@ -793,7 +1049,9 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
   constexpr int EPL = BPL / EB;
   constexpr int QW = EPL / 2;
   constexpr int RG = 64 / LPR;
-  constexpr int RPP = 4 * RG;
+  // rows per workgroup pass: the floor of a workgroup's share in the split
+  constexpr int RPP = MF ? 64 : 4 * RG;
+  static_assert(!MF || !FP8, "the matrix-core variant reads bf16 pages");
   constexpr int NV = BPL / 16;
   static_assert(NP % 2 == 0, "passes are paired for the P.V dot products");
   static_assert(BPL % 16 == 0, "a lane loads whole 16-byte pieces");
@@ -824,7 +1082,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       const int nrec = P[kPlanNrec];
       int bad = !(P[kPlanValid] == 1 && P[kPlanB] == a.B && P[kPlanGrid] == grid &&
                   P[kPlanSeqNull] == (a.seq_ids == nullptr ? 1 : 0) &&
-                  P[kPlanVariant] == plan_variant<D, G, FP8, LPR>());
+                  P[kPlanVariant] == plan_variant<D, G, FP8, LPR, MF>());
       for (int r = tid; r < a.B; r += 256)
         if ((a.seq_ids ? a.seq_ids[r] : r) != plan_rows(d)[r]) bad = 1;
       use_plan = !__syncthreads_or(bad);
@@ -1057,6 +1315,9 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       }
     }
 
+    if constexpr (MF) {
+      mf_segment<D, G, STEP>(a, sa, lds, use_plan, p_np, p_page, pt, row, kh, lo, hi, vrow, skip, wave, lane);
+    } else {
     uint32_t qv[G][QW];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -1142,6 +1403,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
 #pragma unroll
       for (int h = 0; h < G; ++h) lds.ml[wave][0][h][0] = m[h];
     }
+    }
     __syncthreads();
     // the unit's workgroups w0..w1 (concatenated split: w0's record is its
     // second one when the unit starts inside w0's range)
@@ -1160,8 +1422,14 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float f = exp2f(lds.ml[w][0][h][0] - M);     // -inf gives 0
-          ov += f * (lds.o[w][0][h][dd] + lds.o[w][1][h][dd] + lds.o[w][2][h][dd] + lds.o[w][3][h][dd]);
-          lv += f * (lds.ml[w][0][h][1] + lds.ml[w][1][h][1] + lds.ml[w][2][h][1] + lds.ml[w][3][h][1]);
+          if constexpr (MF) {
+            // (one entry per wave)
+            ov += f * lds.o[w][0][h][dd];
+            lv += f * lds.ml[w][0][h][1];
+          } else {
+            ov += f * (lds.o[w][0][h][dd] + lds.o[w][1][h][dd] + lds.o[w][2][h][dd] + lds.o[w][3][h][dd]);
+            lv += f * (lds.ml[w][0][h][1] + lds.ml[w][1][h][1] + lds.ml[w][2][h][1] + lds.ml[w][3][h][1]);
+          }
         }
       }
       if (!split) {
@@ -1204,10 +1472,11 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
 }
 
 
-template <int D, int G, int NP, bool FP8, int LPR>
-__global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
+template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 3 : 1)))
+void decode_attn_fast_kernel(DecodeArgs a) {
   __shared__ FastLds<G, D, false> lds;
-  decode_attn_fast_body<D, G, NP, FP8, LPR, false>(a, nullptr, blockIdx.x, gridDim.x, lds);
+  decode_attn_fast_body<D, G, NP, FP8, LPR, false, MF>(a, nullptr, blockIdx.x, gridDim.x, lds);
 }
 
 // The next step's plan, built by the committing workgroup once its commit's
@@ -1220,9 +1489,9 @@ __global__ __launch_bounds__(256) void decode_attn_fast_kernel(DecodeArgs a) {
 // split one per workgroup, at most kPlanMaxWgs workgroups; else the plan is
 // marked invalid.  Sequence ids of one call are distinct, so no unit has two
 // pairs.
-template <int D, int G, bool FP8, int LPR>
+template <int D, int G, bool FP8, int LPR, bool MF>
 __device__ void plan_build(const DecodeArgs& a, const StepArgs& sa, FastLds<G, D, true>& lds) {
-  constexpr int RPP = 4 * (64 / LPR);
+  constexpr int RPP = MF ? 64 : 4 * (64 / LPR);     // as the attention's split
   const DevCache& d = a.d;
   const Geo& g = a.g;
   const int tid = threadIdx.x;
@@ -1335,7 +1604,7 @@ __device__ void plan_build(const DecodeArgs& a, const StepArgs& sa, FastLds<G, D
     d.plan[kPlanB] = a.B;
     d.plan[kPlanGrid] = grid;
     d.plan[kPlanSeqNull] = a.seq_ids == nullptr ? 1 : 0;
-    d.plan[kPlanVariant] = plan_variant<D, G, FP8, LPR>();
+    d.plan[kPlanVariant] = plan_variant<D, G, FP8, LPR, MF>();
     d.plan[kPlanNrec] = tot;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1347,8 +1616,12 @@ __device__ void plan_build(const DecodeArgs& a, const StepArgs& sa, FastLds<G, D
 // (row, KV head) pair each (decision, placement, plan record); the others run
 // the attention (STEP).  The last pair to finish waits until every attention
 // workgroup has arrived (read the tables it works from), then commits.
-template <int D, int G, int NP, bool FP8, int LPR>
-__global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
+// (the matrix-core variant for groups of up to 4 heads is held to 3 waves per
+// SIMD: the one-launch step needs its prepare and attention workgroups
+// resident together)
+template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 3 : 1)))
+void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
   constexpr int KV = FP8 ? DMS_FP8_E4M3 : DMS_BF16;
   __shared__ FastLds<G, D, true> lds;
   if (static_cast<int>(blockIdx.x) < sa.npairs) {
@@ -1391,12 +1664,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a, AppendAr
       return;
     }
     prep_commit<KV>(ap, pin, sa.npairs, sh);
-    plan_build<D, G, FP8, LPR>(a, sa, lds);
+    plan_build<D, G, FP8, LPR, MF>(a, sa, lds);
     if (threadIdx.x < sa.groups)
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  decode_attn_fast_body<D, G, NP, FP8, LPR, true>(a, &sa, blockIdx.x - sa.npairs, sa.agrid, lds);
+  decode_attn_fast_body<D, G, NP, FP8, LPR, true, MF>(a, &sa, blockIdx.x - sa.npairs, sa.agrid, lds);
 }
 
 template <int D, int G, bool FP8, int NP>
@@ -1416,6 +1689,13 @@ static void launch_fast_np(const DecodeArgs& a, int grid, hipStream_t st) {
 
 template <int D, int G, bool FP8>
 static int launch_fast_dg(const DecodeArgs& a, int grid, int np, hipStream_t st) {
+  if constexpr (!FP8) {
+    if (a.mfma) {
+      constexpr int LPR1 = D * 2 / 16 >= 16 ? 16 : D * 2 / 16;
+      hipLaunchKernelGGL((decode_attn_fast_kernel<D, G, 2, false, LPR1, true>), dim3(grid), dim3(256), 0, st, a);
+      return DMS_OK;
+    }
+  }
   switch (np) {
     case 2: launch_fast_np<D, G, FP8, 2>(a, grid, st); break;
     case 4: launch_fast_np<D, G, FP8, 4>(a, grid, st); break;
@@ -1470,10 +1750,11 @@ static int launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
 using StepKernel = void (*)(DecodeArgs, AppendArgs, PrepIn, StepArgs);
 
 template <int D, int G>
-static StepKernel step_kernel_dg(const Geo& g, int lanes_per_row) {
+static StepKernel step_kernel_dg(const Geo& g, int lanes_per_row, bool mfma) {
   if (g.kv_dtype == DMS_FP8_E4M3) return decode_step_kernel<D, G, 2, true, D / 16>;
   constexpr int RB = D * 2;
   constexpr int LPR1 = RB / 16 >= 16 ? 16 : RB / 16;
+  if (mfma) return decode_step_kernel<D, G, 2, false, LPR1, true>;
   if constexpr (RB / 16 >= 16) {
     if (lanes_per_row == 8) return decode_step_kernel<D, G, 2, false, 8>;
   }
@@ -1481,18 +1762,18 @@ static StepKernel step_kernel_dg(const Geo& g, int lanes_per_row) {
 }
 
 template <int D>
-static StepKernel step_kernel_d(const Geo& g, int lanes_per_row) {
+static StepKernel step_kernel_d(const Geo& g, int lanes_per_row, bool mfma) {
   switch (g.g) {
-    case 1: return step_kernel_dg<D, 1>(g, lanes_per_row);
-    case 2: return step_kernel_dg<D, 2>(g, lanes_per_row);
-    case 4: return step_kernel_dg<D, 4>(g, lanes_per_row);
-    case 8: return step_kernel_dg<D, 8>(g, lanes_per_row);
+    case 1: return step_kernel_dg<D, 1>(g, lanes_per_row, mfma);
+    case 2: return step_kernel_dg<D, 2>(g, lanes_per_row, mfma);
+    case 4: return step_kernel_dg<D, 4>(g, lanes_per_row, mfma);
+    case 8: return step_kernel_dg<D, 8>(g, lanes_per_row, mfma);
     default: return nullptr;
   }
 }
 
-static StepKernel step_kernel(const Geo& g, int lanes_per_row) {
-  return g.D == 128 ? step_kernel_d<128>(g, lanes_per_row) : step_kernel_d<64>(g, lanes_per_row);
+static StepKernel step_kernel(const Geo& g, int lanes_per_row, bool mfma) {
+  return g.D == 128 ? step_kernel_d<128>(g, lanes_per_row, mfma) : step_kernel_d<64>(g, lanes_per_row, mfma);
 }
 
 // The fast decode attention applies: bf16/fp8 pages, D 64/128, power-of-two
@@ -1506,6 +1787,13 @@ static bool fast_decode_ok(const dms_cache* cache, int* lpr_out) {
   return (g.kv_dtype == DMS_BF16 || g.kv_dtype == DMS_FP8_E4M3) && (g.D == 64 || g.D == 128) && g.Pshift >= 0 &&
          (1 << g.Pshift) >= 64 / lpr && cache->layout.v_pages - cache->layout.k_pages < (1ull << 32) &&
          !cache->force_generic;
+}
+
+// The matrix-core variant applies to the fast kernel's bf16 pages of at least
+// 16 rows (a 16-row tile lies in one page); DMS_DECODE_MFMA=0 turns it off.
+static bool mfma_decode_ok(const dms_cache* cache) {
+  const Geo& g = cache->geo;
+  return cache->decode_mfma != 0 && g.kv_dtype == DMS_BF16 && g.Pshift >= 4 && fast_decode_ok(cache, nullptr);
 }
 
 // ---- decode attention without an allocation ------------------------------
@@ -1563,7 +1851,8 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
   int s = check_workspace(cache, B, workspace, ws_bytes);
   if (s) return s;
-  DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr, static_cast<float*>(workspace)};
+  DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr, static_cast<float*>(workspace),
+               mfma_decode_ok(cache) ? cache->decode_mfma : 0};
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
   // the fast kernels read q and write out in 16-byte pieces
@@ -1605,10 +1894,13 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
     al |= reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(rms_gamma) |
           reinterpret_cast<uintptr_t>(W);
   const int npairs = B * g.Hkv;
-  const int agrid = decode_grid_for(cache);
+  // the attention workgroups fill what the prepare workgroups leave of the
+  // decode grid (two workgroups per CU by default), so that no CU holds a
+  // third workgroup beside two attention ones
+  const int agrid = std::max(decode_grid_for(cache) / 2, decode_grid_for(cache) - npairs);
   bool fused = cache->step_fuse != 0 && fast_decode_ok(cache, nullptr) && al % 16 == 0 &&
                (!linear || c.hidden % 8 == 0) && npairs <= kMaxUnits;
-  StepKernel kern = fused ? step_kernel(g, cache->decode_lpr) : nullptr;
+  StepKernel kern = fused ? step_kernel(g, cache->decode_lpr, mfma_decode_ok(cache)) : nullptr;
   if (!kern) fused = false;
   if (fused && cache->step_fuse < 0) {
     // One launch only when every workgroup can be resident at once: else the
@@ -1631,7 +1923,8 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
     if (s) return s;
     return dms_decode_attn(cache, seq_ids, q_inout, out, B, workspace, ws_bytes, stream);
   }
-  DecodeArgs a{cache->dev, g, seq_ids, q_inout, out, B, cache->decode_lpr, static_cast<float*>(workspace)};
+  DecodeArgs a{cache->dev, g, seq_ids, q_inout, out, B, cache->decode_lpr, static_cast<float*>(workspace),
+               mfma_decode_ok(cache) ? cache->decode_mfma : 0};
   AppendArgs ap{};
   ap.d = cache->dev;
   ap.g = g;

@@ -259,6 +259,8 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   if (const char* e = std::getenv("DMS_DECODE_NP")) c->decode_np = std::atoi(e);
   c->decode_lpr = 0;
   if (const char* e = std::getenv("DMS_DECODE_LPR")) c->decode_lpr = std::atoi(e);
+  c->decode_mfma = 1;
+  if (const char* e = std::getenv("DMS_DECODE_MFMA")) c->decode_mfma = std::atoi(e);
   const char* fg = std::getenv("DMS_GENERIC_KERNELS");
   c->force_generic = fg && fg[0] == '1';
   c->step_fuse = -1;

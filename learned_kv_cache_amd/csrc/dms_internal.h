@@ -66,6 +66,7 @@ struct dms_cache {
   int decode_grid;
   int decode_np;         // passes in flight per round of the decode kernel (DMS_DECODE_NP; 0: default)
   int decode_lpr;        // lanes per row of the decode kernel (DMS_DECODE_LPR; 0: default)
+  int decode_mfma;       // matrix-core decode for bf16 pages of >= 16 rows (DMS_DECODE_MFMA; default 1)
   bool force_generic;    // DMS_GENERIC_KERNELS=1: vector-ALU decode and prefill attention kernels only
   int step_fuse;         // dms_decode_step in one launch: -1 when all its workgroups fit at once (default),
                          // 0 never, 1 always (DMS_DECODE_STEP_FUSE)

@@ -11,7 +11,8 @@ and page bytes (fp8 pages: codes and per-page scales, the current token's
 row quantised by the attention exactly as the append stores it, in place,
 into the current page or as the first row of a new page).  Shapes cover GQA
 groups 1, 2, 4 and 8, head_dim 64 and 128, bf16 and fp8 pages, both decision
-sources, layer mode, and more than 64 (row, KV head) units.
+sources, layer mode, and more than 64 (row, KV head) units; bf16 pages run
+the matrix-core decode, and, for two shapes, the lane-per-row-piece one.
 """
 import copy
 
@@ -32,6 +33,9 @@ SHAPES = {
     "g1_d128_qneuron_80_units": (20, 4, 4, 128, "qneuron", "head", "bf16"),
     "g4_d128_linear_fp8": (3, 8, 2, 128, "linear", "head", "fp8"),
     "g2_d64_qneuron_fp8": (3, 8, 4, 64, "qneuron", "head", "fp8"),
+    # bf16 pages through the lane-per-row-piece kernel (the matrix-core one off)
+    "g4_d128_linear_vector": (3, 8, 2, 128, "linear", "head", "bf16"),
+    "g2_d64_qneuron_vector": (3, 8, 4, 64, "qneuron", "head", "bf16"),
 }
 
 
@@ -71,8 +75,10 @@ def _fill(r, seqs):
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
-def test_step_ragged_positions(name):
+def test_step_ragged_positions(name, monkeypatch):
     _cuda()
+    if name.endswith("_vector"):
+        monkeypatch.setenv("DMS_DECODE_MFMA", "0")
     wl = _workload(name, list(SHAPES).index(name))
     prep = prepare(wl)
     r = Runner(prep, max_chunk=64)
