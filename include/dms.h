@@ -263,10 +263,14 @@ int dms_decode_attn_noalloc(dms_cache* cache, const int32_t* seq_ids, const void
  * the current token from k/v (fp8: quantised with the scale its page has or
  * gets, as the append stores it) and masks the slot it overwrites; the last
  * preparing workgroup commits the append once every attention workgroup has
- * read the shared tables.  Other configurations and larger steps call
+ * read the shared tables, and leaves the next step of the same rows a plan
+ * of its attention split (kept in the cache; any other call that changes
+ * the cache drops it).  Other configurations and larger steps call
  * dms_decode_prepare, then dms_decode_attn (the environment variable
  * DMS_DECODE_STEP_FUSE, read at cache creation, forces one (1) or two (0)
- * launches).  workspace / ws_bytes as in dms_decode_attn.  Device-side
+ * launches; DMS_DECODE_STEP_ROWS=1, read at every call, prepares one batch
+ * row per workgroup instead of one pair).  workspace / ws_bytes as in
+ * dms_decode_attn.  Device-side
  * errors as in dms_append_evict, and DMS_DEV_STEP_SYNC if the commit's
  * bounded wait for the attention workgroups ran out (only when far more
  * workgroups than the GPU holds at once queue behind it; the environment

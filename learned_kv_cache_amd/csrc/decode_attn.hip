@@ -870,7 +870,10 @@ __device__ __forceinline__ void merge_unit_records(float* partials, int w0, int 
 struct StepArgs {
   const uint8_t* k;        // [B][Hkv][D] bf16 rows of the current token
   const uint8_t* v;
-  int npairs;              // workgroups of the prepare role (B * Hkv), placed first in the grid
+  int npairs;              // (row, KV head) pairs of the call (B * Hkv)
+  int nprep;               // workgroups of the prepare role, placed first in the grid: one per pair, or
+                           // (per_row) one per batch row
+  int per_row;
   int groups;              // arrival groups of the attention workgroups (min(kArriveGroups, their count))
   int agrid;               // attention workgroups
   int qneuron;             // the decision neuron (last element of each group's first query head) reads as zero
@@ -1624,14 +1627,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <=
 void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
   constexpr int KV = FP8 ? DMS_FP8_E4M3 : DMS_BF16;
   __shared__ FastLds<G, D, true> lds;
-  if (static_cast<int>(blockIdx.x) < sa.npairs) {
+  if (static_cast<int>(blockIdx.x) < sa.nprep) {
     PrepShared& sh = lds.prep;
-    prep_pair<KV>(ap, pin, blockIdx.x, true, sh);
+    if (sa.per_row) prep_row<KV>(ap, pin, blockIdx.x, sh);
+    else prep_pair<KV>(ap, pin, blockIdx.x, true, sh);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
       sh.last = __hip_atomic_fetch_add(ap.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                sa.npairs - 1;
+                sa.nprep - 1;
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(sh.last)) return;
     // the last pair commits once every attention workgroup has arrived: lane
@@ -1669,7 +1673,7 @@ void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  decode_attn_fast_body<D, G, NP, FP8, LPR, true, MF>(a, &sa, blockIdx.x - sa.npairs, sa.agrid, lds);
+  decode_attn_fast_body<D, G, NP, FP8, LPR, true, MF>(a, &sa, blockIdx.x - sa.nprep, sa.agrid, lds);
 }
 
 template <int D, int G, bool FP8, int NP>
@@ -1897,7 +1901,11 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
   // the attention workgroups fill what the prepare workgroups leave of the
   // decode grid (two workgroups per CU by default), so that no CU holds a
   // third workgroup beside two attention ones
-  const int agrid = std::max(decode_grid_for(cache) / 2, decode_grid_for(cache) - npairs);
+  const int dgrid = decode_grid_for(cache);
+  auto attn_grid = [&](int nprep) { return std::max(dgrid / 2, dgrid - nprep); };
+  int nprep = npairs;
+  bool per_row = false;
+  int agrid = attn_grid(nprep);
   bool fused = cache->step_fuse != 0 && fast_decode_ok(cache, nullptr) && al % 16 == 0 &&
                (!linear || c.hidden % 8 == 0) && npairs <= kMaxUnits;
   StepKernel kern = fused ? step_kernel(g, cache->decode_lpr, mfma_decode_ok(cache)) : nullptr;
@@ -1913,8 +1921,17 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
         return DMS_ERR_HIP;
       cache->step_blocks_per_cu = n;
     }
-    fused = npairs + agrid <= cache->step_blocks_per_cu * cache->num_cus;
   }
+  // DMS_DECODE_STEP_ROWS=1 (read at every call): one prepare workgroup per
+  // batch row instead of one per pair.  It lets a large batch run in one
+  // launch, but with the attention a grid of pairs smaller; for fp8 pages at
+  // 64 rows the two calls in turn are faster, so it is not the default.
+  if (const char* e = std::getenv("DMS_DECODE_STEP_ROWS")) per_row = std::atoi(e) != 0 && g.Hkv > 1;
+  if (per_row) {
+    nprep = B;
+    agrid = attn_grid(B);
+  }
+  if (fused && cache->step_fuse < 0) fused = nprep + agrid <= cache->step_blocks_per_cu * cache->num_cus;
   hipStream_t st = as_stream(stream);
   if (!fused) {
     // other shapes, or a step too large for one resident launch: the two calls in turn
@@ -1949,9 +1966,9 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
   // DMS_DEV_STEP_SYNC path with every kernel exiting normally)
   int spin = kArriveSpinLimit;
   if (const char* e = std::getenv("DMS_STEP_SPIN_LIMIT")) spin = std::max(0, std::atoi(e));
-  StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, groups, agrid,
+  StepArgs sa{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), npairs, nprep, per_row ? 1 : 0, groups, agrid,
               linear ? 0 : 1, spin};
-  hipLaunchKernelGGL(kern, dim3(npairs + agrid), dim3(256), 0, st, a, ap, pin, sa);
+  hipLaunchKernelGGL(kern, dim3(nprep + agrid), dim3(256), 0, st, a, ap, pin, sa);
   return check_hip(hipGetLastError(), "dms_decode_step launch");
 }
 

@@ -116,6 +116,8 @@ struct PrepIn {
 // LDS of the prepare role.
 struct PrepShared {
   float red[4][2];
+  float rowred[4][17];      // prep_row: per-wave sums of h^2 and of the KV heads' products
+  float lg[16];             // prep_row: the row's logits
   int last, free_top, used, n;
   int wave_cnt[4];
   int q[kPrepThreads], dst[kPrepThreads], page[kPrepThreads];
@@ -280,6 +282,140 @@ __device__ __forceinline__ void prep_pair(const AppendArgs& a, const PrepIn& in,
     const int vals[8] = {kind, unit, t, slot, e, dst, appended, len};
 #pragma unroll
     for (int i = 0; i < 8; ++i) __hip_atomic_store(pl + i, vals[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One batch row's pairs in one workgroup (the fused decode step with many
+// rows, where one workgroup per pair would not leave the attention room to be
+// resident beside it): the linear adapter's sums over the row's hidden state
+// are taken once for all the KV heads (each head's products in the same order
+// as prep_pair, so the same logits), then wave w places pairs w, w + 4, ...
+// exactly as prep_pair does (deferred tables).
+template <int KV>
+__device__ __forceinline__ void prep_row(const AppendArgs& a, const PrepIn& in, int row, PrepShared& sh) {
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Hkv = g.Hkv;
+  const int nk = a.per_layer ? 1 : Hkv;          // distinct logits of the row
+  const int seq = a.seq_ids ? a.seq_ids[row] : row;
+  const bool seq_ok = seq >= 0 && seq < g.Bmax;
+  const int ppr = g.D / 8;
+  // 1. the logits
+  if (in.qneuron) {
+    if (tid < nk) {
+      const uint16_t qn = in.q[(static_cast<size_t>(row) * g.Hq + tid * g.g) * g.D + g.D - 1];
+      sh.lg[tid] = a.alpha * bf16_to_f32(qn) - a.offsets[tid];
+    }
+  } else {
+    float ss = 0.0f, dk[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dk[k] = 0.0f;
+    const uint16_t* h = in.hidden + static_cast<size_t>(row) * g.H;
+    for (int m = 8 * tid; m < g.H; m += 8 * kPrepThreads) {
+      const uint4 hv = *reinterpret_cast<const uint4*>(h + m);
+      const float4 g0 = *reinterpret_cast<const float4*>(in.gamma + m);
+      const float4 g1 = *reinterpret_cast<const float4*>(in.gamma + m + 4);
+      const uint32_t u[4] = {hv.x, hv.y, hv.z, hv.w};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = __uint_as_float((e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16));
+        ss = fmaf(x[e], x[e], ss);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k >= nk) break;
+        const float* w = in.W + static_cast<size_t>(k) * g.H;
+        const float4 w0 = *reinterpret_cast<const float4*>(w + m), w1 = *reinterpret_cast<const float4*>(w + m + 4);
+        const float gw[8] = {g0.x * w0.x, g0.y * w0.y, g0.z * w0.z, g0.w * w0.w,
+                             g1.x * w1.x, g1.y * w1.y, g1.z * w1.z, g1.w * w1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dk[k] = fmaf(gw[e], x[e], dk[k]);
+      }
+    }
+    ss = wave_sum_dpp(ss);
+    if (lane == 0) sh.rowred[wave][16] = ss;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k >= nk) break;
+      const float v = wave_sum_dpp(dk[k]);
+      if (lane == 0) sh.rowred[wave][k] = v;
+    }
+    __syncthreads();
+    if (tid < nk) {
+      const float s2 = (sh.rowred[0][16] + sh.rowred[1][16]) + (sh.rowred[2][16] + sh.rowred[3][16]);
+      const float dd = (sh.rowred[0][tid] + sh.rowred[1][tid]) + (sh.rowred[2][tid] + sh.rowred[3][tid]);
+      const float r = 1.0f / sqrtf(s2 / static_cast<float>(g.H) + a.eps);
+      float z = r * dd;
+      if (a.bias) z += a.bias[tid];
+      sh.lg[tid] = a.alpha * z - a.offsets[tid];
+    }
+  }
+  __syncthreads();
+  if (!seq_ok) {
+    if (tid == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+  }
+  const int t = seq_ok ? d.pos[seq] : 0;
+  // 2. the pairs, one wave each
+  for (int kh = wave; kh < Hkv; kh += 4) {
+    const int p = row * Hkv + kh;
+    const int unit = seq_ok ? seq * Hkv + kh : 0;
+    int len = 0, cur = -1;
+    if (seq_ok) {
+      len = d.lengths[unit];
+      cur = d.cur_page[unit];
+    }
+    uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+    const size_t rowoff = static_cast<size_t>(p) * g.D * 2;
+    if (lane < ppr) {
+      kx = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + rowoff + 16 * lane);
+      vx = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v) + rowoff + 16 * lane);
+    }
+    const int64_t ri = static_cast<int64_t>(unit) * g.w + (t % g.w);
+    int rv = 0, rrow = -1;
+    if (seq_ok && t >= g.w) {
+      rv = d.ring[ri];
+      rrow = d.ring_row[ri];
+    }
+    const float lg = sh.lg[a.per_layer ? 0 : kh];
+    const int e = (!a.disable && lg > 0.0f) ? 1 : 0;
+    if (lane == 0) {
+      a.evict_out[p] = static_cast<uint8_t>(e);
+      if (a.logits_out) a.logits_out[p] = lg;
+    }
+    bool valid = seq_ok, new_page = false;
+    int slot = 0, dst = -1, page = -1;
+    if (seq_ok) {
+      if (t + 1 > g.max_tokens) {
+        if (lane == 0) set_status(d.ctl, DMS_DEV_CAPACITY);
+        valid = false;
+      } else if (t >= g.w && rv < 0) {
+        slot = rv & 0x7FFFFFFF;
+        dst = rrow;
+        page = dst / g.P;
+      } else {
+        slot = len;
+        if (slot % g.P == 0) {
+          new_page = true;
+        } else {
+          page = cur;
+          dst = page * g.P + slot % g.P;
+        }
+      }
+    }
+    const int appended = slot == len;
+    if (valid && !new_page) {
+      if (lane == 0) d.slot_meta[dst] = t | (e << 31);
+      prep_store_row<KV>(d, dst, page, false, ppr, lane % ppr, kx, vx, lane < ppr);
+    }
+    if (lane == 0) {
+      const int kind = !valid ? kPlanNone : new_page ? kPlanNewPage : kPlanTables;
+      int32_t* pl = d.chunk_info + static_cast<int64_t>(p) * 8;
+      const int vals[8] = {kind, unit, t, slot, e, dst, appended, len};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) __hip_atomic_store(pl + i, vals[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

@@ -12,7 +12,9 @@ row quantised by the attention exactly as the append stores it, in place,
 into the current page or as the first row of a new page).  Shapes cover GQA
 groups 1, 2, 4 and 8, head_dim 64 and 128, bf16 and fp8 pages, both decision
 sources, layer mode, and more than 64 (row, KV head) units; bf16 pages run
-the matrix-core decode, and, for two shapes, the lane-per-row-piece one.
+the matrix-core decode, and, for two shapes, the lane-per-row-piece one; the
+decisions and placements run one workgroup per (row, KV head) pair or, for
+three shapes, one per batch row.
 """
 import copy
 
@@ -36,6 +38,10 @@ SHAPES = {
     # bf16 pages through the lane-per-row-piece kernel (the matrix-core one off)
     "g4_d128_linear_vector": (3, 8, 2, 128, "linear", "head", "bf16"),
     "g2_d64_qneuron_vector": (3, 8, 4, 64, "qneuron", "head", "bf16"),
+    # one prepare workgroup per batch row (the layout of large batches)
+    "g4_d128_linear_fp8_rows": (3, 8, 2, 128, "linear", "head", "fp8"),
+    "g2_d64_qneuron_rows": (3, 8, 4, 64, "qneuron", "head", "bf16"),
+    "g8_d64_linear_layer_rows": (2, 16, 2, 64, "linear", "layer", "bf16"),
 }
 
 
@@ -79,6 +85,8 @@ def test_step_ragged_positions(name, monkeypatch):
     _cuda()
     if name.endswith("_vector"):
         monkeypatch.setenv("DMS_DECODE_MFMA", "0")
+    if name.endswith("_rows"):
+        monkeypatch.setenv("DMS_DECODE_STEP_ROWS", "1")
     wl = _workload(name, list(SHAPES).index(name))
     prep = prepare(wl)
     r = Runner(prep, max_chunk=64)
