@@ -15,6 +15,7 @@
 // Rounding the normalised activations to bf16 for a matrix-core product would
 // move logits by ~0.1, far more than the 1e-2 margin decisions are compared at.
 #include <algorithm>
+#include <cstdlib>
 
 #include "dms_internal.h"
 
@@ -308,8 +309,141 @@ __global__ __launch_bounds__(256) void decide_linear_chunk_kernel(DecideArgs a) 
   }
 }
 
+// Prefill chunks on the matrix cores (bf16 hidden states, H a multiple of
+// 2048, at most 8 KV heads).  decide_w_kernel first writes gamma * W of each
+// head as two bf16 parts, the nearest bf16 and the rest, whose sum carries
+// about 16 significant bits of the fp32 product (so z differs from the fp32
+// sum by about 1e-6 of its terms' magnitude), laid out as the matrix cores
+// read it.  decide_linear_mfma_kernel then takes 16 tokens per workgroup,
+// each of its four waves over a quarter of H: v_mfma_f32_16x16x32_bf16 with
+// the tokens as rows (A: lane (g, n) holds elements 32s + 8g.. of token n's
+// row, as stored) and 16 columns (head c's two parts in columns c and c + 8),
+// the hidden states streaming from HBM once with 8 to 16 steps (8-16 KB per
+// wave) in flight; the sums of squares run on the vector ALU beside them.
+typedef __bf16 dc_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float dc_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t dc_pack_bf16(float lo, float hi) {
+  typedef __bf16 dc_bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float dc_f32x2 __attribute__((ext_vector_type(2)));
+  dc_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, dc_bf16x2));
+}
+
+// gw[kb][n] = 8 bf16 of column n (head n % 8, part n / 8) for elements 8kb..8kb+7
+template <int HKV>
+__global__ __launch_bounds__(256) void decide_w_kernel(DecideArgs a, uint4* gw) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int kb = i >> 4, n = i & 15, c = n & 7;
+  if (kb >= a.H / 8) return;
+  float part[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = 8 * kb + e;
+    const float p = c < HKV ? a.gamma[k] * a.W[static_cast<size_t>(c) * a.H + k] : 0.0f;
+    const float hi = static_cast<float>(static_cast<__bf16>(p));
+    part[e] = n >= 8 ? p - hi : p;
+  }
+  gw[i] = make_uint4(dc_pack_bf16(part[0], part[1]), dc_pack_bf16(part[2], part[3]), dc_pack_bf16(part[4], part[5]),
+                     dc_pack_bf16(part[6], part[7]));
+}
+
+constexpr int kDcWaves = 4;
+
+template <int HKV>
+__global__ __launch_bounds__(64 * kDcWaves) void decide_linear_mfma_kernel(DecideArgs a, const uint4* __restrict__ gw) {
+  constexpr int U = 8;                              // steps per round; two rounds in flight
+  constexpr int NW = kDcWaves;
+  __shared__ float s_acc[NW][16][16];
+  __shared__ float s_ss[NW][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int tok0 = blockIdx.x * 16;
+  const bool live = tok0 + n16 < a.ntok;
+  const uint16_t* hrow = static_cast<const uint16_t*>(a.hidden) +
+                         static_cast<size_t>(live ? tok0 + n16 : tok0) * a.H;
+  const int kq = a.H / NW;                          // this wave's share
+  const int k0 = wave * kq;
+  const int nsteps = kq / 32;                       // a multiple of U
+  const int nr = nsteps / U;
+  dc_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float ss = 0.0f;
+  uint4 ha[U], ba[U], hb[U], bb[U];
+  // round r's loads (past the last round: the last round again, from cache)
+  auto load = [&](uint4 (&h)[U], uint4 (&b)[U], int r) {
+    const int s0 = min(r, nr - 1) * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + 32 * (s0 + u) + 8 * g4;
+      h[u] = *reinterpret_cast<const uint4*>(hrow + k);
+      b[u] = gw[(k >> 3) * 16 + n16];
+    }
+  };
+  auto compute = [&](const uint4 (&h)[U], const uint4 (&b)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint4 x4 = live ? h[u] : make_uint4(0, 0, 0, 0);
+      const uint32_t hw[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __uint_as_float((e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16));
+        ss = fmaf(x, x, ss);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dc_bf16x8, x4),
+                                                    __builtin_bit_cast(dc_bf16x8, b[u]), acc, 0, 0, 0);
+    }
+  };
+  load(ha, ba, 0);
+  for (int r = 0; r < nr; r += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(hb, bb, r + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ha, ba);
+    __builtin_amdgcn_sched_barrier(0);
+    load(ha, ba, r + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (r + 1 < nr) compute(hb, bb);
+  }
+  // sums of squares: lane (g, n) has token n's over its elements; fold the row groups
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  // acc[i] = this wave's share of token 4g + i, column n
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_acc[wave][4 * g4 + i][n16] = acc[i];
+  if (g4 == 0) s_ss[wave][n16] = ss;
+  __syncthreads();
+  if (tid >= 16 || tok0 + tid >= a.ntok) return;
+  const int tok = tok0 + tid;
+  float s2 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s2 += s_ss[w][tid];
+  const float r = 1.0f / sqrtf(s2 / static_cast<float>(a.H) + a.eps);
+  const int b = tok / a.T, t = tok % a.T;
+  float lg0 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < HKV; ++k) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) dot += s_acc[w][tid][k] + s_acc[w][tid][k + 8];
+    float z = r * dot;
+    if (a.bias) z += a.bias[k];
+    float lg = a.alpha * z - a.offsets[k];
+    if (k == 0) lg0 = lg;
+    if (a.per_layer) lg = lg0;
+    const size_t o = (static_cast<size_t>(b) * HKV + k) * a.T + t;
+    if (a.logits) a.logits[o] = lg;
+    a.evict[o] = (!a.disable && lg > 0.0f) ? 1 : 0;
+  }
+}
+
+// DMS_DECIDE_MFMA=0 keeps prefill chunks on the vector-ALU kernel.
+static bool dc_mfma_enabled() {
+  const char* e = std::getenv("DMS_DECIDE_MFMA");
+  return !e || std::atoi(e) != 0;
+}
+
 template <typename ACT, int HKV>
-static void launch_linear_h(const DecideArgs& a, hipStream_t st) {
+static void launch_linear_h(const DecideArgs& a, uint4* gw, hipStream_t st) {
   // few tokens (decode): one token per workgroup, all loads of a thread in
   // flight at once; many tokens (prefill chunks): 8 tokens share gamma * W
   // registers (bf16), or 4 tokens share W (fp32 activations)
@@ -318,6 +452,12 @@ static void launch_linear_h(const DecideArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((decide_linear_tok_kernel<HKV <= 8 ? HKV : 8>), dim3(a.ntok), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((decide_linear_kernel<ACT, HKV, 1, (HKV <= 8 ? 4 : 2)>), dim3(a.ntok), dim3(256), 0, st, a);
+  } else if (sizeof(ACT) == 2 && HKV <= 8 && a.H % 2048 == 0 && reinterpret_cast<uintptr_t>(a.hidden) % 16 == 0 &&
+             gw && dc_mfma_enabled()) {
+    constexpr int HK = HKV <= 8 ? HKV : 8;
+    hipLaunchKernelGGL((decide_w_kernel<HK>), dim3((a.H / 8 * 16 + 255) / 256), dim3(256), 0, st, a, gw);
+    hipLaunchKernelGGL((decide_linear_mfma_kernel<HK>), dim3((a.ntok + 15) / 16), dim3(64 * kDcWaves), 0, st, a,
+                       static_cast<const uint4*>(gw));
   } else if (sizeof(ACT) == 2 && HKV <= 8 && a.H % 8 == 0 && reinterpret_cast<uintptr_t>(a.hidden) % 16 == 0) {
     constexpr int TT = 8;
     hipLaunchKernelGGL((decide_linear_chunk_kernel<HKV <= 8 ? HKV : 8, TT>), dim3((a.ntok + TT - 1) / TT), dim3(256),
@@ -329,13 +469,13 @@ static void launch_linear_h(const DecideArgs& a, hipStream_t st) {
 }
 
 template <typename ACT>
-static void launch_linear(const DecideArgs& a, int hkv, hipStream_t st) {
+static void launch_linear(const DecideArgs& a, int hkv, uint4* gw, hipStream_t st) {
   switch (hkv) {
-    case 1: launch_linear_h<ACT, 1>(a, st); break;
-    case 2: launch_linear_h<ACT, 2>(a, st); break;
-    case 4: launch_linear_h<ACT, 4>(a, st); break;
-    case 8: launch_linear_h<ACT, 8>(a, st); break;
-    case 16: launch_linear_h<ACT, 16>(a, st); break;
+    case 1: launch_linear_h<ACT, 1>(a, gw, st); break;
+    case 2: launch_linear_h<ACT, 2>(a, gw, st); break;
+    case 4: launch_linear_h<ACT, 4>(a, gw, st); break;
+    case 8: launch_linear_h<ACT, 8>(a, gw, st); break;
+    case 16: launch_linear_h<ACT, 16>(a, gw, st); break;
     default: break;
   }
 }
@@ -362,8 +502,8 @@ extern "C" int dms_decide(dms_cache* cache, const void* hidden, const float* rms
       return fail(DMS_ERR_ARG, "rms_gamma and W must be 16-byte aligned");
     DecideArgs a{hidden, rms_gamma, W, bias, offsets, B * T, T, c.hidden, c.alpha_scale, c.rms_eps,
                  c.alpha_per == DMS_ALPHA_PER_LAYER, c.disable_eviction != 0, logits_out, evict_out};
-    if (act_f32) launch_linear<float>(a, hkv, st);
-    else launch_linear<uint16_t>(a, hkv, st);
+    if (act_f32) launch_linear<float>(a, hkv, nullptr, st);
+    else launch_linear<uint16_t>(a, hkv, cache->dev.decide_w, st);
   } else {
     if (!q_inout) return fail(DMS_ERR_ARG, "q_inout is required for the query-neuron decision");
     QneuronArgs a{q_inout, offsets, B * T, T, c.num_kv_heads, c.num_q_heads / c.num_kv_heads, c.head_dim,

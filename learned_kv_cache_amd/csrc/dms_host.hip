@@ -228,6 +228,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
   c->dev.unit_info = reinterpret_cast<int32_t*>(base + L.unit_info);
   c->dev.arrive = reinterpret_cast<int32_t*>(base + L.arrive);
   c->dev.plan = reinterpret_cast<int32_t*>(base + L.plan);
+  c->dev.decide_w = reinterpret_cast<uint4*>(base + L.decide_w);
   Geo& g = c->geo;
   g.Bmax = cfg->max_batch;
   g.Hq = cfg->num_q_heads;

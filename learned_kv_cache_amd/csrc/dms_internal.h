@@ -39,6 +39,7 @@ struct DevCache {
   int32_t* unit_info;    // [kMaxUnits][4] decode: partial base, partial count, merge counter
   int32_t* arrive;       // [kArriveGroups][kArriveStride] decode step arrival counters (word 0 of each)
   int32_t* plan;         // decode plan of the fused step: [kPlanHeader] header, [Bmax] rows, [kPlanMaxWgs][kPlanRec]
+  uint4* decide_w;       // [hidden / 8][16] linear adapter's gamma * W, split bf16 (prefill chunk decisions)
 };
 
 // Decode plan header words (plan[0] = 1 marks the plan valid; every other

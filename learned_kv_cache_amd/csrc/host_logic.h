@@ -33,7 +33,7 @@ constexpr int kPlanRec = 16;           // int32 words per workgroup record
 // Byte offsets of the regions carved out of one cache buffer.
 struct Layout {
   size_t k_pages, v_pages, scales, page_amax, slot_meta, page_table, lengths, ring, ring_row, cur_page, pos,
-      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, plan, total;
+      free_stack, ctl, chunk_slot, chunk_info, unit_info, arrive, plan, decide_w, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -87,6 +87,11 @@ inline size_t plan_words(int Bmax) {
          static_cast<size_t>(kPlanMaxWgs) * kPlanRec;
 }
 
+// The linear adapter's gamma * W of a prefill chunk decision as the matrix
+// cores read it: per 8 hidden elements, 16 columns (8 heads, two bf16 parts
+// each) of 8 bf16.
+inline size_t decide_w_bytes(int hidden) { return (static_cast<size_t>(hidden) + 7) / 8 * 16 * 16; }
+
 // The regions of one cache buffer, each 256-byte aligned, in this order (the
 // configuration must be valid).
 inline void compute_layout(const dms_config& c, Layout* L) {
@@ -120,6 +125,7 @@ inline void compute_layout(const dms_config& c, Layout* L) {
   L->unit_info = take(static_cast<size_t>(kMaxUnits) * 4 * sizeof(int32_t));
   L->arrive = take(static_cast<size_t>(kArriveGroups) * kArriveStride * sizeof(int32_t));
   L->plan = take(plan_words(c.max_batch) * sizeof(int32_t));
+  L->decide_w = take(decide_w_bytes(c.hidden));
   L->total = off;
 }
 

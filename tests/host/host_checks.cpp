@@ -95,13 +95,14 @@ static void check_layout() {
     c.pool_pages = 1 + static_cast<int>(rng() % 5000);
     c.max_chunk = 1 + static_cast<int>(rng() % kMaxChunk);
     c.kv_dtype = pick({DMS_F32, DMS_BF16, DMS_FP8_E4M3});
+    c.hidden = 4 * (1 + static_cast<int>(rng() % 2048));
     int st;
     if (config_error(&c, &st)) continue;
     Layout L;
     compute_layout(c, &L);
     const size_t off[] = {L.k_pages, L.v_pages, L.scales, L.page_amax, L.slot_meta, L.page_table, L.lengths, L.ring,
                           L.ring_row, L.cur_page, L.pos, L.free_stack, L.ctl, L.chunk_slot, L.chunk_info,
-                          L.unit_info, L.arrive, L.plan, L.total};
+                          L.unit_info, L.arrive, L.plan, L.decide_w, L.total};
     const size_t units = static_cast<size_t>(c.max_batch) * c.num_kv_heads;
     const size_t maxp = (static_cast<size_t>(c.max_tokens_per_seq) + c.block_size - 1) / c.block_size;
     const size_t pool = c.pool_pages, P = c.block_size;
@@ -110,9 +111,10 @@ static void check_layout() {
                            pool * 8, pool * 8, pool * P * 4, units * maxp * 4, units * 4,
                            units * c.window * 4, units * c.window * 4, units * 4, static_cast<size_t>(c.max_batch) * 4,
                            pool * 4, kCtlWords * 4, units * c.max_chunk * 4, units * 32, kMaxUnits * 16,
-                           kArriveGroups * kArriveStride * 4, plan_words(c.max_batch) * 4};
+                           kArriveGroups * kArriveStride * 4, plan_words(c.max_batch) * 4,
+                           decide_w_bytes(c.hidden)};
     CHECK(L.k_pages == 0);
-    for (int r = 0; r < 18; ++r) {
+    for (int r = 0; r < 19; ++r) {
       CHECK(off[r] % 256 == 0);
       CHECK(off[r + 1] >= off[r] + need[r]);          // no region overlaps the next
       CHECK(off[r + 1] - off[r] < need[r] + 256);     // and no more than alignment in between
