@@ -670,14 +670,16 @@ def cpu_baseline(steps: int):
 
 def measure_peaks(dms, torch) -> dict:
     """The box's own rates (libdms_probe): a streaming read of a 4 GiB buffer
-    (16 times the Infinity Cache) with a few launch shapes, best of them, and a
+    (16 times the Infinity Cache) over 15 launch shapes, best of them, and a
     dense bf16 matrix-core loop (8 independent 16x16x32 products per wave,
     8 waves per CU); HIP events on the launch stream around repeated calls."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     buf = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(8 * cus * 8, dtype=torch.int32, device="cuda")
     best = (0.0, None)
-    for grid, unroll in ((cus * 4, 8), (cus * 8, 8), (cus * 4, 16), (cus * 8, 16)):
+    sweep = []
+    # one to eight workgroups per CU, 4 to 16 loads of 16 bytes in flight per thread
+    for grid, unroll in [(cus * w, u) for w in (1, 2, 3, 4, 8) for u in (4, 8, 16)]:
         dms.probe_read(buf, grid, unroll, sink)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -688,6 +690,7 @@ def measure_peaks(dms, torch) -> dict:
         e1.record()
         torch.cuda.synchronize()
         gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        sweep.append({"grid": grid, "unroll": unroll, "gbs": round(gbs, 1)})
         if gbs > best[0]:
             best = (gbs, {"grid": grid, "unroll": unroll, "bytes": nbytes})
     del buf
@@ -700,7 +703,7 @@ def measure_peaks(dms, torch) -> dict:
     e1.record()
     torch.cuda.synchronize()
     tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
-    return {"hbm_read_gbs": best[0], "hbm_read_shape": best[1], "bf16_mfma_tflops": tflops,
+    return {"hbm_read_gbs": best[0], "hbm_read_shape": best[1], "hbm_read_sweep": sweep, "bf16_mfma_tflops": tflops,
             "hbm_nominal_gbs": HBM_PEAK_GBS, "bf16_nominal_tflops": BF16_PEAK_TFLOPS, "compute_units": cus}
 
 
