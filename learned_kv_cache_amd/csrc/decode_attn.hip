@@ -1021,6 +1021,194 @@ __device__ __forceinline__ void mf_segment(const DecodeArgs& a, const StepArgs* 
   }
 }
 
+// Matrix-core variant for fp8 pages (D = 128, dms_decode_attn).  The same
+// tiles and lane roles as the bf16 variant, with the contraction index of the
+// score product permuted: lane (g, n) loads the 32 contiguous codes
+// 32g..32g+31 of key n's row (two 16-byte loads) and uses codes 32g + 8s..
+// at k-step s, widened exactly to bf16; the query operand takes the same
+// elements.  V rows are 128 bytes: lane (g, s, c) holds codes 16c..16c+15 of
+// the rows of keys 4g + s and 4g + 2 + s.  A tile lies in one page, so the
+// page's K scale multiplies the tile's scores and its V scale the
+// probabilities of the P.V products (l sums the unscaled ones).
+struct Mf8Tile {
+  uint4 k[2];
+  uint4 v[2];
+  float sk, sv;
+};
+
+__device__ __forceinline__ void mf8_load(Mf8Tile& b, int t, int nt, int t0, int pb, int pt_reg,
+                                         const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
+                                         const float* __restrict__ scales, int hi, int psh, int pmask, int lane) {
+  constexpr int RB = 128;
+  const int tb = t0 + 16 * min(t, nt - 1);
+  const int page = __builtin_amdgcn_readlane(pt_reg, (tb >> psh) - pb);
+  const uint32_t prow = static_cast<uint32_t>(page) * static_cast<uint32_t>(pmask + 1);
+  const int g4 = lane >> 4, n16 = lane & 15;
+  b.sk = scales[2 * page];
+  b.sv = scales[2 * page + 1];
+  {
+    const int r = tb + n16;
+    const int rr = r >= hi ? tb : r;
+    const uint8_t* base = kp + (prow + static_cast<uint32_t>(rr & pmask)) * static_cast<uint32_t>(RB) + 32 * g4;
+    b.k[0] = *reinterpret_cast<const uint4*>(base);
+    b.k[1] = *reinterpret_cast<const uint4*>(base + 16);
+  }
+  const int vs = (lane & 15) >> 3, vc = lane & 7;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = tb + 4 * g4 + 2 * j + vs;
+    const int rr = r >= hi ? tb : r;
+    b.v[j] = *reinterpret_cast<const uint4*>(vp + (prow + static_cast<uint32_t>(rr & pmask)) *
+                                                      static_cast<uint32_t>(RB) + 16 * vc);
+  }
+}
+
+// o[16] += P (bf16 pair: keys a, b) . (fp8 V rows a, b, 16 codes each, widened exactly)
+__device__ __forceinline__ void mf8_pv_pair(const uint4& va, const uint4& vb, uint32_t P, float* o) {
+  const uint32_t x[4] = {va.x, va.y, va.z, va.w};
+  const uint32_t y[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t xl, xh, yl, yh;                      // codes 4w..4w+3 as two bf16 pairs
+    fp8x4_to_bf16(x[w], xl, xh);
+    fp8x4_to_bf16(y[w], yl, yh);
+    const uint32_t xs[2] = {xl, xh}, ys[2] = {yl, yh};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t lo2 = __builtin_amdgcn_perm(ys[q], xs[q], 0x05040100u);
+      const uint32_t hi2 = __builtin_amdgcn_perm(ys[q], xs[q], 0x07060302u);
+      o[4 * w + 2 * q] = dot2(P, lo2, o[4 * w + 2 * q]);
+      o[4 * w + 2 * q + 1] = dot2(P, hi2, o[4 * w + 2 * q + 1]);
+    }
+  }
+}
+
+template <int G, int H>
+__device__ __forceinline__ void mf8_pv_head(const Mf8Tile& b, uint32_t pa, uint32_t pb, bool vs1, float (&o)[G][16]) {
+  if constexpr (H < G) {
+    const uint32_t Pa = mf_row_bcast<H>(pa), Pb = mf_row_bcast<H>(pb);
+    mf8_pv_pair(b.v[0], b.v[1], vs1 ? Pb : Pa, o[H]);
+    mf8_pv_head<G, H + 1>(b, pa, pb, vs1, o);
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void mf8_compute(const Mf8Tile& b, int t, int t0, int lo, int hi, float scale_log2,
+                                            const uint4 (&qb)[4], float& m, float& lsum, float (&o)[G][16],
+                                            int lane) {
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int tb = t0 + 16 * t;
+  mf_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t kw[8] = {b.k[0].x, b.k[0].y, b.k[0].z, b.k[0].w, b.k[1].x, b.k[1].y, b.k[1].z, b.k[1].w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t a0, a1, a2, a3;
+    fp8x4_to_bf16(kw[2 * s], a0, a1);
+    fp8x4_to_bf16(kw[2 * s + 1], a2, a3);
+    const uint4 a = make_uint4(a0, a1, a2, a3);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, a),
+                                                  __builtin_bit_cast(mf_bf16x8, qb[s]), acc, 0, 0, 0);
+  }
+  const float sc_k = scale_log2 * b.sk;
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tb + 4 * g4 + i;
+    const bool ok = n16 < G && r >= lo && r < hi;
+    sc[i] = ok ? acc[i] * sc_k : -INFINITY;
+  }
+  float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  tmax = mf_max_x16(mf_max_x32(tmax));
+  const bool need = tmax > m + kDecRescaleLog2;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;
+    if (need) m = tmax;
+    lsum *= alpha;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ah = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[h][e] *= ah;
+    }
+  }
+  const float msub = (m == -INFINITY) ? 0.0f : m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - msub);
+  lsum += (p[0] + p[1]) + (p[2] + p[3]);
+  // V rows of a lane: keys 4g + s and 4g + 2 + s
+  const uint32_t pa = pack_bf16(p[0] * b.sv, p[2] * b.sv);
+  const uint32_t pb = pack_bf16(p[1] * b.sv, p[3] * b.sv);
+  mf8_pv_head<G, 0>(b, pa, pb, (lane & 15) >= 8, o);
+}
+
+template <int G>
+__device__ __forceinline__ void mf8_segment(const DecodeArgs& a, FastLds<G, 128, false>& lds, const int32_t* pt,
+                                            int row, int kh, int lo, int hi, int wave, int lane) {
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int psh = g.Pshift, pmask = g.P - 1;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  // query operand: lane (g, n) holds elements 32g + 8s.. of head n at k-step s
+  uint4 qb[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<size_t>(row) * g.Hq + kh * G + min(n16, G - 1)) * 128 + 32 * g4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qb[s] = n16 < G ? *reinterpret_cast<const uint4*>(qp + 8 * s) : make_uint4(0, 0, 0, 0);
+  }
+  float m = -INFINITY, lsum = 0.0f;
+  float o[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[h][e] = 0.0f;
+  for (int pb = lo >> psh; pb <= (hi - 1) >> psh; pb += 64) {
+    const int plast = min((hi - 1) >> psh, pb + 63);
+    const int pt_reg = (pb + lane <= plast) ? pt[pb + lane] : 0;
+    const int blo = max(lo, pb << psh), bhi = min(hi, (plast + 1) << psh);
+    const int t0 = blo & ~15;
+    const int nt = (bhi - t0 + 15) >> 4;
+    Mf8Tile ta, tb;
+    auto load = [&](Mf8Tile& b, int t) {
+      mf8_load(b, t, nt, t0, pb, pt_reg, d.k_pages, d.v_pages, d.scales, hi, psh, pmask, lane);
+    };
+    auto compute = [&](const Mf8Tile& b, int t) { mf8_compute<G>(b, t, t0, lo, hi, g.scale_log2, qb, m, lsum, o, lane); };
+    load(ta, wave);
+    for (int t = wave; t < nt; t += 8) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(tb, t + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ta, t);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ta, t + 8);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 4 < nt) compute(tb, t + 4);
+    }
+  }
+  // sums over the row groups and the two rows of a group
+  lsum = mf_sum_x16(mf_sum_x32(lsum));
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[h][e] = mf_sum_x16(mf_sum_x32(o[h][e]));
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[h][e] += dpp_f<0x128, 0xF>(o[h][e], 0.0f);   // row_ror:8
+  if (lane < 8) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lds.o[wave][0][h][16 * lane + e] = o[h][e];
+  }
+  if (lane < G) {
+    lds.ml[wave][0][lane][0] = m;
+    lds.ml[wave][0][lane][1] = lsum;
+  }
+}
+
 // The decode plan (fused step): the kernel variant a plan was split for, and
 // where its rows and records start.
 template <int D, int G, bool FP8, int LPR, bool MF>
@@ -1054,7 +1242,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
   constexpr int RG = 64 / LPR;
   // rows per workgroup pass: the floor of a workgroup's share in the split
   constexpr int RPP = MF ? 64 : 4 * RG;
-  static_assert(!MF || !FP8, "the matrix-core variant reads bf16 pages");
+  static_assert(!MF || !FP8 || (!STEP && D == 128), "matrix-core fp8: dms_decode_attn with head_dim 128");
   constexpr int NV = BPL / 16;
   static_assert(NP % 2 == 0, "passes are paired for the P.V dot products");
   static_assert(BPL % 16 == 0, "a lane loads whole 16-byte pieces");
@@ -1318,7 +1506,9 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
       }
     }
 
-    if constexpr (MF) {
+    if constexpr (MF && FP8) {
+      mf8_segment<G>(a, lds, pt, row, kh, lo, hi, wave, lane);
+    } else if constexpr (MF) {
       mf_segment<D, G, STEP>(a, sa, lds, use_plan, p_np, p_page, pt, row, kh, lo, hi, vrow, skip, wave, lane);
     } else {
     uint32_t qv[G][QW];
@@ -1699,6 +1889,11 @@ static int launch_fast_dg(const DecodeArgs& a, int grid, int np, hipStream_t st)
       hipLaunchKernelGGL((decode_attn_fast_kernel<D, G, 2, false, LPR1, true>), dim3(grid), dim3(256), 0, st, a);
       return DMS_OK;
     }
+  } else if constexpr (D == 128) {
+    if (a.mfma) {
+      hipLaunchKernelGGL((decode_attn_fast_kernel<128, G, 2, true, 8, true>), dim3(grid), dim3(256), 0, st, a);
+      return DMS_OK;
+    }
   }
   switch (np) {
     case 2: launch_fast_np<D, G, FP8, 2>(a, grid, st); break;
@@ -1799,6 +1994,13 @@ static bool mfma_decode_ok(const dms_cache* cache) {
   const Geo& g = cache->geo;
   return cache->decode_mfma != 0 && g.kv_dtype == DMS_BF16 && g.Pshift >= 4 && fast_decode_ok(cache, nullptr);
 }
+// dms_decode_attn also takes it for fp8 pages of head_dim 128 (the one-launch
+// step keeps fp8 pages on the lane-per-row-piece kernel).
+static bool mfma_attn_ok(const dms_cache* cache) {
+  const Geo& g = cache->geo;
+  return mfma_decode_ok(cache) || (cache->decode_mfma != 0 && g.kv_dtype == DMS_FP8_E4M3 && g.D == 128 &&
+                                   g.Pshift >= 4 && fast_decode_ok(cache, nullptr));
+}
 
 // ---- decode attention without an allocation ------------------------------
 // For callers that cannot allocate (code under HIP graph capture, serving
@@ -1856,7 +2058,7 @@ extern "C" int dms_decode_attn(dms_cache* cache, const int32_t* seq_ids, const v
   int s = check_workspace(cache, B, workspace, ws_bytes);
   if (s) return s;
   DecodeArgs a{cache->dev, g, seq_ids, q, out, B, cache->decode_lpr, static_cast<float*>(workspace),
-               mfma_decode_ok(cache) ? cache->decode_mfma : 0};
+               mfma_attn_ok(cache) ? cache->decode_mfma : 0};
   const int grid = decode_grid_for(cache);
   hipStream_t st = as_stream(stream);
   // the fast kernels read q and write out in 16-byte pieces
