@@ -295,6 +295,20 @@ int dms_train_gate(const float* logits, const float* noise, float tau, int64_t n
                    float* probs_out, float* hard_out, void* stream);
 
 /*
+ * Backward of dms_train_gate (walkthrough, Gumbel 噪声与可微门控): the gradient
+ * to the decision logits given the loss's gradients with respect to y (dy,
+ * e.g. dms_train_attn_bwd's), to the straight-through decision (dhard: its
+ * forward value is the hard threshold, its gradient that of probs) and to
+ * probs (dprobs):
+ *   dlogits = (dy + (dhard + dprobs) * probs * (1 - probs)) / tau,
+ * probs = sigmoid((logits + noise) / tau) recomputed from the same logits,
+ * noise and tau as the forward.  All arrays are n device floats; dy, dhard,
+ * dprobs and noise may be NULL (zero); logits and dlogits_out are required.
+ */
+int dms_train_gate_bwd(const float* logits, const float* noise, float tau, int64_t n, const float* dy,
+                       const float* dhard, const float* dprobs, float* dlogits_out, void* stream);
+
+/*
  * Forward of the training-mode attention (walkthrough, 训练模式): causal
  * attention over the whole sequence in which key j keeps its score for
  * queries closer than `window` and gets logsigmoid(-y[j]) added for queries
@@ -342,6 +356,22 @@ int dms_cache_clear_status(dms_cache* cache, void* stream);
 
 /* Synchronises `stream` and copies the tables into host buffers. */
 int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out);
+
+/* Debug check of the cache's structural invariants (walkthrough, 推理模式:
+ * the delayed-eviction slot rule that keeps the live slots equal to the keys
+ * the last query may see; the shared page pool).  Synchronises `stream`,
+ * copies the tables to the host and checks there: per (sequence, head),
+ * min(position, window) <= L <= position; live slots 0..L-1 each hold one
+ * distinct token, kept or inside the window of the last position; the
+ * window entries of the last `window` positions name the slots holding
+ * those tokens (slot, evict flag and page row); the current page is the page
+ * of slot L - 1; page ids lie in the pool, each page is held by one head or
+ * free, and held + free = pool.  *violations gets a bit mask (0 =
+ * consistent): 0x1 length, 0x2 page id, 0x4 page ownership, 0x8 slot
+ * occupants, 0x10 window entries, 0x20 current page, 0x40 free stack;
+ * *first_unit (may be NULL) the first sequence * Hkv + head found wrong, or
+ * -1.  Returns DMS_ERR_ARG for NULL cache or violations. */
+int dms_cache_check(dms_cache* cache, void* stream, uint32_t* violations, int32_t* first_unit);
 
 /* Synchronises `stream` and summarises occupancy (walkthrough, 损失函数与压缩比调度:
  * realised compression; here tokens / live slots). */

@@ -538,7 +538,36 @@ __global__ __launch_bounds__(256) void train_gate_kernel(const float* __restrict
   }
 }
 
+// dlogits = (dy + (dhard + dprobs) * p * (1 - p)) / tau, p = sigmoid(y); a
+// missing gradient is zero.
+__global__ __launch_bounds__(256) void train_gate_bwd_kernel(const float* __restrict__ logits,
+                                                             const float* __restrict__ noise, float inv_tau, int64_t n,
+                                                             const float* __restrict__ dy,
+                                                             const float* __restrict__ dhard,
+                                                             const float* __restrict__ dprobs,
+                                                             float* __restrict__ dlogits) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float y = (logits[i] + (noise ? noise[i] : 0.0f)) * inv_tau;
+    const float p = 1.0f / (1.0f + __expf(-y));
+    const float via_p = (dhard ? dhard[i] : 0.0f) + (dprobs ? dprobs[i] : 0.0f);
+    dlogits[i] = ((dy ? dy[i] : 0.0f) + via_p * (p * (1.0f - p))) * inv_tau;
+  }
+}
+
 }  // namespace dms
+
+extern "C" int dms_train_gate_bwd(const float* logits, const float* noise, float tau, int64_t n, const float* dy,
+                                  const float* dhard, const float* dprobs, float* dlogits_out, void* stream) {
+  if (!logits || !dlogits_out) return fail(DMS_ERR_ARG, "logits and dlogits_out are required");
+  if (n < 0) return fail(DMS_ERR_ARG, "n must be non-negative");
+  if (!(tau > 0.0f)) return fail(DMS_ERR_ARG, "tau must be positive");
+  if (n == 0) return DMS_OK;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(train_gate_bwd_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
+                     logits, noise, 1.0f / tau, n, dy, dhard, dprobs, dlogits_out);
+  return check_hip(hipGetLastError(), "dms_train_gate_bwd launch");
+}
 
 extern "C" int dms_train_gate(const float* logits, const float* noise, float tau, int64_t n, float* y_out,
                               float* probs_out, float* hard_out, void* stream) {

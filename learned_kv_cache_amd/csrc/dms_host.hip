@@ -334,6 +334,37 @@ int dms_cache_dump(dms_cache* cache, void* stream, const dms_dump* out) {
   return check_hip(hipStreamSynchronize(st), "hipStreamSynchronize");
 }
 
+int dms_cache_check(dms_cache* cache, void* stream, uint32_t* violations, int32_t* first_unit) {
+  if (!cache || !violations) return fail(DMS_ERR_ARG, "NULL argument");
+  const Geo& g = cache->geo;
+  const size_t units = static_cast<size_t>(g.Bmax) * g.Hkv;
+  std::vector<int32_t> len(units), pt(units * g.maxp), meta(static_cast<size_t>(g.pool) * g.P),
+      ring(units * g.w), ring_row(units * g.w), cur(units), pos(g.Bmax), fs(g.pool);
+  int32_t free_count = 0;
+  dms_dump d;
+  std::memset(&d, 0, sizeof(d));
+  d.lengths = len.data();
+  d.page_table = pt.data();
+  d.slot_meta = meta.data();
+  d.ring = ring.data();
+  d.positions = pos.data();
+  d.free_stack = fs.data();
+  d.free_count = &free_count;
+  hipStream_t st = as_stream(stream);
+  int s = check_hip(hipMemcpyAsync(ring_row.data(), cache->dev.ring_row, ring_row.size() * sizeof(int32_t),
+                                   hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+  if (!s) s = check_hip(hipMemcpyAsync(cur.data(), cache->dev.cur_page, cur.size() * sizeof(int32_t),
+                                       hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+  if (!s) s = dms_cache_dump(cache, stream, &d);
+  if (s) return s;
+  const TableView t{g.Bmax, g.Hkv, g.w, g.P, g.maxp, g.pool, len.data(), pt.data(), meta.data(), ring.data(),
+                    ring_row.data(), cur.data(), pos.data(), fs.data(), free_count};
+  int where = -1;
+  *violations = check_tables(t, &where);
+  if (first_unit) *first_unit = where;
+  return DMS_OK;
+}
+
 int dms_cache_stats(dms_cache* cache, void* stream, dms_stats* out) {
   if (!cache || !out) return fail(DMS_ERR_ARG, "NULL argument");
   const Geo& g = cache->geo;

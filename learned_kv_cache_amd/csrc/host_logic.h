@@ -5,8 +5,10 @@
 // address and undefined-behaviour sanitizers.
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "dms.h"
 
@@ -185,6 +187,123 @@ inline int64_t worst_pages_for_seq(int seq, int64_t n, int Hkv, int w, int P, in
     pages += (slots + P - 1) / P - (L + P - 1) / P;
   }
   return pages;
+}
+
+// ---- structural invariants of the cache tables ----------------------------
+// (walkthrough, 推理模式: the delayed-eviction slot rule; the shared pool).  A
+// bit per kind of violation; 0 means consistent.
+constexpr uint32_t kChkLength = 1u << 0;      // L outside [min(pos, w), pos]
+constexpr uint32_t kChkPageId = 1u << 1;      // a held page id outside [0, pool)
+constexpr uint32_t kChkOwnership = 1u << 2;   // a page held twice, held and free, or pages lost
+constexpr uint32_t kChkSlot = 1u << 3;        // a live slot whose occupant is not one visible token
+constexpr uint32_t kChkRing = 1u << 4;        // a window entry that does not name its token's slot
+constexpr uint32_t kChkCurPage = 1u << 5;     // the current page is not the page of slot L - 1
+constexpr uint32_t kChkFreeStack = 1u << 6;   // free count or a free id out of range
+
+struct TableView {
+  int Bmax, Hkv, w, P, maxp, pool;
+  const int32_t* lengths;     // [Bmax][Hkv]
+  const int32_t* page_table;  // [Bmax][Hkv][maxp]
+  const int32_t* slot_meta;   // [pool][P] position | evict << 31
+  const int32_t* ring;        // [Bmax][Hkv][w] slot | evict << 31 of position p at p % w
+  const int32_t* ring_row;    // [Bmax][Hkv][w] page * P + slot % P of that slot
+  const int32_t* cur_page;    // [Bmax][Hkv]
+  const int32_t* pos;         // [Bmax]
+  const int32_t* free_stack;  // [pool]
+  int32_t free_count;
+};
+
+// Checks every sequence's heads: live slots 0..L-1 each hold one distinct
+// token visible to the sequence's last query (kept, or inside the window),
+// the window entries of the last w positions name the slots holding them,
+// the page ids are the pool's, each page has one owner or is free, and no
+// page is lost.  *first_unit gets the first (sequence * Hkv + head) with a
+// slot, ring or page violation, else -1.
+inline uint32_t check_tables(const TableView& t, int* first_unit) {
+  uint32_t bad = 0;
+  *first_unit = -1;
+  auto flag = [&](uint32_t bit, int unit) {
+    bad |= bit;
+    if (*first_unit < 0 && unit >= 0) *first_unit = unit;
+  };
+  if (t.free_count < 0 || t.free_count > t.pool) {
+    flag(kChkFreeStack, -1);
+    return bad;
+  }
+  std::vector<int> owner(static_cast<size_t>(t.pool), -1);
+  int64_t held = 0;
+  for (int i = 0; i < t.free_count; ++i) {
+    const int pg = t.free_stack[i];
+    if (pg < 0 || pg >= t.pool) {
+      flag(kChkFreeStack, -1);
+      continue;
+    }
+    if (owner[pg] != -1) flag(kChkOwnership, -1);
+    owner[pg] = -2;
+  }
+  std::vector<int32_t> seen;
+  for (int seq = 0; seq < t.Bmax; ++seq) {
+    const int32_t T = t.pos[seq];
+    for (int k = 0; k < t.Hkv; ++k) {
+      const int unit = seq * t.Hkv + k;
+      const int32_t L = t.lengths[unit];
+      if (L < 0 || L > T || L < std::min(T, t.w)) {
+        flag(kChkLength, unit);
+        continue;
+      }
+      const int np = static_cast<int>((static_cast<int64_t>(L) + t.P - 1) / t.P);
+      if (np > t.maxp) {
+        flag(kChkLength, unit);
+        continue;
+      }
+      const int32_t* pt = t.page_table + static_cast<size_t>(unit) * t.maxp;
+      bool ids_ok = true;
+      for (int i = 0; i < np; ++i) {
+        const int pg = pt[i];
+        if (pg < 0 || pg >= t.pool) {
+          flag(kChkPageId, unit);
+          ids_ok = false;
+          continue;
+        }
+        if (owner[pg] != -1) flag(kChkOwnership, unit);
+        owner[pg] = unit;
+        ++held;
+      }
+      if (!ids_ok) continue;
+      if (L > 0 && t.cur_page[unit] != pt[(L - 1) / t.P]) flag(kChkCurPage, unit);
+      // live slots: distinct tokens, each visible to the query at T - 1
+      seen.assign(static_cast<size_t>(T > 0 ? T : 1), 0);
+      for (int32_t s = 0; s < L; ++s) {
+        const uint32_t meta = static_cast<uint32_t>(t.slot_meta[static_cast<size_t>(pt[s / t.P]) * t.P + s % t.P]);
+        const int32_t p = static_cast<int32_t>(meta & 0x7FFFFFFFu);
+        const bool marked = (meta >> 31) != 0;
+        if (p >= T || seen[p] || (marked && (T - 1) - p >= t.w)) {
+          flag(kChkSlot, unit);
+          break;
+        }
+        seen[p] = 1;
+      }
+      // the window: position p at p % w names the slot holding p
+      for (int32_t p = std::max(0, T - t.w); p < T; ++p) {
+        const size_t ri = static_cast<size_t>(unit) * t.w + static_cast<size_t>(p % t.w);
+        const uint32_t e = static_cast<uint32_t>(t.ring[ri]);
+        const int32_t s = static_cast<int32_t>(e & 0x7FFFFFFFu);
+        if (s >= L) {
+          flag(kChkRing, unit);
+          break;
+        }
+        const int32_t row = pt[s / t.P] * t.P + s % t.P;
+        const uint32_t meta = static_cast<uint32_t>(t.slot_meta[static_cast<size_t>(row)]);
+        if (static_cast<int32_t>(meta & 0x7FFFFFFFu) != p || (meta >> 31) != (e >> 31) ||
+            (t.ring_row && t.ring_row[ri] != row)) {
+          flag(kChkRing, unit);
+          break;
+        }
+      }
+    }
+  }
+  if (held + t.free_count != t.pool) flag(kChkOwnership, -1);
+  return bad;
 }
 
 }  // namespace dms

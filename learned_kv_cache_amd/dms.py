@@ -45,9 +45,9 @@ EXPORTS = (
     "dms_cache_destroy", "dms_cache_config", "dms_decide", "dms_append_evict", "dms_decode_attn",
     "dms_prefill_attn", "dms_seq_reset", "dms_cache_status", "dms_cache_clear_status",
     "dms_cache_dump", "dms_cache_stats", "dms_last_error", "dms_decode_prepare", "dms_decode_step",
-    "dms_train_gate", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed", "dms_kvzap_score",
-    "dms_kvzap_workspace_bytes", "dms_train_attn_bwd", "dms_train_attn_bwd_workspace_bytes",
-    "dms_decode_workspace_bytes", "dms_decode_attn_noalloc",
+    "dms_train_gate", "dms_train_gate_bwd", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed",
+    "dms_kvzap_score", "dms_kvzap_workspace_bytes", "dms_train_attn_bwd", "dms_train_attn_bwd_workspace_bytes",
+    "dms_decode_workspace_bytes", "dms_decode_attn_noalloc", "dms_cache_check",
 )
 
 
@@ -112,6 +112,8 @@ def lib():
             "dms_decode_prepare": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
             "dms_decode_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
             "dms_train_gate": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp],
+            "dms_train_gate_bwd": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp, vp],
+            "dms_cache_check": [vp, vp, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32)],
             "dms_seq_info_get": [vp, vp, i32, vp, ctypes.POINTER(dms_seq_info)],
             "dms_pages_needed": [vp, vp, vp, i32, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
             "dms_train_attn_fwd": [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp],
@@ -353,6 +355,23 @@ def dms_train_gate(logits, noise, tau: float, y_out=None, probs_out=None, hard_o
         _ptr(logits, "logits", torch.float32), _ptr(noise, "noise", torch.float32, n), ctypes.c_float(tau),
         ctypes.c_int64(n), _ptr(y_out, "y_out", torch.float32, n), _ptr(probs_out, "probs_out", torch.float32, n),
         _ptr(hard_out, "hard_out", torch.float32, n), _stream(stream)))
+
+
+def dms_cache_check(cache: DmsCache, stream=None):
+    """(violation bits, first unit found wrong or -1); bits 0 = consistent."""
+    bits, unit = ctypes.c_uint32(), ctypes.c_int32()
+    _check(lib().dms_cache_check(cache.handle, _stream(stream), ctypes.byref(bits), ctypes.byref(unit)))
+    return int(bits.value), int(unit.value)
+
+
+def dms_train_gate_bwd(logits, noise, tau: float, dlogits_out, dy=None, dhard=None, dprobs=None,
+                       stream=None) -> int:
+    n = logits.numel()
+    return _check(lib().dms_train_gate_bwd(
+        _ptr(logits, "logits", torch.float32), _ptr(noise, "noise", torch.float32, n), ctypes.c_float(tau),
+        ctypes.c_int64(n), _ptr(dy, "dy", torch.float32, n), _ptr(dhard, "dhard", torch.float32, n),
+        _ptr(dprobs, "dprobs", torch.float32, n), _ptr(dlogits_out, "dlogits_out", torch.float32, n),
+        _stream(stream)))
 
 
 def dms_train_attn_fwd(q, k, v, gate_logits, out, lse, *, window: int, softmax_scale: float = 0.0,

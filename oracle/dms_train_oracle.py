@@ -56,6 +56,29 @@ def train_gate(logits: np.ndarray, noise: Optional[np.ndarray], tau: float):
     return y, probs, hard
 
 
+def train_gate_backward(logits: np.ndarray, noise: Optional[np.ndarray], tau: float,
+                        dy: Optional[np.ndarray] = None, dhard: Optional[np.ndarray] = None,
+                        dprobs: Optional[np.ndarray] = None) -> np.ndarray:
+    """Gradient to the decision logits of train_gate (walkthrough, Gumbel
+    噪声与可微门控).  y = (logits + noise) / tau reaches the loss directly (the
+    training attention's penalty, gradient dy), through probs = sigmoid(y)
+    (gradient dprobs) and through the straight-through decision, whose forward
+    value is the hard threshold and whose gradient is that of probs (reading
+    T4; gradient dhard).  So
+        dlogits = (dy + (dhard + dprobs) * probs * (1 - probs)) / tau.
+    A missing gradient is zero.  float64."""
+    y, probs, _ = train_gate(logits, noise, tau)
+    g = np.zeros_like(y)
+    if dy is not None:
+        g = g + np.asarray(dy, dtype=np.float64)
+    via_probs = np.zeros_like(y)
+    if dhard is not None:
+        via_probs = via_probs + np.asarray(dhard, dtype=np.float64)
+    if dprobs is not None:
+        via_probs = via_probs + np.asarray(dprobs, dtype=np.float64)
+    return (g + via_probs * probs * (1.0 - probs)) / float(tau)
+
+
 def _scored(q_rows: np.ndarray, kk: np.ndarray, pen: np.ndarray, rows: np.ndarray, w: int, scale: float) -> np.ndarray:
     """score_mod of the walkthrough's training mode for query positions `rows`
     against all T keys of one (sequence, head): [R, T] float64."""

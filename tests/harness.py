@@ -372,8 +372,10 @@ class Runner:
     # -- tables ------------------------------------------------------------------
     def check_tables(self, pages: bool = False):
         """Lengths, page tables, slot metadata, ring, positions and the free stack
-        must equal the oracle's sequential model bit for bit."""
+        must equal the oracle's sequential model bit for bit; the library's own
+        invariant check (dms_cache_check) must find nothing."""
         wl, sim = self.wl, self.sim
+        assert self.dms.dms_cache_check(self.cache) == (0, -1)
         dump = self.dms.dms_cache_dump(self.cache, pages=pages)
         assert np.array_equal(dump["positions"], np.asarray(sim.pos, np.int32))
         assert np.array_equal(dump["lengths"], np.asarray(sim.L, np.int32))

@@ -59,6 +59,7 @@ assert L.dms_cache_clear_status(None, None) == dms.DMS_ERR_ARG
 assert L.dms_cache_dump(None, None, None) == dms.DMS_ERR_ARG
 assert L.dms_cache_stats(None, None, None) == dms.DMS_ERR_ARG
 assert L.dms_cache_config(None, None) == dms.DMS_ERR_ARG
+assert L.dms_cache_check(None, None, None, None) == dms.DMS_ERR_ARG
 info = dms.dms_seq_info()
 assert L.dms_seq_info_get(None, None, 1, None, ctypes.byref(info)) == dms.DMS_ERR_ARG
 pg, fr = ctypes.c_int64(), ctypes.c_int64()
@@ -77,6 +78,13 @@ assert L.dms_train_attn_bwd(1, 8, 4, 2, 128, 4, f, *t11, a16, ctypes.c_size_t(1)
 assert L.dms_kvzap_score(1, 8, 4016, 8, 512, dms.DMS_BF16, a16, a16, None, a16, None, ctypes.c_float(-4.0), None,
                          a16, a16, ctypes.c_size_t(1 << 20), None) == dms.DMS_ERR_UNSUPPORTED
 assert L.dms_train_gate(None, None, ctypes.c_float(0.1), ctypes.c_int64(4), None, None, None, None) != 0
+assert L.dms_train_gate_bwd(None, None, ctypes.c_float(0.1), ctypes.c_int64(4), None, None, None, a16, None) == \
+    dms.DMS_ERR_ARG
+assert L.dms_train_gate_bwd(a16, None, ctypes.c_float(0.0), ctypes.c_int64(4), None, None, None, a16, None) == \
+    dms.DMS_ERR_ARG
+assert L.dms_train_gate_bwd(a16, None, ctypes.c_float(1.0), ctypes.c_int64(-1), None, None, None, a16, None) == \
+    dms.DMS_ERR_ARG
+assert L.dms_train_gate_bwd(a16, None, ctypes.c_float(1.0), ctypes.c_int64(0), None, None, None, a16, None) == 0
 maps = open("/proc/self/maps").read()
 assert "libdms_san.so" in maps and "/libdms.so" not in maps, "not the sanitizer build"
 print("abi checks ok", flush=True)

@@ -1,8 +1,10 @@
 // Host-side checks of the DMS library's pure C++ logic (host_logic.h), built
 // with the address and undefined-behaviour sanitizers by
 // tests/test_host_sanitizers.py: configuration checks, the cache buffer's
-// layout, statistics and the serving accounting (worst-case pages of a
-// continuation against a brute-force replay of the slot rule).
+// layout, statistics, the serving accounting (worst-case pages of a
+// continuation against a brute-force replay of the slot rule) and the
+// structural invariant check (consistent tables from random histories pass;
+// each planted mistake sets its bit).
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -196,7 +198,152 @@ static void check_worst_pages() {
   }
 }
 
+// A consistent set of cache tables built from random histories (the slot
+// rule applied token by token, pages popped 0, 1, 2, ... from the pool), then
+// one planted mistake per kind of invariant.
+struct Tables {
+  int Bmax = 2, Hkv = 2, w = 5, P = 3, maxp = 0, pool = 64;
+  std::vector<int32_t> len, pt, meta, ring, ring_row, cur, pos, fs;
+  int32_t free_count = 0;
+  TableView view() const {
+    return TableView{Bmax, Hkv, w, P, maxp, pool, len.data(), pt.data(), meta.data(), ring.data(),
+                     ring_row.data(), cur.data(), pos.data(), fs.data(), free_count};
+  }
+};
+
+static Tables build_tables(std::mt19937& rng) {
+  Tables t;
+  const int max_tokens = 40;
+  t.maxp = (max_tokens + t.P - 1) / t.P;
+  const int units = t.Bmax * t.Hkv;
+  t.len.assign(units, 0);
+  t.pt.assign(static_cast<size_t>(units) * t.maxp, -1);
+  t.meta.assign(static_cast<size_t>(t.pool) * t.P, 0);
+  t.ring.assign(static_cast<size_t>(units) * t.w, 0);
+  t.ring_row.assign(static_cast<size_t>(units) * t.w, 0);
+  t.cur.assign(units, -1);
+  t.pos.assign(t.Bmax, 0);
+  int next_page = 0;
+  for (int seq = 0; seq < t.Bmax; ++seq) {
+    const int T = static_cast<int>(rng() % (max_tokens + 1));
+    t.pos[seq] = T;
+    for (int k = 0; k < t.Hkv; ++k) {
+      const int unit = seq * t.Hkv + k;
+      std::vector<int> slot(T), mark(T);
+      int L = 0;
+      for (int p = 0; p < T; ++p) {
+        mark[p] = static_cast<int>(rng() % 2);
+        if (p >= t.w && mark[p - t.w]) {
+          slot[p] = slot[p - t.w];
+        } else {
+          slot[p] = L++;
+          if ((L - 1) % t.P == 0) t.pt[static_cast<size_t>(unit) * t.maxp + (L - 1) / t.P] = next_page++;
+        }
+        const int row = t.pt[static_cast<size_t>(unit) * t.maxp + slot[p] / t.P] * t.P + slot[p] % t.P;
+        t.meta[row] = static_cast<int32_t>(static_cast<uint32_t>(p) | (static_cast<uint32_t>(mark[p]) << 31));
+        t.ring[static_cast<size_t>(unit) * t.w + p % t.w] =
+            static_cast<int32_t>(static_cast<uint32_t>(slot[p]) | (static_cast<uint32_t>(mark[p]) << 31));
+        t.ring_row[static_cast<size_t>(unit) * t.w + p % t.w] = row;
+      }
+      t.len[unit] = L;
+      if (L > 0) t.cur[unit] = t.pt[static_cast<size_t>(unit) * t.maxp + (L - 1) / t.P];
+    }
+  }
+  for (int pg = t.pool - 1; pg >= next_page; --pg) t.fs.push_back(pg);
+  t.free_count = static_cast<int32_t>(t.fs.size());
+  t.fs.resize(t.pool, 0);
+  return t;
+}
+
+static void check_invariants() {
+  std::mt19937 rng(4242);
+  int planted = 0;
+  for (int it = 0; it < 500; ++it) {
+    Tables t = build_tables(rng);
+    int where = 0;
+    CHECK(check_tables(t.view(), &where) == 0 && where == -1);
+    // the longest head, for mistakes that need live slots
+    int u = 0;
+    for (int i = 1; i < t.Bmax * t.Hkv; ++i)
+      if (t.len[i] > t.len[u]) u = i;
+    const int L = t.len[u], T = t.pos[u / t.Hkv];
+    if (L < 2 || T <= t.w) continue;
+    ++planted;
+    int32_t* ptu = t.pt.data() + static_cast<size_t>(u) * t.maxp;
+    {  // a page held twice
+      Tables x = t;
+      int v = u == 0 ? 1 : 0;
+      if (x.len[v] > 0) {
+        x.pt[static_cast<size_t>(v) * x.maxp] = ptu[0];
+        CHECK(check_tables(x.view(), &where) & kChkOwnership);
+      }
+    }
+    {  // a page lost (one fewer free)
+      Tables x = t;
+      if (x.free_count > 0) {
+        x.free_count -= 1;
+        CHECK(check_tables(x.view(), &where) & kChkOwnership);
+      }
+    }
+    {  // a page id outside the pool
+      Tables x = t;
+      x.pt[static_cast<size_t>(u) * x.maxp] = x.pool;
+      CHECK((check_tables(x.view(), &where) & kChkPageId) && where == u);
+    }
+    {  // a live slot holding a token that left the window marked: use the
+       // position of a slot's second occupant minus w (the overwritten one)
+      Tables x = t;
+      bool done = false;
+      for (int s = 0; s < L && !done; ++s) {
+        const int row = ptu[s / x.P] * x.P + s % x.P;
+        const int p = static_cast<int>(static_cast<uint32_t>(x.meta[row]) & 0x7FFFFFFFu);
+        if (p >= x.w) {
+          // position p - w: marked (its slot was reused) or kept elsewhere
+          x.meta[row] = static_cast<int32_t>(static_cast<uint32_t>(p - x.w) | (1u << 31));
+          if ((T - 1) - (p - x.w) >= x.w) {
+            CHECK((check_tables(x.view(), &where) & kChkSlot) && where == u);
+            done = true;
+          } else {
+            x.meta[row] = t.meta[row];
+          }
+        }
+      }
+    }
+    {  // two slots holding the same token
+      Tables x = t;
+      const int r0 = ptu[0] * x.P, r1 = ptu[1 / x.P] * x.P + 1 % x.P;
+      x.meta[r1] = x.meta[r0];
+      CHECK(check_tables(x.view(), &where) & (kChkSlot | kChkRing));
+    }
+    {  // a window entry naming another slot
+      Tables x = t;
+      const size_t ri = static_cast<size_t>(u) * x.w + static_cast<size_t>((T - 1) % x.w);
+      const uint32_t e = static_cast<uint32_t>(x.ring[ri]);
+      const uint32_t s2 = ((e & 0x7FFFFFFFu) + 1) % static_cast<uint32_t>(L);
+      x.ring[ri] = static_cast<int32_t>(s2 | (e & 0x80000000u));
+      CHECK((check_tables(x.view(), &where) & kChkRing) && where == u);
+    }
+    {  // a wrong current page
+      Tables x = t;
+      x.cur[u] = x.pool + 5;
+      CHECK((check_tables(x.view(), &where) & kChkCurPage) && where == u);
+    }
+    {  // a length past the position
+      Tables x = t;
+      x.len[u] = T + 1;
+      CHECK(check_tables(x.view(), &where) & kChkLength);
+    }
+    {  // a bad free count
+      Tables x = t;
+      x.free_count = x.pool + 1;
+      CHECK(check_tables(x.view(), &where) & kChkFreeStack);
+    }
+  }
+  CHECK(planted > 100);
+}
+
 int main() {
+  check_invariants();
   check_config();
   check_layout();
   check_stats_and_info();

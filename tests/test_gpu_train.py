@@ -131,6 +131,34 @@ def test_train_gate():
     assert np.array_equal(from_dev(y), logits.astype(np.float64))
 
 
+def test_train_gate_bwd():
+    """dms_train_gate_bwd against the oracle's chain rule (pinned on the CPU by
+    central differences and by torch autograd through the straight-through
+    construct), every combination of present and missing gradients."""
+    torch = _torch()
+    from learned_kv_cache_amd import dms
+    gen = np.random.default_rng(803)
+    n = 100_003
+    logits = gen.normal(0.0, 3.0, n).astype(np.float32)
+    noise = gen.logistic(0.0, 1.0, n).astype(np.float32)
+    grads = {k: gen.standard_normal(n).astype(np.float32) for k in ("dy", "dhard", "dprobs")}
+    ld, nd = to_dev(logits, "f32"), to_dev(noise, "f32")
+    gd = {k: to_dev(v, "f32") for k, v in grads.items()}
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    for tau in (0.1, 1.0):
+        for mask in range(8):
+            use = {k: bool(mask >> i & 1) for i, k in enumerate(("dy", "dhard", "dprobs"))}
+            for with_noise in (True, False):
+                dms.dms_train_gate_bwd(ld, nd if with_noise else None, tau, out,
+                                       **{k: (gd[k] if use[k] else None) for k in use})
+                ref = tor.train_gate_backward(logits.astype(np.float64),
+                                              noise.astype(np.float64) if with_noise else None, tau,
+                                              **{k: (grads[k].astype(np.float64) if use[k] else None) for k in use})
+                got = from_dev(out)
+                scale = max(1.0, float(np.abs(ref).max()))
+                np.testing.assert_allclose(got, ref, rtol=1e-5, atol=2e-6 * scale)
+
+
 # ---------------------------------------------------------------------------
 # backward
 

@@ -3,6 +3,10 @@
 * logsigmoid     -> the direct formula log(1 / (1 + e^-x)) where it is exact
                     enough, log(0.5) at 0, and the two asymptotes
 * train_gate     -> torch.sigmoid; the forward decision is [logit + noise > 0]
+* train_gate_backward -> central differences of train_gate's y and probs
+                    (the dy and dprobs paths); torch autograd through the
+                    straight-through construct hard - probs.detach() + probs
+                    built with torch ops (the dhard path)
 * train_attention:
     - every key kept (gate logits -> -inf: penalty 0)       -> torch SDPA causal
     - every key evicted (gate logits -> +inf: no weight past the window)
@@ -60,6 +64,43 @@ def test_train_gate_matches_torch_sigmoid_and_threshold():
         assert np.array_equal(hard, (logits + noise > 0).astype(np.float64))
     y0, _, h0 = tor.train_gate(logits, None, 0.5)
     assert np.array_equal(h0, (logits > 0).astype(np.float64))
+
+
+def test_gate_backward_matches_central_differences():
+    n = 400
+    logits = RNG.normal(0, 2, n)
+    noise = RNG.logistic(0, 1, n)
+    dy = RNG.standard_normal(n)
+    dprobs = RNG.standard_normal(n)
+    for tau in (0.25, 1.0, 3.0):
+        got = tor.train_gate_backward(logits, noise, tau, dy=dy, dprobs=dprobs)
+        # L(logits) = sum(dy * y + dprobs * probs), elementwise in the logits
+        h = 1e-6
+
+        def loss_terms(lg):
+            y, p, _ = tor.train_gate(lg, noise, tau)
+            return dy * y + dprobs * p
+        fd = (loss_terms(logits + h) - loss_terms(logits - h)) / (2 * h)
+        np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-8)
+    assert np.array_equal(tor.train_gate_backward(logits, noise, 1.0), np.zeros(n))
+
+
+def test_gate_backward_straight_through_matches_torch_autograd():
+    n = 300
+    logits = RNG.normal(0, 2, n)
+    noise = RNG.logistic(0, 1, n)
+    dhard = RNG.standard_normal(n)
+    dy = RNG.standard_normal(n)
+    for tau in (0.5, 2.0):
+        t = torch.tensor(logits, dtype=torch.float64, requires_grad=True)
+        y = (t + torch.from_numpy(noise)) / tau
+        probs = torch.sigmoid(y)
+        hard = (probs > 0.5).to(probs.dtype) - probs.detach() + probs
+        (torch.from_numpy(dhard) * hard + torch.from_numpy(dy) * y).sum().backward()
+        got = tor.train_gate_backward(logits, noise, tau, dy=dy, dhard=dhard)
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-12, atol=1e-15)
+        # the construct's forward value is the hard decision
+        assert np.array_equal(hard.detach().numpy(), tor.train_gate(logits, noise, tau)[2])
 
 
 def _inputs(B, T, Hq, Hkv, D):
