@@ -932,9 +932,13 @@ __device__ __forceinline__ int unit_slots(const DecodeArgs& a, int u, int wg, in
   return L;
 }
 
+// Tiles in flight per wave in the matrix-core decode (a ring of buffers); 3
+// or 4 also fit two waves per SIMD (221, 254 registers) but measured slower.
+constexpr int kMfTiles = 2;
+
 // One wave's share of a segment (rows [lo, hi) of unit (row, kh)) on the
 // matrix cores: the wave takes tiles wave, wave + 4, ... of each page block,
-// keeps NB = 2 tiles in flight, and leaves its (m, l, o) in entry 0 of the
+// keeps kMfTiles tiles in flight, and leaves its (m, l, o) in entry 0 of the
 // workgroup's LDS rows (m, l of head h from lane h, o from the lanes of row
 // group 0).
 template <int D, int G, bool STEP>
@@ -980,23 +984,24 @@ __device__ __forceinline__ void mf_segment(const DecodeArgs& a, const StepArgs* 
     const int nt = (bhi - t0 + 15) >> 4;
     // loads one tile ahead, unconditionally (past the block's end they reread
     // its last tile), in written order (see the lane-per-row-piece kernel)
-    MfTile<D> ta, tb;
+    constexpr int NB = kMfTiles;
+    MfTile<D> ring[NB];
     auto load = [&](MfTile<D>& b, int t) {
       mf_load<D, STEP>(b, t, nt, t0, pb, pt_reg, d.k_pages, d.v_pages, hi, psh, pmask, vrow, kin0, vin0, lane);
     };
     auto compute = [&](const MfTile<D>& b, int t) {
       mf_compute<D, G, STEP>(b, t, t0, lo, hi, skip, g.scale_log2, qb, m, lsum, o, lane);
     };
-    load(ta, wave);
-    for (int t = wave; t < nt; t += 8) {
-      __builtin_amdgcn_sched_barrier(0);
-      load(tb, t + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(ta, t);
-      __builtin_amdgcn_sched_barrier(0);
-      load(ta, t + 8);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + 4 < nt) compute(tb, t + 4);
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) load(ring[k], wave + 4 * k);
+    for (int t = wave; t < nt; t += 4 * NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(ring[(k + NB - 1) % NB], t + 4 * (k + NB - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 4 * k < nt) compute(ring[k], t + 4 * k);
+      }
     }
   }
   // sums over the row groups (and, D = 64, the two rows of a group)
@@ -1666,7 +1671,7 @@ __device__ __forceinline__ void decode_attn_fast_body(const DecodeArgs& a, const
 
 
 template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 3 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 2 : 1)))
 void decode_attn_fast_kernel(DecodeArgs a) {
   __shared__ FastLds<G, D, false> lds;
   decode_attn_fast_body<D, G, NP, FP8, LPR, false, MF>(a, nullptr, blockIdx.x, gridDim.x, lds);
@@ -1809,11 +1814,12 @@ __device__ void plan_build(const DecodeArgs& a, const StepArgs& sa, FastLds<G, D
 // (row, KV head) pair each (decision, placement, plan record); the others run
 // the attention (STEP).  The last pair to finish waits until every attention
 // workgroup has arrived (read the tables it works from), then commits.
-// (the matrix-core variant for groups of up to 4 heads is held to 3 waves per
-// SIMD: the one-launch step needs its prepare and attention workgroups
-// resident together)
+// (the matrix-core variant for groups of up to 4 heads is built for 2 waves
+// per SIMD, i.e. two workgroups per CU: the one-launch step needs its prepare
+// and attention workgroups resident together, and the launch shape asks for
+// exactly two per CU; at 3 the register cap leaves one tile fewer in flight)
 template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 3 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 2 : 1)))
 void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
   constexpr int KV = FP8 ? DMS_FP8_E4M3 : DMS_BF16;
   __shared__ FastLds<G, D, true> lds;
