@@ -17,6 +17,7 @@
 //    softmax statistics of a column never leave its lane.
 //  * prefill_attn_generic_kernel: vector ALU, every dtype and head size.
 #include <cmath>
+#include <cstdlib>
 
 #include "dms_internal.h"
 
@@ -736,12 +737,491 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_mfma_kernel(PrefillAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined matrix-core kernel (bf16 pages and the training forward).
+//
+// Same workgroup shape, operand layouts and LDS row swizzle as the kernel
+// above; the work per key block is reordered so that both the matrix cores
+// and the vector ALU stay busy inside every wave:
+//  * K and V of a block live in separate LDS rings of four buffers.  Step j
+//    issues the direct global->LDS loads of K for block j+4 and V for block
+//    j+3, and waits only for the loads issued two steps earlier, so every
+//    load has two steps to land.
+//  * Step j computes S of block j+1 (K from LDS) while the same wave turns
+//    the scores of block j into probabilities (exp2), then P.V of block j
+//    while it takes the maxima of block j+1; the running maximum is raised
+//    after P.V (lazily, as above).
+//  * Visibility enters the score product as its accumulator's initial value:
+//    0 for a visible key, -inf for a hidden one (training: the key's
+//    penalty once the query is w or more positions past it).  A block whose
+//    keys are all visible to every query of the workgroup (the common case
+//    for cached keys) starts from 0 without any per-key test; the lane that
+//    stages the block's intervals decides that with one ballot.
+// The ring buffers are separate arrays and the block loop is unrolled by
+// four, so each step's buffers are static and the compiler can tell that
+// the loads in flight do not alias the LDS reads of the step.
+constexpr int kPpRing = 4;
+
+template <int D, int G, bool TRAIN>
+struct PpShape {
+  using S = PfShape<D, G, false>;
+  static constexpr int KROWS = kPfKB * S::ROW;
+  static constexpr int META = KROWS;            // 32 ints: slot metadata (cache keys)
+  static constexpr int LO = META + 4 * kPfKB;   // 32 ints
+  static constexpr int HI = LO + 4 * kPfKB;     // 32 ints
+  static constexpr int PEN = HI + 4 * kPfKB;    // 32 floats (training: gate logit, then penalty / scale)
+  static constexpr int FLAG = PEN + 4 * kPfKB;  // 1 int: 1 every key visible to the whole block of queries,
+                                                //        2 (training) every key penalised for all of them
+  static constexpr int KBUF = FLAG + 16;
+  static constexpr int VBUF = KROWS;
+};
+
+template <int D, int G, bool TRAIN>
+__global__ __launch_bounds__(kPfThreads) void prefill_attn_pipe_kernel(PrefillArgs a) {
+  using S = PfShape<D, G, false>;
+  using P = PpShape<D, G, TRAIN>;
+  constexpr int TG = S::TG, NT = S::NT, HW = S::HW, KS = S::KS, DT = S::DT;
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[P::KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[P::KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t kb2[P::KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t kb3[P::KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t vb0[P::VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t vb1[P::VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t vb2[P::VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t vb3[P::VBUF];
+  __shared__ int s_pt[TRAIN ? 1 : kPfMaxPages];
+  __shared__ uint8_t s_ev[TRAIN ? 1 : kMaxChunk];
+  const DevCache& d = a.d;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, G4 = lane >> 4;
+
+  // workgroup -> (pair, token block): heaviest token blocks first
+  const int npairs = a.B * g.Hkv;
+  const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
+  const int pair = blockIdx.x % npairs;
+  const int tb = ntb - 1 - static_cast<int>(blockIdx.x) / npairs;
+  const int row = pair / g.Hkv, kh = pair % g.Hkv;
+  const int seq = (a.seq_ids && !TRAIN) ? a.seq_ids[row] : row;
+  if (!TRAIN && (seq < 0 || seq >= g.Bmax)) {
+    if (tid == 0 && tb == 0 && kh == 0) set_status(d.ctl, DMS_DEV_BAD_SEQ);
+    return;
+  }
+  const int unit = seq * g.Hkv + kh;
+  const int L = TRAIN ? 0 : d.lengths[unit];
+  const int s0 = TRAIN ? 0 : d.pos[seq];
+  const int tok0 = tb * S::TOKB;
+  const int tok_end = min(tok0 + S::TOKB, a.C);
+  const int nk = L + tok_end;
+  const int nblk = (nk + kPfKB - 1) / kPfKB;
+  const int64_t stride = static_cast<int64_t>(g.Hkv) * D * 2;   // bytes between chunk keys
+  const size_t chunk0 = (static_cast<size_t>(row) * a.C * g.Hkv + kh) * D * 2;
+  const uint8_t* kchunk = static_cast<const uint8_t*>(a.k) + chunk0;
+  const uint8_t* vchunk = static_cast<const uint8_t*>(a.v) + chunk0;
+  const float* gate = TRAIN ? a.gate + static_cast<int64_t>(pair) * a.C : nullptr;
+  // query positions of the whole workgroup (the all-visible test)
+  const int qlo_wg = s0 + tok0, qhi_wg = s0 + tok_end - 1;
+
+  // ---- this wave's query columns
+  const int hp = wave % S::HS, tp = wave / S::HS;
+  const int wtok = tok0 + tp * S::TOKW;
+  const int head0 = kh * G + hp * HW;
+  int qpos[TG];
+  bool qok[TG];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    const int t = wtok + tg * 16 + l16;
+    qok[tg] = t < a.C;
+    qpos[tg] = qok[tg] ? s0 + t : -1;
+  }
+  pf_bf16x8 qf[NT][KS];
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      const int c = tg * HW + h;
+      const int t = wtok + tg * 16 + l16;
+      const size_t qrow = ((static_cast<size_t>(row) * a.C + t) * g.Hq + head0 + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (qok[tg]) w = *reinterpret_cast<const uint4*>(qbase + qrow + 32 * ks + 8 * G4);
+        qf[c][ks] = __builtin_bit_cast(pf_bf16x8, w);
+      }
+    }
+  }
+
+  pf_f32x4 o[NT][DT], lacc[NT];
+  float m[NT], mb[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    m[c] = -INFINITY;
+    mb[c] = 0.0f;
+    lacc[c] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[c][dt] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const float cs = g.scale_log2;
+  const pf_bf16x8 ones = __builtin_bit_cast(pf_bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+  if constexpr (!TRAIN) {
+    const int npages = (L + g.P - 1) >> g.Pshift;   // <= kPfMaxPages (checked at launch)
+    const int32_t* pt = d.page_table + static_cast<int64_t>(unit) * g.maxp;
+    const uint8_t* ev = a.evict + static_cast<int64_t>(pair) * a.C;
+    for (int i = tid; i < npages; i += kPfThreads) s_pt[i] = pt[i];
+    for (int i = tid; i < tok_end; i += kPfThreads) s_ev[i] = ev[i];
+  }
+  __syncthreads();
+
+  // ---- direct global->LDS loads of one tensor (K or V) of one key block.
+  // D = 128: every wave loads 4 rows of K and 4 rows of V; D = 64: waves
+  // 0-3 load K (8 rows each), waves 4-7 V.  Lane i writes bytes
+  // [16 i, 16 i + 16) of the wave's 1 KB stretch: row rl, the chunk that the
+  // row's swizzle places there.  Rows past the keys read the last key's row.
+  constexpr int RPW = 1024 / S::ROW;
+  constexpr int RB = 2 * D;
+  const int rl = (D == 128 ? wave : (wave & 3)) * RPW + lane / S::CPR;
+  const int cl = (lane % S::CPR) ^ S::swz(rl);
+  const int loff = (D == 128 ? wave : (wave & 3)) * 1024;
+  const uint32_t off_page = static_cast<uint32_t>(rl * RB + 16 * cl);
+  const uint32_t off_chunk = static_cast<uint32_t>(rl * stride + 16 * cl);
+  const bool vis_wave = wave == kPfWaves - 1;
+  auto block_page = [&](int kb) { return (!TRAIN && kb < L) ? s_pt[kb >> g.Pshift] : 0; };
+  auto dma_rows = [&](int blk, bool v, uint8_t* buf) {
+    const int kb = blk * kPfKB;
+    const uint8_t* pages = v ? d.v_pages : d.k_pages;
+    const uint8_t* chunk = v ? vchunk : kchunk;
+    const uint8_t* src;
+    if (!TRAIN && kb + kPfKB <= L) {
+      const uint8_t* base = pages + ((static_cast<int64_t>(block_page(kb)) << g.Pshift) + (kb & (g.P - 1))) * RB;
+      src = base + off_page;
+    } else if (kb >= L && kb + kPfKB <= nk) {
+      src = chunk + static_cast<int64_t>(kb - L) * stride + off_chunk;
+    } else {
+      const int kc = min(kb + rl, nk - 1);
+      if (!TRAIN && kc < L)
+        src = pages + ((static_cast<int64_t>(block_page(kb)) << g.Pshift) + (kc & (g.P - 1))) * RB + 16 * cl;
+      else
+        src = chunk + static_cast<int64_t>(kc - L) * stride + 16 * cl;
+    }
+    __builtin_amdgcn_global_load_lds((const pf_glb_void*)src, (pf_lds_void*)(buf + loff), 16, 0, 0);
+  };
+  // the staging wave's extra load per block: slot metadata (cache keys) or
+  // the gate logits (training); one load per block in either case, so every
+  // wave issues a fixed number of loads per step
+  auto dma_meta = [&](int blk, uint8_t* kbuf) {
+    if (vis_wave && lane < kPfKB) {
+      const int kb = blk * kPfKB;
+      if constexpr (TRAIN) {
+        __builtin_amdgcn_global_load_lds((const pf_glb_void*)(gate + min(kb + lane, nk - 1)),
+                                         (pf_lds_void*)(kbuf + P::PEN), 4, 0, 0);
+      } else {
+        const int kc = min(kb + lane, L - 1);
+        const int64_t mi = kb < L ? (static_cast<int64_t>(block_page(kb)) << g.Pshift) + (kc & (g.P - 1)) : 0;
+        __builtin_amdgcn_global_load_lds((const pf_glb_void*)(d.slot_meta + mi), (pf_lds_void*)(kbuf + P::META), 4,
+                                         0, 0);
+      }
+    }
+  };
+  auto issue_k = [&](int blk, uint8_t* kbuf) {
+    if (D == 128 || wave < 4) dma_rows(blk, false, kbuf);
+    dma_meta(blk, kbuf);
+  };
+  auto issue_v = [&](int blk, uint8_t* vbuf) {
+    if (D == 128 || wave >= 4) dma_rows(blk, true, vbuf);
+  };
+  // loads one step issues per wave
+  constexpr int LD_STEP = D == 128 ? 2 : 1;
+  auto wait_two_steps_back = [&]() {
+    // the loads of the two latest steps may stay in flight
+    if (vis_wave) {
+      if constexpr (D == 128) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      if constexpr (D == 128) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    }
+  };
+  static_assert(LD_STEP == (D == 128 ? 2 : 1), "load count");
+
+  // A workgroup barrier that orders LDS only: __syncthreads() would also
+  // wait for every global->LDS load in flight (its fence covers global
+  // memory), which the ring leaves in flight on purpose; the loads a step
+  // needs are waited for explicitly (wait_two_steps_back) before it.
+  auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // ---- visibility intervals [lo, hi) of a landed block's keys and the
+  // block flag (staging wave, lanes 0..31)
+  auto vis_write = [&](int blk, uint8_t* kbuf) {
+    if (vis_wave) {
+      const int kk = blk * kPfKB + (lane & 31);
+      int lo, hi;
+      if constexpr (TRAIN) {
+        float* pen = reinterpret_cast<float*>(kbuf + P::PEN);
+        float pv = 0.0f;
+        if (kk < nk) {
+          lo = kk;
+          hi = kk + g.w;
+          const float y = lane < kPfKB ? pen[lane] : 0.0f;
+          // logsigmoid(-y) = -softplus(y), stable for either sign
+          const float ls = -(fmaxf(y, 0.0f) + log1pf(__expf(-fabsf(y))));
+          pv = ls * (1.4426950408889634f / g.scale_log2);
+        } else {
+          lo = kPfNoLimit;
+          hi = 0;
+        }
+        if (lane < kPfKB) pen[lane] = pv;
+      } else {
+        const int meta = lane < kPfKB ? reinterpret_cast<const int*>(kbuf + P::META)[lane] : 0;
+        if (kk < L) {
+          lo = meta & 0x7FFFFFFF;
+          hi = meta < 0 ? lo + g.w : kPfNoLimit;
+        } else if (kk < nk) {
+          lo = s0 + (kk - L);
+          hi = s_ev[kk - L] ? lo + g.w : kPfNoLimit;
+        } else {
+          lo = kPfNoLimit;
+          hi = 0;
+        }
+      }
+      const uint64_t half = 0xFFFFFFFFull;
+      const bool all_vis = lo <= qlo_wg && hi > qhi_wg;
+      const bool all_pen = TRAIN && lo <= qlo_wg && hi <= qlo_wg;
+      const uint64_t bv = __builtin_amdgcn_ballot_w64(all_vis) & half;
+      const uint64_t bp = __builtin_amdgcn_ballot_w64(all_pen) & half;
+      if (lane < kPfKB) {
+        reinterpret_cast<int*>(kbuf + P::LO)[lane] = lo;
+        reinterpret_cast<int*>(kbuf + P::HI)[lane] = hi;
+      }
+      if (lane == 0) *reinterpret_cast<int*>(kbuf + P::FLAG) = bv == half ? 1 : (bp == half ? 2 : 0);
+    }
+  };
+
+  // ---- the score accumulators' initial values for a block: lane (G4, l16)
+  // holds keys 4 G4 + i (kt 0) and 16 + 4 G4 + i (kt 1)
+  auto bias_of = [&](const uint8_t* kbuf, pf_f32x4 (&bias)[TG][2]) {
+    const int flag = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(kbuf + P::FLAG));
+    if (flag == 1) {
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) bias[tg][0] = bias[tg][1] = pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      return;
+    }
+    pf_f32x4 pen[2] = {pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pf_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+    if constexpr (TRAIN) {
+      pen[0] = *reinterpret_cast<const pf_f32x4*>(kbuf + P::PEN + 16 * G4);
+      pen[1] = *reinterpret_cast<const pf_f32x4*>(kbuf + P::PEN + 64 + 16 * G4);
+      if (flag == 2) {
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          bias[tg][0] = pen[0];
+          bias[tg][1] = pen[1];
+        }
+        return;
+      }
+    }
+    const int4 lo0 = *reinterpret_cast<const int4*>(kbuf + P::LO + 16 * G4);
+    const int4 lo1 = *reinterpret_cast<const int4*>(kbuf + P::LO + 64 + 16 * G4);
+    const int4 hi0 = *reinterpret_cast<const int4*>(kbuf + P::HI + 16 * G4);
+    const int4 hi1 = *reinterpret_cast<const int4*>(kbuf + P::HI + 64 + 16 * G4);
+    const int los[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
+    const int his[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      const int qp = qpos[tg];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float b;
+        if constexpr (TRAIN) b = los[e] <= qp ? (qp >= his[e] ? pen[e >> 2][e & 3] : 0.0f) : -INFINITY;
+        else b = (los[e] <= qp && qp < his[e]) ? 0.0f : -INFINITY;
+        bias[tg][e >> 2][e & 3] = b;
+      }
+    }
+  };
+
+  // S^T = K Q^T of one block from its bias
+  auto scores = [&](const uint8_t* kbuf, const pf_f32x4 (&bias)[TG][2], pf_f32x4 (&s)[2][NT]) {
+    pf_bf16x8 kf[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        kf[ks][kt] = *reinterpret_cast<const pf_bf16x8*>(kbuf + S::off(16 * kt + l16, 4 * ks + G4));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+          s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][kt], qf[c][ks], ks == 0 ? bias[c / HW][kt] : s[kt][c],
+                                                             0, 0, 0);
+  };
+  // block maxima; true where the running maximum must be raised
+  auto maxima = [&](const pf_f32x4 (&s)[2][NT], float (&mx)[NT]) {
+    bool need = false;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      float x = fmaxf(fmaxf(fmaxf(s[0][c][0], s[0][c][1]), fmaxf(s[0][c][2], s[0][c][3])),
+                      fmaxf(fmaxf(s[1][c][0], s[1][c][1]), fmaxf(s[1][c][2], s[1][c][3])));
+      x = pf_max_x32(x);
+      x = pf_max_x16(x);
+      mx[c] = x;
+      need |= x * cs > m[c] * cs + kPfRescaleLog2;
+    }
+    return need;
+  };
+  auto raise = [&](const float (&mx)[NT]) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      if (mx[c] * cs > m[c] * cs + kPfRescaleLog2) {
+        const float alpha = __builtin_amdgcn_exp2f((m[c] - mx[c]) * cs);   // 0 from -inf
+        m[c] = mx[c];
+        mb[c] = mx[c] * cs;
+        lacc[c] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[c][dt] *= alpha;
+      }
+    }
+  };
+  // probabilities of a block (bf16, the second product's operand) and the
+  // denominator
+  auto probs = [&](const pf_f32x4 (&s)[2][NT], pf_bf16x8 (&pk)[NT]) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][c][e & 3], cs, -mb[c]));
+      const uint4 w = make_uint4(pf_pack(p[0], p[1]), pf_pack(p[2], p[3]), pf_pack(p[4], p[5]), pf_pack(p[6], p[7]));
+      pk[c] = __builtin_bit_cast(pf_bf16x8, w);
+      lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[c], lacc[c], 0, 0, 0);
+    }
+  };
+  // O^T += V^T P^T of a block
+  auto pv = [&](const uint8_t* vbuf, const pf_bf16x8 (&pk)[NT]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int r0 = 4 * G4 + (l16 >> 2), ch = 2 * dt + ((l16 & 3) >> 1), half = 8 * (l16 & 1);
+      const pf_i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vbuf + S::off(r0, ch) + half));
+      const pf_i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_i16x4*)(vbuf + S::off(r0 + 16, ch) + half));
+      const pf_bf16x8 vf = __builtin_bit_cast(pf_bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int c = 0; c < NT; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[c], o[c][dt], 0, 0, 0);
+    }
+  };
+
+  // ---- prologue: K 0, K 1, V 0 landed with their intervals, S of block 0
+  // and its maxima; then the loads of the two steps before step 0
+  issue_k(0, kb0);
+  issue_v(0, vb0);
+  issue_k(1, kb1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vis_write(0, kb0);
+  vis_write(1, kb1);
+  __syncthreads();
+  issue_k(2, kb2);
+  issue_v(1, vb1);
+  issue_k(3, kb3);
+  issue_v(2, vb2);
+  pf_f32x4 sa[2][NT], sb[2][NT];
+  {
+    pf_f32x4 bias[TG][2];
+    bias_of(kb0, bias);
+    scores(kb0, bias, sa);
+    float mx[NT];
+    if (__any(maxima(sa, mx))) raise(mx);
+  }
+  __syncthreads();   // kb0 is step 0's load target
+
+  // step j: loads of K j+4 into K j's buffer and V j+3 into V j-1's; S of
+  // block j+1 beside the probabilities of block j; P.V of block j beside the
+  // maxima of block j+1; the running maximum; then the loads of two steps
+  // back, block j+2's intervals, and the barrier
+  auto step = [&](int j, uint8_t* ku, uint8_t* kd, uint8_t* kl, uint8_t* vu, uint8_t* vd, pf_f32x4 (&sc)[2][NT],
+                  pf_f32x4 (&sn)[2][NT]) {
+    issue_k(j + 4, kd);
+    issue_v(j + 3, vd);
+    pf_f32x4 bias[TG][2];
+    bias_of(ku, bias);
+    pf_bf16x8 pk[NT];
+    float mx[NT];
+    scores(ku, bias, sn);
+    probs(sc, pk);
+    pv(vu, pk);
+    const bool need = maxima(sn, mx);
+    // the K fragment reads, the score products (each beside exp2 /
+    // conversion work), the V fragment reads (into the K fragments'
+    // registers), the denominators, then P.V beside the maxima
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS * NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NT + DT * NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__any(need)) raise(mx);
+    wait_two_steps_back();
+    vis_write(j + 2, kl);
+    lds_barrier();
+  };
+  for (int j = 0; j < nblk; j += 4) {
+    step(j, kb1, kb0, kb2, vb0, vb3, sa, sb);
+    if (j + 1 >= nblk) break;
+    step(j + 1, kb2, kb1, kb3, vb1, vb0, sb, sa);
+    if (j + 2 >= nblk) break;
+    step(j + 2, kb3, kb2, kb0, vb2, vb1, sa, sb);
+    if (j + 3 >= nblk) break;
+    step(j + 3, kb0, kb3, kb1, vb3, vb2, sb, sa);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load outlives the workgroup
+
+  // ---- normalise and store
+  uint16_t* obase = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    if (!qok[tg]) continue;
+    const int t = wtok + tg * 16 + l16;
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      const int c = tg * HW + h;
+      const float inv = 1.0f / lacc[c][0];
+      if (TRAIN && G4 == 0)
+        a.lse[(static_cast<size_t>(row) * g.Hq + head0 + h) * a.C + t] = (mb[c] + __log2f(lacc[c][0])) * 0.6931471805599453f;
+      uint16_t* orow = obase + ((static_cast<size_t>(row) * a.C + t) * g.Hq + head0 + h) * D + 4 * G4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const pf_f32x4 v = o[c][dt];
+        *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pf_pack(v[0] * inv, v[1] * inv), pf_pack(v[2] * inv, v[3] * inv));
+      }
+    }
+  }
+}
+
+// DMS_PREFILL_PIPE=0 keeps bf16 pages and the training forward on the
+// kernel without the software pipeline.
+static bool pf_pipe_enabled() {
+  const char* e = std::getenv("DMS_PREFILL_PIPE");
+  return !e || std::atoi(e) != 0;
+}
+
 template <int D, int G, bool FP8>
 static int launch_mfma_dgf(const PrefillArgs& a, hipStream_t st) {
   using S = PfShape<D, G, FP8>;
   const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
   const dim3 grid(ntb * a.B * a.g.Hkv), block(kPfThreads);
-  hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, FP8>), grid, block, 0, st, a);
+  if (!FP8 && pf_pipe_enabled())
+    hipLaunchKernelGGL((prefill_attn_pipe_kernel<D, G, false>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, FP8>), grid, block, 0, st, a);
   return DMS_OK;
 }
 
@@ -770,8 +1250,11 @@ template <int D, int G>
 static void launch_train_dg(const PrefillArgs& a, hipStream_t st) {
   using S = PfShape<D, G, false>;
   const int ntb = (a.C + S::TOKB - 1) / S::TOKB;
-  hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, false, true>), dim3(ntb * a.B * a.g.Hkv), dim3(kPfThreads), 0, st,
-                     a);
+  if (pf_pipe_enabled())
+    hipLaunchKernelGGL((prefill_attn_pipe_kernel<D, G, true>), dim3(ntb * a.B * a.g.Hkv), dim3(kPfThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_mfma_kernel<D, G, false, true>), dim3(ntb * a.B * a.g.Hkv), dim3(kPfThreads), 0,
+                       st, a);
 }
 
 template <int D>
