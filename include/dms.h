@@ -282,6 +282,60 @@ int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const void* hidden
                     const void* v, void* out, int B, float* logits_out, uint8_t* evict_out, void* workspace,
                     size_t ws_bytes, void* stream);
 
+/*
+ * The decode step of every layer of a model in one launch (the FastDMS post's
+ * subsystem table, Decode kernel row: keep/evict, the retention window and
+ * the compact append at every decode step, here for all layers at once).
+ *
+ * dms_step_layers_create binds n_layers (1..512) distinct caches of one shape
+ * (head counts, head_dim, window, block size, kv dtype, decision source,
+ * max_batch and device) and, per layer, the device buffers of its step,
+ * io[l], with the meaning, layout and dtype of the same-named arguments of
+ * dms_decode_step.  The pointers are copied: the buffers must stay valid, and
+ * each call reads and writes them (the serving-loop pattern of static
+ * per-layer buffers).  Allocates a small device buffer (the per-layer
+ * arguments and a barrier counter) on the caches' device, which must be
+ * current.  *out receives the binding.  DMS_ERR_ARG for NULL, duplicate or
+ * mismatched caches and missing buffers.
+ *
+ * dms_step_layers_run runs one decode step of rows seq_ids[0..B) through
+ * layers 0, 1, ..., n_layers - 1 in order; results equal n_layers
+ * dms_decode_step calls in that order, up to the order of the attention's
+ * floating-point sums.  When the one-launch step applies (as in
+ * dms_decode_step: fast decode shapes, 16-byte aligned buffers) and all of a
+ * layer's workgroups can be resident at once, it is one launch: each layer's
+ * step as in dms_decode_step, and a grid-wide barrier after each layer's
+ * attention, so that no workgroup starts layer l + 1 before every output of
+ * layer l is written (a model computes layer l + 1's inputs from them).
+ * Otherwise it makes the n_layers dms_decode_step calls.  workspace / ws_bytes
+ * as in dms_decode_attn (one workspace serves all layers).  Calls on one
+ * binding are ordered by their stream and must not overlap.  Device-side
+ * errors as in dms_decode_step (per layer's cache); DMS_DEV_STEP_SYNC also
+ * when the barrier's bounded wait ran out (DMS_STEP_SPIN_LIMIT as there).
+ *
+ * dms_step_layers_one_launch tells (*one_launch = 1) whether a run of B rows
+ * is one launch.  dms_step_layers_destroy frees a binding (NULL is a no-op).
+ */
+typedef struct dms_step_layers dms_step_layers;
+typedef struct dms_layer_io {
+  const void* hidden;      /* [B][hidden] act dtype (LINEAR), else NULL */
+  const float* rms_gamma;  /* [hidden] (LINEAR) */
+  const float* W;          /* [Hkv][hidden] (LINEAR) */
+  const float* bias;       /* [Hkv] or NULL */
+  const float* offsets;    /* decision offsets, as in dms_decode_prepare */
+  void* q_inout;           /* [B][Hq][D] act dtype */
+  const void* k;           /* [B][Hkv][D] act dtype */
+  const void* v;           /* [B][Hkv][D] act dtype */
+  void* out;               /* [B][Hq][D] act dtype */
+  float* logits_out;       /* [B][Hkv] or NULL */
+  uint8_t* evict_out;      /* [B][Hkv] */
+} dms_layer_io;
+int dms_step_layers_create(dms_cache* const* caches, const dms_layer_io* io, int n_layers, dms_step_layers** out);
+int dms_step_layers_run(dms_step_layers* layers, const int32_t* seq_ids, int B, void* workspace, size_t ws_bytes,
+                        void* stream);
+int dms_step_layers_one_launch(const dms_step_layers* layers, int B, int32_t* one_launch);
+int dms_step_layers_destroy(dms_step_layers* layers);
+
 /* ---- training mode (walkthrough, Gumbel 噪声与可微门控 and 注意力 / 训练模式) ---- */
 
 /*

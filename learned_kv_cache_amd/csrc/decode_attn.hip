@@ -24,6 +24,8 @@
 #include <cstdlib>
 #include <mutex>
 
+#include <memory>
+#include <vector>
 #include "dms_internal.h"
 #include "decode_prep.h"
 
@@ -1818,15 +1820,16 @@ __device__ void plan_build(const DecodeArgs& a, const StepArgs& sa, FastLds<G, D
 // per SIMD, i.e. two workgroups per CU: the one-launch step needs its prepare
 // and attention workgroups resident together, and the launch shape asks for
 // exactly two per CU; at 3 the register cap leaves one tile fewer in flight)
-template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 2 : 1)))
-void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
+// Workgroup wg of one step (the body of the kernel below, and of each layer
+// of the persistent kernel after it).
+template <int D, int G, int NP, bool FP8, int LPR, bool MF>
+__device__ __forceinline__ void step_body(const DecodeArgs& a, const AppendArgs& ap, const PrepIn& pin,
+                                          const StepArgs& sa, int wg, FastLds<G, D, true>& lds) {
   constexpr int KV = FP8 ? DMS_FP8_E4M3 : DMS_BF16;
-  __shared__ FastLds<G, D, true> lds;
-  if (static_cast<int>(blockIdx.x) < sa.nprep) {
+  if (wg < sa.nprep) {
     PrepShared& sh = lds.prep;
-    if (sa.per_row) prep_row<KV>(ap, pin, blockIdx.x, sh);
-    else prep_pair<KV>(ap, pin, blockIdx.x, true, sh);
+    if (sa.per_row) prep_row<KV>(ap, pin, wg, sh);
+    else prep_pair<KV>(ap, pin, wg, true, sh);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
@@ -1869,7 +1872,89 @@ void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  decode_attn_fast_body<D, G, NP, FP8, LPR, true, MF>(a, &sa, blockIdx.x - sa.nprep, sa.agrid, lds);
+  decode_attn_fast_body<D, G, NP, FP8, LPR, true, MF>(a, &sa, wg - sa.nprep, sa.agrid, lds);
+}
+
+template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 2 : 1)))
+void decode_step_kernel(DecodeArgs a, AppendArgs ap, PrepIn pin, StepArgs sa) {
+  __shared__ FastLds<G, D, true> lds;
+  step_body<D, G, NP, FP8, LPR, MF>(a, ap, pin, sa, blockIdx.x, lds);
+}
+
+// The decode step of every layer of a model in one launch (dms_step_layers_run).
+// Layer l is the step above on layer l's cache, with layer l's inputs and
+// outputs; a grid-wide barrier between layers lets layer l+1 start only once
+// every attention workgroup of layer l has written its outputs (in a model,
+// layer l+1's inputs are computed from them), which also frees the shared
+// workspace's partial records for the next layer.  The prepare role of a
+// layer's last pair commits that layer while the others go on.  All
+// workgroups are resident (checked at launch); each wait is bounded.
+struct LayerDesc {
+  DecodeArgs a;                 // seq_ids, B and partials are the call's
+  AppendArgs ap;                // seq_ids and B are the call's
+  PrepIn pin;
+  const uint8_t* k;             // [B][Hkv][D] rows of the current token
+  const uint8_t* v;
+};
+struct LayersRun {
+  const int32_t* seq_ids;
+  int B;
+  float* partials;              // caller's workspace, shared by the layers
+  StepArgs sa;                  // k and v are each layer's
+  int32_t* bar;                 // [0] attention workgroups done, over the layers; [1] workgroups finished
+  int n_layers;
+  int nwg;
+};
+
+template <int D, int G, int NP, bool FP8, int LPR, bool MF = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MF && G <= 4) ? 2 : 1)))
+void decode_layers_kernel(const LayerDesc* __restrict__ desc, LayersRun r) {
+  __shared__ FastLds<G, D, true> lds;
+  const int wg = blockIdx.x;
+  const bool attn = wg >= r.sa.nprep;
+  for (int l = 0; l < r.n_layers; ++l) {
+    DecodeArgs a = desc[l].a;
+    a.seq_ids = r.seq_ids;
+    a.B = r.B;
+    a.partials = r.partials;
+    AppendArgs ap = desc[l].ap;
+    ap.seq_ids = r.seq_ids;
+    ap.B = r.B;
+    const PrepIn pin = desc[l].pin;
+    StepArgs sa = r.sa;
+    sa.k = desc[l].k;
+    sa.v = desc[l].v;
+    step_body<D, G, NP, FP8, LPR, MF>(a, ap, pin, sa, wg, lds);
+    if (l + 1 == r.n_layers) break;
+    // layer barrier: attention workgroups count themselves once their
+    // outputs (and, for a unit's last one, the merge) are written
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (attn) {
+        __threadfence();
+        __hip_atomic_fetch_add(r.bar, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const int want = (l + 1) * sa.agrid;
+      for (int it = 0;; ++it) {
+        if (__hip_atomic_load(r.bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+        if (it >= sa.spin_limit) {
+          set_status(a.d.ctl, DMS_DEV_STEP_SYNC);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+  }
+  // every workgroup is past its last wait: the last one to finish clears the
+  // counters for the next launch
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(r.bar + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == r.nwg - 1) {
+    __hip_atomic_store(r.bar, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(r.bar + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int D, int G, bool FP8, int NP>
@@ -2178,6 +2263,216 @@ extern "C" int dms_decode_step(dms_cache* cache, const int32_t* seq_ids, const v
               linear ? 0 : 1, spin};
   hipLaunchKernelGGL(kern, dim3(nprep + agrid), dim3(256), 0, st, a, ap, pin, sa);
   return check_hip(hipGetLastError(), "dms_decode_step launch");
+}
+
+namespace dms {
+
+// The persistent kernel of a cache's shape (the variants of step_kernel).
+using LayersKernel = void (*)(const LayerDesc*, LayersRun);
+
+template <int D, int G>
+static LayersKernel layers_kernel_dg(const Geo& g, int lanes_per_row, bool mfma) {
+  if (g.kv_dtype == DMS_FP8_E4M3) return decode_layers_kernel<D, G, 2, true, D / 16>;
+  constexpr int RB = D * 2;
+  constexpr int LPR1 = RB / 16 >= 16 ? 16 : RB / 16;
+  if (mfma) return decode_layers_kernel<D, G, 2, false, LPR1, true>;
+  if constexpr (RB / 16 >= 16) {
+    if (lanes_per_row == 8) return decode_layers_kernel<D, G, 2, false, 8>;
+  }
+  return decode_layers_kernel<D, G, 2, false, LPR1>;
+}
+
+template <int D>
+static LayersKernel layers_kernel_d(const Geo& g, int lanes_per_row, bool mfma) {
+  switch (g.g) {
+    case 1: return layers_kernel_dg<D, 1>(g, lanes_per_row, mfma);
+    case 2: return layers_kernel_dg<D, 2>(g, lanes_per_row, mfma);
+    case 4: return layers_kernel_dg<D, 4>(g, lanes_per_row, mfma);
+    case 8: return layers_kernel_dg<D, 8>(g, lanes_per_row, mfma);
+    default: return nullptr;
+  }
+}
+
+}  // namespace dms
+
+struct dms_step_layers {
+  std::vector<dms_cache*> caches;
+  std::vector<dms_layer_io> io;
+  int device = -1;
+  dms::LayersKernel kern = nullptr;   // null: the layers run as one dms_decode_step each
+  int blocks_per_cu = 0;
+  dms::LayerDesc* desc = nullptr;     // [n_layers] device
+  int32_t* bar = nullptr;             // [2] device, zero between launches
+};
+
+namespace dms {
+
+static bool same_shape(const dms_cache* a, const dms_cache* b) {
+  const Geo &x = a->geo, &y = b->geo;
+  return x.Bmax == y.Bmax && x.Hq == y.Hq && x.Hkv == y.Hkv && x.D == y.D && x.H == y.H && x.w == y.w &&
+         x.P == y.P && x.kv_dtype == y.kv_dtype && a->cfg.decide_mode == b->cfg.decide_mode &&
+         a->device == b->device && a->decode_lpr == b->decode_lpr && a->decode_mfma == b->decode_mfma &&
+         a->decode_grid == b->decode_grid && a->step_fuse == b->step_fuse;
+}
+
+static int layers_fallback(dms_step_layers* p, const int32_t* seq_ids, int B, void* ws, size_t ws_bytes, void* stream) {
+  for (size_t l = 0; l < p->caches.size(); ++l) {
+    const dms_layer_io& o = p->io[l];
+    int s = dms_decode_step(p->caches[l], seq_ids, o.hidden, o.rms_gamma, o.W, o.bias, o.offsets, o.q_inout, o.k, o.v,
+                            o.out, B, o.logits_out, o.evict_out, ws, ws_bytes, stream);
+    if (s) return s;
+  }
+  return DMS_OK;
+}
+
+}  // namespace dms
+
+extern "C" int dms_step_layers_create(dms_cache* const* caches, const dms_layer_io* io, int n_layers,
+                                      dms_step_layers** out) {
+  if (!out) return fail(DMS_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!caches || !io) return fail(DMS_ERR_ARG, "caches and io are required");
+  if (n_layers <= 0 || n_layers > kMaxStepLayers)
+    return fail(DMS_ERR_ARG, "n_layers must be in 1.." + std::to_string(kMaxStepLayers));
+  for (int l = 0; l < n_layers; ++l) {
+    if (!caches[l]) return fail(DMS_ERR_ARG, "cache " + std::to_string(l) + " is NULL");
+    if (!same_shape(caches[0], caches[l]))
+      return fail(DMS_ERR_ARG, "cache " + std::to_string(l) + " differs from cache 0 in shape, mode or device");
+    for (int j = 0; j < l; ++j)
+      if (caches[j] == caches[l]) return fail(DMS_ERR_ARG, "a cache appears twice");
+    const dms_layer_io& o = io[l];
+    if (!o.q_inout || !o.out || !o.k || !o.v || !o.offsets || !o.evict_out)
+      return fail(DMS_ERR_ARG, "layer " + std::to_string(l) + ": q_inout, out, k, v, offsets and evict_out are required");
+    if (caches[0]->cfg.decide_mode == DMS_DECIDE_LINEAR && (!o.hidden || !o.rms_gamma || !o.W))
+      return fail(DMS_ERR_ARG, "layer " + std::to_string(l) + ": hidden, rms_gamma and W are required");
+  }
+  dms_cache* c0 = caches[0];
+  const Geo& g = c0->geo;
+  const bool linear = c0->cfg.decide_mode == DMS_DECIDE_LINEAR;
+  // one launch needs the one-launch step's conditions in every layer
+  bool fused = c0->step_fuse != 0 && fast_decode_ok(c0, nullptr) && (!linear || c0->cfg.hidden % 8 == 0);
+  for (int l = 0; l < n_layers && fused; ++l) {
+    const dms_layer_io& o = io[l];
+    uintptr_t al = reinterpret_cast<uintptr_t>(o.q_inout) | reinterpret_cast<uintptr_t>(o.k) |
+                   reinterpret_cast<uintptr_t>(o.v) | reinterpret_cast<uintptr_t>(o.out);
+    if (linear)
+      al |= reinterpret_cast<uintptr_t>(o.hidden) | reinterpret_cast<uintptr_t>(o.rms_gamma) |
+            reinterpret_cast<uintptr_t>(o.W);
+    if (al % 16) fused = false;
+  }
+  std::unique_ptr<dms_step_layers> p(new dms_step_layers());
+  p->caches.assign(caches, caches + n_layers);
+  p->io.assign(io, io + n_layers);
+  p->device = c0->device;
+  if (fused) {
+    p->kern = g.D == 128 ? layers_kernel_d<128>(g, c0->decode_lpr, mfma_decode_ok(c0))
+                         : layers_kernel_d<64>(g, c0->decode_lpr, mfma_decode_ok(c0));
+  }
+  if (p->kern) {
+    int dev = -1;
+    if (int s = check_hip(hipGetDevice(&dev), "hipGetDevice")) return s;
+    if (dev != c0->device) return fail(DMS_ERR_ARG, "the caches' device must be the current device");
+    if (int s = check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&p->blocks_per_cu,
+                                                                        reinterpret_cast<const void*>(p->kern), 256, 0),
+                          "layers kernel occupancy"))
+      return s;
+    std::vector<LayerDesc> h(n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+      const dms_cache* c = caches[l];
+      const dms_layer_io& o = io[l];
+      LayerDesc& L = h[l];
+      L.a = DecodeArgs{c->dev, c->geo, nullptr, o.q_inout, o.out, 0, c->decode_lpr, nullptr,
+                       mfma_decode_ok(c) ? c->decode_mfma : 0};
+      L.ap = AppendArgs{};
+      L.ap.d = c->dev;
+      L.ap.g = c->geo;
+      L.ap.k = o.k;
+      L.ap.v = o.v;
+      L.ap.T = 1;
+      L.ap.bias = o.bias;
+      L.ap.offsets = o.offsets;
+      L.ap.alpha = c->cfg.alpha_scale;
+      L.ap.eps = c->cfg.rms_eps;
+      L.ap.per_layer = c->cfg.alpha_per == DMS_ALPHA_PER_LAYER;
+      L.ap.disable = c->cfg.disable_eviction != 0;
+      L.ap.logits_out = o.logits_out;
+      L.ap.evict_out = o.evict_out;
+      L.pin = PrepIn{static_cast<const uint16_t*>(o.hidden), o.rms_gamma, o.W, static_cast<uint16_t*>(o.q_inout),
+                     linear ? 0 : 1};
+      L.k = static_cast<const uint8_t*>(o.k);
+      L.v = static_cast<const uint8_t*>(o.v);
+    }
+    void* d = nullptr;
+    if (int s = check_hip(hipMalloc(&d, sizeof(LayerDesc) * n_layers + 64), "hipMalloc (layer descriptors)"))
+      return s;
+    p->desc = static_cast<LayerDesc*>(d);
+    p->bar = reinterpret_cast<int32_t*>(static_cast<char*>(d) + sizeof(LayerDesc) * n_layers);
+    int s = check_hip(hipMemcpy(p->desc, h.data(), sizeof(LayerDesc) * n_layers, hipMemcpyHostToDevice),
+                      "hipMemcpy (layer descriptors)");
+    if (!s) s = check_hip(hipMemset(p->bar, 0, 64), "hipMemset (layer barrier)");
+    if (s) {
+      hipFree(d);
+      return s;
+    }
+  }
+  *out = p.release();
+  return DMS_OK;
+}
+
+extern "C" int dms_step_layers_run(dms_step_layers* p, const int32_t* seq_ids, int B, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  if (!p) return fail(DMS_ERR_ARG, "layers is NULL");
+  dms_cache* c0 = p->caches[0];
+  const Geo& g = c0->geo;
+  if (B <= 0) return fail(DMS_ERR_ARG, "B must be positive");
+  if (B > g.Bmax) return fail(DMS_ERR_CAPACITY, "B above max_batch");
+  if (int s = check_workspace(c0, B, workspace, ws_bytes)) return s;
+  const int npairs = B * g.Hkv;
+  const int dgrid = decode_grid_for(c0);
+  const int agrid = std::max(dgrid / 2, dgrid - npairs);
+  const int nwg = npairs + agrid;
+  if (!p->kern || npairs > kMaxUnits || nwg > p->blocks_per_cu * c0->num_cus)
+    return layers_fallback(p, seq_ids, B, workspace, ws_bytes, stream);
+  int spin = kArriveSpinLimit;
+  if (const char* e = std::getenv("DMS_STEP_SPIN_LIMIT")) spin = std::max(0, std::atoi(e));
+  LayersRun r{};
+  r.seq_ids = seq_ids;
+  r.B = B;
+  r.partials = static_cast<float*>(workspace);
+  r.sa = StepArgs{nullptr, nullptr, npairs, npairs, 0, std::min(kArriveGroups, agrid), agrid,
+                  c0->cfg.decide_mode == DMS_DECIDE_LINEAR ? 0 : 1, spin};
+  r.bar = p->bar;
+  r.n_layers = static_cast<int>(p->caches.size());
+  r.nwg = nwg;
+  hipLaunchKernelGGL(p->kern, dim3(nwg), dim3(256), 0, as_stream(stream), p->desc, r);
+  return check_hip(hipGetLastError(), "dms_step_layers_run launch");
+}
+
+extern "C" int dms_step_layers_one_launch(const dms_step_layers* p, int B, int32_t* one_launch) {
+  if (!p || !one_launch) return fail(DMS_ERR_ARG, "layers and one_launch are required");
+  const dms_cache* c0 = p->caches[0];
+  const int npairs = B * c0->geo.Hkv;
+  const int dgrid = decode_grid_for(c0);
+  const int nwg = npairs + std::max(dgrid / 2, dgrid - npairs);
+  *one_launch = (p->kern && B > 0 && B <= c0->geo.Bmax && npairs <= kMaxUnits &&
+                 nwg <= p->blocks_per_cu * c0->num_cus)
+                    ? 1
+                    : 0;
+  return DMS_OK;
+}
+
+extern "C" int dms_step_layers_destroy(dms_step_layers* p) {
+  if (!p) return DMS_OK;
+  int s = DMS_OK;
+  if (p->desc) {
+    int dev = -1;
+    s = check_hip(hipGetDevice(&dev), "hipGetDevice");
+    if (!s && dev != p->device) s = check_hip(hipSetDevice(p->device), "hipSetDevice");
+    if (!s) s = check_hip(hipFree(p->desc), "hipFree (layer descriptors)");
+    if (dev >= 0 && dev != p->device) hipSetDevice(dev);
+  }
+  delete p;
+  return s;
 }
 
 extern "C" int dms_decode_attn_noalloc(dms_cache* cache, const int32_t* seq_ids, const void* q, void* out, int B,

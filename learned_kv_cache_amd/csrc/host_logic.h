@@ -15,6 +15,7 @@
 namespace dms {
 
 constexpr int kMaxUnits = 2048;        // B * Hkv of one decode/append call
+constexpr int kMaxStepLayers = 512;    // layers of one dms_step_layers binding
 constexpr int kMaxChunk = 8192;        // largest T of one append / prefill call
 constexpr int kMaxDecodeGrid = 2048;   // workgroups of the decode attention kernel
 constexpr int kCtlWords = 64;

@@ -48,6 +48,7 @@ EXPORTS = (
     "dms_train_gate", "dms_train_gate_bwd", "dms_train_attn_fwd", "dms_seq_info_get", "dms_pages_needed",
     "dms_kvzap_score", "dms_kvzap_workspace_bytes", "dms_train_attn_bwd", "dms_train_attn_bwd_workspace_bytes",
     "dms_decode_workspace_bytes", "dms_decode_attn_noalloc", "dms_cache_check",
+    "dms_step_layers_create", "dms_step_layers_run", "dms_step_layers_one_launch", "dms_step_layers_destroy",
 )
 
 
@@ -77,6 +78,11 @@ class dms_dump(ctypes.Structure):
 class dms_seq_info(ctypes.Structure):
     _fields_ = [("position", ctypes.c_int32), ("live_slots", ctypes.c_int32), ("max_head_slots", ctypes.c_int32),
                 ("pages", ctypes.c_int32)]
+
+
+class dms_layer_io(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "hidden", "rms_gamma", "W", "bias", "offsets", "q_inout", "k", "v", "out", "logits_out", "evict_out")]
 
 
 class dms_stats(ctypes.Structure):
@@ -114,6 +120,10 @@ def lib():
             "dms_train_gate": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp],
             "dms_train_gate_bwd": [vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp, vp, vp, vp],
             "dms_cache_check": [vp, vp, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32)],
+            "dms_step_layers_create": [ctypes.POINTER(vp), ctypes.POINTER(dms_layer_io), i32, ctypes.POINTER(vp)],
+            "dms_step_layers_run": [vp, vp, i32, vp, sz, vp],
+            "dms_step_layers_one_launch": [vp, i32, ctypes.POINTER(ctypes.c_int32)],
+            "dms_step_layers_destroy": [vp],
             "dms_seq_info_get": [vp, vp, i32, vp, ctypes.POINTER(dms_seq_info)],
             "dms_pages_needed": [vp, vp, vp, i32, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
             "dms_train_attn_fwd": [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp],
@@ -347,6 +357,68 @@ def dms_decode_step(cache: DmsCache, seq_ids, hidden, rms_gamma, W, bias, offset
         _ptr(q_inout, "q_inout", ad, nq), _ptr(k, "k", ad, n), _ptr(v, "v", ad, n), _ptr(out, "out", ad, nq), B,
         _ptr(logits_out, "logits_out", torch.float32, B * c.num_kv_heads),
         _ptr(evict_out, "evict_out", torch.uint8, B * c.num_kv_heads), *_ws(cache, workspace, B), _stream(stream)))
+
+
+class StepLayers:
+    """dms_step_layers: the decode step of every layer in one launch.
+
+    caches: the layers' DmsCache objects (one shape); io: per layer a dict of
+    device tensors sized for max_batch rows, with the keys of dms_layer_io
+    (hidden, rms_gamma, W, bias, offsets, q_inout, k, v, out, logits_out,
+    evict_out; hidden / rms_gamma / W only for the linear decision, bias and
+    logits_out optional).  The tensors are bound, not copied: each run reads
+    and writes them (rows [0, B) of a call)."""
+
+    def __init__(self, caches: Sequence[DmsCache], io: Sequence[dict]):
+        if len(caches) != len(io):
+            raise ValueError("one io dict per cache")
+        c = caches[0].cfg
+        ad = caches[0].act_dtype
+        Bm = c.max_batch
+        nq = Bm * c.num_q_heads * c.head_dim
+        n = Bm * c.num_kv_heads * c.head_dim
+        arr = (dms_layer_io * len(caches))()
+        self._keep = []
+        for i, d in enumerate(io):
+            lin = c.decide_mode == DMS_DECIDE_LINEAR
+            arr[i].hidden = _ptr(d.get("hidden"), "hidden", ad, Bm * c.hidden) if lin else None
+            arr[i].rms_gamma = _ptr(d.get("rms_gamma"), "rms_gamma", torch.float32, c.hidden) if lin else None
+            arr[i].W = _ptr(d.get("W"), "W", torch.float32, c.num_kv_heads * c.hidden) if lin else None
+            arr[i].bias = _ptr(d.get("bias"), "bias", torch.float32, c.num_kv_heads)
+            arr[i].offsets = _ptr(d.get("offsets"), "offsets", torch.float32, c.num_kv_heads)
+            arr[i].q_inout = _ptr(d.get("q_inout"), "q_inout", ad, nq)
+            arr[i].k = _ptr(d.get("k"), "k", ad, n)
+            arr[i].v = _ptr(d.get("v"), "v", ad, n)
+            arr[i].out = _ptr(d.get("out"), "out", ad, nq)
+            arr[i].logits_out = _ptr(d.get("logits_out"), "logits_out", torch.float32, Bm * c.num_kv_heads)
+            arr[i].evict_out = _ptr(d.get("evict_out"), "evict_out", torch.uint8, Bm * c.num_kv_heads)
+            self._keep.append(dict(d))
+        handles = (ctypes.c_void_p * len(caches))(*[x.handle.value for x in caches])
+        h = ctypes.c_void_p()
+        _check(lib().dms_step_layers_create(handles, arr, len(caches), ctypes.byref(h)))
+        self.handle = h
+        self.caches = list(caches)
+
+    def run(self, seq_ids, B: int, workspace=None, stream=None) -> int:
+        c = self.caches[0]
+        return _check(lib().dms_step_layers_run(self.handle, _ptr(seq_ids, "seq_ids", torch.int32, B), B,
+                                                *_ws(c, workspace, B), _stream(stream)))
+
+    def one_launch(self, B: int) -> bool:
+        r = ctypes.c_int32()
+        _check(lib().dms_step_layers_one_launch(self.handle, B, ctypes.byref(r)))
+        return bool(r.value)
+
+    def close(self):
+        if self.handle:
+            lib().dms_step_layers_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def dms_train_gate(logits, noise, tau: float, y_out=None, probs_out=None, hard_out=None, stream=None) -> int:

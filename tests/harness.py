@@ -297,44 +297,66 @@ class Runner:
         self.sim.append(list(seqs), e_np, k_np, v_np)
         return stats
 
+    def step_inputs(self, seqs: Sequence[int], positions: Sequence[int]) -> dict:
+        """Device inputs and output buffers of one decode token per listed sequence."""
+        torch, wl = self.torch, self.wl
+        B = len(seqs)
+        x = dict(B=B, seqs=list(seqs), positions=list(positions))
+        x["seq_dev"] = to_dev(np.asarray(seqs, np.int32), "i32")
+        x["q_np"] = np.stack([self.row("q", b, t) for b, t in zip(seqs, positions)])
+        x["q_dev"] = to_dev(x["q_np"][:, None], wl.act_dtype)
+        x["k_np"] = np.stack([self.row("k", b, t) for b, t in zip(seqs, positions)])[:, None]
+        x["v_np"] = np.stack([self.row("v", b, t) for b, t in zip(seqs, positions)])[:, None]
+        x["k_dev"], x["v_dev"] = to_dev(x["k_np"], wl.act_dtype), to_dev(x["v_np"], wl.act_dtype)
+        x["e_np"] = np.stack([self.prep.evict[b][:, t:t + 1] for b, t in zip(seqs, positions)])
+        x["out"] = torch.empty(B * wl.Hq * wl.D, dtype=x["q_dev"].dtype, device="cuda")
+        x["logits"] = torch.empty(B * wl.Hkv, dtype=torch.float32, device="cuda")
+        x["evict"] = torch.empty(B * wl.Hkv, dtype=torch.uint8, device="cuda")
+        x["h_dev"] = None
+        if wl.decide == "linear":
+            x["h_dev"] = to_dev(np.stack([self.row("h", b, t) for b, t in zip(seqs, positions)]), wl.act_dtype)
+        return x
+
+    def check_prepare_outputs(self, x: dict) -> None:
+        """Decisions and logits of a step (and, query neuron, q_inout after the
+        decision) against the oracle's."""
+        wl = self.wl
+        B, seqs, positions, e_np, q_np = x["B"], x["seqs"], x["positions"], x["e_np"], x["q_np"]
+        ref_l = np.stack([self.prep.logits[b][:, t] for b, t in zip(seqs, positions)])
+        got_e = x["evict"].cpu().numpy().reshape(B, wl.Hkv)
+        assert np.array_equal(got_e, e_np[:, :, 0]), f"decisions differ at {np.argwhere(got_e != e_np[:, :, 0])[:5]}"
+        np.testing.assert_allclose(x["logits"].cpu().numpy().reshape(B, wl.Hkv), ref_l, atol=5e-3, rtol=0)
+        if wl.decide == "qneuron":
+            # the decision neuron is zeroed in place, nothing else changes
+            qz = from_dev(x["q_dev"]).reshape(B, wl.Hq, wl.D)
+            want = q_np.reshape(B, wl.Hq, wl.D).astype(np.float64).copy()
+            want[:, :: wl.g, -1] = 0.0
+            assert np.array_equal(qz, want), "q_inout after the decision"
+
     def decode_step(self, seqs: Sequence[int], positions: Sequence[int], check: bool = True, fused: bool = False,
-                    step: bool = False):
+                    step: bool = False, launched: Optional[dict] = None):
         """decide -> append -> decode attention for one token per listed sequence.
 
         fused=True runs decide + append as one dms_decode_prepare call; step=True
-        runs the whole step as one dms_decode_step call."""
+        runs the whole step as one dms_decode_step call; launched (the dict of
+        step_inputs, its outputs filled by a call made elsewhere, such as a
+        multi-layer step) only checks the results."""
         torch, dms, wl, d = self.torch, self.dms, self.wl, self.prep.draw
-        B = len(seqs)
-        seq_dev = to_dev(np.asarray(seqs, np.int32), "i32")
-        q_np = np.stack([self.row("q", b, t) for b, t in zip(seqs, positions)])
-        q_dev = to_dev(q_np[:, None], wl.act_dtype)
-        k_np = np.stack([self.row("k", b, t) for b, t in zip(seqs, positions)])[:, None]
-        v_np = np.stack([self.row("v", b, t) for b, t in zip(seqs, positions)])[:, None]
-        k_dev, v_dev = to_dev(k_np, wl.act_dtype), to_dev(v_np, wl.act_dtype)
-        e_np = np.stack([self.prep.evict[b][:, t:t + 1] for b, t in zip(seqs, positions)])
-        out = torch.empty(B * wl.Hq * wl.D, dtype=q_dev.dtype, device="cuda")
+        x = launched if launched is not None else self.step_inputs(seqs, positions)
+        if launched is not None:
+            step = True
+        B = x["B"]
+        seq_dev, q_np, q_dev = x["seq_dev"], x["q_np"], x["q_dev"]
+        k_np, v_np, k_dev, v_dev, e_np, out = x["k_np"], x["v_np"], x["k_dev"], x["v_dev"], x["e_np"], x["out"]
         if fused or step:
-            logits = torch.empty(B * wl.Hkv, dtype=torch.float32, device="cuda")
-            evict = torch.empty(B * wl.Hkv, dtype=torch.uint8, device="cuda")
-            h_dev = None
-            if wl.decide == "linear":
-                h_dev = to_dev(np.stack([self.row("h", b, t) for b, t in zip(seqs, positions)]), wl.act_dtype)
-            if step:
+            logits, evict, h_dev = x["logits"], x["evict"], x["h_dev"]
+            if launched is None and step:
                 dms.dms_decode_step(self.cache, seq_dev, h_dev, self.gamma, self.W, None, self.off, q_dev.view(-1),
                                     k_dev, v_dev, out, B, logits, evict)
-            else:
+            elif launched is None:
                 dms.dms_decode_prepare(self.cache, seq_dev, h_dev, self.gamma, self.W, None, self.off,
                                        q_dev.view(-1), k_dev, v_dev, B, logits, evict)
-            ref_l = np.stack([self.prep.logits[b][:, t] for b, t in zip(seqs, positions)])
-            got_e = evict.cpu().numpy().reshape(B, wl.Hkv)
-            assert np.array_equal(got_e, e_np[:, :, 0]), f"decisions differ at {np.argwhere(got_e != e_np[:, :, 0])[:5]}"
-            np.testing.assert_allclose(logits.cpu().numpy().reshape(B, wl.Hkv), ref_l, atol=5e-3, rtol=0)
-            if wl.decide == "qneuron":
-                # the decision neuron is zeroed in place, nothing else changes
-                qz = from_dev(q_dev).reshape(B, wl.Hq, wl.D)
-                want = q_np.reshape(B, wl.Hq, wl.D).astype(np.float64).copy()
-                want[:, :: wl.g, -1] = 0.0
-                assert np.array_equal(qz, want), "q_inout after the decision"
+            self.check_prepare_outputs(x)
         else:
             # decide works per (row, T=1); rows may sit at different positions
             if len(set(positions)) == 1:
