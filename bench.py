@@ -163,10 +163,27 @@ def calibrate_and_fill_ragged(layer, wl, ctx, dms, torch):
         dms.dms_append_evict(layer.cache, seq, k, v, ev[: Hkv * n], 1, n)
 
 
-def decode_step(layers, s, wl, dms, path, ws):
+def step_bindings(layers, wl, dms, torch, S):
+    """One dms_step_layers binding per decode step s: every layer's inputs and
+    outputs of step s (the tensors are bound, not copied, so no copy runs in
+    the timed region) and all B rows in order."""
+    seq = torch.arange(wl.B, dtype=torch.int32, device="cuda")
+    binds = []
+    for s in range(S):
+        io = [dict(hidden=L.h_dec[s], rms_gamma=L.gamma, W=L.W, offsets=L.off, q_inout=L.q_dec[s], k=L.k_dec[s],
+                   v=L.v_dec[s], out=L.out, evict_out=L.evict) for L in layers]
+        binds.append(dms.StepLayers([L.cache for L in layers], io))
+    return seq, binds
+
+
+def decode_step(layers, s, wl, dms, path, ws, binds=None):
     """One decode step over every layer; `ws` is the decode workspace all
     layers share (their calls run in stream order)."""
     B = wl.B
+    if path == "layers":
+        seq, b = binds
+        b[s].run(seq, B, workspace=ws)
+        return
     for L in layers:
         if path == "step":
             dms.dms_decode_step(L.cache, None, L.h_dec[s], L.gamma, L.W, None, L.off, L.q_dec[s], L.k_dec[s],
@@ -184,10 +201,13 @@ def decode_step(layers, s, wl, dms, path, ws):
 # ---------------------------------------------------------------------------
 
 
-def run_decode(args, dms, synth, torch):
+def run_decode(args, dms, synth, torch, extra_paths=()):
+    """The headline decode figures (path args.path), then those of each path
+    in extra_paths on the same caches (the step inputs are replayed; the
+    caches hold room for every run), under "paths"."""
     wl = synth.QWEN8B_DECODE
     S = args.warmup + args.steps
-    max_tokens = wl.prefill + S
+    max_tokens = wl.prefill + S * (1 + len(extra_paths))
     pool_pages = wl.B * wl.Hkv * math.ceil(max_tokens / wl.block)
     cfg = dms.make_config(
         max_batch=wl.B, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
@@ -207,7 +227,12 @@ def run_decode(args, dms, synth, torch):
         assert st == 0, f"device status {st:#x}"
     log(f"{args.layers} layers filled with {wl.prefill} tokens x {wl.B} sequences in {time.time() - t0:.1f}s")
 
-    return time_decode(layers, wl, dms, torch, S, args.warmup, args.steps, args.path, args.attn_reps, args.eager)
+    out = time_decode(layers, wl, dms, torch, S, args.warmup, args.steps, args.path, args.attn_reps, args.eager)
+    for path in extra_paths:
+        r = time_decode(layers, wl, dms, torch, S, args.warmup, args.steps, path, args.attn_reps, args.eager)
+        out.setdefault("paths", {})[path] = {k: r[k] for k in ("value", "ms_per_step", "layer_step_us",
+                                                               "launch_bytes", "launch_gbs", "one_launch")}
+    return out
 
 
 def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager=False):
@@ -215,12 +240,17 @@ def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager
     caches from one captured graph per step, then the attention alone; HIP
     events on the launch stream; figures per layer step."""
     ws = dms.decode_workspace(layers[0].cache.cfg, wl.B)
+    binds = None
+    if path == "layers":
+        binds = step_bindings(layers, wl, dms, torch, S)
+        one = binds[1][0].one_launch(wl.B)
+        log(f"{wl.name}: dms_step_layers over {len(layers)} layers, one launch: {one}")
     graphs = []
     if not eager:
         for s in range(S):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                decode_step(layers, s, wl, dms, path, ws)
+                decode_step(layers, s, wl, dms, path, ws, binds)
             graphs.append(g)
         torch.cuda.synchronize()
         log(f"captured {S} step graphs")
@@ -229,7 +259,7 @@ def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager
         if graphs:
             graphs[s].replay()
         else:
-            decode_step(layers, s, wl, dms, path, ws)
+            decode_step(layers, s, wl, dms, path, ws, binds)
 
     for s in range(warmup):
         step(s)
@@ -305,23 +335,28 @@ def time_decode(layers, wl, dms, torch, S, warmup, steps, path, attn_reps, eager
         "dense_bf16_kv_bytes_per_layer": float(wl.B * wl.Hkv * (wl.prefill + S) * 2 * wl.D * 2),
         "cache_cr": stats["cache_cr"],
         "graphs": bool(graphs),
+        "one_launch": None if binds is None else binds[1][0].one_launch(wl.B),
     }
 
 
-def run_other_decode(dms, synth, torch, wl, n_layers, steps, warmup):
+def run_other_decode(dms, synth, torch, wl, n_layers, steps, warmup, paths=("step",)):
     """A further decode configuration, reported beside the headline: wl's
     layer shape and prompts (uniform, or per-sequence log-uniform lengths),
     n_layers separate layer caches (enough to exceed the Infinity Cache),
-    the step path.  Returns the per-layer-step figures of time_decode."""
+    each step path of `paths` in turn on the same caches (the step inputs are
+    replayed; the caches hold room for every run).  Returns the
+    per-layer-step figures of time_decode for the first path, and those of
+    the others under "paths"."""
     S = warmup + steps
+    cap = S * len(paths)
     if wl.ctx_range is None:
         ctx = np.full(wl.B, wl.prefill)
     else:
         rng = np.random.default_rng(1000 + wl.cfg_id)
         lo, hi = wl.ctx_range
         ctx = np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), wl.B))).astype(np.int64)
-    max_tokens = int(ctx.max()) + S
-    pool_pages = int(sum(wl.Hkv * math.ceil((int(c) + S) / wl.block) for c in ctx))
+    max_tokens = int(ctx.max()) + cap
+    pool_pages = int(sum(wl.Hkv * math.ceil((int(c) + cap) / wl.block) for c in ctx))
     cfg = dms.make_config(
         max_batch=wl.B, num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, head_dim=wl.D, hidden=wl.hidden,
         window=wl.window, block_size=wl.block, max_tokens_per_seq=max_tokens, pool_pages=pool_pages,
@@ -342,12 +377,17 @@ def run_other_decode(dms, synth, torch, wl, n_layers, steps, warmup):
         st = dms.dms_cache_status(L.cache)
         assert st == 0, f"device status {st:#x}"
     log(f"{wl.name}: {n_layers} layers filled (mean prompt {ctx.mean():.0f}) in {time.time() - t0:.1f}s")
-    r = time_decode(layers, wl, dms, torch, S, warmup, steps, "step", 10)
+    keys = ("value", "layer_step_us", "attn_us", "attn_gbs", "attn_bytes", "launch_bytes", "launch_gbs",
+            "mean_live_slots_per_head", "kv_bytes_live_per_layer", "cache_cr", "one_launch")
     out = {"workload": wl.name, "layers": n_layers, "batch": wl.B, "kv_dtype": wl.kv_dtype,
-           "mean_prompt": float(ctx.mean()), "steps": steps}
-    out.update({k: r[k] for k in ("value", "layer_step_us", "attn_us", "attn_gbs", "attn_bytes",
-                                  "mean_live_slots_per_head", "kv_bytes_live_per_layer", "cache_cr")})
-    out["attn_frac_hbm_peak"] = r["attn_gbs"] / HBM_PEAK_GBS
+           "mean_prompt": float(ctx.mean()), "steps": steps, "path": paths[0]}
+    for i, path in enumerate(paths):
+        r = time_decode(layers, wl, dms, torch, S, warmup, steps, path, 10)
+        if i == 0:
+            out.update({k: r[k] for k in keys})
+            out["attn_frac_hbm_peak"] = r["attn_gbs"] / HBM_PEAK_GBS
+        else:
+            out.setdefault("paths", {})[path] = {k: r[k] for k in keys}
     del layers
     torch.cuda.empty_cache()
     return out
@@ -729,9 +769,10 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying graphs")
-    ap.add_argument("--path", choices=("step", "prepare", "unfused"), default="step",
-                    help="step: one dms_decode_step launch per layer; prepare: dms_decode_prepare -> "
-                         "dms_decode_attn; unfused: dms_decide -> dms_append_evict -> dms_decode_attn")
+    ap.add_argument("--path", choices=("step", "layers", "prepare", "unfused"), default="step",
+                    help="step: one dms_decode_step launch per layer; layers: one dms_step_layers launch for "
+                         "every layer; prepare: dms_decode_prepare -> dms_decode_attn; unfused: dms_decide -> "
+                         "dms_append_evict -> dms_decode_attn")
     ap.add_argument("--cpu-steps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -748,7 +789,9 @@ def main() -> int:
     from learned_kv_cache_amd import dms, synth
     dms.lib()
     torch.cuda.set_device(0)
-    dec = run_decode(args, dms, synth, torch)
+    dec = run_decode(args, dms, synth, torch, () if args.path == "layers" else ("layers",))
+    for p, r in dec.get("paths", {}).items():
+        log(f"headline [{p}]: {r['layer_step_us']:.2f} us per layer step, one launch {r['one_launch']}")
     pre = None
     if not args.no_prefill:
         pre = {v: run_prefill(args, dms, synth, torch, v) for v in ("qneuron", "linear")}
@@ -766,12 +809,15 @@ def main() -> int:
     if not args.no_prefill:
         # Llama-3.2-1B has 16 layers; the fp8 serving figure rotates 4 layer caches
         others = {
-            "llama1b_ctx8k_b1": run_other_decode(dms, synth, torch, synth.LLAMA1B_DECODE, 16, 64, 4),
+            "llama1b_ctx8k_b1": run_other_decode(dms, synth, torch, synth.LLAMA1B_DECODE, 16, 64, 4,
+                                                 ("step", "layers")),
             "qwen8b_fp8kv_b64": run_other_decode(dms, synth, torch, synth.QWEN8B_FP8_SERVING, 4, 32, 4),
         }
         for k, r in others.items():
             log(f"{k}: {r['layer_step_us']:.2f} us per layer step ({r['value'] / 1e6:.3f} M tok/s/layer), "
                 f"attention {r['attn_us']:.2f} us = {r['attn_gbs']:.0f} GB/s")
+            for p, rp in r.get("paths", {}).items():
+                log(f"{k} [{p}]: {rp['layer_step_us']:.2f} us per layer step, one launch {rp['one_launch']}")
     kvzap = None
     if not args.no_prefill:
         kvzap = run_kvzap(args, dms, torch)
@@ -796,7 +842,12 @@ def main() -> int:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(args.cpu_steps)
         log(f"cpu baseline {cpu['value']:.1f} tok/s/layer in {cpu['seconds']:.1f}s")
-    if args.path == "step":
+    if args.path == "layers":
+        traffic = traffic_from_profiles("decode_layers")
+        roof = {"kernel": "decode_layers_kernel (dms_step_layers_run)", "achieved": dec["launch_gbs"],
+                "algorithmic_bytes_per_launch": dec["launch_bytes"] * args.layers,
+                "avg_launch_us": dec["ms_per_step"] * 1e3}
+    elif args.path == "step":
         traffic = traffic_from_profiles("decode_step")
         roof = {"kernel": "decode_step_kernel (dms_decode_step)", "achieved": dec["launch_gbs"],
                 "algorithmic_bytes_per_launch": dec["launch_bytes"], "avg_launch_us": dec["layer_step_us"]}
@@ -806,6 +857,8 @@ def main() -> int:
                 "algorithmic_bytes_per_launch": dec["attn_bytes"], "avg_launch_us": dec["attn_us"]}
     steps_desc = {
         "step": "per layer: dms_decode_step (decide + append + attention, one launch)",
+        "layers": "every layer in one dms_step_layers launch (per layer: decide + append + attention; "
+                  "a grid barrier between layers)",
         "prepare": "per layer: dms_decode_prepare (decide + append) -> dms_decode_attn",
         "unfused": "per layer: dms_decide -> dms_append_evict -> dms_decode_attn",
     }
@@ -842,6 +895,8 @@ def main() -> int:
             "algorithmic_bytes_per_launch": roof["algorithmic_bytes_per_launch"],
             "avg_launch_us": roof["avg_launch_us"],
         },
+        "other_paths": {p: dict(r, frac=r["launch_gbs"] / HBM_PEAK_GBS, step=steps_desc[p])
+                        for p, r in dec.get("paths", {}).items()},
         "attn_only": {"kernel": "decode_attn_fast_kernel (dms_decode_attn)", "avg_launch_us": dec["attn_us"],
                       "achieved_gbs": dec["attn_gbs"], "algorithmic_bytes_per_launch": dec["attn_bytes"]},
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},

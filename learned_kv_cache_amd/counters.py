@@ -31,6 +31,7 @@ CSRC = os.path.join(ROOT, "learned_kv_cache_amd", "csrc")
 KINDS = {
     "decode_attn": ("decode_attn_fast_kernel", ("decode_attn.hip", "dms_internal.h")),
     "decode_step": ("decode_step_kernel", ("decode_attn.hip", "decode_prep.h", "dms_internal.h")),
+    "decode_layers": ("decode_layers_kernel", ("decode_attn.hip", "decode_prep.h", "dms_internal.h")),
 }
 COPY_KERNEL = "neg_kernel"
 
