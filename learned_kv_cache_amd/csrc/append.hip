@@ -247,12 +247,11 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(AppendArgs
   prep_pair<KV>(a, in, blockIdx.x, false, sh);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0)
-    sh.last = __hip_atomic_fetch_add(a.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              npairs - 1;
+  if (threadIdx.x == 0) sh.last = prep_arrive(a.d, blockIdx.x, npairs);
   __syncthreads();
   if (!sh.last) return;
   prep_commit<KV>(a, in, npairs, sh);
+  prep_arrive_reset(a.d, npairs, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -1832,9 +1832,7 @@ __device__ __forceinline__ void step_body(const DecodeArgs& a, const AppendArgs&
     else prep_pair<KV>(ap, pin, wg, true, sh);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0)
-      sh.last = __hip_atomic_fetch_add(ap.d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                sa.nprep - 1;
+    if (threadIdx.x == 0) sh.last = prep_arrive(ap.d, wg, sa.nprep);
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(sh.last)) return;
     // the last pair commits once every attention workgroup has arrived: lane
@@ -1870,6 +1868,7 @@ __device__ __forceinline__ void step_body(const DecodeArgs& a, const AppendArgs&
     plan_build<D, G, FP8, LPR, MF>(a, sa, lds);
     if (threadIdx.x < sa.groups)
       __hip_atomic_store(ap.d.arrive + threadIdx.x * kArriveStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prep_arrive_reset(ap.d, sa.nprep, threadIdx.x);
     return;
   }
   decode_attn_fast_body<D, G, NP, FP8, LPR, true, MF>(a, &sa, wg - sa.nprep, sa.agrid, lds);

@@ -123,6 +123,26 @@ struct PrepShared {
   int q[kPrepThreads], dst[kPrepThreads], page[kPrepThreads];
 };
 
+// Prepare workgroup p of nprep counts its arrival (thread 0, after its
+// stores are complete): in group p % ng of the arrive lines, and the last of
+// a group in the control word.  True for the one workgroup that completes
+// the count, which commits.
+__device__ __forceinline__ bool prep_arrive(const DevCache& d, int p, int nprep) {
+  const int ng = min(kArriveGroups, nprep), gi = p % ng;
+  const int n_g = nprep / ng + (gi < nprep % ng ? 1 : 0);
+  return __hip_atomic_fetch_add(d.arrive + gi * kArriveStride + kPrepArriveWord, 1, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT) == n_g - 1 &&
+         __hip_atomic_fetch_add(d.ctl + kCtlPrepArrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ng - 1;
+}
+
+// Resets what prep_arrive counted (the committing workgroup, once all have arrived).
+__device__ __forceinline__ void prep_arrive_reset(const DevCache& d, int nprep, int tid) {
+  const int ng = min(kArriveGroups, nprep);
+  if (tid < ng)
+    __hip_atomic_store(d.arrive + tid * kArriveStride + kPrepArriveWord, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(d.ctl + kCtlPrepArrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // plan record kinds (chunk_info[pair][0..7]: kind, unit, t, slot, e, dst, appended, length before)
 constexpr int kPlanNone = 0;      // nothing to do (bad sequence id, capacity)
 constexpr int kPlanDone = 1;      // the pair's workgroup wrote everything
@@ -504,10 +524,7 @@ __device__ __forceinline__ void prep_commit(const AppendArgs& a, const PrepIn& i
     for (int q = tid; q < npairs; q += kPrepThreads)
       in.q[(static_cast<size_t>(q / g.Hkv) * g.Hq + (q % g.Hkv) * g.g) * g.D + g.D - 1] = 0;
   }
-  if (tid == 0) {
-    d.ctl[kCtlFreeCount] = sh.free_top - min(sh.used, sh.free_top);
-    __hip_atomic_store(d.ctl + kCtlPrepArrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) d.ctl[kCtlFreeCount] = sh.free_top - min(sh.used, sh.free_top);
 }
 
 }  // namespace dms

@@ -145,7 +145,10 @@ __global__ void clear_status_kernel(int32_t* ctl, int32_t* arrive) {
     ctl[kCtlStatus] = 0;
     ctl[kCtlPrepArrive] = 0;
   }
-  if (i < kArriveGroups) arrive[i * kArriveStride] = 0;
+  if (i < kArriveGroups) {
+    arrive[i * kArriveStride] = 0;
+    arrive[i * kArriveStride + kPrepArriveWord] = 0;
+  }
 }
 
 }  // namespace dms

@@ -26,6 +26,12 @@ constexpr int kCtlWords = 64;
 // other.
 constexpr int kArriveGroups = 32;
 constexpr int kArriveStride = 64;      // int32 words between counters
+// The prepare workgroups' arrival counters share those lines, 128 bytes on:
+// prepare workgroup p adds to group p % 32 and the last of a group adds to
+// the control word kCtlPrepArrive, so no counter takes more than a group's
+// returning atomics (one counter for all 512 pairs of a 64-row step
+// serialised them).
+constexpr int kPrepArriveWord = 32;
 // Decode plan of the fused step (written by one step's commit for the next):
 // a header, the sequence id of each batch row, and one record per attention
 // workgroup; used only for launches of at most kPlanMaxWgs workgroups.
