@@ -31,6 +31,19 @@ static int validate(const dms_config* c) {
 
 int decode_grid_for(const dms_cache* c) { return c->decode_grid; }
 
+// The decode grid of a call over `units` (row, KV head) units: two
+// workgroups per CU, or one per CU when the units are at most a quarter of
+// the CUs.  Then every unit gets workgroups of its own, and fewer, longer
+// ranges per workgroup measured faster (Qwen3-8B layer, B 8: 18.7-19.1
+// against 20.1-20.4 us per layer step; Llama-3.2-1B, B 1: within 0.2 us),
+// while 512 units (B 64) measured slower at one per CU.  DMS_DECODE_WGS
+// fixes the grid for every call.  Never above decode_grid, which sizes the
+// workspace.
+int decode_grid_call(const dms_cache* c, int units) {
+  if (c->decode_grid_fixed || 4 * units > c->num_cus) return c->decode_grid;
+  return std::min(c->decode_grid, c->num_cus);
+}
+
 int decode_grid_default(int cus) {
   int grid = 2 * cus;
   if (const char* e = std::getenv("DMS_DECODE_WGS")) grid = std::atoi(e);
@@ -259,6 +272,7 @@ int dms_cache_create(const dms_config* cfg, void* dev_buf, size_t bytes, void* s
                      "hipDeviceGetAttribute"))) { delete c; return s; }
   c->num_cus = cus;
   c->decode_grid = decode_grid_default(cus);
+  c->decode_grid_fixed = std::getenv("DMS_DECODE_WGS") != nullptr;
   c->decode_np = 0;
   if (const char* e = std::getenv("DMS_DECODE_NP")) c->decode_np = std::atoi(e);
   c->decode_lpr = 0;

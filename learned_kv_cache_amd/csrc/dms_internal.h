@@ -64,7 +64,8 @@ struct dms_cache {
   dms::Layout layout;
   int device;
   int num_cus;
-  int decode_grid;
+  int decode_grid;       // the decode attention's workgroups at most (2 per CU, or DMS_DECODE_WGS)
+  bool decode_grid_fixed;  // DMS_DECODE_WGS was set: every call uses decode_grid
   int decode_np;         // passes in flight per round of the decode kernel (DMS_DECODE_NP; 0: default)
   int decode_lpr;        // lanes per row of the decode kernel (DMS_DECODE_LPR; 0: default)
   int decode_mfma;       // matrix-core decode for bf16 pages of >= 16 rows (DMS_DECODE_MFMA; default 1)
@@ -80,6 +81,7 @@ namespace dms {
 int fail(int status, const std::string& msg);
 int check_hip(hipError_t e, const char* what);
 int decode_grid_for(const dms_cache* c);
+int decode_grid_call(const dms_cache* c, int units);
 // Decode attention workgroups on a device with `cus` compute units (2 per CU,
 // or DMS_DECODE_WGS), capped at kMaxDecodeGrid.
 int decode_grid_default(int cus);
