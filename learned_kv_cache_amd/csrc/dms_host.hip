@@ -32,16 +32,17 @@ static int validate(const dms_config* c) {
 int decode_grid_for(const dms_cache* c) { return c->decode_grid; }
 
 // The decode grid of a call over `units` (row, KV head) units: two
-// workgroups per CU, or one per CU when the units are at most a quarter of
-// the CUs.  Then every unit gets workgroups of its own, and fewer, longer
-// ranges per workgroup measured faster (Qwen3-8B layer, B 8: 18.7-19.1
-// against 20.1-20.4 us per layer step; Llama-3.2-1B, B 1: within 0.2 us),
-// while 512 units (B 64) measured slower at one per CU.  DMS_DECODE_WGS
-// fixes the grid for every call.  Never above decode_grid, which sizes the
-// workspace.
+// workgroups per CU, or about one per CU (the CUs plus a quarter of the
+// units) when the units are at most a quarter of the CUs.  Then every unit
+// gets workgroups of its own, and fewer, longer ranges per workgroup
+// measured faster (Qwen3-8B layer, B 8: 18.2-18.5 us per layer step at 272
+// workgroups, 18.7-19.1 at 256, 20.1-20.4 at 512; Llama-3.2-1B, B 1: within
+// 0.2 us), while 512 units (B 64) measured slower at one per CU.
+// DMS_DECODE_WGS fixes the grid for every call.  Never above decode_grid,
+// which sizes the workspace.
 int decode_grid_call(const dms_cache* c, int units) {
   if (c->decode_grid_fixed || 4 * units > c->num_cus) return c->decode_grid;
-  return std::min(c->decode_grid, c->num_cus);
+  return std::min(c->decode_grid, c->num_cus + units / 4);
 }
 
 int decode_grid_default(int cus) {
